@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode megakernel on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama1b_ctx128]
+
+A step is one whole decode step (every stage of the hot path, one launch) of
+the Llama-3.2-1B-shaped decoder at batch 1 over synthetic bf16 weights, with
+the greedy token chained on the device.  W warm-up steps run from the
+pre-filled context, then the position is reset and exactly K steps are timed,
+bracketed by device synchronisation.  Prints ONE JSON line.
+
+roofline.achieved = algorithmic bytes of one launch (every weight once, the
+KV rows [0, pos) read and the new row written) / the average kernel duration
+measured with HIP events recorded around every launch on its stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per decode step @batch1 (Llama-1B shape); achieved HBM GB/s vs peak"
+PEAK_HBM = 8.0e12  # MI355X published HBM3E bandwidth, bytes/s
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("mk_kernel.hip", "mk_isa.h"):
+        with open(os.path.join(ROOT, "persistent_megakernel_wg_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shape, weights, kc, vc, tokens, budget_s: float = 20.0):
+    """Time the CPU oracle on a bounded sample of the same workload."""
+    import numpy as np
+    from oracle import DecoderOracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    orc = DecoderOracle(shape, weights)
+    k, v = kc.copy(), vc.copy()
+    tok = np.asarray(tokens)
+    t0 = time.perf_counter()
+    _, tok = orc.step(tok, shape.prefill, k, v)       # warm-up: widens the weights
+    warm = time.perf_counter() - t0
+    times = []
+    pos = shape.prefill + 1
+    while sum(times) < budget_s and pos < shape.max_seq and len(times) < shape.steps:
+        t0 = time.perf_counter()
+        _, tok = orc.step(tok, pos, k, v)
+        times.append(time.perf_counter() - t0)
+        pos += 1
+    us = 1e6 * sum(times) / len(times)
+    return {"value": round(us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": "%s: %d float64 decode steps at positions %d..%d after one warm-up step "
+                      "(%.1f s, weight widening) on the host" % (
+                          shape.name, len(times), shape.prefill + 1, pos - 1, warm)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama1b_ctx128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--n-cus", type=int, default=0)
+    ap.add_argument("--attn-block", type=int, default=0)
+    ap.add_argument("--mlp-chunks", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode megakernel runs on a single device "
+              "(--gpus %d is not supported)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from persistent_megakernel_wg_amd import binding as B
+    from persistent_megakernel_wg_amd import synth
+    from persistent_megakernel_wg_amd.engine import Engine
+
+    shape = synth.SHAPES[args.workload]
+    if shape.is_moe:
+        print("workload %s is not built" % shape.name, file=sys.stderr)
+        return 2
+    t0 = time.perf_counter()
+    weights = synth.make_weights(shape)
+    kc, vc = synth.make_kv_cache(shape)
+    tokens = synth.make_tokens(shape)
+    t_gen = time.perf_counter() - t0
+    print("[bench] inputs generated in %.1f s" % t_gen, file=sys.stderr, flush=True)
+
+    eng = Engine(shape, weights, kc, vc,
+                 plan=B.plan_opts(n_cus=args.n_cus, attn_block=args.attn_block,
+                                  mlp_chunks=args.mlp_chunks))
+    info = eng.plan_info()
+    dev = eng.dev
+    stream = torch.cuda.current_stream(dev)
+    span = shape.max_seq - shape.prefill
+    K, W = args.steps, args.warmup
+    bufs = [torch.zeros(shape.batch, dtype=torch.int32, device=dev) for _ in range(K + W + 1)]
+    bufs[0].copy_(torch.from_numpy(tokens))
+
+    def pos_of(i):
+        return shape.prefill + (i % span)
+
+    # warm-up from the initial state, then restart at the pre-filled position
+    for i in range(W):
+        eng.launch(pos_of(i), tokens=bufs[i], next_out=bufs[i + 1], stream=stream)
+    eng.sync()
+    bufs[W].copy_(bufs[0])
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize(dev)
+    t_start = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        eng.launch(pos_of(i), tokens=bufs[W + i], next_out=bufs[W + i + 1], stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t_start
+    eng.sync()
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_kernel_s = float(np.mean(kern_ms)) / 1e3
+    ms_per_step = 1e3 * wall / K
+
+    wbytes = synth.weight_bytes_per_step(shape)
+    kvb = [synth.kv_bytes_per_step(shape, pos_of(i)) for i in range(K)]
+    alg_bytes = wbytes + float(np.mean(kvb))
+    achieved = alg_bytes / avg_kernel_s
+    traffic = traffic_from_profiles(shape.name)
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_per_step * 1e3, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": shape.name, "layers": shape.n_layers, "hidden": shape.hidden,
+                   "q_heads": shape.n_q_heads, "kv_heads": shape.n_kv_heads,
+                   "head_dim": shape.head_dim, "ffn": shape.ffn, "vocab": shape.vocab,
+                   "batch": shape.batch, "context": shape.prefill, "weights": "bf16",
+                   "kv_cache": "bf16", "n_cus": info["n_cus"], "attn_block": info["attn_block"],
+                   "mlp_chunks": info["mlp_chunks"]},
+        "kernel_us_per_step": round(avg_kernel_s * 1e6, 2),
+        "kernel_us_median": round(float(np.median(kern_ms)) * 1e3, 2),
+        "kernel_us_p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 2),
+        "tok_per_s": round(1.0 / (ms_per_step / 1e3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": int(alg_bytes)},
+        "cpu_baseline": None,
+    }
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle (bounded sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(shape, weights, kc, vc, tokens, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

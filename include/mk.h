@@ -1,0 +1,176 @@
+/*
+ * mk.h — C ABI of the MI355X (gfx950) batch-1 decode megakernel.
+ *
+ * One decode step of a Llama-style decoder (RMSNorm, QKV projection, RoPE, GQA
+ * attention over a bf16 KV cache, O projection, SwiGLU MLP, LM head + greedy
+ * argmax) runs as ONE persistent HIP kernel with one workgroup per compute
+ * unit.  Each workgroup interprets a host-built queue of tile-sized
+ * instructions; instructions wait on each other through counters in global
+ * memory instead of kernel boundaries.  This follows the design described in
+ * Hazy Research's Llama-1B megakernel write-up ("Fusing Operations with an
+ * On-GPU Interpreter", "Efficient Shared Memory Management" and "Custom
+ * Synchronization Mechanism" in the rocketrecap.com summary) and the persistent
+ * per-SM task-list kernel in Cohere's write-up (airebao.com, «Megakernel
+ * 是什么»), re-designed for gfx950.
+ *
+ * Conventions
+ *   - Every call returns an mk_status; nothing throws or aborts across the ABI.
+ *     On error, mk_last_error() returns a message.
+ *   - Weights, KV cache, tokens, next-token and logits buffers are device
+ *     memory owned by the CALLER.  They must outlive the context and any step
+ *     in flight.  The library never frees them.
+ *   - The library owns its arena (activations, counters, RoPE tables, plan,
+ *     argmax/attention scratch, status word) and frees it in mk_destroy.
+ *   - bf16 tensors are row-major [out, in] (PyTorch nn.Linear layout), stacked
+ *     over layers.  KV caches are bf16 [L][B][G][max_seq][Dh]; cached keys are
+ *     stored after RoPE.
+ *   - One context is used by one host thread at a time.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mk_ctx mk_ctx; /* opaque, owned by the library */
+
+typedef enum {
+  MK_OK = 0,
+  MK_ERR_INVALID_ARG = -1, /* bad pointer, shape, option or position       */
+  MK_ERR_HIP = -2,         /* a HIP runtime call failed                     */
+  MK_ERR_NO_PLAN = -3,     /* mk_decode_step before mk_build_plan           */
+  MK_ERR_UNSUPPORTED = -4, /* shape the kernel has no code path for         */
+  MK_ERR_OOM = -5,         /* device allocation failed                      */
+  MK_ERR_TIMEOUT = -6,     /* a counter wait exceeded the watchdog          */
+  MK_ERR_DEVICE = -7       /* the kernel reported an error (e.g. NaN logits)*/
+} mk_status;
+
+/* Model shape.  Dense decoders set n_experts = top_k = expert_ffn = 0 and
+ * parallel_block = 0. */
+typedef struct {
+  int32_t n_layers;       /* L                                   */
+  int32_t hidden;         /* d                                   */
+  int32_t n_q_heads;      /* H                                   */
+  int32_t n_kv_heads;     /* G (H % G == 0)                      */
+  int32_t head_dim;       /* Dh (64 or 128)                      */
+  int32_t ffn;            /* F (dense SwiGLU width)              */
+  int32_t vocab;          /* V                                   */
+  int32_t max_seq;        /* KV-cache capacity in positions      */
+  int32_t batch;          /* B (1 for the dense path)            */
+  int32_t tied_embedding; /* 1: lm_head may equal embed          */
+  int32_t n_experts;      /* MoE only                            */
+  int32_t top_k;          /* MoE only                            */
+  int32_t expert_ffn;     /* MoE only                            */
+  int32_t parallel_block; /* MoE only                            */
+  float rms_eps;          /* RMSNorm epsilon (inside the sqrt)   */
+  float rope_theta;       /* RoPE base                           */
+} mk_config;
+
+/* Caller-owned DEVICE pointers.  bf16 unless noted.  Unused entries are NULL. */
+typedef struct {
+  const void *embed;      /* [V, d]                                */
+  const void *lm_head;    /* [V, d]; may equal embed               */
+  const void *final_norm; /* [d]                                   */
+  const void *attn_norm;  /* [L, d]                                */
+  const void *wq;         /* [L, H*Dh, d]                          */
+  const void *wk;         /* [L, G*Dh, d]                          */
+  const void *wv;         /* [L, G*Dh, d]                          */
+  const void *wo;         /* [L, d, H*Dh]                          */
+  const void *mlp_norm;   /* [L, d]                                */
+  const void *w_gate;     /* [L, F, d]                             */
+  const void *w_up;       /* [L, F, d]                             */
+  const void *w_down;     /* [L, d, F]                             */
+  const void *router;     /* MoE: [L, E, d]                        */
+  const void *e_gate;     /* MoE: [L, E, Fe, d]                    */
+  const void *e_up;       /* MoE: [L, E, Fe, d]                    */
+  const void *e_down;     /* MoE: [L, E, d, Fe]                    */
+  void *k_cache;          /* [L, B, G, max_seq, Dh], written at pos */
+  void *v_cache;          /* [L, B, G, max_seq, Dh], written at pos */
+} mk_weights;
+
+/* Plan options.  Zero means "default" for every field. */
+typedef struct {
+  int32_t n_cus;      /* workgroups = CUs used (default: all CUs of the device) */
+  int32_t mlp_chunks; /* MLP intermediate split into this many chunks, each with
+                         its own counter so down-projection tiles start early
+                         (default 4, as in the Llama-1B megakernel write-up,
+                         "Custom Synchronization Mechanism") */
+  int32_t attn_block; /* KV positions per attention tile (multiple of 64;
+                         default: chosen from max_seq and the CU count) */
+  int32_t watchdog_ms;/* counter-wait limit before MK_ERR_TIMEOUT (default 2000) */
+  int32_t debug_corrupt_target; /* tests only: 1 raises one wait target so the
+                                   step must end in MK_ERR_TIMEOUT */
+  int32_t reserved[3];
+} mk_plan_opts;
+
+/* Plan summary (filled by mk_plan_info / mk_plan_check). */
+typedef struct {
+  int32_t n_cus;           /* workgroups in the launch                    */
+  int32_t n_instr;         /* instructions over all queues                */
+  int32_t max_queue;       /* longest per-CU queue                        */
+  int32_t n_counters;      /* counters in use                             */
+  int32_t lds_bytes;       /* LDS per workgroup                           */
+  int32_t n_pages;         /* LDS weight pages per workgroup              */
+  int32_t page_bytes;      /* bytes per page                              */
+  int32_t attn_block;      /* KV positions per attention tile             */
+  int32_t attn_tiles;      /* attention tiles per layer                   */
+  int32_t mlp_chunks;
+  int64_t weight_bytes;    /* weight bytes streamed per step              */
+  int64_t max_cu_bytes;    /* largest per-CU streamed bytes (KV at max_seq)*/
+  int64_t min_cu_bytes;    /* smallest per-CU streamed bytes              */
+} mk_plan_summary;
+
+/* Create a context on `device` for this model and these caller-owned buffers.
+ * Validates the shape, allocates the arena and builds the RoPE tables.
+ * Errors: MK_ERR_INVALID_ARG (NULL/inconsistent arguments), MK_ERR_UNSUPPORTED
+ * (shape outside the kernel's code paths), MK_ERR_HIP, MK_ERR_OOM. */
+mk_status mk_create(const mk_config *cfg, const mk_weights *w, int device, mk_ctx **out);
+
+/* Build, verify and upload the per-CU instruction queues (host-side static
+ * scheduling: the Llama-1B write-up, javascript.cn article, section
+ * "Megakernel：从零设计的融合思路").  opts may be NULL (all defaults).  A plan
+ * that fails the verifier (counter targets, dependency order, page budgets,
+ * read coverage) is rejected with MK_ERR_INVALID_ARG. */
+mk_status mk_build_plan(mk_ctx *ctx, const mk_plan_opts *opts);
+
+/* Enqueue one decode step on `stream` (a hipStream_t; NULL = default stream).
+ *   d_tokens: device int32 [B], the input token of each sequence;
+ *   pos:      position of the new token (= cached positions), 0 <= pos < max_seq;
+ *   d_next:   device int32 [B], receives the greedy next token;
+ *   d_logits: device float [B, V] or NULL.
+ * Appends the new key/value rows at `pos` to the caller's caches.  Asynchronous:
+ * a watchdog timeout or device error surfaces from mk_sync (or the next call).
+ * d_tokens may alias d_next of the previous step (device-side chaining).
+ * Errors: MK_ERR_NO_PLAN, MK_ERR_INVALID_ARG, MK_ERR_HIP. */
+mk_status mk_decode_step(mk_ctx *ctx, const int32_t *d_tokens, int32_t pos,
+                         int32_t *d_next, float *d_logits, void *stream);
+
+/* Wait for the context's last step and read the device status word.
+ * Returns MK_ERR_TIMEOUT / MK_ERR_DEVICE with a message if the kernel reported
+ * one; the counters are then reset so the context can be used again. */
+mk_status mk_sync(mk_ctx *ctx);
+
+/* Destroy the context and free the arena.  NULL is accepted (MK_OK). */
+mk_status mk_destroy(mk_ctx *ctx);
+
+/* Message for the last error on ctx (or of the calling thread if ctx is NULL).
+ * The string is owned by the library and valid until the next call. */
+const char *mk_last_error(const mk_ctx *ctx);
+
+/* Summary of the context's current plan.  Errors: MK_ERR_NO_PLAN. */
+mk_status mk_plan_info(const mk_ctx *ctx, mk_plan_summary *out);
+
+/* Host-only planning for tests and tools: build and verify a plan for
+ * `n_cus` workgroups without a device or buffers.  Writes a text report
+ * (truncated to report_len, may be NULL) and the summary (may be NULL). */
+mk_status mk_plan_check(const mk_config *cfg, const mk_plan_opts *opts, int32_t n_cus,
+                        mk_plan_summary *summary, char *report, size_t report_len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

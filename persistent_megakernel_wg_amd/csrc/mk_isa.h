@@ -1,0 +1,140 @@
+// mk_isa.h — instruction records and launch arguments shared by the host
+// planner and the persistent megakernel.
+//
+// Every instruction follows one template, as in the Llama-1B megakernel
+// write-up (javascript.cn article, "Megakernel：从零设计的融合思路": each
+// instruction standardises load, compute and store): its weight (or KV) stream
+// is copied into LDS pages by the loader waves, its input dependencies are
+// counters in global memory, its compute waves read the pages, and its last
+// wave increments one counter when the outputs are visible.
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+// ---------------------------------------------------------------- constants
+constexpr int kNLoad = 2;            // loader waves per workgroup
+constexpr int kNComp = 6;            // compute waves per workgroup (2 waves per SIMD with the loaders)
+constexpr int kThreads = 64 * (kNLoad + kNComp);
+constexpr int kUnit = 1024;          // bytes per wave-wide 16 B/lane DMA
+constexpr int kPageBytes = 16384;    // LDS page (16 KiB, as on the pages' design)
+constexpr int kUnitsPerPage = kPageBytes / kUnit;
+constexpr int kPages = 8;            // pages in the LDS ring
+constexpr int kCtrStride = 32;       // u32 per counter (128 B apart)
+constexpr int kMaxK = 4096;          // largest GEMV input length
+constexpr int kDoneRing = 4;         // per-instruction completion counters
+
+// LDS layout (bytes)
+constexpr int kLdsCtrl = 0;          // control words
+constexpr int kLdsAcc = 1024;        // down-projection accumulators (256 floats)
+constexpr int kLdsX = 2048;          // staged input vector / q,k,v (16 KiB)
+constexpr int kLdsXBytes = 4 * kMaxK;
+constexpr int kLdsAttn = kLdsX + kLdsXBytes;   // attention scratch
+constexpr int kLdsAttnBytes = 12800;   // scores 8 KiB, new V row 512 B, partials 4 KiB
+constexpr int kLdsPages = kLdsAttn + kLdsAttnBytes;
+constexpr int kLdsTotal = kLdsPages + kPages * kPageBytes;   // 162304
+constexpr int kAttnScoreFloats = 2048;                       // 8 KiB of scores
+
+// ------------------------------------------------------------------- opcodes
+enum Op : uint8_t { OP_GEMV = 1, OP_ATTN = 2 };
+
+// GEMV epilogues
+enum Epi : uint8_t {
+  EPI_STORE = 0,      // out[r] = dot                        (q/k/v projection)
+  EPI_RESID = 1,      // out[r] = res[r] + dot               (O projection)
+  EPI_SWIGLU = 2,     // out[r] = silu(dot_gate) * dot_up    (gate/up pairs)
+  EPI_ACC_FIRST = 3,  // acc[r] = res[r] + dot               (down-proj chunk 0)
+  EPI_ACC_MID = 4,    // acc[r] += dot
+  EPI_ACC_LAST = 5,   // out[r] = acc[r] + dot               (last chunk)
+  EPI_ACC_ONLY = 6,   // out[r] = res[r] + dot  (single-chunk down projection)
+  EPI_ARGMAX = 7,     // logits + greedy argmax              (LM head)
+};
+
+// instruction flags
+enum Flag : uint16_t {
+  F_NORM = 1,         // RMSNorm the input vector with gain_ptr before the GEMV
+  F_IN_EMBED = 2,     // input vector is the bf16 embedding row of the token
+  F_RES_EMBED = 4,    // residual is the bf16 embedding row of the token
+  F_INTERLEAVE = 8,   // stream rows alternate between segments 0 and 1
+  F_SIGNAL = 16,      // increment sig_ctr when done
+  F_OWN_POS = 32,     // (attention) placeholder, decided at run time
+};
+
+constexpr uint32_t kNoCounter = 0xFFFFFFFFu;
+
+// One instruction.  Pointers are device addresses fixed at plan time.
+struct alignas(16) Instr {
+  uint8_t op;
+  uint8_t epi;
+  uint8_t nit;         // 1 KiB units per stream row (rows >= 1 KiB), else 1
+  uint8_t rpu;         // stream rows per 1 KiB unit (1, or 2 for 512 B rows)
+  uint16_t flags;
+  uint16_t layer;
+  uint32_t n_items;    // GEMV: output items; ATTN: unused
+  uint32_t row0;       // first output row
+  uint32_t page0;      // first page of this instruction in the CU's page stream
+  uint32_t n_pages;    // pages reserved for this instruction
+  uint32_t row_bytes;  // bytes per stream row
+  uint32_t n_rows;     // stream rows (all segments)
+  uint32_t k;          // GEMV input length (floats)
+  uint32_t wait_ctr[2];
+  uint32_t wait_cnt[2];  // producers per step (0 = no wait); target = epoch * cnt
+  uint32_t sig_ctr;
+  uint32_t aux[5];     // op-specific
+  uint64_t seg_ptr[3]; // stream segment base addresses
+  uint32_t seg_rows[3];
+  uint32_t seg_stride[3];
+  uint64_t in_ptr;     // input vector (fp32) or embedding table (bf16)
+  uint64_t res_ptr;    // residual (fp32) or embedding table (bf16)
+  uint64_t out_ptr;    // output
+  uint64_t gain_ptr;   // RMSNorm gain (bf16)
+};
+static_assert(sizeof(Instr) % 16 == 0, "Instr must stay 16 B aligned");
+
+// Attention instruction aux fields
+//   aux[0] = kv group g         aux[1] = block index b
+//   aux[2] = positions/block    aux[3] = blocks per group (1 = no merge)
+//   aux[4] = pages per K (and V) region
+//   seg_ptr[0] = K cache rows of (layer, seq, g) from position 0
+//   seg_ptr[1] = V cache rows of (layer, seq, g) from position 0
+//   in_ptr = q|k|v activations of the layer; out_ptr = attention output
+//   res_ptr = split partials of the layer; wait/sig as usual
+//   seg_rows[0] = merge-ticket counter (blocks > 1)
+// GEMV aux fields
+//   aux[0] = LDS accumulator offset (down projection)
+//   aux[1] = argmax slot index (LM head)
+//   aux[2] = LM-head ticket counter, aux[3] = LM-head tiles
+
+// Kernel launch arguments.
+struct KArgs {
+  const Instr* instrs;      // all queues back to back
+  const uint32_t* q_off;    // [n_cus + 1] queue offsets
+  uint32_t* counters;       // [n_ctr * kCtrStride]
+  uint32_t* status;         // [16] error record
+  const int32_t* tokens;    // [B]
+  int32_t* next;            // [B]
+  float* logits;            // [B, V] or null
+  const float* rope_cos;    // [max_seq][Dh/2]
+  const float* rope_sin;
+  float* lm_slots;          // [n_lm_tiles][2] (value, index)
+  const void* zero_page;    // 1 KiB of zeros (padding DMA source)
+  uint32_t epoch;           // 1-based step count since the counters were zeroed
+  int32_t pos;
+  int32_t vocab;
+  int32_t hidden;
+  int32_t head_dim;
+  int32_t hpg;              // query heads per KV group
+  int32_t q_dim;            // H * Dh (offset of k in the qkv buffer)
+  int32_t kv_dim;           // G * Dh
+  int32_t max_seq;
+  float rms_eps;
+  float attn_scale;         // 1/sqrt(Dh)
+  uint64_t watchdog_ticks;  // s_memrealtime ticks (100 MHz)
+};
+
+// status words
+enum StatusWord { ST_CODE = 0, ST_CU = 1, ST_INSTR = 2, ST_CTR = 3, ST_SEEN = 4, ST_TARGET = 5,
+                  ST_NAN = 6, ST_BADTOK = 7 };
+enum StatusCode { STC_OK = 0, STC_TIMEOUT = 1, STC_LOCAL_TIMEOUT = 2 };
+
+}  // namespace mk

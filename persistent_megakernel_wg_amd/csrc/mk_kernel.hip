@@ -1,0 +1,975 @@
+// mk_kernel.hip — the persistent decode megakernel for gfx950 (MI355X).
+//
+// One workgroup per CU interprets its queue of tile instructions (the on-GPU
+// interpreter of the Llama-1B megakernel write-up, rocketrecap.com summary,
+// "Fusing Operations with an On-GPU Interpreter"; Cohere's resident
+// one-block-per-SM task list, airebao.com «Megakernel 是什么»).
+//
+// Workgroup = 2 loader waves + 6 compute waves (512 threads, 1 WG/CU, two
+// waves per SIMD so each wave may hold up to 256 VGPRs).
+//  * Loader waves walk the queue ahead of the compute waves and copy each
+//    instruction's weight (or KV-cache) stream into a ring of 8 x 16 KiB LDS
+//    pages with global_load_lds_dwordx4 (the shared-memory paging of the
+//    write-up, "Efficient Shared Memory Management"; weights are immutable, so
+//    they are fetched before the activation dependency is met, as in Cohere's
+//    «三点关键差异» item 3 and «快在哪里» item 3).  Loaders never wait on
+//    global counters; they track their own DMA with vmcnt and publish each
+//    page through an LDS word.
+//  * Compute wave 0 (the leader) waits on the instruction's counters in global
+//    memory and stages the input vector (or q/k/v) into LDS; then all compute
+//    waves run the op from the LDS pages.  The last wave to finish an
+//    instruction increments its counter (the counter system of the write-up,
+//    "Custom Synchronization Mechanism").
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_isa.h"
+
+#define DEV __device__ __forceinline__
+
+#ifndef MK_SYNC_FENCED
+// 0: activations travel with device-coherent (sc1) loads/stores and counters
+//    are bumped after s_waitcnt vmcnt(0) — no L2 writeback/invalidate.
+// 1: plain loads/stores bracketed by agent-scope release/acquire fences.
+#define MK_SYNC_FENCED 0
+#endif
+
+namespace mk {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const Instr* InstrCP;
+
+extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+// Sub-dword header fields are read as whole dwords (scalar loads only move
+// dwords; a byte field would otherwise become a vector load, whose vmcnt would
+// disturb the loader's DMA accounting).
+typedef __attribute__((address_space(4))) const uint32_t* WordCP;
+DEV uint32_t hw0(InstrCP I) { return reinterpret_cast<WordCP>(I)[0]; }
+DEV uint32_t hw1(InstrCP I) { return reinterpret_cast<WordCP>(I)[1]; }
+DEV uint32_t i_op(InstrCP I) { return hw0(I) & 0xFFu; }
+DEV uint32_t i_epi(InstrCP I) { return (hw0(I) >> 8) & 0xFFu; }
+DEV uint32_t i_nit(InstrCP I) { return (hw0(I) >> 16) & 0xFFu; }
+DEV uint32_t i_rpu(InstrCP I) { return hw0(I) >> 24; }
+DEV uint32_t i_flags(InstrCP I) { return hw1(I) & 0xFFFFu; }
+
+// --------------------------------------------------------------- LDS control
+enum : int {
+  C_FILLED = 0,        // [kNLoad] pages published by each loader
+  C_RELEASED = 16,     // [kNComp] pages below this index are done, per wave
+  C_XOK = 64,          // instructions whose inputs are staged
+  C_XCONS = 96,        // [kNComp] instructions whose staged inputs each wave read
+  C_DONE = 128,        // [kDoneRing] waves finished, per instruction slot
+  C_ABORT = 160,
+  C_BAR = 176,
+  C_ARGV = 192,        // [kNComp] best value per wave
+  C_ARGI = 224,        // [kNComp] best index per wave
+  C_STATUS_LO = 256,   // status pointer (written once at kernel entry)
+  C_STATUS_HI = 260,
+  C_LIMIT_LO = 264,    // time limit of local waits, s_memrealtime ticks
+  C_LIMIT_HI = 268,
+  C_CTRL_END = 272,
+};
+static_assert(C_FILLED + 4 * kNLoad <= C_RELEASED, "ctrl layout");
+static_assert(C_RELEASED + 4 * kNComp <= C_XOK, "ctrl layout");
+static_assert(C_XCONS + 4 * kNComp <= C_DONE, "ctrl layout");
+static_assert(C_DONE + 4 * kDoneRing <= C_ABORT, "ctrl layout");
+
+DEV uint32_t* lw(int off) { return reinterpret_cast<uint32_t*>(lds + off); }
+DEV uint32_t lds_ld(int off) {
+  return __hip_atomic_load(lw(off), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+DEV void lds_st(int off, uint32_t v) {
+  __hip_atomic_store(lw(off), v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+DEV uint32_t lds_add(int off, uint32_t v) {
+  return __hip_atomic_fetch_add(lw(off), v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+DEV bool aborted() { return lds_ld(C_ABORT) != 0; }
+
+// The status pointer and the local time limit live in LDS so that wait loops
+// deep in the call tree can reach them.
+DEV uint32_t* status_ptr() {
+  return reinterpret_cast<uint32_t*>((uint64_t(*lw(C_STATUS_HI)) << 32) | *lw(C_STATUS_LO));
+}
+DEV uint64_t local_limit() { return (uint64_t(*lw(C_LIMIT_HI)) << 32) | *lw(C_LIMIT_LO); }
+DEV uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+DEV uint32_t page_off(uint32_t g) { return kLdsPages + (g & (kPages - 1)) * kPageBytes; }
+
+// ------------------------------------------------------ global memory access
+DEV void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+DEV uint32_t ctr_load(const uint32_t* p) {
+#if MK_SYNC_FENCED
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#endif
+}
+DEV uint32_t ctr_add(uint32_t* p) {
+#if MK_SYNC_FENCED
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  wait_vm0();
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#endif
+}
+// activation store / load (device-coherent)
+DEV void st_act(float* p, float v) {
+#if MK_SYNC_FENCED
+  *p = v;
+#else
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#endif
+}
+DEV float ld_act(const float* p) {
+#if MK_SYNC_FENCED
+  return *p;
+#else
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#endif
+}
+// 16-byte activation load through a buffer resource (sc1 = device scope)
+DEV __amdgpu_buffer_rsrc_t act_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+DEV f4 ld_act4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+#if MK_SYNC_FENCED
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#else
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16 /* sc1 */);
+#endif
+}
+
+DEV float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+DEV float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+DEV uint16_t f2bf(float f) {  // round to nearest even (no NaN inputs expected)
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+// input token, checked against the vocabulary (an out-of-range id is reported
+// and replaced by 0 so that no access leaves the embedding table)
+DEV uint32_t token0(const KArgs& a) {
+  const int32_t t = a.tokens[0];
+  if (t >= 0 && t < a.vocab) return uint32_t(t);
+  __hip_atomic_store(a.status + ST_BADTOK, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return 0;
+}
+DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+DEV float dot8(u4 w, const float* x) {
+  float a = bf_lo(w.x) * x[0];
+  a = fmaf(bf_hi(w.x), x[1], a);
+  float b = bf_lo(w.y) * x[2];
+  b = fmaf(bf_hi(w.y), x[3], b);
+  a = fmaf(bf_lo(w.z), x[4], a);
+  a = fmaf(bf_hi(w.z), x[5], a);
+  b = fmaf(bf_lo(w.w), x[6], b);
+  b = fmaf(bf_hi(w.w), x[7], b);
+  return a + b;
+}
+
+template <int LPR>
+DEV float reduce_lanes(float v) {
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+DEV float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// ----------------------------------------------------------------- watchdog
+DEV void record_timeout(const KArgs& a, int cu, uint32_t instr, uint32_t ctr, uint32_t seen,
+                        uint32_t target) {
+  uint32_t expected = 0;
+  if (__hip_atomic_compare_exchange_strong(a.status + ST_CODE, &expected, uint32_t(STC_TIMEOUT),
+                                           __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(a.status + ST_CU, uint32_t(cu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.status + ST_INSTR, instr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.status + ST_CTR, ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.status + ST_SEEN, seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.status + ST_TARGET, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Wait until counter >= target (wrap-safe).  false = watchdog or abort.
+DEV bool wait_counter(const KArgs& a, uint32_t ctr, uint32_t target, int cu, uint32_t instr) {
+  const uint32_t* p = a.counters + size_t(ctr) * kCtrStride;
+  uint64_t t0 = 0;
+  for (uint32_t it = 0;; it++) {
+    uint32_t v = uni(ctr_load(p));
+    if (int32_t(v - target) >= 0) return true;
+    uint64_t now = __builtin_amdgcn_s_memrealtime();
+    if (t0 == 0) t0 = now;
+    if (now - t0 > a.watchdog_ticks) {
+      record_timeout(a, cu, instr, ctr, v, target);
+      return false;
+    }
+    if ((it & 63) == 63 &&
+        __hip_atomic_load(a.status + ST_CODE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+      return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Time limit of waits inside the workgroup (pages, staged inputs, barriers).
+// They can only stall if the workgroup itself is stuck; the limit turns that
+// into an error instead of a hang.
+DEV bool local_timeout(uint64_t& t0, uint64_t limit) {
+  const uint64_t now = __builtin_amdgcn_s_memrealtime();
+  if (t0 == 0) t0 = now;
+  return now - t0 > limit;
+}
+DEV void local_abort(uint32_t code) {
+  uint32_t expected = 0;
+  __hip_atomic_compare_exchange_strong(status_ptr() + ST_CODE, &expected, code, __ATOMIC_RELAXED,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lds_st(C_ABORT, 1);
+}
+
+// Wait for an LDS word to reach `want` (or abort).
+DEV bool wait_lds_ge(int off, uint32_t want) {
+  uint64_t t0 = 0;
+  while (int32_t(lds_ld(off) - want) < 0) {
+    if (aborted()) return false;
+    if (local_timeout(t0, local_limit())) {
+      local_abort(STC_LOCAL_TIMEOUT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(0);
+  }
+  return true;
+}
+DEV uint32_t min_filled() {
+  uint32_t m = lds_ld(C_FILLED);
+#pragma unroll
+  for (int v = 1; v < kNLoad; v++) m = min(m, lds_ld(C_FILLED + 4 * v));
+  return m;
+}
+// Wait until page g is published by every loader.
+DEV bool wait_page(uint32_t g, uint32_t& cache) {
+  uint64_t t0 = 0;
+  while (cache <= g) {
+    cache = min_filled();
+    if (cache > g) break;
+    if (aborted()) return false;
+    if (local_timeout(t0, local_limit())) {
+      local_abort(STC_LOCAL_TIMEOUT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(0);
+  }
+  return true;
+}
+
+// Software barrier of the compute waves (monotonic count).
+DEV bool comp_barrier() {
+  uint32_t c = 0;
+  if ((threadIdx.x & 63) == 0) c = lds_add(C_BAR, 1) + 1;
+  c = uni(c);
+  const uint32_t target = ((c + kNComp - 1) / kNComp) * kNComp;
+  return wait_lds_ge(C_BAR, target);
+}
+
+// ================================================================== loader
+DEV void dma_uniform(uint32_t lds_addr, uint64_t src, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(src)
+      : "memory");
+}
+DEV void dma_lane(uint32_t lds_addr, uint64_t src) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(src)
+      : "memory");
+}
+
+constexpr uint32_t kDmaPerPage = kUnitsPerPage / kNLoad;  // 8
+constexpr uint32_t kMaxOut = 7;                           // pages in flight per loader
+
+// wait until at most `pages_after` pages of this loader's DMA are in flight
+DEV void wait_vm_pages(uint32_t pages_after) {
+  static_assert(kDmaPerPage == 8, "vmcnt table assumes 8 DMA per page");
+  switch (pages_after) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(40)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+struct LoaderState {
+  uint32_t g_issue, g_pub, min_rel;
+};
+
+DEV void publish_oldest(LoaderState& s, int v) {
+  wait_vm_pages(s.g_issue - s.g_pub - 1);
+  s.g_pub++;
+  if ((threadIdx.x & 63) == 0) lds_st(C_FILLED + 4 * v, s.g_pub);
+}
+
+DEV uint32_t min_released() {
+  uint32_t m = lds_ld(C_RELEASED);
+#pragma unroll
+  for (int w = 1; w < kNComp; w++) m = min(m, lds_ld(C_RELEASED + 4 * w));
+  return m;
+}
+
+// source address of stream row r (uniform)
+DEV uint64_t row_src(InstrCP I, uint32_t r, uint32_t interleave) {
+  if (interleave) {
+    const uint32_t s = r & 1, i = r >> 1;
+    return I->seg_ptr[s] + uint64_t(i) * I->seg_stride[s];
+  }
+  uint32_t r0 = I->seg_rows[0];
+  if (r < r0) return I->seg_ptr[0] + uint64_t(r) * I->seg_stride[0];
+  r -= r0;
+  uint32_t r1 = I->seg_rows[1];
+  if (r < r1) return I->seg_ptr[1] + uint64_t(r) * I->seg_stride[1];
+  r -= r1;
+  return I->seg_ptr[2] + uint64_t(r) * I->seg_stride[2];
+}
+
+// Issue this loader's share (units v, v + kNLoad, ...) of page p of instruction I.
+DEV void issue_page(const KArgs& a, InstrCP I, uint32_t p, uint32_t g, int v, uint32_t lane) {
+  const uint32_t ldsbase = uint32_t(size_t(lds)) + page_off(g);
+  const uint64_t zero = uint64_t(a.zero_page);
+  if (i_op(I) == OP_GEMV) {
+    const uint32_t nit = i_nit(I), rpu = i_rpu(I), rb = I->row_bytes;
+    const uint32_t stream_units = (I->n_rows * rb + kUnit - 1) / kUnit;
+    const uint32_t inter = i_flags(I) & F_INTERLEAVE;
+    for (uint32_t k = v; k < kUnitsPerPage; k += kNLoad) {
+      const uint32_t u = p * kUnitsPerPage + k;
+      const uint32_t dst = ldsbase + k * kUnit;
+      if (u >= stream_units) {
+        dma_uniform(dst, zero, lane * 16);
+      } else if (rpu == 1) {
+        const uint32_t r = u / nit, part = u - r * nit;
+        dma_uniform(dst, row_src(I, r, inter) + part * kUnit, lane * 16);
+      } else {
+        // 512 B rows: lanes 0-31 read row 2u, lanes 32-63 row 2u+1
+        const uint32_t r0 = 2 * u;
+        const uint64_t s0 = row_src(I, r0, inter), s1 = row_src(I, r0 + 1, inter);
+        const uint64_t src = (lane < 32 ? s0 : s1) + (lane & 31) * 16;
+        dma_lane(dst, src);
+      }
+    }
+  } else {  // OP_ATTN: K block region then V block region, rows < n_cached valid
+    const uint32_t kp = I->aux[4];
+    const int32_t p0 = int32_t(I->aux[1] * I->aux[2]);
+    int32_t nc = a.pos - p0;
+    nc = nc < 0 ? 0 : (nc > int32_t(I->aux[2]) ? int32_t(I->aux[2]) : nc);
+    const uint32_t valid_bytes = uint32_t(nc) * I->row_bytes;
+    const uint32_t region = p < kp ? 0 : 1;
+    const uint32_t pp = p - region * kp;
+    const uint64_t base = I->seg_ptr[region] + uint64_t(p0) * I->row_bytes;
+    for (uint32_t k = v; k < kUnitsPerPage; k += kNLoad) {
+      const uint32_t off = (pp * kUnitsPerPage + k) * kUnit;
+      const uint32_t dst = ldsbase + k * kUnit;
+      if (off + kUnit <= valid_bytes) {
+        dma_uniform(dst, base + off, lane * 16);
+      } else if (off >= valid_bytes) {
+        dma_uniform(dst, zero, lane * 16);
+      } else {
+        const uint32_t lo = off + lane * 16;
+        dma_lane(dst, lo < valid_bytes ? base + lo : zero + lane * 16);
+      }
+    }
+  }
+}
+
+DEV void loader(const KArgs& a, InstrCP q, uint32_t n, int v) {
+  const uint32_t lane = threadIdx.x & 63;
+  LoaderState s{0, 0, 0};
+  for (uint32_t i = 0; i < n; i++) {
+    InstrCP I = q + i;
+    const uint32_t np = I->n_pages, page0 = I->page0;
+    for (uint32_t p = 0; p < np; p++) {
+      const uint32_t g = page0 + p;
+      if (g - s.g_pub >= kMaxOut) publish_oldest(s, v);
+      uint64_t t0 = 0;
+      while (g >= s.min_rel + kPages) {
+        if (s.g_pub < g) {
+          publish_oldest(s, v);
+          continue;
+        }
+        s.min_rel = uni(min_released());
+        if (g < s.min_rel + kPages) break;
+        if (aborted() || local_timeout(t0, local_limit())) {
+          if (!aborted()) local_abort(STC_LOCAL_TIMEOUT);
+          wait_vm0();
+          return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      issue_page(a, I, p, g, v, lane);
+      s.g_issue = g + 1;
+    }
+  }
+  while (s.g_pub < s.g_issue) publish_oldest(s, v);
+  wait_vm0();
+}
+
+// ================================================================ compute
+struct Comp {
+  const KArgs* a;
+  int cu;
+  int w;          // compute wave index
+  uint32_t lane;
+  uint32_t fcache;  // cached min published page
+};
+
+// ---- GEMV epilogue for one output row
+struct ArgBest {
+  float v;
+  uint32_t i;
+};
+DEV void arg_update(ArgBest& b, float v, uint32_t i) {
+  if (v > b.v || (v == b.v && i < b.i)) {
+    b.v = v;
+    b.i = i;
+  }
+}
+
+DEV void epi_row(Comp& c, InstrCP I, uint32_t t_row, uint32_t row, float v, ArgBest& best) {
+  const KArgs& a = *c.a;
+  float* out = reinterpret_cast<float*>(I->out_ptr);
+  switch (i_epi(I)) {
+    case EPI_STORE:
+    case EPI_SWIGLU:
+      st_act(out + row, v);
+      break;
+    case EPI_RESID:
+    case EPI_ACC_ONLY: {
+      float r;
+      if (i_flags(I) & F_RES_EMBED) {
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(I->res_ptr) +
+                            size_t(token0(a)) * a.hidden;
+        r = __uint_as_float(uint32_t(e[row]) << 16);
+      } else {
+        r = ld_act(reinterpret_cast<const float*>(I->res_ptr) + row);
+      }
+      st_act(out + row, r + v);
+      break;
+    }
+    case EPI_ACC_FIRST: {
+      float r = ld_act(reinterpret_cast<const float*>(I->res_ptr) + row);
+      reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] = r + v;
+      break;
+    }
+    case EPI_ACC_MID:
+      reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] += v;
+      break;
+    case EPI_ACC_LAST:
+      st_act(out + row, reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] + v);
+      break;
+    case EPI_ARGMAX:
+      if (a.logits) a.logits[row] = v;
+      if (v != v) __hip_atomic_store(a.status + ST_NAN, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      arg_update(best, v, row);
+      break;
+  }
+}
+
+template <int NIT, int RPU>
+DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
+  constexpr int LPR = 64 / RPU;
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane;
+  const float* xs = reinterpret_cast<const float*>(lds + kLdsX);
+  float xv[NIT][8];
+#pragma unroll
+  for (int j = 0; j < NIT; j++) {
+    const uint32_t col = RPU == 1 ? j * 512 + lane * 8 : (lane % LPR) * 8;
+    const f4 lo = *reinterpret_cast<const f4*>(xs + col);
+    const f4 hi = *reinterpret_cast<const f4*>(xs + col + 4);
+    xv[j][0] = lo.x; xv[j][1] = lo.y; xv[j][2] = lo.z; xv[j][3] = lo.w;
+    xv[j][4] = hi.x; xv[j][5] = hi.y; xv[j][6] = hi.z; xv[j][7] = hi.w;
+  }
+  if (i_flags(I) & F_NORM) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NIT; j++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) ss = fmaf(xv[j][e], xv[j][e], ss);
+    ss = reduce_lanes<LPR>(ss);
+    const float inv = rsqrtf(ss / float(I->k) + a.rms_eps);
+    const uint16_t* gain = reinterpret_cast<const uint16_t*>(I->gain_ptr);
+#pragma unroll
+    for (int j = 0; j < NIT; j++) {
+      const uint32_t col = RPU == 1 ? j * 512 + lane * 8 : (lane % LPR) * 8;
+      const u4 gv = *reinterpret_cast<const u4*>(gain + col);
+      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        xv[j][2 * e] *= inv * bf_lo(gw[e]);
+        xv[j][2 * e + 1] *= inv * bf_hi(gw[e]);
+      }
+    }
+  }
+  if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
+
+  const uint32_t n_items = I->n_items, page0 = I->page0;
+  const bool pair = i_epi(I) == EPI_SWIGLU;
+  const uint32_t upi = RPU == 1 ? (pair ? 2 * NIT : NIT) : 1;
+  ArgBest best{-__builtin_inff(), 0xFFFFFFFFu};
+  for (uint32_t t = c.w; t < n_items; t += kNComp) {
+    const uint32_t u0 = t * upi;
+    if (lane == 0) lds_st(C_RELEASED + 4 * c.w, page0 + u0 / kUnitsPerPage);
+    if (!wait_page(page0 + (u0 + upi - 1) / kUnitsPerPage, c.fcache)) return false;
+    float acc0 = 0.f, acc1 = 0.f;
+    if (RPU == 1) {
+      // gate (or only) row, then the up row of a pair: one row of loads live at a time
+      for (int r = 0; r < (pair ? 2 : 1); r++) {
+        u4 wr[NIT];
+#pragma unroll
+        for (int j = 0; j < NIT; j++) {
+          const uint32_t u = u0 + r * NIT + j;
+          wr[j] = *reinterpret_cast<const u4*>(lds + page_off(page0 + u / kUnitsPerPage) +
+                                               (u % kUnitsPerPage) * kUnit + lane * 16);
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < NIT; j++) acc += dot8(wr[j], xv[j]);
+        if (r == 0) acc0 = acc; else acc1 = acc;
+      }
+      acc0 = reduce_lanes<64>(acc0);
+      if (pair) acc1 = reduce_lanes<64>(acc1);
+      if (lane == 0) epi_row(c, I, t, I->row0 + t, pair ? silu(acc0) * acc1 : acc0, best);
+    } else {
+      const u4 wa = *reinterpret_cast<const u4*>(lds + page_off(page0 + u0 / kUnitsPerPage) +
+                                                 (u0 % kUnitsPerPage) * kUnit + lane * 16);
+      acc0 = reduce_lanes<LPR>(dot8(wa, xv[0]));
+      if (pair) {
+        const float up = __shfl(acc0, 32, 64);
+        if (lane == 0) epi_row(c, I, t, I->row0 + t, silu(acc0) * up, best);
+      } else if ((lane & 31) == 0) {
+        const uint32_t tr = 2 * t + (lane >> 5);
+        epi_row(c, I, tr, I->row0 + tr, acc0, best);
+      }
+    }
+  }
+  if (i_epi(I) == EPI_ARGMAX) {
+    // combine lanes 0 and 32 (512 B rows) and publish the wave's best
+    float ov = __shfl(best.v, 32, 64);
+    uint32_t oi = __shfl(best.i, 32, 64);
+    if (RPU == 2) arg_update(best, ov, oi);
+    if (lane == 0) {
+      *lw(C_ARGV + 4 * c.w) = __float_as_uint(best.v);
+      *lw(C_ARGI + 4 * c.w) = best.i;
+    }
+  }
+  if (lane == 0) lds_st(C_RELEASED + 4 * c.w, page0 + I->n_pages);
+  return true;
+}
+
+// ---- attention: one KV group, one position block
+// x slot holds raw q [HPG*Dh] | k [Dh] | v [Dh] of the group (staged by the leader).
+template <int HPG, int DH>
+DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane;
+  constexpr int LPRA = DH / 8;          // lanes per cached row (8 dims per lane)
+  constexpr int UPOS = kUnit / (2 * DH);  // rows per 1 KiB unit
+  constexpr int HALF = DH / 2;
+  const uint32_t g = I->aux[0], blk = I->aux[1], Bat = I->aux[2], nblk = I->aux[3], kp = I->aux[4];
+  const int32_t P = a.pos;
+  const int32_t p0 = int32_t(blk * Bat);
+  int32_t nc = P - p0;
+  nc = nc < 0 ? 0 : (nc > int32_t(Bat) ? int32_t(Bat) : nc);
+  const bool own = P >= p0 && P < p0 + int32_t(Bat);
+  const int32_t ntot = nc + (own ? 1 : 0);
+  const float* xs = reinterpret_cast<const float*>(lds + kLdsX);
+  float* scores = reinterpret_cast<float*>(lds + kLdsAttn);
+  uint16_t* newv = reinterpret_cast<uint16_t*>(lds + kLdsAttn + 8192);
+  float* parts = reinterpret_cast<float*>(lds + kLdsAttn + 8192 + 512);
+  const uint32_t s = lane % LPRA;        // dims [8s, 8s+8)
+  const uint32_t jrow = lane / LPRA;     // row within a unit
+  const float* cs = a.rope_cos + size_t(P) * HALF;
+  const float* sn = a.rope_sin + size_t(P) * HALF;
+
+  // rotated, scaled query slices of every head of the group
+  auto rot = [&](const float* vec, int d) {  // rotated component d of vec
+    if (d < HALF) return vec[d] * cs[d] - vec[d + HALF] * sn[d];
+    return vec[d] * cs[d - HALF] + vec[d - HALF] * sn[d - HALF];
+  };
+  float qr[HPG][8];
+#pragma unroll
+  for (int h = 0; h < HPG; h++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) qr[h][e] = rot(xs + h * DH, 8 * s + e) * a.attn_scale;
+  // the new key/value row, rounded to bf16
+  float kn[8];
+  uint16_t kb[8], vb[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    kb[e] = f2bf(rot(xs + HPG * DH, 8 * s + e));
+    kn[e] = __uint_as_float(uint32_t(kb[e]) << 16);
+    vb[e] = f2bf(xs[HPG * DH + DH + 8 * s + e]);
+  }
+  if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
+
+  // pass 1: scores of cached rows (units round-robin over the compute waves)
+  const uint32_t n_units = (uint32_t(nc) + UPOS - 1) / UPOS;
+  for (uint32_t u = c.w; u < n_units; u += kNComp) {
+    if (!wait_page(I->page0 + u / kUnitsPerPage, c.fcache)) return false;
+    const u4 kw = *reinterpret_cast<const u4*>(lds + page_off(I->page0 + u / kUnitsPerPage) +
+                                               (u % kUnitsPerPage) * kUnit + lane * 16);
+    const uint32_t p = u * UPOS + jrow;
+#pragma unroll
+    for (int h = 0; h < HPG; h++) {
+      const float d = reduce_lanes<LPRA>(dot8(kw, qr[h]));
+      if (s == 0 && p < uint32_t(nc)) scores[h * Bat + p] = d;
+    }
+  }
+  if (c.w == 0 && own) {
+    // score of the new row; append it to the cache
+#pragma unroll
+    for (int h = 0; h < HPG; h++) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e++) d = fmaf(qr[h][e], kn[e], d);
+      d = reduce_lanes<LPRA>(d);
+      if (lane == 0) scores[h * Bat + nc] = d;
+    }
+    if (lane < uint32_t(LPRA)) {
+      const size_t row = size_t(P) * DH + 8 * s;
+      uint16_t* kc = reinterpret_cast<uint16_t*>(I->seg_ptr[0]) + row;
+      uint16_t* vc = reinterpret_cast<uint16_t*>(I->seg_ptr[1]) + row;
+      u4 kk, vv;
+      kk.x = kb[0] | uint32_t(kb[1]) << 16; kk.y = kb[2] | uint32_t(kb[3]) << 16;
+      kk.z = kb[4] | uint32_t(kb[5]) << 16; kk.w = kb[6] | uint32_t(kb[7]) << 16;
+      vv.x = vb[0] | uint32_t(vb[1]) << 16; vv.y = vb[2] | uint32_t(vb[3]) << 16;
+      vv.z = vb[4] | uint32_t(vb[5]) << 16; vv.w = vb[6] | uint32_t(vb[7]) << 16;
+      *reinterpret_cast<u4*>(kc) = kk;
+      *reinterpret_cast<u4*>(vc) = vv;
+#pragma unroll
+      for (int e = 0; e < 8; e++) newv[8 * s + e] = vb[e];
+    }
+  }
+  if (!comp_barrier()) return false;
+
+  // pass 2: softmax statistics per head (every wave, redundantly)
+  float mh[HPG], lh[HPG];
+#pragma unroll
+  for (int h = 0; h < HPG; h++) {
+    float m = -__builtin_inff();
+    for (int32_t p = lane; p < ntot; p += 64) m = fmaxf(m, scores[h * Bat + p]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int32_t p = lane; p < ntot; p += 64) l += __expf(scores[h * Bat + p] - m);
+    l = reduce_lanes<64>(l);
+    mh[h] = m;
+    lh[h] = l;
+  }
+
+  // pass 3: o~ = sum_p e_p V_p, lanes own (head, dim pair), positions split
+  constexpr int T = HPG * HALF;              // tasks
+  constexpr int NL = 64 * kNComp;
+  constexpr int S = NL / T > 0 ? NL / T : 1;  // position splits
+  static_assert(T <= NL, "too many attention tasks");
+  const uint32_t L = c.w * 64 + lane;
+  const uint32_t task = L % T, split = L / T;
+  const uint32_t h = task / HALF, dp = task % HALF;
+  float m_sel = mh[0];
+#pragma unroll
+  for (int hh = 1; hh < HPG; hh++)
+    if (h == uint32_t(hh)) m_sel = mh[hh];
+  float o0 = 0.f, o1 = 0.f;
+  if (kp && !wait_page(I->page0 + 2 * kp - 1, c.fcache)) return false;
+  if (split < uint32_t(S)) {
+    for (int32_t p = split; p < ntot; p += S) {
+      const float e = __expf(scores[h * Bat + p] - m_sel);
+      uint32_t vw;
+      if (p < nc) {
+        const uint32_t off = uint32_t(p) * (2 * DH) + 4 * dp;
+        vw = *reinterpret_cast<const uint32_t*>(lds + page_off(I->page0 + kp + off / kPageBytes) +
+                                                (off % kPageBytes));
+      } else {
+        vw = *reinterpret_cast<const uint32_t*>(newv + 2 * dp);
+      }
+      o0 = fmaf(e, bf_lo(vw), o0);
+      o1 = fmaf(e, bf_hi(vw), o1);
+    }
+    parts[2 * L] = o0;
+    parts[2 * L + 1] = o1;
+  }
+  if (lane == 0) lds_st(C_RELEASED + 4 * c.w, I->page0 + I->n_pages);
+  if (!comp_barrier()) return false;
+
+  // final: sum the splits in order
+  if (L < uint32_t(T)) {
+    float s0 = 0.f, s1 = 0.f;
+    for (int sp = 0; sp < S; sp++) {
+      s0 += parts[2 * (sp * T + L)];
+      s1 += parts[2 * (sp * T + L) + 1];
+    }
+    float l_sel = lh[0];
+#pragma unroll
+    for (int hh = 1; hh < HPG; hh++)
+      if (h == uint32_t(hh)) l_sel = lh[hh];
+    const uint32_t head = g * HPG + h;
+    if (nblk == 1) {
+      float* out = reinterpret_cast<float*>(I->out_ptr) + head * DH + 2 * dp;
+      st_act(out, s0 / l_sel);
+      st_act(out + 1, s1 / l_sel);
+    } else {
+      // partial record [HPG][DH + 2] of (group, block): o~ | m | l
+      float* part = reinterpret_cast<float*>(I->res_ptr) +
+                    (size_t(g) * nblk + blk) * (HPG * (DH + 2)) + h * (DH + 2);
+      st_act(part + 2 * dp, s0);
+      st_act(part + 2 * dp + 1, s1);
+      if (dp == 0) {
+        st_act(part + DH, m_sel);
+        st_act(part + DH + 1, l_sel);
+      }
+    }
+  }
+  return true;
+}
+
+// Last-arriving tile of a group merges the block partials (log-sum-exp).
+template <int HPG, int DH>
+DEV void attn_merge(Comp& c, InstrCP I) {
+  const uint32_t g = I->aux[0], nblk = I->aux[3];
+  const float* part = reinterpret_cast<const float*>(I->res_ptr) + size_t(g) * nblk * (HPG * (DH + 2));
+  constexpr int PER = HPG * DH / 64;  // outputs per lane
+  for (int k = 0; k < PER; k++) {
+    const uint32_t o = k * 64 + c.lane;
+    const uint32_t h = o / DH, d = o % DH;
+    float M = -__builtin_inff();
+    for (uint32_t b = 0; b < nblk; b++) M = fmaxf(M, ld_act(part + b * (HPG * (DH + 2)) + h * (DH + 2) + DH));
+    float num = 0.f, den = 0.f;
+    for (uint32_t b = 0; b < nblk; b++) {
+      const float* rec = part + b * (HPG * (DH + 2)) + h * (DH + 2);
+      const float mb = ld_act(rec + DH);
+      const float wgt = mb == -__builtin_inff() ? 0.f : __expf(mb - M);
+      num = fmaf(wgt, ld_act(rec + d), num);
+      den = fmaf(wgt, ld_act(rec + DH + 1), den);
+    }
+    st_act(reinterpret_cast<float*>(I->out_ptr) + (g * HPG + h) * DH + d, num / den);
+  }
+}
+
+// ---- staging of the instruction's inputs into the LDS x slot (leader wave)
+DEV void stage_inputs(Comp& c, InstrCP I) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane;
+  float* xs = reinterpret_cast<float*>(lds + kLdsX);
+  if (i_op(I) == OP_GEMV) {
+    const uint32_t K = I->k;
+    if (i_flags(I) & F_IN_EMBED) {
+      const uint16_t* e = reinterpret_cast<const uint16_t*>(I->in_ptr) + size_t(token0(a)) * K;
+      for (uint32_t o = lane * 8; o < K; o += 512) {
+        const u4 v = *reinterpret_cast<const u4*>(e + o);
+        f4 lo = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y)};
+        f4 hi = {bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+        *reinterpret_cast<f4*>(xs + o) = lo;
+        *reinterpret_cast<f4*>(xs + o + 4) = hi;
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t r = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), K * 4);
+      for (uint32_t o = lane * 4; o < K; o += 256) *reinterpret_cast<f4*>(xs + o) = ld_act4(r, o * 4);
+    }
+  } else {
+    const int hpg = a.hpg, dh = a.head_dim;
+    const uint32_t g = I->aux[0];
+    const float* qkv = reinterpret_cast<const float*>(I->in_ptr);
+    const uint32_t nq = hpg * dh;
+    const __amdgpu_buffer_rsrc_t rq = act_rsrc(qkv + g * nq, nq * 4);
+    for (uint32_t o = lane * 4; o < nq; o += 256) *reinterpret_cast<f4*>(xs + o) = ld_act4(rq, o * 4);
+    const __amdgpu_buffer_rsrc_t rk = act_rsrc(qkv + a.q_dim + g * dh, dh * 4);
+    const __amdgpu_buffer_rsrc_t rv = act_rsrc(qkv + a.q_dim + a.kv_dim + g * dh, dh * 4);
+    for (uint32_t o = lane * 4; o < uint32_t(dh); o += 256) {
+      *reinterpret_cast<f4*>(xs + nq + o) = ld_act4(rk, o * 4);
+      *reinterpret_cast<f4*>(xs + nq + dh + o) = ld_act4(rv, o * 4);
+    }
+  }
+}
+
+DEV bool run_gemv(Comp& c, InstrCP I, uint32_t i) {
+  if (i_rpu(I) == 2) return gemv<1, 2>(c, I, i);
+  switch (i_nit(I)) {
+    case 1: return gemv<1, 1>(c, I, i);
+    case 2: return gemv<2, 1>(c, I, i);
+    case 3: return gemv<3, 1>(c, I, i);
+    case 4: return gemv<4, 1>(c, I, i);
+    case 5: return gemv<5, 1>(c, I, i);
+    case 6: return gemv<6, 1>(c, I, i);
+    case 7: return gemv<7, 1>(c, I, i);
+    default: return gemv<8, 1>(c, I, i);
+  }
+}
+
+DEV bool run_attn(Comp& c, InstrCP I, uint32_t i) {
+  const int hpg = c.a->hpg, dh = c.a->head_dim;
+  if (dh == 64) {
+    switch (hpg) {
+      case 1: return attn<1, 64>(c, I, i);
+      case 2: return attn<2, 64>(c, I, i);
+      case 4: return attn<4, 64>(c, I, i);
+      default: return attn<8, 64>(c, I, i);
+    }
+  }
+  switch (hpg) {
+    case 1: return attn<1, 128>(c, I, i);
+    case 2: return attn<2, 128>(c, I, i);
+    default: return attn<4, 128>(c, I, i);
+  }
+}
+
+DEV void run_merge(Comp& c, InstrCP I) {
+  const int hpg = c.a->hpg, dh = c.a->head_dim;
+  if (dh == 64) {
+    switch (hpg) {
+      case 1: return attn_merge<1, 64>(c, I);
+      case 2: return attn_merge<2, 64>(c, I);
+      case 4: return attn_merge<4, 64>(c, I);
+      default: return attn_merge<8, 64>(c, I);
+    }
+  }
+  switch (hpg) {
+    case 1: return attn_merge<1, 128>(c, I);
+    case 2: return attn_merge<2, 128>(c, I);
+    default: return attn_merge<4, 128>(c, I);
+  }
+}
+
+// LM head: combine the per-wave bests, publish the CU's slot, take a ticket;
+// the last CU reduces all slots (lowest index wins ties) and writes the token.
+DEV void lm_finish(Comp& c, InstrCP I) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane;
+  ArgBest b{-__builtin_inff(), 0xFFFFFFFFu};
+  for (int w = 0; w < kNComp; w++) arg_update(b, __uint_as_float(*lw(C_ARGV + 4 * w)), *lw(C_ARGI + 4 * w));
+  const uint32_t tile = I->aux[1], n_tiles = I->aux[3];
+  if (lane == 0) {
+    st_act(a.lm_slots + 2 * tile, b.v);
+    st_act(a.lm_slots + 2 * tile + 1, __uint_as_float(b.i));
+  }
+  uint32_t old = 0;
+  if (lane == 0) old = ctr_add(a.counters + size_t(I->sig_ctr) * kCtrStride);
+  old = uni(old);
+  if (old + 1 != a.epoch * n_tiles) return;
+  ArgBest all{-__builtin_inff(), 0xFFFFFFFFu};
+  for (uint32_t t = lane; t < n_tiles; t += 64)
+    arg_update(all, ld_act(a.lm_slots + 2 * t), __float_as_uint(ld_act(a.lm_slots + 2 * t + 1)));
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const float ov = __shfl_xor(all.v, m, 64);
+    const uint32_t oi = __shfl_xor(all.i, m, 64);
+    arg_update(all, ov, oi);
+  }
+  if (lane == 0) a.next[0] = int32_t(all.i);
+}
+
+DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
+  Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0};
+  for (uint32_t i = 0; i < n; i++) {
+    InstrCP I = q + i;
+    if (w == 0) {
+      bool ok = true;
+      for (int k = 0; k < 2 && ok; k++)
+        if (I->wait_cnt[k]) ok = wait_counter(a, I->wait_ctr[k], a.epoch * I->wait_cnt[k], cu, i);
+#if MK_SYNC_FENCED
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#endif
+      // every compute wave has read the previous instruction's staged inputs
+      for (int v = 0; v < kNComp && ok; v++) ok = wait_lds_ge(C_XCONS + 4 * v, i);
+      if (!ok) {
+        if (c.lane == 0) lds_st(C_ABORT, 1);
+        return;
+      }
+      stage_inputs(c, I);
+      if (c.lane == 0) lds_st(C_XOK, i + 1);
+    } else if (!wait_lds_ge(C_XOK, i + 1)) {
+      return;
+    }
+    bool ok = i_op(I) == OP_GEMV ? run_gemv(c, I, i) : run_attn(c, I, i);
+    if (!ok) return;
+    // completion: the last wave signals
+    wait_vm0();
+    uint32_t prev = 0;
+    if (c.lane == 0) prev = lds_add(C_DONE + 4 * (i % kDoneRing), 1);
+    prev = uni(prev);
+    if (prev != kNComp - 1) continue;
+    if (c.lane == 0) lds_st(C_DONE + 4 * (i % kDoneRing), 0);
+    if (i_op(I) == OP_GEMV && i_epi(I) == EPI_ARGMAX) {
+      lm_finish(c, I);
+      continue;
+    }
+    if (i_op(I) == OP_ATTN && I->aux[3] > 1) {
+      uint32_t old = 0;
+      if (c.lane == 0) old = ctr_add(a.counters + size_t(I->seg_rows[0]) * kCtrStride);
+      old = uni(old);
+      if (old + 1 != a.epoch * I->aux[3]) continue;
+      run_merge(c, I);
+      wait_vm0();
+    }
+    if ((i_flags(I) & F_SIGNAL) && c.lane == 0) ctr_add(a.counters + size_t(I->sig_ctr) * kCtrStride);
+  }
+}
+
+extern "C" __global__ __launch_bounds__(kThreads, 1) void mk_megakernel(KArgs a) {
+  for (int o = threadIdx.x * 4; o < C_CTRL_END; o += kThreads * 4) *lw(o) = 0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    *lw(C_STATUS_LO) = uint32_t(uint64_t(a.status));
+    *lw(C_STATUS_HI) = uint32_t(uint64_t(a.status) >> 32);
+    *lw(C_LIMIT_LO) = uint32_t(a.watchdog_ticks);
+    *lw(C_LIMIT_HI) = uint32_t(a.watchdog_ticks >> 32);
+  }
+  __syncthreads();
+  const int cu = blockIdx.x;
+  const uint32_t beg = a.q_off[cu], end = a.q_off[cu + 1];
+  InstrCP q = (InstrCP)(a.instrs + beg);
+  const int wave = int(uni(threadIdx.x >> 6));
+  if (wave < kNLoad)
+    loader(a, q, end - beg, wave);
+  else
+    compute(a, q, end - beg, wave - kNLoad, cu);
+}
+
+}  // namespace mk
+
+// Launch entry used by the runtime (not part of the public ABI).
+extern "C" hipError_t mk_launch_megakernel(const mk::KArgs* args, int n_cus, hipStream_t stream,
+                                           int cooperative) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mk::mk_megakernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, mk::kLdsTotal);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  mk::KArgs a = *args;
+  void* params[] = {&a};
+  if (cooperative)
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mk::mk_megakernel), dim3(n_cus),
+                                      dim3(mk::kThreads), params, mk::kLdsTotal, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&mk::mk_megakernel), dim3(n_cus),
+                         dim3(mk::kThreads), params, mk::kLdsTotal, stream);
+}

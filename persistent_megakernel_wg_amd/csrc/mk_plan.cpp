@@ -1,0 +1,911 @@
+// mk_plan.cpp — host planner and plan verifier (pure C++).
+//
+// Stages per layer (each cut into tiles, one tile per CU where possible):
+//   QKV   rows of [Wq; Wk; Wv] . RMSNorm(x_l)               -> qkv_l
+//   ATTN  per KV group (and position block): RoPE, KV append, GQA attention
+//   O     rows of Wo . o_l + x_l                            -> h_l
+//   GU c  pairs of (gate, up) rows of MLP chunk c, SwiGLU    -> m_l[chunk c]
+//   DOWN  rows of Wd, one instruction per chunk, accumulated -> x_{l+1}
+// then the LM head with a tile argmax and a last-arriver reduction.
+//
+// The MLP intermediate is split into chunks with their own counters so that
+// down-projection tiles can start early (Llama-1B megakernel write-up,
+// rocketrecap.com summary, "Custom Synchronization Mechanism": four chunks).
+// Attention and its consumers are synchronised through counters in global
+// memory (same section; Cohere's write-up, «Megakernel 是什么»).
+#include "mk_plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <random>
+#include <sstream>
+
+namespace mk {
+namespace {
+
+enum Buf { BUF_EMBED = 0, BUF_X, BUF_QKV, BUF_O, BUF_H, BUF_M, BUF_LOGITS, BUF_COUNT };
+const char* kBufName[] = {"embed", "x", "qkv", "o", "h", "m", "logits"};
+enum LStage { ST_QKV = 0, ST_ATTN = 1, ST_O = 2, ST_GU = 3, ST_DOWN = 4, ST_PER_LAYER = 8 };
+
+uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+struct Geo {
+  int nit = 0, rpu = 0;
+};
+
+// Row geometry for a GEMV whose rows hold K bf16 values.
+bool geo_for_k(int K, Geo* g) {
+  int rb = 2 * K;
+  if (rb >= kUnit && rb % kUnit == 0 && rb / kUnit <= 8) {
+    g->nit = rb / kUnit;
+    g->rpu = 1;
+    return true;
+  }
+  if (rb == kUnit / 2) {
+    g->nit = 1;
+    g->rpu = 2;
+    return true;
+  }
+  return false;
+}
+
+int ceil_div(int64_t a, int64_t b) { return int((a + b - 1) / b); }
+
+struct Builder {
+  const PlanInput& in;
+  Plan* P;
+  std::vector<std::vector<Instr>> q;
+  std::vector<std::vector<InstrMeta>> qm;
+  std::vector<uint32_t> page_cursor;
+  std::vector<int64_t> cu_bytes;
+  explicit Builder(const PlanInput& i, Plan* p) : in(i), P(p) {
+    q.resize(i.n_cus);
+    qm.resize(i.n_cus);
+    page_cursor.assign(i.n_cus, 0);
+    cu_bytes.assign(i.n_cus, 0);
+  }
+  uint32_t new_counter(int stage) {
+    P->ctr_stage.push_back(stage);
+    P->ctr_producers.push_back(0);
+    return uint32_t(P->ctr_stage.size() - 1);
+  }
+  void push(int cu, Instr ins, InstrMeta m, int64_t stream_bytes) {
+    ins.page0 = page_cursor[cu];
+    page_cursor[cu] += ins.n_pages;
+    cu_bytes[cu] += stream_bytes;
+    m.cu = cu;
+    q[cu].push_back(ins);
+    qm[cu].push_back(std::move(m));
+  }
+};
+
+Instr blank() {
+  Instr i;
+  std::memset(&i, 0, sizeof(i));
+  i.sig_ctr = kNoCounter;
+  i.wait_ctr[0] = i.wait_ctr[1] = kNoCounter;
+  return i;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ config
+mk_status check_config(const mk_config& c, std::string* err) {
+  auto bad = [&](const char* m) {
+    *err = m;
+    return MK_ERR_INVALID_ARG;
+  };
+  if (c.n_layers <= 0 || c.hidden <= 0 || c.n_q_heads <= 0 || c.n_kv_heads <= 0 ||
+      c.head_dim <= 0 || c.vocab <= 0 || c.max_seq <= 0 || c.batch <= 0)
+    return bad("config: every dimension must be positive");
+  if (c.n_q_heads % c.n_kv_heads) return bad("config: n_q_heads must be a multiple of n_kv_heads");
+  if (!(c.rms_eps > 0.f) || !(c.rope_theta > 1.f)) return bad("config: rms_eps > 0 and rope_theta > 1 required");
+  if (c.n_experts || c.parallel_block || c.batch != 1) {
+    *err = "config: MoE / parallel-block / batch > 1 decoders are not built in this library version";
+    return MK_ERR_UNSUPPORTED;
+  }
+  if (c.ffn <= 0) return bad("config: ffn must be positive");
+  if (c.n_layers > 128) {
+    *err = "config: at most 128 layers";
+    return MK_ERR_UNSUPPORTED;
+  }
+  if (c.head_dim != 64 && c.head_dim != 128) {
+    *err = "config: head_dim must be 64 or 128";
+    return MK_ERR_UNSUPPORTED;
+  }
+  const int q = c.n_q_heads * c.head_dim;
+  Geo g;
+  if (!geo_for_k(c.hidden, &g) || !geo_for_k(q, &g) || c.hidden > kMaxK || q > kMaxK) {
+    *err = "config: hidden and n_q_heads*head_dim must be 256 or a multiple of 512 up to 4096";
+    return MK_ERR_UNSUPPORTED;
+  }
+  const int hpg = c.n_q_heads / c.n_kv_heads;
+  if (hpg * c.head_dim > 1024) {
+    *err = "config: at most 1024 query values per KV group";
+    return MK_ERR_UNSUPPORTED;
+  }
+  if ((hpg + 2) * c.head_dim * 4 > kLdsXBytes) {
+    *err = "config: q/k/v of one KV group exceed the staging buffer";
+    return MK_ERR_UNSUPPORTED;
+  }
+  if (c.vocab % 2 || c.hidden % 2) return bad("config: vocab and hidden must be even");
+  return MK_OK;
+}
+
+mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) {
+  mk_plan_opts r;
+  std::memset(&r, 0, sizeof(r));
+  if (o) r = *o;
+  r.n_cus = n_cus;
+  if (r.mlp_chunks <= 0) {
+    r.mlp_chunks = 4;
+    // fall back to fewer chunks if the chunk width has no code path
+    while (r.mlp_chunks > 1) {
+      Geo g;
+      if (c.ffn % r.mlp_chunks == 0 && geo_for_k(c.ffn / r.mlp_chunks, &g)) break;
+      r.mlp_chunks /= 2;
+    }
+  }
+  if (r.attn_block <= 0) {
+    const int rows_per_page = kPageBytes / (2 * c.head_dim);
+    if (c.max_seq <= 512 && c.max_seq * 2 * c.head_dim <= (kPages / 2) * kPageBytes) {
+      r.attn_block = ((c.max_seq + 63) / 64) * 64;
+    } else {
+      int64_t want = (int64_t(c.max_seq) * c.n_kv_heads + n_cus - 1) / n_cus;
+      int64_t blk = ((want + 63) / 64) * 64;
+      int64_t cap = int64_t(rows_per_page) * (kPages / 2);
+      if (blk > cap) blk = cap;
+      r.attn_block = int(blk);
+    }
+  }
+  if (r.watchdog_ms <= 0) r.watchdog_ms = 2000;
+  return r;
+}
+
+ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
+  ArenaLayout a;
+  std::memset(&a, 0, sizeof(a));
+  const uint64_t d = c.hidden, q = uint64_t(c.n_q_heads) * c.head_dim,
+                 kv = uint64_t(c.n_kv_heads) * c.head_dim, F = c.ffn;
+  const uint64_t hpg = c.n_q_heads / c.n_kv_heads;
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    uint64_t r = off;
+    off = align256(off + bytes);
+    return r;
+  };
+  for (int l = 1; l <= c.n_layers; l++) a.x[l] = take(4 * d);
+  for (int l = 0; l < c.n_layers; l++) {
+    a.qkv[l] = take(4 * (q + 2 * kv));
+    a.o[l] = take(4 * q);
+    a.h[l] = take(4 * d);
+    a.m[l] = take(4 * F);
+    a.part[l] = take(4 * uint64_t(max_parts) * hpg * (c.head_dim + 2));
+  }
+  a.rope_cos = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
+  a.rope_sin = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
+  a.zero_page = take(kUnit);
+  a.lm_slots = take(8 * uint64_t(max_lm_tiles));
+  a.status = take(64);
+  a.total = off;
+  return a;
+}
+
+// ------------------------------------------------------------------- build
+mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
+  const mk_config& c = in.cfg;
+  mk_status st = check_config(c, err);
+  if (st != MK_OK) return st;
+  const mk_plan_opts& o = in.opts;
+  const int C = in.n_cus;
+  if (C <= 0 || C > 4096) {
+    *err = "plan: n_cus out of range";
+    return MK_ERR_INVALID_ARG;
+  }
+  const int L = c.n_layers, d = c.hidden, H = c.n_q_heads, G = c.n_kv_heads, Dh = c.head_dim,
+            F = c.ffn, V = c.vocab, S = c.max_seq;
+  const int qd = H * Dh, kvd = G * Dh, hpg = H / G;
+  const int chunks = o.mlp_chunks;
+  if (chunks <= 0 || F % chunks) {
+    *err = "plan: mlp_chunks must divide ffn";
+    return MK_ERR_INVALID_ARG;
+  }
+  const int Fc = F / chunks;
+  Geo gd, gq, gf;
+  if (!geo_for_k(d, &gd) || !geo_for_k(qd, &gq) || !geo_for_k(Fc, &gf) || Fc > kMaxK) {
+    *err = "plan: ffn/mlp_chunks must be 256 or a multiple of 512 up to 4096";
+    return MK_ERR_UNSUPPORTED;
+  }
+  const int Bat = o.attn_block;
+  const int kv_rb = 2 * Dh;
+  if (Bat <= 0 || Bat % 64) {
+    *err = "plan: attn_block must be a positive multiple of 64";
+    return MK_ERR_INVALID_ARG;
+  }
+  const int kp = ceil_div(int64_t(Bat) * kv_rb, kPageBytes);
+  if (2 * kp > kPages) {
+    *err = "plan: attention tile (K and V blocks) exceeds the LDS page ring";
+    return MK_ERR_INVALID_ARG;
+  }
+  if (hpg * Bat > kAttnScoreFloats) {
+    *err = "plan: attention scores of one tile exceed the LDS scratch";
+    return MK_ERR_INVALID_ARG;
+  }
+  const int nblk = ceil_div(S, Bat);
+  *P = Plan();
+  P->n_cus = C;
+  P->attn_block = Bat;
+  P->attn_nblk = nblk;
+  P->attn_tiles = G * nblk;
+  P->mlp_chunks = chunks;
+  P->arena = arena_layout(c, C, G * nblk);
+  const uint64_t A = in.arena_base;
+  const ArenaLayout& ar = P->arena;
+  Builder b(in, P);
+
+  const uint64_t embed = uint64_t(in.w.embed), lm = uint64_t(in.w.lm_head);
+  auto lptr = [](const void* base, int l, uint64_t per_layer_elems) {
+    return uint64_t(base) + 2ull * per_layer_elems * uint64_t(l);
+  };
+
+  std::vector<uint32_t> c_qkv(L), c_attn(L), c_o(L), c_down(L);
+  std::vector<std::vector<uint32_t>> c_gu(L), c_ticket(L);
+  for (int l = 0; l < L; l++) {
+    c_qkv[l] = b.new_counter(l * ST_PER_LAYER + ST_QKV);
+    c_attn[l] = b.new_counter(l * ST_PER_LAYER + ST_ATTN);
+    if (nblk > 1)
+      for (int g = 0; g < G; g++) c_ticket[l].push_back(b.new_counter(l * ST_PER_LAYER + ST_ATTN));
+    c_o[l] = b.new_counter(l * ST_PER_LAYER + ST_O);
+    for (int ch = 0; ch < chunks; ch++) c_gu[l].push_back(b.new_counter(l * ST_PER_LAYER + ST_GU));
+    c_down[l] = b.new_counter(l * ST_PER_LAYER + ST_DOWN);
+  }
+  const uint32_t c_lm = b.new_counter(L * ST_PER_LAYER);
+
+  // evenly split N items over C CUs
+  auto split = [&](int64_t N, int cu, int64_t* lo, int64_t* hi) {
+    *lo = N * cu / C;
+    *hi = N * (cu + 1) / C;
+  };
+  auto set_wait = [](Instr& I, int k, uint32_t ctr) { I.wait_ctr[k] = ctr; };
+
+  // attention tile -> CU: spread over the CUs, and over XCDs when sparse
+  const int n_att = G * nblk;
+  auto att_cu = [&](int a) {
+    int64_t spacing = C / std::max(1, n_att);
+    int64_t cu = int64_t(a) * C / n_att;
+    if (spacing >= 8) cu += a % 8;
+    return int(cu % C);
+  };
+
+  for (int l = 0; l < L; l++) {
+    const int stg = l * ST_PER_LAYER;
+    // ------------------------------------------------------------ QKV
+    {
+      const int R = qd + 2 * kvd;
+      const int64_t N = R / gd.rpu;
+      for (int cu = 0; cu < C; cu++) {
+        int64_t i0, i1;
+        split(N, cu, &i0, &i1);
+        if (i1 <= i0) continue;
+        const int r0 = int(i0 * gd.rpu), r1 = int(i1 * gd.rpu);
+        Instr I = blank();
+        I.op = OP_GEMV;
+        I.epi = EPI_STORE;
+        I.nit = uint8_t(gd.nit);
+        I.rpu = uint8_t(gd.rpu);
+        I.layer = uint16_t(l);
+        I.flags = F_NORM | F_SIGNAL | (l == 0 ? F_IN_EMBED : 0);
+        I.n_items = uint32_t(i1 - i0);
+        I.row0 = uint32_t(r0);
+        I.row_bytes = uint32_t(2 * d);
+        I.n_rows = uint32_t(r1 - r0);
+        I.k = uint32_t(d);
+        // split [r0, r1) over Wq | Wk | Wv
+        const int bounds[4] = {0, qd, qd + kvd, qd + 2 * kvd};
+        const void* mats[3] = {in.w.wq, in.w.wk, in.w.wv};
+        const int mrows[3] = {qd, kvd, kvd};
+        int ns = 0;
+        for (int s = 0; s < 3; s++) {
+          int lo = std::max(r0, bounds[s]), hi = std::min(r1, bounds[s + 1]);
+          if (hi <= lo) continue;
+          I.seg_ptr[ns] = lptr(mats[s], l, uint64_t(mrows[s]) * d) + 2ull * d * (lo - bounds[s]);
+          I.seg_rows[ns] = uint32_t(hi - lo);
+          I.seg_stride[ns] = uint32_t(2 * d);
+          ns++;
+        }
+        I.aux[4] = uint32_t(ns);
+        I.in_ptr = l == 0 ? embed : A + ar.x[l];
+        I.out_ptr = A + ar.qkv[l];
+        I.gain_ptr = lptr(in.w.attn_norm, l, d);
+        if (l > 0) set_wait(I, 0, c_down[l - 1]);
+        I.sig_ctr = c_qkv[l];
+        I.n_pages = uint32_t(ceil_div(int64_t(I.n_rows) * I.row_bytes, kPageBytes));
+        InstrMeta m;
+        m.stage = stg + ST_QKV;
+        m.merge_write = false;
+        m.reads.push_back({l == 0 ? BUF_EMBED : BUF_X, l, 0, uint64_t(d)});
+        m.writes.push_back({BUF_QKV, l, uint64_t(r0), uint64_t(r1)});
+        b.push(cu, I, std::move(m), int64_t(I.n_rows) * I.row_bytes);
+      }
+    }
+    // ----------------------------------------------------------- ATTN
+    for (int a = 0; a < n_att; a++) {
+      const int g = a / nblk, blk = a % nblk;
+      Instr I = blank();
+      I.op = OP_ATTN;
+      I.layer = uint16_t(l);
+      I.flags = F_SIGNAL;
+      I.row_bytes = uint32_t(kv_rb);
+      I.n_rows = uint32_t(2 * Bat);
+      I.aux[0] = uint32_t(g);
+      I.aux[1] = uint32_t(blk);
+      I.aux[2] = uint32_t(Bat);
+      I.aux[3] = uint32_t(nblk);
+      I.aux[4] = uint32_t(kp);
+      const uint64_t head_rows = uint64_t(S) * Dh;  // elements per (layer, seq, group)
+      I.seg_ptr[0] = uint64_t(in.w.k_cache) + 2ull * head_rows * (uint64_t(l) * G + g);
+      I.seg_ptr[1] = uint64_t(in.w.v_cache) + 2ull * head_rows * (uint64_t(l) * G + g);
+      I.seg_rows[0] = nblk > 1 ? c_ticket[l][g] : kNoCounter;
+      I.in_ptr = A + ar.qkv[l];
+      I.out_ptr = A + ar.o[l];
+      I.res_ptr = A + ar.part[l];
+      set_wait(I, 0, c_qkv[l]);
+      I.sig_ctr = c_attn[l];
+      I.n_pages = uint32_t(2 * kp);
+      InstrMeta m;
+      m.stage = stg + ST_ATTN;
+      m.merge_write = nblk > 1;
+      m.reads.push_back({BUF_QKV, l, uint64_t(g) * hpg * Dh, uint64_t(g + 1) * hpg * Dh});
+      m.reads.push_back({BUF_QKV, l, uint64_t(qd + g * Dh), uint64_t(qd + (g + 1) * Dh)});
+      m.reads.push_back({BUF_QKV, l, uint64_t(qd + kvd + g * Dh), uint64_t(qd + kvd + (g + 1) * Dh)});
+      m.writes.push_back({BUF_O, l, uint64_t(g) * hpg * Dh, uint64_t(g + 1) * hpg * Dh});
+      // bytes streamed at full context
+      const int64_t rows = std::min<int64_t>(Bat, std::max<int64_t>(0, int64_t(S) - int64_t(blk) * Bat));
+      b.push(att_cu(a), I, std::move(m), 2 * rows * kv_rb);
+    }
+    // -------------------------------------------------------------- O
+    {
+      const int64_t N = d / gq.rpu;
+      for (int cu = 0; cu < C; cu++) {
+        int64_t i0, i1;
+        split(N, cu, &i0, &i1);
+        if (i1 <= i0) continue;
+        const int r0 = int(i0 * gq.rpu), r1 = int(i1 * gq.rpu);
+        Instr I = blank();
+        I.op = OP_GEMV;
+        I.epi = EPI_RESID;
+        I.nit = uint8_t(gq.nit);
+        I.rpu = uint8_t(gq.rpu);
+        I.layer = uint16_t(l);
+        I.flags = F_SIGNAL | (l == 0 ? F_RES_EMBED : 0);
+        I.n_items = uint32_t(i1 - i0);
+        I.row0 = uint32_t(r0);
+        I.row_bytes = uint32_t(2 * qd);
+        I.n_rows = uint32_t(r1 - r0);
+        I.k = uint32_t(qd);
+        I.seg_ptr[0] = lptr(in.w.wo, l, uint64_t(d) * qd) + 2ull * qd * r0;
+        I.seg_rows[0] = uint32_t(r1 - r0);
+        I.seg_stride[0] = uint32_t(2 * qd);
+        I.aux[4] = 1;
+        I.in_ptr = A + ar.o[l];
+        I.res_ptr = l == 0 ? embed : A + ar.x[l];
+        I.out_ptr = A + ar.h[l];
+        set_wait(I, 0, c_attn[l]);
+        I.sig_ctr = c_o[l];
+        I.n_pages = uint32_t(ceil_div(int64_t(I.n_rows) * I.row_bytes, kPageBytes));
+        InstrMeta m;
+        m.stage = stg + ST_O;
+        m.merge_write = false;
+        m.reads.push_back({BUF_O, l, 0, uint64_t(qd)});
+        m.reads.push_back({l == 0 ? BUF_EMBED : BUF_X, l, uint64_t(r0), uint64_t(r1)});
+        m.writes.push_back({BUF_H, l, uint64_t(r0), uint64_t(r1)});
+        b.push(cu, I, std::move(m), int64_t(I.n_rows) * I.row_bytes);
+      }
+    }
+    // ------------------------------------------------------- GATE/UP
+    for (int ch = 0; ch < chunks; ch++) {
+      const int64_t N = Fc;  // pairs
+      for (int cu = 0; cu < C; cu++) {
+        int64_t i0, i1;
+        split(N, cu, &i0, &i1);
+        if (i1 <= i0) continue;
+        const int p0 = ch * Fc + int(i0), p1 = ch * Fc + int(i1);
+        Instr I = blank();
+        I.op = OP_GEMV;
+        I.epi = EPI_SWIGLU;
+        I.nit = uint8_t(gd.nit);
+        I.rpu = uint8_t(gd.rpu);
+        I.layer = uint16_t(l);
+        I.flags = F_NORM | F_SIGNAL | F_INTERLEAVE;
+        I.n_items = uint32_t(p1 - p0);
+        I.row0 = uint32_t(p0);
+        I.row_bytes = uint32_t(2 * d);
+        I.n_rows = uint32_t(2 * (p1 - p0));
+        I.k = uint32_t(d);
+        I.seg_ptr[0] = lptr(in.w.w_gate, l, uint64_t(F) * d) + 2ull * d * p0;
+        I.seg_ptr[1] = lptr(in.w.w_up, l, uint64_t(F) * d) + 2ull * d * p0;
+        I.seg_rows[0] = I.seg_rows[1] = uint32_t(p1 - p0);
+        I.seg_stride[0] = I.seg_stride[1] = uint32_t(2 * d);
+        I.aux[4] = 2;
+        I.in_ptr = A + ar.h[l];
+        I.out_ptr = A + ar.m[l];
+        I.gain_ptr = lptr(in.w.mlp_norm, l, d);
+        set_wait(I, 0, c_o[l]);
+        I.sig_ctr = c_gu[l][ch];
+        I.n_pages = uint32_t(ceil_div(int64_t(I.n_rows) * I.row_bytes, kPageBytes));
+        InstrMeta m;
+        m.stage = stg + ST_GU;
+        m.merge_write = false;
+        m.reads.push_back({BUF_H, l, 0, uint64_t(d)});
+        m.writes.push_back({BUF_M, l, uint64_t(p0), uint64_t(p1)});
+        b.push(cu, I, std::move(m), int64_t(I.n_rows) * I.row_bytes);
+      }
+    }
+    // ---------------------------------------------------------- DOWN
+    {
+      const int64_t N = d / gf.rpu;
+      for (int cu = 0; cu < C; cu++) {
+        int64_t i0, i1;
+        split(N, cu, &i0, &i1);
+        if (i1 <= i0) continue;
+        const int r0 = int(i0 * gf.rpu), r1 = int(i1 * gf.rpu);
+        if (r1 - r0 > 256) {
+          *err = "plan: more than 256 down-projection rows on one CU";
+          return MK_ERR_UNSUPPORTED;
+        }
+        for (int ch = 0; ch < chunks; ch++) {
+          Instr I = blank();
+          I.op = OP_GEMV;
+          I.epi = chunks == 1 ? EPI_ACC_ONLY
+                              : (ch == 0 ? EPI_ACC_FIRST : (ch == chunks - 1 ? EPI_ACC_LAST : EPI_ACC_MID));
+          I.nit = uint8_t(gf.nit);
+          I.rpu = uint8_t(gf.rpu);
+          I.layer = uint16_t(l);
+          const bool last = ch == chunks - 1;
+          I.flags = last ? F_SIGNAL : 0;
+          I.n_items = uint32_t(i1 - i0);
+          I.row0 = uint32_t(r0);
+          I.row_bytes = uint32_t(2 * Fc);
+          I.n_rows = uint32_t(r1 - r0);
+          I.k = uint32_t(Fc);
+          I.seg_ptr[0] = lptr(in.w.w_down, l, uint64_t(d) * F) + 2ull * (uint64_t(F) * r0 + uint64_t(ch) * Fc);
+          I.seg_rows[0] = uint32_t(r1 - r0);
+          I.seg_stride[0] = uint32_t(2 * F);
+          I.aux[0] = 0;  // LDS accumulator offset
+          I.aux[4] = 1;
+          I.in_ptr = A + ar.m[l] + 4ull * ch * Fc;
+          I.res_ptr = A + ar.h[l];
+          I.out_ptr = A + ar.x[l + 1];
+          set_wait(I, 0, c_gu[l][ch]);
+          I.sig_ctr = last ? c_down[l] : kNoCounter;
+          I.n_pages = uint32_t(ceil_div(int64_t(I.n_rows) * I.row_bytes, kPageBytes));
+          InstrMeta m;
+          m.stage = stg + ST_DOWN;
+          m.merge_write = false;
+          m.reads.push_back({BUF_M, l, uint64_t(ch) * Fc, uint64_t(ch + 1) * Fc});
+          if (ch == 0) m.reads.push_back({BUF_H, l, uint64_t(r0), uint64_t(r1)});
+          if (last) m.writes.push_back({BUF_X, l + 1, uint64_t(r0), uint64_t(r1)});
+          b.push(cu, I, std::move(m), int64_t(I.n_rows) * I.row_bytes);
+        }
+      }
+    }
+  }
+  // ------------------------------------------------------------ LM head
+  {
+    const int64_t N = V / gd.rpu;
+    int tile = 0;
+    std::vector<int> lm_cus;
+    for (int cu = 0; cu < C; cu++) {
+      int64_t i0, i1;
+      split(N, cu, &i0, &i1);
+      if (i1 > i0) lm_cus.push_back(cu);
+    }
+    const int n_lm = int(lm_cus.size());
+    for (int cu : lm_cus) {
+      int64_t i0, i1;
+      split(N, cu, &i0, &i1);
+      const int r0 = int(i0 * gd.rpu), r1 = int(i1 * gd.rpu);
+      Instr I = blank();
+      I.op = OP_GEMV;
+      I.epi = EPI_ARGMAX;
+      I.nit = uint8_t(gd.nit);
+      I.rpu = uint8_t(gd.rpu);
+      I.layer = uint16_t(L);
+      I.flags = F_NORM | F_SIGNAL;
+      I.n_items = uint32_t(i1 - i0);
+      I.row0 = uint32_t(r0);
+      I.row_bytes = uint32_t(2 * d);
+      I.n_rows = uint32_t(r1 - r0);
+      I.k = uint32_t(d);
+      I.seg_ptr[0] = lm + 2ull * d * r0;
+      I.seg_rows[0] = uint32_t(r1 - r0);
+      I.seg_stride[0] = uint32_t(2 * d);
+      I.aux[1] = uint32_t(tile);
+      I.aux[3] = uint32_t(n_lm);
+      I.aux[4] = 1;
+      I.in_ptr = A + ar.x[L];
+      I.gain_ptr = uint64_t(in.w.final_norm);
+      set_wait(I, 0, c_down[L - 1]);
+      I.sig_ctr = c_lm;
+      I.n_pages = uint32_t(ceil_div(int64_t(I.n_rows) * I.row_bytes, kPageBytes));
+      InstrMeta m;
+      m.stage = L * ST_PER_LAYER;
+      m.merge_write = false;
+      m.reads.push_back({BUF_X, L, 0, uint64_t(d)});
+      m.writes.push_back({BUF_LOGITS, 0, uint64_t(r0), uint64_t(r1)});
+      b.push(cu, I, std::move(m), int64_t(I.n_rows) * I.row_bytes);
+      tile++;
+    }
+    P->lm_tiles = n_lm;
+  }
+
+  // producers per counter (per step)
+  for (int cu = 0; cu < C; cu++)
+    for (const Instr& I : b.q[cu]) {
+      if (I.op == OP_ATTN && I.aux[3] > 1) {
+        // every tile of the group takes a ticket; the last one signals ATTN
+        P->ctr_producers[I.seg_rows[0]]++;
+        continue;
+      }
+      if ((I.flags & F_SIGNAL) && I.sig_ctr != kNoCounter) P->ctr_producers[I.sig_ctr]++;
+    }
+  for (int l = 0; l < L; l++)
+    if (nblk > 1) P->ctr_producers[c_attn[l]] = uint32_t(G);
+  // fill wait counts
+  for (int cu = 0; cu < C; cu++)
+    for (Instr& I : b.q[cu])
+      for (int k = 0; k < 2; k++)
+        if (I.wait_ctr[k] != kNoCounter) I.wait_cnt[k] = P->ctr_producers[I.wait_ctr[k]];
+  // flatten
+  P->q_off.assign(C + 1, 0);
+  for (int cu = 0; cu < C; cu++) {
+    P->q_off[cu + 1] = P->q_off[cu] + uint32_t(b.q[cu].size());
+    P->instrs.insert(P->instrs.end(), b.q[cu].begin(), b.q[cu].end());
+    P->meta.insert(P->meta.end(), b.qm[cu].begin(), b.qm[cu].end());
+  }
+  P->n_counters = int(P->ctr_stage.size());
+  // bytes
+  int64_t wbytes = 0;
+  wbytes += int64_t(L) * 2 * (int64_t(qd + 2 * kvd) * d + int64_t(d) * qd + 3ll * F * d + 2ll * d);
+  wbytes += 2ll * V * d + 2ll * d + 2ll * d;
+  P->weight_bytes = wbytes;
+  P->max_cu_bytes = *std::max_element(b.cu_bytes.begin(), b.cu_bytes.end());
+  P->min_cu_bytes = *std::min_element(b.cu_bytes.begin(), b.cu_bytes.end());
+  return MK_OK;
+}
+
+// ------------------------------------------------------------------ verify
+mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint64_t seed) {
+  auto fail = [&](const std::string& m) {
+    *err = "verify: " + m;
+    return MK_ERR_INVALID_ARG;
+  };
+  const int C = p.n_cus;
+  const int NC = p.n_counters;
+  const mk_config& c = in.cfg;
+  // 1. counter producers match signalling instructions; waits use them
+  std::vector<uint32_t> sig(NC, 0);
+  for (const Instr& I : p.instrs) {
+    if (I.op == OP_ATTN && I.aux[3] > 1) {
+      if (I.seg_rows[0] >= uint32_t(NC)) return fail("attention ticket counter out of range");
+      sig[I.seg_rows[0]]++;
+    } else if ((I.flags & F_SIGNAL) && I.sig_ctr != kNoCounter) {
+      if (I.sig_ctr >= uint32_t(NC)) return fail("signal counter out of range");
+      sig[I.sig_ctr]++;
+    }
+  }
+  for (size_t i = 0; i < p.instrs.size(); i++) {
+    const Instr& I = p.instrs[i];
+    for (int k = 0; k < 2; k++) {
+      if (I.wait_ctr[k] == kNoCounter) continue;
+      const uint32_t ct = I.wait_ctr[k];
+      if (ct >= uint32_t(NC)) return fail("wait counter out of range");
+      if (I.wait_cnt[k] != p.ctr_producers[ct]) {
+        std::ostringstream s;
+        s << "instruction " << i << " waits for " << I.wait_cnt[k] << " signals on counter " << ct
+          << " which has " << p.ctr_producers[ct] << " producers";
+        return fail(s.str());
+      }
+      // 2. stage order: every wait names a counter of a strictly earlier stage
+      if (p.ctr_stage[ct] >= p.meta[i].stage) return fail("wait on a counter of the same or a later stage");
+    }
+  }
+  for (int ct = 0; ct < NC; ct++) {
+    bool attn_merged = false;
+    for (const Instr& I : p.instrs)
+      if (I.op == OP_ATTN && I.aux[3] > 1 && I.sig_ctr == uint32_t(ct)) attn_merged = true;
+    const uint32_t expect = attn_merged ? uint32_t(c.n_kv_heads) : sig[ct];
+    if (expect != p.ctr_producers[ct]) {
+      std::ostringstream s;
+      s << "counter " << ct << " expects " << p.ctr_producers[ct] << " producers, plan has " << expect;
+      return fail(s.str());
+    }
+  }
+  // 3. queue order per CU is by stage; pages are contiguous and within budget
+  for (int cu = 0; cu < C; cu++) {
+    uint32_t page = 0;
+    int last_stage = -1;
+    for (uint32_t i = p.q_off[cu]; i < p.q_off[cu + 1]; i++) {
+      const Instr& I = p.instrs[i];
+      const InstrMeta& m = p.meta[i];
+      if (m.stage < last_stage) return fail("queue not ordered by stage");
+      last_stage = m.stage;
+      if (I.page0 != page) return fail("page stream not contiguous");
+      page += I.n_pages;
+      if (I.op == OP_GEMV) {
+        const uint64_t need = uint64_t(I.n_rows) * I.row_bytes;
+        if (uint64_t(I.n_pages) * kPageBytes < need) return fail("page budget smaller than the tile");
+        if (I.rpu == 1 && I.row_bytes != uint32_t(I.nit) * kUnit) return fail("row geometry");
+        if (I.rpu == 2 && I.row_bytes != kUnit / 2) return fail("row geometry (512 B rows)");
+        // bytes one compute wave needs resident at once (a row, or a gate/up pair)
+        const uint32_t item_bytes = I.rpu == 2 ? uint32_t(kUnit)
+                                               : (I.epi == EPI_SWIGLU ? 2 : 1) * I.row_bytes;
+        if (uint32_t(ceil_div(item_bytes, kPageBytes)) + 1 > uint32_t(kPages))
+          return fail("an item spans more pages than the ring holds");
+        if (I.k > uint32_t(kMaxK)) return fail("input longer than the staging buffer");
+        if (I.epi == EPI_SWIGLU && I.n_rows != 2 * I.n_items) return fail("gate/up pairs");
+        if (I.epi != EPI_SWIGLU && I.n_rows != I.n_items * I.rpu) return fail("items vs rows");
+        uint32_t srows = 0;
+        for (uint32_t s = 0; s < I.aux[4]; s++) srows += I.seg_rows[s];
+        if (srows != I.n_rows) return fail("segments do not cover the stream rows");
+      } else {
+        if (2 * I.aux[4] != I.n_pages || 2 * I.aux[4] > uint32_t(kPages))
+          return fail("attention page regions");
+      }
+    }
+  }
+  // 4. read coverage: every element read must be written by an instruction
+  //    whose signal the reader transitively waits for; each element written once
+  // happens-before closure over counters (bitsets)
+  std::vector<std::vector<uint64_t>> hb(NC, std::vector<uint64_t>((NC + 63) / 64, 0));
+  // counters each counter's producers wait on
+  std::vector<std::vector<uint32_t>> waits_of(NC);
+  for (const Instr& I : p.instrs) {
+    uint32_t sc = kNoCounter;
+    if (I.op == OP_ATTN && I.aux[3] > 1) sc = I.sig_ctr;  // the merger waits like every tile
+    else if ((I.flags & F_SIGNAL) && I.sig_ctr != kNoCounter) sc = I.sig_ctr;
+    if (I.op == OP_ATTN && I.aux[3] > 1) waits_of[I.seg_rows[0]].push_back(I.wait_ctr[0]);
+    if (sc == kNoCounter) continue;
+    for (int k = 0; k < 2; k++)
+      if (I.wait_ctr[k] != kNoCounter) waits_of[sc].push_back(I.wait_ctr[k]);
+  }
+  // DOWN chunks other than the last do not signal, yet the last chunk's result
+  // depends on them (same waves, program order): their waits belong to the
+  // down counter's closure too.
+  for (size_t i = 0; i < p.instrs.size(); i++) {
+    const Instr& I = p.instrs[i];
+    if (I.op == OP_GEMV && (I.epi == EPI_ACC_FIRST || I.epi == EPI_ACC_MID)) {
+      // find the last chunk of the same tile later in the same queue
+      for (size_t j = i + 1; j < p.instrs.size() && p.meta[j].cu == p.meta[i].cu; j++) {
+        const Instr& J = p.instrs[j];
+        if (J.op == OP_GEMV && J.epi == EPI_ACC_LAST && J.layer == I.layer && J.row0 == I.row0) {
+          for (int k = 0; k < 2; k++)
+            if (I.wait_ctr[k] != kNoCounter) waits_of[J.sig_ctr].push_back(I.wait_ctr[k]);
+          break;
+        }
+      }
+    }
+  }
+  // counters are numbered in stage order, so one pass in increasing order works
+  std::vector<int> order(NC);
+  for (int i = 0; i < NC; i++) order[i] = i;
+  std::sort(order.begin(), order.end(), [&](int a, int b2) { return p.ctr_stage[a] < p.ctr_stage[b2]; });
+  for (int ct : order) {
+    hb[ct][ct / 64] |= 1ull << (ct % 64);
+    for (uint32_t w : waits_of[ct]) {
+      if (p.ctr_stage[w] >= p.ctr_stage[ct]) return fail("cyclic counter dependency");
+      for (size_t k = 0; k < hb[ct].size(); k++) hb[ct][k] |= hb[w][k];
+    }
+  }
+  auto in_closure = [&](const Instr& I, uint32_t ct) {
+    for (int k = 0; k < 2; k++)
+      if (I.wait_ctr[k] != kNoCounter && (hb[I.wait_ctr[k]][ct / 64] >> (ct % 64) & 1)) return true;
+    return false;
+  };
+  // writers per buffer: (layer, lo, hi, signal counter, merge)
+  struct W {
+    uint64_t lo, hi;
+    uint32_t ctr;
+    bool merge;
+  };
+  std::map<std::pair<int, int>, std::vector<W>> writers;
+  for (size_t i = 0; i < p.instrs.size(); i++) {
+    const Instr& I = p.instrs[i];
+    uint32_t ct = I.sig_ctr;
+    if (I.op == OP_GEMV && I.epi == EPI_ACC_LAST) ct = I.sig_ctr;
+    for (const Range& r : p.meta[i].writes) writers[{r.buf, r.layer}].push_back({r.lo, r.hi, ct, p.meta[i].merge_write});
+  }
+  for (auto& kv : writers) {
+    auto& v = kv.second;
+    std::sort(v.begin(), v.end(), [](const W& a, const W& b2) { return a.lo < b2.lo; });
+    for (size_t k = 1; k < v.size(); k++)
+      if (v[k].lo < v[k - 1].hi && !(v[k].merge && v[k - 1].merge && v[k].lo == v[k - 1].lo && v[k].hi == v[k - 1].hi))
+        return fail(std::string("buffer ") + kBufName[kv.first.first] + " written twice");
+  }
+  for (size_t i = 0; i < p.instrs.size(); i++) {
+    const Instr& I = p.instrs[i];
+    for (const Range& r : p.meta[i].reads) {
+      if (r.buf == BUF_EMBED) continue;  // input of the step
+      auto it = writers.find({r.buf, r.layer});
+      if (it == writers.end()) return fail(std::string("read of never-written buffer ") + kBufName[r.buf]);
+      uint64_t covered = r.lo;
+      for (const W& w : it->second) {
+        if (w.hi <= r.lo || w.lo >= r.hi) continue;
+        if (w.lo > covered) break;
+        if (!in_closure(I, w.ctr)) {
+          std::ostringstream s;
+          s << "instruction " << i << " (stage " << p.meta[i].stage << ") reads " << kBufName[r.buf]
+            << "[" << r.layer << "] without waiting for its writer's counter " << w.ctr;
+          return fail(s.str());
+        }
+        covered = std::max(covered, w.hi);
+      }
+      if (covered < r.hi) {
+        std::ostringstream s;
+        s << "instruction " << i << " reads " << kBufName[r.buf] << "[" << r.layer << "][" << covered
+          << "] which no instruction writes";
+        return fail(s.str());
+      }
+    }
+  }
+  // 5. memory bounds: every DMA source range lies inside a weight tensor or
+  //    the KV cache, every activation pointer inside the arena or embedding
+  {
+    struct Ext {
+      uint64_t lo, hi;
+      const char* name;
+    };
+    const uint64_t L = c.n_layers, d = c.hidden, qd = uint64_t(c.n_q_heads) * c.head_dim,
+                   kvd = uint64_t(c.n_kv_heads) * c.head_dim, F = c.ffn, V = c.vocab;
+    const uint64_t kv_bytes = 2ull * L * c.batch * c.n_kv_heads * c.max_seq * c.head_dim;
+    const Ext ext[] = {
+        {uint64_t(in.w.embed), uint64_t(in.w.embed) + 2 * V * d, "embed"},
+        {uint64_t(in.w.lm_head), uint64_t(in.w.lm_head) + 2 * V * d, "lm_head"},
+        {uint64_t(in.w.wq), uint64_t(in.w.wq) + 2 * L * qd * d, "wq"},
+        {uint64_t(in.w.wk), uint64_t(in.w.wk) + 2 * L * kvd * d, "wk"},
+        {uint64_t(in.w.wv), uint64_t(in.w.wv) + 2 * L * kvd * d, "wv"},
+        {uint64_t(in.w.wo), uint64_t(in.w.wo) + 2 * L * d * qd, "wo"},
+        {uint64_t(in.w.w_gate), uint64_t(in.w.w_gate) + 2 * L * F * d, "w_gate"},
+        {uint64_t(in.w.w_up), uint64_t(in.w.w_up) + 2 * L * F * d, "w_up"},
+        {uint64_t(in.w.w_down), uint64_t(in.w.w_down) + 2 * L * d * F, "w_down"},
+        {uint64_t(in.w.k_cache), uint64_t(in.w.k_cache) + kv_bytes, "k_cache"},
+        {uint64_t(in.w.v_cache), uint64_t(in.w.v_cache) + kv_bytes, "v_cache"},
+    };
+    auto inside = [&](uint64_t lo, uint64_t hi) {
+      for (const Ext& e : ext)
+        if (lo >= e.lo && hi <= e.hi) return true;
+      return false;
+    };
+    const uint64_t A = in.arena_base, Aend = in.arena_base + p.arena.total;
+    auto in_arena = [&](uint64_t lo, uint64_t hi) { return lo >= A && hi <= Aend; };
+    for (size_t i = 0; i < p.instrs.size(); i++) {
+      const Instr& I = p.instrs[i];
+      if (I.op == OP_GEMV) {
+        for (uint32_t sg = 0; sg < I.aux[4]; sg++) {
+          if (!I.seg_rows[sg]) continue;
+          const uint64_t lo = I.seg_ptr[sg];
+          const uint64_t hi = lo + uint64_t(I.seg_rows[sg] - 1) * I.seg_stride[sg] + I.row_bytes;
+          if (!inside(lo, hi)) {
+            std::ostringstream m;
+            m << "instruction " << i << " streams bytes outside every weight tensor";
+            return fail(m.str());
+          }
+        }
+        const uint64_t kb = 4ull * I.k;
+        if (I.flags & F_IN_EMBED) {
+          if (I.in_ptr != uint64_t(in.w.embed)) return fail("embedding input pointer");
+        } else if (!in_arena(I.in_ptr, I.in_ptr + kb)) {
+          return fail("GEMV input outside the arena");
+        }
+        uint64_t out_rows = I.rpu == 2 && I.epi != EPI_SWIGLU ? uint64_t(I.n_items) * 2 : I.n_items;
+        if (I.epi != EPI_ARGMAX && I.epi != EPI_ACC_FIRST && I.epi != EPI_ACC_MID &&
+            !in_arena(I.out_ptr + 4ull * I.row0, I.out_ptr + 4ull * (I.row0 + out_rows)))
+          return fail("GEMV output outside the arena");
+        if ((I.epi == EPI_RESID || I.epi == EPI_ACC_ONLY || I.epi == EPI_ACC_FIRST) &&
+            !(I.flags & F_RES_EMBED) &&
+            !in_arena(I.res_ptr + 4ull * I.row0, I.res_ptr + 4ull * (I.row0 + out_rows)))
+          return fail("GEMV residual outside the arena");
+        if ((I.epi == EPI_ACC_FIRST || I.epi == EPI_ACC_MID || I.epi == EPI_ACC_LAST) &&
+            I.aux[0] + out_rows > 256)
+          return fail("down-projection accumulators exceed the LDS area");
+      } else {
+        const uint64_t span = uint64_t(c.max_seq) * I.row_bytes;
+        if (!inside(I.seg_ptr[0], I.seg_ptr[0] + span) || !inside(I.seg_ptr[1], I.seg_ptr[1] + span))
+          return fail("attention cache rows outside the KV cache");
+        const uint64_t hpg = c.n_q_heads / c.n_kv_heads;
+        const uint64_t rec = hpg * (c.head_dim + 2) * 4;
+        if (I.aux[3] > 1 &&
+            !in_arena(I.res_ptr, I.res_ptr + rec * (uint64_t(I.aux[0]) * I.aux[3] + I.aux[3])))
+          return fail("attention partials outside the arena");
+        if (!in_arena(I.in_ptr, I.in_ptr + 4 * (qd + 2 * kvd)) || !in_arena(I.out_ptr, I.out_ptr + 4 * qd))
+          return fail("attention activations outside the arena");
+      }
+    }
+  }
+  // 6. randomized execution of the queues: every instruction must run
+  std::mt19937_64 rng(seed);
+  for (int trial = 0; trial < 3; trial++) {
+    std::vector<uint32_t> val(NC, 0), head(C, 0), ticket(NC, 0);
+    size_t done = 0, total = p.instrs.size();
+    std::vector<int> cus(C);
+    for (int i = 0; i < C; i++) cus[i] = i;
+    while (done < total) {
+      std::shuffle(cus.begin(), cus.end(), rng);
+      bool progress = false;
+      for (int cu : cus) {
+        uint32_t idx = p.q_off[cu] + head[cu];
+        if (idx >= p.q_off[cu + 1]) continue;
+        const Instr& I = p.instrs[idx];
+        bool ready = true;
+        for (int k = 0; k < 2; k++)
+          if (I.wait_ctr[k] != kNoCounter && val[I.wait_ctr[k]] < I.wait_cnt[k]) ready = false;
+        if (!ready) continue;
+        if (I.op == OP_ATTN && I.aux[3] > 1) {
+          if (++ticket[I.seg_rows[0]] == I.aux[3]) val[I.sig_ctr]++;
+        } else if ((I.flags & F_SIGNAL) && I.sig_ctr != kNoCounter) {
+          val[I.sig_ctr]++;
+        }
+        head[cu]++;
+        done++;
+        progress = true;
+      }
+      if (!progress) {
+        std::ostringstream s;
+        s << "deadlock in queue simulation after " << done << " of " << total << " instructions";
+        return fail(s.str());
+      }
+    }
+  }
+  return MK_OK;
+}
+
+void corrupt_one_target(Plan* p) {
+  // raise the target of the first waiting instruction of the last CU queue
+  for (int cu = p->n_cus - 1; cu >= 0; cu--)
+    for (uint32_t i = p->q_off[cu]; i < p->q_off[cu + 1]; i++)
+      if (p->instrs[i].wait_ctr[0] != kNoCounter) {
+        p->instrs[i].wait_cnt[0] += 1;
+        return;
+      }
+}
+
+void summarize(const PlanInput& in, const Plan& p, mk_plan_summary* s) {
+  std::memset(s, 0, sizeof(*s));
+  s->n_cus = p.n_cus;
+  s->n_instr = int32_t(p.instrs.size());
+  uint32_t mq = 0;
+  for (int cu = 0; cu < p.n_cus; cu++) mq = std::max(mq, p.q_off[cu + 1] - p.q_off[cu]);
+  s->max_queue = int32_t(mq);
+  s->n_counters = p.n_counters;
+  s->lds_bytes = kLdsTotal;
+  s->n_pages = kPages;
+  s->page_bytes = kPageBytes;
+  s->attn_block = p.attn_block;
+  s->attn_tiles = p.attn_tiles;
+  s->mlp_chunks = p.mlp_chunks;
+  s->weight_bytes = p.weight_bytes;
+  s->max_cu_bytes = p.max_cu_bytes;
+  s->min_cu_bytes = p.min_cu_bytes;
+  (void)in;
+}
+
+std::string plan_report(const PlanInput& in, const Plan& p) {
+  std::ostringstream s;
+  mk_plan_summary sm;
+  summarize(in, p, &sm);
+  s << "{\"n_cus\": " << sm.n_cus << ", \"n_instr\": " << sm.n_instr << ", \"max_queue\": " << sm.max_queue
+    << ", \"n_counters\": " << sm.n_counters << ", \"lds_bytes\": " << sm.lds_bytes
+    << ", \"n_pages\": " << sm.n_pages << ", \"attn_block\": " << sm.attn_block
+    << ", \"attn_tiles\": " << sm.attn_tiles << ", \"mlp_chunks\": " << sm.mlp_chunks
+    << ", \"lm_tiles\": " << p.lm_tiles << ", \"weight_bytes\": " << sm.weight_bytes
+    << ", \"max_cu_bytes\": " << sm.max_cu_bytes << ", \"min_cu_bytes\": " << sm.min_cu_bytes
+    << ", \"arena_bytes\": " << p.arena.total << ", \"queue_lengths\": [";
+  for (int cu = 0; cu < p.n_cus; cu++) s << (cu ? ", " : "") << (p.q_off[cu + 1] - p.q_off[cu]);
+  s << "]}";
+  return s.str();
+}
+
+}  // namespace mk

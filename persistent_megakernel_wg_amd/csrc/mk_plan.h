@@ -1,0 +1,92 @@
+// mk_plan.h — host planner for the decode megakernel (pure C++, no HIP).
+//
+// Static scheduling as in the Llama-1B megakernel write-up (javascript.cn
+// article, "Megakernel：从零设计的融合思路": every SM gets an execution plan,
+// dependencies are settled before the run): the planner cuts each stage of the
+// decoder into tiles, places them on per-CU queues ordered by (layer, stage),
+// gives every counter its producer count, sizes each tile's LDS page budget,
+// and verifies the result.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_isa.h"
+
+namespace mk {
+
+// Activation buffers of one step, as offsets from the arena base (bytes).
+struct ArenaLayout {
+  uint64_t x[129];        // residual stream entering layer l (x[0] unused: embedding)
+  uint64_t qkv[128], o[128], h[128], m[128], part[128];
+  uint64_t rope_cos, rope_sin, zero_page, lm_slots, status;
+  uint64_t total;
+};
+
+// Everything the planner needs: shape, options and the device addresses it
+// bakes into the instructions (fake but consistent addresses in a dry run).
+struct PlanInput {
+  mk_config cfg;
+  mk_plan_opts opts;
+  int n_cus;
+  mk_weights w;          // device pointers (may be fake)
+  uint64_t arena_base;   // device address of the arena
+};
+
+// Verification view of one instruction.
+struct Range {
+  int buf;               // buffer id (see kBuf*)
+  int layer;
+  uint64_t lo, hi;       // element range [lo, hi)
+};
+struct InstrMeta {
+  int cu;
+  int stage;             // global stage order
+  std::vector<Range> reads, writes;
+  bool merge_write;      // writes shared by the tiles of one attention group
+};
+
+struct Plan {
+  ArenaLayout arena;
+  std::vector<uint32_t> q_off;      // [n_cus + 1]
+  std::vector<Instr> instrs;        // queues back to back
+  std::vector<InstrMeta> meta;      // parallel to instrs
+  std::vector<uint32_t> ctr_producers;  // per counter: signals per step
+  std::vector<int> ctr_stage;       // stage of the counter's producers
+  int n_cus = 0, n_counters = 0;
+  int attn_block = 0, attn_nblk = 0, attn_tiles = 0, mlp_chunks = 0, lm_tiles = 0;
+  int64_t weight_bytes = 0, max_cu_bytes = 0, min_cu_bytes = 0;
+};
+
+// Arena layout for a shape (does not depend on the plan options).
+ArenaLayout arena_layout(const mk_config& cfg, int max_lm_tiles, int max_parts);
+
+// Validate a shape for the kernel's code paths.  Returns MK_OK or an error
+// with a message.
+mk_status check_config(const mk_config& cfg, std::string* err);
+
+// Build the plan.  Returns MK_OK, or MK_ERR_* with a message in *err.
+mk_status build_plan(const PlanInput& in, Plan* out, std::string* err);
+
+// Verify a plan: counter targets, stage order (no cycles), page budgets, read
+// coverage through counter waits, single writers, and a randomized
+// queue-order simulation that must run every instruction.  Returns MK_OK or
+// MK_ERR_INVALID_ARG with the first violation in *err.
+mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint64_t seed = 1);
+
+// Test hook: make one wait target unreachable (applied after verification by
+// the runtime so that a step must end in the watchdog; mk_plan_check applies
+// it before verification to show that the verifier rejects it).
+void corrupt_one_target(Plan* p);
+
+// Human-readable report (used by mk_plan_check).
+std::string plan_report(const PlanInput& in, const Plan& p);
+
+void summarize(const PlanInput& in, const Plan& p, mk_plan_summary* s);
+
+// Resolved defaults for the options.
+mk_plan_opts resolve_opts(const mk_config& cfg, const mk_plan_opts* opts, int n_cus);
+
+}  // namespace mk

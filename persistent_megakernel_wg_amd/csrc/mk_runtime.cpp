@@ -1,0 +1,297 @@
+// mk_runtime.cpp — the C ABI (include/mk.h) over the HIP host API: context,
+// arena, RoPE tables, plan upload, launch, status readback.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_plan.h"
+
+extern "C" hipError_t mk_launch_megakernel(const mk::KArgs* args, int n_cus, hipStream_t stream,
+                                           int cooperative);
+
+struct mk_ctx {
+  mk_config cfg;
+  mk_weights w;
+  int device = 0;
+  int dev_cus = 0;
+  std::string err;
+  std::vector<float> rope_cos, rope_sin;
+  // plan state
+  bool planned = false;
+  mk::PlanInput pin;
+  mk::Plan plan;
+  char* arena = nullptr;
+  mk::Instr* d_instrs = nullptr;
+  uint32_t* d_qoff = nullptr;
+  uint32_t* d_counters = nullptr;
+  uint32_t epoch = 0;
+  hipStream_t last_stream = nullptr;
+  bool has_step = false;
+  int cooperative = 1;
+};
+
+namespace {
+thread_local std::string g_err;
+
+mk_status fail(mk_ctx* c, mk_status st, const std::string& m) {
+  if (c) c->err = m;
+  g_err = m;
+  return st;
+}
+mk_status hip_fail(mk_ctx* c, hipError_t e, const char* what) {
+  return fail(c, e == hipErrorOutOfMemory ? MK_ERR_OOM : MK_ERR_HIP,
+              std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void free_plan(mk_ctx* c) {
+  if (c->arena) (void)hipFree(c->arena);
+  if (c->d_instrs) (void)hipFree(c->d_instrs);
+  if (c->d_qoff) (void)hipFree(c->d_qoff);
+  if (c->d_counters) (void)hipFree(c->d_counters);
+  c->arena = nullptr;
+  c->d_instrs = nullptr;
+  c->d_qoff = nullptr;
+  c->d_counters = nullptr;
+  c->planned = false;
+}
+
+// RoPE tables: angle p * theta^(-2j/Dh) in double precision, stored as float.
+void rope_tables(const mk_config& cfg, std::vector<float>* cs, std::vector<float>* sn) {
+  const int half = cfg.head_dim / 2;
+  cs->resize(size_t(cfg.max_seq) * half);
+  sn->resize(size_t(cfg.max_seq) * half);
+  for (int j = 0; j < half; j++) {
+    const double inv = std::pow(double(cfg.rope_theta), -2.0 * j / cfg.head_dim);
+    for (int p = 0; p < cfg.max_seq; p++) {
+      const double ang = double(p) * inv;
+      (*cs)[size_t(p) * half + j] = float(std::cos(ang));
+      (*sn)[size_t(p) * half + j] = float(std::sin(ang));
+    }
+  }
+}
+
+bool dense_pointers_ok(const mk_weights& w) {
+  return w.embed && w.final_norm && w.attn_norm && w.wq && w.wk && w.wv && w.wo && w.mlp_norm &&
+         w.w_gate && w.w_up && w.w_down && w.k_cache && w.v_cache;
+}
+}  // namespace
+
+extern "C" {
+
+mk_status mk_create(const mk_config* cfg, const mk_weights* w, int device, mk_ctx** out) {
+  if (!out) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_create: out is NULL");
+  *out = nullptr;
+  if (!cfg || !w) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_create: cfg and w are required");
+  std::string err;
+  mk_status st = mk::check_config(*cfg, &err);
+  if (st != MK_OK) return fail(nullptr, st, err);
+  if (!dense_pointers_ok(*w)) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_create: a weight or cache pointer is NULL");
+  if (!w->lm_head && !cfg->tied_embedding)
+    return fail(nullptr, MK_ERR_INVALID_ARG, "mk_create: lm_head is NULL and the embedding is not tied");
+  int n_dev = 0;
+  hipError_t e = hipGetDeviceCount(&n_dev);
+  if (e != hipSuccess || n_dev <= 0) return fail(nullptr, MK_ERR_HIP, "mk_create: no HIP device");
+  if (device < 0 || device >= n_dev) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_create: bad device index");
+  if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(nullptr, e, "hipSetDevice");
+  hipDeviceProp_t prop;
+  if ((e = hipGetDeviceProperties(&prop, device)) != hipSuccess) return hip_fail(nullptr, e, "hipGetDeviceProperties");
+  if (size_t(prop.maxSharedMemoryPerMultiProcessor) < size_t(mk::kLdsTotal))
+    return fail(nullptr, MK_ERR_UNSUPPORTED, "mk_create: device has too little LDS per CU");
+  mk_ctx* c = new mk_ctx();
+  c->cfg = *cfg;
+  c->w = *w;
+  if (!c->w.lm_head) c->w.lm_head = c->w.embed;
+  c->device = device;
+  c->dev_cus = prop.multiProcessorCount;
+  const char* nc = std::getenv("MK_NONCOOP");
+  c->cooperative = (nc && nc[0] == '1') ? 0 : 1;
+  rope_tables(c->cfg, &c->rope_cos, &c->rope_sin);
+  *out = c;
+  return MK_OK;
+}
+
+mk_status mk_build_plan(mk_ctx* c, const mk_plan_opts* opts) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_build_plan: ctx is NULL");
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
+  if (c->has_step) (void)hipStreamSynchronize(c->last_stream);
+  free_plan(c);
+  int n_cus = (opts && opts->n_cus > 0) ? opts->n_cus : c->dev_cus;
+  if (n_cus > c->dev_cus) return fail(c, MK_ERR_INVALID_ARG, "mk_build_plan: n_cus exceeds the device's CUs");
+  mk::PlanInput& in = c->pin;
+  in.cfg = c->cfg;
+  in.opts = mk::resolve_opts(c->cfg, opts, n_cus);
+  in.n_cus = n_cus;
+  in.w = c->w;
+  if (in.opts.attn_block <= 0 || in.opts.attn_block % 64)
+    return fail(c, MK_ERR_INVALID_ARG, "mk_build_plan: attn_block must be a positive multiple of 64");
+  const int nblk = (c->cfg.max_seq + in.opts.attn_block - 1) / in.opts.attn_block;
+  const mk::ArenaLayout lay = mk::arena_layout(c->cfg, n_cus, c->cfg.n_kv_heads * nblk);
+  if ((e = hipMalloc(&c->arena, lay.total)) != hipSuccess) return hip_fail(c, e, "hipMalloc(arena)");
+  in.arena_base = uint64_t(c->arena);
+  std::string err;
+  mk_status st = mk::build_plan(in, &c->plan, &err);
+  if (st == MK_OK) st = mk::verify_plan(in, c->plan, &err);
+  if (st != MK_OK) {
+    free_plan(c);
+    return fail(c, st, err);
+  }
+  if (in.opts.debug_corrupt_target) mk::corrupt_one_target(&c->plan);
+  const mk::Plan& p = c->plan;
+  (void)hipMemset(c->arena, 0, lay.total);
+  e = hipMemcpy(c->arena + p.arena.rope_cos, c->rope_cos.data(), c->rope_cos.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(c->arena + p.arena.rope_sin, c->rope_sin.data(), c->rope_sin.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMalloc(&c->d_instrs, std::max<size_t>(1, p.instrs.size()) * sizeof(mk::Instr));
+  if (e == hipSuccess)
+    e = hipMemcpy(c->d_instrs, p.instrs.data(), p.instrs.size() * sizeof(mk::Instr), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMalloc(&c->d_qoff, p.q_off.size() * 4);
+  if (e == hipSuccess) e = hipMemcpy(c->d_qoff, p.q_off.data(), p.q_off.size() * 4, hipMemcpyHostToDevice);
+  const size_t ctr_bytes = size_t(std::max(1, p.n_counters)) * mk::kCtrStride * 4;
+  if (e == hipSuccess) e = hipMalloc(&c->d_counters, ctr_bytes);
+  if (e == hipSuccess) e = hipMemset(c->d_counters, 0, ctr_bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    free_plan(c);
+    return hip_fail(c, e, "mk_build_plan upload");
+  }
+  c->epoch = 0;
+  c->planned = true;
+  return MK_OK;
+}
+
+mk_status mk_decode_step(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_t* d_next,
+                         float* d_logits, void* stream) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_decode_step: ctx is NULL");
+  if (!c->planned) return fail(c, MK_ERR_NO_PLAN, "mk_decode_step: call mk_build_plan first");
+  if (!d_tokens || !d_next) return fail(c, MK_ERR_INVALID_ARG, "mk_decode_step: tokens and next are required");
+  if (pos < 0 || pos >= c->cfg.max_seq) return fail(c, MK_ERR_INVALID_ARG, "mk_decode_step: pos outside [0, max_seq)");
+  const mk::Plan& p = c->plan;
+  mk::KArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.instrs = c->d_instrs;
+  a.q_off = c->d_qoff;
+  a.counters = c->d_counters;
+  a.status = reinterpret_cast<uint32_t*>(c->arena + p.arena.status);
+  a.tokens = d_tokens;
+  a.next = d_next;
+  a.logits = d_logits;
+  a.rope_cos = reinterpret_cast<const float*>(c->arena + p.arena.rope_cos);
+  a.rope_sin = reinterpret_cast<const float*>(c->arena + p.arena.rope_sin);
+  a.lm_slots = reinterpret_cast<float*>(c->arena + p.arena.lm_slots);
+  a.zero_page = c->arena + p.arena.zero_page;
+  a.epoch = c->epoch + 1;
+  a.pos = pos;
+  a.vocab = c->cfg.vocab;
+  a.hidden = c->cfg.hidden;
+  a.head_dim = c->cfg.head_dim;
+  a.hpg = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+  a.q_dim = c->cfg.n_q_heads * c->cfg.head_dim;
+  a.kv_dim = c->cfg.n_kv_heads * c->cfg.head_dim;
+  a.max_seq = c->cfg.max_seq;
+  a.rms_eps = c->cfg.rms_eps;
+  a.attn_scale = float(1.0 / std::sqrt(double(c->cfg.head_dim)));
+  a.watchdog_ticks = uint64_t(c->pin.opts.watchdog_ms) * 100000ull;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = mk_launch_megakernel(&a, p.n_cus, s, c->cooperative);
+  if (e != hipSuccess) return hip_fail(c, e, "launch");
+  c->epoch++;
+  c->last_stream = s;
+  c->has_step = true;
+  return MK_OK;
+}
+
+mk_status mk_sync(mk_ctx* c) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_sync: ctx is NULL");
+  if (!c->planned || !c->has_step) return MK_OK;
+  hipError_t e = hipStreamSynchronize(c->last_stream);
+  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  uint32_t stw[8];
+  e = hipMemcpy(stw, c->arena + c->plan.arena.status, sizeof(stw), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(c, e, "status readback");
+  if (stw[mk::ST_CODE] == 0 && stw[mk::ST_NAN] == 0 && stw[mk::ST_BADTOK] == 0) return MK_OK;
+  char msg[256];
+  mk_status st;
+  if (stw[mk::ST_CODE] == mk::STC_TIMEOUT) {
+    std::snprintf(msg, sizeof(msg),
+                  "watchdog: CU %u instruction %u waited on counter %u (seen %u, target %u)",
+                  stw[mk::ST_CU], stw[mk::ST_INSTR], stw[mk::ST_CTR], stw[mk::ST_SEEN], stw[mk::ST_TARGET]);
+    st = MK_ERR_TIMEOUT;
+  } else if (stw[mk::ST_CODE] == mk::STC_LOCAL_TIMEOUT) {
+    std::snprintf(msg, sizeof(msg), "watchdog: a workgroup stalled on its own LDS pages or barrier");
+    st = MK_ERR_TIMEOUT;
+  } else if (stw[mk::ST_BADTOK]) {
+    std::snprintf(msg, sizeof(msg), "device: input token outside [0, vocab)");
+    st = MK_ERR_DEVICE;
+  } else {
+    std::snprintf(msg, sizeof(msg), "device: NaN logits in the LM head");
+    st = MK_ERR_DEVICE;
+  }
+  // reset so the context can be used again
+  const size_t ctr_bytes = size_t(std::max(1, c->plan.n_counters)) * mk::kCtrStride * 4;
+  (void)hipMemset(c->d_counters, 0, ctr_bytes);
+  (void)hipMemset(c->arena + c->plan.arena.status, 0, 64);
+  (void)hipDeviceSynchronize();
+  c->epoch = 0;
+  return fail(c, st, msg);
+}
+
+mk_status mk_destroy(mk_ctx* c) {
+  if (!c) return MK_OK;
+  (void)hipSetDevice(c->device);
+  if (c->has_step) (void)hipStreamSynchronize(c->last_stream);
+  free_plan(c);
+  delete c;
+  return MK_OK;
+}
+
+const char* mk_last_error(const mk_ctx* c) { return c ? c->err.c_str() : g_err.c_str(); }
+
+mk_status mk_plan_info(const mk_ctx* c, mk_plan_summary* out) {
+  if (!c || !out) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_plan_info: NULL argument");
+  if (!c->planned) return fail(const_cast<mk_ctx*>(c), MK_ERR_NO_PLAN, "mk_plan_info: no plan");
+  mk::summarize(c->pin, c->plan, out);
+  return MK_OK;
+}
+
+mk_status mk_plan_check(const mk_config* cfg, const mk_plan_opts* opts, int32_t n_cus,
+                        mk_plan_summary* summary, char* report, size_t report_len) {
+  if (!cfg) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_plan_check: cfg is NULL");
+  if (n_cus <= 0) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_plan_check: n_cus must be positive");
+  std::string err;
+  mk_status st = mk::check_config(*cfg, &err);
+  if (st != MK_OK) return fail(nullptr, st, err);
+  mk::PlanInput in;
+  in.cfg = *cfg;
+  in.opts = mk::resolve_opts(*cfg, opts, n_cus);
+  in.n_cus = n_cus;
+  // distinct fake device addresses: only the structure is checked
+  uintptr_t base = uintptr_t(1) << 40;
+  const void** fields[] = {&in.w.embed, &in.w.lm_head, &in.w.final_norm, &in.w.attn_norm, &in.w.wq,
+                           &in.w.wk, &in.w.wv, &in.w.wo, &in.w.mlp_norm, &in.w.w_gate, &in.w.w_up,
+                           &in.w.w_down, &in.w.router, &in.w.e_gate, &in.w.e_up, &in.w.e_down};
+  for (size_t i = 0; i < sizeof(fields) / sizeof(fields[0]); i++)
+    *fields[i] = reinterpret_cast<const void*>(base * (i + 1));
+  in.w.k_cache = reinterpret_cast<void*>(base * 20);
+  in.w.v_cache = reinterpret_cast<void*>(base * 21);
+  in.arena_base = uint64_t(base) * 30;
+  mk::Plan p;
+  st = mk::build_plan(in, &p, &err);
+  if (st == MK_OK && in.opts.debug_corrupt_target) mk::corrupt_one_target(&p);
+  if (st == MK_OK) st = mk::verify_plan(in, p, &err);
+  if (st != MK_OK) return fail(nullptr, st, err);
+  if (summary) mk::summarize(in, p, summary);
+  if (report && report_len) {
+    std::string r = mk::plan_report(in, p);
+    std::snprintf(report, report_len, "%s", r.c_str());
+  }
+  return MK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+"""GPU parity of the megakernel decode step against the CPU oracle.
+
+Bar (per step and sequence): logits within relative L2 error 1e-2 of the
+oracle, the same greedy token, and appended K/V rows within one bf16 step.
+Every case prints its name and shape first, so a failing run names it."""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import DecoderOracle, bf16_to_f64
+from persistent_megakernel_wg_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2       # contract
+TIGHT = 1e-4     # fp32 accumulation over these sizes stays far below this
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b))
+
+
+def _engine(shape, w, kc, vc, **opts):
+    from persistent_megakernel_wg_amd import binding as B
+    from persistent_megakernel_wg_amd.engine import Engine
+    return Engine(shape, w, kc, vc, plan=B.plan_opts(**opts) if opts else None)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def kv_rows_close(got_bits, ref_bits):
+    """Appended rows agree within one bf16 step of the larger magnitude, plus a
+    floor of 1e-5 of the row's RMS for values that round across zero."""
+    a, b = bf16_to_f64(got_bits), bf16_to_f64(ref_bits)
+    big = np.maximum(np.abs(a), np.abs(b))
+    step = np.exp2(np.floor(np.log2(np.maximum(big, 1e-30))) - 7)
+    floor = 1e-5 * np.sqrt(np.mean(b * b, axis=-1, keepdims=True))
+    return bool(np.all(np.abs(a - b) <= step + floor))
+
+
+def _check_kv(shape, kg, vg, k_ref, v_ref, pos):
+    # appended rows within one bf16 step, every other row untouched
+    for got, ref in ((kg, k_ref), (vg, v_ref)):
+        assert kv_rows_close(got[:, :, :, pos], ref[:, :, :, pos])
+        mask = np.ones(shape.max_seq, bool)
+        mask[pos] = False
+        assert np.array_equal(got[:, :, :, mask], ref[:, :, :, mask])
+
+
+def _one_step_case(shape, pos=None, tok=None, **opts):
+    _say("case %s pos=%s opts=%s" % (shape.name, pos, opts))
+    w = synth.make_weights(shape)
+    kc, vc = synth.make_kv_cache(shape, prefill=pos)
+    tok = synth.make_tokens(shape) if tok is None else np.array([tok], np.int32)
+    p = shape.prefill if pos is None else pos
+    eng = _engine(shape, w, kc, vc, **opts)
+    try:
+        lg, nx = eng.step(tok, p)
+        kg, vg = eng.read_kv()
+    finally:
+        eng.close()
+    k_ref, v_ref = kc.copy(), vc.copy()
+    ref_lg, ref_nx = DecoderOracle(shape, w).step(tok, p, k_ref, v_ref)
+    err = rel_l2(lg[0], ref_lg[0])
+    _say("  rel_l2 %.3e  next %d / oracle %d" % (err, nx[0], ref_nx[0]))
+    assert err <= TOL and err <= TIGHT
+    assert nx[0] == ref_nx[0]
+    _check_kv(shape, kg, vg, k_ref, v_ref, p)
+
+
+def test_tiny_step_default_plan(need_gpu):
+    _one_step_case(synth.SHAPES["tiny"])
+
+
+def test_tiny_step_split_attention(need_gpu):
+    # two KV blocks per group: the last-arriving tile merges the partials
+    _one_step_case(synth.SHAPES["tiny"], attn_block=64)
+
+
+def test_tiny_step_few_cus_one_chunk(need_gpu):
+    # several items per wave and per CU, single-chunk down projection
+    _one_step_case(synth.SHAPES["tiny"], n_cus=7, mlp_chunks=1)
+
+
+def test_tiny_step_two_chunks_odd_cus(need_gpu):
+    _one_step_case(synth.SHAPES["tiny"], n_cus=37, mlp_chunks=2, attn_block=64)
+
+
+def test_tiny_empty_cache_position_zero(need_gpu):
+    # attention over the single new row returns its value row
+    _one_step_case(synth.SHAPES["tiny"], pos=0)
+
+
+def test_tiny_last_position(need_gpu):
+    s = synth.SHAPES["tiny"]
+    _one_step_case(s, pos=s.max_seq - 1, attn_block=64)
+
+
+def test_tiny_greedy_chain_on_device(need_gpu):
+    from persistent_megakernel_wg_amd.engine import Engine
+    s = synth.SHAPES["tiny"]
+    _say("case tiny greedy 8 steps")
+    w = synth.make_weights(s)
+    kc, vc = synth.make_kv_cache(s)
+    tok = synth.make_tokens(s)
+    eng = Engine(s, w, kc, vc)
+    try:
+        lgs, toks = eng.generate(tok, s.prefill, 8, logits=True)
+    finally:
+        eng.close()
+    orc = DecoderOracle(s, w)
+    k_ref, v_ref = kc.copy(), vc.copy()
+    t = tok
+    for i in range(8):
+        ref_lg, ref_nx = orc.step(t, s.prefill + i, k_ref, v_ref)
+        assert rel_l2(lgs[i][0], ref_lg[0]) <= TIGHT
+        assert toks[i][0] == ref_nx[0], (i, toks[i][0], ref_nx[0])
+        t = ref_nx
+
+
+def test_tiny_repeat_is_bitwise_deterministic(need_gpu):
+    from persistent_megakernel_wg_amd.engine import Engine
+    s = synth.SHAPES["tiny"]
+    w = synth.make_weights(s)
+    kc, vc = synth.make_kv_cache(s)
+    tok = synth.make_tokens(s)
+    eng = Engine(s, w, kc, vc)
+    try:
+        outs = [eng.step(tok, s.prefill)[0] for _ in range(5)]
+    finally:
+        eng.close()
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_abi_errors(need_gpu):
+    from persistent_megakernel_wg_amd import binding as B
+    from persistent_megakernel_wg_amd.engine import Engine
+    s = synth.SHAPES["tiny"]
+    w = synth.make_weights(s)
+    kc, vc = synth.make_kv_cache(s)
+    eng = Engine(s, w, kc, vc)
+    try:
+        with pytest.raises(B.MkError) as e:
+            B.mk_decode_step(eng.ctx, eng.tokens.data_ptr(), s.max_seq, eng.next.data_ptr())
+        assert e.value.status == -1
+        with pytest.raises(B.MkError) as e:
+            B.mk_decode_step(eng.ctx, 0, 3, eng.next.data_ptr())
+        assert e.value.status == -1
+    finally:
+        eng.close()
+    B.mk_destroy(None)
+
+
+def test_watchdog_turns_a_stuck_wait_into_an_error(need_gpu):
+    from persistent_megakernel_wg_amd import binding as B
+    from persistent_megakernel_wg_amd.engine import Engine
+    s = synth.SHAPES["tiny"]
+    _say("case watchdog (one wait target raised by one)")
+    w = synth.make_weights(s)
+    kc, vc = synth.make_kv_cache(s)
+    tok = synth.make_tokens(s)
+    eng = Engine(s, w, kc, vc, plan=B.plan_opts(debug_corrupt_target=1, watchdog_ms=200))
+    try:
+        eng.tokens.copy_(eng.torch.from_numpy(tok))
+        eng.launch(s.prefill)
+        with pytest.raises(B.MkError) as e:
+            eng.sync()
+        assert e.value.status == -6
+        # the context is usable again with a correct plan
+        eng.rebuild_plan()
+        _, nx = eng.step(tok, s.prefill)
+        k_ref, v_ref = kc.copy(), vc.copy()
+        _, ref_nx = DecoderOracle(s, w).step(tok, s.prefill, k_ref, v_ref)
+        assert nx[0] == ref_nx[0]
+    finally:
+        eng.close()

@@ -1,0 +1,87 @@
+"""Host-side tests of libmk.so: exported symbols, the planner and its verifier,
+and argument checking.  No GPU needed (no compute call is made)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from persistent_megakernel_wg_amd import binding as B
+from persistent_megakernel_wg_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DENSE = ["tiny", "llama1b_ctx128", "llama1b_ctx8192", "llama8b_ctx2048"]
+
+
+def _cfg(name, **kw):
+    return B.config_from_shape(synth.SHAPES[name].replace(**kw))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = B.load_library()
+    with open(os.path.join(ROOT, "include", "mk.h")) as fh:
+        header = fh.read()
+    declared = set(re.findall(r"^(?:mk_status|const char \*)\s*(mk_\w+)\s*\(", header, re.M))
+    assert declared == set(B.EXPORTS)
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+@pytest.mark.parametrize("name", DENSE)
+def test_default_plan_verifies(name):
+    s = synth.SHAPES[name]
+    summ, rep = B.mk_plan_check(B.config_from_shape(s), 256)
+    r = json.loads(rep)
+    assert summ["n_cus"] == 256 and len(r["queue_lengths"]) == 256
+    assert summ["weight_bytes"] == synth.weight_bytes_per_step(s)
+    assert summ["mlp_chunks"] == 4
+    assert summ["lds_bytes"] <= 160 * 1024
+    # every CU streams about the same number of bytes (the tiny decoder has
+    # fewer rows than there are CUs, so it cannot be balanced)
+    if name != "tiny":
+        assert summ["max_cu_bytes"] <= 1.25 * summ["min_cu_bytes"]
+
+
+@pytest.mark.parametrize("name,n_cus,opts", [
+    ("tiny", 1, {}), ("tiny", 7, {"mlp_chunks": 1}), ("tiny", 37, {"attn_block": 64}),
+    ("tiny", 256, {"mlp_chunks": 2, "attn_block": 64}),
+    ("llama1b_ctx128", 100, {"attn_block": 64}), ("llama1b_ctx8192", 256, {"attn_block": 128}),
+    ("llama8b_ctx2048", 128, {}),
+])
+def test_plan_variants_verify(name, n_cus, opts):
+    B.mk_plan_check(_cfg(name), n_cus, B.plan_opts(**opts))
+
+
+def test_verifier_rejects_a_wrong_counter_target():
+    with pytest.raises(B.MkError) as e:
+        B.mk_plan_check(_cfg("tiny"), 64, B.plan_opts(debug_corrupt_target=1))
+    assert e.value.status == -1 and "waits for" in str(e.value)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"head_dim": 96}, -4), ({"n_kv_heads": 3}, -1), ({"batch": 2}, -4),
+    ({"n_experts": 4, "top_k": 2, "expert_ffn": 512}, -4), ({"hidden": 384}, -4),
+    ({"n_layers": 0}, -1),
+])
+def test_unsupported_or_bad_shapes_are_rejected(kw, status):
+    with pytest.raises(B.MkError) as e:
+        B.mk_plan_check(_cfg("tiny", **kw), 64)
+    assert e.value.status == status
+
+
+@pytest.mark.parametrize("opts", [{"attn_block": 100}, {"mlp_chunks": 3}, {"attn_block": 1024}])
+def test_bad_plan_options_are_rejected(opts):
+    with pytest.raises(B.MkError):
+        B.mk_plan_check(_cfg("tiny"), 64, B.plan_opts(**opts))
+
+
+def test_null_arguments():
+    lib = B.load_library()
+    assert lib.mk_destroy(None) == 0
+    out = ctypes.c_void_p()
+    assert lib.mk_create(None, None, 0, ctypes.byref(out)) == -1
+    assert "required" in B.mk_last_error()
+    assert lib.mk_build_plan(None, None) == -1
+    assert lib.mk_decode_step(None, None, 0, None, None, None) == -1
+    assert lib.mk_sync(None) == -1
