@@ -170,6 +170,18 @@ mk_status mk_plan_info(const mk_ctx *ctx, mk_plan_summary *out);
 mk_status mk_plan_check(const mk_config *cfg, const mk_plan_opts *opts, int32_t n_cus,
                         mk_plan_summary *summary, char *report, size_t report_len);
 
+/* ---- diagnostics -------------------------------------------------------
+ * Per-instruction timestamps of the next steps (s_memrealtime, 100 MHz, low
+ * 32 bits): for every CU and queue slot 8 words
+ *   {start, deps satisfied, inputs staged, leader's items done, signal,
+ *    leader's page-wait ticks, header word 0, header word 1}.
+ * mk_trace_enable allocates (on != 0) or frees the trace buffer; it costs a
+ * few stores per instruction.  mk_trace_read copies it to host memory
+ * (n_words >= n_cus * stride * 8) after mk_sync; *stride receives the slots
+ * per CU.  Errors: MK_ERR_NO_PLAN, MK_ERR_INVALID_ARG, MK_ERR_HIP. */
+mk_status mk_trace_enable(mk_ctx *ctx, int on);
+mk_status mk_trace_read(mk_ctx *ctx, uint32_t *host, size_t n_words, int32_t *stride);
+
 #ifdef __cplusplus
 }
 #endif

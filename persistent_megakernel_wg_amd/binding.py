@@ -58,7 +58,7 @@ class MkPlanSummary(ctypes.Structure):
 
 
 EXPORTS = ("mk_create", "mk_build_plan", "mk_decode_step", "mk_sync", "mk_destroy",
-           "mk_last_error", "mk_plan_info", "mk_plan_check")
+           "mk_last_error", "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -83,8 +83,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_plan_info.argtypes = [vp, ctypes.POINTER(MkPlanSummary)]
     lib.mk_plan_check.argtypes = [ctypes.POINTER(MkConfig), ctypes.POINTER(MkPlanOpts), i32,
                                   ctypes.POINTER(MkPlanSummary), ctypes.c_char_p, ctypes.c_size_t]
+    lib.mk_trace_enable.argtypes = [vp, ctypes.c_int]
+    lib.mk_trace_read.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), ctypes.c_size_t,
+                                  ctypes.POINTER(i32)]
     for name in ("mk_create", "mk_build_plan", "mk_decode_step", "mk_sync", "mk_destroy",
-                 "mk_plan_info", "mk_plan_check"):
+                 "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read"):
         getattr(lib, name).restype = st
     _lib = lib
     return lib
@@ -158,3 +161,18 @@ def mk_plan_check(cfg: MkConfig, n_cus: int, opts: Optional[MkPlanOpts] = None):
                                          ctypes.byref(opts) if opts is not None else None,
                                          n_cus, ctypes.byref(s), buf, len(buf)))
     return s.as_dict(), buf.value.decode()
+
+
+def mk_trace_enable(ctx: int, on: bool = True) -> None:
+    _check(load_library().mk_trace_enable(ctx, int(on)), ctx)
+
+
+def mk_trace_read(ctx: int, n_cus: int, max_queue: int):
+    """Trace of the last step as a uint32 array [n_cus, stride, 8]."""
+    import numpy as np
+    buf = np.zeros(n_cus * max_queue * 8, dtype=np.uint32)
+    stride = ctypes.c_int32()
+    _check(load_library().mk_trace_read(
+        ctx, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), buf.size,
+        ctypes.byref(stride)), ctx)
+    return buf[: n_cus * stride.value * 8].reshape(n_cus, stride.value, 8)

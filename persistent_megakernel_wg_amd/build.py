@@ -33,7 +33,8 @@ def _run(cmd, verbose):
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines()
-                    if "packed-fp32-ops" not in l and "is not a recognized feature" not in l)
+                    if "packed-fp32-ops" not in l and "is not a recognized feature" not in l
+                    and "reserved registers" not in l)
     if r.returncode != 0:
         raise RuntimeError("build step failed: %s\n%s" % (" ".join(cmd), out))
     if verbose and out.strip():

@@ -32,7 +32,10 @@ constexpr int kLdsXBytes = 4 * kMaxK;
 constexpr int kLdsAttn = kLdsX + kLdsXBytes;   // attention scratch
 constexpr int kLdsAttnBytes = 12800;   // scores 8 KiB, new V row 512 B, partials 4 KiB
 constexpr int kLdsPages = kLdsAttn + kLdsAttnBytes;
-constexpr int kLdsTotal = kLdsPages + kPages * kPageBytes;   // 162304
+// staged residual rows: two slots (by instruction parity) of 128 floats
+constexpr int kLdsRes = kLdsPages + kPages * kPageBytes;
+constexpr int kMaxResRows = 128;
+constexpr int kLdsTotal = kLdsRes + 2 * 4 * kMaxResRows;      // 163328
 constexpr int kAttnScoreFloats = 2048;                       // 8 KiB of scores
 
 // ------------------------------------------------------------------- opcodes
@@ -130,7 +133,13 @@ struct KArgs {
   float rms_eps;
   float attn_scale;         // 1/sqrt(Dh)
   uint64_t watchdog_ticks;  // s_memrealtime ticks (100 MHz)
+  uint32_t* trace;          // [n_cus][trace_stride][8] timestamps, or null
+  uint32_t trace_stride;    // instructions per CU in the trace buffer
 };
+
+// trace record words (s_memrealtime, 100 MHz, low 32 bits)
+enum TraceWord { TR_START = 0, TR_DEPS = 1, TR_STAGED = 2, TR_ITEMS = 3, TR_SIGNAL = 4,
+                 TR_PAGEWAIT = 5, TR_HW0 = 6, TR_HW1 = 7, TR_WORDS = 8 };
 
 // status words
 enum StatusWord { ST_CODE = 0, ST_CU = 1, ST_INSTR = 2, ST_CTR = 3, ST_SEEN = 4, ST_TARGET = 5,

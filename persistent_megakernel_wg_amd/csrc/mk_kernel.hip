@@ -95,6 +95,9 @@ DEV uint32_t* status_ptr() {
 }
 DEV uint64_t local_limit() { return (uint64_t(*lw(C_LIMIT_HI)) << 32) | *lw(C_LIMIT_LO); }
 DEV uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+DEV uint64_t uni64(uint64_t v) {
+  return (uint64_t(uni(uint32_t(v >> 32))) << 32) | uni(uint32_t(v));
+}
 DEV uint32_t page_off(uint32_t g) { return kLdsPages + (g & (kPages - 1)) * kPageBytes; }
 
 // ------------------------------------------------------ global memory access
@@ -171,16 +174,51 @@ DEV float dot8(u4 w, const float* x) {
   return a + b;
 }
 
-template <int LPR>
-DEV float reduce_lanes(float v) {
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m, 64);
+// Cross-lane reductions with DPP (quad permutes and row rotates/shifts inside
+// 16-lane rows) and readlane across rows.  Fixed order: deterministic.
+template <int CTRL>
+DEV float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+DEV float rl(float v, int lane) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane)); }
+// every lane receives the sum of its 16-lane row
+DEV float row_sum16(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
   return v;
 }
-DEV float wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+// wave-uniform sum of all 64 lanes
+DEV float sum64(float v) {
+  v = row_sum16(v);
+  return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
+}
+// sums of lanes [0,32) and [32,64)
+DEV void sum32x2(float v, float& lo, float& hi) {
+  v = row_sum16(v);
+  lo = rl(v, 0) + rl(v, 16);
+  hi = rl(v, 32) + rl(v, 48);
+}
+// sum over aligned groups of G (8 or 16) lanes, valid in the group's first lane
+template <int G>
+DEV float group_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x104>(v);              // row_shl:4
+  if (G == 16) v += dpp<0x108>(v); // row_shl:8
   return v;
+}
+template <int CTRL>
+DEV float dpp_max(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+DEV float max64(float v) {
+  v = fmaxf(v, dpp_max<0xB1>(v));
+  v = fmaxf(v, dpp_max<0x4E>(v));
+  v = fmaxf(v, dpp_max<0x124>(v));
+  v = fmaxf(v, dpp_max<0x128>(v));
+  return fmaxf(fmaxf(rl(v, 0), rl(v, 16)), fmaxf(rl(v, 32), rl(v, 48)));
 }
 
 // ----------------------------------------------------------------- watchdog
@@ -211,10 +249,9 @@ DEV bool wait_counter(const KArgs& a, uint32_t ctr, uint32_t target, int cu, uin
       record_timeout(a, cu, instr, ctr, v, target);
       return false;
     }
-    if ((it & 63) == 63 &&
+    if ((it & 255) == 255 &&
         __hip_atomic_load(a.status + ST_CODE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
       return false;
-    __builtin_amdgcn_s_sleep(1);
   }
 }
 
@@ -278,33 +315,31 @@ DEV bool comp_barrier() {
 }
 
 // ================================================================== loader
+// One wave-wide 16 B/lane DMA from global memory into LDS at M0.  M0 is set
+// per DMA and not restored: the loader waves use M0 for nothing else, and
+// writing M0 back right after an LDS DMA stalls issue until that DMA has been
+// accepted, which cut the streaming rate by more than half.
+#ifndef MK_DMA_NOP
+#define MK_DMA_NOP "s_nop 0"
+#endif
 DEV void dma_uniform(uint32_t lds_addr, uint64_t src, uint32_t voff) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %0\n\t" MK_DMA_NOP "\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
       : "s"(lds_addr), "v"(voff), "s"(src)
-      : "memory");
+      : "memory", "m0");
 }
 DEV void dma_lane(uint32_t lds_addr, uint64_t src) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %0\n\t" MK_DMA_NOP "\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
       : "s"(lds_addr), "v"(src)
-      : "memory");
+      : "memory", "m0");
 }
 
 constexpr uint32_t kDmaPerPage = kUnitsPerPage / kNLoad;  // 8
-constexpr uint32_t kMaxOut = 7;                           // pages in flight per loader
 
 // wait until at most `pages_after` pages of this loader's DMA are in flight
 DEV void wait_vm_pages(uint32_t pages_after) {
@@ -321,16 +356,6 @@ DEV void wait_vm_pages(uint32_t pages_after) {
   }
 }
 
-struct LoaderState {
-  uint32_t g_issue, g_pub, min_rel;
-};
-
-DEV void publish_oldest(LoaderState& s, int v) {
-  wait_vm_pages(s.g_issue - s.g_pub - 1);
-  s.g_pub++;
-  if ((threadIdx.x & 63) == 0) lds_st(C_FILLED + 4 * v, s.g_pub);
-}
-
 DEV uint32_t min_released() {
   uint32_t m = lds_ld(C_RELEASED);
 #pragma unroll
@@ -338,99 +363,222 @@ DEV uint32_t min_released() {
   return m;
 }
 
-// source address of stream row r (uniform)
-DEV uint64_t row_src(InstrCP I, uint32_t r, uint32_t interleave) {
-  if (interleave) {
-    const uint32_t s = r & 1, i = r >> 1;
-    return I->seg_ptr[s] + uint64_t(i) * I->seg_stride[s];
-  }
-  uint32_t r0 = I->seg_rows[0];
-  if (r < r0) return I->seg_ptr[0] + uint64_t(r) * I->seg_stride[0];
-  r -= r0;
-  uint32_t r1 = I->seg_rows[1];
-  if (r < r1) return I->seg_ptr[1] + uint64_t(r) * I->seg_stride[1];
-  r -= r1;
-  return I->seg_ptr[2] + uint64_t(r) * I->seg_stride[2];
-}
+// Per-instruction loader view: every field the DMA address arithmetic needs,
+// loaded once into registers (the DMA asm clobbers memory, so fields read
+// through the instruction pointer would be reloaded for every DMA).
+struct LoadView {
+  uint64_t seg[3];
+  uint32_t rows0, rows1, stride[3];
+  uint32_t op, nit, rpu, inter, rb, stream_units, kp;
+  uint64_t kv_base[2];
+  uint32_t valid_bytes;
+};
 
-// Issue this loader's share (units v, v + kNLoad, ...) of page p of instruction I.
-DEV void issue_page(const KArgs& a, InstrCP I, uint32_t p, uint32_t g, int v, uint32_t lane) {
-  const uint32_t ldsbase = uint32_t(size_t(lds)) + page_off(g);
-  const uint64_t zero = uint64_t(a.zero_page);
-  if (i_op(I) == OP_GEMV) {
-    const uint32_t nit = i_nit(I), rpu = i_rpu(I), rb = I->row_bytes;
-    const uint32_t stream_units = (I->n_rows * rb + kUnit - 1) / kUnit;
-    const uint32_t inter = i_flags(I) & F_INTERLEAVE;
-    for (uint32_t k = v; k < kUnitsPerPage; k += kNLoad) {
-      const uint32_t u = p * kUnitsPerPage + k;
-      const uint32_t dst = ldsbase + k * kUnit;
-      if (u >= stream_units) {
-        dma_uniform(dst, zero, lane * 16);
-      } else if (rpu == 1) {
-        const uint32_t r = u / nit, part = u - r * nit;
-        dma_uniform(dst, row_src(I, r, inter) + part * kUnit, lane * 16);
-      } else {
-        // 512 B rows: lanes 0-31 read row 2u, lanes 32-63 row 2u+1
-        const uint32_t r0 = 2 * u;
-        const uint64_t s0 = row_src(I, r0, inter), s1 = row_src(I, r0 + 1, inter);
-        const uint64_t src = (lane < 32 ? s0 : s1) + (lane & 31) * 16;
-        dma_lane(dst, src);
-      }
-    }
-  } else {  // OP_ATTN: K block region then V block region, rows < n_cached valid
-    const uint32_t kp = I->aux[4];
+DEV void load_view(const KArgs& a, InstrCP I, LoadView& L) {
+  L.op = i_op(I);
+  L.nit = i_nit(I);
+  L.rpu = i_rpu(I);
+  L.inter = i_flags(I) & F_INTERLEAVE;
+  L.rb = I->row_bytes;
+  L.stream_units = (I->n_rows * L.rb + kUnit - 1) / kUnit;
+  for (int k = 0; k < 3; k++) {
+    L.seg[k] = I->seg_ptr[k];
+    L.stride[k] = I->seg_stride[k];
+  }
+  L.rows0 = I->seg_rows[0];
+  L.rows1 = I->seg_rows[1];
+  L.kp = I->aux[4];
+  if (L.op == OP_ATTN) {
     const int32_t p0 = int32_t(I->aux[1] * I->aux[2]);
     int32_t nc = a.pos - p0;
     nc = nc < 0 ? 0 : (nc > int32_t(I->aux[2]) ? int32_t(I->aux[2]) : nc);
-    const uint32_t valid_bytes = uint32_t(nc) * I->row_bytes;
-    const uint32_t region = p < kp ? 0 : 1;
-    const uint32_t pp = p - region * kp;
-    const uint64_t base = I->seg_ptr[region] + uint64_t(p0) * I->row_bytes;
-    for (uint32_t k = v; k < kUnitsPerPage; k += kNLoad) {
-      const uint32_t off = (pp * kUnitsPerPage + k) * kUnit;
+    L.valid_bytes = uint32_t(nc) * L.rb;
+    L.kv_base[0] = L.seg[0] + uint64_t(p0) * L.rb;
+    L.kv_base[1] = L.seg[1] + uint64_t(p0) * L.rb;
+  }
+}
+
+// source address of stream row r (uniform)
+DEV uint64_t row_src(const LoadView& L, uint32_t r) {
+  if (L.inter) {
+    const uint32_t sg = r & 1, i = r >> 1;
+    return (sg ? L.seg[1] : L.seg[0]) + uint64_t(i) * (sg ? L.stride[1] : L.stride[0]);
+  }
+  if (r < L.rows0) return L.seg[0] + uint64_t(r) * L.stride[0];
+  r -= L.rows0;
+  if (r < L.rows1) return L.seg[1] + uint64_t(r) * L.stride[1];
+  r -= L.rows1;
+  return L.seg[2] + uint64_t(r) * L.stride[2];
+}
+
+// Source address of stream row r without branches: interleaved segments
+// alternate by row; concatenated segments are picked by row ranges.
+DEV uint64_t row_src_fast(const LoadView& L, uint32_t r) {
+  if (L.inter) {
+    const bool up = r & 1;
+    return (up ? L.seg[1] : L.seg[0]) + uint64_t(r >> 1) * (up ? L.stride[1] : L.stride[0]);
+  }
+  const bool in0 = r < L.rows0;
+  const bool in1 = !in0 && r < L.rows0 + L.rows1;
+  const uint32_t local = in0 ? r : (in1 ? r - L.rows0 : r - L.rows0 - L.rows1);
+  const uint64_t base = in0 ? L.seg[0] : (in1 ? L.seg[1] : L.seg[2]);
+  const uint32_t stride = in0 ? L.stride[0] : (in1 ? L.stride[1] : L.stride[2]);
+  return base + uint64_t(local) * stride;
+}
+
+// Each loader wave takes a contiguous share of every page (kDmaPerPage units
+// starting at v * kDmaPerPage), so one wave's burst covers consecutive bytes.
+#ifndef MK_INTERLEAVED_UNITS
+#define MK_UNIT(j) (uint32_t(v) * kDmaPerPage + (j))
+#else
+#define MK_UNIT(j) (uint32_t(v) + kNLoad * (j))
+#endif
+// Issue this loader's share of page p.
+// DMAs each loader wave keeps in flight.  A DMA is issued, then the wave
+// waits until at most kVmT of its DMAs are outstanding: vmcnt decrements in
+// issue order, so every DMA older than the last kVmT has landed in LDS.
+// Issuing one DMA per wait (rather than a page-sized burst per wait) keeps
+// the request stream smooth; bursts streamed at well under half the rate.
+constexpr uint32_t kVmT = 24;
+static_assert(kVmT % kDmaPerPage == 0, "kVmT is a whole number of pages");
+
+// Eight DMAs of one page share, issued from one straight-line block: M0
+// steps by 1 KiB per DMA, and each DMA is followed by the in-flight throttle
+// (a no-op while fewer than kVmT DMAs are outstanding).
+DEV void dma_page8(uint32_t lds_addr, const uint64_t (&src)[8], uint32_t voff) {
+  static_assert(kVmT == 24, "the throttle below is written for kVmT = 24");
+  asm volatile(
+      "s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_waitcnt vmcnt(24)\n\t"
+      "s_add_u32 m0, %0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %3\n\ts_waitcnt vmcnt(24)\n\t"
+      "s_add_u32 m0, %0, 0x800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4\n\ts_waitcnt vmcnt(24)\n\t"
+      "s_add_u32 m0, %0, 0xc00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %5\n\ts_waitcnt vmcnt(24)\n\t"
+      "s_add_u32 m0, %0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %6\n\ts_waitcnt vmcnt(24)\n\t"
+      "s_add_u32 m0, %0, 0x1400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %7\n\ts_waitcnt vmcnt(24)\n\t"
+      "s_add_u32 m0, %0, 0x1800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %8\n\ts_waitcnt vmcnt(24)\n\t"
+      "s_add_u32 m0, %0, 0x1c00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %9\n\ts_waitcnt vmcnt(24)"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(src[0]), "s"(src[1]), "s"(src[2]), "s"(src[3]), "s"(src[4]),
+        "s"(src[5]), "s"(src[6]), "s"(src[7])
+      : "memory", "m0");
+}
+
+DEV void vm_throttle(uint32_t& nd) {
+  if (++nd > kVmT) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+}
+DEV void issue_page(const KArgs& a, const LoadView& L, uint32_t p, uint32_t g, int v,
+                    uint32_t lane, uint32_t& nd) {
+  const uint32_t ldsbase = uint32_t(size_t(lds)) + page_off(g);
+  const uint64_t zero = uint64_t(a.zero_page);
+  const uint32_t voff = lane * 16;
+  if (L.op == OP_GEMV && L.rpu == 1) {
+    // Cursor over the stream: row r, 1 KiB part within the row.  One division
+    // per page; every unit then steps the cursor with selects only.
+    const uint32_t u0 = p * kUnitsPerPage + MK_UNIT(0);
+    uint32_t r = L.nit == 4 ? (u0 >> 2) : (L.nit == 1 ? u0 : u0 / L.nit);
+    uint32_t part = u0 - r * L.nit;
+    uint64_t src[8];
+#pragma unroll
+    for (uint32_t j = 0; j < kDmaPerPage; j++) {
+      src[j] = uni64((u0 + j < L.stream_units) ? row_src_fast(L, r) + part * kUnit : zero);
+      const bool wrap = part + 1 == L.nit;
+      part = wrap ? 0 : part + 1;
+      r = wrap ? r + 1 : r;
+    }
+    dma_page8(ldsbase + MK_UNIT(0) * kUnit, src, voff);
+    nd += kDmaPerPage;
+  } else if (L.op == OP_GEMV) {
+    for (uint32_t j = 0; j < kDmaPerPage; j++) {
+      const uint32_t k = MK_UNIT(j);
+      const uint32_t u = p * kUnitsPerPage + k;
       const uint32_t dst = ldsbase + k * kUnit;
-      if (off + kUnit <= valid_bytes) {
-        dma_uniform(dst, base + off, lane * 16);
-      } else if (off >= valid_bytes) {
-        dma_uniform(dst, zero, lane * 16);
+      if (u >= L.stream_units) {
+        dma_uniform(dst, zero, voff);
       } else {
-        const uint32_t lo = off + lane * 16;
-        dma_lane(dst, lo < valid_bytes ? base + lo : zero + lane * 16);
+        // 512 B rows: lanes 0-31 read row 2u, lanes 32-63 row 2u+1
+        const uint64_t s0 = row_src(L, 2 * u), s1 = row_src(L, 2 * u + 1);
+        dma_lane(dst, (lane < 32 ? s0 : s1) + (lane & 31) * 16);
+      }
+      vm_throttle(nd);
+    }
+  } else {  // OP_ATTN: K block region then V block region, rows < n_cached valid
+    const uint32_t region = p < L.kp ? 0 : 1;
+    const uint32_t pp = p - region * L.kp;
+    const uint64_t base = L.kv_base[region];
+    const uint32_t off0 = (pp * kUnitsPerPage + MK_UNIT(0)) * kUnit;
+    if (off0 + kDmaPerPage * kUnit <= L.valid_bytes || off0 >= L.valid_bytes) {
+      // the whole share is valid rows, or none of it is
+      uint64_t src[8];
+#pragma unroll
+      for (uint32_t j = 0; j < kDmaPerPage; j++)
+        src[j] = uni64(off0 >= L.valid_bytes ? zero : base + off0 + j * kUnit);
+      dma_page8(ldsbase + MK_UNIT(0) * kUnit, src, voff);
+      nd += kDmaPerPage;
+    } else {
+      for (uint32_t j = 0; j < kDmaPerPage; j++) {
+        const uint32_t k = MK_UNIT(j);
+        const uint32_t off = (pp * kUnitsPerPage + k) * kUnit;
+        const uint32_t dst = ldsbase + k * kUnit;
+        if (off + kUnit <= L.valid_bytes) {
+          dma_uniform(dst, base + off, voff);
+        } else if (off >= L.valid_bytes) {
+          dma_uniform(dst, zero, voff);
+        } else {
+          const uint32_t lo = off + voff;
+          dma_lane(dst, lo < L.valid_bytes ? base + lo : zero + voff);
+        }
+        vm_throttle(nd);
       }
     }
+  }
+}
+
+
+DEV void publish(uint32_t& g_pub, uint32_t upto, int v) {
+  if (upto > g_pub) {
+    g_pub = upto;
+    if ((threadIdx.x & 63) == 0) lds_st(C_FILLED + 4 * v, g_pub);
   }
 }
 
 DEV void loader(const KArgs& a, InstrCP q, uint32_t n, int v) {
   const uint32_t lane = threadIdx.x & 63;
-  LoaderState s{0, 0, 0};
+  uint32_t nd = 0;       // DMAs issued by this wave (kDmaPerPage per page)
+  uint32_t g_issue = 0;  // pages issued
+  uint32_t g_pub = 0;    // pages published
+  uint32_t min_rel = 0;  // oldest page a compute wave may still read
   for (uint32_t i = 0; i < n; i++) {
     InstrCP I = q + i;
+    LoadView L;
+    load_view(a, I, L);
     const uint32_t np = I->n_pages, page0 = I->page0;
     for (uint32_t p = 0; p < np; p++) {
       const uint32_t g = page0 + p;
-      if (g - s.g_pub >= kMaxOut) publish_oldest(s, v);
-      uint64_t t0 = 0;
-      while (g >= s.min_rel + kPages) {
-        if (s.g_pub < g) {
-          publish_oldest(s, v);
-          continue;
+      if (g >= min_rel + kPages) {
+        uint64_t t0 = 0;
+        for (;;) {
+          min_rel = uni(min_released());
+          if (g < min_rel + kPages) break;
+          if (g_pub < g_issue) {  // nothing free yet: complete the oldest page
+            wait_vm_pages(g_issue - g_pub - 1);
+            publish(g_pub, g_pub + 1, v);
+            continue;
+          }
+          if (aborted() || local_timeout(t0, local_limit())) {
+            if (!aborted()) local_abort(STC_LOCAL_TIMEOUT);
+            wait_vm0();
+            return;
+          }
+          __builtin_amdgcn_s_sleep(1);
         }
-        s.min_rel = uni(min_released());
-        if (g < s.min_rel + kPages) break;
-        if (aborted() || local_timeout(t0, local_limit())) {
-          if (!aborted()) local_abort(STC_LOCAL_TIMEOUT);
-          wait_vm0();
-          return;
-        }
-        __builtin_amdgcn_s_sleep(1);
       }
-      issue_page(a, I, p, g, v, lane);
-      s.g_issue = g + 1;
+      issue_page(a, L, p, g, v, lane, nd);
+      g_issue = g + 1;
+      // pages whose DMAs all precede the last kVmT are complete
+      if (nd > kVmT) publish(g_pub, (nd - kVmT) / kDmaPerPage, v);
     }
   }
-  while (s.g_pub < s.g_issue) publish_oldest(s, v);
   wait_vm0();
+  publish(g_pub, g_issue, v);
 }
 
 // ================================================================ compute
@@ -440,7 +588,14 @@ struct Comp {
   int w;          // compute wave index
   uint32_t lane;
   uint32_t fcache;  // cached min published page
+  uint32_t pagewait;  // ticks spent waiting for pages (leader, traced runs)
 };
+
+DEV uint32_t now32() { return uint32_t(__builtin_amdgcn_s_memrealtime()); }
+DEV void trace_put(const KArgs& a, int cu, uint32_t i, int word, uint32_t v) {
+  if (a.trace && i < a.trace_stride)
+    a.trace[(size_t(cu) * a.trace_stride + i) * TR_WORDS + word] = v;
+}
 
 // ---- GEMV epilogue for one output row
 struct ArgBest {
@@ -454,7 +609,11 @@ DEV void arg_update(ArgBest& b, float v, uint32_t i) {
   }
 }
 
-DEV void epi_row(Comp& c, InstrCP I, uint32_t t_row, uint32_t row, float v, ArgBest& best) {
+DEV const float* res_slot(uint32_t i) {
+  return reinterpret_cast<const float*>(lds + kLdsRes + (i & 1) * 4 * kMaxResRows);
+}
+
+DEV void epi_row(Comp& c, InstrCP I, uint32_t i, uint32_t t_row, uint32_t row, float v, ArgBest& best) {
   const KArgs& a = *c.a;
   float* out = reinterpret_cast<float*>(I->out_ptr);
   switch (i_epi(I)) {
@@ -463,23 +622,12 @@ DEV void epi_row(Comp& c, InstrCP I, uint32_t t_row, uint32_t row, float v, ArgB
       st_act(out + row, v);
       break;
     case EPI_RESID:
-    case EPI_ACC_ONLY: {
-      float r;
-      if (i_flags(I) & F_RES_EMBED) {
-        const uint16_t* e = reinterpret_cast<const uint16_t*>(I->res_ptr) +
-                            size_t(token0(a)) * a.hidden;
-        r = __uint_as_float(uint32_t(e[row]) << 16);
-      } else {
-        r = ld_act(reinterpret_cast<const float*>(I->res_ptr) + row);
-      }
-      st_act(out + row, r + v);
+    case EPI_ACC_ONLY:
+      st_act(out + row, res_slot(i)[t_row] + v);
       break;
-    }
-    case EPI_ACC_FIRST: {
-      float r = ld_act(reinterpret_cast<const float*>(I->res_ptr) + row);
-      reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] = r + v;
+    case EPI_ACC_FIRST:
+      reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] = res_slot(i)[t_row] + v;
       break;
-    }
     case EPI_ACC_MID:
       reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] += v;
       break;
@@ -515,7 +663,13 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
     for (int j = 0; j < NIT; j++)
 #pragma unroll
       for (int e = 0; e < 8; e++) ss = fmaf(xv[j][e], xv[j][e], ss);
-    ss = reduce_lanes<LPR>(ss);
+    if (RPU == 1) {
+      ss = sum64(ss);
+    } else {
+      float lo, hi;
+      sum32x2(ss, lo, hi);
+      ss = lo;
+    }
     const float inv = rsqrtf(ss / float(I->k) + a.rms_eps);
     const uint16_t* gain = reinterpret_cast<const uint16_t*>(I->gain_ptr);
 #pragma unroll
@@ -539,7 +693,11 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
   for (uint32_t t = c.w; t < n_items; t += kNComp) {
     const uint32_t u0 = t * upi;
     if (lane == 0) lds_st(C_RELEASED + 4 * c.w, page0 + u0 / kUnitsPerPage);
-    if (!wait_page(page0 + (u0 + upi - 1) / kUnitsPerPage, c.fcache)) return false;
+    {
+      const uint32_t tw = c.w == 0 ? now32() : 0;
+      if (!wait_page(page0 + (u0 + upi - 1) / kUnitsPerPage, c.fcache)) return false;
+      if (c.w == 0) c.pagewait += now32() - tw;
+    }
     float acc0 = 0.f, acc1 = 0.f;
     if (RPU == 1) {
       // gate (or only) row, then the up row of a pair: one row of loads live at a time
@@ -556,19 +714,19 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
         for (int j = 0; j < NIT; j++) acc += dot8(wr[j], xv[j]);
         if (r == 0) acc0 = acc; else acc1 = acc;
       }
-      acc0 = reduce_lanes<64>(acc0);
-      if (pair) acc1 = reduce_lanes<64>(acc1);
-      if (lane == 0) epi_row(c, I, t, I->row0 + t, pair ? silu(acc0) * acc1 : acc0, best);
+      acc0 = sum64(acc0);
+      if (pair) acc1 = sum64(acc1);
+      if (lane == 0) epi_row(c, I, i, t, I->row0 + t, pair ? silu(acc0) * acc1 : acc0, best);
     } else {
       const u4 wa = *reinterpret_cast<const u4*>(lds + page_off(page0 + u0 / kUnitsPerPage) +
                                                  (u0 % kUnitsPerPage) * kUnit + lane * 16);
-      acc0 = reduce_lanes<LPR>(dot8(wa, xv[0]));
+      float lo, hi;
+      sum32x2(dot8(wa, xv[0]), lo, hi);
       if (pair) {
-        const float up = __shfl(acc0, 32, 64);
-        if (lane == 0) epi_row(c, I, t, I->row0 + t, silu(acc0) * up, best);
+        if (lane == 0) epi_row(c, I, i, t, I->row0 + t, silu(lo) * hi, best);
       } else if ((lane & 31) == 0) {
         const uint32_t tr = 2 * t + (lane >> 5);
-        epi_row(c, I, tr, I->row0 + tr, acc0, best);
+        epi_row(c, I, i, tr, I->row0 + tr, lane ? hi : lo, best);
       }
     }
   }
@@ -641,7 +799,7 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
     const uint32_t p = u * UPOS + jrow;
 #pragma unroll
     for (int h = 0; h < HPG; h++) {
-      const float d = reduce_lanes<LPRA>(dot8(kw, qr[h]));
+      const float d = group_sum<LPRA>(dot8(kw, qr[h]));
       if (s == 0 && p < uint32_t(nc)) scores[h * Bat + p] = d;
     }
   }
@@ -652,7 +810,7 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e++) d = fmaf(qr[h][e], kn[e], d);
-      d = reduce_lanes<LPRA>(d);
+      d = group_sum<LPRA>(d);
       if (lane == 0) scores[h * Bat + nc] = d;
     }
     if (lane < uint32_t(LPRA)) {
@@ -678,10 +836,10 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
   for (int h = 0; h < HPG; h++) {
     float m = -__builtin_inff();
     for (int32_t p = lane; p < ntot; p += 64) m = fmaxf(m, scores[h * Bat + p]);
-    m = wave_max(m);
+    m = max64(m);
     float l = 0.f;
     for (int32_t p = lane; p < ntot; p += 64) l += __expf(scores[h * Bat + p] - m);
-    l = reduce_lanes<64>(l);
+    l = sum64(l);
     mh[h] = m;
     lh[h] = l;
   }
@@ -774,11 +932,32 @@ DEV void attn_merge(Comp& c, InstrCP I) {
   }
 }
 
+// rows of the residual an epilogue adds (staged with the inputs)
+DEV bool needs_res(InstrCP I) {
+  const uint32_t e = i_epi(I);
+  return i_op(I) == OP_GEMV && (e == EPI_RESID || e == EPI_ACC_ONLY || e == EPI_ACC_FIRST);
+}
+DEV uint32_t out_rows(InstrCP I) {
+  return (i_rpu(I) == 2 && i_epi(I) != EPI_SWIGLU) ? 2 * I->n_items : I->n_items;
+}
+
 // ---- staging of the instruction's inputs into the LDS x slot (leader wave)
-DEV void stage_inputs(Comp& c, InstrCP I) {
+DEV void stage_inputs(Comp& c, InstrCP I, uint32_t i, bool reuse_x) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane;
   float* xs = reinterpret_cast<float*>(lds + kLdsX);
+  if (needs_res(I)) {
+    float* rs = const_cast<float*>(res_slot(i));
+    const uint32_t n = out_rows(I), r0 = I->row0;
+    if (i_flags(I) & F_RES_EMBED) {
+      const uint16_t* e = reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(token0(a)) * a.hidden;
+      for (uint32_t t = lane; t < n; t += 64) rs[t] = __uint_as_float(uint32_t(e[r0 + t]) << 16);
+    } else {
+      const float* r = reinterpret_cast<const float*>(I->res_ptr);
+      for (uint32_t t = lane; t < n; t += 64) rs[t] = ld_act(r + r0 + t);
+    }
+  }
+  if (reuse_x) return;
   if (i_op(I) == OP_GEMV) {
     const uint32_t K = I->k;
     if (i_flags(I) & F_IN_EMBED) {
@@ -887,29 +1066,62 @@ DEV void lm_finish(Comp& c, InstrCP I) {
 }
 
 DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
-  Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0};
+  Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0, 0};
+  const bool tr = a.trace != nullptr;
+  uint64_t staged_in = 0;          // leader: input currently in the x slot
+  uint32_t staged_flags = 0, staged_k = 0;
+  uint32_t seen_ctr = kNoCounter, seen_val = 0;  // leader: last satisfied wait
   for (uint32_t i = 0; i < n; i++) {
     InstrCP I = q + i;
     if (w == 0) {
+      // the staged input of the previous GEMV can be reused as is
+      const bool reuse = i_op(I) == OP_GEMV && I->in_ptr == staged_in &&
+                         (i_flags(I) & (F_IN_EMBED | F_NORM)) == staged_flags && I->k == staged_k;
+      if (tr && c.lane == 0) {
+        trace_put(a, cu, i, TR_START, now32());
+        trace_put(a, cu, i, TR_HW0, hw0(I));
+        trace_put(a, cu, i, TR_HW1, hw1(I));
+      }
+      c.pagewait = 0;
       bool ok = true;
-      for (int k = 0; k < 2 && ok; k++)
-        if (I->wait_cnt[k]) ok = wait_counter(a, I->wait_ctr[k], a.epoch * I->wait_cnt[k], cu, i);
+      for (int k = 0; k < 2 && ok; k++) {
+        if (!I->wait_cnt[k]) continue;
+        const uint32_t ctr = I->wait_ctr[k], target = a.epoch * I->wait_cnt[k];
+        if (ctr == seen_ctr && int32_t(seen_val - target) >= 0) continue;  // already satisfied
+        ok = wait_counter(a, ctr, target, cu, i);
+        seen_ctr = ctr;
+        seen_val = target;
+      }
 #if MK_SYNC_FENCED
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #endif
+      if (tr && c.lane == 0) trace_put(a, cu, i, TR_DEPS, now32());
       // every compute wave has read the previous instruction's staged inputs
+      // (the residual rows are restaged every time)
       for (int v = 0; v < kNComp && ok; v++) ok = wait_lds_ge(C_XCONS + 4 * v, i);
       if (!ok) {
         if (c.lane == 0) lds_st(C_ABORT, 1);
         return;
       }
-      stage_inputs(c, I);
+      stage_inputs(c, I, i, reuse);
+      if (i_op(I) == OP_GEMV) {
+        staged_in = I->in_ptr;
+        staged_flags = i_flags(I) & (F_IN_EMBED | F_NORM);
+        staged_k = I->k;
+      } else {
+        staged_in = 0;
+      }
       if (c.lane == 0) lds_st(C_XOK, i + 1);
+      if (tr && c.lane == 0) trace_put(a, cu, i, TR_STAGED, now32());
     } else if (!wait_lds_ge(C_XOK, i + 1)) {
       return;
     }
     bool ok = i_op(I) == OP_GEMV ? run_gemv(c, I, i) : run_attn(c, I, i);
     if (!ok) return;
+    if (tr && w == 0 && c.lane == 0) {
+      trace_put(a, cu, i, TR_ITEMS, now32());
+      trace_put(a, cu, i, TR_PAGEWAIT, c.pagewait);
+    }
     // completion: the last wave signals
     wait_vm0();
     uint32_t prev = 0;
@@ -930,6 +1142,7 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       wait_vm0();
     }
     if ((i_flags(I) & F_SIGNAL) && c.lane == 0) ctr_add(a.counters + size_t(I->sig_ctr) * kCtrStride);
+    if (tr && c.lane == 0) trace_put(a, cu, i, TR_SIGNAL, now32());
   }
 }
 

@@ -370,9 +370,11 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     {
       const int64_t N = d / gq.rpu;
       for (int cu = 0; cu < C; cu++) {
-        int64_t i0, i1;
-        split(N, cu, &i0, &i1);
-        if (i1 <= i0) continue;
+        int64_t c0, c1;
+        split(N, cu, &c0, &c1);
+        const int64_t step = kMaxResRows / gq.rpu;  // residual rows staged per tile
+        for (int64_t i0 = c0; i0 < c1; i0 += step) {
+        const int64_t i1 = std::min(c1, i0 + step);
         const int r0 = int(i0 * gq.rpu), r1 = int(i1 * gq.rpu);
         Instr I = blank();
         I.op = OP_GEMV;
@@ -403,6 +405,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
         m.reads.push_back({l == 0 ? BUF_EMBED : BUF_X, l, uint64_t(r0), uint64_t(r1)});
         m.writes.push_back({BUF_H, l, uint64_t(r0), uint64_t(r1)});
         b.push(cu, I, std::move(m), int64_t(I.n_rows) * I.row_bytes);
+        }
       }
     }
     // ------------------------------------------------------- GATE/UP
@@ -448,14 +451,17 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     {
       const int64_t N = d / gf.rpu;
       for (int cu = 0; cu < C; cu++) {
-        int64_t i0, i1;
-        split(N, cu, &i0, &i1);
-        if (i1 <= i0) continue;
-        const int r0 = int(i0 * gf.rpu), r1 = int(i1 * gf.rpu);
-        if (r1 - r0 > 256) {
+        int64_t c0, c1;
+        split(N, cu, &c0, &c1);
+        if ((c1 - c0) * gf.rpu > 256) {
           *err = "plan: more than 256 down-projection rows on one CU";
           return MK_ERR_UNSUPPORTED;
         }
+        const int64_t step = kMaxResRows / gf.rpu;
+        for (int64_t i0 = c0; i0 < c1; i0 += step) {
+        const int64_t i1 = std::min(c1, i0 + step);
+        const int r0 = int(i0 * gf.rpu), r1 = int(i1 * gf.rpu);
+        const uint32_t acc_off = uint32_t((i0 - c0) * gf.rpu);
         for (int ch = 0; ch < chunks; ch++) {
           Instr I = blank();
           I.op = OP_GEMV;
@@ -474,7 +480,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
           I.seg_ptr[0] = lptr(in.w.w_down, l, uint64_t(d) * F) + 2ull * (uint64_t(F) * r0 + uint64_t(ch) * Fc);
           I.seg_rows[0] = uint32_t(r1 - r0);
           I.seg_stride[0] = uint32_t(2 * F);
-          I.aux[0] = 0;  // LDS accumulator offset
+          I.aux[0] = acc_off;  // LDS accumulator offset
           I.aux[4] = 1;
           I.in_ptr = A + ar.m[l] + 4ull * ch * Fc;
           I.res_ptr = A + ar.h[l];
@@ -489,6 +495,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
           if (ch == 0) m.reads.push_back({BUF_H, l, uint64_t(r0), uint64_t(r1)});
           if (last) m.writes.push_back({BUF_X, l + 1, uint64_t(r0), uint64_t(r1)});
           b.push(cu, I, std::move(m), int64_t(I.n_rows) * I.row_bytes);
+        }
         }
       }
     }
@@ -811,6 +818,9 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         if ((I.epi == EPI_ACC_FIRST || I.epi == EPI_ACC_MID || I.epi == EPI_ACC_LAST) &&
             I.aux[0] + out_rows > 256)
           return fail("down-projection accumulators exceed the LDS area");
+        if ((I.epi == EPI_RESID || I.epi == EPI_ACC_ONLY || I.epi == EPI_ACC_FIRST) &&
+            out_rows > uint64_t(kMaxResRows))
+          return fail("residual rows exceed the LDS staging slot");
       } else {
         const uint64_t span = uint64_t(c.max_seq) * I.row_bytes;
         if (!inside(I.seg_ptr[0], I.seg_ptr[0] + span) || !inside(I.seg_ptr[1], I.seg_ptr[1] + span))

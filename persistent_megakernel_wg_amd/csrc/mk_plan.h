@@ -12,7 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/mk.h"
+#include "mk.h"
 #include "mk_isa.h"
 
 namespace mk {

@@ -9,7 +9,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/mk.h"
+#include "mk.h"
 #include "mk_plan.h"
 
 extern "C" hipError_t mk_launch_megakernel(const mk::KArgs* args, int n_cus, hipStream_t stream,
@@ -34,6 +34,8 @@ struct mk_ctx {
   hipStream_t last_stream = nullptr;
   bool has_step = false;
   int cooperative = 1;
+  uint32_t* d_trace = nullptr;
+  uint32_t trace_stride = 0;
 };
 
 namespace {
@@ -49,7 +51,14 @@ mk_status hip_fail(mk_ctx* c, hipError_t e, const char* what) {
               std::string(what) + ": " + hipGetErrorString(e));
 }
 
+void free_trace(mk_ctx* c) {
+  if (c->d_trace) (void)hipFree(c->d_trace);
+  c->d_trace = nullptr;
+  c->trace_stride = 0;
+}
+
 void free_plan(mk_ctx* c) {
+  free_trace(c);
   if (c->arena) (void)hipFree(c->arena);
   if (c->d_instrs) (void)hipFree(c->d_instrs);
   if (c->d_qoff) (void)hipFree(c->d_qoff);
@@ -111,6 +120,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, int device, mk_ct
   c->dev_cus = prop.multiProcessorCount;
   const char* nc = std::getenv("MK_NONCOOP");
   c->cooperative = (nc && nc[0] == '1') ? 0 : 1;
+
   rope_tables(c->cfg, &c->rope_cos, &c->rope_sin);
   *out = c;
   return MK_OK;
@@ -198,6 +208,9 @@ mk_status mk_decode_step(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_
   a.rms_eps = c->cfg.rms_eps;
   a.attn_scale = float(1.0 / std::sqrt(double(c->cfg.head_dim)));
   a.watchdog_ticks = uint64_t(c->pin.opts.watchdog_ms) * 100000ull;
+  a.trace = c->d_trace;
+  a.trace_stride = c->trace_stride;
+
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = mk_launch_megakernel(&a, p.n_cus, s, c->cooperative);
   if (e != hipSuccess) return hip_fail(c, e, "launch");
@@ -248,6 +261,36 @@ mk_status mk_destroy(mk_ctx* c) {
   if (c->has_step) (void)hipStreamSynchronize(c->last_stream);
   free_plan(c);
   delete c;
+  return MK_OK;
+}
+
+mk_status mk_trace_enable(mk_ctx* c, int on) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_trace_enable: ctx is NULL");
+  if (!c->planned) return fail(c, MK_ERR_NO_PLAN, "mk_trace_enable: no plan");
+  if (c->has_step) (void)hipStreamSynchronize(c->last_stream);
+  free_trace(c);
+  if (!on) return MK_OK;
+  uint32_t mq = 0;
+  for (int cu = 0; cu < c->plan.n_cus; cu++) mq = std::max(mq, c->plan.q_off[cu + 1] - c->plan.q_off[cu]);
+  const size_t bytes = size_t(c->plan.n_cus) * mq * mk::TR_WORDS * 4;
+  hipError_t e = hipMalloc(&c->d_trace, std::max<size_t>(bytes, 4));
+  if (e == hipSuccess) e = hipMemset(c->d_trace, 0, std::max<size_t>(bytes, 4));
+  if (e != hipSuccess) {
+    c->d_trace = nullptr;
+    return hip_fail(c, e, "trace buffer");
+  }
+  c->trace_stride = mq;
+  return MK_OK;
+}
+
+mk_status mk_trace_read(mk_ctx* c, uint32_t* host, size_t n_words, int32_t* stride) {
+  if (!c || !host || !stride) return fail(c, MK_ERR_INVALID_ARG, "mk_trace_read: NULL argument");
+  if (!c->d_trace) return fail(c, MK_ERR_NO_PLAN, "mk_trace_read: tracing is off");
+  const size_t need = size_t(c->plan.n_cus) * c->trace_stride * mk::TR_WORDS;
+  if (n_words < need) return fail(c, MK_ERR_INVALID_ARG, "mk_trace_read: buffer too small");
+  hipError_t e = hipMemcpy(host, c->d_trace, need * 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(c, e, "trace readback");
+  *stride = int32_t(c->trace_stride);
   return MK_OK;
 }
 

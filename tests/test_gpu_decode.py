@@ -32,13 +32,20 @@ def _say(msg):
 
 
 def kv_rows_close(got_bits, ref_bits):
-    """Appended rows agree within one bf16 step of the larger magnitude, plus a
-    floor of 1e-5 of the row's RMS for values that round across zero."""
+    """Appended rows agree within one bf16 step of the larger magnitude, plus
+    1e-4 of the row's RMS: the float32 path's pre-rounding difference, which
+    grows to ~1e-5 of the RMS in the last layers and decides rounding across
+    zero or a half-step."""
     a, b = bf16_to_f64(got_bits), bf16_to_f64(ref_bits)
     big = np.maximum(np.abs(a), np.abs(b))
     step = np.exp2(np.floor(np.log2(np.maximum(big, 1e-30))) - 7)
-    floor = 1e-5 * np.sqrt(np.mean(b * b, axis=-1, keepdims=True))
-    return bool(np.all(np.abs(a - b) <= step + floor))
+    floor = 1e-4 * np.sqrt(np.mean(b * b, axis=-1, keepdims=True))
+    bad = np.abs(a - b) > step + floor
+    if bad.any():
+        worst = np.max((np.abs(a - b) - step) / np.sqrt(np.mean(b * b, axis=-1, keepdims=True)))
+        print("kv rows: %d of %d beyond one step, worst excess %.3e of the row RMS"
+              % (bad.sum(), bad.size, worst), flush=True)
+    return not bad.any()
 
 
 def _check_kv(shape, kg, vg, k_ref, v_ref, pos):
@@ -87,6 +94,11 @@ def test_tiny_step_few_cus_one_chunk(need_gpu):
 
 def test_tiny_step_two_chunks_odd_cus(need_gpu):
     _one_step_case(synth.SHAPES["tiny"], n_cus=37, mlp_chunks=2, attn_block=64)
+
+
+def test_tiny_step_one_cu(need_gpu):
+    # the whole decoder on one workgroup: split residual tiles, long queue
+    _one_step_case(synth.SHAPES["tiny"], n_cus=1)
 
 
 def test_tiny_empty_cache_position_zero(need_gpu):
