@@ -91,8 +91,23 @@ struct alignas(16) Instr {
   uint64_t res_ptr;    // residual (fp32) or embedding table (bf16)
   uint64_t out_ptr;    // output
   uint64_t gain_ptr;   // RMSNorm gain (bf16)
+  uint64_t src_ptr;    // GEMV: this instruction's packed weight stream
 };
 static_assert(sizeof(Instr) % 16 == 0, "Instr must stay 16 B aligned");
+
+// Packed weight stream.  At plan time every GEMV instruction's rows are copied,
+// in the order the compute waves consume them (interleaved gate/up pairs,
+// down-projection column chunks, the Wq|Wk|Wv concatenation), into one
+// contiguous zero-padded run of n_pages * kPageBytes bytes at src_ptr, so
+// that the loader waves stream plain consecutive 1 KiB units.
+struct PackCopy {
+  uint64_t src;        // first source row (device address)
+  uint64_t dst;        // byte offset of the first row in the packed buffer
+  uint32_t rows;
+  uint32_t row_bytes;  // multiple of 16
+  uint32_t src_stride; // bytes between source rows
+  uint32_t dst_stride; // bytes between packed rows
+};
 
 // Attention instruction aux fields
 //   aux[0] = kv group g         aux[1] = block index b
@@ -120,7 +135,7 @@ struct KArgs {
   const float* rope_cos;    // [max_seq][Dh/2]
   const float* rope_sin;
   float* lm_slots;          // [n_lm_tiles][2] (value, index)
-  const void* zero_page;    // 1 KiB of zeros (padding DMA source)
+  const void* zero_page;    // 16 KiB of zeros (padding DMA source)
   uint32_t epoch;           // 1-based step count since the counters were zeroed
   int32_t pos;
   int32_t vocab;

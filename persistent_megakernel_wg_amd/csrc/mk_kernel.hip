@@ -367,73 +367,28 @@ DEV uint32_t min_released() {
 // loaded once into registers (the DMA asm clobbers memory, so fields read
 // through the instruction pointer would be reloaded for every DMA).
 struct LoadView {
-  uint64_t seg[3];
-  uint32_t rows0, rows1, stride[3];
-  uint32_t op, nit, rpu, inter, rb, stream_units, kp;
-  uint64_t kv_base[2];
-  uint32_t valid_bytes;
+  uint64_t src;            // GEMV: packed stream of the instruction
+  uint64_t kv_base[2];     // ATTN: first K / V row of the position block
+  uint32_t op, stream_units, kp, valid_bytes;
 };
 
 DEV void load_view(const KArgs& a, InstrCP I, LoadView& L) {
   L.op = i_op(I);
-  L.nit = i_nit(I);
-  L.rpu = i_rpu(I);
-  L.inter = i_flags(I) & F_INTERLEAVE;
-  L.rb = I->row_bytes;
-  L.stream_units = (I->n_rows * L.rb + kUnit - 1) / kUnit;
-  for (int k = 0; k < 3; k++) {
-    L.seg[k] = I->seg_ptr[k];
-    L.stride[k] = I->seg_stride[k];
-  }
-  L.rows0 = I->seg_rows[0];
-  L.rows1 = I->seg_rows[1];
+  L.stream_units = (I->n_rows * I->row_bytes + kUnit - 1) / kUnit;
+  L.src = I->src_ptr;
   L.kp = I->aux[4];
+  L.valid_bytes = 0;
+  L.kv_base[0] = L.kv_base[1] = 0;
   if (L.op == OP_ATTN) {
     const int32_t p0 = int32_t(I->aux[1] * I->aux[2]);
     int32_t nc = a.pos - p0;
     nc = nc < 0 ? 0 : (nc > int32_t(I->aux[2]) ? int32_t(I->aux[2]) : nc);
-    L.valid_bytes = uint32_t(nc) * L.rb;
-    L.kv_base[0] = L.seg[0] + uint64_t(p0) * L.rb;
-    L.kv_base[1] = L.seg[1] + uint64_t(p0) * L.rb;
+    L.valid_bytes = uint32_t(nc) * I->row_bytes;
+    L.kv_base[0] = I->seg_ptr[0] + uint64_t(p0) * I->row_bytes;
+    L.kv_base[1] = I->seg_ptr[1] + uint64_t(p0) * I->row_bytes;
   }
 }
 
-// source address of stream row r (uniform)
-DEV uint64_t row_src(const LoadView& L, uint32_t r) {
-  if (L.inter) {
-    const uint32_t sg = r & 1, i = r >> 1;
-    return (sg ? L.seg[1] : L.seg[0]) + uint64_t(i) * (sg ? L.stride[1] : L.stride[0]);
-  }
-  if (r < L.rows0) return L.seg[0] + uint64_t(r) * L.stride[0];
-  r -= L.rows0;
-  if (r < L.rows1) return L.seg[1] + uint64_t(r) * L.stride[1];
-  r -= L.rows1;
-  return L.seg[2] + uint64_t(r) * L.stride[2];
-}
-
-// Source address of stream row r without branches: interleaved segments
-// alternate by row; concatenated segments are picked by row ranges.
-DEV uint64_t row_src_fast(const LoadView& L, uint32_t r) {
-  if (L.inter) {
-    const bool up = r & 1;
-    return (up ? L.seg[1] : L.seg[0]) + uint64_t(r >> 1) * (up ? L.stride[1] : L.stride[0]);
-  }
-  const bool in0 = r < L.rows0;
-  const bool in1 = !in0 && r < L.rows0 + L.rows1;
-  const uint32_t local = in0 ? r : (in1 ? r - L.rows0 : r - L.rows0 - L.rows1);
-  const uint64_t base = in0 ? L.seg[0] : (in1 ? L.seg[1] : L.seg[2]);
-  const uint32_t stride = in0 ? L.stride[0] : (in1 ? L.stride[1] : L.stride[2]);
-  return base + uint64_t(local) * stride;
-}
-
-// Each loader wave takes a contiguous share of every page (kDmaPerPage units
-// starting at v * kDmaPerPage), so one wave's burst covers consecutive bytes.
-#ifndef MK_INTERLEAVED_UNITS
-#define MK_UNIT(j) (uint32_t(v) * kDmaPerPage + (j))
-#else
-#define MK_UNIT(j) (uint32_t(v) + kNLoad * (j))
-#endif
-// Issue this loader's share of page p.
 // DMAs each loader wave keeps in flight.  A DMA is issued, then the wave
 // waits until at most kVmT of its DMAs are outstanding: vmcnt decrements in
 // issue order, so every DMA older than the last kVmT has landed in LDS.
@@ -442,92 +397,71 @@ DEV uint64_t row_src_fast(const LoadView& L, uint32_t r) {
 constexpr uint32_t kVmT = 24;
 static_assert(kVmT % kDmaPerPage == 0, "kVmT is a whole number of pages");
 
-// Eight DMAs of one page share, issued from one straight-line block: M0
-// steps by 1 KiB per DMA, and each DMA is followed by the in-flight throttle
-// (a no-op while fewer than kVmT DMAs are outstanding).
-DEV void dma_page8(uint32_t lds_addr, const uint64_t (&src)[8], uint32_t voff) {
+// Eight DMAs of 8 consecutive 1 KiB units starting at `src` into LDS at
+// `lds_addr`.  The instruction offset moves the global source and the LDS
+// destination together, so four DMAs share one M0 value; the second four use
+// a VGPR offset 4 KiB higher and M0 + 4 KiB.  Each DMA is followed by the
+// in-flight throttle (a no-op while fewer than kVmT DMAs are outstanding).
+DEV void dma_run8(uint32_t lds_addr, uint64_t src, uint32_t voff, uint32_t voff4k) {
   static_assert(kVmT == 24, "the throttle below is written for kVmT = 24");
   asm volatile(
-      "s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_waitcnt vmcnt(24)\n\t"
-      "s_add_u32 m0, %0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %3\n\ts_waitcnt vmcnt(24)\n\t"
-      "s_add_u32 m0, %0, 0x800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4\n\ts_waitcnt vmcnt(24)\n\t"
-      "s_add_u32 m0, %0, 0xc00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %5\n\ts_waitcnt vmcnt(24)\n\t"
-      "s_add_u32 m0, %0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %6\n\ts_waitcnt vmcnt(24)\n\t"
-      "s_add_u32 m0, %0, 0x1400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %7\n\ts_waitcnt vmcnt(24)\n\t"
-      "s_add_u32 m0, %0, 0x1800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %8\n\ts_waitcnt vmcnt(24)\n\t"
-      "s_add_u32 m0, %0, 0x1c00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %9\n\ts_waitcnt vmcnt(24)"
+      "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\ts_waitcnt vmcnt(24)\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:1024\n\ts_waitcnt vmcnt(24)\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:2048\n\ts_waitcnt vmcnt(24)\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:3072\n\ts_waitcnt vmcnt(24)\n\t"
+      "s_add_u32 m0, %0, 0x1000\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\ts_waitcnt vmcnt(24)\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:1024\n\ts_waitcnt vmcnt(24)\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:2048\n\ts_waitcnt vmcnt(24)\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:3072\n\ts_waitcnt vmcnt(24)"
       :
-      : "s"(lds_addr), "v"(voff), "s"(src[0]), "s"(src[1]), "s"(src[2]), "s"(src[3]), "s"(src[4]),
-        "s"(src[5]), "s"(src[6]), "s"(src[7])
+      : "s"(lds_addr), "v"(voff), "v"(voff4k), "s"(src)
       : "memory", "m0");
 }
 
 DEV void vm_throttle(uint32_t& nd) {
   if (++nd > kVmT) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
 }
+
+// Issue this loader wave's half of page p (units v*8 .. v*8+7): one
+// contiguous 8 KiB run, so consecutive DMAs of a wave read consecutive bytes.
 DEV void issue_page(const KArgs& a, const LoadView& L, uint32_t p, uint32_t g, int v,
-                    uint32_t lane, uint32_t& nd) {
-  const uint32_t ldsbase = uint32_t(size_t(lds)) + page_off(g);
+                    uint32_t voff, uint32_t voff4k, uint32_t& nd) {
+  const uint32_t half = uint32_t(v) * kDmaPerPage;
+  const uint32_t dst = uint32_t(size_t(lds)) + page_off(g) + half * kUnit;
   const uint64_t zero = uint64_t(a.zero_page);
-  const uint32_t voff = lane * 16;
-  if (L.op == OP_GEMV && L.rpu == 1) {
-    // Cursor over the stream: row r, 1 KiB part within the row.  One division
-    // per page; every unit then steps the cursor with selects only.
-    const uint32_t u0 = p * kUnitsPerPage + MK_UNIT(0);
-    uint32_t r = L.nit == 4 ? (u0 >> 2) : (L.nit == 1 ? u0 : u0 / L.nit);
-    uint32_t part = u0 - r * L.nit;
-    uint64_t src[8];
-#pragma unroll
-    for (uint32_t j = 0; j < kDmaPerPage; j++) {
-      src[j] = uni64((u0 + j < L.stream_units) ? row_src_fast(L, r) + part * kUnit : zero);
-      const bool wrap = part + 1 == L.nit;
-      part = wrap ? 0 : part + 1;
-      r = wrap ? r + 1 : r;
-    }
-    dma_page8(ldsbase + MK_UNIT(0) * kUnit, src, voff);
+  if (L.op == OP_GEMV) {
+    // Packed stream: the run is inside the instruction's zero-padded pages;
+    // a half page wholly past the rows reads the zero page instead of HBM.
+    const uint32_t u0 = p * kUnitsPerPage + half;
+    dma_run8(dst, u0 < L.stream_units ? L.src + uint64_t(u0) * kUnit : zero, voff, voff4k);
     nd += kDmaPerPage;
-  } else if (L.op == OP_GEMV) {
+    return;
+  }
+  // OP_ATTN: K block region then V block region; rows < n_cached are valid
+  const uint32_t region = p < L.kp ? 0 : 1;
+  const uint64_t base = region ? L.kv_base[1] : L.kv_base[0];
+  const uint32_t off0 = ((p - region * L.kp) * kUnitsPerPage + half) * kUnit;
+  if (off0 + kDmaPerPage * kUnit <= L.valid_bytes) {
+    dma_run8(dst, base + off0, voff, voff4k);
+    nd += kDmaPerPage;
+  } else if (off0 >= L.valid_bytes) {
+    dma_run8(dst, zero, voff, voff4k);
+    nd += kDmaPerPage;
+  } else {
     for (uint32_t j = 0; j < kDmaPerPage; j++) {
-      const uint32_t k = MK_UNIT(j);
-      const uint32_t u = p * kUnitsPerPage + k;
-      const uint32_t dst = ldsbase + k * kUnit;
-      if (u >= L.stream_units) {
-        dma_uniform(dst, zero, voff);
+      const uint32_t off = off0 + j * kUnit;
+      const uint32_t d = dst + j * kUnit;
+      if (off + kUnit <= L.valid_bytes) {
+        dma_uniform(d, base + off, voff);
+      } else if (off >= L.valid_bytes) {
+        dma_uniform(d, zero, voff);
       } else {
-        // 512 B rows: lanes 0-31 read row 2u, lanes 32-63 row 2u+1
-        const uint64_t s0 = row_src(L, 2 * u), s1 = row_src(L, 2 * u + 1);
-        dma_lane(dst, (lane < 32 ? s0 : s1) + (lane & 31) * 16);
+        const uint32_t lo = off + voff;
+        dma_lane(d, lo < L.valid_bytes ? base + lo : zero + voff);
       }
       vm_throttle(nd);
-    }
-  } else {  // OP_ATTN: K block region then V block region, rows < n_cached valid
-    const uint32_t region = p < L.kp ? 0 : 1;
-    const uint32_t pp = p - region * L.kp;
-    const uint64_t base = L.kv_base[region];
-    const uint32_t off0 = (pp * kUnitsPerPage + MK_UNIT(0)) * kUnit;
-    if (off0 + kDmaPerPage * kUnit <= L.valid_bytes || off0 >= L.valid_bytes) {
-      // the whole share is valid rows, or none of it is
-      uint64_t src[8];
-#pragma unroll
-      for (uint32_t j = 0; j < kDmaPerPage; j++)
-        src[j] = uni64(off0 >= L.valid_bytes ? zero : base + off0 + j * kUnit);
-      dma_page8(ldsbase + MK_UNIT(0) * kUnit, src, voff);
-      nd += kDmaPerPage;
-    } else {
-      for (uint32_t j = 0; j < kDmaPerPage; j++) {
-        const uint32_t k = MK_UNIT(j);
-        const uint32_t off = (pp * kUnitsPerPage + k) * kUnit;
-        const uint32_t dst = ldsbase + k * kUnit;
-        if (off + kUnit <= L.valid_bytes) {
-          dma_uniform(dst, base + off, voff);
-        } else if (off >= L.valid_bytes) {
-          dma_uniform(dst, zero, voff);
-        } else {
-          const uint32_t lo = off + voff;
-          dma_lane(dst, lo < L.valid_bytes ? base + lo : zero + voff);
-        }
-        vm_throttle(nd);
-      }
     }
   }
 }
@@ -541,7 +475,7 @@ DEV void publish(uint32_t& g_pub, uint32_t upto, int v) {
 }
 
 DEV void loader(const KArgs& a, InstrCP q, uint32_t n, int v) {
-  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t voff = (threadIdx.x & 63) * 16, voff4k = voff + 4096;
   uint32_t nd = 0;       // DMAs issued by this wave (kDmaPerPage per page)
   uint32_t g_issue = 0;  // pages issued
   uint32_t g_pub = 0;    // pages published
@@ -571,7 +505,7 @@ DEV void loader(const KArgs& a, InstrCP q, uint32_t n, int v) {
           __builtin_amdgcn_s_sleep(1);
         }
       }
-      issue_page(a, L, p, g, v, lane, nd);
+      issue_page(a, L, p, g, v, voff, voff4k, nd);
       g_issue = g + 1;
       // pages whose DMAs all precede the last kVmT are complete
       if (nd > kVmT) publish(g_pub, (nd - kVmT) / kDmaPerPage, v);
@@ -1166,7 +1100,32 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void mk_megakernel(KArgs a)
     compute(a, q, end - beg, wave - kNLoad, cu);
 }
 
+// Plan-time fill of the packed weight stream: one workgroup column per copy,
+// 16-byte loads and stores, rows split over gridDim.y.
+__global__ void __launch_bounds__(256) mk_pack_kernel(const PackCopy* copies, uint32_t n,
+                                                       uint8_t* base) {
+  for (uint32_t c = blockIdx.x; c < n; c += gridDim.x) {
+    const PackCopy cp = copies[c];
+    const uint32_t per_row = cp.row_bytes / 16;
+    const uint64_t total = uint64_t(cp.rows) * per_row;
+    for (uint64_t t = threadIdx.x + uint64_t(blockIdx.y) * blockDim.x; t < total;
+         t += uint64_t(blockDim.x) * gridDim.y) {
+      const uint64_t r = t / per_row, k = t - r * per_row;
+      const u4 v = *reinterpret_cast<const u4*>(cp.src + r * cp.src_stride + k * 16);
+      *reinterpret_cast<u4*>(base + cp.dst + r * cp.dst_stride + k * 16) = v;
+    }
+  }
+}
+
 }  // namespace mk
+
+extern "C" hipError_t mk_launch_pack(const mk::PackCopy* copies, uint32_t n, void* base,
+                                     hipStream_t stream) {
+  const uint32_t gx = n < 65535u ? n : 65535u;
+  hipLaunchKernelGGL(mk::mk_pack_kernel, dim3(gx, 16), dim3(256), 0, stream, copies, n,
+                     static_cast<uint8_t*>(base));
+  return hipGetLastError();
+}
 
 // Launch entry used by the runtime (not part of the public ABI).
 extern "C" hipError_t mk_launch_megakernel(const mk::KArgs* args, int n_cus, hipStream_t stream,

@@ -187,7 +187,7 @@ ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
   }
   a.rope_cos = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
   a.rope_sin = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
-  a.zero_page = take(kUnit);
+  a.zero_page = take(kPageBytes);
   a.lm_slots = take(8 * uint64_t(max_lm_tiles));
   a.status = take(64);
   a.total = off;
@@ -574,6 +574,28 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     P->meta.insert(P->meta.end(), b.qm[cu].begin(), b.qm[cu].end());
   }
   P->n_counters = int(P->ctr_stage.size());
+  // packed weight stream: each GEMV instruction's rows in consumption order
+  uint64_t pack = 0;
+  for (Instr& I : P->instrs) {
+    if (I.op != OP_GEMV) continue;
+    I.src_ptr = in.pack_base + pack;
+    const bool inter = I.flags & F_INTERLEAVE;
+    uint64_t row = 0;
+    for (uint32_t sg = 0; sg < I.aux[4]; sg++) {
+      if (!I.seg_rows[sg]) continue;
+      PackCopy cp;
+      cp.src = I.seg_ptr[sg];
+      cp.rows = I.seg_rows[sg];
+      cp.row_bytes = I.row_bytes;
+      cp.src_stride = I.seg_stride[sg];
+      cp.dst = pack + (inter ? uint64_t(sg) * I.row_bytes : row * I.row_bytes);
+      cp.dst_stride = inter ? 2 * I.row_bytes : I.row_bytes;
+      row += cp.rows;
+      P->pack.push_back(cp);
+    }
+    pack += uint64_t(I.n_pages) * kPageBytes;
+  }
+  P->pack_bytes = pack;
   // bytes
   int64_t wbytes = 0;
   wbytes += int64_t(L) * 2 * (int64_t(qd + 2 * kvd) * d + int64_t(d) * qd + 3ll * F * d + 2ll * d);
@@ -788,6 +810,26 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
     };
     const uint64_t A = in.arena_base, Aend = in.arena_base + p.arena.total;
     auto in_arena = [&](uint64_t lo, uint64_t hi) { return lo >= A && hi <= Aend; };
+    // packed stream: instruction runs back to back inside the buffer, and
+    // every copy reads weight rows and writes inside the buffer
+    uint64_t next_src = in.pack_base, stream_bytes = 0, copied = 0;
+    for (const Instr& I : p.instrs) {
+      if (I.op != OP_GEMV) continue;
+      if (I.src_ptr != next_src) return fail("packed weight runs are not back to back");
+      next_src += uint64_t(I.n_pages) * kPageBytes;
+      stream_bytes += uint64_t(I.n_rows) * I.row_bytes;
+    }
+    if (next_src != in.pack_base + p.pack_bytes) return fail("packed weight stream size");
+    for (const PackCopy& cp : p.pack) {
+      if (!cp.rows || cp.row_bytes % 16 || cp.src_stride % 16 || cp.dst_stride % 16 || cp.src % 16)
+        return fail("packed copy not in 16-byte units");
+      if (!inside(cp.src, cp.src + uint64_t(cp.rows - 1) * cp.src_stride + cp.row_bytes))
+        return fail("packed copy reads outside every weight tensor");
+      if (cp.dst + uint64_t(cp.rows - 1) * cp.dst_stride + cp.row_bytes > p.pack_bytes)
+        return fail("packed copy writes outside the packed stream");
+      copied += uint64_t(cp.rows) * cp.row_bytes;
+    }
+    if (copied != stream_bytes) return fail("packed copies do not cover the weight streams");
     for (size_t i = 0; i < p.instrs.size(); i++) {
       const Instr& I = p.instrs[i];
       if (I.op == OP_GEMV) {
@@ -880,6 +922,11 @@ void corrupt_one_target(Plan* p) {
         p->instrs[i].wait_cnt[0] += 1;
         return;
       }
+}
+
+void rebase_pack(Plan* p, uint64_t old_base, uint64_t base) {
+  for (Instr& I : p->instrs)
+    if (I.op == OP_GEMV) I.src_ptr = I.src_ptr - old_base + base;
 }
 
 void summarize(const PlanInput& in, const Plan& p, mk_plan_summary* s) {

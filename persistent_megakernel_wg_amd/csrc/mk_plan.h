@@ -33,6 +33,7 @@ struct PlanInput {
   int n_cus;
   mk_weights w;          // device pointers (may be fake)
   uint64_t arena_base;   // device address of the arena
+  uint64_t pack_base;    // device address of the packed weight stream
 };
 
 // Verification view of one instruction.
@@ -55,6 +56,8 @@ struct Plan {
   std::vector<InstrMeta> meta;      // parallel to instrs
   std::vector<uint32_t> ctr_producers;  // per counter: signals per step
   std::vector<int> ctr_stage;       // stage of the counter's producers
+  std::vector<PackCopy> pack;       // copies that fill the packed weight stream
+  uint64_t pack_bytes = 0;          // size of the packed weight stream
   int n_cus = 0, n_counters = 0;
   int attn_block = 0, attn_nblk = 0, attn_tiles = 0, mlp_chunks = 0, lm_tiles = 0;
   int64_t weight_bytes = 0, max_cu_bytes = 0, min_cu_bytes = 0;
@@ -75,6 +78,10 @@ mk_status build_plan(const PlanInput& in, Plan* out, std::string* err);
 // queue-order simulation that must run every instruction.  Returns MK_OK or
 // MK_ERR_INVALID_ARG with the first violation in *err.
 mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint64_t seed = 1);
+
+// Move the packed weight stream to `base` (the plan is built against
+// in.pack_base; the runtime allocates the stream once its size is known).
+void rebase_pack(Plan* p, uint64_t old_base, uint64_t base);
 
 // Test hook: make one wait target unreachable (applied after verification by
 // the runtime so that a step must end in the watchdog; mk_plan_check applies

@@ -14,6 +14,8 @@
 
 extern "C" hipError_t mk_launch_megakernel(const mk::KArgs* args, int n_cus, hipStream_t stream,
                                            int cooperative);
+extern "C" hipError_t mk_launch_pack(const mk::PackCopy* copies, uint32_t n, void* base,
+                                     hipStream_t stream);
 
 struct mk_ctx {
   mk_config cfg;
@@ -27,6 +29,7 @@ struct mk_ctx {
   mk::PlanInput pin;
   mk::Plan plan;
   char* arena = nullptr;
+  char* pack = nullptr;   // packed weight stream (library-owned copy)
   mk::Instr* d_instrs = nullptr;
   uint32_t* d_qoff = nullptr;
   uint32_t* d_counters = nullptr;
@@ -60,6 +63,8 @@ void free_trace(mk_ctx* c) {
 void free_plan(mk_ctx* c) {
   free_trace(c);
   if (c->arena) (void)hipFree(c->arena);
+  if (c->pack) (void)hipFree(c->pack);
+  c->pack = nullptr;
   if (c->d_instrs) (void)hipFree(c->d_instrs);
   if (c->d_qoff) (void)hipFree(c->d_qoff);
   if (c->d_counters) (void)hipFree(c->d_counters);
@@ -112,6 +117,11 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, int device, mk_ct
   if ((e = hipGetDeviceProperties(&prop, device)) != hipSuccess) return hip_fail(nullptr, e, "hipGetDeviceProperties");
   if (size_t(prop.maxSharedMemoryPerMultiProcessor) < size_t(mk::kLdsTotal))
     return fail(nullptr, MK_ERR_UNSUPPORTED, "mk_create: device has too little LDS per CU");
+  const void* aligned[] = {w->embed, w->lm_head, w->wq, w->wk, w->wv, w->wo, w->w_gate, w->w_up,
+                           w->w_down, w->k_cache, w->v_cache};
+  for (const void* ptr : aligned)
+    if (uintptr_t(ptr) % 16)
+      return fail(nullptr, MK_ERR_INVALID_ARG, "mk_create: weight and cache pointers must be 16-byte aligned");
   mk_ctx* c = new mk_ctx();
   c->cfg = *cfg;
   c->w = *w;
@@ -145,9 +155,19 @@ mk_status mk_build_plan(mk_ctx* c, const mk_plan_opts* opts) {
   const mk::ArenaLayout lay = mk::arena_layout(c->cfg, n_cus, c->cfg.n_kv_heads * nblk);
   if ((e = hipMalloc(&c->arena, lay.total)) != hipSuccess) return hip_fail(c, e, "hipMalloc(arena)");
   in.arena_base = uint64_t(c->arena);
+  in.pack_base = 0;
   std::string err;
+  c->plan = mk::Plan();
   mk_status st = mk::build_plan(in, &c->plan, &err);
-  if (st == MK_OK) st = mk::verify_plan(in, c->plan, &err);
+  if (st == MK_OK) {
+    if ((e = hipMalloc(&c->pack, std::max<uint64_t>(c->plan.pack_bytes, 16))) != hipSuccess) {
+      free_plan(c);
+      return hip_fail(c, e, "hipMalloc(packed weights)");
+    }
+    mk::rebase_pack(&c->plan, 0, uint64_t(c->pack));
+    in.pack_base = uint64_t(c->pack);
+    st = mk::verify_plan(in, c->plan, &err);
+  }
   if (st != MK_OK) {
     free_plan(c);
     return fail(c, st, err);
@@ -163,6 +183,17 @@ mk_status mk_build_plan(mk_ctx* c, const mk_plan_opts* opts) {
     e = hipMemcpy(c->d_instrs, p.instrs.data(), p.instrs.size() * sizeof(mk::Instr), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMalloc(&c->d_qoff, p.q_off.size() * 4);
   if (e == hipSuccess) e = hipMemcpy(c->d_qoff, p.q_off.data(), p.q_off.size() * 4, hipMemcpyHostToDevice);
+  // fill the packed weight stream (zero padding, then the rows)
+  mk::PackCopy* d_copies = nullptr;
+  if (e == hipSuccess) e = hipMemset(c->pack, 0, p.pack_bytes);
+  if (e == hipSuccess && !p.pack.empty()) {
+    e = hipMalloc(&d_copies, p.pack.size() * sizeof(mk::PackCopy));
+    if (e == hipSuccess)
+      e = hipMemcpy(d_copies, p.pack.data(), p.pack.size() * sizeof(mk::PackCopy), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = mk_launch_pack(d_copies, uint32_t(p.pack.size()), c->pack, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (d_copies) (void)hipFree(d_copies);
+  }
   const size_t ctr_bytes = size_t(std::max(1, p.n_counters)) * mk::kCtrStride * 4;
   if (e == hipSuccess) e = hipMalloc(&c->d_counters, ctr_bytes);
   if (e == hipSuccess) e = hipMemset(c->d_counters, 0, ctr_bytes);
@@ -324,6 +355,7 @@ mk_status mk_plan_check(const mk_config* cfg, const mk_plan_opts* opts, int32_t 
   in.w.k_cache = reinterpret_cast<void*>(base * 20);
   in.w.v_cache = reinterpret_cast<void*>(base * 21);
   in.arena_base = uint64_t(base) * 30;
+  in.pack_base = uint64_t(base) * 31;
   mk::Plan p;
   st = mk::build_plan(in, &p, &err);
   if (st == MK_OK && in.opts.debug_corrupt_target) mk::corrupt_one_target(&p);
