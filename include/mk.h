@@ -97,14 +97,19 @@ typedef struct {
   int32_t n_cus;      /* workgroups = CUs used (default: all CUs of the device) */
   int32_t mlp_chunks; /* MLP intermediate split into this many chunks, each with
                          its own counter so down-projection tiles start early
-                         (default 4, as in the Llama-1B megakernel write-up,
-                         "Custom Synchronization Mechanism") */
+                         (the Llama-1B megakernel write-up, "Custom
+                         Synchronization Mechanism", uses 4).  Default: the
+                         fewest chunks of at most 4096 values each, since
+                         every chunk adds two instructions per CU */
   int32_t attn_block; /* KV positions per attention tile (multiple of 64;
                          default: chosen from max_seq and the CU count) */
   int32_t watchdog_ms;/* counter-wait limit before MK_ERR_TIMEOUT (default 2000) */
   int32_t debug_corrupt_target; /* tests only: 1 raises one wait target so the
                                    step must end in MK_ERR_TIMEOUT */
-  int32_t reserved[3];
+  int32_t generic_kernel; /* 1: always launch the kernel built for every shape
+                             (default 0: the kernel built for this shape when
+                             the library has one; see kernel_variant) */
+  int32_t reserved[2];
 } mk_plan_opts;
 
 /* Plan summary (filled by mk_plan_info / mk_plan_check). */
@@ -122,6 +127,10 @@ typedef struct {
   int64_t weight_bytes;    /* weight bytes streamed per step              */
   int64_t max_cu_bytes;    /* largest per-CU streamed bytes (KV at max_seq)*/
   int64_t min_cu_bytes;    /* smallest per-CU streamed bytes              */
+  int32_t kernel_variant;  /* 0: the generic kernel; > 0: the kernel built
+                              for this shape (the Llama-3.2-1B, Llama-3-8B
+                              and small test decoder geometries)         */
+  int32_t reserved;
 } mk_plan_summary;
 
 /* Create a context on `device` for this model and these caller-owned buffers.
@@ -172,12 +181,18 @@ mk_status mk_plan_check(const mk_config *cfg, const mk_plan_opts *opts, int32_t 
 
 /* ---- diagnostics -------------------------------------------------------
  * Per-instruction timestamps of the next steps (s_memrealtime, 100 MHz, low
- * 32 bits): for every CU and queue slot 8 words
+ * 32 bits): for every CU and queue slot 16 words
  *   {start, deps satisfied, inputs staged, leader's items done, signal,
- *    leader's page-wait ticks, header word 0, header word 1}.
+ *    leader's page-wait ticks, header word 0, header word 1,
+ *    leader's input vector ready, leader's first item done, leader's stores
+ *    visible, previous inputs released, then for attention the ends of the
+ *    score pass, the softmax statistics and the value pass, the leader's
+ *    re-reads of inputs whose step tag was not yet current}.
+ * For attention instructions words 8 and 9 are the end of the query
+ * preparation and of the leader's own score work.
  * mk_trace_enable allocates (on != 0) or frees the trace buffer; it costs a
  * few stores per instruction.  mk_trace_read copies it to host memory
- * (n_words >= n_cus * stride * 8) after mk_sync; *stride receives the slots
+ * (n_words >= n_cus * stride * 16) after mk_sync; *stride receives the slots
  * per CU.  Errors: MK_ERR_NO_PLAN, MK_ERR_INVALID_ARG, MK_ERR_HIP. */
 mk_status mk_trace_enable(mk_ctx *ctx, int on);
 mk_status mk_trace_read(mk_ctx *ctx, uint32_t *host, size_t n_words, int32_t *stride);

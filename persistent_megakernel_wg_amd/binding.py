@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmk.so")
 
 MK_OK = 0
+TRACE_WORDS = 16  # words per traced instruction
 STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_HIP", -3: "MK_ERR_NO_PLAN",
                 -4: "MK_ERR_UNSUPPORTED", -5: "MK_ERR_OOM", -6: "MK_ERR_TIMEOUT",
                 -7: "MK_ERR_DEVICE"}
@@ -43,18 +44,19 @@ class MkWeights(ctypes.Structure):
 
 class MkPlanOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "n_cus", "mlp_chunks", "attn_block", "watchdog_ms", "debug_corrupt_target")] + [
-        ("reserved", ctypes.c_int32 * 3)]
+        "n_cus", "mlp_chunks", "attn_block", "watchdog_ms", "debug_corrupt_target",
+        "generic_kernel")] + [("reserved", ctypes.c_int32 * 2)]
 
 
 class MkPlanSummary(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_cus", "n_instr", "max_queue", "n_counters", "lds_bytes", "n_pages", "page_bytes",
         "attn_block", "attn_tiles", "mlp_chunks")] + [
-        (n, ctypes.c_int64) for n in ("weight_bytes", "max_cu_bytes", "min_cu_bytes")]
+        (n, ctypes.c_int64) for n in ("weight_bytes", "max_cu_bytes", "min_cu_bytes")] + [
+        ("kernel_variant", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
     def as_dict(self):
-        return {n: getattr(self, n) for n, _ in self._fields_}
+        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
 
 
 EXPORTS = ("mk_create", "mk_build_plan", "mk_decode_step", "mk_sync", "mk_destroy",
@@ -110,9 +112,11 @@ def config_from_shape(shape) -> MkConfig:
                     rope_theta=shape.rope_theta)
 
 
-def plan_opts(n_cus=0, mlp_chunks=0, attn_block=0, watchdog_ms=0, debug_corrupt_target=0):
+def plan_opts(n_cus=0, mlp_chunks=0, attn_block=0, watchdog_ms=0, debug_corrupt_target=0,
+              generic_kernel=0):
     return MkPlanOpts(n_cus=n_cus, mlp_chunks=mlp_chunks, attn_block=attn_block,
-                      watchdog_ms=watchdog_ms, debug_corrupt_target=debug_corrupt_target)
+                      watchdog_ms=watchdog_ms, debug_corrupt_target=debug_corrupt_target,
+                      generic_kernel=generic_kernel)
 
 
 # ------------------------------------------------------------ the C entry points
@@ -168,11 +172,11 @@ def mk_trace_enable(ctx: int, on: bool = True) -> None:
 
 
 def mk_trace_read(ctx: int, n_cus: int, max_queue: int):
-    """Trace of the last step as a uint32 array [n_cus, stride, 8]."""
+    """Trace of the last step as a uint32 array [n_cus, stride, 16]."""
     import numpy as np
-    buf = np.zeros(n_cus * max_queue * 8, dtype=np.uint32)
+    buf = np.zeros(n_cus * max_queue * TRACE_WORDS, dtype=np.uint32)
     stride = ctypes.c_int32()
     _check(load_library().mk_trace_read(
         ctx, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), buf.size,
         ctypes.byref(stride)), ctx)
-    return buf[: n_cus * stride.value * 8].reshape(n_cus, stride.value, 8)
+    return buf[: n_cus * stride.value * TRACE_WORDS].reshape(n_cus, stride.value, TRACE_WORDS)

@@ -23,6 +23,10 @@ constexpr int kPages = 8;            // pages in the LDS ring
 constexpr int kCtrStride = 32;       // u32 per counter (128 B apart)
 constexpr int kMaxK = 4096;          // largest GEMV input length
 constexpr int kDoneRing = 4;         // per-instruction completion counters
+// Activation element in global memory: fp32 value | u32 tag (the step that
+// wrote it).  A consumer accepts an element only when its tag is the current
+// step, so producers signal their counters without waiting for their stores.
+constexpr int kActBytes = 8;
 
 // LDS layout (bytes)
 constexpr int kLdsCtrl = 0;          // control words
@@ -154,7 +158,9 @@ struct KArgs {
 
 // trace record words (s_memrealtime, 100 MHz, low 32 bits)
 enum TraceWord { TR_START = 0, TR_DEPS = 1, TR_STAGED = 2, TR_ITEMS = 3, TR_SIGNAL = 4,
-                 TR_PAGEWAIT = 5, TR_HW0 = 6, TR_HW1 = 7, TR_WORDS = 8 };
+                 TR_PAGEWAIT = 5, TR_HW0 = 6, TR_HW1 = 7, TR_XREADY = 8, TR_ITEM0 = 9,
+                 TR_VISIBLE = 10, TR_XFREE = 11, TR_A_PASS1 = 12, TR_A_STATS = 13,
+                 TR_A_PASS3 = 14, TR_RETRY = 15, TR_WORDS = 16 };
 
 // status words
 enum StatusWord { ST_CODE = 0, ST_CU = 1, ST_INSTR = 2, ST_CTR = 3, ST_SEEN = 4, ST_TARGET = 5,

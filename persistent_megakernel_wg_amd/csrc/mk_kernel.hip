@@ -26,15 +26,17 @@
 #include "mk_isa.h"
 
 #define DEV __device__ __forceinline__
-
-#ifndef MK_SYNC_FENCED
-// 0: activations travel with device-coherent (sc1) loads/stores and counters
-//    are bumped after s_waitcnt vmcnt(0) — no L2 writeback/invalidate.
-// 1: plain loads/stores bracketed by agent-scope release/acquire fences.
-#define MK_SYNC_FENCED 0
-#endif
+// Global memory is addressed through address-space-1 pointers so that every
+// access is a global_* instruction: a flat access would also count on the
+// LDS counter, and every LDS wait after it would wait for global memory.
+#define GLB __attribute__((address_space(1)))
 
 namespace mk {
+
+template <class T>
+DEV GLB T* gp(T* p) { return (GLB T*)p; }
+template <class T>
+DEV GLB T* gp(const T* p) { return (GLB T*)const_cast<T*>(p); }
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -103,46 +105,47 @@ DEV uint32_t page_off(uint32_t g) { return kLdsPages + (g & (kPages - 1)) * kPag
 // ------------------------------------------------------ global memory access
 DEV void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Counters and activations use device-scope (sc1) loads and stores; no L2
+// writeback or invalidate is issued.
 DEV uint32_t ctr_load(const uint32_t* p) {
-#if MK_SYNC_FENCED
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-#else
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#endif
+  return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-DEV uint32_t ctr_add(uint32_t* p) {
-#if MK_SYNC_FENCED
-  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-#else
+// Signal: the counter is bumped without waiting for this wave's stores.
+// Consumers take activations only with the current step's tag, so the
+// counter only says when it is worth looking.
+DEV uint32_t ctr_signal(uint32_t* p) {
+  return __hip_atomic_fetch_add(gp(p), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Release: every store of this wave lands before the counter moves (used
+// for the untagged data behind tickets: attention partials, argmax slots).
+DEV uint32_t ctr_release(uint32_t* p) {
   wait_vm0();
-  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#endif
+  return __hip_atomic_fetch_add(gp(p), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// activation store / load (device-coherent)
+// untagged device-coherent scalar store / load
 DEV void st_act(float* p, float v) {
-#if MK_SYNC_FENCED
-  *p = v;
-#else
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#endif
+  __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 DEV float ld_act(const float* p) {
-#if MK_SYNC_FENCED
-  return *p;
-#else
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#endif
+  return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// 16-byte activation load through a buffer resource (sc1 = device scope)
+// Tagged activation element (8 bytes): the fp32 value in the low word, the
+// step (epoch) that wrote it in the high word, stored as one 8-byte access.
+DEV void st_tag(uint64_t* p, float v, uint32_t tag) {
+  const uint64_t w = uint64_t(__float_as_uint(v)) | (uint64_t(tag) << 32);
+  __hip_atomic_store(gp(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Loads through buffer resources: reads past the resource's size return
+// zero without touching memory.  sc1 = device scope.
 DEV __amdgpu_buffer_rsrc_t act_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 DEV f4 ld_act4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-#if MK_SYNC_FENCED
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-#else
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16 /* sc1 */);
-#endif
+}
+// two tagged elements {v0, tag0, v1, tag1}
+DEV u4 ld_tag2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
 }
 
 DEV float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -155,9 +158,9 @@ DEV uint16_t f2bf(float f) {  // round to nearest even (no NaN inputs expected)
 // input token, checked against the vocabulary (an out-of-range id is reported
 // and replaced by 0 so that no access leaves the embedding table)
 DEV uint32_t token0(const KArgs& a) {
-  const int32_t t = a.tokens[0];
+  const int32_t t = *gp(a.tokens);
   if (t >= 0 && t < a.vocab) return uint32_t(t);
-  __hip_atomic_store(a.status + ST_BADTOK, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gp(a.status) + ST_BADTOK, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return 0;
 }
 DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
@@ -225,14 +228,14 @@ DEV float max64(float v) {
 DEV void record_timeout(const KArgs& a, int cu, uint32_t instr, uint32_t ctr, uint32_t seen,
                         uint32_t target) {
   uint32_t expected = 0;
-  if (__hip_atomic_compare_exchange_strong(a.status + ST_CODE, &expected, uint32_t(STC_TIMEOUT),
+  if (__hip_atomic_compare_exchange_strong(gp(a.status) + ST_CODE, &expected, uint32_t(STC_TIMEOUT),
                                            __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT)) {
-    __hip_atomic_store(a.status + ST_CU, uint32_t(cu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a.status + ST_INSTR, instr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a.status + ST_CTR, ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a.status + ST_SEEN, seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a.status + ST_TARGET, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gp(a.status) + ST_CU, uint32_t(cu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gp(a.status) + ST_INSTR, instr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gp(a.status) + ST_CTR, ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gp(a.status) + ST_SEEN, seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gp(a.status) + ST_TARGET, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -243,36 +246,45 @@ DEV bool wait_counter(const KArgs& a, uint32_t ctr, uint32_t target, int cu, uin
   for (uint32_t it = 0;; it++) {
     uint32_t v = uni(ctr_load(p));
     if (int32_t(v - target) >= 0) return true;
-    uint64_t now = __builtin_amdgcn_s_memrealtime();
+    // The clock is a scalar memory read: read it every 64 polls only, so that
+    // a poll is not held up by its latency.
+    if ((it & 63) != 63) continue;
+    const uint64_t now = __builtin_amdgcn_s_memrealtime();
     if (t0 == 0) t0 = now;
     if (now - t0 > a.watchdog_ticks) {
       record_timeout(a, cu, instr, ctr, v, target);
       return false;
     }
-    if ((it & 255) == 255 &&
-        __hip_atomic_load(a.status + ST_CODE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+    if (__hip_atomic_load(gp(a.status) + ST_CODE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
       return false;
   }
 }
 
 // Time limit of waits inside the workgroup (pages, staged inputs, barriers).
 // They can only stall if the workgroup itself is stuck; the limit turns that
-// into an error instead of a hang.
-DEV bool local_timeout(uint64_t& t0, uint64_t limit) {
+// into an error instead of a hang.  The clock (a scalar memory read, waited
+// for together with LDS reads) is read every 256 polls, so the limit counts
+// from the 256th poll.
+struct Watch {
+  uint32_t n = 0;
+  uint64_t t0 = 0;
+};
+DEV bool local_timeout(Watch& w, uint64_t limit) {
+  if ((++w.n & 255) != 0) return false;
   const uint64_t now = __builtin_amdgcn_s_memrealtime();
-  if (t0 == 0) t0 = now;
-  return now - t0 > limit;
+  if (w.t0 == 0) w.t0 = now;
+  return now - w.t0 > limit;
 }
 DEV void local_abort(uint32_t code) {
   uint32_t expected = 0;
-  __hip_atomic_compare_exchange_strong(status_ptr() + ST_CODE, &expected, code, __ATOMIC_RELAXED,
+  __hip_atomic_compare_exchange_strong(gp(status_ptr()) + ST_CODE, &expected, code, __ATOMIC_RELAXED,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   lds_st(C_ABORT, 1);
 }
 
 // Wait for an LDS word to reach `want` (or abort).
 DEV bool wait_lds_ge(int off, uint32_t want) {
-  uint64_t t0 = 0;
+  Watch t0;
   while (int32_t(lds_ld(off) - want) < 0) {
     if (aborted()) return false;
     if (local_timeout(t0, local_limit())) {
@@ -291,7 +303,7 @@ DEV uint32_t min_filled() {
 }
 // Wait until page g is published by every loader.
 DEV bool wait_page(uint32_t g, uint32_t& cache) {
-  uint64_t t0 = 0;
+  Watch t0;
   while (cache <= g) {
     cache = min_filled();
     if (cache > g) break;
@@ -488,7 +500,7 @@ DEV void loader(const KArgs& a, InstrCP q, uint32_t n, int v) {
     for (uint32_t p = 0; p < np; p++) {
       const uint32_t g = page0 + p;
       if (g >= min_rel + kPages) {
-        uint64_t t0 = 0;
+        Watch t0;
         for (;;) {
           min_rel = uni(min_released());
           if (g < min_rel + kPages) break;
@@ -523,12 +535,13 @@ struct Comp {
   uint32_t lane;
   uint32_t fcache;  // cached min published page
   uint32_t pagewait;  // ticks spent waiting for pages (leader, traced runs)
+  uint32_t retries;   // re-reads of stale tagged inputs (leader, traced runs)
 };
 
 DEV uint32_t now32() { return uint32_t(__builtin_amdgcn_s_memrealtime()); }
 DEV void trace_put(const KArgs& a, int cu, uint32_t i, int word, uint32_t v) {
   if (a.trace && i < a.trace_stride)
-    a.trace[(size_t(cu) * a.trace_stride + i) * TR_WORDS + word] = v;
+    gp(a.trace)[(size_t(cu) * a.trace_stride + i) * TR_WORDS + word] = v;
 }
 
 // ---- GEMV epilogue for one output row
@@ -549,15 +562,15 @@ DEV const float* res_slot(uint32_t i) {
 
 DEV void epi_row(Comp& c, InstrCP I, uint32_t i, uint32_t t_row, uint32_t row, float v, ArgBest& best) {
   const KArgs& a = *c.a;
-  float* out = reinterpret_cast<float*>(I->out_ptr);
+  uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
   switch (i_epi(I)) {
     case EPI_STORE:
     case EPI_SWIGLU:
-      st_act(out + row, v);
+      st_tag(out + row, v, a.epoch);
       break;
     case EPI_RESID:
     case EPI_ACC_ONLY:
-      st_act(out + row, res_slot(i)[t_row] + v);
+      st_tag(out + row, res_slot(i)[t_row] + v, a.epoch);
       break;
     case EPI_ACC_FIRST:
       reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] = res_slot(i)[t_row] + v;
@@ -566,11 +579,11 @@ DEV void epi_row(Comp& c, InstrCP I, uint32_t i, uint32_t t_row, uint32_t row, f
       reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] += v;
       break;
     case EPI_ACC_LAST:
-      st_act(out + row, reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] + v);
+      st_tag(out + row, reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] + v, a.epoch);
       break;
     case EPI_ARGMAX:
-      if (a.logits) a.logits[row] = v;
-      if (v != v) __hip_atomic_store(a.status + ST_NAN, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (a.logits) gp(a.logits)[row] = v;
+      if (v != v) __hip_atomic_store(gp(a.status) + ST_NAN, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       arg_update(best, v, row);
       break;
   }
@@ -591,34 +604,9 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
     xv[j][0] = lo.x; xv[j][1] = lo.y; xv[j][2] = lo.z; xv[j][3] = lo.w;
     xv[j][4] = hi.x; xv[j][5] = hi.y; xv[j][6] = hi.z; xv[j][7] = hi.w;
   }
-  if (i_flags(I) & F_NORM) {
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < NIT; j++)
-#pragma unroll
-      for (int e = 0; e < 8; e++) ss = fmaf(xv[j][e], xv[j][e], ss);
-    if (RPU == 1) {
-      ss = sum64(ss);
-    } else {
-      float lo, hi;
-      sum32x2(ss, lo, hi);
-      ss = lo;
-    }
-    const float inv = rsqrtf(ss / float(I->k) + a.rms_eps);
-    const uint16_t* gain = reinterpret_cast<const uint16_t*>(I->gain_ptr);
-#pragma unroll
-    for (int j = 0; j < NIT; j++) {
-      const uint32_t col = RPU == 1 ? j * 512 + lane * 8 : (lane % LPR) * 8;
-      const u4 gv = *reinterpret_cast<const u4*>(gain + col);
-      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        xv[j][2 * e] *= inv * bf_lo(gw[e]);
-        xv[j][2 * e + 1] *= inv * bf_hi(gw[e]);
-      }
-    }
-  }
   if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
+  const bool trl = c.a->trace && c.w == 0 && lane == 0;
+  if (trl) trace_put(a, c.cu, i, TR_XREADY, now32());
 
   const uint32_t n_items = I->n_items, page0 = I->page0;
   const bool pair = i_epi(I) == EPI_SWIGLU;
@@ -628,9 +616,9 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
     const uint32_t u0 = t * upi;
     if (lane == 0) lds_st(C_RELEASED + 4 * c.w, page0 + u0 / kUnitsPerPage);
     {
-      const uint32_t tw = c.w == 0 ? now32() : 0;
+      const uint32_t tw = trl ? now32() : 0;
       if (!wait_page(page0 + (u0 + upi - 1) / kUnitsPerPage, c.fcache)) return false;
-      if (c.w == 0) c.pagewait += now32() - tw;
+      if (trl) c.pagewait += now32() - tw;
     }
     float acc0 = 0.f, acc1 = 0.f;
     if (RPU == 1) {
@@ -663,6 +651,7 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
         epi_row(c, I, i, tr, I->row0 + tr, lane ? hi : lo, best);
       }
     }
+    if (trl && t == 0) trace_put(a, c.cu, i, TR_ITEM0, now32());
   }
   if (i_epi(I) == EPI_ARGMAX) {
     // combine lanes 0 and 32 (512 B rows) and publish the wave's best
@@ -679,14 +668,20 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
 }
 
 // ---- attention: one KV group, one position block
-// x slot holds raw q [HPG*Dh] | k [Dh] | v [Dh] of the group (staged by the leader).
+// The x slot holds, staged by the leader: q [HPG*Dh] | k [Dh] | v [Dh] of the
+// group | cos [Dh/2] | sin [Dh/2] of the position.  After the query and the
+// new row are in registers the x slot is reused for the value-pass partials,
+// so the instruction releases it (C_XCONS) only at its end.
 template <int HPG, int DH>
 DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane;
-  constexpr int LPRA = DH / 8;          // lanes per cached row (8 dims per lane)
+  constexpr int LPRA = DH / 8;            // lanes per cached row (8 dims per lane)
   constexpr int UPOS = kUnit / (2 * DH);  // rows per 1 KiB unit
   constexpr int HALF = DH / 2;
+  constexpr int OUT = HPG * DH;           // outputs of the group
+  constexpr int PER = OUT / 64;           // value-pass outputs per lane
+  static_assert(PER >= 1 && PER <= 8 && OUT * kNComp <= kMaxK, "attention shape");
   const uint32_t g = I->aux[0], blk = I->aux[1], Bat = I->aux[2], nblk = I->aux[3], kp = I->aux[4];
   const int32_t P = a.pos;
   const int32_t p0 = int32_t(blk * Bat);
@@ -694,37 +689,60 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
   nc = nc < 0 ? 0 : (nc > int32_t(Bat) ? int32_t(Bat) : nc);
   const bool own = P >= p0 && P < p0 + int32_t(Bat);
   const int32_t ntot = nc + (own ? 1 : 0);
-  const float* xs = reinterpret_cast<const float*>(lds + kLdsX);
-  float* scores = reinterpret_cast<float*>(lds + kLdsAttn);
+  float* xs = reinterpret_cast<float*>(lds + kLdsX);
+  float* scores = reinterpret_cast<float*>(lds + kLdsAttn);     // [HPG][Bat]
   uint16_t* newv = reinterpret_cast<uint16_t*>(lds + kLdsAttn + 8192);
-  float* parts = reinterpret_cast<float*>(lds + kLdsAttn + 8192 + 512);
+  float* stat_m = reinterpret_cast<float*>(lds + kLdsAttn + 8192 + 512);
+  float* stat_l = stat_m + 8;
+  const float* cs = xs + HPG * DH + 2 * DH;
+  const float* sn = cs + HALF;
   const uint32_t s = lane % LPRA;        // dims [8s, 8s+8)
   const uint32_t jrow = lane / LPRA;     // row within a unit
-  const float* cs = a.rope_cos + size_t(P) * HALF;
-  const float* sn = a.rope_sin + size_t(P) * HALF;
+  const bool trl = a.trace && c.w == 0 && lane == 0;
 
-  // rotated, scaled query slices of every head of the group
-  auto rot = [&](const float* vec, int d) {  // rotated component d of vec
-    if (d < HALF) return vec[d] * cs[d] - vec[d + HALF] * sn[d];
-    return vec[d] * cs[d - HALF] + vec[d - HALF] * sn[d - HALF];
+  // rotated (RoPE, rotate-half pairing), scaled query slices of every head.
+  // A lane's 8 dims [8s, 8s+8) lie in one half, so every operand is two
+  // 16-byte LDS reads: the dims themselves, their partners in the other
+  // half, and cos / sin at the dims' frequencies.
+  const uint32_t d0 = 8 * s;
+  const bool first_half = d0 < uint32_t(HALF);
+  const uint32_t pd = first_half ? d0 + HALF : d0 - HALF;  // partner dims
+  const uint32_t fd = first_half ? d0 : d0 - HALF;         // frequency index
+  const float sgn = first_half ? -1.f : 1.f;
+  auto ld8 = [&](const float* p, float (&o)[8]) {
+    const f4 lo = *reinterpret_cast<const f4*>(p);
+    const f4 hi = *reinterpret_cast<const f4*>(p + 4);
+    o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w;
+    o[4] = hi.x; o[5] = hi.y; o[6] = hi.z; o[7] = hi.w;
+  };
+  float cv[8], sv[8];
+  ld8(cs + fd, cv);
+  ld8(sn + fd, sv);
+  auto rot8 = [&](const float* vec, float (&o)[8], float scale) {
+    float self[8], part[8];
+    ld8(vec + d0, self);
+    ld8(vec + pd, part);
+#pragma unroll
+    for (int e = 0; e < 8; e++) o[e] = (self[e] * cv[e] + sgn * part[e] * sv[e]) * scale;
   };
   float qr[HPG][8];
 #pragma unroll
-  for (int h = 0; h < HPG; h++)
-#pragma unroll
-    for (int e = 0; e < 8; e++) qr[h][e] = rot(xs + h * DH, 8 * s + e) * a.attn_scale;
+  for (int h = 0; h < HPG; h++) rot8(xs + h * DH, qr[h], a.attn_scale);
   // the new key/value row, rounded to bf16
-  float kn[8];
+  float kr[8], vr[8], kn[8];
   uint16_t kb[8], vb[8];
+  rot8(xs + HPG * DH, kr, 1.f);
+  ld8(xs + HPG * DH + DH + d0, vr);
 #pragma unroll
   for (int e = 0; e < 8; e++) {
-    kb[e] = f2bf(rot(xs + HPG * DH, 8 * s + e));
+    kb[e] = f2bf(kr[e]);
     kn[e] = __uint_as_float(uint32_t(kb[e]) << 16);
-    vb[e] = f2bf(xs[HPG * DH + DH + 8 * s + e]);
+    vb[e] = f2bf(vr[e]);
   }
-  if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
+  if (trl) trace_put(a, c.cu, i, TR_XREADY, now32());
 
-  // pass 1: scores of cached rows (units round-robin over the compute waves)
+  // pass 1: scores of cached rows (units round-robin over the compute waves);
+  // the wave after the last unit's scores the new row and appends it
   const uint32_t n_units = (uint32_t(nc) + UPOS - 1) / UPOS;
   for (uint32_t u = c.w; u < n_units; u += kNComp) {
     if (!wait_page(I->page0 + u / kUnitsPerPage, c.fcache)) return false;
@@ -737,8 +755,7 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
       if (s == 0 && p < uint32_t(nc)) scores[h * Bat + p] = d;
     }
   }
-  if (c.w == 0 && own) {
-    // score of the new row; append it to the cache
+  if (own && uint32_t(c.w) == n_units % kNComp) {
 #pragma unroll
     for (int h = 0; h < HPG; h++) {
       float d = 0.f;
@@ -756,90 +773,99 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
       kk.z = kb[4] | uint32_t(kb[5]) << 16; kk.w = kb[6] | uint32_t(kb[7]) << 16;
       vv.x = vb[0] | uint32_t(vb[1]) << 16; vv.y = vb[2] | uint32_t(vb[3]) << 16;
       vv.z = vb[4] | uint32_t(vb[5]) << 16; vv.w = vb[6] | uint32_t(vb[7]) << 16;
-      *reinterpret_cast<u4*>(kc) = kk;
-      *reinterpret_cast<u4*>(vc) = vv;
+      *gp(reinterpret_cast<u4*>(kc)) = kk;
+      *gp(reinterpret_cast<u4*>(vc)) = vv;
 #pragma unroll
       for (int e = 0; e < 8; e++) newv[8 * s + e] = vb[e];
     }
   }
+  if (trl) trace_put(a, c.cu, i, TR_ITEM0, now32());
   if (!comp_barrier()) return false;
+  if (trl) trace_put(a, c.cu, i, TR_A_PASS1, now32());
 
-  // pass 2: softmax statistics per head (every wave, redundantly)
-  float mh[HPG], lh[HPG];
-#pragma unroll
-  for (int h = 0; h < HPG; h++) {
+  // pass 2: per head (heads round-robin over the waves) the maximum, the
+  // weights exp(score - max) in place of the scores, and their sum
+  for (int h = c.w; h < HPG; h += kNComp) {
     float m = -__builtin_inff();
     for (int32_t p = lane; p < ntot; p += 64) m = fmaxf(m, scores[h * Bat + p]);
     m = max64(m);
     float l = 0.f;
-    for (int32_t p = lane; p < ntot; p += 64) l += __expf(scores[h * Bat + p] - m);
-    l = sum64(l);
-    mh[h] = m;
-    lh[h] = l;
-  }
-
-  // pass 3: o~ = sum_p e_p V_p, lanes own (head, dim pair), positions split
-  constexpr int T = HPG * HALF;              // tasks
-  constexpr int NL = 64 * kNComp;
-  constexpr int S = NL / T > 0 ? NL / T : 1;  // position splits
-  static_assert(T <= NL, "too many attention tasks");
-  const uint32_t L = c.w * 64 + lane;
-  const uint32_t task = L % T, split = L / T;
-  const uint32_t h = task / HALF, dp = task % HALF;
-  float m_sel = mh[0];
-#pragma unroll
-  for (int hh = 1; hh < HPG; hh++)
-    if (h == uint32_t(hh)) m_sel = mh[hh];
-  float o0 = 0.f, o1 = 0.f;
-  if (kp && !wait_page(I->page0 + 2 * kp - 1, c.fcache)) return false;
-  if (split < uint32_t(S)) {
-    for (int32_t p = split; p < ntot; p += S) {
-      const float e = __expf(scores[h * Bat + p] - m_sel);
-      uint32_t vw;
-      if (p < nc) {
-        const uint32_t off = uint32_t(p) * (2 * DH) + 4 * dp;
-        vw = *reinterpret_cast<const uint32_t*>(lds + page_off(I->page0 + kp + off / kPageBytes) +
-                                                (off % kPageBytes));
-      } else {
-        vw = *reinterpret_cast<const uint32_t*>(newv + 2 * dp);
-      }
-      o0 = fmaf(e, bf_lo(vw), o0);
-      o1 = fmaf(e, bf_hi(vw), o1);
+    for (int32_t p = lane; p < ntot; p += 64) {
+      const float e = __expf(scores[h * Bat + p] - m);
+      scores[h * Bat + p] = e;
+      l += e;
     }
-    parts[2 * L] = o0;
-    parts[2 * L + 1] = o1;
+    l = sum64(l);
+    if (lane == 0) {
+      stat_m[h] = m;
+      stat_l[h] = l;
+    }
+  }
+  if (!comp_barrier()) return false;
+  if (trl) trace_put(a, c.cu, i, TR_A_STATS, now32());
+
+  // pass 3: o~ = sum_p w_p V_p; wave w takes positions p = w (mod waves),
+  // lane l the PER consecutive outputs from l*PER (one head); per-wave
+  // partials go to the x slot
+  const uint32_t o0 = lane * PER, h3 = o0 / DH, d3 = o0 % DH;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; e++) acc[e] = 0.f;
+  if (kp && !wait_page(I->page0 + 2 * kp - 1, c.fcache)) return false;
+  for (int32_t p = c.w; p < ntot; p += kNComp) {
+    const float wp = scores[h3 * Bat + p];
+    const char* vrow;
+    if (p < nc) {
+      const uint32_t off = uint32_t(p) * (2 * DH) + 2 * d3;
+      vrow = lds + page_off(I->page0 + kp + off / kPageBytes) + (off % kPageBytes);
+    } else {
+      vrow = reinterpret_cast<const char*>(newv + d3);
+    }
+    uint32_t vw[(PER + 1) / 2];
+    if constexpr (PER == 8) {
+      const u4 t = *reinterpret_cast<const u4*>(vrow);
+      vw[0] = t.x; vw[1] = t.y; vw[2] = t.z; vw[3] = t.w;
+    } else if constexpr (PER == 4) {
+      const uint2 t = *reinterpret_cast<const uint2*>(vrow);
+      vw[0] = t.x; vw[1] = t.y;
+    } else if constexpr (PER == 2) {
+      vw[0] = *reinterpret_cast<const uint32_t*>(vrow);
+    } else {
+      vw[0] = *reinterpret_cast<const uint16_t*>(vrow);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; e++)
+      acc[e] = fmaf(wp, (e & 1) ? bf_hi(vw[e / 2]) : bf_lo(vw[e / 2]), acc[e]);
   }
   if (lane == 0) lds_st(C_RELEASED + 4 * c.w, I->page0 + I->n_pages);
-  if (!comp_barrier()) return false;
-
-  // final: sum the splits in order
-  if (L < uint32_t(T)) {
-    float s0 = 0.f, s1 = 0.f;
-    for (int sp = 0; sp < S; sp++) {
-      s0 += parts[2 * (sp * T + L)];
-      s1 += parts[2 * (sp * T + L) + 1];
-    }
-    float l_sel = lh[0];
 #pragma unroll
-    for (int hh = 1; hh < HPG; hh++)
-      if (h == uint32_t(hh)) l_sel = lh[hh];
+  for (int e = 0; e < PER; e++) xs[c.w * OUT + o0 + e] = acc[e];
+  if (!comp_barrier()) return false;
+  if (trl) trace_put(a, c.cu, i, TR_A_PASS3, now32());
+
+  // final: sum the wave partials in order, normalise, store
+  for (uint32_t o = c.w * 64 + lane; o < uint32_t(OUT); o += 64 * kNComp) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNComp; w++) sum += xs[w * OUT + o];
+    const uint32_t h = o / DH, d = o % DH;
     const uint32_t head = g * HPG + h;
     if (nblk == 1) {
-      float* out = reinterpret_cast<float*>(I->out_ptr) + head * DH + 2 * dp;
-      st_act(out, s0 / l_sel);
-      st_act(out + 1, s1 / l_sel);
+      st_tag(reinterpret_cast<uint64_t*>(I->out_ptr) + head * DH + d, sum / stat_l[h], a.epoch);
     } else {
       // partial record [HPG][DH + 2] of (group, block): o~ | m | l
       float* part = reinterpret_cast<float*>(I->res_ptr) +
                     (size_t(g) * nblk + blk) * (HPG * (DH + 2)) + h * (DH + 2);
-      st_act(part + 2 * dp, s0);
-      st_act(part + 2 * dp + 1, s1);
-      if (dp == 0) {
-        st_act(part + DH, m_sel);
-        st_act(part + DH + 1, l_sel);
+      st_act(part + d, sum);
+      if (d == 0) {
+        st_act(part + DH, stat_m[h]);
+        st_act(part + DH + 1, stat_l[h]);
       }
     }
   }
+  // every wave has read the x slot: the next inputs may be staged
+  if (!comp_barrier()) return false;
+  if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
   return true;
 }
 
@@ -862,7 +888,7 @@ DEV void attn_merge(Comp& c, InstrCP I) {
       num = fmaf(wgt, ld_act(rec + d), num);
       den = fmaf(wgt, ld_act(rec + DH + 1), den);
     }
-    st_act(reinterpret_cast<float*>(I->out_ptr) + (g * HPG + h) * DH + d, num / den);
+    st_tag(reinterpret_cast<uint64_t*>(I->out_ptr) + (g * HPG + h) * DH + d, num / den, c.a->epoch);
   }
 }
 
@@ -876,98 +902,307 @@ DEV uint32_t out_rows(InstrCP I) {
 }
 
 // ---- staging of the instruction's inputs into the LDS x slot (leader wave)
-DEV void stage_inputs(Comp& c, InstrCP I, uint32_t i, bool reuse_x) {
+// Re-read tagged entries of `t` (the first `live` of this lane) until every
+// one holds the current step's tag.  The producer's counter has already
+// moved, so a stale entry is a store still in flight; the wait is bounded by
+// the workgroup's local watchdog.  T is u4 (two elements) or uint2 (one).
+DEV bool is_fresh(const u4& t, uint32_t tag) { return t.y == tag && t.w == tag; }
+DEV bool is_fresh(const uint2& t, uint32_t tag) { return t.y == tag; }
+DEV void reload(u4& t, __amdgpu_buffer_rsrc_t r, uint32_t off) { t = ld_tag2(r, off); }
+DEV void reload(uint2& t, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16));
+}
+template <typename T, int N>
+DEV bool wait_fresh(T (&t)[N], uint32_t live, __amdgpu_buffer_rsrc_t r, const uint32_t (&off)[N],
+                    uint32_t tag, uint32_t& retries) {
+  Watch wt;
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < N; j++)
+      if (j < int(live) && !is_fresh(t[j], tag)) ok = false;
+    if (__builtin_amdgcn_ballot_w64(!ok) == 0) return true;
+    retries++;
+#pragma unroll
+    for (int j = 0; j < N; j++)
+      if (j < int(live) && !is_fresh(t[j], tag)) reload(t[j], r, off[j]);
+    if (aborted()) return false;
+    if (local_timeout(wt, local_limit())) {
+      local_abort(STC_LOCAL_TIMEOUT);
+      return false;
+    }
+  }
+}
+
+// Inputs of instruction I into LDS: the input vector into the x slot
+// (RMS-normalised with the gain when F_NORM; for attention the group's q, k,
+// v and the position's cos, sin) and the residual rows of the epilogue into
+// the instruction's residual slot.  Every load is issued before the first
+// is waited for, so the staging costs one memory round trip when the
+// producers' stores have landed.  false = abort or watchdog.
+DEV bool stage_inputs(Comp& c, InstrCP I, uint32_t i, bool reuse_x) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane;
+  const uint32_t tag = a.epoch;
   float* xs = reinterpret_cast<float*>(lds + kLdsX);
-  if (needs_res(I)) {
-    float* rs = const_cast<float*>(res_slot(i));
-    const uint32_t n = out_rows(I), r0 = I->row0;
-    if (i_flags(I) & F_RES_EMBED) {
-      const uint16_t* e = reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(token0(a)) * a.hidden;
-      for (uint32_t t = lane; t < n; t += 64) rs[t] = __uint_as_float(uint32_t(e[r0 + t]) << 16);
-    } else {
-      const float* r = reinterpret_cast<const float*>(I->res_ptr);
-      for (uint32_t t = lane; t < n; t += 64) rs[t] = ld_act(r + r0 + t);
-    }
+  static_assert(kMaxResRows == 128, "residual staging takes two rows per lane");
+
+  // residual rows r0 + 2*lane + {0,1}: tagged elements, or the bf16 row of
+  // the token's embedding (per-element loads: a resource of n_res elements
+  // reads zero past the tile)
+  const bool has_res = needs_res(I);
+  const bool res_embed = has_res && (i_flags(I) & F_RES_EMBED);
+  const uint32_t n_res = has_res ? out_rows(I) : 0;
+  const uint32_t r0 = I->row0;
+  const __amdgpu_buffer_rsrc_t rr = act_rsrc(reinterpret_cast<const char*>(I->res_ptr) + size_t(r0) * kActBytes,
+                                             (has_res && !res_embed) ? n_res * kActBytes : 0);
+  uint2 res_t[2];
+  const uint32_t res_off[2] = {2 * lane * kActBytes, (2 * lane + 1) * kActBytes};
+  reload(res_t[0], rr, res_off[0]);
+  reload(res_t[1], rr, res_off[1]);
+  uint16_t res_e[2] = {0, 0};
+  if (res_embed) {
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(token0(a)) * a.hidden + r0;
+    const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(e), 0, n_res * 2, 0x00020000);
+    res_e[0] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane, 0, 0);
+    res_e[1] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane + 2, 0, 0);
   }
-  if (reuse_x) return;
-  if (i_op(I) == OP_GEMV) {
-    const uint32_t K = I->k;
-    if (i_flags(I) & F_IN_EMBED) {
-      const uint16_t* e = reinterpret_cast<const uint16_t*>(I->in_ptr) + size_t(token0(a)) * K;
-      for (uint32_t o = lane * 8; o < K; o += 512) {
-        const u4 v = *reinterpret_cast<const u4*>(e + o);
-        f4 lo = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y)};
-        f4 hi = {bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
-        *reinterpret_cast<f4*>(xs + o) = lo;
-        *reinterpret_cast<f4*>(xs + o + 4) = hi;
+  const uint32_t res_live = 2 * lane >= n_res ? 0 : (2 * lane + 1 < n_res ? 2 : 1);
+
+  if (!reuse_x) {
+    if (i_op(I) == OP_GEMV) {
+      const uint32_t K = I->k;
+      const bool norm = i_flags(I) & F_NORM;
+      // gain (a resource of zero bytes without F_NORM: reads return zero)
+      const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>(I->gain_ptr), 0, norm ? K * 2 : 0, 0x00020000);
+      if (i_flags(I) & F_IN_EMBED) {
+        // bf16 embedding row of the token: 8 values per lane per 512
+        constexpr int NE = kMaxK / 512;
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(I->in_ptr) + size_t(token0(a)) * K;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(e), 0, K * 2, 0x00020000);
+        u4 raw[NE], gw[NE];
+#pragma unroll
+        for (int j = 0; j < NE; j++) {
+          raw[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (lane * 8 + 512 * j) * 2, 0, 0));
+          gw[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rg, (lane * 8 + 512 * j) * 2, 0, 0));
+        }
+        float v[NE][8];
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NE; j++) {
+          const uint32_t w4[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            v[j][2 * q] = bf_lo(w4[q]);
+            v[j][2 * q + 1] = bf_hi(w4[q]);
+            ss += v[j][2 * q] * v[j][2 * q] + v[j][2 * q + 1] * v[j][2 * q + 1];
+          }
+        }
+        if (norm) {
+          const float inv = rsqrtf(sum64(ss) / float(K) + a.rms_eps);
+#pragma unroll
+          for (int j = 0; j < NE; j++) {
+            const uint32_t g4[4] = {gw[j].x, gw[j].y, gw[j].z, gw[j].w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              v[j][2 * q] *= inv * bf_lo(g4[q]);
+              v[j][2 * q + 1] *= inv * bf_hi(g4[q]);
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NE; j++) {
+          *reinterpret_cast<f4*>(xs + lane * 8 + 512 * j) = f4{v[j][0], v[j][1], v[j][2], v[j][3]};
+          *reinterpret_cast<f4*>(xs + lane * 8 + 512 * j + 4) = f4{v[j][4], v[j][5], v[j][6], v[j][7]};
+        }
+      } else {
+        // tagged activations: two values per lane per 16-byte load, 128 per
+        // wave-wide load; up to 2048 values per round
+        constexpr int NL = 16;
+        const __amdgpu_buffer_rsrc_t r = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), K * kActBytes);
+        float ss = 0.f;
+        const uint32_t rounds = (K + 128 * NL - 1) / (128 * NL);
+        for (uint32_t rd = 0; rd < rounds; rd++) {
+          const uint32_t base = rd * 128 * NL;
+          u4 t[NL];
+          uint32_t off[NL], gw[NL];
+#pragma unroll
+          for (int j = 0; j < NL; j++) {
+            off[j] = (base + 2 * lane + 128 * j) * kActBytes;
+            t[j] = ld_tag2(r, off[j]);
+            gw[j] = __builtin_amdgcn_raw_buffer_load_b32(rg, (base + 2 * lane + 128 * j) * 2, 0, 0);
+          }
+          const uint32_t live = (K - base) / 128 < uint32_t(NL) ? (K - base) / 128 : uint32_t(NL);
+          if (!wait_fresh(t, live, r, off, tag, c.retries)) return false;
+#pragma unroll
+          for (int j = 0; j < NL; j++) {
+            const float v0 = __uint_as_float(t[j].x), v1 = __uint_as_float(t[j].z);
+            ss += v0 * v0 + v1 * v1;
+            // raw values now; scaled below once the whole sum is known
+            if (j < int(live)) *reinterpret_cast<float2*>(xs + base + 2 * lane + 128 * j) = float2{v0, v1};
+          }
+          if (norm && rounds == 1) {
+            // one round: scale in place with the gains still in registers
+            const float inv = rsqrtf(sum64(ss) / float(K) + a.rms_eps);
+#pragma unroll
+            for (int j = 0; j < NL; j++) {
+              if (j >= int(live)) continue;
+              float2* px = reinterpret_cast<float2*>(xs + 2 * lane + 128 * j);
+              const float2 xv = *px;
+              *px = float2{xv.x * inv * bf_lo(gw[j]), xv.y * inv * bf_hi(gw[j])};
+            }
+          }
+        }
+        if (norm && rounds > 1) {
+          // several rounds: scale from LDS, gains read again (cached)
+          const float inv = rsqrtf(sum64(ss) / float(K) + a.rms_eps);
+          for (uint32_t o = 2 * lane; o < K; o += 128) {
+            const uint32_t gv = __builtin_amdgcn_raw_buffer_load_b32(rg, o * 2, 0, 0);
+            float2* px = reinterpret_cast<float2*>(xs + o);
+            const float2 xv = *px;
+            *px = float2{xv.x * inv * bf_lo(gv), xv.y * inv * bf_hi(gv)};
+          }
+        }
       }
     } else {
-      const __amdgpu_buffer_rsrc_t r = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), K * 4);
-      for (uint32_t o = lane * 4; o < K; o += 256) *reinterpret_cast<f4*>(xs + o) = ld_act4(r, o * 4);
-    }
-  } else {
-    const int hpg = a.hpg, dh = a.head_dim;
-    const uint32_t g = I->aux[0];
-    const float* qkv = reinterpret_cast<const float*>(I->in_ptr);
-    const uint32_t nq = hpg * dh;
-    const __amdgpu_buffer_rsrc_t rq = act_rsrc(qkv + g * nq, nq * 4);
-    for (uint32_t o = lane * 4; o < nq; o += 256) *reinterpret_cast<f4*>(xs + o) = ld_act4(rq, o * 4);
-    const __amdgpu_buffer_rsrc_t rk = act_rsrc(qkv + a.q_dim + g * dh, dh * 4);
-    const __amdgpu_buffer_rsrc_t rv = act_rsrc(qkv + a.q_dim + a.kv_dim + g * dh, dh * 4);
-    for (uint32_t o = lane * 4; o < uint32_t(dh); o += 256) {
-      *reinterpret_cast<f4*>(xs + nq + o) = ld_act4(rk, o * 4);
-      *reinterpret_cast<f4*>(xs + nq + dh + o) = ld_act4(rv, o * 4);
+      // attention: q, k, v of the group (tagged) and cos | sin (tables)
+      const int hpg = a.hpg, dh = a.head_dim;
+      const uint32_t g = I->aux[0];
+      const char* qkv = reinterpret_cast<const char*>(I->in_ptr);
+      const uint32_t nq = hpg * dh, half = dh / 2;
+      const __amdgpu_buffer_rsrc_t rq = act_rsrc(qkv + size_t(g) * nq * kActBytes, nq * kActBytes);
+      const __amdgpu_buffer_rsrc_t rk = act_rsrc(qkv + size_t(a.q_dim + g * dh) * kActBytes, dh * kActBytes);
+      const __amdgpu_buffer_rsrc_t rv =
+          act_rsrc(qkv + size_t(a.q_dim + a.kv_dim + g * dh) * kActBytes, dh * kActBytes);
+      const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.rope_cos + size_t(a.pos) * half), 0, half * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.rope_sin + size_t(a.pos) * half), 0, half * 4, 0x00020000);
+      static_assert(kMaxK >= 512, "q staging");
+      constexpr int NQ = 4;  // up to 512 q values
+      u4 tq[NQ], tk[1], tv[1];
+      uint32_t oq[NQ], ok1[1] = {lane * 16};
+#pragma unroll
+      for (int j = 0; j < NQ; j++) {
+        oq[j] = (2 * lane + 128 * j) * kActBytes;
+        tq[j] = ld_tag2(rq, oq[j]);
+      }
+      tk[0] = ld_tag2(rk, ok1[0]);
+      tv[0] = ld_tag2(rv, ok1[0]);
+      const f4 cv = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, 0, 0);
+      const f4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, (lane - half / 4) * 16, 0, 0);
+      const bool kv_lane = 2 * lane < uint32_t(dh);
+      const uint32_t q_live = nq > 2 * lane ? (nq - 2 * lane + 127) / 128 : 0;
+      if (!wait_fresh(tq, q_live, rq, oq, tag, c.retries)) return false;
+      if (!wait_fresh(tk, kv_lane ? 1 : 0, rk, ok1, tag, c.retries)) return false;
+      if (!wait_fresh(tv, kv_lane ? 1 : 0, rv, ok1, tag, c.retries)) return false;
+#pragma unroll
+      for (int j = 0; j < NQ; j++)
+        if (2 * lane + 128 * j < nq)
+          *reinterpret_cast<float2*>(xs + 2 * lane + 128 * j) =
+              float2{__uint_as_float(tq[j].x), __uint_as_float(tq[j].z)};
+      if (kv_lane) {
+        *reinterpret_cast<float2*>(xs + nq + 2 * lane) = float2{__uint_as_float(tk[0].x), __uint_as_float(tk[0].z)};
+        *reinterpret_cast<float2*>(xs + nq + dh + 2 * lane) =
+            float2{__uint_as_float(tv[0].x), __uint_as_float(tv[0].z)};
+      }
+      if (lane * 4 < uint32_t(dh)) *reinterpret_cast<f4*>(xs + nq + 2 * dh + lane * 4) = lane * 4 < half ? cv : sv;
     }
   }
+
+  if (has_res) {
+    float* rs = const_cast<float*>(res_slot(i));
+    if (!res_embed && !wait_fresh(res_t, res_live, rr, res_off, tag, c.retries)) return false;
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+      if (j < int(res_live))
+        rs[2 * lane + j] = res_embed ? __uint_as_float(uint32_t(res_e[j]) << 16) : __uint_as_float(res_t[j].x);
+  }
+  return true;
 }
 
+// ---- kernel variants
+// GeoAny: one kernel for every supported shape; the GEMV width, the KV
+// group size and the head dimension are dispatched per instruction.
+// GeoFix: the kernel for one shape.  Only the code paths that shape uses are
+// compiled, which keeps the kernel inside the register file (the generic
+// kernel spills) and its code small.  The runtime picks a GeoFix kernel when
+// every instruction of the plan matches it.
+struct GeoAny {
+  static constexpr bool any = true;
+};
+template <int ND, int RD, int NQ, int RQ, int NF, int RF, int H, int D>
+struct GeoFix {
+  static constexpr bool any = false;
+  static constexpr int nd = ND, rd = RD, nq = NQ, rq = RQ, nf = NF, rf = RF, hpg = H, dh = D;
+};
+
+template <class G>
 DEV bool run_gemv(Comp& c, InstrCP I, uint32_t i) {
-  if (i_rpu(I) == 2) return gemv<1, 2>(c, I, i);
-  switch (i_nit(I)) {
-    case 1: return gemv<1, 1>(c, I, i);
-    case 2: return gemv<2, 1>(c, I, i);
-    case 3: return gemv<3, 1>(c, I, i);
-    case 4: return gemv<4, 1>(c, I, i);
-    case 5: return gemv<5, 1>(c, I, i);
-    case 6: return gemv<6, 1>(c, I, i);
-    case 7: return gemv<7, 1>(c, I, i);
-    default: return gemv<8, 1>(c, I, i);
+  if constexpr (!G::any) {
+    const uint32_t nit = i_nit(I), rpu = i_rpu(I);
+    if (nit == uint32_t(G::nd) && rpu == uint32_t(G::rd)) return gemv<G::nd, G::rd>(c, I, i);
+    if (nit == uint32_t(G::nq) && rpu == uint32_t(G::rq)) return gemv<G::nq, G::rq>(c, I, i);
+    return gemv<G::nf, G::rf>(c, I, i);
+  } else {
+    if (i_rpu(I) == 2) return gemv<1, 2>(c, I, i);
+    switch (i_nit(I)) {
+      case 1: return gemv<1, 1>(c, I, i);
+      case 2: return gemv<2, 1>(c, I, i);
+      case 3: return gemv<3, 1>(c, I, i);
+      case 4: return gemv<4, 1>(c, I, i);
+      case 5: return gemv<5, 1>(c, I, i);
+      case 6: return gemv<6, 1>(c, I, i);
+      case 7: return gemv<7, 1>(c, I, i);
+      default: return gemv<8, 1>(c, I, i);
+    }
   }
 }
 
+template <class G>
 DEV bool run_attn(Comp& c, InstrCP I, uint32_t i) {
-  const int hpg = c.a->hpg, dh = c.a->head_dim;
-  if (dh == 64) {
-    switch (hpg) {
-      case 1: return attn<1, 64>(c, I, i);
-      case 2: return attn<2, 64>(c, I, i);
-      case 4: return attn<4, 64>(c, I, i);
-      default: return attn<8, 64>(c, I, i);
+  if constexpr (!G::any) {
+    return attn<G::hpg, G::dh>(c, I, i);
+  } else {
+    const int hpg = c.a->hpg, dh = c.a->head_dim;
+    if (dh == 64) {
+      switch (hpg) {
+        case 1: return attn<1, 64>(c, I, i);
+        case 2: return attn<2, 64>(c, I, i);
+        case 4: return attn<4, 64>(c, I, i);
+        default: return attn<8, 64>(c, I, i);
+      }
     }
-  }
-  switch (hpg) {
-    case 1: return attn<1, 128>(c, I, i);
-    case 2: return attn<2, 128>(c, I, i);
-    default: return attn<4, 128>(c, I, i);
+    switch (hpg) {
+      case 1: return attn<1, 128>(c, I, i);
+      case 2: return attn<2, 128>(c, I, i);
+      default: return attn<4, 128>(c, I, i);
+    }
   }
 }
 
+template <class G>
 DEV void run_merge(Comp& c, InstrCP I) {
-  const int hpg = c.a->hpg, dh = c.a->head_dim;
-  if (dh == 64) {
-    switch (hpg) {
-      case 1: return attn_merge<1, 64>(c, I);
-      case 2: return attn_merge<2, 64>(c, I);
-      case 4: return attn_merge<4, 64>(c, I);
-      default: return attn_merge<8, 64>(c, I);
+  if constexpr (!G::any) {
+    attn_merge<G::hpg, G::dh>(c, I);
+  } else {
+    const int hpg = c.a->hpg, dh = c.a->head_dim;
+    if (dh == 64) {
+      switch (hpg) {
+        case 1: return attn_merge<1, 64>(c, I);
+        case 2: return attn_merge<2, 64>(c, I);
+        case 4: return attn_merge<4, 64>(c, I);
+        default: return attn_merge<8, 64>(c, I);
+      }
     }
-  }
-  switch (hpg) {
-    case 1: return attn_merge<1, 128>(c, I);
-    case 2: return attn_merge<2, 128>(c, I);
-    default: return attn_merge<4, 128>(c, I);
+    switch (hpg) {
+      case 1: return attn_merge<1, 128>(c, I);
+      case 2: return attn_merge<2, 128>(c, I);
+      default: return attn_merge<4, 128>(c, I);
+    }
   }
 }
 
@@ -984,7 +1219,7 @@ DEV void lm_finish(Comp& c, InstrCP I) {
     st_act(a.lm_slots + 2 * tile + 1, __uint_as_float(b.i));
   }
   uint32_t old = 0;
-  if (lane == 0) old = ctr_add(a.counters + size_t(I->sig_ctr) * kCtrStride);
+  if (lane == 0) old = ctr_release(a.counters + size_t(I->sig_ctr) * kCtrStride);
   old = uni(old);
   if (old + 1 != a.epoch * n_tiles) return;
   ArgBest all{-__builtin_inff(), 0xFFFFFFFFu};
@@ -996,27 +1231,31 @@ DEV void lm_finish(Comp& c, InstrCP I) {
     const uint32_t oi = __shfl_xor(all.i, m, 64);
     arg_update(all, ov, oi);
   }
-  if (lane == 0) a.next[0] = int32_t(all.i);
+  if (lane == 0) *gp(a.next) = int32_t(all.i);
 }
 
+template <class G>
 DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
-  Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0, 0};
+  Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0, 0, 0};
   const bool tr = a.trace != nullptr;
   uint64_t staged_in = 0;          // leader: input currently in the x slot
   uint32_t staged_flags = 0, staged_k = 0;
+  uint64_t staged_gain = 0;
   uint32_t seen_ctr = kNoCounter, seen_val = 0;  // leader: last satisfied wait
   for (uint32_t i = 0; i < n; i++) {
     InstrCP I = q + i;
     if (w == 0) {
       // the staged input of the previous GEMV can be reused as is
       const bool reuse = i_op(I) == OP_GEMV && I->in_ptr == staged_in &&
-                         (i_flags(I) & (F_IN_EMBED | F_NORM)) == staged_flags && I->k == staged_k;
+                         (i_flags(I) & (F_IN_EMBED | F_NORM)) == staged_flags && I->k == staged_k &&
+                         (!(i_flags(I) & F_NORM) || I->gain_ptr == staged_gain);
       if (tr && c.lane == 0) {
         trace_put(a, cu, i, TR_START, now32());
         trace_put(a, cu, i, TR_HW0, hw0(I));
         trace_put(a, cu, i, TR_HW1, hw1(I));
       }
       c.pagewait = 0;
+      c.retries = 0;
       bool ok = true;
       for (int k = 0; k < 2 && ok; k++) {
         if (!I->wait_cnt[k]) continue;
@@ -1026,9 +1265,6 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
         seen_ctr = ctr;
         seen_val = target;
       }
-#if MK_SYNC_FENCED
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#endif
       if (tr && c.lane == 0) trace_put(a, cu, i, TR_DEPS, now32());
       // every compute wave has read the previous instruction's staged inputs
       // (the residual rows are restaged every time)
@@ -1037,27 +1273,40 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
         if (c.lane == 0) lds_st(C_ABORT, 1);
         return;
       }
-      stage_inputs(c, I, i, reuse);
+      if (tr && c.lane == 0) trace_put(a, cu, i, TR_XFREE, now32());
+      if (!stage_inputs(c, I, i, reuse)) {
+        if (c.lane == 0) lds_st(C_ABORT, 1);
+        return;
+      }
       if (i_op(I) == OP_GEMV) {
         staged_in = I->in_ptr;
         staged_flags = i_flags(I) & (F_IN_EMBED | F_NORM);
         staged_k = I->k;
+        staged_gain = I->gain_ptr;
       } else {
         staged_in = 0;
       }
       if (c.lane == 0) lds_st(C_XOK, i + 1);
-      if (tr && c.lane == 0) trace_put(a, cu, i, TR_STAGED, now32());
+      if (tr && c.lane == 0) {
+        trace_put(a, cu, i, TR_STAGED, now32());
+        trace_put(a, cu, i, TR_RETRY, c.retries);
+      }
     } else if (!wait_lds_ge(C_XOK, i + 1)) {
       return;
     }
-    bool ok = i_op(I) == OP_GEMV ? run_gemv(c, I, i) : run_attn(c, I, i);
+    bool ok = i_op(I) == OP_GEMV ? run_gemv<G>(c, I, i) : run_attn<G>(c, I, i);
     if (!ok) return;
     if (tr && w == 0 && c.lane == 0) {
       trace_put(a, cu, i, TR_ITEMS, now32());
       trace_put(a, cu, i, TR_PAGEWAIT, c.pagewait);
     }
-    // completion: the last wave signals
-    wait_vm0();
+    // completion: the last wave signals.  Tagged outputs need no wait; the
+    // untagged data behind a ticket (argmax slots, attention partials) must
+    // have landed before the ticket moves.
+    const bool release = (i_op(I) == OP_GEMV && i_epi(I) == EPI_ARGMAX) ||
+                         (i_op(I) == OP_ATTN && I->aux[3] > 1);
+    if (release) wait_vm0();
+    if (tr && w == 0 && c.lane == 0) trace_put(a, cu, i, TR_VISIBLE, now32());
     uint32_t prev = 0;
     if (c.lane == 0) prev = lds_add(C_DONE + 4 * (i % kDoneRing), 1);
     prev = uni(prev);
@@ -1069,18 +1318,18 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
     }
     if (i_op(I) == OP_ATTN && I->aux[3] > 1) {
       uint32_t old = 0;
-      if (c.lane == 0) old = ctr_add(a.counters + size_t(I->seg_rows[0]) * kCtrStride);
+      if (c.lane == 0) old = ctr_release(a.counters + size_t(I->seg_rows[0]) * kCtrStride);
       old = uni(old);
       if (old + 1 != a.epoch * I->aux[3]) continue;
-      run_merge(c, I);
-      wait_vm0();
+      run_merge<G>(c, I);
     }
-    if ((i_flags(I) & F_SIGNAL) && c.lane == 0) ctr_add(a.counters + size_t(I->sig_ctr) * kCtrStride);
+    if ((i_flags(I) & F_SIGNAL) && c.lane == 0) ctr_signal(a.counters + size_t(I->sig_ctr) * kCtrStride);
     if (tr && c.lane == 0) trace_put(a, cu, i, TR_SIGNAL, now32());
   }
 }
 
-extern "C" __global__ __launch_bounds__(kThreads, 1) void mk_megakernel(KArgs a) {
+template <class G>
+__global__ __launch_bounds__(kThreads, 1) void mk_megakernel(KArgs a) {
   for (int o = threadIdx.x * 4; o < C_CTRL_END; o += kThreads * 4) *lw(o) = 0;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -1097,7 +1346,7 @@ extern "C" __global__ __launch_bounds__(kThreads, 1) void mk_megakernel(KArgs a)
   if (wave < kNLoad)
     loader(a, q, end - beg, wave);
   else
-    compute(a, q, end - beg, wave - kNLoad, cu);
+    compute<G>(a, q, end - beg, wave - kNLoad, cu);
 }
 
 // Plan-time fill of the packed weight stream: one workgroup column per copy,
@@ -1127,21 +1376,50 @@ extern "C" hipError_t mk_launch_pack(const mk::PackCopy* copies, uint32_t n, voi
   return hipGetLastError();
 }
 
-// Launch entry used by the runtime (not part of the public ABI).
+// ---- kernel table (used by the runtime; not part of the public ABI)
+namespace {
+struct Variant {
+  int nd, rd, nq, rq, nf, rf, hpg, dh;  // 0 = generic
+  const void* fn;
+};
+// Shapes with their own kernel: the Llama-3.2-1B shape (MLP in two chunks),
+// the Llama-3-8B shape (four chunks) and the small test decoder (one chunk).
+const Variant kVariants[] = {
+    {0, 0, 0, 0, 0, 0, 0, 0, reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoAny>)},
+    {4, 1, 4, 1, 8, 1, 4, 64,
+     reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoFix<4, 1, 4, 1, 8, 1, 4, 64>>)},
+    {8, 1, 8, 1, 7, 1, 4, 128,
+     reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoFix<8, 1, 8, 1, 7, 1, 4, 128>>)},
+    {1, 2, 1, 2, 2, 1, 2, 64,
+     reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoFix<1, 2, 1, 2, 2, 1, 2, 64>>)},
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+bool g_attr_set[kNumVariants] = {};
+}  // namespace
+
+// Index of the kernel built for this geometry, or 0 (the generic kernel).
+extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpg, int dh) {
+  for (int v = 1; v < kNumVariants; v++) {
+    const Variant& k = kVariants[v];
+    if (k.nd == nd && k.rd == rd && k.nq == nq && k.rq == rq && k.nf == nf && k.rf == rf && k.hpg == hpg &&
+        k.dh == dh)
+      return v;
+  }
+  return 0;
+}
+
 extern "C" hipError_t mk_launch_megakernel(const mk::KArgs* args, int n_cus, hipStream_t stream,
-                                           int cooperative) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mk::mk_megakernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, mk::kLdsTotal);
+                                           int cooperative, int variant) {
+  if (variant < 0 || variant >= kNumVariants) return hipErrorInvalidValue;
+  const void* fn = kVariants[variant].fn;
+  if (!g_attr_set[variant]) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, mk::kLdsTotal);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    g_attr_set[variant] = true;
   }
   mk::KArgs a = *args;
   void* params[] = {&a};
   if (cooperative)
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mk::mk_megakernel), dim3(n_cus),
-                                      dim3(mk::kThreads), params, mk::kLdsTotal, stream);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&mk::mk_megakernel), dim3(n_cus),
-                         dim3(mk::kThreads), params, mk::kLdsTotal, stream);
+    return hipLaunchCooperativeKernel(fn, dim3(n_cus), dim3(mk::kThreads), params, mk::kLdsTotal, stream);
+  return hipLaunchKernel(fn, dim3(n_cus), dim3(mk::kThreads), params, mk::kLdsTotal, stream);
 }

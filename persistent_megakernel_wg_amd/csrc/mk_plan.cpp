@@ -92,6 +92,14 @@ Instr blank() {
 
 }  // namespace
 
+bool gemv_geometry(int K, int* nit, int* rpu) {
+  Geo g;
+  if (!geo_for_k(K, &g)) return false;
+  *nit = g.nit;
+  *rpu = g.rpu;
+  return true;
+}
+
 // ------------------------------------------------------------------ config
 mk_status check_config(const mk_config& c, std::string* err) {
   auto bad = [&](const char* m) {
@@ -123,12 +131,14 @@ mk_status check_config(const mk_config& c, std::string* err) {
     return MK_ERR_UNSUPPORTED;
   }
   const int hpg = c.n_q_heads / c.n_kv_heads;
-  if (hpg * c.head_dim > 1024) {
-    *err = "config: at most 1024 query values per KV group";
+  if ((hpg & (hpg - 1)) || hpg > 8 || hpg * c.head_dim > 512) {
+    *err = "config: query heads per KV group must be 1, 2, 4 or 8, with at most 512 query values per group";
     return MK_ERR_UNSUPPORTED;
   }
-  if ((hpg + 2) * c.head_dim * 4 > kLdsXBytes) {
-    *err = "config: q/k/v of one KV group exceed the staging buffer";
+  // the x slot holds q, k, v, cos, sin of a group, then the value-pass
+  // partials of every compute wave
+  if ((hpg + 3) * c.head_dim * 4 > kLdsXBytes || hpg * c.head_dim * kNComp > kMaxK) {
+    *err = "config: one KV group exceeds the staging buffer";
     return MK_ERR_UNSUPPORTED;
   }
   if (c.vocab % 2 || c.hidden % 2) return bad("config: vocab and hidden must be even");
@@ -141,12 +151,17 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
   if (o) r = *o;
   r.n_cus = n_cus;
   if (r.mlp_chunks <= 0) {
-    r.mlp_chunks = 4;
-    // fall back to fewer chunks if the chunk width has no code path
-    while (r.mlp_chunks > 1) {
+    // the fewest chunks whose width has a GEMV code path: every chunk costs
+    // each CU one more gate/up and one more down instruction (staging, item
+    // latency, a signal), which outweighs the earlier start of the down
+    // projection that more chunks allow
+    r.mlp_chunks = 1;
+    for (int ch = 1; ch <= 64; ch *= 2) {
       Geo g;
-      if (c.ffn % r.mlp_chunks == 0 && geo_for_k(c.ffn / r.mlp_chunks, &g)) break;
-      r.mlp_chunks /= 2;
+      if (c.ffn % ch == 0 && geo_for_k(c.ffn / ch, &g)) {
+        r.mlp_chunks = ch;
+        break;
+      }
     }
   }
   if (r.attn_block <= 0) {
@@ -177,12 +192,14 @@ ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
     off = align256(off + bytes);
     return r;
   };
-  for (int l = 1; l <= c.n_layers; l++) a.x[l] = take(4 * d);
+  // tagged activations first: the runtime clears [0, rope_cos) to reset tags
+  const uint64_t E = kActBytes;
+  for (int l = 1; l <= c.n_layers; l++) a.x[l] = take(E * d);
   for (int l = 0; l < c.n_layers; l++) {
-    a.qkv[l] = take(4 * (q + 2 * kv));
-    a.o[l] = take(4 * q);
-    a.h[l] = take(4 * d);
-    a.m[l] = take(4 * F);
+    a.qkv[l] = take(E * (q + 2 * kv));
+    a.o[l] = take(E * q);
+    a.h[l] = take(E * d);
+    a.m[l] = take(E * F);
     a.part[l] = take(4 * uint64_t(max_parts) * hpg * (c.head_dim + 2));
   }
   a.rope_cos = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
@@ -482,7 +499,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
           I.seg_stride[0] = uint32_t(2 * F);
           I.aux[0] = acc_off;  // LDS accumulator offset
           I.aux[4] = 1;
-          I.in_ptr = A + ar.m[l] + 4ull * ch * Fc;
+          I.in_ptr = A + ar.m[l] + uint64_t(kActBytes) * ch * Fc;
           I.res_ptr = A + ar.h[l];
           I.out_ptr = A + ar.x[l + 1];
           set_wait(I, 0, c_gu[l][ch]);
@@ -843,7 +860,7 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
             return fail(m.str());
           }
         }
-        const uint64_t kb = 4ull * I.k;
+        const uint64_t kb = uint64_t(kActBytes) * I.k;
         if (I.flags & F_IN_EMBED) {
           if (I.in_ptr != uint64_t(in.w.embed)) return fail("embedding input pointer");
         } else if (!in_arena(I.in_ptr, I.in_ptr + kb)) {
@@ -851,11 +868,11 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         }
         uint64_t out_rows = I.rpu == 2 && I.epi != EPI_SWIGLU ? uint64_t(I.n_items) * 2 : I.n_items;
         if (I.epi != EPI_ARGMAX && I.epi != EPI_ACC_FIRST && I.epi != EPI_ACC_MID &&
-            !in_arena(I.out_ptr + 4ull * I.row0, I.out_ptr + 4ull * (I.row0 + out_rows)))
+            !in_arena(I.out_ptr + uint64_t(kActBytes) * I.row0, I.out_ptr + uint64_t(kActBytes) * (I.row0 + out_rows)))
           return fail("GEMV output outside the arena");
         if ((I.epi == EPI_RESID || I.epi == EPI_ACC_ONLY || I.epi == EPI_ACC_FIRST) &&
             !(I.flags & F_RES_EMBED) &&
-            !in_arena(I.res_ptr + 4ull * I.row0, I.res_ptr + 4ull * (I.row0 + out_rows)))
+            !in_arena(I.res_ptr + uint64_t(kActBytes) * I.row0, I.res_ptr + uint64_t(kActBytes) * (I.row0 + out_rows)))
           return fail("GEMV residual outside the arena");
         if ((I.epi == EPI_ACC_FIRST || I.epi == EPI_ACC_MID || I.epi == EPI_ACC_LAST) &&
             I.aux[0] + out_rows > 256)
@@ -872,7 +889,8 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         if (I.aux[3] > 1 &&
             !in_arena(I.res_ptr, I.res_ptr + rec * (uint64_t(I.aux[0]) * I.aux[3] + I.aux[3])))
           return fail("attention partials outside the arena");
-        if (!in_arena(I.in_ptr, I.in_ptr + 4 * (qd + 2 * kvd)) || !in_arena(I.out_ptr, I.out_ptr + 4 * qd))
+        if (!in_arena(I.in_ptr, I.in_ptr + uint64_t(kActBytes) * (qd + 2 * kvd)) ||
+            !in_arena(I.out_ptr, I.out_ptr + uint64_t(kActBytes) * qd))
           return fail("attention activations outside the arena");
       }
     }

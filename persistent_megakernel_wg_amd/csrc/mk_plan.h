@@ -93,6 +93,10 @@ std::string plan_report(const PlanInput& in, const Plan& p);
 
 void summarize(const PlanInput& in, const Plan& p, mk_plan_summary* s);
 
+// GEMV row geometry for input length K: 1 KiB units per row (nit) and rows
+// per unit (rpu).  false if the kernel has no code path for K.
+bool gemv_geometry(int K, int* nit, int* rpu);
+
 // Resolved defaults for the options.
 mk_plan_opts resolve_opts(const mk_config& cfg, const mk_plan_opts* opts, int n_cus);
 

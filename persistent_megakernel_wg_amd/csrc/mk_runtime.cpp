@@ -13,7 +13,8 @@
 #include "mk_plan.h"
 
 extern "C" hipError_t mk_launch_megakernel(const mk::KArgs* args, int n_cus, hipStream_t stream,
-                                           int cooperative);
+                                           int cooperative, int variant);
+extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpg, int dh);
 extern "C" hipError_t mk_launch_pack(const mk::PackCopy* copies, uint32_t n, void* base,
                                      hipStream_t stream);
 
@@ -37,6 +38,7 @@ struct mk_ctx {
   hipStream_t last_stream = nullptr;
   bool has_step = false;
   int cooperative = 1;
+  int variant = 0;        // kernel launched for the current plan
   uint32_t* d_trace = nullptr;
   uint32_t trace_stride = 0;
 };
@@ -88,6 +90,17 @@ void rope_tables(const mk_config& cfg, std::vector<float>* cs, std::vector<float
       (*sn)[size_t(p) * half + j] = float(std::sin(ang));
     }
   }
+}
+
+// The shape-specific kernel for this plan, or 0 (the generic kernel).
+int variant_for(const mk_config& cfg, const mk_plan_opts& o) {
+  if (o.generic_kernel) return 0;
+  int nd, rd, nq, rq, nf, rf;
+  if (!mk::gemv_geometry(cfg.hidden, &nd, &rd) ||
+      !mk::gemv_geometry(cfg.n_q_heads * cfg.head_dim, &nq, &rq) ||
+      !mk::gemv_geometry(cfg.ffn / o.mlp_chunks, &nf, &rf))
+    return 0;
+  return mk_pick_variant(nd, rd, nq, rq, nf, rf, cfg.n_q_heads / cfg.n_kv_heads, cfg.head_dim);
 }
 
 bool dense_pointers_ok(const mk_weights& w) {
@@ -203,6 +216,7 @@ mk_status mk_build_plan(mk_ctx* c, const mk_plan_opts* opts) {
     return hip_fail(c, e, "mk_build_plan upload");
   }
   c->epoch = 0;
+  c->variant = variant_for(c->cfg, in.opts);
   c->planned = true;
   return MK_OK;
 }
@@ -243,7 +257,7 @@ mk_status mk_decode_step(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_
   a.trace_stride = c->trace_stride;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = mk_launch_megakernel(&a, p.n_cus, s, c->cooperative);
+  hipError_t e = mk_launch_megakernel(&a, p.n_cus, s, c->cooperative, c->variant);
   if (e != hipSuccess) return hip_fail(c, e, "launch");
   c->epoch++;
   c->last_stream = s;
@@ -277,9 +291,11 @@ mk_status mk_sync(mk_ctx* c) {
     std::snprintf(msg, sizeof(msg), "device: NaN logits in the LM head");
     st = MK_ERR_DEVICE;
   }
-  // reset so the context can be used again
+  // reset so the context can be used again: counters, status and the
+  // activation tags (the step count restarts at 1)
   const size_t ctr_bytes = size_t(std::max(1, c->plan.n_counters)) * mk::kCtrStride * 4;
   (void)hipMemset(c->d_counters, 0, ctr_bytes);
+  (void)hipMemset(c->arena, 0, c->plan.arena.rope_cos);
   (void)hipMemset(c->arena + c->plan.arena.status, 0, 64);
   (void)hipDeviceSynchronize();
   c->epoch = 0;
@@ -331,6 +347,7 @@ mk_status mk_plan_info(const mk_ctx* c, mk_plan_summary* out) {
   if (!c || !out) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_plan_info: NULL argument");
   if (!c->planned) return fail(const_cast<mk_ctx*>(c), MK_ERR_NO_PLAN, "mk_plan_info: no plan");
   mk::summarize(c->pin, c->plan, out);
+  out->kernel_variant = c->variant;
   return MK_OK;
 }
 
@@ -361,7 +378,10 @@ mk_status mk_plan_check(const mk_config* cfg, const mk_plan_opts* opts, int32_t 
   if (st == MK_OK && in.opts.debug_corrupt_target) mk::corrupt_one_target(&p);
   if (st == MK_OK) st = mk::verify_plan(in, p, &err);
   if (st != MK_OK) return fail(nullptr, st, err);
-  if (summary) mk::summarize(in, p, summary);
+  if (summary) {
+    mk::summarize(in, p, summary);
+    summary->kernel_variant = variant_for(*cfg, in.opts);
+  }
   if (report && report_len) {
     std::string r = mk::plan_report(in, p);
     std::snprintf(report, report_len, "%s", r.c_str());

@@ -96,6 +96,26 @@ def test_tiny_step_two_chunks_odd_cus(need_gpu):
     _one_step_case(synth.SHAPES["tiny"], n_cus=37, mlp_chunks=2, attn_block=64)
 
 
+def test_tiny_step_generic_kernel(need_gpu):
+    # the kernel built for every shape, on the shape that has its own kernel
+    _one_step_case(synth.SHAPES["tiny"], generic_kernel=1)
+    _one_step_case(synth.SHAPES["tiny"], generic_kernel=1, attn_block=64, n_cus=37)
+
+
+def test_tiny_step_four_chunks(need_gpu):
+    # first / middle / last down-projection accumulations
+    _one_step_case(synth.SHAPES["tiny"], mlp_chunks=4)
+
+
+@pytest.mark.parametrize("heads", [(4, 4, 64), (8, 2, 64), (8, 1, 64), (4, 2, 128), (4, 1, 128)])
+def test_tiny_step_head_layouts(need_gpu, heads):
+    # every attention code path: 1, 2, 4, 8 query heads per KV group, Dh 64/128
+    h, g, dh = heads
+    s = synth.SHAPES["tiny"].replace(n_q_heads=h, n_kv_heads=g, head_dim=dh)
+    _one_step_case(s)
+    _one_step_case(s, attn_block=64)
+
+
 def test_tiny_step_one_cu(need_gpu):
     # the whole decoder on one workgroup: split residual tiles, long queue
     _one_step_case(synth.SHAPES["tiny"], n_cus=1)

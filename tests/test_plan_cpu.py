@@ -35,7 +35,12 @@ def test_default_plan_verifies(name):
     r = json.loads(rep)
     assert summ["n_cus"] == 256 and len(r["queue_lengths"]) == 256
     assert summ["weight_bytes"] == synth.weight_bytes_per_step(s)
-    assert summ["mlp_chunks"] == 4
+    # the shape-specific kernels: 1B, 8B, the small test decoder
+    assert summ["kernel_variant"] == {"tiny": 3, "llama1b_ctx128": 1, "llama1b_ctx8192": 1,
+                                      "llama8b_ctx2048": 2}[name]
+    # default: the fewest chunks of at most 4096 values
+    assert summ["mlp_chunks"] == {"tiny": 1, "llama1b_ctx128": 2, "llama1b_ctx8192": 2,
+                                  "llama8b_ctx2048": 4}[name]
     assert summ["lds_bytes"] <= 160 * 1024
     # every CU streams about the same number of bytes (the tiny decoder has
     # fewer rows than there are CUs, so it cannot be balanced)
