@@ -20,7 +20,13 @@ constexpr int kUnit = 1024;          // bytes per wave-wide 16 B/lane DMA
 constexpr int kPageBytes = 16384;    // LDS page (16 KiB, as on the pages' design)
 constexpr int kUnitsPerPage = kPageBytes / kUnit;
 constexpr int kPages = 8;            // pages in the LDS ring
-constexpr int kCtrStride = 32;       // u32 per counter (128 B apart)
+constexpr int kCtrStride = 32;       // u32 per counter line (128 B apart)
+// A counter is kCtrSpread lines: a producer on CU c adds to line
+// c % kCtrSpread and a waiter sums the lines.  Many producers adding to one
+// line serialise on it (256 atomics on one address take several
+// microseconds); spread, each line takes a sixteenth of them.  Tickets
+// (counters whose returned value picks the last arriver) use line 0 only.
+constexpr int kCtrSpread = 16;
 constexpr int kMaxK = 4096;          // largest GEMV input length
 constexpr int kDoneRing = 4;         // per-instruction completion counters
 // Activation element in global memory: fp32 value | u32 tag (the step that
@@ -131,7 +137,7 @@ struct PackCopy {
 struct KArgs {
   const Instr* instrs;      // all queues back to back
   const uint32_t* q_off;    // [n_cus + 1] queue offsets
-  uint32_t* counters;       // [n_ctr * kCtrStride]
+  uint32_t* counters;       // [n_ctr][kCtrSpread][kCtrStride]
   uint32_t* status;         // [16] error record
   const int32_t* tokens;    // [B]
   int32_t* next;            // [B]

@@ -240,11 +240,24 @@ DEV void record_timeout(const KArgs& a, int cu, uint32_t instr, uint32_t ctr, ui
 }
 
 // Wait until counter >= target (wrap-safe).  false = watchdog or abort.
+DEV uint32_t* ctr_line(const KArgs& a, uint32_t ctr, uint32_t line) {
+  return a.counters + (size_t(ctr) * kCtrSpread + line) * kCtrStride;
+}
+// sum of the counter's lines (lanes 0 .. kCtrSpread-1 load one line each)
+DEV uint32_t ctr_sum(const KArgs& a, uint32_t ctr) {
+  static_assert(kCtrSpread == 16, "one DPP row per counter");
+  const uint32_t lane = threadIdx.x & 63;
+  int v = lane < uint32_t(kCtrSpread) ? int(ctr_load(ctr_line(a, ctr, lane))) : 0;
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, true);  // row_ror:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, true);  // row_ror:8
+  return uint32_t(__builtin_amdgcn_readlane(v, 0));
+}
 DEV bool wait_counter(const KArgs& a, uint32_t ctr, uint32_t target, int cu, uint32_t instr) {
-  const uint32_t* p = a.counters + size_t(ctr) * kCtrStride;
   uint64_t t0 = 0;
   for (uint32_t it = 0;; it++) {
-    uint32_t v = uni(ctr_load(p));
+    const uint32_t v = ctr_sum(a, ctr);
     if (int32_t(v - target) >= 0) return true;
     // The clock is a scalar memory read: read it every 64 polls only, so that
     // a poll is not held up by its latency.
@@ -406,8 +419,15 @@ DEV void load_view(const KArgs& a, InstrCP I, LoadView& L) {
 // issue order, so every DMA older than the last kVmT has landed in LDS.
 // Issuing one DMA per wait (rather than a page-sized burst per wait) keeps
 // the request stream smooth; bursts streamed at well under half the rate.
-constexpr uint32_t kVmT = 24;
-static_assert(kVmT % kDmaPerPage == 0, "kVmT is a whole number of pages");
+#ifndef MK_VMT
+#define MK_VMT 8
+#endif
+#define MK_STR2(x) #x
+#define MK_STR(x) MK_STR2(x)
+#define MK_THROTTLE "s_waitcnt vmcnt(" MK_STR(MK_VMT) ")"
+constexpr uint32_t kVmT = MK_VMT;
+static_assert(kVmT % kDmaPerPage == 0 && kVmT >= kDmaPerPage && kVmT <= 48,
+              "kVmT is a whole number of pages within the vmcnt range");
 
 // Eight DMAs of 8 consecutive 1 KiB units starting at `src` into LDS at
 // `lds_addr`.  The instruction offset moves the global source and the LDS
@@ -415,25 +435,24 @@ static_assert(kVmT % kDmaPerPage == 0, "kVmT is a whole number of pages");
 // a VGPR offset 4 KiB higher and M0 + 4 KiB.  Each DMA is followed by the
 // in-flight throttle (a no-op while fewer than kVmT DMAs are outstanding).
 DEV void dma_run8(uint32_t lds_addr, uint64_t src, uint32_t voff, uint32_t voff4k) {
-  static_assert(kVmT == 24, "the throttle below is written for kVmT = 24");
   asm volatile(
       "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %3\n\ts_waitcnt vmcnt(24)\n\t"
-      "global_load_lds_dwordx4 %1, %3 offset:1024\n\ts_waitcnt vmcnt(24)\n\t"
-      "global_load_lds_dwordx4 %1, %3 offset:2048\n\ts_waitcnt vmcnt(24)\n\t"
-      "global_load_lds_dwordx4 %1, %3 offset:3072\n\ts_waitcnt vmcnt(24)\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:1024\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:2048\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:3072\n\t" MK_THROTTLE "\n\t"
       "s_add_u32 m0, %0, 0x1000\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\ts_waitcnt vmcnt(24)\n\t"
-      "global_load_lds_dwordx4 %2, %3 offset:1024\n\ts_waitcnt vmcnt(24)\n\t"
-      "global_load_lds_dwordx4 %2, %3 offset:2048\n\ts_waitcnt vmcnt(24)\n\t"
-      "global_load_lds_dwordx4 %2, %3 offset:3072\n\ts_waitcnt vmcnt(24)"
+      "global_load_lds_dwordx4 %2, %3\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:1024\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:2048\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:3072\n\t" MK_THROTTLE
       :
       : "s"(lds_addr), "v"(voff), "v"(voff4k), "s"(src)
       : "memory", "m0");
 }
 
 DEV void vm_throttle(uint32_t& nd) {
-  if (++nd > kVmT) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  if (++nd > kVmT) asm volatile(MK_THROTTLE ::: "memory");
 }
 
 // Issue this loader wave's half of page p (units v*8 .. v*8+7): one
@@ -1219,7 +1238,7 @@ DEV void lm_finish(Comp& c, InstrCP I) {
     st_act(a.lm_slots + 2 * tile + 1, __uint_as_float(b.i));
   }
   uint32_t old = 0;
-  if (lane == 0) old = ctr_release(a.counters + size_t(I->sig_ctr) * kCtrStride);
+  if (lane == 0) old = ctr_release(ctr_line(a, I->sig_ctr, 0));
   old = uni(old);
   if (old + 1 != a.epoch * n_tiles) return;
   ArgBest all{-__builtin_inff(), 0xFFFFFFFFu};
@@ -1318,12 +1337,12 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
     }
     if (i_op(I) == OP_ATTN && I->aux[3] > 1) {
       uint32_t old = 0;
-      if (c.lane == 0) old = ctr_release(a.counters + size_t(I->seg_rows[0]) * kCtrStride);
+      if (c.lane == 0) old = ctr_release(ctr_line(a, I->seg_rows[0], 0));
       old = uni(old);
       if (old + 1 != a.epoch * I->aux[3]) continue;
       run_merge<G>(c, I);
     }
-    if ((i_flags(I) & F_SIGNAL) && c.lane == 0) ctr_signal(a.counters + size_t(I->sig_ctr) * kCtrStride);
+    if ((i_flags(I) & F_SIGNAL) && c.lane == 0) ctr_signal(ctr_line(a, I->sig_ctr, uint32_t(cu) % kCtrSpread));
     if (tr && c.lane == 0) trace_put(a, cu, i, TR_SIGNAL, now32());
   }
 }

@@ -207,7 +207,7 @@ mk_status mk_build_plan(mk_ctx* c, const mk_plan_opts* opts) {
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (d_copies) (void)hipFree(d_copies);
   }
-  const size_t ctr_bytes = size_t(std::max(1, p.n_counters)) * mk::kCtrStride * 4;
+  const size_t ctr_bytes = size_t(std::max(1, p.n_counters)) * mk::kCtrSpread * mk::kCtrStride * 4;
   if (e == hipSuccess) e = hipMalloc(&c->d_counters, ctr_bytes);
   if (e == hipSuccess) e = hipMemset(c->d_counters, 0, ctr_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -293,7 +293,7 @@ mk_status mk_sync(mk_ctx* c) {
   }
   // reset so the context can be used again: counters, status and the
   // activation tags (the step count restarts at 1)
-  const size_t ctr_bytes = size_t(std::max(1, c->plan.n_counters)) * mk::kCtrStride * 4;
+  const size_t ctr_bytes = size_t(std::max(1, c->plan.n_counters)) * mk::kCtrSpread * mk::kCtrStride * 4;
   (void)hipMemset(c->d_counters, 0, ctr_bytes);
   (void)hipMemset(c->arena, 0, c->plan.arena.rope_cos);
   (void)hipMemset(c->arena + c->plan.arena.status, 0, 64);
