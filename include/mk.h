@@ -109,7 +109,10 @@ typedef struct {
   int32_t generic_kernel; /* 1: always launch the kernel built for every shape
                              (default 0: the kernel built for this shape when
                              the library has one; see kernel_variant) */
-  int32_t reserved[2];
+  int32_t attn_heads; /* query heads per attention tile, dividing the heads per
+                         KV group (default: 1 while n_q_heads * position
+                         blocks <= n_cus, else the whole group) */
+  int32_t reserved;
 } mk_plan_opts;
 
 /* Plan summary (filled by mk_plan_info / mk_plan_check). */

@@ -45,7 +45,7 @@ class MkWeights(ctypes.Structure):
 class MkPlanOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_cus", "mlp_chunks", "attn_block", "watchdog_ms", "debug_corrupt_target",
-        "generic_kernel")] + [("reserved", ctypes.c_int32 * 2)]
+        "generic_kernel", "attn_heads")] + [("reserved", ctypes.c_int32)]
 
 
 class MkPlanSummary(ctypes.Structure):
@@ -113,10 +113,10 @@ def config_from_shape(shape) -> MkConfig:
 
 
 def plan_opts(n_cus=0, mlp_chunks=0, attn_block=0, watchdog_ms=0, debug_corrupt_target=0,
-              generic_kernel=0):
+              generic_kernel=0, attn_heads=0):
     return MkPlanOpts(n_cus=n_cus, mlp_chunks=mlp_chunks, attn_block=attn_block,
                       watchdog_ms=watchdog_ms, debug_corrupt_target=debug_corrupt_target,
-                      generic_kernel=generic_kernel)
+                      generic_kernel=generic_kernel, attn_heads=attn_heads)
 
 
 # ------------------------------------------------------------ the C entry points

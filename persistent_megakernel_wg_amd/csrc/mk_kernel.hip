@@ -687,21 +687,23 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
 }
 
 // ---- attention: one KV group, one position block
-// The x slot holds, staged by the leader: q [HPG*Dh] | k [Dh] | v [Dh] of the
+// The x slot holds, staged by the leader: q [HPT*Dh] of the tile's heads | k [Dh] | v [Dh] of the
 // group | cos [Dh/2] | sin [Dh/2] of the position.  After the query and the
 // new row are in registers the x slot is reused for the value-pass partials,
 // so the instruction releases it (C_XCONS) only at its end.
-template <int HPG, int DH>
+template <int HPT, int DH>
 DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane;
   constexpr int LPRA = DH / 8;            // lanes per cached row (8 dims per lane)
   constexpr int UPOS = kUnit / (2 * DH);  // rows per 1 KiB unit
   constexpr int HALF = DH / 2;
-  constexpr int OUT = HPG * DH;           // outputs of the group
+  constexpr int OUT = HPT * DH;           // outputs of the group
   constexpr int PER = OUT / 64;           // value-pass outputs per lane
   static_assert(PER >= 1 && PER <= 8 && OUT * kNComp <= kMaxK, "attention shape");
   const uint32_t g = I->aux[0], blk = I->aux[1], Bat = I->aux[2], nblk = I->aux[3], kp = I->aux[4];
+  const uint32_t h0 = I->row0;                  // first query head of the tile in its group
+  const uint32_t head0 = g * uint32_t(a.hpg) + h0;  // ... in the layer
   const int32_t P = a.pos;
   const int32_t p0 = int32_t(blk * Bat);
   int32_t nc = P - p0;
@@ -709,11 +711,11 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
   const bool own = P >= p0 && P < p0 + int32_t(Bat);
   const int32_t ntot = nc + (own ? 1 : 0);
   float* xs = reinterpret_cast<float*>(lds + kLdsX);
-  float* scores = reinterpret_cast<float*>(lds + kLdsAttn);     // [HPG][Bat]
+  float* scores = reinterpret_cast<float*>(lds + kLdsAttn);     // [HPT][Bat]
   uint16_t* newv = reinterpret_cast<uint16_t*>(lds + kLdsAttn + 8192);
   float* stat_m = reinterpret_cast<float*>(lds + kLdsAttn + 8192 + 512);
   float* stat_l = stat_m + 8;
-  const float* cs = xs + HPG * DH + 2 * DH;
+  const float* cs = xs + HPT * DH + 2 * DH;
   const float* sn = cs + HALF;
   const uint32_t s = lane % LPRA;        // dims [8s, 8s+8)
   const uint32_t jrow = lane / LPRA;     // row within a unit
@@ -744,14 +746,14 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
 #pragma unroll
     for (int e = 0; e < 8; e++) o[e] = (self[e] * cv[e] + sgn * part[e] * sv[e]) * scale;
   };
-  float qr[HPG][8];
+  float qr[HPT][8];
 #pragma unroll
-  for (int h = 0; h < HPG; h++) rot8(xs + h * DH, qr[h], a.attn_scale);
+  for (int h = 0; h < HPT; h++) rot8(xs + h * DH, qr[h], a.attn_scale);
   // the new key/value row, rounded to bf16
   float kr[8], vr[8], kn[8];
   uint16_t kb[8], vb[8];
-  rot8(xs + HPG * DH, kr, 1.f);
-  ld8(xs + HPG * DH + DH + d0, vr);
+  rot8(xs + HPT * DH, kr, 1.f);
+  ld8(xs + HPT * DH + DH + d0, vr);
 #pragma unroll
   for (int e = 0; e < 8; e++) {
     kb[e] = f2bf(kr[e]);
@@ -769,21 +771,23 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
                                                (u % kUnitsPerPage) * kUnit + lane * 16);
     const uint32_t p = u * UPOS + jrow;
 #pragma unroll
-    for (int h = 0; h < HPG; h++) {
+    for (int h = 0; h < HPT; h++) {
       const float d = group_sum<LPRA>(dot8(kw, qr[h]));
       if (s == 0 && p < uint32_t(nc)) scores[h * Bat + p] = d;
     }
   }
   if (own && uint32_t(c.w) == n_units % kNComp) {
+    // (every tile of the group scores the new row; the one holding the
+    // group's first head appends it to the cache)
 #pragma unroll
-    for (int h = 0; h < HPG; h++) {
+    for (int h = 0; h < HPT; h++) {
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e++) d = fmaf(qr[h][e], kn[e], d);
       d = group_sum<LPRA>(d);
       if (lane == 0) scores[h * Bat + nc] = d;
     }
-    if (lane < uint32_t(LPRA)) {
+    if (lane < uint32_t(LPRA) && h0 == 0) {
       const size_t row = size_t(P) * DH + 8 * s;
       uint16_t* kc = reinterpret_cast<uint16_t*>(I->seg_ptr[0]) + row;
       uint16_t* vc = reinterpret_cast<uint16_t*>(I->seg_ptr[1]) + row;
@@ -794,6 +798,8 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
       vv.z = vb[4] | uint32_t(vb[5]) << 16; vv.w = vb[6] | uint32_t(vb[7]) << 16;
       *gp(reinterpret_cast<u4*>(kc)) = kk;
       *gp(reinterpret_cast<u4*>(vc)) = vv;
+    }
+    if (lane < uint32_t(LPRA)) {
 #pragma unroll
       for (int e = 0; e < 8; e++) newv[8 * s + e] = vb[e];
     }
@@ -804,7 +810,7 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
 
   // pass 2: per head (heads round-robin over the waves) the maximum, the
   // weights exp(score - max) in place of the scores, and their sum
-  for (int h = c.w; h < HPG; h += kNComp) {
+  for (int h = c.w; h < HPT; h += kNComp) {
     float m = -__builtin_inff();
     for (int32_t p = lane; p < ntot; p += 64) m = fmaxf(m, scores[h * Bat + p]);
     m = max64(m);
@@ -831,8 +837,9 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
 #pragma unroll
   for (int e = 0; e < PER; e++) acc[e] = 0.f;
   if (kp && !wait_page(I->page0 + 2 * kp - 1, c.fcache)) return false;
-  for (int32_t p = c.w; p < ntot; p += kNComp) {
-    const float wp = scores[h3 * Bat + p];
+  // this lane's PER values of V row p (cached rows from the pages, the new
+  // row from LDS), as bf16 pairs
+  auto v_of = [&](int32_t p, uint32_t (&vw)[(PER + 1) / 2]) {
     const char* vrow;
     if (p < nc) {
       const uint32_t off = uint32_t(p) * (2 * DH) + 2 * d3;
@@ -840,7 +847,6 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
     } else {
       vrow = reinterpret_cast<const char*>(newv + d3);
     }
-    uint32_t vw[(PER + 1) / 2];
     if constexpr (PER == 8) {
       const u4 t = *reinterpret_cast<const u4*>(vrow);
       vw[0] = t.x; vw[1] = t.y; vw[2] = t.z; vw[3] = t.w;
@@ -852,9 +858,24 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
     } else {
       vw[0] = *reinterpret_cast<const uint16_t*>(vrow);
     }
+  };
+  // four positions per step, all LDS reads issued before the FMAs
+  constexpr int U = 4;
+  for (int32_t p = c.w; p < ntot; p += U * kNComp) {
+    float wp[U];
+    uint32_t vw[U][(PER + 1) / 2];
 #pragma unroll
-    for (int e = 0; e < PER; e++)
-      acc[e] = fmaf(wp, (e & 1) ? bf_hi(vw[e / 2]) : bf_lo(vw[e / 2]), acc[e]);
+    for (int k = 0; k < U; k++) {
+      const int32_t pk = p + k * kNComp;
+      const int32_t pc = pk < ntot ? pk : p;  // past the end: re-read p, weight 0
+      wp[k] = pk < ntot ? scores[h3 * Bat + pc] : 0.f;
+      v_of(pc, vw[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < U; k++)
+#pragma unroll
+      for (int e = 0; e < PER; e++)
+        acc[e] = fmaf(wp[k], (e & 1) ? bf_hi(vw[k][e / 2]) : bf_lo(vw[k][e / 2]), acc[e]);
   }
   if (lane == 0) lds_st(C_RELEASED + 4 * c.w, I->page0 + I->n_pages);
 #pragma unroll
@@ -868,13 +889,13 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
 #pragma unroll
     for (int w = 0; w < kNComp; w++) sum += xs[w * OUT + o];
     const uint32_t h = o / DH, d = o % DH;
-    const uint32_t head = g * HPG + h;
+    const uint32_t head = head0 + h;
     if (nblk == 1) {
       st_tag(reinterpret_cast<uint64_t*>(I->out_ptr) + head * DH + d, sum / stat_l[h], a.epoch);
     } else {
-      // partial record [HPG][DH + 2] of (group, block): o~ | m | l
-      float* part = reinterpret_cast<float*>(I->res_ptr) +
-                    (size_t(g) * nblk + blk) * (HPG * (DH + 2)) + h * (DH + 2);
+      // partial record of (head tile, block, head): o~ [DH] | m | l
+      const size_t tg = head0 / HPT;
+      float* part = reinterpret_cast<float*>(I->res_ptr) + ((tg * nblk + blk) * HPT + h) * (DH + 2);
       st_act(part + d, sum);
       if (d == 0) {
         st_act(part + DH, stat_m[h]);
@@ -888,26 +909,26 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i) {
   return true;
 }
 
-// Last-arriving tile of a group merges the block partials (log-sum-exp).
-template <int HPG, int DH>
+// Last-arriving tile of a head tile's blocks merges their partials
+// (log-sum-exp of the block maxima).
+template <int HPT, int DH>
 DEV void attn_merge(Comp& c, InstrCP I) {
   const uint32_t g = I->aux[0], nblk = I->aux[3];
-  const float* part = reinterpret_cast<const float*>(I->res_ptr) + size_t(g) * nblk * (HPG * (DH + 2));
-  constexpr int PER = HPG * DH / 64;  // outputs per lane
-  for (int k = 0; k < PER; k++) {
-    const uint32_t o = k * 64 + c.lane;
+  const uint32_t head0 = g * uint32_t(c.a->hpg) + I->row0;
+  const float* part = reinterpret_cast<const float*>(I->res_ptr) + size_t(head0 / HPT) * nblk * (HPT * (DH + 2));
+  for (uint32_t o = c.lane; o < uint32_t(HPT * DH); o += 64) {
     const uint32_t h = o / DH, d = o % DH;
     float M = -__builtin_inff();
-    for (uint32_t b = 0; b < nblk; b++) M = fmaxf(M, ld_act(part + b * (HPG * (DH + 2)) + h * (DH + 2) + DH));
+    for (uint32_t b = 0; b < nblk; b++) M = fmaxf(M, ld_act(part + (b * HPT + h) * (DH + 2) + DH));
     float num = 0.f, den = 0.f;
     for (uint32_t b = 0; b < nblk; b++) {
-      const float* rec = part + b * (HPG * (DH + 2)) + h * (DH + 2);
+      const float* rec = part + (b * HPT + h) * (DH + 2);
       const float mb = ld_act(rec + DH);
       const float wgt = mb == -__builtin_inff() ? 0.f : __expf(mb - M);
       num = fmaf(wgt, ld_act(rec + d), num);
       den = fmaf(wgt, ld_act(rec + DH + 1), den);
     }
-    st_tag(reinterpret_cast<uint64_t*>(I->out_ptr) + (g * HPG + h) * DH + d, num / den, c.a->epoch);
+    st_tag(reinterpret_cast<uint64_t*>(I->out_ptr) + (head0 + h) * DH + d, num / den, c.a->epoch);
   }
 }
 
@@ -1088,11 +1109,11 @@ DEV bool stage_inputs(Comp& c, InstrCP I, uint32_t i, bool reuse_x) {
       }
     } else {
       // attention: q, k, v of the group (tagged) and cos | sin (tables)
-      const int hpg = a.hpg, dh = a.head_dim;
-      const uint32_t g = I->aux[0];
+      const int dh = a.head_dim;
+      const uint32_t g = I->aux[0], hpt = I->n_items, head0 = g * uint32_t(a.hpg) + I->row0;
       const char* qkv = reinterpret_cast<const char*>(I->in_ptr);
-      const uint32_t nq = hpg * dh, half = dh / 2;
-      const __amdgpu_buffer_rsrc_t rq = act_rsrc(qkv + size_t(g) * nq * kActBytes, nq * kActBytes);
+      const uint32_t nq = hpt * dh, half = dh / 2;
+      const __amdgpu_buffer_rsrc_t rq = act_rsrc(qkv + size_t(head0) * dh * kActBytes, nq * kActBytes);
       const __amdgpu_buffer_rsrc_t rk = act_rsrc(qkv + size_t(a.q_dim + g * dh) * kActBytes, dh * kActBytes);
       const __amdgpu_buffer_rsrc_t rv =
           act_rsrc(qkv + size_t(a.q_dim + a.kv_dim + g * dh) * kActBytes, dh * kActBytes);
@@ -1153,10 +1174,11 @@ DEV bool stage_inputs(Comp& c, InstrCP I, uint32_t i, bool reuse_x) {
 struct GeoAny {
   static constexpr bool any = true;
 };
+// H = query heads per attention tile, D = head dimension
 template <int ND, int RD, int NQ, int RQ, int NF, int RF, int H, int D>
 struct GeoFix {
   static constexpr bool any = false;
-  static constexpr int nd = ND, rd = RD, nq = NQ, rq = RQ, nf = NF, rf = RF, hpg = H, dh = D;
+  static constexpr int nd = ND, rd = RD, nq = NQ, rq = RQ, nf = NF, rf = RF, hpt = H, dh = D;
 };
 
 template <class G>
@@ -1184,18 +1206,18 @@ DEV bool run_gemv(Comp& c, InstrCP I, uint32_t i) {
 template <class G>
 DEV bool run_attn(Comp& c, InstrCP I, uint32_t i) {
   if constexpr (!G::any) {
-    return attn<G::hpg, G::dh>(c, I, i);
+    return attn<G::hpt, G::dh>(c, I, i);
   } else {
-    const int hpg = c.a->hpg, dh = c.a->head_dim;
-    if (dh == 64) {
-      switch (hpg) {
+    const uint32_t hpt = I->n_items;
+    if (c.a->head_dim == 64) {
+      switch (hpt) {
         case 1: return attn<1, 64>(c, I, i);
         case 2: return attn<2, 64>(c, I, i);
         case 4: return attn<4, 64>(c, I, i);
         default: return attn<8, 64>(c, I, i);
       }
     }
-    switch (hpg) {
+    switch (hpt) {
       case 1: return attn<1, 128>(c, I, i);
       case 2: return attn<2, 128>(c, I, i);
       default: return attn<4, 128>(c, I, i);
@@ -1206,18 +1228,18 @@ DEV bool run_attn(Comp& c, InstrCP I, uint32_t i) {
 template <class G>
 DEV void run_merge(Comp& c, InstrCP I) {
   if constexpr (!G::any) {
-    attn_merge<G::hpg, G::dh>(c, I);
+    attn_merge<G::hpt, G::dh>(c, I);
   } else {
-    const int hpg = c.a->hpg, dh = c.a->head_dim;
-    if (dh == 64) {
-      switch (hpg) {
+    const uint32_t hpt = I->n_items;
+    if (c.a->head_dim == 64) {
+      switch (hpt) {
         case 1: return attn_merge<1, 64>(c, I);
         case 2: return attn_merge<2, 64>(c, I);
         case 4: return attn_merge<4, 64>(c, I);
         default: return attn_merge<8, 64>(c, I);
       }
     }
-    switch (hpg) {
+    switch (hpt) {
       case 1: return attn_merge<1, 128>(c, I);
       case 2: return attn_merge<2, 128>(c, I);
       default: return attn_merge<4, 128>(c, I);
@@ -1398,29 +1420,31 @@ extern "C" hipError_t mk_launch_pack(const mk::PackCopy* copies, uint32_t n, voi
 // ---- kernel table (used by the runtime; not part of the public ABI)
 namespace {
 struct Variant {
-  int nd, rd, nq, rq, nf, rf, hpg, dh;  // 0 = generic
+  int nd, rd, nq, rq, nf, rf, hpt, dh;  // 0 = generic
   const void* fn;
 };
-// Shapes with their own kernel: the Llama-3.2-1B shape (MLP in two chunks),
-// the Llama-3-8B shape (four chunks) and the small test decoder (one chunk).
+#define MK_VARIANT(ND, RD, NQ, RQ, NF, RF, H, D) \
+  {ND, RD, NQ, RQ, NF, RF, H, D,                 \
+   reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoFix<ND, RD, NQ, RQ, NF, RF, H, D>>)}
+// Shapes with their own kernel: the Llama-3.2-1B shape (MLP in two chunks;
+// one query head per attention tile at short contexts, the whole KV group at
+// long ones), the Llama-3-8B shape (four chunks) and the small test decoder.
 const Variant kVariants[] = {
     {0, 0, 0, 0, 0, 0, 0, 0, reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoAny>)},
-    {4, 1, 4, 1, 8, 1, 4, 64,
-     reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoFix<4, 1, 4, 1, 8, 1, 4, 64>>)},
-    {8, 1, 8, 1, 7, 1, 4, 128,
-     reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoFix<8, 1, 8, 1, 7, 1, 4, 128>>)},
-    {1, 2, 1, 2, 2, 1, 2, 64,
-     reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoFix<1, 2, 1, 2, 2, 1, 2, 64>>)},
+    MK_VARIANT(4, 1, 4, 1, 8, 1, 1, 64),
+    MK_VARIANT(4, 1, 4, 1, 8, 1, 4, 64),
+    MK_VARIANT(8, 1, 8, 1, 7, 1, 4, 128),
+    MK_VARIANT(1, 2, 1, 2, 2, 1, 1, 64),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 bool g_attr_set[kNumVariants] = {};
 }  // namespace
 
 // Index of the kernel built for this geometry, or 0 (the generic kernel).
-extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpg, int dh) {
+extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpt, int dh) {
   for (int v = 1; v < kNumVariants; v++) {
     const Variant& k = kVariants[v];
-    if (k.nd == nd && k.rd == rd && k.nq == nq && k.rq == rq && k.nf == nf && k.rf == rf && k.hpg == hpg &&
+    if (k.nd == nd && k.rd == rd && k.nq == nq && k.rq == rq && k.nf == nf && k.rf == rf && k.hpt == hpt &&
         k.dh == dh)
       return v;
   }

@@ -176,6 +176,15 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
       r.attn_block = int(blk);
     }
   }
+  if (r.attn_heads <= 0) {
+    // one query head per tile while the tiles still fit on the CUs (short
+    // contexts: attention is a chain of latencies, so smaller tiles finish
+    // sooner); otherwise the whole KV group per tile, so that every K/V row
+    // is streamed once
+    const int hpg = c.n_q_heads / c.n_kv_heads;
+    const int nblk = (c.max_seq + r.attn_block - 1) / r.attn_block;
+    r.attn_heads = (int64_t(c.n_q_heads) * nblk <= n_cus) ? 1 : hpg;
+  }
   if (r.watchdog_ms <= 0) r.watchdog_ms = 2000;
   return r;
 }
@@ -247,16 +256,23 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     *err = "plan: attention tile (K and V blocks) exceeds the LDS page ring";
     return MK_ERR_INVALID_ARG;
   }
-  if (hpg * Bat > kAttnScoreFloats) {
+  const int hpt = o.attn_heads;  // query heads per attention tile
+  if (hpt <= 0 || hpg % hpt) {
+    *err = "plan: attn_heads must divide the query heads per KV group";
+    return MK_ERR_INVALID_ARG;
+  }
+  if (hpt * Bat > kAttnScoreFloats) {
     *err = "plan: attention scores of one tile exceed the LDS scratch";
     return MK_ERR_INVALID_ARG;
   }
   const int nblk = ceil_div(S, Bat);
+  const int tpg = hpg / hpt;  // head tiles per KV group
   *P = Plan();
   P->n_cus = C;
   P->attn_block = Bat;
   P->attn_nblk = nblk;
-  P->attn_tiles = G * nblk;
+  P->attn_tiles = G * tpg * nblk;
+  P->attn_heads = hpt;
   P->mlp_chunks = chunks;
   P->arena = arena_layout(c, C, G * nblk);
   const uint64_t A = in.arena_base;
@@ -274,7 +290,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     c_qkv[l] = b.new_counter(l * ST_PER_LAYER + ST_QKV);
     c_attn[l] = b.new_counter(l * ST_PER_LAYER + ST_ATTN);
     if (nblk > 1)
-      for (int g = 0; g < G; g++) c_ticket[l].push_back(b.new_counter(l * ST_PER_LAYER + ST_ATTN));
+      for (int t = 0; t < G * tpg; t++) c_ticket[l].push_back(b.new_counter(l * ST_PER_LAYER + ST_ATTN));
     c_o[l] = b.new_counter(l * ST_PER_LAYER + ST_O);
     for (int ch = 0; ch < chunks; ch++) c_gu[l].push_back(b.new_counter(l * ST_PER_LAYER + ST_GU));
     c_down[l] = b.new_counter(l * ST_PER_LAYER + ST_DOWN);
@@ -289,7 +305,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
   auto set_wait = [](Instr& I, int k, uint32_t ctr) { I.wait_ctr[k] = ctr; };
 
   // attention tile -> CU: spread over the CUs, and over XCDs when sparse
-  const int n_att = G * nblk;
+  const int n_att = G * tpg * nblk;
   auto att_cu = [&](int a) {
     int64_t spacing = C / std::max(1, n_att);
     int64_t cu = int64_t(a) * C / n_att;
@@ -350,11 +366,15 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     }
     // ----------------------------------------------------------- ATTN
     for (int a = 0; a < n_att; a++) {
-      const int g = a / nblk, blk = a % nblk;
+      // tile a: head tile tg = a / nblk (heads tg*hpt .. of the layer), block a % nblk
+      const int tg = a / nblk, blk = a % nblk;
+      const int g = tg / tpg, h0 = (tg % tpg) * hpt;
       Instr I = blank();
       I.op = OP_ATTN;
       I.layer = uint16_t(l);
       I.flags = F_SIGNAL;
+      I.n_items = uint32_t(hpt);  // query heads of the tile
+      I.row0 = uint32_t(h0);      // first of them within the group
       I.row_bytes = uint32_t(kv_rb);
       I.n_rows = uint32_t(2 * Bat);
       I.aux[0] = uint32_t(g);
@@ -365,7 +385,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
       const uint64_t head_rows = uint64_t(S) * Dh;  // elements per (layer, seq, group)
       I.seg_ptr[0] = uint64_t(in.w.k_cache) + 2ull * head_rows * (uint64_t(l) * G + g);
       I.seg_ptr[1] = uint64_t(in.w.v_cache) + 2ull * head_rows * (uint64_t(l) * G + g);
-      I.seg_rows[0] = nblk > 1 ? c_ticket[l][g] : kNoCounter;
+      I.seg_rows[0] = nblk > 1 ? c_ticket[l][tg] : kNoCounter;
       I.in_ptr = A + ar.qkv[l];
       I.out_ptr = A + ar.o[l];
       I.res_ptr = A + ar.part[l];
@@ -375,10 +395,11 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
       InstrMeta m;
       m.stage = stg + ST_ATTN;
       m.merge_write = nblk > 1;
-      m.reads.push_back({BUF_QKV, l, uint64_t(g) * hpg * Dh, uint64_t(g + 1) * hpg * Dh});
+      const uint64_t q0 = uint64_t(g * hpg + h0) * Dh, q1 = q0 + uint64_t(hpt) * Dh;
+      m.reads.push_back({BUF_QKV, l, q0, q1});
       m.reads.push_back({BUF_QKV, l, uint64_t(qd + g * Dh), uint64_t(qd + (g + 1) * Dh)});
       m.reads.push_back({BUF_QKV, l, uint64_t(qd + kvd + g * Dh), uint64_t(qd + kvd + (g + 1) * Dh)});
-      m.writes.push_back({BUF_O, l, uint64_t(g) * hpg * Dh, uint64_t(g + 1) * hpg * Dh});
+      m.writes.push_back({BUF_O, l, q0, q1});
       // bytes streamed at full context
       const int64_t rows = std::min<int64_t>(Bat, std::max<int64_t>(0, int64_t(S) - int64_t(blk) * Bat));
       b.push(att_cu(a), I, std::move(m), 2 * rows * kv_rb);
@@ -577,7 +598,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
       if ((I.flags & F_SIGNAL) && I.sig_ctr != kNoCounter) P->ctr_producers[I.sig_ctr]++;
     }
   for (int l = 0; l < L; l++)
-    if (nblk > 1) P->ctr_producers[c_attn[l]] = uint32_t(G);
+    if (nblk > 1) P->ctr_producers[c_attn[l]] = uint32_t(G * tpg);
   // fill wait counts
   for (int cu = 0; cu < C; cu++)
     for (Instr& I : b.q[cu])
@@ -659,11 +680,16 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
       if (p.ctr_stage[ct] >= p.meta[i].stage) return fail("wait on a counter of the same or a later stage");
     }
   }
+  // a split attention signals once per head tile: by the tile that takes
+  // the last ticket of that head tile's blocks
+  std::vector<std::vector<uint32_t>> merged_by(NC);
+  for (const Instr& I : p.instrs)
+    if (I.op == OP_ATTN && I.aux[3] > 1 && I.sig_ctr < uint32_t(NC)) merged_by[I.sig_ctr].push_back(I.seg_rows[0]);
   for (int ct = 0; ct < NC; ct++) {
-    bool attn_merged = false;
-    for (const Instr& I : p.instrs)
-      if (I.op == OP_ATTN && I.aux[3] > 1 && I.sig_ctr == uint32_t(ct)) attn_merged = true;
-    const uint32_t expect = attn_merged ? uint32_t(c.n_kv_heads) : sig[ct];
+    std::vector<uint32_t>& t = merged_by[ct];
+    std::sort(t.begin(), t.end());
+    t.erase(std::unique(t.begin(), t.end()), t.end());
+    const uint32_t expect = t.empty() ? sig[ct] : uint32_t(t.size());
     if (expect != p.ctr_producers[ct]) {
       std::ostringstream s;
       s << "counter " << ct << " expects " << p.ctr_producers[ct] << " producers, plan has " << expect;
@@ -884,10 +910,12 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         const uint64_t span = uint64_t(c.max_seq) * I.row_bytes;
         if (!inside(I.seg_ptr[0], I.seg_ptr[0] + span) || !inside(I.seg_ptr[1], I.seg_ptr[1] + span))
           return fail("attention cache rows outside the KV cache");
-        const uint64_t hpg = c.n_q_heads / c.n_kv_heads;
-        const uint64_t rec = hpg * (c.head_dim + 2) * 4;
-        if (I.aux[3] > 1 &&
-            !in_arena(I.res_ptr, I.res_ptr + rec * (uint64_t(I.aux[0]) * I.aux[3] + I.aux[3])))
+        const uint64_t hpg = c.n_q_heads / c.n_kv_heads, hpt = I.n_items;
+        if (!hpt || hpg % hpt || I.row0 % hpt || I.row0 + hpt > hpg) return fail("attention head tile");
+        // partial records of the tile's head group: [tg][nblk][hpt][Dh + 2]
+        const uint64_t tg = (uint64_t(I.aux[0]) * hpg + I.row0) / hpt;
+        const uint64_t rec = hpt * (c.head_dim + 2) * 4;
+        if (I.aux[3] > 1 && !in_arena(I.res_ptr, I.res_ptr + rec * (tg + 1) * I.aux[3]))
           return fail("attention partials outside the arena");
         if (!in_arena(I.in_ptr, I.in_ptr + uint64_t(kActBytes) * (qd + 2 * kvd)) ||
             !in_arena(I.out_ptr, I.out_ptr + uint64_t(kActBytes) * qd))

@@ -59,7 +59,7 @@ struct Plan {
   std::vector<PackCopy> pack;       // copies that fill the packed weight stream
   uint64_t pack_bytes = 0;          // size of the packed weight stream
   int n_cus = 0, n_counters = 0;
-  int attn_block = 0, attn_nblk = 0, attn_tiles = 0, mlp_chunks = 0, lm_tiles = 0;
+  int attn_block = 0, attn_nblk = 0, attn_tiles = 0, attn_heads = 0, mlp_chunks = 0, lm_tiles = 0;
   int64_t weight_bytes = 0, max_cu_bytes = 0, min_cu_bytes = 0;
 };
 

@@ -14,7 +14,7 @@
 
 extern "C" hipError_t mk_launch_megakernel(const mk::KArgs* args, int n_cus, hipStream_t stream,
                                            int cooperative, int variant);
-extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpg, int dh);
+extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpt, int dh);
 extern "C" hipError_t mk_launch_pack(const mk::PackCopy* copies, uint32_t n, void* base,
                                      hipStream_t stream);
 
@@ -100,7 +100,7 @@ int variant_for(const mk_config& cfg, const mk_plan_opts& o) {
       !mk::gemv_geometry(cfg.n_q_heads * cfg.head_dim, &nq, &rq) ||
       !mk::gemv_geometry(cfg.ffn / o.mlp_chunks, &nf, &rf))
     return 0;
-  return mk_pick_variant(nd, rd, nq, rq, nf, rf, cfg.n_q_heads / cfg.n_kv_heads, cfg.head_dim);
+  return mk_pick_variant(nd, rd, nq, rq, nf, rf, o.attn_heads, cfg.head_dim);
 }
 
 bool dense_pointers_ok(const mk_weights& w) {

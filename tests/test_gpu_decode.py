@@ -112,8 +112,10 @@ def test_tiny_step_head_layouts(need_gpu, heads):
     # every attention code path: 1, 2, 4, 8 query heads per KV group, Dh 64/128
     h, g, dh = heads
     s = synth.SHAPES["tiny"].replace(n_q_heads=h, n_kv_heads=g, head_dim=dh)
-    _one_step_case(s)
-    _one_step_case(s, attn_block=64)
+    _one_step_case(s)                                  # one query head per tile
+    _one_step_case(s, attn_block=64)                   # ... with split KV blocks
+    _one_step_case(s, attn_heads=h // g)               # whole groups per tile
+    _one_step_case(s, attn_heads=h // g, attn_block=64)
 
 
 def test_tiny_step_one_cu(need_gpu):

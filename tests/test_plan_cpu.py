@@ -36,8 +36,12 @@ def test_default_plan_verifies(name):
     assert summ["n_cus"] == 256 and len(r["queue_lengths"]) == 256
     assert summ["weight_bytes"] == synth.weight_bytes_per_step(s)
     # the shape-specific kernels: 1B, 8B, the small test decoder
-    assert summ["kernel_variant"] == {"tiny": 3, "llama1b_ctx128": 1, "llama1b_ctx8192": 1,
-                                      "llama8b_ctx2048": 2}[name]
+    assert summ["kernel_variant"] == {"tiny": 4, "llama1b_ctx128": 1, "llama1b_ctx8192": 2,
+                                      "llama8b_ctx2048": 3}[name]
+    # one query head per attention tile at short contexts, whole groups at long ones
+    nblk = -(-s.max_seq // summ["attn_block"])
+    per_block = s.n_q_heads if name in ("tiny", "llama1b_ctx128") else s.n_kv_heads
+    assert summ["attn_tiles"] == per_block * nblk
     # default: the fewest chunks of at most 4096 values
     assert summ["mlp_chunks"] == {"tiny": 1, "llama1b_ctx128": 2, "llama1b_ctx8192": 2,
                                   "llama8b_ctx2048": 4}[name]
@@ -53,6 +57,8 @@ def test_default_plan_verifies(name):
     ("tiny", 256, {"mlp_chunks": 2, "attn_block": 64}),
     ("llama1b_ctx128", 100, {"attn_block": 64}), ("llama1b_ctx8192", 256, {"attn_block": 128}),
     ("llama8b_ctx2048", 128, {}),
+    ("tiny", 64, {"attn_heads": 2, "attn_block": 64}), ("llama1b_ctx128", 256, {"attn_heads": 4}),
+    ("llama1b_ctx128", 256, {"attn_heads": 2, "attn_block": 64}),
 ])
 def test_plan_variants_verify(name, n_cus, opts):
     B.mk_plan_check(_cfg(name), n_cus, B.plan_opts(**opts))
@@ -75,7 +81,8 @@ def test_unsupported_or_bad_shapes_are_rejected(kw, status):
     assert e.value.status == status
 
 
-@pytest.mark.parametrize("opts", [{"attn_block": 100}, {"mlp_chunks": 3}, {"attn_block": 1024}])
+@pytest.mark.parametrize("opts", [{"attn_block": 100}, {"mlp_chunks": 3}, {"attn_block": 1024},
+                                  {"attn_heads": 3}])
 def test_bad_plan_options_are_rejected(opts):
     with pytest.raises(B.MkError):
         B.mk_plan_check(_cfg("tiny"), 64, B.plan_opts(**opts))
