@@ -430,22 +430,22 @@ static_assert(kVmT % kDmaPerPage == 0 && kVmT >= kDmaPerPage && kVmT <= 48,
               "kVmT is a whole number of pages within the vmcnt range");
 
 // Eight DMAs of 8 consecutive 1 KiB units starting at `src` into LDS at
-// `lds_addr`.  The instruction offset moves the global source and the LDS
+// `lds_addr`, marked non-temporal (weights are read once per step).  The instruction offset moves the global source and the LDS
 // destination together, so four DMAs share one M0 value; the second four use
 // a VGPR offset 4 KiB higher and M0 + 4 KiB.  Each DMA is followed by the
 // in-flight throttle (a no-op while fewer than kVmT DMAs are outstanding).
 DEV void dma_run8(uint32_t lds_addr, uint64_t src, uint32_t voff, uint32_t voff4k) {
   asm volatile(
       "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %3\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %1, %3 offset:1024\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %1, %3 offset:2048\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %1, %3 offset:3072\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %1, %3 nt\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:1024 nt\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:2048 nt\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:3072 nt\n\t" MK_THROTTLE "\n\t"
       "s_add_u32 m0, %0, 0x1000\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %2, %3 offset:1024\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %2, %3 offset:2048\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %2, %3 offset:3072\n\t" MK_THROTTLE
+      "global_load_lds_dwordx4 %2, %3 nt\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:1024 nt\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:2048 nt\n\t" MK_THROTTLE "\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:3072 nt\n\t" MK_THROTTLE
       :
       : "s"(lds_addr), "v"(voff), "v"(voff4k), "s"(src)
       : "memory", "m0");
@@ -952,9 +952,9 @@ DEV void reload(u4& t, __amdgpu_buffer_rsrc_t r, uint32_t off) { t = ld_tag2(r, 
 DEV void reload(uint2& t, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16));
 }
-template <typename T, int N>
-DEV bool wait_fresh(T (&t)[N], uint32_t live, __amdgpu_buffer_rsrc_t r, const uint32_t (&off)[N],
-                    uint32_t tag, uint32_t& retries) {
+template <typename T, int N, typename Off>
+DEV bool wait_fresh(T (&t)[N], uint32_t live, __amdgpu_buffer_rsrc_t r, Off off, int h, uint32_t tag,
+                    uint32_t& retries) {
   Watch wt;
   for (;;) {
     bool ok = true;
@@ -965,7 +965,7 @@ DEV bool wait_fresh(T (&t)[N], uint32_t live, __amdgpu_buffer_rsrc_t r, const ui
     retries++;
 #pragma unroll
     for (int j = 0; j < N; j++)
-      if (j < int(live) && !is_fresh(t[j], tag)) reload(t[j], r, off[j]);
+      if (j < int(live) && !is_fresh(t[j], tag)) reload(t[j], r, off(h, j));
     if (aborted()) return false;
     if (local_timeout(wt, local_limit())) {
       local_abort(STC_LOCAL_TIMEOUT);
@@ -1060,50 +1060,56 @@ DEV bool stage_inputs(Comp& c, InstrCP I, uint32_t i, bool reuse_x) {
         }
       } else {
         // tagged activations: two values per lane per 16-byte load, 128 per
-        // wave-wide load; up to 2048 values per round
+        // wave-wide load, 2048 per half; the second half (K > 2048) is
+        // loaded in the same round trip
         constexpr int NL = 16;
         const __amdgpu_buffer_rsrc_t r = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), K * kActBytes);
-        float ss = 0.f;
-        const uint32_t rounds = (K + 128 * NL - 1) / (128 * NL);
-        for (uint32_t rd = 0; rd < rounds; rd++) {
-          const uint32_t base = rd * 128 * NL;
-          u4 t[NL];
-          uint32_t off[NL], gw[NL];
+        const bool two = K > 128 * NL;
+        auto off = [&](int h, int j) -> uint32_t { return (128 * NL * h + 2 * lane + 128 * j) * kActBytes; };
+        u4 t0[NL], t1[NL];
+        uint32_t gw[NL];
 #pragma unroll
-          for (int j = 0; j < NL; j++) {
-            off[j] = (base + 2 * lane + 128 * j) * kActBytes;
-            t[j] = ld_tag2(r, off[j]);
-            gw[j] = __builtin_amdgcn_raw_buffer_load_b32(rg, (base + 2 * lane + 128 * j) * 2, 0, 0);
-          }
-          const uint32_t live = (K - base) / 128 < uint32_t(NL) ? (K - base) / 128 : uint32_t(NL);
-          if (!wait_fresh(t, live, r, off, tag, c.retries)) return false;
+        for (int j = 0; j < NL; j++) t0[j] = ld_tag2(r, off(0, j));
+        if (two) {
 #pragma unroll
-          for (int j = 0; j < NL; j++) {
-            const float v0 = __uint_as_float(t[j].x), v1 = __uint_as_float(t[j].z);
-            ss += v0 * v0 + v1 * v1;
-            // raw values now; scaled below once the whole sum is known
-            if (j < int(live)) *reinterpret_cast<float2*>(xs + base + 2 * lane + 128 * j) = float2{v0, v1};
-          }
-          if (norm && rounds == 1) {
-            // one round: scale in place with the gains still in registers
-            const float inv = rsqrtf(sum64(ss) / float(K) + a.rms_eps);
-#pragma unroll
-            for (int j = 0; j < NL; j++) {
-              if (j >= int(live)) continue;
-              float2* px = reinterpret_cast<float2*>(xs + 2 * lane + 128 * j);
-              const float2 xv = *px;
-              *px = float2{xv.x * inv * bf_lo(gw[j]), xv.y * inv * bf_hi(gw[j])};
-            }
-          }
+          for (int j = 0; j < NL; j++) t1[j] = ld_tag2(r, off(1, j));
         }
-        if (norm && rounds > 1) {
-          // several rounds: scale from LDS, gains read again (cached)
-          const float inv = rsqrtf(sum64(ss) / float(K) + a.rms_eps);
-          for (uint32_t o = 2 * lane; o < K; o += 128) {
-            const uint32_t gv = __builtin_amdgcn_raw_buffer_load_b32(rg, o * 2, 0, 0);
-            float2* px = reinterpret_cast<float2*>(xs + o);
-            const float2 xv = *px;
-            *px = float2{xv.x * inv * bf_lo(gv), xv.y * inv * bf_hi(gv)};
+        // gains of the first half (a single-half norm scales in registers)
+#pragma unroll
+        for (int j = 0; j < NL; j++) gw[j] = __builtin_amdgcn_raw_buffer_load_b32(rg, (2 * lane + 128 * j) * 2, 0, 0);
+        const uint32_t live0 = K / 128 < uint32_t(NL) ? K / 128 : uint32_t(NL);
+        if (!wait_fresh(t0, live0, r, off, 0, tag, c.retries)) return false;
+        if (two && !wait_fresh(t1, K / 128 - NL, r, off, 1, tag, c.retries)) return false;
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NL; j++) {
+          ss += __uint_as_float(t0[j].x) * __uint_as_float(t0[j].x) + __uint_as_float(t0[j].z) * __uint_as_float(t0[j].z);
+          if (two)
+            ss += __uint_as_float(t1[j].x) * __uint_as_float(t1[j].x) + __uint_as_float(t1[j].z) * __uint_as_float(t1[j].z);
+        }
+        const float inv = norm ? rsqrtf(sum64(ss) / float(K) + a.rms_eps) : 1.f;
+        const bool scale_now = norm && !two;
+#pragma unroll
+        for (int j = 0; j < NL; j++) {
+          if (j >= int(live0)) continue;
+          float2 v{__uint_as_float(t0[j].x), __uint_as_float(t0[j].z)};
+          if (scale_now) v = float2{v.x * inv * bf_lo(gw[j]), v.y * inv * bf_hi(gw[j])};
+          *reinterpret_cast<float2*>(xs + 2 * lane + 128 * j) = v;
+        }
+        if (two) {
+#pragma unroll
+          for (int j = 0; j < NL; j++)
+            if (128 * NL + 128 * j < K)
+              *reinterpret_cast<float2*>(xs + 128 * NL + 2 * lane + 128 * j) =
+                  float2{__uint_as_float(t1[j].x), __uint_as_float(t1[j].z)};
+          if (norm) {
+            // two halves with a norm: scale from LDS with the gains read again
+            for (uint32_t o = 2 * lane; o < K; o += 128) {
+              const uint32_t gv = __builtin_amdgcn_raw_buffer_load_b32(rg, o * 2, 0, 0);
+              float2* px = reinterpret_cast<float2*>(xs + o);
+              const float2 xv = *px;
+              *px = float2{xv.x * inv * bf_lo(gv), xv.y * inv * bf_hi(gv)};
+            }
           }
         }
       }
@@ -1136,9 +1142,9 @@ DEV bool stage_inputs(Comp& c, InstrCP I, uint32_t i, bool reuse_x) {
       const f4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, (lane - half / 4) * 16, 0, 0);
       const bool kv_lane = 2 * lane < uint32_t(dh);
       const uint32_t q_live = nq > 2 * lane ? (nq - 2 * lane + 127) / 128 : 0;
-      if (!wait_fresh(tq, q_live, rq, oq, tag, c.retries)) return false;
-      if (!wait_fresh(tk, kv_lane ? 1 : 0, rk, ok1, tag, c.retries)) return false;
-      if (!wait_fresh(tv, kv_lane ? 1 : 0, rv, ok1, tag, c.retries)) return false;
+      if (!wait_fresh(tq, q_live, rq, [&](int, int j) { return oq[j]; }, 0, tag, c.retries)) return false;
+      if (!wait_fresh(tk, kv_lane ? 1 : 0, rk, [&](int, int) { return ok1[0]; }, 0, tag, c.retries)) return false;
+      if (!wait_fresh(tv, kv_lane ? 1 : 0, rv, [&](int, int) { return ok1[0]; }, 0, tag, c.retries)) return false;
 #pragma unroll
       for (int j = 0; j < NQ; j++)
         if (2 * lane + 128 * j < nq)
@@ -1155,7 +1161,7 @@ DEV bool stage_inputs(Comp& c, InstrCP I, uint32_t i, bool reuse_x) {
 
   if (has_res) {
     float* rs = const_cast<float*>(res_slot(i));
-    if (!res_embed && !wait_fresh(res_t, res_live, rr, res_off, tag, c.retries)) return false;
+    if (!res_embed && !wait_fresh(res_t, res_live, rr, [&](int, int j) { return res_off[j]; }, 0, tag, c.retries)) return false;
 #pragma unroll
     for (int j = 0; j < 2; j++)
       if (j < int(res_live))
