@@ -37,6 +37,7 @@ def _greedy_case(name, steps, keep_f64=True):
         ref_lg, ref_nx = orc.step(t, s.prefill + i, k_ref, v_ref)
         err = rel_l2(lgs[i][0], ref_lg[0])
         worst = max(worst, err)
+        print("  step %d: rel_l2 %.3e token %d / oracle %d" % (i, err, toks[i][0], ref_nx[0]), flush=True)
         if toks[i][0] != ref_nx[0]:
             top = np.sort(ref_lg[0])[-2:]
             pytest.fail("step %d: token %d vs oracle %d (oracle top-2 margin %.3e)"
