@@ -82,6 +82,11 @@ DEV uint32_t* lw(int off) { return reinterpret_cast<uint32_t*>(lds + off); }
 DEV uint32_t lds_ld(int off) {
   return __hip_atomic_load(lw(off), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+// relaxed LDS read: several of them are issued together; the caller adds a
+// workgroup acquire fence once it has seen what it waited for
+DEV uint32_t lds_ld_rlx(int off) {
+  return __hip_atomic_load(lw(off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 DEV void lds_st(int off, uint32_t v) {
   __hip_atomic_store(lw(off), v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -308,10 +313,31 @@ DEV bool wait_lds_ge(int off, uint32_t want) {
   }
   return true;
 }
-DEV uint32_t min_filled() {
-  uint32_t m = lds_ld(C_FILLED);
+// Wait until every compute wave's word at off + 4*w has reached `want` (the
+// kNComp words are read together each poll).
+DEV bool wait_all_ge(int off, uint32_t want) {
+  Watch t0;
+  for (;;) {
+    uint32_t m = lds_ld_rlx(off);
 #pragma unroll
-  for (int v = 1; v < kNLoad; v++) m = min(m, lds_ld(C_FILLED + 4 * v));
+    for (int w = 1; w < kNComp; w++) m = min(m, lds_ld_rlx(off + 4 * w));
+    if (int32_t(m - want) >= 0) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      return true;
+    }
+    if (aborted()) return false;
+    if (local_timeout(t0, local_limit())) {
+      local_abort(STC_LOCAL_TIMEOUT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(0);
+  }
+}
+DEV uint32_t min_filled() {
+  uint32_t m = lds_ld_rlx(C_FILLED);
+#pragma unroll
+  for (int v = 1; v < kNLoad; v++) m = min(m, lds_ld_rlx(C_FILLED + 4 * v));
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   return m;
 }
 // Wait until page g is published by every loader.
@@ -382,9 +408,10 @@ DEV void wait_vm_pages(uint32_t pages_after) {
 }
 
 DEV uint32_t min_released() {
-  uint32_t m = lds_ld(C_RELEASED);
+  uint32_t m = lds_ld_rlx(C_RELEASED);
 #pragma unroll
-  for (int w = 1; w < kNComp; w++) m = min(m, lds_ld(C_RELEASED + 4 * w));
+  for (int w = 1; w < kNComp; w++) m = min(m, lds_ld_rlx(C_RELEASED + 4 * w));
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   return m;
 }
 
@@ -395,10 +422,12 @@ struct LoadView {
   uint64_t src;            // GEMV: packed stream of the instruction
   uint64_t kv_base[2];     // ATTN: first K / V row of the position block
   uint32_t op, stream_units, kp, valid_bytes;
+  bool deep;               // deep DMA queue (the LM head)
 };
 
 DEV void load_view(const KArgs& a, InstrCP I, LoadView& L) {
   L.op = i_op(I);
+  L.deep = L.op == OP_GEMV && i_epi(I) == EPI_ARGMAX;
   L.stream_units = (I->n_rows * I->row_bytes + kUnit - 1) / kUnit;
   L.src = I->src_ptr;
   L.kp = I->aux[4];
@@ -422,37 +451,49 @@ DEV void load_view(const KArgs& a, InstrCP I, LoadView& L) {
 #ifndef MK_VMT
 #define MK_VMT 8
 #endif
+#ifndef MK_VMT_DEEP
+#define MK_VMT_DEEP 24
+#endif
 #define MK_STR2(x) #x
 #define MK_STR(x) MK_STR2(x)
-#define MK_THROTTLE "s_waitcnt vmcnt(" MK_STR(MK_VMT) ")"
-constexpr uint32_t kVmT = MK_VMT;
-static_assert(kVmT % kDmaPerPage == 0 && kVmT >= kDmaPerPage && kVmT <= 48,
-              "kVmT is a whole number of pages within the vmcnt range");
+// DMAs in flight per loader wave: shallow while the layers run (their weights
+// are prefetched during the waits between stages, and a deep queue only
+// lengthens the latency of the activation loads behind it), deep for the LM
+// head, which is the one long pure stream of the step.
+constexpr uint32_t kVmT = MK_VMT, kVmTDeep = MK_VMT_DEEP;
+static_assert(kVmT % kDmaPerPage == 0 && kVmT >= kDmaPerPage && kVmTDeep % kDmaPerPage == 0 &&
+                  kVmTDeep >= kVmT && kVmTDeep <= 48,
+              "throttles are whole numbers of pages within the vmcnt range");
 
 // Eight DMAs of 8 consecutive 1 KiB units starting at `src` into LDS at
-// `lds_addr`, marked non-temporal (weights are read once per step).  The instruction offset moves the global source and the LDS
-// destination together, so four DMAs share one M0 value; the second four use
-// a VGPR offset 4 KiB higher and M0 + 4 KiB.  Each DMA is followed by the
-// in-flight throttle (a no-op while fewer than kVmT DMAs are outstanding).
-DEV void dma_run8(uint32_t lds_addr, uint64_t src, uint32_t voff, uint32_t voff4k) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %3 nt\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %1, %3 offset:1024 nt\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %1, %3 offset:2048 nt\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %1, %3 offset:3072 nt\n\t" MK_THROTTLE "\n\t"
-      "s_add_u32 m0, %0, 0x1000\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3 nt\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %2, %3 offset:1024 nt\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %2, %3 offset:2048 nt\n\t" MK_THROTTLE "\n\t"
-      "global_load_lds_dwordx4 %2, %3 offset:3072 nt\n\t" MK_THROTTLE
-      :
-      : "s"(lds_addr), "v"(voff), "v"(voff4k), "s"(src)
-      : "memory", "m0");
+// `lds_addr`, marked non-temporal (weights are read once per step).  The
+// instruction offset moves the global source and the LDS destination
+// together, so four DMAs share one M0 value; the second four use a VGPR
+// offset 4 KiB higher and M0 + 4 KiB.  Each DMA is followed by the in-flight
+// throttle (a no-op while fewer than T DMAs are outstanding).
+#define MK_DMA8(T)                                                                                  \
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"                                                   \
+               "global_load_lds_dwordx4 %1, %3 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"              \
+               "global_load_lds_dwordx4 %1, %3 offset:1024 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"  \
+               "global_load_lds_dwordx4 %1, %3 offset:2048 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"  \
+               "global_load_lds_dwordx4 %1, %3 offset:3072 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"  \
+               "s_add_u32 m0, %0, 0x1000\n\ts_nop 0\n\t"                                              \
+               "global_load_lds_dwordx4 %2, %3 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"              \
+               "global_load_lds_dwordx4 %2, %3 offset:1024 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"  \
+               "global_load_lds_dwordx4 %2, %3 offset:2048 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"  \
+               "global_load_lds_dwordx4 %2, %3 offset:3072 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")"        \
+               :                                                                                    \
+               : "s"(lds_addr), "v"(voff), "v"(voff4k), "s"(src)                                    \
+               : "memory", "m0")
+DEV void dma_run8(uint32_t lds_addr, uint64_t src, uint32_t voff, uint32_t voff4k, bool deep) {
+  if (deep)
+    MK_DMA8(MK_VMT_DEEP);
+  else
+    MK_DMA8(MK_VMT);
 }
 
 DEV void vm_throttle(uint32_t& nd) {
-  if (++nd > kVmT) asm volatile(MK_THROTTLE ::: "memory");
+  if (++nd > kVmT) asm volatile("s_waitcnt vmcnt(" MK_STR(MK_VMT) ")" ::: "memory");
 }
 
 // Issue this loader wave's half of page p (units v*8 .. v*8+7): one
@@ -466,7 +507,7 @@ DEV void issue_page(const KArgs& a, const LoadView& L, uint32_t p, uint32_t g, i
     // Packed stream: the run is inside the instruction's zero-padded pages;
     // a half page wholly past the rows reads the zero page instead of HBM.
     const uint32_t u0 = p * kUnitsPerPage + half;
-    dma_run8(dst, u0 < L.stream_units ? L.src + uint64_t(u0) * kUnit : zero, voff, voff4k);
+    dma_run8(dst, u0 < L.stream_units ? L.src + uint64_t(u0) * kUnit : zero, voff, voff4k, L.deep);
     nd += kDmaPerPage;
     return;
   }
@@ -475,10 +516,10 @@ DEV void issue_page(const KArgs& a, const LoadView& L, uint32_t p, uint32_t g, i
   const uint64_t base = region ? L.kv_base[1] : L.kv_base[0];
   const uint32_t off0 = ((p - region * L.kp) * kUnitsPerPage + half) * kUnit;
   if (off0 + kDmaPerPage * kUnit <= L.valid_bytes) {
-    dma_run8(dst, base + off0, voff, voff4k);
+    dma_run8(dst, base + off0, voff, voff4k, false);
     nd += kDmaPerPage;
   } else if (off0 >= L.valid_bytes) {
-    dma_run8(dst, zero, voff, voff4k);
+    dma_run8(dst, zero, voff, voff4k, false);
     nd += kDmaPerPage;
   } else {
     for (uint32_t j = 0; j < kDmaPerPage; j++) {
@@ -538,8 +579,10 @@ DEV void loader(const KArgs& a, InstrCP q, uint32_t n, int v) {
       }
       issue_page(a, L, p, g, v, voff, voff4k, nd);
       g_issue = g + 1;
-      // pages whose DMAs all precede the last kVmT are complete
-      if (nd > kVmT) publish(g_pub, (nd - kVmT) / kDmaPerPage, v);
+      // pages whose DMAs all precede the last T (the throttle just applied)
+      // are complete
+      const uint32_t vmt = L.deep ? kVmTDeep : kVmT;
+      if (nd > vmt) publish(g_pub, (nd - vmt) / kDmaPerPage, v);
     }
   }
   wait_vm0();
@@ -1315,7 +1358,7 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       if (tr && c.lane == 0) trace_put(a, cu, i, TR_DEPS, now32());
       // every compute wave has read the previous instruction's staged inputs
       // (the residual rows are restaged every time)
-      for (int v = 0; v < kNComp && ok; v++) ok = wait_lds_ge(C_XCONS + 4 * v, i);
+      if (ok) ok = wait_all_ge(C_XCONS, i);
       if (!ok) {
         if (c.lane == 0) lds_st(C_ABORT, 1);
         return;
