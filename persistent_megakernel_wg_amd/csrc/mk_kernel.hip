@@ -60,7 +60,8 @@ DEV uint32_t i_flags(InstrCP I) { return hw1(I) & 0xFFFFu; }
 enum : int {
   C_FILLED = 0,        // [kNLoad] pages published by each loader
   C_RELEASED = 16,     // [kNComp] pages below this index are done, per wave
-  C_XOK = 64,          // instructions whose inputs are staged
+  C_XOK = 64,          // instructions whose inputs are staged (leader staging)
+  C_DEPOK = 68,        // instructions whose counter waits are satisfied
   C_XCONS = 96,        // [kNComp] instructions whose staged inputs each wave read
   C_DONE = 128,        // [kDoneRing] waves finished, per instruction slot
   C_ABORT = 160,
@@ -667,6 +668,35 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
     xv[j][4] = hi.x; xv[j][5] = hi.y; xv[j][6] = hi.z; xv[j][7] = hi.w;
   }
   if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
+  if (i_flags(I) & F_NORM) {
+    // RMSNorm: every wave holds the whole input (RPU 2: each half-wave does),
+    // so each one normalises its own copy with the staged gain
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NIT; j++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) ss = fmaf(xv[j][e], xv[j][e], ss);
+    if (RPU == 1) {
+      ss = sum64(ss);
+    } else {
+      float lo, hi;
+      sum32x2(ss, lo, hi);
+      ss = lo;
+    }
+    const float inv = rsqrtf(ss / float(I->k) + a.rms_eps);
+    const uint16_t* gs = reinterpret_cast<const uint16_t*>(lds + kLdsGain);
+#pragma unroll
+    for (int j = 0; j < NIT; j++) {
+      const uint32_t col = RPU == 1 ? j * 512 + lane * 8 : (lane % LPR) * 8;
+      const u4 gv = *reinterpret_cast<const u4*>(gs + col);
+      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        xv[j][2 * e] *= inv * bf_lo(gw[e]);
+        xv[j][2 * e + 1] *= inv * bf_hi(gw[e]);
+      }
+    }
+  }
   const bool trl = c.a->trace && c.w == 0 && lane == 0;
   if (trl) trace_put(a, c.cu, i, TR_XREADY, now32());
 
@@ -1017,146 +1047,40 @@ DEV bool wait_fresh(T (&t)[N], uint32_t live, __amdgpu_buffer_rsrc_t r, Off off,
   }
 }
 
-// Inputs of instruction I into LDS: the input vector into the x slot
-// (RMS-normalised with the gain when F_NORM; for attention the group's q, k,
-// v and the position's cos, sin) and the residual rows of the epilogue into
-// the instruction's residual slot.  Every load is issued before the first
-// is waited for, so the staging costs one memory round trip when the
-// producers' stores have landed.  false = abort or watchdog.
-DEV bool stage_inputs(Comp& c, InstrCP I, uint32_t i, bool reuse_x) {
+// Leader staging (attention and the embedding input of the first layer):
+// the input into the x slot and, for a GEMV, its RMSNorm gain into the gain
+// area (the compute waves normalise; see gemv).  For attention: the group's
+// q, k, v and the position's cos, sin.  Every load is issued before the first
+// is waited for: one memory round trip.  false = abort or watchdog.
+DEV bool stage_leader(Comp& c, InstrCP I, uint32_t i) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane;
   const uint32_t tag = a.epoch;
   float* xs = reinterpret_cast<float*>(lds + kLdsX);
-  static_assert(kMaxResRows == 128, "residual staging takes two rows per lane");
-
-  // residual rows r0 + 2*lane + {0,1}: tagged elements, or the bf16 row of
-  // the token's embedding (per-element loads: a resource of n_res elements
-  // reads zero past the tile)
-  const bool has_res = needs_res(I);
-  const bool res_embed = has_res && (i_flags(I) & F_RES_EMBED);
-  const uint32_t n_res = has_res ? out_rows(I) : 0;
-  const uint32_t r0 = I->row0;
-  const __amdgpu_buffer_rsrc_t rr = act_rsrc(reinterpret_cast<const char*>(I->res_ptr) + size_t(r0) * kActBytes,
-                                             (has_res && !res_embed) ? n_res * kActBytes : 0);
-  uint2 res_t[2];
-  const uint32_t res_off[2] = {2 * lane * kActBytes, (2 * lane + 1) * kActBytes};
-  reload(res_t[0], rr, res_off[0]);
-  reload(res_t[1], rr, res_off[1]);
-  uint16_t res_e[2] = {0, 0};
-  if (res_embed) {
-    const uint16_t* e = reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(token0(a)) * a.hidden + r0;
-    const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(e), 0, n_res * 2, 0x00020000);
-    res_e[0] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane, 0, 0);
-    res_e[1] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane + 2, 0, 0);
-  }
-  const uint32_t res_live = 2 * lane >= n_res ? 0 : (2 * lane + 1 < n_res ? 2 : 1);
-
-  if (!reuse_x) {
-    if (i_op(I) == OP_GEMV) {
-      const uint32_t K = I->k;
-      const bool norm = i_flags(I) & F_NORM;
-      // gain (a resource of zero bytes without F_NORM: reads return zero)
-      const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-          reinterpret_cast<void*>(I->gain_ptr), 0, norm ? K * 2 : 0, 0x00020000);
-      if (i_flags(I) & F_IN_EMBED) {
-        // bf16 embedding row of the token: 8 values per lane per 512
-        constexpr int NE = kMaxK / 512;
-        const uint16_t* e = reinterpret_cast<const uint16_t*>(I->in_ptr) + size_t(token0(a)) * K;
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(e), 0, K * 2, 0x00020000);
-        u4 raw[NE], gw[NE];
+  if (i_op(I) == OP_GEMV) {
+    // bf16 embedding row of the token (8 values per lane per 512) and the gain
+    constexpr int NE = kMaxK / 512;
+    const uint32_t K = I->k;
+    const bool norm = i_flags(I) & F_NORM;
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(I->in_ptr) + size_t(token0(a)) * K;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(e), 0, K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(I->gain_ptr), 0, norm ? K * 2 : 0, 0x00020000);
+    u4 raw[NE], gw[NE];
 #pragma unroll
-        for (int j = 0; j < NE; j++) {
-          raw[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (lane * 8 + 512 * j) * 2, 0, 0));
-          gw[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rg, (lane * 8 + 512 * j) * 2, 0, 0));
-        }
-        float v[NE][8];
-        float ss = 0.f;
+    for (int j = 0; j < NE; j++) {
+      raw[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (lane * 8 + 512 * j) * 2, 0, 0));
+      gw[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rg, (lane * 8 + 512 * j) * 2, 0, 0));
+    }
+    uint16_t* gs = reinterpret_cast<uint16_t*>(lds + kLdsGain);
 #pragma unroll
-        for (int j = 0; j < NE; j++) {
-          const uint32_t w4[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            v[j][2 * q] = bf_lo(w4[q]);
-            v[j][2 * q + 1] = bf_hi(w4[q]);
-            ss += v[j][2 * q] * v[j][2 * q] + v[j][2 * q + 1] * v[j][2 * q + 1];
-          }
-        }
-        if (norm) {
-          const float inv = rsqrtf(sum64(ss) / float(K) + a.rms_eps);
-#pragma unroll
-          for (int j = 0; j < NE; j++) {
-            const uint32_t g4[4] = {gw[j].x, gw[j].y, gw[j].z, gw[j].w};
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-              v[j][2 * q] *= inv * bf_lo(g4[q]);
-              v[j][2 * q + 1] *= inv * bf_hi(g4[q]);
-            }
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < NE; j++) {
-          *reinterpret_cast<f4*>(xs + lane * 8 + 512 * j) = f4{v[j][0], v[j][1], v[j][2], v[j][3]};
-          *reinterpret_cast<f4*>(xs + lane * 8 + 512 * j + 4) = f4{v[j][4], v[j][5], v[j][6], v[j][7]};
-        }
-      } else {
-        // tagged activations: two values per lane per 16-byte load, 128 per
-        // wave-wide load, 2048 per half; the second half (K > 2048) is
-        // loaded in the same round trip
-        constexpr int NL = 16;
-        const __amdgpu_buffer_rsrc_t r = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), K * kActBytes);
-        const bool two = K > 128 * NL;
-        auto off = [&](int h, int j) -> uint32_t { return (128 * NL * h + 2 * lane + 128 * j) * kActBytes; };
-        u4 t0[NL], t1[NL];
-        uint32_t gw[NL];
-#pragma unroll
-        for (int j = 0; j < NL; j++) t0[j] = ld_tag2(r, off(0, j));
-        if (two) {
-#pragma unroll
-          for (int j = 0; j < NL; j++) t1[j] = ld_tag2(r, off(1, j));
-        }
-        // gains of the first half (a single-half norm scales in registers)
-#pragma unroll
-        for (int j = 0; j < NL; j++) gw[j] = __builtin_amdgcn_raw_buffer_load_b32(rg, (2 * lane + 128 * j) * 2, 0, 0);
-        const uint32_t live0 = K / 128 < uint32_t(NL) ? K / 128 : uint32_t(NL);
-        if (!wait_fresh(t0, live0, r, off, 0, tag, c.retries)) return false;
-        if (two && !wait_fresh(t1, K / 128 - NL, r, off, 1, tag, c.retries)) return false;
-        float ss = 0.f;
-#pragma unroll
-        for (int j = 0; j < NL; j++) {
-          ss += __uint_as_float(t0[j].x) * __uint_as_float(t0[j].x) + __uint_as_float(t0[j].z) * __uint_as_float(t0[j].z);
-          if (two)
-            ss += __uint_as_float(t1[j].x) * __uint_as_float(t1[j].x) + __uint_as_float(t1[j].z) * __uint_as_float(t1[j].z);
-        }
-        const float inv = norm ? rsqrtf(sum64(ss) / float(K) + a.rms_eps) : 1.f;
-        const bool scale_now = norm && !two;
-#pragma unroll
-        for (int j = 0; j < NL; j++) {
-          if (j >= int(live0)) continue;
-          float2 v{__uint_as_float(t0[j].x), __uint_as_float(t0[j].z)};
-          if (scale_now) v = float2{v.x * inv * bf_lo(gw[j]), v.y * inv * bf_hi(gw[j])};
-          *reinterpret_cast<float2*>(xs + 2 * lane + 128 * j) = v;
-        }
-        if (two) {
-#pragma unroll
-          for (int j = 0; j < NL; j++)
-            if (128 * NL + 128 * j < K)
-              *reinterpret_cast<float2*>(xs + 128 * NL + 2 * lane + 128 * j) =
-                  float2{__uint_as_float(t1[j].x), __uint_as_float(t1[j].z)};
-          if (norm) {
-            // two halves with a norm: scale from LDS with the gains read again
-            for (uint32_t o = 2 * lane; o < K; o += 128) {
-              const uint32_t gv = __builtin_amdgcn_raw_buffer_load_b32(rg, o * 2, 0, 0);
-              float2* px = reinterpret_cast<float2*>(xs + o);
-              const float2 xv = *px;
-              *px = float2{xv.x * inv * bf_lo(gv), xv.y * inv * bf_hi(gv)};
-            }
-          }
-        }
-      }
-    } else {
+    for (int j = 0; j < NE; j++) {
+      const uint32_t o = lane * 8 + 512 * j;
+      *reinterpret_cast<f4*>(xs + o) = f4{bf_lo(raw[j].x), bf_hi(raw[j].x), bf_lo(raw[j].y), bf_hi(raw[j].y)};
+      *reinterpret_cast<f4*>(xs + o + 4) = f4{bf_lo(raw[j].z), bf_hi(raw[j].z), bf_lo(raw[j].w), bf_hi(raw[j].w)};
+      if (norm) *reinterpret_cast<u4*>(gs + o) = gw[j];
+    }
+  } else {
       // attention: q, k, v of the group (tagged) and cos | sin (tables)
       const int dh = a.head_dim;
       const uint32_t g = I->aux[0], hpt = I->n_items, head0 = g * uint32_t(a.hpg) + I->row0;
@@ -1199,12 +1123,77 @@ DEV bool stage_inputs(Comp& c, InstrCP I, uint32_t i, bool reuse_x) {
             float2{__uint_as_float(tv[0].x), __uint_as_float(tv[0].z)};
       }
       if (lane * 4 < uint32_t(dh)) *reinterpret_cast<f4*>(xs + nq + 2 * dh + lane * 4) = lane * 4 < half ? cv : sv;
+  }
+  return true;
+}
+
+// Cooperative staging of a GEMV's tagged input: wave w loads the chunks of
+// 128 values j = w, w + kNComp, ... (every load before the first wait: one
+// round trip per wave, all waves in parallel), re-reads stale ones, and
+// writes them raw to the x slot with their RMSNorm gains to the gain area
+// once every wave has read the previous input.  The leader also stages the
+// epilogue's residual rows.  A barrier of the compute waves follows.
+// false = abort or watchdog.
+DEV bool coop_stage(Comp& c, InstrCP I, uint32_t i, bool stage_x) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane;
+  const uint32_t tag = a.epoch;
+  constexpr int NC = (kMaxK / 128 + kNComp - 1) / kNComp;
+  static_assert(kMaxResRows == 128, "residual staging takes two rows per lane");
+  const uint32_t K = I->k, nch = K / 128;
+  const bool norm = i_flags(I) & F_NORM;
+  const __amdgpu_buffer_rsrc_t r = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), stage_x ? K * kActBytes : 0);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(I->gain_ptr), 0, (stage_x && norm) ? K * 2 : 0, 0x00020000);
+  auto chunk = [&](int q) -> uint32_t { return uint32_t(c.w) + kNComp * q; };
+  auto off = [&](int, int q) -> uint32_t { return (chunk(q) * 128 + 2 * lane) * kActBytes; };
+  u4 t[NC];
+  uint32_t gw[NC];
+#pragma unroll
+  for (int q = 0; q < NC; q++) {
+    t[q] = ld_tag2(r, off(0, q));
+    gw[q] = __builtin_amdgcn_raw_buffer_load_b32(rg, (chunk(q) * 128 + 2 * lane) * 2, 0, 0);
+  }
+  // residual rows r0 + 2*lane + {0,1} (leader): tagged elements, or the bf16
+  // row of the token's embedding (per-element loads: a resource of n_res
+  // elements reads zero past the tile)
+  const bool has_res = c.w == 0 && needs_res(I);
+  const bool res_embed = has_res && (i_flags(I) & F_RES_EMBED);
+  const uint32_t n_res = has_res ? out_rows(I) : 0;
+  const uint32_t r0 = I->row0;
+  const __amdgpu_buffer_rsrc_t rr = act_rsrc(reinterpret_cast<const char*>(I->res_ptr) + size_t(r0) * kActBytes,
+                                             (has_res && !res_embed) ? n_res * kActBytes : 0);
+  uint2 res_t[2];
+  const uint32_t res_off[2] = {2 * lane * kActBytes, (2 * lane + 1) * kActBytes};
+  reload(res_t[0], rr, res_off[0]);
+  reload(res_t[1], rr, res_off[1]);
+  uint16_t res_e[2] = {0, 0};
+  if (res_embed) {
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(token0(a)) * a.hidden + r0;
+    const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(e), 0, n_res * 2, 0x00020000);
+    res_e[0] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane, 0, 0);
+    res_e[1] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane + 2, 0, 0);
+  }
+  const uint32_t res_live = 2 * lane >= n_res ? 0 : (2 * lane + 1 < n_res ? 2 : 1);
+  if (stage_x) {
+    const uint32_t live = uint32_t(c.w) < nch ? (nch - c.w + kNComp - 1) / kNComp : 0;
+    if (!wait_fresh(t, live, r, off, 0, tag, c.retries)) return false;
+    // every wave has read the previous input out of the x slot
+    if (!wait_all_ge(C_XCONS, i)) return false;
+    float* xs = reinterpret_cast<float*>(lds + kLdsX);
+    uint16_t* gs = reinterpret_cast<uint16_t*>(lds + kLdsGain);
+#pragma unroll
+    for (int q = 0; q < NC; q++) {
+      if (q >= int(live)) continue;
+      const uint32_t o = chunk(q) * 128 + 2 * lane;
+      *reinterpret_cast<float2*>(xs + o) = float2{__uint_as_float(t[q].x), __uint_as_float(t[q].z)};
+      if (norm) *reinterpret_cast<uint32_t*>(gs + o) = gw[q];
     }
   }
-
   if (has_res) {
     float* rs = const_cast<float*>(res_slot(i));
-    if (!res_embed && !wait_fresh(res_t, res_live, rr, [&](int, int j) { return res_off[j]; }, 0, tag, c.retries)) return false;
+    if (!res_embed && !wait_fresh(res_t, res_live, rr, [&](int, int j) { return res_off[j]; }, 0, tag, c.retries))
+      return false;
 #pragma unroll
     for (int j = 0; j < 2; j++)
       if (j < int(res_live))
@@ -1328,17 +1317,23 @@ template <class G>
 DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
   Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0, 0, 0};
   const bool tr = a.trace != nullptr;
-  uint64_t staged_in = 0;          // leader: input currently in the x slot
+  // input currently in the x slot (every wave tracks it, so all take the
+  // same staging decision)
+  uint64_t staged_in = 0;
   uint32_t staged_flags = 0, staged_k = 0;
   uint64_t staged_gain = 0;
   uint32_t seen_ctr = kNoCounter, seen_val = 0;  // leader: last satisfied wait
   for (uint32_t i = 0; i < n; i++) {
     InstrCP I = q + i;
+    const bool is_gemv = i_op(I) == OP_GEMV;
+    // the staged input of the previous GEMV can be reused as is
+    const bool reuse = is_gemv && I->in_ptr == staged_in &&
+                       (i_flags(I) & (F_IN_EMBED | F_NORM)) == staged_flags && I->k == staged_k &&
+                       (!(i_flags(I) & F_NORM) || I->gain_ptr == staged_gain);
+    // tagged GEMV inputs are staged by all compute waves together; the
+    // embedding input and attention inputs by the leader
+    const bool coop = is_gemv && !(i_flags(I) & F_IN_EMBED);
     if (w == 0) {
-      // the staged input of the previous GEMV can be reused as is
-      const bool reuse = i_op(I) == OP_GEMV && I->in_ptr == staged_in &&
-                         (i_flags(I) & (F_IN_EMBED | F_NORM)) == staged_flags && I->k == staged_k &&
-                         (!(i_flags(I) & F_NORM) || I->gain_ptr == staged_gain);
       if (tr && c.lane == 0) {
         trace_put(a, cu, i, TR_START, now32());
         trace_put(a, cu, i, TR_HW0, hw0(I));
@@ -1355,26 +1350,39 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
         seen_ctr = ctr;
         seen_val = target;
       }
-      if (tr && c.lane == 0) trace_put(a, cu, i, TR_DEPS, now32());
-      // every compute wave has read the previous instruction's staged inputs
-      // (the residual rows are restaged every time)
-      if (ok) ok = wait_all_ge(C_XCONS, i);
       if (!ok) {
         if (c.lane == 0) lds_st(C_ABORT, 1);
         return;
       }
-      if (tr && c.lane == 0) trace_put(a, cu, i, TR_XFREE, now32());
-      if (!stage_inputs(c, I, i, reuse)) {
+      if (c.lane == 0) lds_st(C_DEPOK, i + 1);
+      if (tr && c.lane == 0) trace_put(a, cu, i, TR_DEPS, now32());
+    }
+    if (coop) {
+      // inputs ready in memory (the leader saw the counters), then every
+      // wave stages its share; a barrier publishes the x slot
+      if (w != 0 && !wait_lds_ge(C_DEPOK, i + 1)) return;
+      if (!reuse || needs_res(I)) {
+        if (!coop_stage(c, I, i, !reuse)) {
+          if (c.lane == 0) lds_st(C_ABORT, 1);
+          return;
+        }
+        if (!comp_barrier()) return;
+      }
+      if (tr && w == 0 && c.lane == 0) {
+        trace_put(a, cu, i, TR_XFREE, now32());
+        trace_put(a, cu, i, TR_STAGED, now32());
+        trace_put(a, cu, i, TR_RETRY, c.retries);
+      }
+    } else if (w == 0) {
+      // every compute wave has read the previous instruction's staged inputs
+      if (!wait_all_ge(C_XCONS, i)) {
         if (c.lane == 0) lds_st(C_ABORT, 1);
         return;
       }
-      if (i_op(I) == OP_GEMV) {
-        staged_in = I->in_ptr;
-        staged_flags = i_flags(I) & (F_IN_EMBED | F_NORM);
-        staged_k = I->k;
-        staged_gain = I->gain_ptr;
-      } else {
-        staged_in = 0;
+      if (tr && c.lane == 0) trace_put(a, cu, i, TR_XFREE, now32());
+      if (!stage_leader(c, I, i)) {
+        if (c.lane == 0) lds_st(C_ABORT, 1);
+        return;
       }
       if (c.lane == 0) lds_st(C_XOK, i + 1);
       if (tr && c.lane == 0) {
@@ -1383,6 +1391,14 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       }
     } else if (!wait_lds_ge(C_XOK, i + 1)) {
       return;
+    }
+    if (is_gemv) {
+      staged_in = I->in_ptr;
+      staged_flags = i_flags(I) & (F_IN_EMBED | F_NORM);
+      staged_k = I->k;
+      staged_gain = I->gain_ptr;
+    } else {
+      staged_in = 0;
     }
     bool ok = i_op(I) == OP_GEMV ? run_gemv<G>(c, I, i) : run_attn<G>(c, I, i);
     if (!ok) return;
