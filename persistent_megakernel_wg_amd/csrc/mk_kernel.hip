@@ -78,6 +78,7 @@ static_assert(C_FILLED + 4 * kNLoad <= C_RELEASED, "ctrl layout");
 static_assert(C_RELEASED + 4 * kNComp <= C_XOK, "ctrl layout");
 static_assert(C_XCONS + 4 * kNComp <= C_DONE, "ctrl layout");
 static_assert(C_DONE + 4 * kDoneRing <= C_ABORT, "ctrl layout");
+static_assert(C_CTRL_END <= kLdsSS && kLdsSS + 4 * kNComp <= kLdsAcc, "ctrl layout");
 
 DEV uint32_t* lw(int off) { return reinterpret_cast<uint32_t*>(lds + off); }
 DEV uint32_t lds_ld(int off) {
@@ -366,6 +367,13 @@ DEV bool comp_barrier() {
   return wait_lds_ge(C_BAR, target);
 }
 
+// ------------------------------------------------------------------- trace
+DEV uint32_t now32() { return uint32_t(__builtin_amdgcn_s_memrealtime()); }
+DEV void trace_put(const KArgs& a, int cu, uint32_t i, int word, uint32_t v) {
+  if (a.trace && i < a.trace_stride)
+    gp(a.trace)[(size_t(cu) * a.trace_stride + i) * TR_WORDS + word] = v;
+}
+
 // ================================================================== loader
 // One wave-wide 16 B/lane DMA from global memory into LDS at M0.  M0 is set
 // per DMA and not restored: the loader waves use M0 for nothing else, and
@@ -601,11 +609,6 @@ struct Comp {
   uint32_t retries;   // re-reads of stale tagged inputs (leader, traced runs)
 };
 
-DEV uint32_t now32() { return uint32_t(__builtin_amdgcn_s_memrealtime()); }
-DEV void trace_put(const KArgs& a, int cu, uint32_t i, int word, uint32_t v) {
-  if (a.trace && i < a.trace_stride)
-    gp(a.trace)[(size_t(cu) * a.trace_stride + i) * TR_WORDS + word] = v;
-}
 
 // ---- GEMV epilogue for one output row
 struct ArgBest {
@@ -669,19 +672,26 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
   }
   if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
   if (i_flags(I) & F_NORM) {
-    // RMSNorm: every wave holds the whole input (RPU 2: each half-wave does),
-    // so each one normalises its own copy with the staged gain
+    // RMSNorm: every wave normalises its copy of the input with the staged
+    // gain.  A cooperatively staged input comes with the waves' shares of the
+    // sum of squares; the embedding input (leader staging) is summed here
+    // (every wave holds the whole input; RPU 2: each half-wave does).
     float ss = 0.f;
+    if (!(i_flags(I) & F_IN_EMBED)) {
 #pragma unroll
-    for (int j = 0; j < NIT; j++)
-#pragma unroll
-      for (int e = 0; e < 8; e++) ss = fmaf(xv[j][e], xv[j][e], ss);
-    if (RPU == 1) {
-      ss = sum64(ss);
+      for (int w = 0; w < kNComp; w++) ss += *reinterpret_cast<const float*>(lds + kLdsSS + 4 * w);
     } else {
-      float lo, hi;
-      sum32x2(ss, lo, hi);
-      ss = lo;
+#pragma unroll
+      for (int j = 0; j < NIT; j++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) ss = fmaf(xv[j][e], xv[j][e], ss);
+      if (RPU == 1) {
+        ss = sum64(ss);
+      } else {
+        float lo, hi;
+        sum32x2(ss, lo, hi);
+        ss = lo;
+      }
     }
     const float inv = rsqrtf(ss / float(I->k) + a.rms_eps);
     const uint16_t* gs = reinterpret_cast<const uint16_t*>(lds + kLdsGain);
@@ -1182,12 +1192,22 @@ DEV bool coop_stage(Comp& c, InstrCP I, uint32_t i, bool stage_x) {
     if (!wait_all_ge(C_XCONS, i)) return false;
     float* xs = reinterpret_cast<float*>(lds + kLdsX);
     uint16_t* gs = reinterpret_cast<uint16_t*>(lds + kLdsGain);
+    float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < NC; q++) {
       if (q >= int(live)) continue;
       const uint32_t o = chunk(q) * 128 + 2 * lane;
-      *reinterpret_cast<float2*>(xs + o) = float2{__uint_as_float(t[q].x), __uint_as_float(t[q].z)};
-      if (norm) *reinterpret_cast<uint32_t*>(gs + o) = gw[q];
+      const float v0 = __uint_as_float(t[q].x), v1 = __uint_as_float(t[q].z);
+      *reinterpret_cast<float2*>(xs + o) = float2{v0, v1};
+      if (norm) {
+        *reinterpret_cast<uint32_t*>(gs + o) = gw[q];
+        ss = fmaf(v0, v0, fmaf(v1, v1, ss));
+      }
+    }
+    // this wave's share of the sum of squares (gemv adds the kNComp shares)
+    if (norm) {
+      ss = sum64(ss);
+      if (lane == 0) *reinterpret_cast<float*>(lds + kLdsSS + 4 * c.w) = ss;
     }
   }
   if (has_res) {
