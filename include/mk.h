@@ -1,10 +1,15 @@
 /*
- * mk.h — C ABI of the MI355X (gfx950) batch-1 decode megakernel.
+ * mk.h — C ABI of the MI355X (gfx950) decode megakernel.
  *
  * One decode step of a Llama-style decoder (RMSNorm, QKV projection, RoPE, GQA
  * attention over a bf16 KV cache, O projection, SwiGLU MLP, LM head + greedy
  * argmax) runs as ONE persistent HIP kernel with one workgroup per compute
- * unit.  Each workgroup interprets a host-built queue of tile-sized
+ * unit.  A second kernel runs the parallel-block mixture-of-experts decoder of
+ * Cohere's write-up (airebao.com, «快在哪里» item 1: attention and the MoE
+ * both read one RMSNorm output, x_{l+1} = x_l + attn + MoE; a router picks the
+ * top-k experts of every token, their softmax weights sum the experts' SwiGLU
+ * outputs) for B <= 8 sequences per step, each streamed weight byte applied to
+ * every sequence that uses it.  Each workgroup interprets a host-built queue of tile-sized
  * instructions; instructions wait on each other through counters in global
  * memory instead of kernel boundaries.  This follows the design described in
  * Hazy Research's Llama-1B megakernel write-up ("Fusing Operations with an
@@ -49,8 +54,12 @@ typedef enum {
   MK_ERR_DEVICE = -7       /* the kernel reported an error (e.g. NaN logits)*/
 } mk_status;
 
-/* Model shape.  Dense decoders set n_experts = top_k = expert_ffn = 0 and
- * parallel_block = 0. */
+/* Model shape.  Dense decoders (batch 1) set n_experts = top_k = expert_ffn = 0
+ * and parallel_block = 0.  The mixture-of-experts decoder sets n_experts
+ * (<= 64), top_k (<= min(8, n_experts)), expert_ffn (a multiple of 512, at most
+ * 2048) and parallel_block = 1, with batch <= 8, hidden and n_q_heads*head_dim
+ * multiples of 512 and batch * max(hidden, n_q_heads*head_dim) <= 16384; ffn
+ * and the dense MLP weights are unused.  Other shapes: MK_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t n_layers;       /* L                                   */
   int32_t hidden;         /* d                                   */
@@ -60,7 +69,7 @@ typedef struct {
   int32_t ffn;            /* F (dense SwiGLU width)              */
   int32_t vocab;          /* V                                   */
   int32_t max_seq;        /* KV-cache capacity in positions      */
-  int32_t batch;          /* B (1 for the dense path)            */
+  int32_t batch;          /* B (1 for the dense decoder)         */
   int32_t tied_embedding; /* 1: lm_head may equal embed          */
   int32_t n_experts;      /* MoE only                            */
   int32_t top_k;          /* MoE only                            */
@@ -80,11 +89,11 @@ typedef struct {
   const void *wk;         /* [L, G*Dh, d]                          */
   const void *wv;         /* [L, G*Dh, d]                          */
   const void *wo;         /* [L, d, H*Dh]                          */
-  const void *mlp_norm;   /* [L, d]                                */
-  const void *w_gate;     /* [L, F, d]                             */
-  const void *w_up;       /* [L, F, d]                             */
-  const void *w_down;     /* [L, d, F]                             */
-  const void *router;     /* MoE: [L, E, d]                        */
+  const void *mlp_norm;   /* dense: [L, d]                         */
+  const void *w_gate;     /* dense: [L, F, d]                      */
+  const void *w_up;       /* dense: [L, F, d]                      */
+  const void *w_down;     /* dense: [L, d, F]                      */
+  const void *router;     /* MoE: [L, E, d] (attn_norm feeds it)   */
   const void *e_gate;     /* MoE: [L, E, Fe, d]                    */
   const void *e_up;       /* MoE: [L, E, Fe, d]                    */
   const void *e_down;     /* MoE: [L, E, d, Fe]                    */
@@ -111,7 +120,8 @@ typedef struct {
                              the library has one; see kernel_variant) */
   int32_t attn_heads; /* query heads per attention tile, dividing the heads per
                          KV group (default: 1 while n_q_heads * position
-                         blocks <= n_cus, else the whole group) */
+                         blocks <= n_cus, else the whole group; the MoE
+                         decoder: the whole group) */
   int32_t reserved;
 } mk_plan_opts;
 
@@ -127,12 +137,16 @@ typedef struct {
   int32_t attn_block;      /* KV positions per attention tile             */
   int32_t attn_tiles;      /* attention tiles per layer                   */
   int32_t mlp_chunks;
-  int64_t weight_bytes;    /* weight bytes streamed per step              */
+  int64_t weight_bytes;    /* weight bytes streamed per step (MoE: the
+                              part that does not depend on the routing;
+                              each selected expert adds 6 * d * Fe bytes
+                              per layer)                                  */
   int64_t max_cu_bytes;    /* largest per-CU streamed bytes (KV at max_seq)*/
   int64_t min_cu_bytes;    /* smallest per-CU streamed bytes              */
   int32_t kernel_variant;  /* 0: the generic kernel; > 0: the kernel built
                               for this shape (the Llama-3.2-1B, Llama-3-8B
-                              and small test decoder geometries)         */
+                              and small test decoder geometries; MoE: 1 for
+                              4 query heads per group of head_dim 128)   */
   int32_t reserved;
 } mk_plan_summary;
 
@@ -154,6 +168,7 @@ mk_status mk_build_plan(mk_ctx *ctx, const mk_plan_opts *opts);
  *   pos:      position of the new token (= cached positions), 0 <= pos < max_seq;
  *   d_next:   device int32 [B], receives the greedy next token;
  *   d_logits: device float [B, V] or NULL.
+ * Every sequence of a batch is at the same position.
  * Appends the new key/value rows at `pos` to the caller's caches.  Asynchronous:
  * a watchdog timeout or device error surfaces from mk_sync (or the next call).
  * d_tokens may alias d_next of the previous step (device-side chaining).

@@ -130,20 +130,23 @@ class DecoderOracle:
         return val
 
     def step(self, tokens: np.ndarray, pos: int, k_cache: np.ndarray,
-             v_cache: np.ndarray, trace: Optional[dict] = None):
+             v_cache: np.ndarray, trace: Optional[dict] = None, seqs=None):
         """Decode one token per sequence at position ``pos``.
 
         tokens: int [B]; k_cache/v_cache: uint16 [L, B, G, max_seq, Dh], updated
         in place at ``pos``.  Returns (logits float64 [B, V], next int64 [B]).
         ``trace`` (optional dict) receives per-layer intermediates of sequence 0.
+        ``seqs`` (optional) limits the work to those sequences (they do not
+        interact); the other rows of the results are NaN / -1 and their cache
+        rows are left as they were.
         """
         s = self.s
         if not 0 <= pos < s.max_seq:
             raise ValueError("pos outside the KV cache")
         B = s.batch
-        logits = np.empty((B, s.vocab), dtype=np.float64)
-        nxt = np.empty(B, dtype=np.int64)
-        for b in range(B):
+        logits = np.full((B, s.vocab), np.nan, dtype=np.float64)
+        nxt = np.full(B, -1, dtype=np.int64)
+        for b in (range(B) if seqs is None else seqs):
             x = bf16_to_f64(self.w["embed"][int(tokens[b])])
             for layer in range(s.n_layers):
                 if s.parallel_block:

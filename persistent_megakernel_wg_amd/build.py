@@ -50,12 +50,14 @@ def build(verbose: bool = False, extra_defines=()) -> str:
     k_obj = os.path.join(BUILD, "mk_kernel.o")
     p_obj = os.path.join(BUILD, "mk_plan.o")
     r_obj = os.path.join(BUILD, "mk_runtime.o")
+    b_obj = os.path.join(BUILD, "mk_batch.o")
     _run([hipcc, *DEVICE_FLAGS, *defs, "-c", os.path.join(CSRC, "mk_kernel.hip"), "-o", k_obj], verbose)
+    _run([hipcc, *DEVICE_FLAGS, *defs, "-c", os.path.join(CSRC, "mk_batch.hip"), "-o", b_obj], verbose)
     _run([gxx, *HOST_FLAGS, "-c", os.path.join(CSRC, "mk_plan.cpp"), "-o", p_obj], verbose)
     _run([gxx, *HOST_FLAGS, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
           "-c", os.path.join(CSRC, "mk_runtime.cpp"), "-o", r_obj], verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, p_obj, r_obj,
+    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, b_obj, p_obj, r_obj,
           "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB

@@ -1,0 +1,843 @@
+// mk_batch.hip — the batched persistent megakernel (B <= 8 sequences per step)
+// for the parallel-block mixture-of-experts decoder.
+//
+// Cohere's decode megakernel write-up (airebao.com) is the model: attention
+// and the MoE branch read one RMSNorm output and meet in one residual add
+// («快在哪里» item 1); the router weights are small and sit in front of the
+// experts («快在哪里» item 3); every weight byte that is streamed is applied to
+// all sequences of the batch that need it («为什么值得做»).
+//
+// Same workgroup shape as the one-sequence kernel (2 loader + 6 compute waves,
+// one workgroup per CU, counters in global memory), with a different LDS
+// layout: the staged GEMV input holds every sequence's vector ([B][K] fp32),
+// and the page ring has five pages.
+//  * OP_BGEMV: a row pair per compute-wave item; each weight element read from
+//    LDS once is multiplied into all B staged vectors (fp32 FMAs), and the
+//    2 x B partial sums are reduced across the wave with one butterfly.
+//  * OP_EGU / OP_EDN: every CU holds a slice of every expert (gate/up pairs,
+//    down-projection rows), so the work per CU is the same whatever the router
+//    picks.  The loader waves read the router logits, take the top-k of every
+//    sequence and stream only the selected experts' slices, straight from the
+//    expert tensors; the compute waves apply each slice to the sequences routed
+//    to that expert.
+//  * The down projection keeps, per (sequence, top-k slot, row), the dot of its
+//    expert and sums the slots in order with the softmax weights, then adds the
+//    residual (the O-projection output): x_{l+1} = x_l + attn + MoE.
+#include "mk_dev.h"
+
+namespace mk {
+
+// --------------------------------------------------------- routing tables
+// One table per layer parity at lb::kRoute, written by the leader wave at the
+// first expert instruction of a layer and read by every compute wave.
+enum : int {
+  RT_MASK = 0,     // u64 selected-expert mask (union over the batch)
+  RT_NSEL = 8,     // u32 number of selected experts
+  RT_TOK = 16,     // u8 [64] sequences routed to expert e (bit b)
+  RT_LIST = 80,    // u8 [64] selected experts in increasing id order
+  RT_SLOT = 144,   // u8 [64][8] top-k slot of expert e for sequence b
+  RT_WT = 656,     // f32 [8][8] softmax weight of sequence b's slot s
+  RT_END = 912,
+};
+static_assert(RT_END <= lb::kRouteBytes, "routing table size");
+
+DEV int rt_base(uint32_t layer) { return lb::kRoute + int(layer & 1) * lb::kRouteBytes; }
+DEV uint32_t rt_u8(int base, int off) { return *reinterpret_cast<const uint8_t*>(lds + base + off); }
+
+// Top-k of every sequence's router logits.  Lane e holds expert e's logit; k
+// rounds take the maximum and the lowest expert id holding it (ties go to the
+// lower id).  Returns the union of the selections; with table >= 0 the leader
+// also records token masks, slots and the softmax weights over each
+// sequence's k selected logits (top-k first, then softmax over those k).
+// false = abort or watchdog while waiting for fresh logits.
+DEV bool route_topk(const KArgs& a, InstrCP I, uint64_t& mask, int table, uint32_t& retries) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t E = I->aux[4], k = uint32_t(a.top_k), nB = uint32_t(a.batch);
+  const __amdgpu_buffer_rsrc_t r = act_rsrc(reinterpret_cast<const void*>(I->seg_ptr[0]), nB * E * kActBytes);
+  uint2 t[lb::kMaxB];
+  auto off = [&](int, int b) -> uint32_t { return (uint32_t(b) * E + lane) * kActBytes; };
+#pragma unroll
+  for (int b = 0; b < lb::kMaxB; b++) reload(t[b], r, off(0, b));
+  if (!wait_fresh(t, lane < E ? nB : 0u, r, off, 0, a.epoch, retries)) return false;
+  mask = 0;
+  uint32_t tokbits = 0;
+#pragma unroll
+  for (int b = 0; b < lb::kMaxB; b++) {
+    if (uint32_t(b) >= nB) break;
+    float v = lane < E ? __uint_as_float(t[b].x) : -__builtin_inff();
+    if (v != v) v = -__builtin_inff();
+    bool taken = false;
+    float lv = -__builtin_inff();  // lane s: the s-th selected logit
+    uint32_t myslot = 0;
+    for (uint32_t s = 0; s < k; s++) {
+      const float m = max64(taken ? -__builtin_inff() : v);
+      const uint64_t ball = __builtin_amdgcn_ballot_w64(!taken && lane < E && v == m);
+      if (ball == 0) break;  // k > E (the planner rejects it)
+      const uint32_t e = uint32_t(__builtin_ctzll(ball));
+      if (lane == e) {
+        taken = true;
+        myslot = s;
+      }
+      if (lane == s) lv = m;
+      mask |= 1ull << e;
+    }
+    if (table >= 0) {
+      if (taken) {
+        tokbits |= 1u << b;
+        *reinterpret_cast<uint8_t*>(lds + table + RT_SLOT + lane * 8 + b) = uint8_t(myslot);
+      }
+      const float top = rl(lv, 0);
+      const float ex = lane < k ? __expf(lv - top) : 0.f;
+      const float den = sum64(ex);
+      if (lane < lb::kMaxTopK)
+        *reinterpret_cast<float*>(lds + table + RT_WT + (b * 8 + int(lane)) * 4) = ex / den;
+    }
+  }
+  if (table >= 0) {
+    if (lane < E) {
+      *reinterpret_cast<uint8_t*>(lds + table + RT_TOK + lane) = uint8_t(tokbits);
+      if ((mask >> lane) & 1) {
+        const uint32_t rank = __builtin_popcountll(mask & ((1ull << lane) - 1));
+        *reinterpret_cast<uint8_t*>(lds + table + RT_LIST + rank) = uint8_t(lane);
+      }
+    }
+    if (lane == 0) {
+      *reinterpret_cast<uint64_t*>(lds + table + RT_MASK) = mask;
+      *lw(table + RT_NSEL) = uint32_t(__builtin_popcountll(mask));
+    }
+  }
+  return true;
+}
+
+// --------------------------------------------------------------- loader
+// Same paging as the one-sequence loader, with a running page index: an
+// expert instruction takes (selected experts) x (pages per expert) pages, a
+// number known only once the loader has read the layer's router logits.
+DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
+  const uint32_t voff = (threadIdx.x & 63) * 16, voff4k = voff + 4096;
+  const uint32_t half = uint32_t(v) * kDmaPerPage;
+  uint32_t nd = 0, g_issue = 0, g_pub = 0, min_rel = 0, pg = 0;
+  uint32_t route_layer = 0xFFFFFFFFu;
+  uint64_t mask = 0;
+  uint32_t retries = 0;
+  // wait for ring space for page g; false = abort
+  auto acquire = [&](uint32_t g) -> bool {
+    if (g < min_rel + lb::kPages) return true;
+    Watch t0;
+    for (;;) {
+      min_rel = uni(min_released());
+      if (g < min_rel + lb::kPages) return true;
+      if (g_pub < g_issue) {
+        wait_vm_pages(g_issue - g_pub - 1);
+        publish(g_pub, g_pub + 1, v);
+        continue;
+      }
+      if (aborted() || local_timeout(t0, local_limit())) {
+        if (!aborted()) local_abort(STC_LOCAL_TIMEOUT);
+        wait_vm0();
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  };
+  auto after_issue = [&](uint32_t g, bool deep) {
+    g_issue = g + 1;
+    const uint32_t vmt = deep ? kVmTDeep : kVmT;
+    if (nd > vmt) publish(g_pub, (nd - vmt) / kDmaPerPage, v);
+  };
+  for (uint32_t i = 0; i < n; i++) {
+    InstrCP I = q + i;
+    const uint32_t op = i_op(I);
+    if (op == OP_EGU || op == OP_EDN) {
+      const uint32_t layer = I->layer;
+      if (layer != route_layer) {
+        // every issued page is published before the wait
+        wait_vm0();
+        publish(g_pub, g_issue, v);
+        if (!wait_counter(a, I->aux[0], a.epoch * I->aux[1], cu, i) ||
+            !route_topk(a, I, mask, -1, retries)) {
+          if ((threadIdx.x & 63) == 0) lds_st(C_ABORT, 1);
+          return;
+        }
+        mask = uni64(mask);
+        route_layer = layer;
+      }
+      const uint32_t ppe = I->aux[2], gpg = I->seg_stride[1], run = I->seg_rows[0];
+      const uint64_t stride = I->seg_stride[0];
+      for (uint64_t m = mask; m; m &= m - 1) {
+        const uint32_t e = uint32_t(__builtin_ctzll(m));
+        const uint64_t b0 = I->seg_ptr[1] + e * stride, b1 = I->seg_ptr[2] + e * stride;
+        for (uint32_t p = 0; p < ppe; p++) {
+          const uint32_t g = pg++;
+          if (!acquire(g)) return;
+          const uint32_t second = p < gpg ? 0 : 1;
+          const uint32_t dst = uint32_t(size_t(lds)) + page_off<LayB>(g) + half * kUnit;
+          issue_run(a, dst, second ? b1 : b0, ((p - second * gpg) * kUnitsPerPage + half) * kUnit, run, voff,
+                    voff4k, nd);
+          after_issue(g, false);
+        }
+      }
+      continue;
+    }
+    LoadView L;
+    load_view(a, I, L);
+    const uint32_t np = I->n_pages;
+    for (uint32_t p = 0; p < np; p++) {
+      const uint32_t g = pg++;
+      if (!acquire(g)) return;
+      issue_page<LayB>(a, L, p, g, v, voff, voff4k, nd);
+      after_issue(g, L.deep);
+    }
+  }
+  wait_vm0();
+  publish(g_pub, g_issue, v);
+}
+
+// ------------------------------------------------------------- reductions
+// Butterfly over 64 lanes of 16 values: afterwards lane l holds the sum over
+// all lanes of v[l % 16].  Each stage pairs lanes (row mirror, half-row
+// mirror, xor 2, xor 1), and the lane keeps one half of its values plus its
+// partner's copy of that half; the 16-lane rows are then added with two
+// exchanges.  Fixed order: deterministic.
+template <int CTRL, int N>
+DEV void bfly_stage(float (&v)[16], bool keep_lo) {
+#pragma unroll
+  for (int j = 0; j < N; j++) {
+    const float send = keep_lo ? v[j + N] : v[j];
+    const float keep = keep_lo ? v[j] : v[j + N];
+    v[j] = keep + dpp<CTRL>(send);
+  }
+}
+DEV float reduce16(float (&v)[16]) {
+  const uint32_t l = threadIdx.x & 63;
+  bfly_stage<0x140, 8>(v, (l & 15) < 8);  // row_mirror
+  bfly_stage<0x141, 4>(v, (l & 7) < 4);   // row_half_mirror
+  bfly_stage<0x4E, 2>(v, (l & 3) < 2);    // quad_perm [2,3,0,1]
+  bfly_stage<0xB1, 1>(v, (l & 1) == 0);   // quad_perm [1,0,3,2]
+  float r = v[0];
+  r += __shfl_xor(r, 16, 64);
+  r += __shfl_xor(r, 32, 64);
+  return r;
+}
+
+DEV const float* res_slot_b(uint32_t i) {
+  return reinterpret_cast<const float*>(lds + lb::kRes + (i & 1) * 4 * kMaxResRows);
+}
+
+// input token of sequence b, checked against the vocabulary
+DEV uint32_t token_b(const KArgs& a, uint32_t b) {
+  const int32_t t = gp(a.tokens)[b];
+  if (t >= 0 && t < a.vocab) return uint32_t(t);
+  __hip_atomic_store(gp(a.status) + ST_BADTOK, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return 0;
+}
+
+// Inverse RMS of every staged sequence (lane b holds sequence b's), from the
+// per-chunk sums of squares; 1 without RMSNorm.
+DEV float inv_rms(const KArgs& a, InstrCP I) {
+  const uint32_t lane = threadIdx.x & 63;
+  if (!(i_flags(I) & F_NORM)) return 1.f;
+  const uint32_t K = I->k, per = K / 128;
+  const float* ss = reinterpret_cast<const float*>(lds + lb::kSS);
+  float s = 0.f;
+  if (lane < uint32_t(a.batch))
+    for (uint32_t j = 0; j < per; j++) s += ss[lane * per + j];
+  return rsqrtf(s / float(K) + a.rms_eps);
+}
+
+// ----------------------------------------------------------------- staging
+// Cooperative staging of a batched GEMV input [B][K] (tagged activations, or
+// the bf16 embedding rows of the B tokens): wave w loads the 128-value chunks
+// w, w + kNComp, ... (every load before the first wait), and once every wave
+// has read the previous input writes g * x (the RMSNorm gain folded in; the
+// inverse RMS is applied to the dot products) and each chunk's sum of squares.
+// The leader also stages the residual rows of an EPI_RESID tile or of an
+// expert down-projection: res[b][row0 .. row0 + n) for every sequence.
+DEV bool stage_res_b(Comp& c, InstrCP I, uint32_t i, uint32_t n_rows, uint32_t rstride);
+
+DEV bool coop_stage_b(Comp& c, InstrCP I, uint32_t i, bool stage_x) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane;
+  constexpr int NC = (lb::kXFloats / 128 + kNComp - 1) / kNComp;
+  const uint32_t K = I->k, nB = uint32_t(a.batch), nch = nB * K / 128;
+  const bool norm = i_flags(I) & F_NORM, embed = i_flags(I) & F_IN_EMBED;
+  const __amdgpu_buffer_rsrc_t r =
+      act_rsrc(reinterpret_cast<const void*>(I->in_ptr), (stage_x && !embed) ? nB * K * kActBytes : 0);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(I->gain_ptr), 0, (stage_x && norm) ? K * 2 : 0, 0x00020000);
+  auto chunk = [&](int qq) -> uint32_t { return uint32_t(c.w) + kNComp * qq; };
+  auto off = [&](int, int qq) -> uint32_t { return (chunk(qq) * 128 + 2 * lane) * kActBytes; };
+  const uint32_t live = (stage_x && uint32_t(c.w) < nch) ? (nch - c.w + kNComp - 1) / kNComp : 0;
+  u4 t[NC];
+  uint32_t gw[NC], ew[NC];
+  const int32_t tokv = (embed && stage_x && lane < nB) ? gp(a.tokens)[lane] : 0;
+#pragma unroll
+  for (int qq = 0; qq < NC; qq++) {
+    const uint32_t flat = chunk(qq) * 128, kk = flat % K;
+    t[qq] = ld_tag2(r, off(0, qq));
+    gw[qq] = __builtin_amdgcn_raw_buffer_load_b32(rg, (kk + 2 * lane) * 2, 0, 0);
+    ew[qq] = 0;
+    if (embed && qq < int(live)) {
+      int32_t tok = __builtin_amdgcn_readlane(tokv, int(flat / K));
+      if (tok < 0 || tok >= a.vocab) {
+        __hip_atomic_store(gp(a.status) + ST_BADTOK, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tok = 0;
+      }
+      ew[qq] = *gp(reinterpret_cast<const uint32_t*>(I->in_ptr) + (size_t(tok) * K + kk) / 2 + lane);
+    }
+  }
+  if (stage_x) {
+    if (!embed && !wait_fresh(t, live, r, off, 0, a.epoch, c.retries)) return false;
+    if (!wait_all_ge(C_XCONS, i)) return false;
+    float* xs = reinterpret_cast<float*>(lds + lb::kX);
+    float* ss = reinterpret_cast<float*>(lds + lb::kSS);
+#pragma unroll
+    for (int qq = 0; qq < NC; qq++) {
+      if (qq >= int(live)) continue;
+      const uint32_t flat = chunk(qq) * 128 + 2 * lane;
+      const float v0 = embed ? bf_lo(ew[qq]) : __uint_as_float(t[qq].x);
+      const float v1 = embed ? bf_hi(ew[qq]) : __uint_as_float(t[qq].z);
+      const float g0 = norm ? bf_lo(gw[qq]) : 1.f, g1 = norm ? bf_hi(gw[qq]) : 1.f;
+      *reinterpret_cast<float2*>(xs + flat) = float2{g0 * v0, g1 * v1};
+      if (norm) {
+        const float s = sum64(fmaf(v0, v0, v1 * v1));
+        if (lane == 0) ss[chunk(qq)] = s;
+      }
+    }
+  }
+  if (c.w == 0 && i_op(I) == OP_BGEMV && i_epi(I) == EPI_RESID)
+    return stage_res_b(c, I, i, I->n_rows, I->aux[2]);
+  return true;
+}
+
+// residual rows res[b][row0 + r] for r < n_rows, b < B (n_rows * B <= 128):
+// tagged activations or, with F_RES_EMBED, the embedding rows of the tokens
+DEV bool stage_res_b(Comp& c, InstrCP I, uint32_t i, uint32_t n_rows, uint32_t rstride) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane, nB = uint32_t(a.batch), total = n_rows * nB;
+  const bool embed = i_flags(I) & F_RES_EMBED;
+  const uint32_t r0 = I->row0;
+  const __amdgpu_buffer_rsrc_t rr = act_rsrc(reinterpret_cast<const void*>(I->res_ptr),
+                                             embed ? 0 : nB * rstride * kActBytes);
+  uint2 t[2];
+  uint32_t eo[2] = {0, 0};
+  uint32_t offs[2];
+  for (int j = 0; j < 2; j++) {
+    const uint32_t idx = 2 * lane + j, b = idx / n_rows, rr_ = idx % n_rows;
+    offs[j] = (b * rstride + r0 + rr_) * kActBytes;
+    reload(t[j], rr, offs[j]);
+    if (embed && idx < total) {
+      const uint32_t tok = token_b(a, b);
+      eo[j] = *gp(reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(tok) * a.hidden + r0 + rr_);
+    }
+  }
+  const uint32_t live = 2 * lane >= total ? 0 : (2 * lane + 1 < total ? 2 : 1);
+  if (!embed && !wait_fresh(t, live, rr, [&](int, int j) { return offs[j]; }, 0, a.epoch, c.retries))
+    return false;
+  float* rs = const_cast<float*>(res_slot_b(i));
+  for (int j = 0; j < 2; j++)
+    if (j < int(live)) rs[2 * lane + j] = embed ? __uint_as_float(eo[j] << 16) : __uint_as_float(t[j].x);
+  return true;
+}
+
+// ------------------------------------------------------------- batched GEMV
+// Unit u of the instruction's page stream (starting at page pg), this lane's
+// 16 bytes.
+DEV u4 unit_ld(uint32_t pg, uint32_t u, uint32_t lane) {
+  return *reinterpret_cast<const u4*>(lds + page_off<LayB>(pg + u / kUnitsPerPage) + (u % kUnitsPerPage) * kUnit +
+                                      lane * 16);
+}
+DEV void x8_ld(const float* p, float (&o)[8]) {
+  const f4 lo = *reinterpret_cast<const f4*>(p);
+  const f4 hi = *reinterpret_cast<const f4*>(p + 4);
+  o[0] = lo.x; o[1] = lo.y; o[2] = lo.z; o[3] = lo.w;
+  o[4] = hi.x; o[5] = hi.y; o[6] = hi.z; o[7] = hi.w;
+}
+
+// acc[b] += row a . x_b and acc[8 + b] += row b . x_b over the K values of
+// the staged inputs of the sequences in `tm`; rows are NIT units from unit ua
+// and ub of the stream; x_b starts at xs + xoff(b).
+template <class XOff>
+DEV void dot_pair(uint32_t pg, uint32_t ua, uint32_t ub, uint32_t nit, uint32_t tm, XOff xoff,
+                  float (&acc)[16]) {
+  const uint32_t lane = threadIdx.x & 63;
+  const float* xs = reinterpret_cast<const float*>(lds + lb::kX);
+#pragma unroll
+  for (int e = 0; e < 16; e++) acc[e] = 0.f;
+  for (uint32_t j = 0; j < nit; j++) {
+    const u4 wa = unit_ld(pg, ua + j, lane);
+    const u4 wb = unit_ld(pg, ub + j, lane);
+#pragma unroll
+    for (int b = 0; b < lb::kMaxB; b++) {
+      if (!((tm >> b) & 1)) continue;
+      float x[8];
+      x8_ld(xs + xoff(b) + j * 512 + lane * 8, x);
+      acc[b] += dot8(wa, x);
+      acc[8 + b] += dot8(wb, x);
+    }
+  }
+}
+
+DEV bool bgemv(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane, nB = uint32_t(a.batch), K = I->k, nit = i_nit(I);
+  const uint32_t epi = i_epi(I), n_rows = I->n_rows, n_items = I->n_items, row0 = I->row0;
+  const uint32_t ostride = I->aux[0];
+  const uint32_t tm = (1u << nB) - 1;
+  const float inv = inv_rms(a, I);
+  const uint32_t li = lane & 15, ri = li >> 3, bb = li & 7;
+  const float my_inv = __shfl(inv, int(bb), 64);
+  uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
+  const float* res = res_slot_b(i);
+  ArgBest best{-__builtin_inff(), 0xFFFFFFFFu};
+  for (uint32_t t = c.w; t < n_items; t += kNComp) {
+    const uint32_t u0 = t * 2 * nit;
+    if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + u0 / kUnitsPerPage);
+    if (!wait_page(pg + (u0 + 2 * nit - 1) / kUnitsPerPage, c.fcache)) return false;
+    float acc[16];
+    dot_pair(pg, u0, u0 + nit, nit, tm, [&](int b) { return uint32_t(b) * K; }, acc);
+    const float s = reduce16(acc) * my_inv;
+    const uint32_t rl_ = 2 * t + ri;
+    if (lane < 16 && bb < nB && rl_ < n_rows) {
+      const uint32_t row = row0 + rl_;
+      switch (epi) {
+        case EPI_STORE:
+          st_tag(out + size_t(bb) * ostride + row, s, a.epoch);
+          break;
+        case EPI_RESID:
+          st_tag(out + size_t(bb) * ostride + row, res[bb * n_rows + rl_] + s, a.epoch);
+          break;
+        default:  // EPI_ARGMAX
+          if (a.logits) gp(a.logits)[size_t(bb) * a.vocab + row] = s;
+          if (s != s) __hip_atomic_store(gp(a.status) + ST_NAN, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          arg_update(best, s, row);
+          break;
+      }
+    }
+  }
+  if (epi == EPI_ARGMAX) {
+    // lanes b and b + 8 hold sequence b's best of even and odd rows
+    const float ov = __shfl(best.v, int(lane + 8) & 63, 64);
+    const uint32_t oi = __shfl(best.i, int(lane + 8) & 63, 64);
+    arg_update(best, ov, oi);
+    if (lane < 8) {
+      *lw(lb::kArg + (c.w * 8 + int(lane)) * 8) = __float_as_uint(best.v);
+      *lw(lb::kArg + (c.w * 8 + int(lane)) * 8 + 4) = best.i;
+    }
+  }
+  if (lane == 0) {
+    lds_st(C_RELEASED + 4 * c.w, pg + I->n_pages);
+    lds_st(C_XCONS + 4 * c.w, i + 1);
+  }
+  return true;
+}
+
+// ------------------------------------------------------ expert gate / up
+// Items are (selected expert, pair of the CU's slice) in expert order; each
+// applies the gate and up rows to the sequences routed to the expert and
+// stores m = silu(gate) * up at [b][slot of e in b's top-k][row].
+DEV bool egu(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane, K = I->k, nit = i_nit(I);
+  const int rt = rt_base(I->layer);
+  const uint32_t nsel = *lw(rt + RT_NSEL), npu = I->aux[3], ppe = I->aux[2], gpg = I->seg_stride[1];
+  const uint32_t Fe = uint32_t(a.expert_ffn), k = uint32_t(a.top_k);
+  const float inv = inv_rms(a, I);
+  const float my_inv = __shfl(inv, int(lane & 7), 64);
+  uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
+  const uint32_t n_items = nsel * npu;
+  for (uint32_t t = c.w; t < n_items; t += kNComp) {
+    const uint32_t er = t / npu, p = t % npu;
+    const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
+    const uint32_t tm = uni(rt_u8(rt, RT_TOK + int(e)));
+    const uint32_t ug = er * ppe * kUnitsPerPage + p * nit, uu = ug + gpg * kUnitsPerPage;
+    if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + ug / kUnitsPerPage);
+    if (!wait_page(pg + (uu + nit - 1) / kUnitsPerPage, c.fcache)) return false;
+    float acc[16];
+    dot_pair(pg, ug, uu, nit, tm, [&](int b) { return uint32_t(b) * K; }, acc);
+    const float s = reduce16(acc);
+    const float up = __shfl(s, int((lane & 7) + 8), 64);
+    if (lane < 8 && ((tm >> lane) & 1)) {
+      const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + lane));
+      const float m = silu(s * my_inv) * (up * my_inv);
+      st_tag(out + (size_t(lane) * k + slot) * Fe + I->row0 + p, m, a.epoch);
+    }
+  }
+  if (lane == 0) {
+    lds_st(C_RELEASED + 4 * c.w, pg + nsel * ppe);
+    lds_st(C_XCONS + 4 * c.w, i + 1);
+  }
+  return true;
+}
+
+// ---------------------------------------------------- expert down projection
+// The routed (expert, sequence) pairs' intermediate vectors are staged into
+// the x slot in groups that fit it; the items of a group are (expert, row
+// pair); each stores its dots per (sequence, slot, row).  At the end
+// x_{l+1}[b][row] = h[b][row] + sum over slots s of w[b][s] * dot[b][s][row].
+DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane, K = I->k, nit = i_nit(I), nB = uint32_t(a.batch);
+  const int rt = rt_base(I->layer);
+  const uint32_t nsel = *lw(rt + RT_NSEL), ppe = I->aux[2], nr = I->aux[3], ipe = (nr + 1) / 2;
+  const uint32_t k = uint32_t(a.top_k), Fe = uint32_t(a.expert_ffn);
+  const uint32_t cap = uint32_t(lb::kXFloats) / K;  // pairs per group
+  float* xs = reinterpret_cast<float*>(lds + lb::kX);
+  float* dots = reinterpret_cast<float*>(lds + lb::kDots);
+  constexpr int NC = (lb::kXFloats / 128 + kNComp - 1) / kNComp;
+  const uint64_t* m_in = reinterpret_cast<const uint64_t*>(I->in_ptr);
+  // residual rows (leader), then every wave has left the previous input
+  if (c.w == 0 && !stage_res_b(c, I, i, nr, uint32_t(a.hidden))) return false;
+  if (!wait_all_ge(C_XCONS, i)) return false;
+  const __amdgpu_buffer_rsrc_t rm = act_rsrc(m_in, nB * k * Fe * kActBytes);
+  uint32_t er0 = 0;
+  while (er0 < nsel) {
+    // the group: experts [er0, er1) with at most cap routed pairs
+    uint32_t er1 = er0, npair = 0;
+    while (er1 < nsel) {
+      const uint32_t pc = __builtin_popcount(rt_u8(rt, RT_TOK + int(rt_u8(rt, RT_LIST + int(er1)))));
+      if (npair + pc > cap) break;
+      npair += pc;
+      er1++;
+    }
+    npair = uni(npair);
+    er1 = uni(er1);
+    // stage: pair pi (in expert, then sequence order) <- m[b][slot][0 .. K)
+    const uint32_t nch = npair * K / 128;
+    const uint32_t live = uint32_t(c.w) < nch ? (nch - c.w + kNComp - 1) / kNComp : 0;
+    u4 t[NC];
+    uint32_t offs[NC];
+#pragma unroll
+    for (int qq = 0; qq < NC; qq++) {
+      offs[qq] = 0;
+      if (qq < int(live)) {
+        const uint32_t ch = uint32_t(c.w) + kNComp * qq, pi = ch * 128 / K, kk = ch * 128 % K;
+        // pair pi -> (expert, sequence)
+        uint32_t left = pi, er = er0, tm = 0;
+        for (;; er++) {
+          tm = rt_u8(rt, RT_TOK + int(rt_u8(rt, RT_LIST + int(er))));
+          const uint32_t pc = __builtin_popcount(tm);
+          if (left < pc) break;
+          left -= pc;
+        }
+        uint32_t b = 0;
+        for (uint32_t bits = tm;; bits &= bits - 1) {
+          if (left == 0) {
+            b = __builtin_ctz(bits);
+            break;
+          }
+          left--;
+        }
+        const uint32_t e = rt_u8(rt, RT_LIST + int(er));
+        const uint32_t s = rt_u8(rt, RT_SLOT + int(e * 8 + b));
+        offs[qq] = ((b * k + s) * Fe + kk + 2 * lane) * kActBytes;
+      }
+      t[qq] = ld_tag2(rm, offs[qq]);
+    }
+    if (!wait_fresh(t, live, rm, [&](int, int qq) { return offs[qq]; }, 0, a.epoch, c.retries)) return false;
+#pragma unroll
+    for (int qq = 0; qq < NC; qq++) {
+      if (qq >= int(live)) continue;
+      const uint32_t flat = (uint32_t(c.w) + kNComp * qq) * 128 + 2 * lane;
+      *reinterpret_cast<float2*>(xs + flat) = float2{__uint_as_float(t[qq].x), __uint_as_float(t[qq].z)};
+    }
+    if (!comp_barrier()) return false;
+    // items: (expert er in the group, row pair p)
+    const uint32_t n_items = (er1 - er0) * ipe;
+    for (uint32_t it = c.w; it < n_items; it += kNComp) {
+      const uint32_t er = er0 + it / ipe, p = it % ipe;
+      uint32_t pbase = 0;
+      for (uint32_t x = er0; x < er; x++) pbase += __builtin_popcount(rt_u8(rt, RT_TOK + int(rt_u8(rt, RT_LIST + int(x)))));
+      pbase = uni(pbase);
+      const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
+      const uint32_t tm = uni(rt_u8(rt, RT_TOK + int(e)));
+      const uint32_t u0 = er * ppe * kUnitsPerPage + 2 * p * nit;
+      if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + u0 / kUnitsPerPage);
+      if (!wait_page(pg + (u0 + 2 * nit - 1) / kUnitsPerPage, c.fcache)) return false;
+      float acc[16];
+      dot_pair(pg, u0, u0 + nit, nit, tm,
+               [&](int b) { return (pbase + __builtin_popcount(tm & ((1u << b) - 1))) * K; }, acc);
+      const float s = reduce16(acc);
+      const uint32_t li = lane & 15, ri = li >> 3, bb = li & 7, row = 2 * p + ri;
+      if (lane < 16 && ((tm >> bb) & 1) && row < nr) {
+        const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + bb));
+        dots[(bb * lb::kMaxTopK + slot) * lb::kMaxDnRows + row] = s;
+      }
+    }
+    if (!comp_barrier()) return false;
+    er0 = er1;
+  }
+  // x_{l+1} = h + sum over the top-k slots in order
+  const float* res = res_slot_b(i);
+  const float* wt = reinterpret_cast<const float*>(lds + rt + RT_WT);
+  uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
+  for (uint32_t idx = c.w * 64 + lane; idx < nB * nr; idx += 64 * kNComp) {
+    const uint32_t b = idx / nr, r = idx % nr;
+    float y = 0.f;
+    for (uint32_t s = 0; s < k; s++) y = fmaf(wt[b * 8 + s], dots[(b * lb::kMaxTopK + s) * lb::kMaxDnRows + r], y);
+    st_tag(out + size_t(b) * a.hidden + I->row0 + r, res[b * nr + r] + y, a.epoch);
+  }
+  if (lane == 0) {
+    lds_st(C_RELEASED + 4 * c.w, pg + nsel * ppe);
+    lds_st(C_XCONS + 4 * c.w, i + 1);
+  }
+  return true;
+}
+
+// LM head: per sequence, combine the waves' bests, publish the CU's slot,
+// take a ticket; the last CU reduces every sequence's slots (lowest index
+// wins ties) and writes the tokens.
+DEV void lm_finish_b(Comp& c, InstrCP I) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane, nB = uint32_t(a.batch);
+  const uint32_t tile = I->aux[1], n_tiles = I->aux[3];
+  if (lane < nB) {
+    ArgBest b{-__builtin_inff(), 0xFFFFFFFFu};
+    for (int w = 0; w < kNComp; w++)
+      arg_update(b, __uint_as_float(*lw(lb::kArg + (w * 8 + int(lane)) * 8)), *lw(lb::kArg + (w * 8 + int(lane)) * 8 + 4));
+    st_act(a.lm_slots + (size_t(tile) * lb::kMaxB + lane) * 2, b.v);
+    st_act(a.lm_slots + (size_t(tile) * lb::kMaxB + lane) * 2 + 1, __uint_as_float(b.i));
+  }
+  uint32_t old = 0;
+  if (lane == 0) old = ctr_release(ctr_line(a, I->sig_ctr, 0));
+  old = uni(old);
+  if (old + 1 != a.epoch * n_tiles) return;
+  for (uint32_t b = 0; b < nB; b++) {
+    ArgBest all{-__builtin_inff(), 0xFFFFFFFFu};
+    for (uint32_t t = lane; t < n_tiles; t += 64)
+      arg_update(all, ld_act(a.lm_slots + (size_t(t) * lb::kMaxB + b) * 2),
+                 __float_as_uint(ld_act(a.lm_slots + (size_t(t) * lb::kMaxB + b) * 2 + 1)));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float ov = __shfl_xor(all.v, m, 64);
+      const uint32_t oi = __shfl_xor(all.i, m, 64);
+      arg_update(all, ov, oi);
+    }
+    if (lane == 0) gp(a.next)[b] = int32_t(all.i);
+  }
+}
+
+// ---------------------------------------------------------------- variants
+// GeoB: attention tile shape (query heads per tile, head dimension) compiled
+// for one shape; GeoBAny dispatches it per instruction.
+template <int H, int D>
+struct GeoB {
+  static constexpr bool any = false;
+  static constexpr int hpt = H, dh = D;
+};
+struct GeoBAny {
+  static constexpr bool any = true;
+};
+
+template <class G>
+DEV bool run_attn_b(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
+  if constexpr (!G::any) {
+    return attn<G::hpt, G::dh, LayB>(c, I, i, pg);
+  } else {
+    const uint32_t hpt = I->n_items;
+    if (c.a->head_dim == 64) {
+      switch (hpt) {
+        case 1: return attn<1, 64, LayB>(c, I, i, pg);
+        case 2: return attn<2, 64, LayB>(c, I, i, pg);
+        case 4: return attn<4, 64, LayB>(c, I, i, pg);
+        default: return attn<8, 64, LayB>(c, I, i, pg);
+      }
+    }
+    switch (hpt) {
+      case 1: return attn<1, 128, LayB>(c, I, i, pg);
+      case 2: return attn<2, 128, LayB>(c, I, i, pg);
+      default: return attn<4, 128, LayB>(c, I, i, pg);
+    }
+  }
+}
+template <class G>
+DEV void run_merge_b(Comp& c, InstrCP I) {
+  if constexpr (!G::any) {
+    attn_merge<G::hpt, G::dh>(c, I);
+  } else {
+    const uint32_t hpt = I->n_items;
+    if (c.a->head_dim == 64) {
+      switch (hpt) {
+        case 1: return attn_merge<1, 64>(c, I);
+        case 2: return attn_merge<2, 64>(c, I);
+        case 4: return attn_merge<4, 64>(c, I);
+        default: return attn_merge<8, 64>(c, I);
+      }
+    }
+    switch (hpt) {
+      case 1: return attn_merge<1, 128>(c, I);
+      case 2: return attn_merge<2, 128>(c, I);
+      default: return attn_merge<4, 128>(c, I);
+    }
+  }
+}
+
+template <class G>
+DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
+  Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0, 0, 0};
+  const bool tr = a.trace != nullptr;
+  uint64_t staged_in = 0, staged_gain = 0;
+  uint32_t staged_flags = 0, staged_k = 0;
+  uint32_t seen_ctr = kNoCounter, seen_val = 0;
+  uint32_t pg = 0;
+  for (uint32_t i = 0; i < n; i++) {
+    InstrCP I = q + i;
+    const uint32_t op = i_op(I);
+    if (w == 0) {
+      if (tr && c.lane == 0) {
+        trace_put(a, cu, i, TR_START, now32());
+        trace_put(a, cu, i, TR_HW0, hw0(I));
+        trace_put(a, cu, i, TR_HW1, hw1(I));
+      }
+      c.retries = 0;
+      bool ok = true;
+      for (int k = 0; k < 2 && ok; k++) {
+        if (!I->wait_cnt[k]) continue;
+        const uint32_t ctr = I->wait_ctr[k], target = a.epoch * I->wait_cnt[k];
+        if (ctr == seen_ctr && int32_t(seen_val - target) >= 0) continue;
+        ok = wait_counter(a, ctr, target, cu, i);
+        seen_ctr = ctr;
+        seen_val = target;
+      }
+      if (ok && (i_flags(I) & F_ROUTE)) {
+        // every wave has finished the earlier instructions (and with them
+        // every read of this table slot) before it is rewritten
+        uint64_t mask = 0;
+        ok = wait_all_ge(C_XCONS, i) && route_topk(a, I, mask, rt_base(I->layer), c.retries);
+      }
+      if (!ok) {
+        if (c.lane == 0) lds_st(C_ABORT, 1);
+        return;
+      }
+      if (c.lane == 0) lds_st(C_DEPOK, i + 1);
+      if (tr && c.lane == 0) trace_put(a, cu, i, TR_DEPS, now32());
+    }
+    if (op == OP_ATTN) {
+      if (w == 0) {
+        if (!wait_all_ge(C_XCONS, i) || !stage_attn<LayB>(c, I)) {
+          if (c.lane == 0) lds_st(C_ABORT, 1);
+          return;
+        }
+        if (c.lane == 0) lds_st(C_XOK, i + 1);
+      } else if (!wait_lds_ge(C_XOK, i + 1)) {
+        return;
+      }
+    } else if (w != 0 && !wait_lds_ge(C_DEPOK, i + 1)) {
+      return;
+    }
+    uint32_t np = I->n_pages;
+    if (op == OP_EGU || op == OP_EDN) np = *lw(rt_base(I->layer) + RT_NSEL) * I->aux[2];
+    bool ok = true;
+    if (op == OP_BGEMV || op == OP_EGU) {
+      const uint32_t fl = i_flags(I) & (F_IN_EMBED | F_NORM);
+      const bool reuse = I->in_ptr == staged_in && fl == staged_flags && I->k == staged_k &&
+                         (!(fl & F_NORM) || I->gain_ptr == staged_gain);
+      const bool res = op == OP_BGEMV && i_epi(I) == EPI_RESID;
+      if (!reuse || res) {
+        if (!coop_stage_b(c, I, i, !reuse)) {
+          if (c.lane == 0) lds_st(C_ABORT, 1);
+          return;
+        }
+        if (!comp_barrier()) return;
+      }
+      if (tr && w == 0 && c.lane == 0) {
+        trace_put(a, cu, i, TR_STAGED, now32());
+        trace_put(a, cu, i, TR_RETRY, c.retries);
+      }
+      staged_in = I->in_ptr;
+      staged_flags = fl;
+      staged_k = I->k;
+      staged_gain = I->gain_ptr;
+      ok = op == OP_BGEMV ? bgemv(c, I, i, pg) : egu(c, I, i, pg);
+    } else {
+      staged_in = 0;
+      ok = op == OP_EDN ? edn(c, I, i, pg) : run_attn_b<G>(c, I, i, pg);
+    }
+    if (!ok) {
+      if (c.lane == 0) lds_st(C_ABORT, 1);
+      return;
+    }
+    pg += np;
+    if (tr && w == 0 && c.lane == 0) trace_put(a, cu, i, TR_ITEMS, now32());
+    const bool lm = op == OP_BGEMV && i_epi(I) == EPI_ARGMAX;
+    const bool ticket = op == OP_ATTN && I->aux[3] > 1;
+    if (lm || ticket) wait_vm0();
+    uint32_t prev = 0;
+    if (c.lane == 0) prev = lds_add(C_DONE + 4 * (i % kDoneRing), 1);
+    prev = uni(prev);
+    if (prev != kNComp - 1) continue;
+    if (c.lane == 0) lds_st(C_DONE + 4 * (i % kDoneRing), 0);
+    if (lm) {
+      lm_finish_b(c, I);
+      continue;
+    }
+    if (ticket) {
+      uint32_t old = 0;
+      if (c.lane == 0) old = ctr_release(ctr_line(a, I->seg_rows[0], 0));
+      old = uni(old);
+      if (old + 1 != a.epoch * I->aux[3]) continue;
+      run_merge_b<G>(c, I);
+    }
+    if ((i_flags(I) & F_SIGNAL) && c.lane == 0) ctr_signal(ctr_line(a, I->sig_ctr, uint32_t(cu) % kCtrSpread));
+    if (tr && c.lane == 0) trace_put(a, cu, i, TR_SIGNAL, now32());
+  }
+}
+
+template <class G>
+__global__ __launch_bounds__(kThreads, 1) void mk_megakernel_b(KArgs a) {
+  for (int o = threadIdx.x * 4; o < C_CTRL_END; o += kThreads * 4) *lw(o) = 0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    *lw(C_STATUS_LO) = uint32_t(uint64_t(a.status));
+    *lw(C_STATUS_HI) = uint32_t(uint64_t(a.status) >> 32);
+    *lw(C_LIMIT_LO) = uint32_t(a.watchdog_ticks);
+    *lw(C_LIMIT_HI) = uint32_t(a.watchdog_ticks >> 32);
+  }
+  __syncthreads();
+  const int cu = blockIdx.x;
+  const uint32_t beg = a.q_off[cu], end = a.q_off[cu + 1];
+  InstrCP q = (InstrCP)(a.instrs + beg);
+  const int wave = int(uni(threadIdx.x >> 6));
+  if (wave < kNLoad)
+    loader_b(a, q, end - beg, wave, cu);
+  else
+    compute_b<G>(a, q, end - beg, wave - kNLoad, cu);
+}
+
+}  // namespace mk
+
+namespace {
+struct BVariant {
+  int hpt, dh;  // 0 = generic
+  const void* fn;
+};
+const BVariant kBVariants[] = {
+    {0, 0, reinterpret_cast<const void*>(&mk::mk_megakernel_b<mk::GeoBAny>)},
+    {4, 128, reinterpret_cast<const void*>(&mk::mk_megakernel_b<mk::GeoB<4, 128>>)},
+};
+constexpr int kNumBVariants = sizeof(kBVariants) / sizeof(kBVariants[0]);
+bool g_battr_set[kNumBVariants] = {};
+}  // namespace
+
+// Index of the batched kernel built for this attention tile shape, or 0.
+extern "C" int mk_pick_batched(int hpt, int dh) {
+  for (int v = 1; v < kNumBVariants; v++)
+    if (kBVariants[v].hpt == hpt && kBVariants[v].dh == dh) return v;
+  return 0;
+}
+
+extern "C" hipError_t mk_launch_batched(const mk::KArgs* args, int n_cus, hipStream_t stream, int cooperative,
+                                        int variant) {
+  if (variant < 0 || variant >= kNumBVariants) return hipErrorInvalidValue;
+  const void* fn = kBVariants[variant].fn;
+  if (!g_battr_set[variant]) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, mk::lb::kTotal);
+    if (e != hipSuccess) return e;
+    g_battr_set[variant] = true;
+  }
+  mk::KArgs a = *args;
+  void* params[] = {&a};
+  if (cooperative)
+    return hipLaunchCooperativeKernel(fn, dim3(n_cus), dim3(mk::kThreads), params, mk::lb::kTotal, stream);
+  return hipLaunchKernel(fn, dim3(n_cus), dim3(mk::kThreads), params, mk::lb::kTotal, stream);
+}

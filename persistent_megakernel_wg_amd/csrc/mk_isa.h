@@ -52,8 +52,40 @@ constexpr int kMaxResRows = 128;
 constexpr int kLdsTotal = kLdsRes + 2 * 4 * kMaxResRows;      // 163328
 constexpr int kAttnScoreFloats = 2048;                       // 8 KiB of scores
 
+// LDS layout of the batched kernel (several sequences per step).  The staged
+// GEMV input holds all B sequences' vectors ([B][K] fp32, 64 KiB), so the page
+// ring is shorter.  Control words keep the offsets of the layout above.
+namespace lb {
+constexpr int kMaxB = 8;             // sequences per step
+constexpr int kPages = 5;
+constexpr int kSS = 512;             // sum of squares per 128-value chunk [128]
+constexpr int kArg = 1024;           // argmax per compute wave and sequence [kNComp][kMaxB][2]
+constexpr int kDots = 1536;          // expert down-projection dots [kMaxB][8 slots][16 rows]
+constexpr int kMaxDnRows = 16;
+constexpr int kMaxTopK = 8;
+constexpr int kRoute = kDots + 4 * kMaxB * kMaxTopK * kMaxDnRows;   // 5632: routing tables
+constexpr int kRouteBytes = 1024;    // one table per layer parity
+constexpr int kRes = kRoute + 2 * kRouteBytes;                      // 7680: residual rows
+constexpr int kX = kRes + 2 * 4 * kMaxResRows;                      // 8704
+constexpr int kXFloats = 16384;      // [B][K] staged input, K <= 16384 / B
+constexpr int kAttn = kX + 4 * kXFloats;                            // 74240
+constexpr int kScoreFloats = 512;    // attention scores of one tile
+constexpr int kAttnBytes = 4 * kScoreFloats + 512 + 64;
+constexpr int kPg = ((kAttn + kAttnBytes + 1023) / 1024) * 1024;   // 77824
+constexpr int kTotal = kPg + kPages * kPageBytes;                   // 159744
+static_assert(kTotal <= 163840, "batched LDS layout exceeds 160 KiB");
+static_assert(kRoute % 16 == 0 && kX % 16 == 0 && kAttn % 16 == 0, "alignment");
+constexpr int kMaxExperts = 64;
+}  // namespace lb
+
 // ------------------------------------------------------------------- opcodes
-enum Op : uint8_t { OP_GEMV = 1, OP_ATTN = 2 };
+enum Op : uint8_t {
+  OP_GEMV = 1,        // one-sequence GEMV tile
+  OP_ATTN = 2,        // decode attention tile (one sequence)
+  OP_BGEMV = 3,       // batched GEMV tile: every row applied to all B sequences
+  OP_EGU = 4,         // expert gate/up slice of every selected expert (SwiGLU)
+  OP_EDN = 5,         // expert down-projection rows, weighted sum over the top-k
+};
 
 // GEMV epilogues
 enum Epi : uint8_t {
@@ -75,6 +107,8 @@ enum Flag : uint16_t {
   F_INTERLEAVE = 8,   // stream rows alternate between segments 0 and 1
   F_SIGNAL = 16,      // increment sig_ctr when done
   F_OWN_POS = 32,     // (attention) placeholder, decided at run time
+  F_ROUTE = 64,       // (experts) first expert instruction of its layer on the CU:
+                      // take the top-k routing decision from the router logits
 };
 
 constexpr uint32_t kNoCounter = 0xFFFFFFFFu;
@@ -136,6 +170,21 @@ struct PackCopy {
 //   aux[0] = LDS accumulator offset (down projection)
 //   aux[1] = argmax slot index (LM head)
 //   aux[2] = LM-head ticket counter, aux[3] = LM-head tiles
+// Batched GEMV (OP_BGEMV): rows are taken in pairs (n_items pairs); the input
+// is [B][k], the output [B][aux[0]] and the residual [B][aux[2]] (elements);
+//   aux[1] = argmax slot index, aux[3] = LM-head tiles (EPI_ARGMAX)
+// Expert instructions (OP_EGU, OP_EDN): the weight runs are read in place.
+//   aux[0] = router counter, aux[1] = its producers per step
+//   aux[2] = pages per expert region, aux[3] = gate/up pairs (EGU) or rows (EDN)
+//   aux[4] = experts
+//   seg_ptr[0] = router logits [B][E] (tagged)
+//   seg_ptr[1] = first gate row (EGU) / first down row (EDN) of expert 0
+//   seg_ptr[2] = first up row of expert 0 (EGU)
+//   seg_stride[0] = bytes between experts' runs; seg_rows[0] = bytes of a run
+//   seg_stride[1] = pages of the gate run within an expert region (EGU)
+//   row0 = first FFN row of the slice (EGU) / first output row (EDN)
+//   in_ptr = x (EGU) or m [B][top_k][Fe] (EDN); res_ptr = h (EDN)
+//   out_ptr = m (EGU) or x_{l+1} (EDN)
 
 // Kernel launch arguments.
 struct KArgs {
@@ -164,6 +213,10 @@ struct KArgs {
   uint64_t watchdog_ticks;  // s_memrealtime ticks (100 MHz)
   uint32_t* trace;          // [n_cus][trace_stride][8] timestamps, or null
   uint32_t trace_stride;    // instructions per CU in the trace buffer
+  int32_t batch;            // sequences per step
+  int32_t n_experts;        // experts per layer (0 = dense MLP)
+  int32_t top_k;            // experts per token
+  int32_t expert_ffn;       // intermediate size of one expert
 };
 
 // trace record words (s_memrealtime, 100 MHz, low 32 bits)

@@ -26,8 +26,8 @@
 namespace mk {
 namespace {
 
-enum Buf { BUF_EMBED = 0, BUF_X, BUF_QKV, BUF_O, BUF_H, BUF_M, BUF_LOGITS, BUF_COUNT };
-const char* kBufName[] = {"embed", "x", "qkv", "o", "h", "m", "logits"};
+enum Buf { BUF_EMBED = 0, BUF_X, BUF_QKV, BUF_O, BUF_H, BUF_M, BUF_LOGITS, BUF_RL, BUF_COUNT };
+const char* kBufName[] = {"embed", "x", "qkv", "o", "h", "m", "logits", "router"};
 enum LStage { ST_QKV = 0, ST_ATTN = 1, ST_O = 2, ST_GU = 3, ST_DOWN = 4, ST_PER_LAYER = 8 };
 
 uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
@@ -101,6 +101,43 @@ bool gemv_geometry(int K, int* nit, int* rpu) {
 }
 
 // ------------------------------------------------------------------ config
+bool is_batched(const mk_config& c) { return c.n_experts > 0; }
+
+// The batched kernel: parallel-block MoE decoder, B <= 8 sequences.  Every
+// GEMV input length is a multiple of 512 and all B staged vectors fit the
+// 16384-float x slot; an expert's intermediate fits it at least 8 times (one
+// staging group holds every sequence routed to an expert).
+static mk_status check_config_moe(const mk_config& c, std::string* err) {
+  auto unsup = [&](const char* m) {
+    *err = m;
+    return MK_ERR_UNSUPPORTED;
+  };
+  if (c.n_experts < 0 || c.top_k <= 0 || c.expert_ffn <= 0) {
+    *err = "config: n_experts, top_k and expert_ffn must be positive";
+    return MK_ERR_INVALID_ARG;
+  }
+  if (!c.parallel_block) return unsup("config: the mixture-of-experts decoder is built as a parallel block only");
+  if (c.batch > lb::kMaxB) return unsup("config: at most 8 sequences per step");
+  if (c.n_experts > lb::kMaxExperts) return unsup("config: at most 64 experts");
+  if (c.top_k > c.n_experts || c.top_k > lb::kMaxTopK) return unsup("config: top_k must be at most min(8, n_experts)");
+  if (c.n_layers > 128) return unsup("config: at most 128 layers");
+  if (c.head_dim != 64 && c.head_dim != 128) return unsup("config: head_dim must be 64 or 128");
+  const int q = c.n_q_heads * c.head_dim;
+  if (c.hidden % 512 || q % 512 || c.expert_ffn % 512)
+    return unsup("config: hidden, n_q_heads*head_dim and expert_ffn must be multiples of 512");
+  if (int64_t(c.batch) * std::max(c.hidden, q) > lb::kXFloats)
+    return unsup("config: batch * max(hidden, n_q_heads*head_dim) must be at most 16384");
+  if (c.expert_ffn > lb::kXFloats / lb::kMaxB) return unsup("config: expert_ffn must be at most 2048");
+  const int hpg = c.n_q_heads / c.n_kv_heads;
+  if ((hpg & (hpg - 1)) || hpg > 8 || hpg * c.head_dim > 512)
+    return unsup("config: query heads per KV group must be 1, 2, 4 or 8, with at most 512 query values per group");
+  if (c.vocab % 2) {
+    *err = "config: vocab must be even";
+    return MK_ERR_INVALID_ARG;
+  }
+  return MK_OK;
+}
+
 mk_status check_config(const mk_config& c, std::string* err) {
   auto bad = [&](const char* m) {
     *err = m;
@@ -111,8 +148,9 @@ mk_status check_config(const mk_config& c, std::string* err) {
     return bad("config: every dimension must be positive");
   if (c.n_q_heads % c.n_kv_heads) return bad("config: n_q_heads must be a multiple of n_kv_heads");
   if (!(c.rms_eps > 0.f) || !(c.rope_theta > 1.f)) return bad("config: rms_eps > 0 and rope_theta > 1 required");
-  if (c.n_experts || c.parallel_block || c.batch != 1) {
-    *err = "config: MoE / parallel-block / batch > 1 decoders are not built in this library version";
+  if (is_batched(c)) return check_config_moe(c, err);
+  if (c.parallel_block || c.batch != 1) {
+    *err = "config: batch > 1 and the parallel block run only with the mixture-of-experts decoder";
     return MK_ERR_UNSUPPORTED;
   }
   if (c.ffn <= 0) return bad("config: ffn must be positive");
@@ -150,6 +188,24 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
   std::memset(&r, 0, sizeof(r));
   if (o) r = *o;
   r.n_cus = n_cus;
+  if (is_batched(c)) {
+    // experts are split over the CUs by rows; the MLP chunk option is unused
+    if (r.mlp_chunks <= 0) r.mlp_chunks = 1;
+    if (r.attn_block <= 0) {
+      // K and V blocks of a tile in four of the five ring pages, scores in
+      // the scratch, whole KV groups per tile
+      const int hpg = c.n_q_heads / c.n_kv_heads;
+      const int cap_pages = (lb::kPages / 2) * kPageBytes / (2 * c.head_dim);
+      const int cap_scores = lb::kScoreFloats / hpg;
+      int blk = std::min(cap_pages, cap_scores);
+      blk = std::max(64, (blk / 64) * 64);
+      const int want = ((c.max_seq + 63) / 64) * 64;
+      r.attn_block = std::min(blk, want);
+    }
+    if (r.attn_heads <= 0) r.attn_heads = c.n_q_heads / c.n_kv_heads;
+    if (r.watchdog_ms <= 0) r.watchdog_ms = 2000;
+    return r;
+  }
   if (r.mlp_chunks <= 0) {
     // the fewest chunks whose width has a GEMV code path: every chunk costs
     // each CU one more gate/up and one more down instruction (staging, item
@@ -192,8 +248,10 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
 ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
   ArenaLayout a;
   std::memset(&a, 0, sizeof(a));
-  const uint64_t d = c.hidden, q = uint64_t(c.n_q_heads) * c.head_dim,
-                 kv = uint64_t(c.n_kv_heads) * c.head_dim, F = c.ffn;
+  const uint64_t B = c.batch;
+  const uint64_t d = B * c.hidden, q = B * uint64_t(c.n_q_heads) * c.head_dim,
+                 kv = B * uint64_t(c.n_kv_heads) * c.head_dim,
+                 F = is_batched(c) ? B * uint64_t(c.top_k) * c.expert_ffn : uint64_t(c.ffn);
   const uint64_t hpg = c.n_q_heads / c.n_kv_heads;
   uint64_t off = 0;
   auto take = [&](uint64_t bytes) {
@@ -209,15 +267,440 @@ ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
     a.o[l] = take(E * q);
     a.h[l] = take(E * d);
     a.m[l] = take(E * F);
+    a.rl[l] = is_batched(c) ? take(E * B * c.n_experts) : 0;
     a.part[l] = take(4 * uint64_t(max_parts) * hpg * (c.head_dim + 2));
   }
   a.rope_cos = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
   a.rope_sin = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
   a.zero_page = take(kPageBytes);
-  a.lm_slots = take(8 * uint64_t(max_lm_tiles));
+  a.lm_slots = take(8 * uint64_t(max_lm_tiles) * (is_batched(c) ? lb::kMaxB : 1));
   a.status = take(64);
   a.total = off;
   return a;
+}
+
+// ------------------------------------------------------- build (batched)
+// Stages per layer of the parallel-block MoE decoder, for B sequences:
+//   QKV    rows of [Wq; Wk; Wv] . RMSNorm(x_l), every sequence        -> qkv_l
+//   ROUTER rows of Wr . RMSNorm(x_l) (same staged input)               -> rl_l
+//   ATTN   per sequence, KV group and position block                   -> o_l
+//   EGU    per CU: its slice of gate/up pairs of every selected expert -> m_l
+//   O      rows of Wo . o_l + x_l                                      -> h_l
+//   EDN    per CU: its rows of every selected expert's down projection,
+//          weighted over the top-k, + h_l                              -> x_{l+1}
+// (attention and the experts both read RMSNorm(x_l); their results meet in
+// x_{l+1} = x_l + attn + MoE, Cohere's parallel block, airebao.com «快在哪里»
+// item 1), then the LM head with a per-sequence argmax.
+static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) {
+  const mk_config& c = in.cfg;
+  const mk_plan_opts& o = in.opts;
+  const int C = in.n_cus;
+  if (C <= 0 || C > 4096) {
+    *err = "plan: n_cus out of range";
+    return MK_ERR_INVALID_ARG;
+  }
+  const int L = c.n_layers, d = c.hidden, H = c.n_q_heads, G = c.n_kv_heads, Dh = c.head_dim, V = c.vocab,
+            S = c.max_seq, B = c.batch, E = c.n_experts, Fe = c.expert_ffn;
+  const int qd = H * Dh, kvd = G * Dh, hpg = H / G, Rq = qd + 2 * kvd;
+  const int Bat = o.attn_block, kv_rb = 2 * Dh;
+  if (Bat <= 0 || Bat % 64) {
+    *err = "plan: attn_block must be a positive multiple of 64";
+    return MK_ERR_INVALID_ARG;
+  }
+  const int kp = ceil_div(int64_t(Bat) * kv_rb, kPageBytes);
+  if (2 * kp > lb::kPages) {
+    *err = "plan: attention tile (K and V blocks) exceeds the LDS page ring";
+    return MK_ERR_INVALID_ARG;
+  }
+  const int hpt = o.attn_heads;
+  if (hpt <= 0 || hpg % hpt) {
+    *err = "plan: attn_heads must divide the query heads per KV group";
+    return MK_ERR_INVALID_ARG;
+  }
+  if (hpt * Bat > lb::kScoreFloats) {
+    *err = "plan: attention scores of one tile exceed the LDS scratch";
+    return MK_ERR_INVALID_ARG;
+  }
+  const int nblk = ceil_div(S, Bat), tpg = hpg / hpt;
+  *P = Plan();
+  P->n_cus = C;
+  P->attn_block = Bat;
+  P->attn_nblk = nblk;
+  P->attn_tiles = B * G * tpg * nblk;
+  P->attn_heads = hpt;
+  P->mlp_chunks = 1;
+  P->batched = true;
+  P->arena = arena_layout(c, C, B * G * nblk);
+  const uint64_t A = in.arena_base;
+  const ArenaLayout& ar = P->arena;
+  Builder b(in, P);
+  const uint64_t embed = uint64_t(in.w.embed), lm = uint64_t(in.w.lm_head);
+  auto lptr = [](const void* base, int l, uint64_t per_layer_elems) {
+    return uint64_t(base) + 2ull * per_layer_elems * uint64_t(l);
+  };
+  auto split = [&](int64_t N, int cu, int64_t* lo, int64_t* hi) {
+    *lo = N * cu / C;
+    *hi = N * (cu + 1) / C;
+  };
+  std::vector<uint32_t> c_qkv(L), c_rt(L), c_attn(L), c_gu(L), c_o(L), c_dn(L);
+  std::vector<std::vector<uint32_t>> c_ticket(L);
+  for (int l = 0; l < L; l++) {
+    c_qkv[l] = b.new_counter(l * ST_PER_LAYER + ST_QKV);
+    c_rt[l] = b.new_counter(l * ST_PER_LAYER + ST_QKV);
+    c_attn[l] = b.new_counter(l * ST_PER_LAYER + ST_ATTN);
+    if (nblk > 1)
+      for (int t = 0; t < B * G * tpg; t++) c_ticket[l].push_back(b.new_counter(l * ST_PER_LAYER + ST_ATTN));
+    c_gu[l] = b.new_counter(l * ST_PER_LAYER + ST_ATTN);
+    c_o[l] = b.new_counter(l * ST_PER_LAYER + ST_O);
+    c_dn[l] = b.new_counter(l * ST_PER_LAYER + ST_DOWN);
+  }
+  const uint32_t c_lm = b.new_counter(L * ST_PER_LAYER);
+  // a batched GEMV tile: rows [r0, r1) of one matrix (or the Wq|Wk|Wv
+  // segments), applied to the B staged vectors
+  auto bgemv = [&](int l, int epi, int K, int r0, int r1) {
+    Instr I = blank();
+    I.op = OP_BGEMV;
+    I.epi = uint8_t(epi);
+    I.nit = uint8_t(K / 512);
+    I.rpu = 1;
+    I.layer = uint16_t(l);
+    I.n_items = uint32_t((r1 - r0 + 1) / 2);
+    I.row0 = uint32_t(r0);
+    I.row_bytes = uint32_t(2 * K);
+    I.n_rows = uint32_t(r1 - r0);
+    I.k = uint32_t(K);
+    I.n_pages = uint32_t(ceil_div(int64_t(2 * I.n_items) * I.row_bytes, kPageBytes));
+    return I;
+  };
+  auto per_seq = [&](std::vector<Range>& v, int buf, int layer, uint64_t stride, uint64_t lo, uint64_t hi) {
+    for (int s = 0; s < B; s++) v.push_back({buf, layer, s * stride + lo, s * stride + hi});
+  };
+  // attention tile -> CU: spread evenly
+  const int n_att = B * G * tpg * nblk;
+  auto att_cu = [&](int a) { return int((int64_t(a) * C / n_att) % C); };
+  const int n_rt = (E + 1) / 2;  // router tiles of two rows
+  auto rt_cu = [&](int t) { return int(int64_t(t) * C / n_rt); };
+  const int max_res_rows = std::min(kMaxResRows / B, lb::kMaxDnRows);
+  // pairs of an expert gate/up instruction: the gate run and the up run of a
+  // pair must be resident together, so each run is at most two pages
+  const int max_pairs = std::max(1, 2 * kPageBytes / (2 * d));
+
+  for (int l = 0; l < L; l++) {
+    const int stg = l * ST_PER_LAYER;
+    const uint64_t x_in = l == 0 ? embed : A + ar.x[l];
+    const int x_buf = l == 0 ? BUF_EMBED : BUF_X;
+    // ---------------------------------------------------------------- QKV
+    for (int cu = 0; cu < C; cu++) {
+      int64_t r0, r1;
+      split(Rq, cu, &r0, &r1);
+      if (r1 <= r0) continue;
+      Instr I = bgemv(l, EPI_STORE, d, int(r0), int(r1));
+      I.flags = F_NORM | F_SIGNAL | (l == 0 ? F_IN_EMBED : 0);
+      const int bounds[4] = {0, qd, qd + kvd, qd + 2 * kvd};
+      const void* mats[3] = {in.w.wq, in.w.wk, in.w.wv};
+      const int mrows[3] = {qd, kvd, kvd};
+      int ns = 0;
+      for (int sg = 0; sg < 3; sg++) {
+        int lo = std::max(int(r0), bounds[sg]), hi = std::min(int(r1), bounds[sg + 1]);
+        if (hi <= lo) continue;
+        I.seg_ptr[ns] = lptr(mats[sg], l, uint64_t(mrows[sg]) * d) + 2ull * d * (lo - bounds[sg]);
+        I.seg_rows[ns] = uint32_t(hi - lo);
+        I.seg_stride[ns] = uint32_t(2 * d);
+        ns++;
+      }
+      I.aux[0] = uint32_t(Rq);
+      I.aux[4] = uint32_t(ns);
+      I.in_ptr = x_in;
+      I.out_ptr = A + ar.qkv[l];
+      I.gain_ptr = lptr(in.w.attn_norm, l, d);
+      if (l > 0) I.wait_ctr[0] = c_dn[l - 1];
+      I.sig_ctr = c_qkv[l];
+      InstrMeta m;
+      m.stage = stg + ST_QKV;
+      m.merge_write = false;
+      m.reads.push_back({x_buf, l, 0, uint64_t(B) * d});
+      per_seq(m.writes, BUF_QKV, l, Rq, r0, r1);
+      b.push(cu, I, std::move(m), (r1 - r0) * 2ll * d);
+    }
+    // ------------------------------------------------------------- ROUTER
+    for (int t = 0; t < n_rt; t++) {
+      const int r0 = 2 * t, r1 = std::min(E, r0 + 2);
+      Instr I = bgemv(l, EPI_STORE, d, r0, r1);
+      I.flags = F_NORM | F_SIGNAL | (l == 0 ? F_IN_EMBED : 0);
+      I.seg_ptr[0] = lptr(in.w.router, l, uint64_t(E) * d) + 2ull * d * r0;
+      I.seg_rows[0] = uint32_t(r1 - r0);
+      I.seg_stride[0] = uint32_t(2 * d);
+      I.aux[0] = uint32_t(E);
+      I.aux[4] = 1;
+      I.in_ptr = x_in;
+      I.out_ptr = A + ar.rl[l];
+      I.gain_ptr = lptr(in.w.attn_norm, l, d);
+      if (l > 0) I.wait_ctr[0] = c_dn[l - 1];
+      I.sig_ctr = c_rt[l];
+      InstrMeta m;
+      m.stage = stg + ST_QKV;
+      m.merge_write = false;
+      m.reads.push_back({x_buf, l, 0, uint64_t(B) * d});
+      per_seq(m.writes, BUF_RL, l, E, r0, r1);
+      b.push(rt_cu(t), I, std::move(m), (r1 - r0) * 2ll * d);
+    }
+    // --------------------------------------------------------------- ATTN
+    for (int a = 0; a < n_att; a++) {
+      // tile a: sequence sq, head tile tg of the layer, block blk
+      const int per_seq_tiles = G * tpg * nblk;
+      const int sq = a / per_seq_tiles, rem = a % per_seq_tiles;
+      const int tg = rem / nblk, blk = rem % nblk;
+      const int g = tg / tpg, h0 = (tg % tpg) * hpt;
+      Instr I = blank();
+      I.op = OP_ATTN;
+      I.layer = uint16_t(l);
+      I.flags = F_SIGNAL;
+      I.n_items = uint32_t(hpt);
+      I.row0 = uint32_t(h0);
+      I.row_bytes = uint32_t(kv_rb);
+      I.n_rows = uint32_t(2 * Bat);
+      I.aux[0] = uint32_t(g);
+      I.aux[1] = uint32_t(blk);
+      I.aux[2] = uint32_t(Bat);
+      I.aux[3] = uint32_t(nblk);
+      I.aux[4] = uint32_t(kp);
+      const uint64_t head_rows = uint64_t(S) * Dh;
+      const uint64_t kvi = (uint64_t(l) * B + sq) * G + g;
+      I.seg_ptr[0] = uint64_t(in.w.k_cache) + 2ull * head_rows * kvi;
+      I.seg_ptr[1] = uint64_t(in.w.v_cache) + 2ull * head_rows * kvi;
+      I.seg_rows[0] = nblk > 1 ? c_ticket[l][sq * G * tpg + tg] : kNoCounter;
+      I.in_ptr = A + ar.qkv[l] + uint64_t(kActBytes) * sq * Rq;
+      I.out_ptr = A + ar.o[l] + uint64_t(kActBytes) * sq * qd;
+      I.res_ptr = A + ar.part[l] + 4ull * sq * H * nblk * (Dh + 2);
+      I.wait_ctr[0] = c_qkv[l];
+      I.sig_ctr = c_attn[l];
+      I.n_pages = uint32_t(2 * kp);
+      InstrMeta m;
+      m.stage = stg + ST_ATTN;
+      m.merge_write = nblk > 1;
+      const uint64_t so = uint64_t(sq) * Rq;
+      const uint64_t q0 = uint64_t(g * hpg + h0) * Dh, q1 = q0 + uint64_t(hpt) * Dh;
+      m.reads.push_back({BUF_QKV, l, so + q0, so + q1});
+      m.reads.push_back({BUF_QKV, l, so + qd + g * Dh, so + qd + (g + 1) * Dh});
+      m.reads.push_back({BUF_QKV, l, so + qd + kvd + g * Dh, so + qd + kvd + (g + 1) * Dh});
+      m.writes.push_back({BUF_O, l, uint64_t(sq) * qd + q0, uint64_t(sq) * qd + q1});
+      const int64_t rows = std::min<int64_t>(Bat, std::max<int64_t>(0, int64_t(S) - int64_t(blk) * Bat));
+      b.push(att_cu(a), I, std::move(m), 2 * rows * kv_rb);
+    }
+    // ---------------------------------------------------------------- EGU
+    std::vector<char> routed(C, 0);  // CU already has an expert instruction of this layer
+    for (int cu = 0; cu < C; cu++) {
+      int64_t f0, f1;
+      split(Fe, cu, &f0, &f1);
+      for (int64_t p0 = f0; p0 < f1; p0 += max_pairs) {
+        const int64_t p1 = std::min<int64_t>(f1, p0 + max_pairs), npu = p1 - p0;
+        const int gpb = ceil_div(npu * 2 * d, kPageBytes);
+        Instr I = blank();
+        I.op = OP_EGU;
+        I.epi = EPI_SWIGLU;
+        I.nit = uint8_t(d / 512);
+        I.rpu = 1;
+        I.layer = uint16_t(l);
+        I.flags = F_NORM | F_SIGNAL | (l == 0 ? F_IN_EMBED : 0) | (routed[cu] ? 0 : F_ROUTE);
+        routed[cu] = 1;
+        I.n_items = uint32_t(npu);
+        I.row0 = uint32_t(p0);
+        I.row_bytes = uint32_t(2 * d);
+        I.n_rows = uint32_t(2 * npu);
+        I.k = uint32_t(d);
+        I.aux[0] = c_rt[l];
+        I.aux[2] = uint32_t(2 * gpb);
+        I.aux[3] = uint32_t(npu);
+        I.aux[4] = uint32_t(E);
+        I.seg_ptr[0] = A + ar.rl[l];
+        I.seg_ptr[1] = lptr(in.w.e_gate, l, uint64_t(E) * Fe * d) + 2ull * d * p0;
+        I.seg_ptr[2] = lptr(in.w.e_up, l, uint64_t(E) * Fe * d) + 2ull * d * p0;
+        I.seg_stride[0] = uint32_t(2ull * Fe * d);
+        I.seg_rows[0] = uint32_t(npu * 2 * d);
+        I.seg_stride[1] = uint32_t(gpb);
+        I.in_ptr = x_in;
+        I.out_ptr = A + ar.m[l];
+        I.gain_ptr = lptr(in.w.attn_norm, l, d);
+        I.wait_ctr[0] = c_rt[l];
+        I.sig_ctr = c_gu[l];
+        I.n_pages = uint32_t(E * 2 * gpb);
+        InstrMeta m;
+        m.stage = stg + ST_ATTN;
+        m.merge_write = false;
+        m.reads.push_back({x_buf, l, 0, uint64_t(B) * d});
+        m.reads.push_back({BUF_RL, l, 0, uint64_t(B) * E});
+        for (int sq = 0; sq < B; sq++)
+          for (int slot = 0; slot < c.top_k; slot++) {
+            const uint64_t base = (uint64_t(sq) * c.top_k + slot) * Fe;
+            m.writes.push_back({BUF_M, l, base + p0, base + p1});
+          }
+        b.push(cu, I, std::move(m), int64_t(E) * npu * 4 * d);
+      }
+    }
+    // ------------------------------------------------------------------ O
+    for (int cu = 0; cu < C; cu++) {
+      int64_t c0, c1;
+      split(d, cu, &c0, &c1);
+      for (int64_t r0 = c0; r0 < c1; r0 += max_res_rows) {
+        const int64_t r1 = std::min<int64_t>(c1, r0 + max_res_rows);
+        Instr I = bgemv(l, EPI_RESID, qd, int(r0), int(r1));
+        I.flags = F_SIGNAL | (l == 0 ? F_RES_EMBED : 0);
+        I.seg_ptr[0] = lptr(in.w.wo, l, uint64_t(d) * qd) + 2ull * qd * r0;
+        I.seg_rows[0] = uint32_t(r1 - r0);
+        I.seg_stride[0] = uint32_t(2 * qd);
+        I.aux[0] = uint32_t(d);
+        I.aux[2] = uint32_t(d);
+        I.aux[4] = 1;
+        I.in_ptr = A + ar.o[l];
+        I.res_ptr = x_in;
+        I.out_ptr = A + ar.h[l];
+        I.wait_ctr[0] = c_attn[l];
+        I.sig_ctr = c_o[l];
+        InstrMeta m;
+        m.stage = stg + ST_O;
+        m.merge_write = false;
+        m.reads.push_back({BUF_O, l, 0, uint64_t(B) * qd});
+        per_seq(m.reads, x_buf, l, d, r0, r1);
+        per_seq(m.writes, BUF_H, l, d, r0, r1);
+        b.push(cu, I, std::move(m), (r1 - r0) * 2ll * qd);
+      }
+    }
+    // ---------------------------------------------------------------- EDN
+    for (int cu = 0; cu < C; cu++) {
+      int64_t c0, c1;
+      split(d, cu, &c0, &c1);
+      for (int64_t r0 = c0; r0 < c1; r0 += max_res_rows) {
+        const int64_t r1 = std::min<int64_t>(c1, r0 + max_res_rows), nr = r1 - r0;
+        const int ppe = ceil_div(nr * 2 * Fe, kPageBytes);
+        Instr I = blank();
+        I.op = OP_EDN;
+        I.nit = uint8_t(Fe / 512);
+        I.rpu = 1;
+        I.layer = uint16_t(l);
+        I.flags = F_SIGNAL | (routed[cu] ? 0 : F_ROUTE);
+        routed[cu] = 1;
+        I.n_items = uint32_t((nr + 1) / 2);
+        I.row0 = uint32_t(r0);
+        I.row_bytes = uint32_t(2 * Fe);
+        I.n_rows = uint32_t(nr);
+        I.k = uint32_t(Fe);
+        I.aux[0] = c_rt[l];
+        I.aux[2] = uint32_t(ppe);
+        I.aux[3] = uint32_t(nr);
+        I.aux[4] = uint32_t(E);
+        I.seg_ptr[0] = A + ar.rl[l];
+        I.seg_ptr[1] = lptr(in.w.e_down, l, uint64_t(E) * d * Fe) + 2ull * Fe * r0;
+        I.seg_stride[0] = uint32_t(2ull * d * Fe);
+        I.seg_rows[0] = uint32_t(nr * 2 * Fe);
+        I.seg_stride[1] = uint32_t(ppe);
+        I.in_ptr = A + ar.m[l];
+        I.res_ptr = A + ar.h[l];
+        I.out_ptr = A + ar.x[l + 1];
+        I.wait_ctr[0] = c_gu[l];
+        I.wait_ctr[1] = c_o[l];
+        I.sig_ctr = c_dn[l];
+        I.n_pages = uint32_t(E * ppe);
+        InstrMeta m;
+        m.stage = stg + ST_DOWN;
+        m.merge_write = false;
+        m.reads.push_back({BUF_M, l, 0, uint64_t(B) * c.top_k * Fe});
+        m.reads.push_back({BUF_RL, l, 0, uint64_t(B) * E});
+        per_seq(m.reads, BUF_H, l, d, r0, r1);
+        per_seq(m.writes, BUF_X, l + 1, d, r0, r1);
+        b.push(cu, I, std::move(m), int64_t(E) * nr * 2 * Fe);
+      }
+    }
+  }
+  // ------------------------------------------------------------- LM head
+  {
+    std::vector<int> lm_cus;
+    for (int cu = 0; cu < C; cu++) {
+      int64_t i0, i1;
+      split(V, cu, &i0, &i1);
+      if (i1 > i0) lm_cus.push_back(cu);
+    }
+    const int n_lm = int(lm_cus.size());
+    int tile = 0;
+    for (int cu : lm_cus) {
+      int64_t r0, r1;
+      split(V, cu, &r0, &r1);
+      Instr I = bgemv(L, EPI_ARGMAX, d, int(r0), int(r1));
+      I.flags = F_NORM | F_SIGNAL;
+      I.seg_ptr[0] = lm + 2ull * d * r0;
+      I.seg_rows[0] = uint32_t(r1 - r0);
+      I.seg_stride[0] = uint32_t(2 * d);
+      I.aux[0] = uint32_t(V);
+      I.aux[1] = uint32_t(tile);
+      I.aux[3] = uint32_t(n_lm);
+      I.aux[4] = 1;
+      I.in_ptr = A + ar.x[L];
+      I.gain_ptr = uint64_t(in.w.final_norm);
+      I.wait_ctr[0] = c_dn[L - 1];
+      I.sig_ctr = c_lm;
+      InstrMeta m;
+      m.stage = L * ST_PER_LAYER;
+      m.merge_write = false;
+      m.reads.push_back({BUF_X, L, 0, uint64_t(B) * d});
+      per_seq(m.writes, BUF_LOGITS, 0, V, r0, r1);
+      b.push(cu, I, std::move(m), (r1 - r0) * 2ll * d);
+      tile++;
+    }
+    P->lm_tiles = n_lm;
+  }
+  // producers per counter (per step)
+  for (int cu = 0; cu < C; cu++)
+    for (const Instr& I : b.q[cu]) {
+      if (I.op == OP_ATTN && I.aux[3] > 1) {
+        P->ctr_producers[I.seg_rows[0]]++;
+        continue;
+      }
+      if ((I.flags & F_SIGNAL) && I.sig_ctr != kNoCounter) P->ctr_producers[I.sig_ctr]++;
+    }
+  for (int l = 0; l < L; l++)
+    if (nblk > 1) P->ctr_producers[c_attn[l]] = uint32_t(B * G * tpg);
+  for (int cu = 0; cu < C; cu++)
+    for (Instr& I : b.q[cu]) {
+      for (int k = 0; k < 2; k++)
+        if (I.wait_ctr[k] != kNoCounter) I.wait_cnt[k] = P->ctr_producers[I.wait_ctr[k]];
+      if (I.op == OP_EGU || I.op == OP_EDN) I.aux[1] = P->ctr_producers[I.aux[0]];
+    }
+  P->q_off.assign(C + 1, 0);
+  for (int cu = 0; cu < C; cu++) {
+    P->q_off[cu + 1] = P->q_off[cu] + uint32_t(b.q[cu].size());
+    P->instrs.insert(P->instrs.end(), b.q[cu].begin(), b.q[cu].end());
+    P->meta.insert(P->meta.end(), b.qm[cu].begin(), b.qm[cu].end());
+  }
+  P->n_counters = int(P->ctr_stage.size());
+  // packed weight stream of the batched GEMV tiles (experts are read in place)
+  uint64_t pack = 0;
+  for (Instr& I : P->instrs) {
+    if (I.op != OP_BGEMV) continue;
+    I.src_ptr = in.pack_base + pack;
+    uint64_t row = 0;
+    for (uint32_t sg = 0; sg < I.aux[4]; sg++) {
+      if (!I.seg_rows[sg]) continue;
+      PackCopy cp;
+      cp.src = I.seg_ptr[sg];
+      cp.rows = I.seg_rows[sg];
+      cp.row_bytes = I.row_bytes;
+      cp.src_stride = I.seg_stride[sg];
+      cp.dst = pack + row * I.row_bytes;
+      cp.dst_stride = I.row_bytes;
+      row += cp.rows;
+      P->pack.push_back(cp);
+    }
+    pack += uint64_t(I.n_pages) * kPageBytes;
+  }
+  P->pack_bytes = pack;
+  // bytes that do not depend on the routing: attention and router
+  // projections, norms, the LM head and B embedding rows (the experts add
+  // 6 * d * Fe bytes per selected expert and layer)
+  int64_t wbytes = int64_t(L) * 2 * (int64_t(Rq) * d + int64_t(d) * qd + int64_t(E) * d + d);
+  wbytes += 2ll * V * d + 2ll * d + 2ll * d * B;
+  P->weight_bytes = wbytes;
+  P->max_cu_bytes = *std::max_element(b.cu_bytes.begin(), b.cu_bytes.end());
+  P->min_cu_bytes = *std::min_element(b.cu_bytes.begin(), b.cu_bytes.end());
+  return MK_OK;
 }
 
 // ------------------------------------------------------------------- build
@@ -225,6 +708,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
   const mk_config& c = in.cfg;
   mk_status st = check_config(c, err);
   if (st != MK_OK) return st;
+  if (is_batched(c)) return build_plan_moe(in, P, err);
   const mk_plan_opts& o = in.opts;
   const int C = in.n_cus;
   if (C <= 0 || C > 4096) {
@@ -679,6 +1163,12 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
       // 2. stage order: every wait names a counter of a strictly earlier stage
       if (p.ctr_stage[ct] >= p.meta[i].stage) return fail("wait on a counter of the same or a later stage");
     }
+    // expert instructions: the loader waits on the router counter
+    if (I.op == OP_EGU || I.op == OP_EDN) {
+      if (I.aux[0] >= uint32_t(NC) || I.aux[1] != p.ctr_producers[I.aux[0]])
+        return fail("expert instruction router counter");
+      if (p.ctr_stage[I.aux[0]] >= p.meta[i].stage) return fail("router counter of the same or a later stage");
+    }
   }
   // a split attention signals once per head tile: by the tile that takes
   // the last ticket of that head tile's blocks
@@ -707,7 +1197,37 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
       last_stage = m.stage;
       if (I.page0 != page) return fail("page stream not contiguous");
       page += I.n_pages;
+      if (I.op == OP_BGEMV) {
+        if (!p.batched) return fail("batched GEMV in a one-sequence plan");
+        if (I.k % 512 || I.nit != I.k / 512 || I.row_bytes != 2 * I.k) return fail("batched row geometry");
+        if (uint64_t(I.k) * c.batch > uint64_t(lb::kXFloats)) return fail("batched input exceeds the x slot");
+        if (uint64_t(I.n_pages) * kPageBytes < uint64_t(2) * I.n_items * I.row_bytes)
+          return fail("page budget smaller than the tile");
+        if (I.n_items != (I.n_rows + 1) / 2) return fail("row pairs");
+        if (uint32_t(ceil_div(2 * I.row_bytes, kPageBytes)) + 1 > uint32_t(lb::kPages))
+          return fail("an item spans more pages than the ring holds");
+        uint32_t srows = 0;
+        for (uint32_t sg = 0; sg < I.aux[4]; sg++) srows += I.seg_rows[sg];
+        if (srows != I.n_rows) return fail("segments do not cover the stream rows");
+        if (I.epi == EPI_RESID && uint64_t(I.n_rows) * c.batch > uint64_t(kMaxResRows))
+          return fail("residual rows exceed the LDS staging slot");
+        continue;
+      }
+      if (I.op == OP_EGU || I.op == OP_EDN) {
+        if (!p.batched) return fail("expert instruction in a one-sequence plan");
+        const uint32_t ppe = I.aux[2], runs = I.op == OP_EGU ? 2 : 1, gpb = I.seg_stride[1];
+        if (I.k % 512 || I.nit != I.k / 512 || I.row_bytes != 2 * I.k) return fail("expert row geometry");
+        if (gpb * runs != ppe || uint64_t(gpb) * kPageBytes < I.seg_rows[0]) return fail("expert page regions");
+        if (I.n_pages != ppe * I.aux[4] || I.aux[4] != uint32_t(c.n_experts)) return fail("expert page budget");
+        if (I.op == OP_EGU && (I.seg_rows[0] != I.aux[3] * I.row_bytes || gpb + 1 > uint32_t(lb::kPages)))
+          return fail("expert gate/up runs");
+        if (I.op == OP_EDN && (I.seg_rows[0] != I.aux[3] * I.row_bytes || I.aux[3] > uint32_t(lb::kMaxDnRows) ||
+                               uint64_t(I.aux[3]) * c.batch > uint64_t(kMaxResRows) || I.aux[3] != I.n_rows))
+          return fail("expert down-projection rows");
+        continue;
+      }
       if (I.op == OP_GEMV) {
+        if (p.batched) return fail("one-sequence GEMV in a batched plan");
         const uint64_t need = uint64_t(I.n_rows) * I.row_bytes;
         if (uint64_t(I.n_pages) * kPageBytes < need) return fail("page budget smaller than the tile");
         if (I.rpu == 1 && I.row_bytes != uint32_t(I.nit) * kUnit) return fail("row geometry");
@@ -724,8 +1244,10 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         for (uint32_t s = 0; s < I.aux[4]; s++) srows += I.seg_rows[s];
         if (srows != I.n_rows) return fail("segments do not cover the stream rows");
       } else {
-        if (2 * I.aux[4] != I.n_pages || 2 * I.aux[4] > uint32_t(kPages))
-          return fail("attention page regions");
+        const int ring = p.batched ? lb::kPages : kPages;
+        if (2 * I.aux[4] != I.n_pages || 2 * I.aux[4] > uint32_t(ring)) return fail("attention page regions");
+        if (I.n_items * I.aux[2] > uint32_t(p.batched ? lb::kScoreFloats : kAttnScoreFloats))
+          return fail("attention scores exceed the LDS scratch");
       }
     }
   }
@@ -833,6 +1355,8 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
     const uint64_t L = c.n_layers, d = c.hidden, qd = uint64_t(c.n_q_heads) * c.head_dim,
                    kvd = uint64_t(c.n_kv_heads) * c.head_dim, F = c.ffn, V = c.vocab;
     const uint64_t kv_bytes = 2ull * L * c.batch * c.n_kv_heads * c.max_seq * c.head_dim;
+    const uint64_t NE = c.n_experts > 0 ? c.n_experts : 0, Fe = c.expert_ffn > 0 ? c.expert_ffn : 0,
+                   NB = c.batch;
     const Ext ext[] = {
         {uint64_t(in.w.embed), uint64_t(in.w.embed) + 2 * V * d, "embed"},
         {uint64_t(in.w.lm_head), uint64_t(in.w.lm_head) + 2 * V * d, "lm_head"},
@@ -845,6 +1369,10 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         {uint64_t(in.w.w_down), uint64_t(in.w.w_down) + 2 * L * d * F, "w_down"},
         {uint64_t(in.w.k_cache), uint64_t(in.w.k_cache) + kv_bytes, "k_cache"},
         {uint64_t(in.w.v_cache), uint64_t(in.w.v_cache) + kv_bytes, "v_cache"},
+        {uint64_t(in.w.router), uint64_t(in.w.router) + 2 * L * NE * d, "router"},
+        {uint64_t(in.w.e_gate), uint64_t(in.w.e_gate) + 2 * L * NE * Fe * d, "e_gate"},
+        {uint64_t(in.w.e_up), uint64_t(in.w.e_up) + 2 * L * NE * Fe * d, "e_up"},
+        {uint64_t(in.w.e_down), uint64_t(in.w.e_down) + 2 * L * NE * d * Fe, "e_down"},
     };
     auto inside = [&](uint64_t lo, uint64_t hi) {
       for (const Ext& e : ext)
@@ -857,7 +1385,7 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
     // every copy reads weight rows and writes inside the buffer
     uint64_t next_src = in.pack_base, stream_bytes = 0, copied = 0;
     for (const Instr& I : p.instrs) {
-      if (I.op != OP_GEMV) continue;
+      if (I.op != OP_GEMV && I.op != OP_BGEMV) continue;
       if (I.src_ptr != next_src) return fail("packed weight runs are not back to back");
       next_src += uint64_t(I.n_pages) * kPageBytes;
       stream_bytes += uint64_t(I.n_rows) * I.row_bytes;
@@ -875,6 +1403,55 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
     if (copied != stream_bytes) return fail("packed copies do not cover the weight streams");
     for (size_t i = 0; i < p.instrs.size(); i++) {
       const Instr& I = p.instrs[i];
+      const uint64_t EB = kActBytes;
+      if (I.op == OP_BGEMV) {
+        for (uint32_t sg = 0; sg < I.aux[4]; sg++) {
+          if (!I.seg_rows[sg]) continue;
+          const uint64_t lo = I.seg_ptr[sg];
+          if (!inside(lo, lo + uint64_t(I.seg_rows[sg] - 1) * I.seg_stride[sg] + I.row_bytes))
+            return fail("batched GEMV streams bytes outside every weight tensor");
+        }
+        if (I.flags & F_IN_EMBED) {
+          if (I.in_ptr != uint64_t(in.w.embed) || I.k != uint32_t(d)) return fail("embedding input pointer");
+        } else if (!in_arena(I.in_ptr, I.in_ptr + EB * NB * I.k)) {
+          return fail("batched GEMV input outside the arena");
+        }
+        const uint64_t last = (NB - 1) * I.aux[0] + I.row0 + I.n_rows;
+        if (I.epi != EPI_ARGMAX && !in_arena(I.out_ptr, I.out_ptr + EB * last))
+          return fail("batched GEMV output outside the arena");
+        if (I.epi == EPI_ARGMAX && (I.aux[0] != V || I.row0 + I.n_rows > V || I.aux[1] >= I.aux[3] ||
+                                    I.aux[3] > uint32_t(p.n_cus)))
+          return fail("LM head tile");
+        if (I.epi == EPI_RESID) {
+          const uint64_t rl = (NB - 1) * I.aux[2] + I.row0 + I.n_rows;
+          if ((I.flags & F_RES_EMBED) ? (I.res_ptr != uint64_t(in.w.embed) || I.aux[2] != d)
+                                      : !in_arena(I.res_ptr, I.res_ptr + EB * rl))
+            return fail("batched GEMV residual outside the arena");
+        }
+        continue;
+      }
+      if (I.op == OP_EGU || I.op == OP_EDN) {
+        const uint64_t stride = I.seg_stride[0], run = I.seg_rows[0];
+        const int nrun = I.op == OP_EGU ? 2 : 1;
+        for (int r = 0; r < nrun; r++) {
+          const uint64_t lo = I.seg_ptr[1 + r];
+          if (!inside(lo, lo + (NE - 1) * stride + run)) return fail("expert runs outside the expert tensors");
+        }
+        if (!in_arena(I.seg_ptr[0], I.seg_ptr[0] + EB * NB * NE)) return fail("router logits outside the arena");
+        const uint64_t mb = EB * NB * c.top_k * Fe;
+        if (I.op == OP_EGU) {
+          if (I.row0 + I.aux[3] > Fe) return fail("expert gate/up slice");
+          if (!(I.flags & F_IN_EMBED) && !in_arena(I.in_ptr, I.in_ptr + EB * NB * d))
+            return fail("expert input outside the arena");
+          if (!in_arena(I.out_ptr, I.out_ptr + mb)) return fail("expert intermediate outside the arena");
+        } else {
+          if (!in_arena(I.in_ptr, I.in_ptr + mb)) return fail("expert intermediate outside the arena");
+          const uint64_t rl = (NB - 1) * d + I.row0 + I.n_rows;
+          if (!in_arena(I.res_ptr, I.res_ptr + EB * rl) || !in_arena(I.out_ptr, I.out_ptr + EB * rl))
+            return fail("expert down-projection rows outside the arena");
+        }
+        continue;
+      }
       if (I.op == OP_GEMV) {
         for (uint32_t sg = 0; sg < I.aux[4]; sg++) {
           if (!I.seg_rows[sg]) continue;
@@ -972,7 +1549,7 @@ void corrupt_one_target(Plan* p) {
 
 void rebase_pack(Plan* p, uint64_t old_base, uint64_t base) {
   for (Instr& I : p->instrs)
-    if (I.op == OP_GEMV) I.src_ptr = I.src_ptr - old_base + base;
+    if (I.op == OP_GEMV || I.op == OP_BGEMV) I.src_ptr = I.src_ptr - old_base + base;
 }
 
 void summarize(const PlanInput& in, const Plan& p, mk_plan_summary* s) {
@@ -983,8 +1560,8 @@ void summarize(const PlanInput& in, const Plan& p, mk_plan_summary* s) {
   for (int cu = 0; cu < p.n_cus; cu++) mq = std::max(mq, p.q_off[cu + 1] - p.q_off[cu]);
   s->max_queue = int32_t(mq);
   s->n_counters = p.n_counters;
-  s->lds_bytes = kLdsTotal;
-  s->n_pages = kPages;
+  s->lds_bytes = p.batched ? lb::kTotal : kLdsTotal;
+  s->n_pages = p.batched ? lb::kPages : kPages;
   s->page_bytes = kPageBytes;
   s->attn_block = p.attn_block;
   s->attn_tiles = p.attn_tiles;

@@ -21,6 +21,7 @@ namespace mk {
 struct ArenaLayout {
   uint64_t x[129];        // residual stream entering layer l (x[0] unused: embedding)
   uint64_t qkv[128], o[128], h[128], m[128], part[128];
+  uint64_t rl[128];       // router logits (mixture-of-experts decoder)
   uint64_t rope_cos, rope_sin, zero_page, lm_slots, status;
   uint64_t total;
 };
@@ -60,11 +61,15 @@ struct Plan {
   uint64_t pack_bytes = 0;          // size of the packed weight stream
   int n_cus = 0, n_counters = 0;
   int attn_block = 0, attn_nblk = 0, attn_tiles = 0, attn_heads = 0, mlp_chunks = 0, lm_tiles = 0;
+  bool batched = false;             // built for the batched (mixture-of-experts) kernel
   int64_t weight_bytes = 0, max_cu_bytes = 0, min_cu_bytes = 0;
 };
 
 // Arena layout for a shape (does not depend on the plan options).
 ArenaLayout arena_layout(const mk_config& cfg, int max_lm_tiles, int max_parts);
+
+// true for shapes run by the batched kernel (the mixture-of-experts decoder).
+bool is_batched(const mk_config& cfg);
 
 // Validate a shape for the kernel's code paths.  Returns MK_OK or an error
 // with a message.

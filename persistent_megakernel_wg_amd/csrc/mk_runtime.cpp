@@ -15,6 +15,9 @@
 extern "C" hipError_t mk_launch_megakernel(const mk::KArgs* args, int n_cus, hipStream_t stream,
                                            int cooperative, int variant);
 extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpt, int dh);
+extern "C" hipError_t mk_launch_batched(const mk::KArgs* args, int n_cus, hipStream_t stream, int cooperative,
+                                        int variant);
+extern "C" int mk_pick_batched(int hpt, int dh);
 extern "C" hipError_t mk_launch_pack(const mk::PackCopy* copies, uint32_t n, void* base,
                                      hipStream_t stream);
 
@@ -94,6 +97,7 @@ void rope_tables(const mk_config& cfg, std::vector<float>* cs, std::vector<float
 
 // The shape-specific kernel for this plan, or 0 (the generic kernel).
 int variant_for(const mk_config& cfg, const mk_plan_opts& o) {
+  if (mk::is_batched(cfg)) return o.generic_kernel ? 0 : mk_pick_batched(o.attn_heads, cfg.head_dim);
   if (o.generic_kernel) return 0;
   int nd, rd, nq, rq, nf, rf;
   if (!mk::gemv_geometry(cfg.hidden, &nd, &rd) ||
@@ -107,6 +111,10 @@ bool dense_pointers_ok(const mk_weights& w) {
   return w.embed && w.final_norm && w.attn_norm && w.wq && w.wk && w.wv && w.wo && w.mlp_norm &&
          w.w_gate && w.w_up && w.w_down && w.k_cache && w.v_cache;
 }
+bool moe_pointers_ok(const mk_weights& w) {
+  return w.embed && w.final_norm && w.attn_norm && w.wq && w.wk && w.wv && w.wo && w.router && w.e_gate &&
+         w.e_up && w.e_down && w.k_cache && w.v_cache;
+}
 }  // namespace
 
 extern "C" {
@@ -118,7 +126,8 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, int device, mk_ct
   std::string err;
   mk_status st = mk::check_config(*cfg, &err);
   if (st != MK_OK) return fail(nullptr, st, err);
-  if (!dense_pointers_ok(*w)) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_create: a weight or cache pointer is NULL");
+  if (!(mk::is_batched(*cfg) ? moe_pointers_ok(*w) : dense_pointers_ok(*w)))
+    return fail(nullptr, MK_ERR_INVALID_ARG, "mk_create: a weight or cache pointer is NULL");
   if (!w->lm_head && !cfg->tied_embedding)
     return fail(nullptr, MK_ERR_INVALID_ARG, "mk_create: lm_head is NULL and the embedding is not tied");
   int n_dev = 0;
@@ -128,10 +137,10 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, int device, mk_ct
   if ((e = hipSetDevice(device)) != hipSuccess) return hip_fail(nullptr, e, "hipSetDevice");
   hipDeviceProp_t prop;
   if ((e = hipGetDeviceProperties(&prop, device)) != hipSuccess) return hip_fail(nullptr, e, "hipGetDeviceProperties");
-  if (size_t(prop.maxSharedMemoryPerMultiProcessor) < size_t(mk::kLdsTotal))
+  if (size_t(prop.maxSharedMemoryPerMultiProcessor) < size_t(mk::is_batched(*cfg) ? mk::lb::kTotal : mk::kLdsTotal))
     return fail(nullptr, MK_ERR_UNSUPPORTED, "mk_create: device has too little LDS per CU");
   const void* aligned[] = {w->embed, w->lm_head, w->wq, w->wk, w->wv, w->wo, w->w_gate, w->w_up,
-                           w->w_down, w->k_cache, w->v_cache};
+                           w->w_down, w->k_cache, w->v_cache, w->router, w->e_gate, w->e_up, w->e_down};
   for (const void* ptr : aligned)
     if (uintptr_t(ptr) % 16)
       return fail(nullptr, MK_ERR_INVALID_ARG, "mk_create: weight and cache pointers must be 16-byte aligned");
@@ -164,8 +173,10 @@ mk_status mk_build_plan(mk_ctx* c, const mk_plan_opts* opts) {
   in.w = c->w;
   if (in.opts.attn_block <= 0 || in.opts.attn_block % 64)
     return fail(c, MK_ERR_INVALID_ARG, "mk_build_plan: attn_block must be a positive multiple of 64");
+  if (mk::is_batched(c->cfg) && in.opts.generic_kernel)
+    return fail(c, MK_ERR_UNSUPPORTED, "mk_build_plan: the batched decoder has no generic-kernel option");
   const int nblk = (c->cfg.max_seq + in.opts.attn_block - 1) / in.opts.attn_block;
-  const mk::ArenaLayout lay = mk::arena_layout(c->cfg, n_cus, c->cfg.n_kv_heads * nblk);
+  const mk::ArenaLayout lay = mk::arena_layout(c->cfg, n_cus, c->cfg.batch * c->cfg.n_kv_heads * nblk);
   if ((e = hipMalloc(&c->arena, lay.total)) != hipSuccess) return hip_fail(c, e, "hipMalloc(arena)");
   in.arena_base = uint64_t(c->arena);
   in.pack_base = 0;
@@ -255,9 +266,14 @@ mk_status mk_decode_step(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_
   a.watchdog_ticks = uint64_t(c->pin.opts.watchdog_ms) * 100000ull;
   a.trace = c->d_trace;
   a.trace_stride = c->trace_stride;
+  a.batch = c->cfg.batch;
+  a.n_experts = c->cfg.n_experts;
+  a.top_k = c->cfg.top_k;
+  a.expert_ffn = c->cfg.expert_ffn;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = mk_launch_megakernel(&a, p.n_cus, s, c->cooperative, c->variant);
+  hipError_t e = p.batched ? mk_launch_batched(&a, p.n_cus, s, c->cooperative, c->variant)
+                           : mk_launch_megakernel(&a, p.n_cus, s, c->cooperative, c->variant);
   if (e != hipSuccess) return hip_fail(c, e, "launch");
   c->epoch++;
   c->last_stream = s;

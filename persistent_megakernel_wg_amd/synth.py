@@ -85,6 +85,10 @@ SHAPES: Dict[str, ModelShape] = {
                                   n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=14336,
                                   vocab=128256, prefill=2048, max_seq=2048 + 64,
                                   steps=32, tied_embedding=False, rope_theta=500000.0),
+    "moe_tiny": ModelShape("moe_tiny", n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2,
+                           head_dim=128, ffn=0, vocab=4096, prefill=64, max_seq=128, steps=1,
+                           batch=8, tied_embedding=False, n_experts=8, top_k=2, expert_ffn=512,
+                           parallel_block=True, rope_theta=10000.0),
     "moe_b8_ctx2048": ModelShape("moe_b8_ctx2048", n_layers=24, hidden=2048,
                                  n_q_heads=16, n_kv_heads=4, head_dim=128, ffn=0,
                                  vocab=65536, prefill=2048, max_seq=2048 + 64, steps=32,

@@ -97,3 +97,71 @@ def test_null_arguments():
     assert lib.mk_build_plan(None, None) == -1
     assert lib.mk_decode_step(None, None, 0, None, None, None) == -1
     assert lib.mk_sync(None) == -1
+
+
+# ------------------------------------------------------------ batched (MoE)
+MOE = ["moe_tiny", "moe_b8_ctx2048"]
+
+
+def moe_fixed_bytes(s):
+    """Weight bytes of one batched step that do not depend on the routing:
+    attention and router projections, norms, the LM head, B embedding rows."""
+    d, L = s.hidden, s.n_layers
+    per_layer = 2 * ((s.q_dim + 2 * s.kv_dim) * d + d * s.q_dim + s.n_experts * d + d)
+    return L * per_layer + 2 * s.vocab * d + 2 * d + 2 * d * s.batch
+
+
+@pytest.mark.parametrize("name", MOE)
+def test_moe_default_plan_verifies(name):
+    s = synth.SHAPES[name]
+    summ, rep = B.mk_plan_check(B.config_from_shape(s), 256)
+    assert summ["weight_bytes"] == moe_fixed_bytes(s)
+    assert summ["kernel_variant"] == 1          # the kernel built for 4 heads/group, Dh 128
+    assert summ["lds_bytes"] == 159744 and summ["n_pages"] == 5
+    hpg = s.n_q_heads // s.n_kv_heads
+    assert summ["attn_block"] * hpg <= 512      # scores of one tile fit the scratch
+    nblk = -(-s.max_seq // summ["attn_block"])
+    assert summ["attn_tiles"] == s.batch * s.n_kv_heads * nblk
+    # every CU holds a slice of every expert: the same bytes per CU up to
+    # the attention tiles and the rounding of the slices (the tiny shape has
+    # fewer attention tiles and router rows than CUs)
+    if name != "moe_tiny":
+        assert summ["max_cu_bytes"] <= 1.25 * summ["min_cu_bytes"]
+
+
+def test_moe_fixed_bytes_of_the_large_shape():
+    # attention + router + LM head + norms of the 24-layer batch-8 shape
+    assert moe_fixed_bytes(synth.SHAPES["moe_b8_ctx2048"]) == 778_178_560
+
+
+@pytest.mark.parametrize("n_cus,kw,opts", [
+    (1, {}, {"attn_block": 64}), (3, {}, {}), (16, {}, {"attn_block": 64}), (37, {"batch": 3}, {}),
+    (256, {"batch": 1}, {}), (256, {"top_k": 1}, {}), (256, {"top_k": 8}, {}),
+    (64, {"expert_ffn": 2048, "top_k": 4, "n_experts": 16}, {}), (256, {}, {"attn_heads": 1}),
+    (256, {"n_q_heads": 8, "n_kv_heads": 1, "head_dim": 64}, {"attn_block": 64}),
+    (100, {"n_experts": 64, "top_k": 8}, {}),
+])
+def test_moe_plan_variants_verify(n_cus, kw, opts):
+    summ, _ = B.mk_plan_check(_cfg("moe_tiny", **kw), n_cus, B.plan_opts(**opts))
+    assert summ["n_cus"] == n_cus
+
+
+def test_moe_plan_for_the_large_shape_on_fewer_cus():
+    B.mk_plan_check(_cfg("moe_b8_ctx2048"), 80)
+
+
+@pytest.mark.parametrize("kw", [
+    {"top_k": 9, "n_experts": 16}, {"top_k": 4, "n_experts": 3}, {"batch": 9},
+    {"expert_ffn": 768}, {"hidden": 4096, "n_q_heads": 32}, {"n_experts": 65},
+    {"expert_ffn": 4096}, {"parallel_block": False},
+])
+def test_unsupported_moe_shapes_are_rejected(kw):
+    with pytest.raises(B.MkError) as e:
+        B.mk_plan_check(_cfg("moe_tiny", **kw), 64)
+    assert e.value.status == -4
+
+
+def test_moe_bad_plan_options_are_rejected():
+    for opts in ({"attn_block": 256}, {"attn_heads": 3}, {"attn_block": 96}):
+        with pytest.raises(B.MkError):
+            B.mk_plan_check(_cfg("moe_tiny"), 64, B.plan_opts(**opts))
