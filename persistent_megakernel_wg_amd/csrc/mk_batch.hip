@@ -486,9 +486,12 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
   float* dots = reinterpret_cast<float*>(lds + lb::kDots);
   constexpr int NC = (lb::kXFloats / 128 + kNComp - 1) / kNComp;
   const uint64_t* m_in = reinterpret_cast<const uint64_t*>(I->in_ptr);
+  const bool trl = a.trace && c.w == 0 && lane == 0;
   // residual rows (leader), then every wave has left the previous input
   if (c.w == 0 && !stage_res_b(c, I, i, nr, uint32_t(a.hidden))) return false;
+  if (trl) trace_put(a, c.cu, i, TR_XREADY, now32());
   if (!wait_all_ge(C_XCONS, i)) return false;
+  if (trl) trace_put(a, c.cu, i, TR_XFREE, now32());
   const __amdgpu_buffer_rsrc_t rm = act_rsrc(m_in, nB * k * Fe * kActBytes);
   uint32_t er0 = 0;
   while (er0 < nsel) {
@@ -534,7 +537,9 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
       }
       t[qq] = ld_tag2(rm, offs[qq]);
     }
+    if (trl) trace_put(a, c.cu, i, TR_RETRY, npair | (er1 << 8) | (nsel << 16));
     if (!wait_fresh(t, live, rm, [&](int, int qq) { return offs[qq]; }, 0, a.epoch, c.retries)) return false;
+    if (trl) trace_put(a, c.cu, i, TR_ITEM0, now32());
 #pragma unroll
     for (int qq = 0; qq < NC; qq++) {
       if (qq >= int(live)) continue;
@@ -542,6 +547,7 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
       *reinterpret_cast<float2*>(xs + flat) = float2{__uint_as_float(t[qq].x), __uint_as_float(t[qq].z)};
     }
     if (!comp_barrier()) return false;
+    if (trl) trace_put(a, c.cu, i, TR_A_PASS1, now32());
     // items: (expert er in the group, row pair p)
     const uint32_t n_items = (er1 - er0) * ipe;
     for (uint32_t it = c.w; it < n_items; it += kNComp) {
@@ -564,7 +570,12 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
         dots[(bb * lb::kMaxTopK + slot) * lb::kMaxDnRows + row] = s;
       }
     }
+    // this wave reads no page of the group any more: release them before the
+    // barrier, or a group longer than the ring would wait on itself
+    if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + er1 * ppe);
+    if (trl) trace_put(a, c.cu, i, TR_A_STATS, now32());
     if (!comp_barrier()) return false;
+    if (trl) trace_put(a, c.cu, i, TR_A_PASS3, now32());
     er0 = er1;
   }
   // x_{l+1} = h + sum over the top-k slots in order
