@@ -9,6 +9,10 @@ the greedy token chained on the device.  W warm-up steps run from the
 pre-filled context, then the position is reset and exactly K steps are timed,
 bracketed by device synchronisation.  Prints ONE JSON line.
 
+--workload moe_b8_ctx2048 runs the batch-8 parallel-block MoE decoder instead
+(a separate line, not the headline metric); its weight bytes per step count
+the experts the router selected in the timed steps.
+
 roofline.achieved = algorithmic bytes of one launch (every weight once, the
 KV rows [0, pos) read and the new row written) / the average kernel duration
 measured with HIP events recorded around every launch on its stream.
@@ -31,7 +35,7 @@ PEAK_HBM = 8.0e12  # MI355X published HBM3E bandwidth, bytes/s
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("mk_kernel.hip", "mk_isa.h"):
+    for f in ("mk_kernel.hip", "mk_dev.h", "mk_isa.h", "mk_batch.hip"):
         with open(os.path.join(ROOT, "persistent_megakernel_wg_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -48,6 +52,28 @@ def traffic_from_profiles(workload: str):
     if rec.get("kernel_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline_moe(shape, weights, kc, vc, tokens):
+    """Time the CPU oracle on one sequence of one step of the batched workload
+    (the sequences of a step are independent) and scale it to the batch."""
+    import numpy as np
+    from oracle import DecoderOracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    orc = DecoderOracle(shape, weights, keep_f64=False)
+    k, v = kc.copy(), vc.copy()
+    t0 = time.perf_counter()
+    orc.step(np.asarray(tokens), shape.prefill, k, v, seqs=[0])
+    one = time.perf_counter() - t0
+    return {"value": round(1e6 * one * shape.batch, 1), "unit": "us/step", "cores": threads,
+            "kind": "oracle",
+            "sample": "%s: sequence 0 of one float64 decode step at position %d (%.1f s, weights "
+                      "widened per use), times %d sequences" % (shape.name, shape.prefill, one,
+                                                                shape.batch)}
 
 
 def cpu_baseline(shape, weights, kc, vc, tokens, budget_s: float = 20.0):
@@ -103,9 +129,6 @@ def main() -> int:
     from persistent_megakernel_wg_amd.engine import Engine
 
     shape = synth.SHAPES[args.workload]
-    if shape.is_moe:
-        print("workload %s is not built" % shape.name, file=sys.stderr)
-        return 2
     t0 = time.perf_counter()
     weights = synth.make_weights(shape)
     kc, vc = synth.make_kv_cache(shape)
@@ -134,6 +157,8 @@ def main() -> int:
     bufs[W].copy_(bufs[0])
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K)]
+    if shape.is_moe:
+        B.mk_route_stats(eng.ctx, shape.n_layers, reset=True)
     torch.cuda.synchronize(dev)
     t_start = time.perf_counter()
     for i in range(K):
@@ -147,14 +172,24 @@ def main() -> int:
     avg_kernel_s = float(np.mean(kern_ms)) / 1e3
     ms_per_step = 1e3 * wall / K
 
-    wbytes = synth.weight_bytes_per_step(shape)
+    if shape.is_moe:
+        # fixed part (attention, router, LM head, norms, embedding rows) + the
+        # selected experts' gate, up and down rows, averaged over the K steps
+        sel = B.mk_route_stats(eng.ctx, shape.n_layers)
+        wbytes = info["weight_bytes"] + 6.0 * shape.hidden * shape.expert_ffn * sum(sel) / K
+        experts_per_layer = sum(sel) / (K * shape.n_layers)
+    else:
+        wbytes = synth.weight_bytes_per_step(shape)
+        experts_per_layer = None
     kvb = [synth.kv_bytes_per_step(shape, pos_of(i)) for i in range(K)]
     alg_bytes = wbytes + float(np.mean(kvb))
     achieved = alg_bytes / avg_kernel_s
     traffic = traffic_from_profiles(shape.name)
 
+    metric = METRIC if not shape.is_moe else \
+        "µs per decode step @batch%d (parallel-block MoE shape); achieved HBM GB/s vs peak" % shape.batch
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(ms_per_step * 1e3, 2),
         "unit": "us/step",
         "n_gpus": 1,
@@ -172,21 +207,27 @@ def main() -> int:
                    "batch": shape.batch, "context": shape.prefill, "weights": "bf16",
                    "kv_cache": "bf16", "n_cus": info["n_cus"], "attn_block": info["attn_block"],
                    "mlp_chunks": info["mlp_chunks"]},
+        "tokens_per_step": shape.batch,
         "kernel_us_per_step": round(avg_kernel_s * 1e6, 2),
         "kernel_us_median": round(float(np.median(kern_ms)) * 1e3, 2),
         "kernel_us_p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 2),
-        "tok_per_s": round(1.0 / (ms_per_step / 1e3), 1),
+        "tok_per_s": round(shape.batch / (ms_per_step / 1e3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
                      "traffic": traffic, "alg_bytes_per_launch": int(alg_bytes)},
         "cpu_baseline": None,
     }
+    if shape.is_moe:
+        out["config"].update({"experts": shape.n_experts, "top_k": shape.top_k,
+                              "expert_ffn": shape.expert_ffn, "parallel_block": True})
+        out["experts_selected_per_layer"] = round(experts_per_layer, 2)
     eng.close()
     del eng
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle (bounded sample)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(shape, weights, kc, vc, tokens, args.cpu_budget)
+        out["cpu_baseline"] = (cpu_baseline_moe(shape, weights, kc, vc, tokens) if shape.is_moe else
+                               cpu_baseline(shape, weights, kc, vc, tokens, args.cpu_budget))
     print(json.dumps(out), flush=True)
     return 0
 

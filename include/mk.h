@@ -188,6 +188,15 @@ mk_status mk_destroy(mk_ctx *ctx);
  * The string is owned by the library and valid until the next call. */
 const char *mk_last_error(const mk_ctx *ctx);
 
+/* Routing statistics of the mixture-of-experts decoder: per_layer[l] receives
+ * the number of distinct experts the router selected in layer l (union over
+ * the batch), summed over the steps since the last reset; each selected
+ * expert streams 6 * hidden * expert_ffn weight bytes.  n >= n_layers.
+ * Waits for the context's last step; reset != 0 zeroes the sums.  Dense
+ * decoders report zeros.  Errors: MK_ERR_NO_PLAN, MK_ERR_INVALID_ARG,
+ * MK_ERR_HIP. */
+mk_status mk_route_stats(mk_ctx *ctx, int64_t *per_layer, int32_t n, int reset);
+
 /* Summary of the context's current plan.  Errors: MK_ERR_NO_PLAN. */
 mk_status mk_plan_info(const mk_ctx *ctx, mk_plan_summary *out);
 

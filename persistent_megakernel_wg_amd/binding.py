@@ -60,7 +60,8 @@ class MkPlanSummary(ctypes.Structure):
 
 
 EXPORTS = ("mk_create", "mk_build_plan", "mk_decode_step", "mk_sync", "mk_destroy",
-           "mk_last_error", "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read")
+           "mk_last_error", "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read",
+           "mk_route_stats")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -88,8 +89,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_trace_enable.argtypes = [vp, ctypes.c_int]
     lib.mk_trace_read.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), ctypes.c_size_t,
                                   ctypes.POINTER(i32)]
+    lib.mk_route_stats.argtypes = [vp, ctypes.POINTER(ctypes.c_int64), i32, ctypes.c_int]
     for name in ("mk_create", "mk_build_plan", "mk_decode_step", "mk_sync", "mk_destroy",
-                 "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read"):
+                 "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read",
+                 "mk_route_stats"):
         getattr(lib, name).restype = st
     _lib = lib
     return lib
@@ -165,6 +168,13 @@ def mk_plan_check(cfg: MkConfig, n_cus: int, opts: Optional[MkPlanOpts] = None):
                                          ctypes.byref(opts) if opts is not None else None,
                                          n_cus, ctypes.byref(s), buf, len(buf)))
     return s.as_dict(), buf.value.decode()
+
+
+def mk_route_stats(ctx: int, n_layers: int, reset: bool = False):
+    """Distinct experts selected per layer, summed over steps (list of ints)."""
+    buf = (ctypes.c_int64 * n_layers)()
+    _check(load_library().mk_route_stats(ctx, buf, n_layers, int(reset)), ctx)
+    return list(buf)
 
 
 def mk_trace_enable(ctx: int, on: bool = True) -> None:

@@ -715,6 +715,10 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
         // every read of this table slot) before it is rewritten
         uint64_t mask = 0;
         ok = wait_all_ge(C_XCONS, i) && route_topk(a, I, mask, rt_base(I->layer), c.retries);
+        // CU 0 counts the layer's selected experts (bytes streamed per step)
+        if (ok && cu == 0 && c.lane == 0)
+          __hip_atomic_fetch_add(gp(a.route_stats) + I->layer, uint32_t(__builtin_popcountll(mask)),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (!ok) {
         if (c.lane == 0) lds_st(C_ABORT, 1);

@@ -217,6 +217,7 @@ struct KArgs {
   int32_t n_experts;        // experts per layer (0 = dense MLP)
   int32_t top_k;            // experts per token
   int32_t expert_ffn;       // intermediate size of one expert
+  uint32_t* route_stats;    // [L] distinct experts selected per layer, summed over steps
 };
 
 // trace record words (s_memrealtime, 100 MHz, low 32 bits)

@@ -275,6 +275,7 @@ ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
   a.zero_page = take(kPageBytes);
   a.lm_slots = take(8 * uint64_t(max_lm_tiles) * (is_batched(c) ? lb::kMaxB : 1));
   a.status = take(64);
+  a.route_stats = take(4 * 128);
   a.total = off;
   return a;
 }

@@ -270,6 +270,7 @@ mk_status mk_decode_step(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_
   a.n_experts = c->cfg.n_experts;
   a.top_k = c->cfg.top_k;
   a.expert_ffn = c->cfg.expert_ffn;
+  a.route_stats = reinterpret_cast<uint32_t*>(c->arena + p.arena.route_stats);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = p.batched ? mk_launch_batched(&a, p.n_cus, s, c->cooperative, c->variant)
@@ -358,6 +359,23 @@ mk_status mk_trace_read(mk_ctx* c, uint32_t* host, size_t n_words, int32_t* stri
 }
 
 const char* mk_last_error(const mk_ctx* c) { return c ? c->err.c_str() : g_err.c_str(); }
+
+mk_status mk_route_stats(mk_ctx* c, int64_t* per_layer, int32_t n, int reset) {
+  if (!c || !per_layer || n < 0) return fail(c, MK_ERR_INVALID_ARG, "mk_route_stats: NULL argument");
+  if (!c->planned) return fail(c, MK_ERR_NO_PLAN, "mk_route_stats: no plan");
+  if (n < c->cfg.n_layers) return fail(c, MK_ERR_INVALID_ARG, "mk_route_stats: buffer shorter than n_layers");
+  if (c->has_step) {
+    hipError_t e = hipStreamSynchronize(c->last_stream);
+    if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  }
+  uint32_t v[128];
+  const size_t L = size_t(c->cfg.n_layers);
+  hipError_t e = hipMemcpy(v, c->arena + c->plan.arena.route_stats, 4 * L, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && reset) e = hipMemset(c->arena + c->plan.arena.route_stats, 0, 4 * L);
+  if (e != hipSuccess) return hip_fail(c, e, "route statistics readback");
+  for (size_t l = 0; l < L; l++) per_layer[l] = c->cfg.n_experts > 0 ? int64_t(v[l]) : 0;
+  return MK_OK;
+}
 
 mk_status mk_plan_info(const mk_ctx* c, mk_plan_summary* out) {
   if (!c || !out) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_plan_info: NULL argument");

@@ -65,3 +65,43 @@ def test_llama1b_ctx8192_4_steps(need_gpu):
 @pytest.mark.timeout(900)
 def test_llama8b_ctx2048_1_step(need_gpu):
     _greedy_case("llama8b_ctx2048", 1, keep_f64=False)
+
+
+@pytest.mark.timeout(1100)
+def test_moe_b8_ctx2048_2_steps_sampled(need_gpu):
+    """The batch-8 MoE shape at full size: two device-chained greedy steps,
+    checked against the oracle on two of the eight sequences (the sequences
+    of a step are independent, so each is a full check of its own outputs)."""
+    from persistent_megakernel_wg_amd.engine import Engine
+    s = synth.SHAPES["moe_b8_ctx2048"]
+    steps, sample = 2, [0, 5]
+    print("case %s: %d greedy steps from position %d, sequences %s checked"
+          % (s.name, steps, s.prefill, sample), flush=True)
+    w = synth.make_weights(s)
+    kc, vc = synth.make_kv_cache(s)
+    tok = synth.make_tokens(s)
+    print("  inputs generated", flush=True)
+    eng = Engine(s, w, kc, vc)
+    try:
+        lgs, toks = eng.generate(tok, s.prefill, steps, logits=True)
+        kg, vg = eng.read_kv()
+    finally:
+        eng.close()
+    print("  device steps done", flush=True)
+    orc = DecoderOracle(s, w, keep_f64=False)
+    k_ref, v_ref = kc.copy(), vc.copy()
+    t = tok.copy()
+    for i in range(steps):
+        ref_lg, ref_nx = orc.step(t, s.prefill + i, k_ref, v_ref, seqs=sample)
+        for b in sample:
+            err = rel_l2(lgs[i][b], ref_lg[b])
+            print("  step %d seq %d: rel_l2 %.3e token %d / oracle %d"
+                  % (i, b, err, toks[i][b], ref_nx[b]), flush=True)
+            assert err <= TOL, (i, b, err)
+            assert toks[i][b] == ref_nx[b], (i, b)
+        t = toks[i].copy()
+    span = slice(s.prefill, s.prefill + steps)
+    for got, ref in ((kg, k_ref), (vg, v_ref)):
+        for b in sample:
+            assert kv_rows_close(got[:, b, :, span], ref[:, b, :, span])
+        assert np.array_equal(got[:, :, :, :s.prefill], ref[:, :, :, :s.prefill])
