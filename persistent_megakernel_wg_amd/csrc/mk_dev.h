@@ -148,7 +148,7 @@ DEV __amdgpu_buffer_rsrc_t act_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 DEV f4 ld_act4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16 /* sc1 */);
+  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16 /* sc1 */));
 }
 // two tagged elements {v0, tag0, v1, tag1}
 DEV u4 ld_tag2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -510,7 +510,7 @@ DEV void vm_throttle(uint32_t& nd) {
 // `valid` bytes at `base`, from byte off0 of the run: whole units past the run
 // read the zero page, a unit that straddles its end is read per lane.
 DEV void issue_run(const KArgs& a, uint32_t dst, uint64_t base, uint32_t off0, uint32_t valid,
-                   uint32_t voff, uint32_t voff4k, uint32_t& nd) {
+                   uint32_t voff, uint32_t voff4k, uint32_t& nd, bool deep = false) {
   // every operand is wave-uniform (the DMA takes scalar addresses)
   dst = uni(dst);
   base = uni64(base);
@@ -518,10 +518,10 @@ DEV void issue_run(const KArgs& a, uint32_t dst, uint64_t base, uint32_t off0, u
   valid = uni(valid);
   const uint64_t zero = uint64_t(a.zero_page);
   if (off0 + kDmaPerPage * kUnit <= valid) {
-    dma_run8(dst, base + off0, voff, voff4k, false);
+    dma_run8(dst, base + off0, voff, voff4k, deep);
     nd += kDmaPerPage;
   } else if (off0 >= valid) {
-    dma_run8(dst, zero, voff, voff4k, false);
+    dma_run8(dst, zero, voff, voff4k, deep);
     nd += kDmaPerPage;
   } else {
     for (uint32_t j = 0; j < kDmaPerPage; j++) {
@@ -817,26 +817,63 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
 }
 
 // Last-arriving tile of a head tile's blocks merges their partials
-// (log-sum-exp of the block maxima).
+// (log-sum-exp of the block maxima, taken as a running maximum over batches
+// of blocks).  Lane l merges the PER consecutive outputs from l*PER (one
+// head); every load of a batch of blocks is issued before the first is used,
+// so a merge of n blocks costs about n/8 memory round trips.
 template <int HPT, int DH>
 DEV void attn_merge(Comp& c, InstrCP I) {
+  constexpr int OUT = HPT * DH, PER = OUT / 64, REC = DH + 2, NB = 8;
+  static_assert(PER == 1 || PER == 2 || PER == 4 || PER == 8, "merge lane shape");
   const uint32_t g = I->aux[0], nblk = I->aux[3];
   const uint32_t head0 = g * uint32_t(c.a->hpg) + I->row0;
-  const float* part = reinterpret_cast<const float*>(I->res_ptr) + size_t(head0 / HPT) * nblk * (HPT * (DH + 2));
-  for (uint32_t o = c.lane; o < uint32_t(HPT * DH); o += 64) {
-    const uint32_t h = o / DH, d = o % DH;
-    float M = -__builtin_inff();
-    for (uint32_t b = 0; b < nblk; b++) M = fmaxf(M, ld_act(part + (b * HPT + h) * (DH + 2) + DH));
-    float num = 0.f, den = 0.f;
-    for (uint32_t b = 0; b < nblk; b++) {
-      const float* rec = part + (b * HPT + h) * (DH + 2);
-      const float mb = ld_act(rec + DH);
-      const float wgt = mb == -__builtin_inff() ? 0.f : __expf(mb - M);
-      num = fmaf(wgt, ld_act(rec + d), num);
-      den = fmaf(wgt, ld_act(rec + DH + 1), den);
+  const float* part = reinterpret_cast<const float*>(I->res_ptr) + size_t(head0 / HPT) * nblk * (HPT * REC);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(part), 0,
+                                                                     nblk * HPT * REC * 4, 0x00020000);
+  const uint32_t o0 = c.lane * PER, h = o0 / DH, d0 = o0 % DH;
+  float M = -__builtin_inff(), den = 0.f, num[PER];
+#pragma unroll
+  for (int e = 0; e < PER; e++) num[e] = 0.f;
+  for (uint32_t b0 = 0; b0 < nblk; b0 += NB) {
+    float mb[NB], lb_[NB], v[NB][PER];
+#pragma unroll
+    for (int k = 0; k < NB; k++) {
+      // blocks past the end read past the resource: zero, and are skipped
+      const uint32_t rec = ((b0 + k) * HPT + h) * REC * 4;
+      mb[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, rec + DH * 4, 0, 16 /* sc1 */));
+      lb_[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, rec + (DH + 1) * 4, 0, 16));
+      if constexpr (PER >= 4) {
+#pragma unroll
+        for (int q4 = 0; q4 < PER / 4; q4++) {
+          const f4 t = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, rec + (d0 + 4 * q4) * 4, 0, 16));
+          v[k][4 * q4] = t.x; v[k][4 * q4 + 1] = t.y; v[k][4 * q4 + 2] = t.z; v[k][4 * q4 + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < PER; e++)
+          v[k][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, rec + (d0 + e) * 4, 0, 16));
+      }
     }
-    st_tag(reinterpret_cast<uint64_t*>(I->out_ptr) + (head0 + h) * DH + d, num / den, c.a->epoch);
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < NB; k++)
+      if (b0 + k < nblk) Mn = fmaxf(Mn, mb[k]);
+    const float scale = M == -__builtin_inff() ? 0.f : __expf(M - Mn);
+    den *= scale;
+#pragma unroll
+    for (int e = 0; e < PER; e++) num[e] *= scale;
+#pragma unroll
+    for (int k = 0; k < NB; k++) {
+      const float w = (b0 + k >= nblk || mb[k] == -__builtin_inff()) ? 0.f : __expf(mb[k] - Mn);
+      den = fmaf(w, lb_[k], den);
+#pragma unroll
+      for (int e = 0; e < PER; e++) num[e] = fmaf(w, v[k][e], num[e]);
+    }
+    M = Mn;
   }
+  uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr) + (head0 + h) * DH + d0;
+#pragma unroll
+  for (int e = 0; e < PER; e++) st_tag(out + e, num[e] / den, c.a->epoch);
 }
 
 // ---- staging of the instruction's inputs into the LDS x slot (leader wave)
@@ -906,8 +943,8 @@ DEV bool stage_attn(Comp& c, InstrCP I) {
       }
       tk[0] = ld_tag2(rk, ok1[0]);
       tv[0] = ld_tag2(rv, ok1[0]);
-      const f4 cv = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, 0, 0);
-      const f4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, (lane - half / 4) * 16, 0, 0);
+      const f4 cv = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, 0, 0));
+      const f4 sv = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rs, (lane - half / 4) * 16, 0, 0));
       const bool kv_lane = 2 * lane < uint32_t(dh);
       const uint32_t q_live = nq > 2 * lane ? (nq - 2 * lane + 127) / 128 : 0;
       if (!wait_fresh(tq, q_live, rq, [&](int, int j) { return oq[j]; }, 0, tag, c.retries)) return false;
