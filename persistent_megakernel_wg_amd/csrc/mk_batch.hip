@@ -23,6 +23,8 @@
 //  * The down projection keeps, per (sequence, top-k slot, row), the dot of its
 //    expert and sums the slots in order with the softmax weights, then adds the
 //    residual (the O-projection output): x_{l+1} = x_l + attn + MoE.
+#include <type_traits>
+
 #include "mk_dev.h"
 
 namespace mk {
@@ -33,83 +35,196 @@ namespace mk {
 enum : int {
   RT_MASK = 0,     // u64 selected-expert mask (union over the batch)
   RT_NSEL = 8,     // u32 number of selected experts
+  RT_NPAIR = 12,   // u32 routed (expert, sequence) pairs = B * top_k
   RT_TOK = 16,     // u8 [64] sequences routed to expert e (bit b)
   RT_LIST = 80,    // u8 [64] selected experts in increasing id order
   RT_SLOT = 144,   // u8 [64][8] top-k slot of expert e for sequence b
   RT_WT = 656,     // f32 [8][8] softmax weight of sequence b's slot s
-  RT_END = 912,
+  RT_PBASE = 912,  // u8 [64] first pair index of the selected expert of each rank
+  RT_PAIR = 976,   // u16 [64] pair index -> expert | sequence << 6 | slot << 9
+  RT_PRANK = 1104, // u8 [64] pair index -> rank of its expert
+  RT_END = 1168,
 };
 static_assert(RT_END <= lb::kRouteBytes, "routing table size");
 
 DEV int rt_base(uint32_t layer) { return lb::kRoute + int(layer & 1) * lb::kRouteBytes; }
 DEV uint32_t rt_u8(int base, int off) { return *reinterpret_cast<const uint8_t*>(lds + base + off); }
+DEV void rt_st8(int base, int off, uint32_t v) { *reinterpret_cast<uint8_t*>(lds + base + off) = uint8_t(v); }
 
-// Top-k of every sequence's router logits.  Lane e holds expert e's logit; k
-// rounds take the maximum and the lowest expert id holding it (ties go to the
-// lower id).  Returns the union of the selections; with table >= 0 the leader
-// also records token masks, slots and the softmax weights over each
-// sequence's k selected logits (top-k first, then softmax over those k).
-// false = abort or watchdog while waiting for fresh logits.
+// Reductions over aligned groups of 8 lanes (every lane of the group gets
+// the result): xor 1, xor 2, then the half-row mirror pairs the two quads.
+template <class T, class Op>
+DEV T group8(T v, Op op) {
+  auto sh = [](T x, auto ctrl) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), decltype(ctrl)::value,
+                                                             0xF, 0xF, false));
+  };
+  v = op(v, sh(v, std::integral_constant<int, 0xB1>{}));
+  v = op(v, sh(v, std::integral_constant<int, 0x4E>{}));
+  v = op(v, sh(v, std::integral_constant<int, 0x141>{}));
+  return v;
+}
+
+// Top-k of every sequence's router logits, all sequences at once: the 8 lanes
+// of group b hold sequence b's logits (lane s: experts 8s .. 8s+7).  Each of
+// the k rounds takes the group maximum and the lowest expert id holding it
+// (ties go to the lower id).  Returns the union of the selections; with
+// table >= 0 the leader also records the per-expert sequence masks and slots,
+// the softmax weights over each sequence's k selected logits (top-k first,
+// then softmax over those k), the selected experts in order and their first
+// pair index.  false = abort or watchdog while waiting for fresh logits.
 DEV bool route_topk(const KArgs& a, InstrCP I, uint64_t& mask, int table, uint32_t& retries) {
-  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t lane = threadIdx.x & 63, b = lane >> 3, s = lane & 7;
   const uint32_t E = I->aux[4], k = uint32_t(a.top_k), nB = uint32_t(a.batch);
   const __amdgpu_buffer_rsrc_t r = act_rsrc(reinterpret_cast<const void*>(I->seg_ptr[0]), nB * E * kActBytes);
-  uint2 t[lb::kMaxB];
-  auto off = [&](int, int b) -> uint32_t { return (uint32_t(b) * E + lane) * kActBytes; };
+  const uint32_t live = (b < nB && 8 * s < E) ? min(8u, E - 8 * s) : 0u;
+  uint2 t[8];
+  auto off = [&](int, int j) -> uint32_t { return (b * E + 8 * s + uint32_t(j)) * kActBytes; };
 #pragma unroll
-  for (int b = 0; b < lb::kMaxB; b++) reload(t[b], r, off(0, b));
-  if (!wait_fresh(t, lane < E ? nB : 0u, r, off, 0, a.epoch, retries)) return false;
-  mask = 0;
-  uint32_t tokbits = 0;
+  for (int j = 0; j < 8; j++) reload(t[j], r, off(0, j));
+  if (!wait_fresh(t, live, r, off, 0, a.epoch, retries)) return false;
+  float v[8];
 #pragma unroll
-  for (int b = 0; b < lb::kMaxB; b++) {
-    if (uint32_t(b) >= nB) break;
-    float v = lane < E ? __uint_as_float(t[b].x) : -__builtin_inff();
-    if (v != v) v = -__builtin_inff();
-    bool taken = false;
-    float lv = -__builtin_inff();  // lane s: the s-th selected logit
-    uint32_t myslot = 0;
-    for (uint32_t s = 0; s < k; s++) {
-      const float m = max64(taken ? -__builtin_inff() : v);
-      const uint64_t ball = __builtin_amdgcn_ballot_w64(!taken && lane < E && v == m);
-      if (ball == 0) break;  // k > E (the planner rejects it)
-      const uint32_t e = uint32_t(__builtin_ctzll(ball));
-      if (lane == e) {
-        taken = true;
-        myslot = s;
-      }
-      if (lane == s) lv = m;
-      mask |= 1ull << e;
+  for (int j = 0; j < 8; j++) {
+    const float x = __uint_as_float(t[j].x);
+    v[j] = (uint32_t(j) < live && x == x) ? x : -__builtin_inff();
+  }
+  uint32_t taken = 0, slot[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float myv = -__builtin_inff();  // lane s of a group: the value of round s
+  auto fmax_ = [](float x, float y) { return fmaxf(x, y); };
+  auto umin_ = [](uint32_t x, uint32_t y) { return min(x, y); };
+  for (uint32_t rd = 0; rd < k; rd++) {
+    float lm = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < 8; j++) lm = fmaxf(lm, ((taken >> j) & 1) ? -__builtin_inff() : v[j]);
+    const float gm = group8(lm, fmax_);
+    uint32_t ci = 0xFFu;
+#pragma unroll
+    for (int j = 7; j >= 0; j--)
+      if (!((taken >> j) & 1) && uint32_t(j) < live && v[j] == gm) ci = 8 * s + uint32_t(j);
+    const uint32_t ge = group8(ci, umin_);
+    if (ge != 0xFFu && (ge >> 3) == s) {
+      taken |= 1u << (ge & 7);
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        if (uint32_t(j) == (ge & 7)) slot[j] = rd;
     }
-    if (table >= 0) {
-      if (taken) {
-        tokbits |= 1u << b;
-        *reinterpret_cast<uint8_t*>(lds + table + RT_SLOT + lane * 8 + b) = uint8_t(myslot);
+    if (s == rd) myv = gm;
+  }
+  // union over the sequences: expert 8s + j is selected if a group took it
+  uint64_t ball[8];
+  mask = 0;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    ball[j] = __builtin_amdgcn_ballot_w64((taken >> j) & 1);
+    uint64_t m8 = ball[j];
+    m8 |= m8 >> 32;
+    m8 |= m8 >> 16;
+    m8 |= m8 >> 8;
+    for (uint32_t ss = 0; ss < 8; ss++)
+      if ((m8 >> ss) & 1) mask |= 1ull << (8 * ss + uint32_t(j));
+  }
+  if (table < 0) return true;
+  // slots of the taken experts; softmax weights of the k selected logits
+#pragma unroll
+  for (int j = 0; j < 8; j++)
+    if ((taken >> j) & 1) rt_st8(table, RT_SLOT + int((8 * s + uint32_t(j)) * 8 + b), slot[j]);
+  const float top = group8(myv, fmax_);
+  const float ex = (s < k && b < nB) ? __expf(myv - top) : 0.f;
+  const float den = group8(ex, [](float x, float y) { return x + y; });
+  if (b < nB) *reinterpret_cast<float*>(lds + table + RT_WT + int(b * 8 + s) * 4) = ex / den;
+  // lane e: the sequences routed to expert e
+  {
+    const uint32_t e = lane, je = e & 7, se = e >> 3;
+    uint64_t bj = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      if (uint32_t(j) == je) bj = ball[j];
+    uint32_t tok = 0;
+    for (uint32_t bb = 0; bb < nB; bb++) tok |= uint32_t((bj >> (8 * bb + se)) & 1) << bb;
+    const bool sel = (mask >> e) & 1;
+    const uint32_t rank = __builtin_popcountll(mask & ((1ull << e) - 1));
+    // exclusive prefix sum of the selected experts' pair counts, in rank order
+    uint32_t pc = sel ? __builtin_popcount(tok) : 0, inc = pc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t up = __shfl_up(inc, d, 64);
+      if (lane >= uint32_t(d)) inc += up;
+    }
+    if (e < E) rt_st8(table, RT_TOK + int(e), tok);
+    if (sel) {
+      rt_st8(table, RT_LIST + int(rank), e);
+      rt_st8(table, RT_PBASE + int(rank), inc - pc);
+      // the expert's pairs, in sequence order (slots were stored above by
+      // the lanes that took them; one wave's LDS accesses are in order)
+      uint32_t pi = inc - pc;
+      for (uint32_t bits = tok; bits; bits &= bits - 1, pi++) {
+        const uint32_t bb = __builtin_ctz(bits);
+        const uint32_t sl = rt_u8(table, RT_SLOT + int(e * 8 + bb));
+        *reinterpret_cast<uint16_t*>(lds + table + RT_PAIR + int(pi) * 2) = uint16_t(e | bb << 6 | sl << 9);
+        rt_st8(table, RT_PRANK + int(pi), rank);
       }
-      const float top = rl(lv, 0);
-      const float ex = lane < k ? __expf(lv - top) : 0.f;
-      const float den = sum64(ex);
-      if (lane < lb::kMaxTopK)
-        *reinterpret_cast<float*>(lds + table + RT_WT + (b * 8 + int(lane)) * 4) = ex / den;
     }
   }
-  if (table >= 0) {
-    if (lane < E) {
-      *reinterpret_cast<uint8_t*>(lds + table + RT_TOK + lane) = uint8_t(tokbits);
-      if ((mask >> lane) & 1) {
-        const uint32_t rank = __builtin_popcountll(mask & ((1ull << lane) - 1));
-        *reinterpret_cast<uint8_t*>(lds + table + RT_LIST + rank) = uint8_t(lane);
-      }
-    }
-    if (lane == 0) {
-      *reinterpret_cast<uint64_t*>(lds + table + RT_MASK) = mask;
-      *lw(table + RT_NSEL) = uint32_t(__builtin_popcountll(mask));
-    }
+  if (lane == 0) {
+    *reinterpret_cast<uint64_t*>(lds + table + RT_MASK) = mask;
+    *lw(table + RT_NSEL) = uint32_t(__builtin_popcountll(mask));
+    *lw(table + RT_NPAIR) = nB * k;
   }
   return true;
 }
 
 // --------------------------------------------------------------- loader
+// Two runs of four 1 KiB units into one half page: src_a's four units at M0,
+// src_b's at M0 + 4 KiB (the gate and up rows of one pair when rows are 4 KiB),
+// non-temporal, each DMA followed by the deep in-flight throttle.
+#define MK_DMA44(T)                                                                                 \
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"                                                   \
+               "global_load_lds_dwordx4 %1, %2 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"              \
+               "global_load_lds_dwordx4 %1, %2 offset:1024 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"  \
+               "global_load_lds_dwordx4 %1, %2 offset:2048 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"  \
+               "global_load_lds_dwordx4 %1, %2 offset:3072 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"  \
+               "s_add_u32 m0, %0, 0x1000\n\ts_nop 0\n\t"                                              \
+               "global_load_lds_dwordx4 %1, %3 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"              \
+               "global_load_lds_dwordx4 %1, %3 offset:1024 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"  \
+               "global_load_lds_dwordx4 %1, %3 offset:2048 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")\n\t"  \
+               "global_load_lds_dwordx4 %1, %3 offset:3072 nt\n\ts_waitcnt vmcnt(" MK_STR(T) ")"        \
+               :                                                                                    \
+               : "s"(lds_addr), "v"(voff), "s"(src_a), "s"(src_b)                                   \
+               : "memory", "m0")
+DEV void dma_44(uint32_t lds_addr, uint64_t src_a, uint64_t src_b, uint32_t voff) {
+  lds_addr = uni(lds_addr);
+  src_a = uni64(src_a);
+  src_b = uni64(src_b);
+  MK_DMA44(MK_VMT_DEEP);
+}
+
+// This loader wave's half page (units u0 .. u0+7) of an expert's gate/up
+// region: pair q occupies units [2q*nit, 2q*nit + 2*nit), its gate row first.
+// Units past the CU's npu pairs read the zero page.
+DEV void issue_gate_up(const KArgs& a, uint32_t dst, uint64_t gate, uint64_t up, uint32_t u0, uint32_t npu,
+                       uint32_t nit, uint32_t rb, uint32_t voff, uint32_t voff4k, uint32_t& nd) {
+  const uint64_t zero = uint64_t(a.zero_page);
+  if (nit == 4 || nit == 8) {
+    const uint32_t q = u0 / (2 * nit);
+    if (q >= npu) {
+      dma_run8(dst, zero, voff, voff4k, true);
+    } else if (nit == 4) {
+      dma_44(dst, gate + uint64_t(q) * rb, up + uint64_t(q) * rb, voff);
+    } else {
+      dma_run8(dst, ((u0 / nit) & 1 ? up : gate) + uint64_t(q) * rb, voff, voff4k, true);
+    }
+    nd += kDmaPerPage;
+    return;
+  }
+  for (uint32_t j = 0; j < kDmaPerPage; j++) {
+    const uint32_t u = u0 + j, q = u / (2 * nit), jj = u % nit;
+    const uint64_t src = q < npu ? ((u / nit) & 1 ? up : gate) + uint64_t(q) * rb + jj * kUnit : zero;
+    dma_uniform(uni(dst + j * kUnit), uni64(src), voff);
+    vm_throttle(nd);
+  }
+}
+
 // Same paging as the one-sequence loader, with a running page index: an
 // expert instruction takes (selected experts) x (pages per expert) pages, a
 // number known only once the loader has read the layer's router logits.
@@ -162,7 +277,7 @@ DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
         mask = uni64(mask);
         route_layer = layer;
       }
-      const uint32_t ppe = I->aux[2], gpg = I->seg_stride[1], run = I->seg_rows[0];
+      const uint32_t ppe = I->aux[2], npu = I->aux[3], run = I->seg_rows[0], nit = i_nit(I), rb = I->row_bytes;
       const uint64_t stride = I->seg_stride[0];
       for (uint64_t m = mask; m; m &= m - 1) {
         const uint32_t e = uint32_t(__builtin_ctzll(m));
@@ -170,11 +285,12 @@ DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
         for (uint32_t p = 0; p < ppe; p++) {
           const uint32_t g = pg++;
           if (!acquire(g)) return;
-          const uint32_t second = p < gpg ? 0 : 1;
           const uint32_t dst = uint32_t(size_t(lds)) + page_off<LayB>(g) + half * kUnit;
-          issue_run(a, dst, second ? b1 : b0, ((p - second * gpg) * kUnitsPerPage + half) * kUnit, run, voff,
-                    voff4k, nd);
-          after_issue(g, false);
+          if (op == OP_EGU)
+            issue_gate_up(a, dst, b0, b1, p * kUnitsPerPage + half, npu, nit, rb, voff, voff4k, nd);
+          else
+            issue_run(a, dst, b0, (p * kUnitsPerPage + half) * kUnit, run, voff, voff4k, nd, true);
+          after_issue(g, true);
         }
       }
       continue;
@@ -433,24 +549,27 @@ DEV bool bgemv(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
 }
 
 // ------------------------------------------------------ expert gate / up
-// Items are (selected expert, pair of the CU's slice) in expert order; each
-// applies the gate and up rows to the sequences routed to the expert and
-// stores m = silu(gate) * up at [b][slot of e in b's top-k][row].
+// Items are (selected expert, pair of the CU's slice) in expert order; the
+// loader lays each pair out as its gate row then its up row.  An item applies
+// the two rows to the sequences routed to the expert and stores
+// m = silu(gate) * up (fp32) at [b][slot of e in b's top-k][row].  The stores
+// are plain device-scope stores: the instruction's counter moves only after
+// every wave's stores have landed.
 DEV bool egu(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane, K = I->k, nit = i_nit(I);
   const int rt = rt_base(I->layer);
-  const uint32_t nsel = *lw(rt + RT_NSEL), npu = I->aux[3], ppe = I->aux[2], gpg = I->seg_stride[1];
+  const uint32_t nsel = *lw(rt + RT_NSEL), npu = I->aux[3], ppe = I->aux[2];
   const uint32_t Fe = uint32_t(a.expert_ffn), k = uint32_t(a.top_k);
   const float inv = inv_rms(a, I);
   const float my_inv = __shfl(inv, int(lane & 7), 64);
-  uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
+  float* out = reinterpret_cast<float*>(I->out_ptr);
   const uint32_t n_items = nsel * npu;
   for (uint32_t t = c.w; t < n_items; t += kNComp) {
     const uint32_t er = t / npu, p = t % npu;
     const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
     const uint32_t tm = uni(rt_u8(rt, RT_TOK + int(e)));
-    const uint32_t ug = er * ppe * kUnitsPerPage + p * nit, uu = ug + gpg * kUnitsPerPage;
+    const uint32_t ug = er * ppe * kUnitsPerPage + 2 * p * nit, uu = ug + nit;
     if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + ug / kUnitsPerPage);
     if (!wait_page(pg + (uu + nit - 1) / kUnitsPerPage, c.fcache)) return false;
     float acc[16];
@@ -460,7 +579,7 @@ DEV bool egu(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
     if (lane < 8 && ((tm >> lane) & 1)) {
       const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + lane));
       const float m = silu(s * my_inv) * (up * my_inv);
-      st_tag(out + (size_t(lane) * k + slot) * Fe + I->row0 + p, m, a.epoch);
+      st_act(out + (size_t(lane) * k + slot) * Fe + I->row0 + p, m);
     }
   }
   if (lane == 0) {
@@ -471,113 +590,95 @@ DEV bool egu(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
 }
 
 // ---------------------------------------------------- expert down projection
-// The routed (expert, sequence) pairs' intermediate vectors are staged into
-// the x slot in groups that fit it; the items of a group are (expert, row
-// pair); each stores its dots per (sequence, slot, row).  At the end
+// The routed (expert, sequence) pairs, in expert then sequence order, are
+// staged into the x slot in groups of cap = 16384 / K pairs (an expert's
+// pairs may straddle two groups).  While a group is computed, the next one is
+// already being loaded into registers.  Items are (expert with pairs in the
+// group, row pair); each stores its dots per (sequence, slot, row).  At the end
 // x_{l+1}[b][row] = h[b][row] + sum over slots s of w[b][s] * dot[b][s][row].
 DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane, K = I->k, nit = i_nit(I), nB = uint32_t(a.batch);
   const int rt = rt_base(I->layer);
-  const uint32_t nsel = *lw(rt + RT_NSEL), ppe = I->aux[2], nr = I->aux[3], ipe = (nr + 1) / 2;
+  const uint32_t nsel = *lw(rt + RT_NSEL), npair = *lw(rt + RT_NPAIR);
+  const uint32_t ppe = I->aux[2], nr = I->aux[3], ipe = (nr + 1) / 2;
   const uint32_t k = uint32_t(a.top_k), Fe = uint32_t(a.expert_ffn);
   const uint32_t cap = uint32_t(lb::kXFloats) / K;  // pairs per group
+  const uint32_t ngroups = (npair + cap - 1) / cap;
   float* xs = reinterpret_cast<float*>(lds + lb::kX);
   float* dots = reinterpret_cast<float*>(lds + lb::kDots);
-  constexpr int NC = (lb::kXFloats / 128 + kNComp - 1) / kNComp;
-  const uint64_t* m_in = reinterpret_cast<const uint64_t*>(I->in_ptr);
+  constexpr int NC = (lb::kXFloats / 256 + kNComp - 1) / kNComp;  // 256-value chunks per wave
   const bool trl = a.trace && c.w == 0 && lane == 0;
+  const __amdgpu_buffer_rsrc_t rm = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), nB * k * Fe * 4);
+  // rank of the selected expert holding pair index pi
+  auto rank_of = [&](uint32_t pi) -> uint32_t { return rt_u8(rt, RT_PRANK + int(pi)); };
+  // this wave's chunks of group g (256 values each), loaded into registers
+  f4 t[NC];
+  auto load_group = [&](uint32_t g) {
+    const uint32_t p0 = g * cap, np = min(cap, npair - p0), nch = np * K / 256;
+#pragma unroll
+    for (int qq = 0; qq < NC; qq++) {
+      const uint32_t ch = uint32_t(c.w) + kNComp * qq;
+      uint32_t off = 0;
+      if (ch < nch) {
+        const uint32_t pi = p0 + ch * 256 / K, kk = ch * 256 % K;
+        const uint32_t pr = *reinterpret_cast<const uint16_t*>(lds + rt + RT_PAIR + int(pi) * 2);
+        const uint32_t b = (pr >> 6) & 7, sl = pr >> 9;
+        off = ((b * k + sl) * Fe + kk + 4 * lane) * 4;
+      }
+      t[qq] = ld_act4(rm, off);
+    }
+  };
   // residual rows (leader), then every wave has left the previous input
   if (c.w == 0 && !stage_res_b(c, I, i, nr, uint32_t(a.hidden))) return false;
-  if (trl) trace_put(a, c.cu, i, TR_XREADY, now32());
   if (!wait_all_ge(C_XCONS, i)) return false;
   if (trl) trace_put(a, c.cu, i, TR_XFREE, now32());
-  const __amdgpu_buffer_rsrc_t rm = act_rsrc(m_in, nB * k * Fe * kActBytes);
-  uint32_t er0 = 0;
-  while (er0 < nsel) {
-    // the group: experts [er0, er1) with at most cap routed pairs
-    uint32_t er1 = er0, npair = 0;
-    while (er1 < nsel) {
-      const uint32_t pc = __builtin_popcount(rt_u8(rt, RT_TOK + int(rt_u8(rt, RT_LIST + int(er1)))));
-      if (npair + pc > cap) break;
-      npair += pc;
-      er1++;
-    }
-    npair = uni(npair);
-    er1 = uni(er1);
-    // stage: pair pi (in expert, then sequence order) <- m[b][slot][0 .. K)
-    const uint32_t nch = npair * K / 128;
-    const uint32_t live = uint32_t(c.w) < nch ? (nch - c.w + kNComp - 1) / kNComp : 0;
-    u4 t[NC];
-    uint32_t offs[NC];
+  load_group(0);
+  for (uint32_t g = 0; g < ngroups; g++) {
+    const uint32_t p0 = g * cap, np = min(cap, npair - p0), nch = np * K / 256;
+    // every wave has finished the previous group before its slot is rewritten
+    if (g > 0 && !comp_barrier()) return false;
 #pragma unroll
     for (int qq = 0; qq < NC; qq++) {
-      offs[qq] = 0;
-      if (qq < int(live)) {
-        const uint32_t ch = uint32_t(c.w) + kNComp * qq, pi = ch * 128 / K, kk = ch * 128 % K;
-        // pair pi -> (expert, sequence)
-        uint32_t left = pi, er = er0, tm = 0;
-        for (;; er++) {
-          tm = rt_u8(rt, RT_TOK + int(rt_u8(rt, RT_LIST + int(er))));
-          const uint32_t pc = __builtin_popcount(tm);
-          if (left < pc) break;
-          left -= pc;
-        }
-        uint32_t b = 0;
-        for (uint32_t bits = tm;; bits &= bits - 1) {
-          if (left == 0) {
-            b = __builtin_ctz(bits);
-            break;
-          }
-          left--;
-        }
-        const uint32_t e = rt_u8(rt, RT_LIST + int(er));
-        const uint32_t s = rt_u8(rt, RT_SLOT + int(e * 8 + b));
-        offs[qq] = ((b * k + s) * Fe + kk + 2 * lane) * kActBytes;
-      }
-      t[qq] = ld_tag2(rm, offs[qq]);
-    }
-    if (trl) trace_put(a, c.cu, i, TR_RETRY, npair | (er1 << 8) | (nsel << 16));
-    if (!wait_fresh(t, live, rm, [&](int, int qq) { return offs[qq]; }, 0, a.epoch, c.retries)) return false;
-    if (trl) trace_put(a, c.cu, i, TR_ITEM0, now32());
-#pragma unroll
-    for (int qq = 0; qq < NC; qq++) {
-      if (qq >= int(live)) continue;
-      const uint32_t flat = (uint32_t(c.w) + kNComp * qq) * 128 + 2 * lane;
-      *reinterpret_cast<float2*>(xs + flat) = float2{__uint_as_float(t[qq].x), __uint_as_float(t[qq].z)};
+      const uint32_t ch = uint32_t(c.w) + kNComp * qq;
+      if (ch < nch) *reinterpret_cast<f4*>(xs + ch * 256 + 4 * lane) = t[qq];
     }
     if (!comp_barrier()) return false;
-    if (trl) trace_put(a, c.cu, i, TR_A_PASS1, now32());
-    // items: (expert er in the group, row pair p)
-    const uint32_t n_items = (er1 - er0) * ipe;
+    if (g + 1 < ngroups) load_group(g + 1);
+    if (trl && g == 0) trace_put(a, c.cu, i, TR_ITEM0, now32());
+    // items: (expert rank er in [er_a, er_b], row pair p)
+    const uint32_t er_a = uni(rank_of(p0)), er_b = uni(rank_of(p0 + np - 1));
+    const uint32_t n_items = (er_b - er_a + 1) * ipe;
     for (uint32_t it = c.w; it < n_items; it += kNComp) {
-      const uint32_t er = er0 + it / ipe, p = it % ipe;
-      uint32_t pbase = 0;
-      for (uint32_t x = er0; x < er; x++) pbase += __builtin_popcount(rt_u8(rt, RT_TOK + int(rt_u8(rt, RT_LIST + int(x)))));
-      pbase = uni(pbase);
+      const uint32_t er = er_a + it / ipe, p = it % ipe;
       const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
-      const uint32_t tm = uni(rt_u8(rt, RT_TOK + int(e)));
+      const uint32_t tok = uni(rt_u8(rt, RT_TOK + int(e)));
+      const uint32_t base = uni(rt_u8(rt, RT_PBASE + int(er)));
+      // the expert's sequences whose pair lies in this group
+      uint32_t tm = 0, rank = 0;
+      for (uint32_t bits = tok; bits; bits &= bits - 1, rank++) {
+        const uint32_t pi = base + rank;
+        if (pi >= p0 && pi < p0 + np) tm |= 1u << __builtin_ctz(bits);
+      }
       const uint32_t u0 = er * ppe * kUnitsPerPage + 2 * p * nit;
       if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + u0 / kUnitsPerPage);
       if (!wait_page(pg + (u0 + 2 * nit - 1) / kUnitsPerPage, c.fcache)) return false;
       float acc[16];
       dot_pair(pg, u0, u0 + nit, nit, tm,
-               [&](int b) { return (pbase + __builtin_popcount(tm & ((1u << b) - 1))) * K; }, acc);
-      const float s = reduce16(acc);
+               [&](int b) { return (base + __builtin_popcount(tok & ((1u << b) - 1)) - p0) * K; }, acc);
+      const float sdot = reduce16(acc);
       const uint32_t li = lane & 15, ri = li >> 3, bb = li & 7, row = 2 * p + ri;
       if (lane < 16 && ((tm >> bb) & 1) && row < nr) {
         const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + bb));
-        dots[(bb * lb::kMaxTopK + slot) * lb::kMaxDnRows + row] = s;
+        dots[(bb * lb::kMaxTopK + slot) * lb::kMaxDnRows + row] = sdot;
       }
     }
-    // this wave reads no page of the group any more: release them before the
-    // barrier, or a group longer than the ring would wait on itself
-    if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + er1 * ppe);
-    if (trl) trace_put(a, c.cu, i, TR_A_STATS, now32());
-    if (!comp_barrier()) return false;
-    if (trl) trace_put(a, c.cu, i, TR_A_PASS3, now32());
-    er0 = er1;
+    // no page before the next group's first expert is read again: release
+    // them, or a group longer than the ring would wait on itself
+    if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + (g + 1 < ngroups ? uni(rank_of(p0 + np)) : nsel) * ppe);
   }
+  if (!comp_barrier()) return false;
+  if (trl) trace_put(a, c.cu, i, TR_A_STATS, now32());
   // x_{l+1} = h + sum over the top-k slots in order
   const float* res = res_slot_b(i);
   const float* wt = reinterpret_cast<const float*>(lds + rt + RT_WT);
@@ -714,7 +815,11 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
         // every wave has finished the earlier instructions (and with them
         // every read of this table slot) before it is rewritten
         uint64_t mask = 0;
-        ok = wait_all_ge(C_XCONS, i) && route_topk(a, I, mask, rt_base(I->layer), c.retries);
+        if (tr && c.lane == 0) trace_put(a, cu, i, TR_A_PASS1, now32());
+        ok = wait_all_ge(C_XCONS, i);
+        if (tr && c.lane == 0) trace_put(a, cu, i, TR_A_STATS, now32());
+        ok = ok && route_topk(a, I, mask, rt_base(I->layer), c.retries);
+        if (tr && c.lane == 0) trace_put(a, cu, i, TR_A_PASS3, now32());
         // CU 0 counts the layer's selected experts (bytes streamed per step)
         if (ok && cu == 0 && c.lane == 0)
           __hip_atomic_fetch_add(gp(a.route_stats) + I->layer, uint32_t(__builtin_popcountll(mask)),
@@ -776,7 +881,9 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
     if (tr && w == 0 && c.lane == 0) trace_put(a, cu, i, TR_ITEMS, now32());
     const bool lm = op == OP_BGEMV && i_epi(I) == EPI_ARGMAX;
     const bool ticket = op == OP_ATTN && I->aux[3] > 1;
-    if (lm || ticket) wait_vm0();
+    // untagged data behind a counter (argmax slots, attention partials, the
+    // expert intermediates) lands before the counter moves
+    if (lm || ticket || op == OP_EGU) wait_vm0();
     uint32_t prev = 0;
     if (c.lane == 0) prev = lds_add(C_DONE + 4 * (i % kDoneRing), 1);
     prev = uni(prev);

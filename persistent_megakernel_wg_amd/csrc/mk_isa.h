@@ -64,11 +64,11 @@ constexpr int kDots = 1536;          // expert down-projection dots [kMaxB][8 sl
 constexpr int kMaxDnRows = 16;
 constexpr int kMaxTopK = 8;
 constexpr int kRoute = kDots + 4 * kMaxB * kMaxTopK * kMaxDnRows;   // 5632: routing tables
-constexpr int kRouteBytes = 1024;    // one table per layer parity
-constexpr int kRes = kRoute + 2 * kRouteBytes;                      // 7680: residual rows
-constexpr int kX = kRes + 2 * 4 * kMaxResRows;                      // 8704
+constexpr int kRouteBytes = 1280;    // one table per layer parity
+constexpr int kRes = kRoute + 2 * kRouteBytes;                      // 8192: residual rows
+constexpr int kX = kRes + 2 * 4 * kMaxResRows;                      // 9216
 constexpr int kXFloats = 16384;      // [B][K] staged input, K <= 16384 / B
-constexpr int kAttn = kX + 4 * kXFloats;                            // 74240
+constexpr int kAttn = kX + 4 * kXFloats;                            // 74752
 constexpr int kScoreFloats = 512;    // attention scores of one tile
 constexpr int kAttnBytes = 4 * kScoreFloats + 512 + 64;
 constexpr int kPg = ((kAttn + kAttnBytes + 1023) / 1024) * 1024;   // 77824

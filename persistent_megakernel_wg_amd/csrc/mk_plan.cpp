@@ -382,9 +382,9 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
   const int n_rt = (E + 1) / 2;  // router tiles of two rows
   auto rt_cu = [&](int t) { return int(int64_t(t) * C / n_rt); };
   const int max_res_rows = std::min(kMaxResRows / B, lb::kMaxDnRows);
-  // pairs of an expert gate/up instruction: the gate run and the up run of a
-  // pair must be resident together, so each run is at most two pages
-  const int max_pairs = std::max(1, 2 * kPageBytes / (2 * d));
+  // pairs of an expert gate/up instruction (each pair is a gate row and an up
+  // row side by side in the page stream): a slice of at most four pages
+  const int max_pairs = std::max(1, 4 * kPageBytes / (4 * d));
 
   for (int l = 0; l < L; l++) {
     const int stg = l * ST_PER_LAYER;
@@ -495,7 +495,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
       split(Fe, cu, &f0, &f1);
       for (int64_t p0 = f0; p0 < f1; p0 += max_pairs) {
         const int64_t p1 = std::min<int64_t>(f1, p0 + max_pairs), npu = p1 - p0;
-        const int gpb = ceil_div(npu * 2 * d, kPageBytes);
+        const int ppe = ceil_div(npu * 4 * d, kPageBytes);
         Instr I = blank();
         I.op = OP_EGU;
         I.epi = EPI_SWIGLU;
@@ -510,7 +510,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.n_rows = uint32_t(2 * npu);
         I.k = uint32_t(d);
         I.aux[0] = c_rt[l];
-        I.aux[2] = uint32_t(2 * gpb);
+        I.aux[2] = uint32_t(ppe);
         I.aux[3] = uint32_t(npu);
         I.aux[4] = uint32_t(E);
         I.seg_ptr[0] = A + ar.rl[l];
@@ -518,13 +518,13 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.seg_ptr[2] = lptr(in.w.e_up, l, uint64_t(E) * Fe * d) + 2ull * d * p0;
         I.seg_stride[0] = uint32_t(2ull * Fe * d);
         I.seg_rows[0] = uint32_t(npu * 2 * d);
-        I.seg_stride[1] = uint32_t(gpb);
+        I.seg_stride[1] = 0;
         I.in_ptr = x_in;
         I.out_ptr = A + ar.m[l];
         I.gain_ptr = lptr(in.w.attn_norm, l, d);
         I.wait_ctr[0] = c_rt[l];
         I.sig_ctr = c_gu[l];
-        I.n_pages = uint32_t(E * 2 * gpb);
+        I.n_pages = uint32_t(E * ppe);
         InstrMeta m;
         m.stage = stg + ST_ATTN;
         m.merge_write = false;
@@ -593,7 +593,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.seg_ptr[1] = lptr(in.w.e_down, l, uint64_t(E) * d * Fe) + 2ull * Fe * r0;
         I.seg_stride[0] = uint32_t(2ull * d * Fe);
         I.seg_rows[0] = uint32_t(nr * 2 * Fe);
-        I.seg_stride[1] = uint32_t(ppe);
+        I.seg_stride[1] = 0;
         I.in_ptr = A + ar.m[l];
         I.res_ptr = A + ar.h[l];
         I.out_ptr = A + ar.x[l + 1];
@@ -1216,12 +1216,12 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
       }
       if (I.op == OP_EGU || I.op == OP_EDN) {
         if (!p.batched) return fail("expert instruction in a one-sequence plan");
-        const uint32_t ppe = I.aux[2], runs = I.op == OP_EGU ? 2 : 1, gpb = I.seg_stride[1];
+        const uint32_t ppe = I.aux[2], runs = I.op == OP_EGU ? 2 : 1;
         if (I.k % 512 || I.nit != I.k / 512 || I.row_bytes != 2 * I.k) return fail("expert row geometry");
-        if (gpb * runs != ppe || uint64_t(gpb) * kPageBytes < I.seg_rows[0]) return fail("expert page regions");
+        if (uint64_t(ppe) * kPageBytes < uint64_t(runs) * I.seg_rows[0] || ppe > uint32_t(lb::kPages) - 1)
+          return fail("expert page regions");
         if (I.n_pages != ppe * I.aux[4] || I.aux[4] != uint32_t(c.n_experts)) return fail("expert page budget");
-        if (I.op == OP_EGU && (I.seg_rows[0] != I.aux[3] * I.row_bytes || gpb + 1 > uint32_t(lb::kPages)))
-          return fail("expert gate/up runs");
+        if (I.op == OP_EGU && I.seg_rows[0] != I.aux[3] * I.row_bytes) return fail("expert gate/up runs");
         if (I.op == OP_EDN && (I.seg_rows[0] != I.aux[3] * I.row_bytes || I.aux[3] > uint32_t(lb::kMaxDnRows) ||
                                uint64_t(I.aux[3]) * c.batch > uint64_t(kMaxResRows) || I.aux[3] != I.n_rows))
           return fail("expert down-projection rows");
