@@ -56,8 +56,8 @@ typedef enum {
 
 /* Model shape.  Dense decoders (batch 1) set n_experts = top_k = expert_ffn = 0
  * and parallel_block = 0.  The mixture-of-experts decoder sets n_experts
- * (<= 64), top_k (<= min(8, n_experts)), expert_ffn (a multiple of 512, at most
- * 2048) and parallel_block = 1, with batch <= 8, hidden and n_q_heads*head_dim
+ * (<= 64), top_k (<= min(8, n_experts)), expert_ffn (512, 1024 or 2048) and
+ * parallel_block = 1, with batch <= 8, hidden and n_q_heads*head_dim
  * multiples of 512 and batch * max(hidden, n_q_heads*head_dim) <= 16384; ffn
  * and the dense MLP weights are unused.  Other shapes: MK_ERR_UNSUPPORTED. */
 typedef struct {

@@ -263,6 +263,7 @@ DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
   for (uint32_t i = 0; i < n; i++) {
     InstrCP I = q + i;
     const uint32_t op = i_op(I);
+    if (i_flags(I) & F_DIRECT) continue;
     if (op == OP_EGU || op == OP_EDN) {
       const uint32_t layer = I->layer;
       if (layer != route_layer) {
@@ -589,6 +590,78 @@ DEV bool egu(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
   return true;
 }
 
+// Gate/up with the weight rows loaded by the compute waves themselves: each
+// wave keeps the rows of its next D-1 items in flight in registers while it
+// computes the current one (NIT 1 KiB units per row), so the loads of six
+// waves cover the memory latency without the LDS ring; the loader meanwhile
+// prefetches the following instructions' pages.
+template <int NIT>
+DEV bool egu_direct(Comp& c, InstrCP I, uint32_t i) {
+  constexpr int D = 3;
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane, K = I->k;
+  const int rt = rt_base(I->layer);
+  const uint32_t nsel = *lw(rt + RT_NSEL), npu = I->aux[3];
+  const uint32_t Fe = uint32_t(a.expert_ffn), k = uint32_t(a.top_k), rb = I->row_bytes;
+  const uint64_t stride = I->seg_stride[0], gate0 = I->seg_ptr[1], up0 = I->seg_ptr[2];
+  const float inv = inv_rms(a, I);
+  const float my_inv = __shfl(inv, int(lane & 7), 64);
+  const float* xs = reinterpret_cast<const float*>(lds + lb::kX);
+  float* out = reinterpret_cast<float*>(I->out_ptr);
+  const uint32_t n_items = nsel * npu;
+  u4 wg[D][NIT], wu[D][NIT];
+  auto issue = [&](int slot_unused, uint32_t t, u4 (&g)[NIT], u4 (&u)[NIT]) {
+    (void)slot_unused;
+    if (t >= n_items) return;
+    const uint32_t er = t / npu, p = t % npu;
+    const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
+    const u4* gs = reinterpret_cast<const u4*>(gate0 + e * stride + uint64_t(p) * rb) + lane;
+    const u4* us = reinterpret_cast<const u4*>(up0 + e * stride + uint64_t(p) * rb) + lane;
+#pragma unroll
+    for (int j = 0; j < NIT; j++) {
+      g[j] = __builtin_nontemporal_load(gp(gs + 64 * j));
+      u[j] = __builtin_nontemporal_load(gp(us + 64 * j));
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < D - 1; s++) issue(s, c.w + kNComp * s, wg[s], wu[s]);
+  for (uint32_t i0 = 0;; i0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; s++) {
+      const uint32_t t = c.w + kNComp * (i0 + s);
+      if (t >= n_items) goto done;
+      issue((s + D - 1) % D, t + kNComp * (D - 1), wg[(s + D - 1) % D], wu[(s + D - 1) % D]);
+      const uint32_t er = t / npu, p = t % npu;
+      const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
+      const uint32_t tm = uni(rt_u8(rt, RT_TOK + int(e)));
+      float acc[16];
+#pragma unroll
+      for (int q = 0; q < 16; q++) acc[q] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NIT; j++) {
+#pragma unroll
+        for (int b = 0; b < lb::kMaxB; b++) {
+          if (!((tm >> b) & 1)) continue;
+          float x[8];
+          x8_ld(xs + uint32_t(b) * K + j * 512 + lane * 8, x);
+          acc[b] += dot8(wg[s][j], x);
+          acc[8 + b] += dot8(wu[s][j], x);
+        }
+      }
+      const float sv = reduce16(acc);
+      const float upv = __shfl(sv, int((lane & 7) + 8), 64);
+      if (lane < 8 && ((tm >> lane) & 1)) {
+        const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + lane));
+        const float m = silu(sv * my_inv) * (upv * my_inv);
+        st_act(out + (size_t(lane) * k + slot) * Fe + I->row0 + p, m);
+      }
+    }
+  }
+done:
+  if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
+  return true;
+}
+
 // ---------------------------------------------------- expert down projection
 // The routed (expert, sequence) pairs, in expert then sequence order, are
 // staged into the x slot in groups of cap = 16384 / K pairs (an expert's
@@ -847,6 +920,7 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
     }
     uint32_t np = I->n_pages;
     if (op == OP_EGU || op == OP_EDN) np = *lw(rt_base(I->layer) + RT_NSEL) * I->aux[2];
+    if (i_flags(I) & F_DIRECT) np = 0;
     bool ok = true;
     if (op == OP_BGEMV || op == OP_EGU) {
       const uint32_t fl = i_flags(I) & (F_IN_EMBED | F_NORM);
@@ -868,7 +942,14 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       staged_flags = fl;
       staged_k = I->k;
       staged_gain = I->gain_ptr;
-      ok = op == OP_BGEMV ? bgemv(c, I, i, pg) : egu(c, I, i, pg);
+      if (op == OP_BGEMV) {
+        ok = bgemv(c, I, i, pg);
+      } else if (i_flags(I) & F_DIRECT) {
+        const uint32_t nit = i_nit(I);
+        ok = nit == 4 ? egu_direct<4>(c, I, i) : nit == 2 ? egu_direct<2>(c, I, i) : egu_direct<1>(c, I, i);
+      } else {
+        ok = egu(c, I, i, pg);
+      }
     } else {
       staged_in = 0;
       ok = op == OP_EDN ? edn(c, I, i, pg) : run_attn_b<G>(c, I, i, pg);

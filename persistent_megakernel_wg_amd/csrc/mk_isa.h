@@ -109,6 +109,8 @@ enum Flag : uint16_t {
   F_OWN_POS = 32,     // (attention) placeholder, decided at run time
   F_ROUTE = 64,       // (experts) first expert instruction of its layer on the CU:
                       // take the top-k routing decision from the router logits
+  F_DIRECT = 128,     // (expert gate/up) the compute waves load the weight rows
+                      // themselves; the instruction takes no LDS pages
 };
 
 constexpr uint32_t kNoCounter = 0xFFFFFFFFu;

@@ -127,7 +127,8 @@ static mk_status check_config_moe(const mk_config& c, std::string* err) {
     return unsup("config: hidden, n_q_heads*head_dim and expert_ffn must be multiples of 512");
   if (int64_t(c.batch) * std::max(c.hidden, q) > lb::kXFloats)
     return unsup("config: batch * max(hidden, n_q_heads*head_dim) must be at most 16384");
-  if (c.expert_ffn > lb::kXFloats / lb::kMaxB) return unsup("config: expert_ffn must be at most 2048");
+  if (c.expert_ffn != 512 && c.expert_ffn != 1024 && c.expert_ffn != 2048)
+    return unsup("config: expert_ffn must be 512, 1024 or 2048");
   const int hpg = c.n_q_heads / c.n_kv_heads;
   if ((hpg & (hpg - 1)) || hpg > 8 || hpg * c.head_dim > 512)
     return unsup("config: query heads per KV group must be 1, 2, 4 or 8, with at most 512 query values per group");
@@ -502,7 +503,10 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.nit = uint8_t(d / 512);
         I.rpu = 1;
         I.layer = uint16_t(l);
-        I.flags = F_NORM | F_SIGNAL | (l == 0 ? F_IN_EMBED : 0) | (routed[cu] ? 0 : F_ROUTE);
+        // rows of at most 4 KiB are loaded by the compute waves directly
+        const bool direct = d / 512 == 1 || d / 512 == 2 || d / 512 == 4;
+        I.flags = F_NORM | F_SIGNAL | (l == 0 ? F_IN_EMBED : 0) | (routed[cu] ? 0 : F_ROUTE) |
+                  (direct ? F_DIRECT : 0);
         routed[cu] = 1;
         I.n_items = uint32_t(npu);
         I.row0 = uint32_t(p0);
@@ -524,7 +528,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.gain_ptr = lptr(in.w.attn_norm, l, d);
         I.wait_ctr[0] = c_rt[l];
         I.sig_ctr = c_gu[l];
-        I.n_pages = uint32_t(E * ppe);
+        I.n_pages = direct ? 0 : uint32_t(E * ppe);
         InstrMeta m;
         m.stage = stg + ST_ATTN;
         m.merge_write = false;
@@ -1220,7 +1224,10 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         if (I.k % 512 || I.nit != I.k / 512 || I.row_bytes != 2 * I.k) return fail("expert row geometry");
         if (uint64_t(ppe) * kPageBytes < uint64_t(runs) * I.seg_rows[0] || ppe > uint32_t(lb::kPages) - 1)
           return fail("expert page regions");
-        if (I.n_pages != ppe * I.aux[4] || I.aux[4] != uint32_t(c.n_experts)) return fail("expert page budget");
+        if (I.n_pages != ((I.flags & F_DIRECT) ? 0 : ppe * I.aux[4]) || I.aux[4] != uint32_t(c.n_experts))
+          return fail("expert page budget");
+        if ((I.flags & F_DIRECT) && (I.op != OP_EGU || (I.nit != 1 && I.nit != 2 && I.nit != 4)))
+          return fail("direct expert loads");
         if (I.op == OP_EGU && I.seg_rows[0] != I.aux[3] * I.row_bytes) return fail("expert gate/up runs");
         if (I.op == OP_EDN && (I.seg_rows[0] != I.aux[3] * I.row_bytes || I.aux[3] > uint32_t(lb::kMaxDnRows) ||
                                uint64_t(I.aux[3]) * c.batch > uint64_t(kMaxResRows) || I.aux[3] != I.n_rows))
