@@ -10,8 +10,10 @@
  * top-k experts of every token, their softmax weights sum the experts' SwiGLU
  * outputs) for B <= 8 sequences per step, each streamed weight byte applied to
  * every sequence that uses it.  Each workgroup interprets a host-built queue of tile-sized
- * instructions; instructions wait on each other through counters in global
- * memory instead of kernel boundaries.  This follows the design described in
+ * instructions; instructions wait on each other instead of on kernel
+ * boundaries: every activation element carries the step that wrote it, so a
+ * consumer polls its inputs until they are this step's (data without such a
+ * tag sits behind counters in global memory).  This follows the design described in
  * Hazy Research's Llama-1B megakernel write-up ("Fusing Operations with an
  * On-GPU Interpreter", "Efficient Shared Memory Management" and "Custom
  * Synchronization Mechanism" in the rocketrecap.com summary) and the persistent
@@ -50,7 +52,7 @@ typedef enum {
   MK_ERR_NO_PLAN = -3,     /* mk_decode_step before mk_build_plan           */
   MK_ERR_UNSUPPORTED = -4, /* shape the kernel has no code path for         */
   MK_ERR_OOM = -5,         /* device allocation failed                      */
-  MK_ERR_TIMEOUT = -6,     /* a counter wait exceeded the watchdog          */
+  MK_ERR_TIMEOUT = -6,     /* a device wait exceeded the watchdog           */
   MK_ERR_DEVICE = -7       /* the kernel reported an error (e.g. NaN logits)*/
 } mk_status;
 
@@ -105,16 +107,20 @@ typedef struct {
 typedef struct {
   int32_t n_cus;      /* workgroups = CUs used (default: all CUs of the device) */
   int32_t mlp_chunks; /* MLP intermediate split into this many chunks, each with
-                         its own counter so down-projection tiles start early
+                         staged on its own so down-projection tiles start early
                          (the Llama-1B megakernel write-up, "Custom
                          Synchronization Mechanism", uses 4).  Default: the
                          fewest chunks of at most 4096 values each, since
                          every chunk adds two instructions per CU */
   int32_t attn_block; /* KV positions per attention tile (multiple of 64;
                          default: chosen from max_seq and the CU count) */
-  int32_t watchdog_ms;/* counter-wait limit before MK_ERR_TIMEOUT (default 2000) */
-  int32_t debug_corrupt_target; /* tests only: 1 raises one wait target so the
-                                   step must end in MK_ERR_TIMEOUT */
+  int32_t watchdog_ms;/* limit of any one wait on the device (a counter, a
+                         step-tagged input, an LDS page or barrier) before
+                         the step ends in MK_ERR_TIMEOUT (default 2000) */
+  int32_t debug_corrupt_target; /* tests only: 1 makes one instruction wait for
+                                   a counter target and an input tag that the
+                                   step never reaches, so the step must end in
+                                   MK_ERR_TIMEOUT */
   int32_t generic_kernel; /* 1: always launch the kernel built for every shape
                              (default 0: the kernel built for this shape when
                              the library has one; see kernel_variant) */

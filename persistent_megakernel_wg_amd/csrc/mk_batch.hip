@@ -82,7 +82,7 @@ DEV bool route_topk(const KArgs& a, InstrCP I, uint64_t& mask, int table, uint32
   auto off = [&](int, int j) -> uint32_t { return (b * E + 8 * s + uint32_t(j)) * kActBytes; };
 #pragma unroll
   for (int j = 0; j < 8; j++) reload(t[j], r, off(0, j));
-  if (!wait_fresh(t, live, r, off, 0, a.epoch, retries)) return false;
+  if (!wait_fresh(t, live, r, off, 0, in_tag(a, I), retries)) return false;
   float v[8];
 #pragma unroll
   for (int j = 0; j < 8; j++) {
@@ -404,7 +404,7 @@ DEV bool coop_stage_b(Comp& c, InstrCP I, uint32_t i, bool stage_x) {
     }
   }
   if (stage_x) {
-    if (!embed && !wait_fresh(t, live, r, off, 0, a.epoch, c.retries)) return false;
+    if (!embed && !wait_fresh(t, live, r, off, 0, in_tag(a, I), c.retries)) return false;
     if (!wait_all_ge(C_XCONS, i)) return false;
     float* xs = reinterpret_cast<float*>(lds + lb::kX);
     float* ss = reinterpret_cast<float*>(lds + lb::kSS);
@@ -449,7 +449,7 @@ DEV bool stage_res_b(Comp& c, InstrCP I, uint32_t i, uint32_t n_rows, uint32_t r
     }
   }
   const uint32_t live = 2 * lane >= total ? 0 : (2 * lane + 1 < total ? 2 : 1);
-  if (!embed && !wait_fresh(t, live, rr, [&](int, int j) { return offs[j]; }, 0, a.epoch, c.retries))
+  if (!embed && !wait_fresh(t, live, rr, [&](int, int j) { return offs[j]; }, 0, in_tag(a, I), c.retries))
     return false;
   float* rs = const_cast<float*>(res_slot_b(i));
   for (int j = 0; j < 2; j++)

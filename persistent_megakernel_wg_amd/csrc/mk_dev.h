@@ -297,8 +297,9 @@ DEV bool local_timeout(Watch& w, uint64_t limit) {
 }
 DEV void local_abort(uint32_t code) {
   uint32_t expected = 0;
-  __hip_atomic_compare_exchange_strong(gp(status_ptr()) + ST_CODE, &expected, code, __ATOMIC_RELAXED,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__hip_atomic_compare_exchange_strong(gp(status_ptr()) + ST_CODE, &expected, code, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    __hip_atomic_store(gp(status_ptr()) + ST_CU, uint32_t(blockIdx.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   lds_st(C_ABORT, 1);
 }
 
@@ -878,9 +879,9 @@ DEV void attn_merge(Comp& c, InstrCP I) {
 
 // ---- staging of the instruction's inputs into the LDS x slot (leader wave)
 // Re-read tagged entries of `t` (the first `live` of this lane) until every
-// one holds the current step's tag.  The producer's counter has already
-// moved, so a stale entry is a store still in flight; the wait is bounded by
-// the workgroup's local watchdog.  T is u4 (two elements) or uint2 (one).
+// one holds the current step's tag: a stale entry is a row its producer has
+// not stored yet, or a store still in flight.  The wait is bounded by the
+// watchdog limit.  T is u4 (two elements) or uint2 (one).
 DEV bool is_fresh(const u4& t, uint32_t tag) { return t.y == tag && t.w == tag; }
 DEV bool is_fresh(const uint2& t, uint32_t tag) { return t.y == tag; }
 DEV void reload(u4& t, __amdgpu_buffer_rsrc_t r, uint32_t off) { t = ld_tag2(r, off); }
@@ -898,16 +899,22 @@ DEV bool wait_fresh(T (&t)[N], uint32_t live, __amdgpu_buffer_rsrc_t r, Off off,
       if (j < int(live) && !is_fresh(t[j], tag)) ok = false;
     if (__builtin_amdgcn_ballot_w64(!ok) == 0) return true;
     retries++;
+#ifdef MK_POLL_SLEEP
+    __builtin_amdgcn_s_sleep(MK_POLL_SLEEP);
+#endif
 #pragma unroll
     for (int j = 0; j < N; j++)
       if (j < int(live) && !is_fresh(t[j], tag)) reload(t[j], r, off(h, j));
     if (aborted()) return false;
     if (local_timeout(wt, local_limit())) {
-      local_abort(STC_LOCAL_TIMEOUT);
+      local_abort(STC_TAG_TIMEOUT);
       return false;
     }
   }
 }
+
+// The tag that an instruction's inputs carry once this step has written them.
+DEV uint32_t in_tag(const KArgs& a, InstrCP I) { return a.epoch + ((i_flags(I) & F_DEBUG_STALL) ? 1u : 0u); }
 
 // Leader staging of an attention tile: the tile's q, the group's k and v
 // (tagged) and cos | sin of the position into the x slot.  Every load is
@@ -916,7 +923,7 @@ template <class Lay>
 DEV bool stage_attn(Comp& c, InstrCP I) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane;
-  const uint32_t tag = a.epoch;
+  const uint32_t tag = in_tag(a, I);
   float* xs = reinterpret_cast<float*>(lds + Lay::x);
   {
       // attention: q, k, v of the group (tagged) and cos | sin (tables)

@@ -111,6 +111,8 @@ enum Flag : uint16_t {
                       // take the top-k routing decision from the router logits
   F_DIRECT = 128,     // (expert gate/up) the compute waves load the weight rows
                       // themselves; the instruction takes no LDS pages
+  F_DEBUG_STALL = 256,  // tests only: staging expects the next step's tag, so the
+                        // inputs never turn fresh and the watchdog ends the step
 };
 
 constexpr uint32_t kNoCounter = 0xFFFFFFFFu;
@@ -231,6 +233,6 @@ enum TraceWord { TR_START = 0, TR_DEPS = 1, TR_STAGED = 2, TR_ITEMS = 3, TR_SIGN
 // status words
 enum StatusWord { ST_CODE = 0, ST_CU = 1, ST_INSTR = 2, ST_CTR = 3, ST_SEEN = 4, ST_TARGET = 5,
                   ST_NAN = 6, ST_BADTOK = 7 };
-enum StatusCode { STC_OK = 0, STC_TIMEOUT = 1, STC_LOCAL_TIMEOUT = 2 };
+enum StatusCode { STC_OK = 0, STC_TIMEOUT = 1, STC_LOCAL_TIMEOUT = 2, STC_TAG_TIMEOUT = 3 };
 
 }  // namespace mk

@@ -272,7 +272,7 @@ DEV bool stage_leader(Comp& c, InstrCP I, uint32_t i) {
 DEV bool coop_stage(Comp& c, InstrCP I, uint32_t i, bool stage_x) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane;
-  const uint32_t tag = a.epoch;
+  const uint32_t tag = in_tag(a, I);
   constexpr int NC = (kMaxK / 128 + kNComp - 1) / kNComp;
   static_assert(kMaxResRows == 128, "residual staging takes two rows per lane");
   const uint32_t K = I->k, nch = K / 128;
@@ -467,7 +467,6 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
   uint64_t staged_in = 0;
   uint32_t staged_flags = 0, staged_k = 0;
   uint64_t staged_gain = 0;
-  uint32_t seen_ctr = kNoCounter, seen_val = 0;  // leader: last satisfied wait
   for (uint32_t i = 0; i < n; i++) {
     InstrCP I = q + i;
     const bool is_gemv = i_op(I) == OP_GEMV;
@@ -486,26 +485,17 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       }
       c.pagewait = 0;
       c.retries = 0;
-      bool ok = true;
-      for (int k = 0; k < 2 && ok; k++) {
-        if (!I->wait_cnt[k]) continue;
-        const uint32_t ctr = I->wait_ctr[k], target = a.epoch * I->wait_cnt[k];
-        if (ctr == seen_ctr && int32_t(seen_val - target) >= 0) continue;  // already satisfied
-        ok = wait_counter(a, ctr, target, cu, i);
-        seen_ctr = ctr;
-        seen_val = target;
-      }
-      if (!ok) {
-        if (c.lane == 0) lds_st(C_ABORT, 1);
-        return;
-      }
-      if (c.lane == 0) lds_st(C_DEPOK, i + 1);
+      // No counter wait: every input of this kernel behind a producer is
+      // tagged per element with the step (activations) or sits behind a
+      // ticket (attention partials, argmax slots), and every activation
+      // buffer is written once per step.  Staging polls the tags of the
+      // elements it reads and re-reads only the stale ones, so it starts
+      // while the producers' last rows are still in flight instead of a
+      // counter round trip after the last of them.
       if (tr && c.lane == 0) trace_put(a, cu, i, TR_DEPS, now32());
     }
     if (coop) {
-      // inputs ready in memory (the leader saw the counters), then every
-      // wave stages its share; a barrier publishes the x slot
-      if (w != 0 && !wait_lds_ge(C_DEPOK, i + 1)) return;
+      // every wave stages its share; a barrier publishes the x slot
       if (!reuse || needs_res(I)) {
         if (!coop_stage(c, I, i, !reuse)) {
           if (c.lane == 0) lds_st(C_ABORT, 1);

@@ -1546,11 +1546,13 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
 }
 
 void corrupt_one_target(Plan* p) {
-  // raise the target of the first waiting instruction of the last CU queue
+  // the first waiting instruction of the last CU queue: raise its counter
+  // target and make its staging expect a tag that this step never writes
   for (int cu = p->n_cus - 1; cu >= 0; cu--)
     for (uint32_t i = p->q_off[cu]; i < p->q_off[cu + 1]; i++)
       if (p->instrs[i].wait_ctr[0] != kNoCounter) {
         p->instrs[i].wait_cnt[0] += 1;
+        p->instrs[i].flags |= F_DEBUG_STALL;
         return;
       }
 }

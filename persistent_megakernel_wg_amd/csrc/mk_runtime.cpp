@@ -299,7 +299,10 @@ mk_status mk_sync(mk_ctx* c) {
                   stw[mk::ST_CU], stw[mk::ST_INSTR], stw[mk::ST_CTR], stw[mk::ST_SEEN], stw[mk::ST_TARGET]);
     st = MK_ERR_TIMEOUT;
   } else if (stw[mk::ST_CODE] == mk::STC_LOCAL_TIMEOUT) {
-    std::snprintf(msg, sizeof(msg), "watchdog: a workgroup stalled on its own LDS pages or barrier");
+    std::snprintf(msg, sizeof(msg), "watchdog: workgroup %u stalled on its own LDS pages or barrier", stw[mk::ST_CU]);
+    st = MK_ERR_TIMEOUT;
+  } else if (stw[mk::ST_CODE] == mk::STC_TAG_TIMEOUT) {
+    std::snprintf(msg, sizeof(msg), "watchdog: workgroup %u waited on inputs this step never wrote", stw[mk::ST_CU]);
     st = MK_ERR_TIMEOUT;
   } else if (stw[mk::ST_BADTOK]) {
     std::snprintf(msg, sizeof(msg), "device: input token outside [0, vocab)");
