@@ -876,7 +876,12 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       }
       c.retries = 0;
       bool ok = true;
-      for (int k = 0; k < 2 && ok; k++) {
+      // Only the expert down projection waits on counters: its input (the
+      // expert intermediates) is untagged fp32 behind release increments.
+      // Every other input is tagged per element with the step, and staging
+      // polls those tags instead, starting while the producers' last rows
+      // are still in flight.
+      for (int k = 0; k < 2 && ok && op == OP_EDN; k++) {
         if (!I->wait_cnt[k]) continue;
         const uint32_t ctr = I->wait_ctr[k], target = a.epoch * I->wait_cnt[k];
         if (ctr == seen_ctr && int32_t(seen_val - target) >= 0) continue;

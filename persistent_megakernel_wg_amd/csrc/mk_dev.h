@@ -899,9 +899,6 @@ DEV bool wait_fresh(T (&t)[N], uint32_t live, __amdgpu_buffer_rsrc_t r, Off off,
       if (j < int(live) && !is_fresh(t[j], tag)) ok = false;
     if (__builtin_amdgcn_ballot_w64(!ok) == 0) return true;
     retries++;
-#ifdef MK_POLL_SLEEP
-    __builtin_amdgcn_s_sleep(MK_POLL_SLEEP);
-#endif
 #pragma unroll
     for (int j = 0; j < N; j++)
       if (j < int(live) && !is_fresh(t[j], tag)) reload(t[j], r, off(h, j));
