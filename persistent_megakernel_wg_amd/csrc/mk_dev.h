@@ -219,6 +219,15 @@ DEV float group_sum(float v) {
   if (G == 16) v += dpp<0x108>(v); // row_shl:8
   return v;
 }
+// sum over aligned groups of G (8 or 16) lanes, in every lane of the group
+template <int G>
+DEV float group_allsum(float v) {
+  v += dpp<0xB1>(v);                // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);                // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);               // row_half_mirror: the other quad of the 8
+  if (G == 16) v += dpp<0x140>(v);  // row_mirror: the other 8 of the row
+  return v;
+}
 template <int CTRL>
 DEV float dpp_max(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -596,9 +605,9 @@ DEV void arg_update(ArgBest& b, float v, uint32_t i) {
 
 // ---- attention: one KV group, one position block
 // The x slot holds, staged by the leader: q [HPT*Dh] of the tile's heads | k [Dh] | v [Dh] of the
-// group | cos [Dh/2] | sin [Dh/2] of the position.  After the query and the
-// new row are in registers the x slot is reused for the value-pass partials,
-// so the instruction releases it (C_XCONS) only at its end.
+// group | cos [Dh/2] | sin [Dh/2] of the position.  The waves' softmax
+// records go to the x slot after those inputs, so the instruction releases
+// the slot (C_XCONS) only at its end.
 template <int HPT, int DH, class Lay>
 DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
   const KArgs& a = *c.a;
@@ -607,8 +616,7 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
   constexpr int UPOS = kUnit / (2 * DH);  // rows per 1 KiB unit
   constexpr int HALF = DH / 2;
   constexpr int OUT = HPT * DH;           // outputs of the group
-  constexpr int PER = OUT / 64;           // value-pass outputs per lane
-  static_assert(PER >= 1 && PER <= 8 && OUT * kNComp <= Lay::x_floats, "attention shape");
+  static_assert(64 % LPRA == 0 && HPT >= 1 && HPT <= 8, "attention shape");
   const uint32_t g = I->aux[0], blk = I->aux[1], Bat = I->aux[2], nblk = I->aux[3], kp = I->aux[4];
   const uint32_t h0 = I->row0;                  // first query head of the tile in its group
   const uint32_t head0 = g * uint32_t(a.hpg) + h0;  // ... in the layer
@@ -617,12 +625,7 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
   int32_t nc = P - p0;
   nc = nc < 0 ? 0 : (nc > int32_t(Bat) ? int32_t(Bat) : nc);
   const bool own = P >= p0 && P < p0 + int32_t(Bat);
-  const int32_t ntot = nc + (own ? 1 : 0);
   float* xs = reinterpret_cast<float*>(lds + Lay::x);
-  float* scores = reinterpret_cast<float*>(lds + Lay::attn);     // [HPT][Bat]
-  uint16_t* newv = reinterpret_cast<uint16_t*>(lds + Lay::attn + 4 * Lay::score_floats);
-  float* stat_m = reinterpret_cast<float*>(lds + Lay::attn + 4 * Lay::score_floats + 512);
-  float* stat_l = stat_m + 8;
   const float* cs = xs + HPT * DH + 2 * DH;
   const float* sn = cs + HALF;
   const uint32_t s = lane % LPRA;        // dims [8s, 8s+8)
@@ -670,30 +673,60 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
   }
   if (trl) trace_put(a, c.cu, i, TR_XREADY, now32());
 
-  // pass 1: scores of cached rows (units round-robin over the compute waves);
-  // the wave after the last unit's scores the new row and appends it
+  // One pass per wave, softmax online: wave w takes the position units
+  // u = w (mod waves); in a unit, lane group jrow holds row u*UPOS + jrow,
+  // its lanes 8 dims each of k and v.  Every lane group keeps, per head, the
+  // running maximum m, the sum l of exp(score - m) and o~ = sum exp(score - m)
+  // v over its rows; the groups of a wave, then the waves, are merged by the
+  // log-sum-exp rule.  The wave after the last unit's takes the new row.
   const uint32_t n_units = (uint32_t(nc) + UPOS - 1) / UPOS;
+  float m[HPT], l[HPT], acc[HPT][8];
+#pragma unroll
+  for (int h = 0; h < HPT; h++) {
+    m[h] = -__builtin_inff();
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[h][e] = 0.f;
+  }
+  // one exponential per row: exp(-|score - m|) is the new row's weight when
+  // the maximum stays, and the rescale of the old sums when it moves
+  auto update = [&](int h, float sc, const float (&v)[8]) {
+    const bool up = sc > m[h];
+    const float d = __expf(-fabsf(sc - m[h]));  // m = -inf: exp(-inf) = 0
+    const float sa = up ? d : 1.f, w = up ? 1.f : d;
+    l[h] = fmaf(l[h], sa, w);
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[h][e] = fmaf(acc[h][e], sa, w * v[e]);
+    m[h] = up ? sc : m[h];
+  };
   for (uint32_t u = c.w; u < n_units; u += kNComp) {
-    if (!wait_page(page0 + u / kUnitsPerPage, c.fcache)) return false;
-    const u4 kw = *reinterpret_cast<const u4*>(lds + page_off<Lay>(page0 + u / kUnitsPerPage) +
-                                               (u % kUnitsPerPage) * kUnit + lane * 16);
-    const uint32_t p = u * UPOS + jrow;
+    // the v unit streams after every k unit of the tile
+    if (!wait_page(page0 + kp + u / kUnitsPerPage, c.fcache)) return false;
+    const uint32_t lo = (u % kUnitsPerPage) * kUnit + lane * 16;
+    const u4 kw = *reinterpret_cast<const u4*>(lds + page_off<Lay>(page0 + u / kUnitsPerPage) + lo);
+    const u4 vw = *reinterpret_cast<const u4*>(lds + page_off<Lay>(page0 + kp + u / kUnitsPerPage) + lo);
+    const bool valid = u * UPOS + jrow < uint32_t(nc);
+    const float v[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
+                        bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
 #pragma unroll
     for (int h = 0; h < HPT; h++) {
-      const float d = group_sum<LPRA>(dot8(kw, qr[h]));
-      if (s == 0 && p < uint32_t(nc)) scores[h * Bat + p] = d;
+      const float sc = group_allsum<LPRA>(dot8(kw, qr[h]));
+      if (valid) update(h, sc, v);
     }
   }
   if (own && uint32_t(c.w) == n_units % kNComp) {
     // (every tile of the group scores the new row; the one holding the
     // group's first head appends it to the cache)
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) v[e] = __uint_as_float(uint32_t(vb[e]) << 16);
 #pragma unroll
     for (int h = 0; h < HPT; h++) {
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e++) d = fmaf(qr[h][e], kn[e], d);
-      d = group_sum<LPRA>(d);
-      if (lane == 0) scores[h * Bat + nc] = d;
+      d = group_allsum<LPRA>(d);
+      if (jrow == 0) update(h, d, v);
     }
     if (lane < uint32_t(LPRA) && h0 == 0) {
       const size_t row = size_t(P) * DH + 8 * s;
@@ -707,107 +740,76 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
       *gp(reinterpret_cast<u4*>(kc)) = kk;
       *gp(reinterpret_cast<u4*>(vc)) = vv;
     }
-    if (lane < uint32_t(LPRA)) {
-#pragma unroll
-      for (int e = 0; e < 8; e++) newv[8 * s + e] = vb[e];
-    }
-  }
-  if (trl) trace_put(a, c.cu, i, TR_ITEM0, now32());
-  if (!comp_barrier()) return false;
-  if (trl) trace_put(a, c.cu, i, TR_A_PASS1, now32());
-
-  // pass 2: per head (heads round-robin over the waves) the maximum, the
-  // weights exp(score - max) in place of the scores, and their sum
-  for (int h = c.w; h < HPT; h += kNComp) {
-    float m = -__builtin_inff();
-    for (int32_t p = lane; p < ntot; p += 64) m = fmaxf(m, scores[h * Bat + p]);
-    m = max64(m);
-    float l = 0.f;
-    for (int32_t p = lane; p < ntot; p += 64) {
-      const float e = __expf(scores[h * Bat + p] - m);
-      scores[h * Bat + p] = e;
-      l += e;
-    }
-    l = sum64(l);
-    if (lane == 0) {
-      stat_m[h] = m;
-      stat_l[h] = l;
-    }
-  }
-  if (!comp_barrier()) return false;
-  if (trl) trace_put(a, c.cu, i, TR_A_STATS, now32());
-
-  // pass 3: o~ = sum_p w_p V_p; wave w takes positions p = w (mod waves),
-  // lane l the PER consecutive outputs from l*PER (one head); per-wave
-  // partials go to the x slot
-  const uint32_t o0 = lane * PER, h3 = o0 / DH, d3 = o0 % DH;
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; e++) acc[e] = 0.f;
-  if (kp && !wait_page(page0 + 2 * kp - 1, c.fcache)) return false;
-  // this lane's PER values of V row p (cached rows from the pages, the new
-  // row from LDS), as bf16 pairs
-  auto v_of = [&](int32_t p, uint32_t (&vw)[(PER + 1) / 2]) {
-    const char* vrow;
-    if (p < nc) {
-      const uint32_t off = uint32_t(p) * (2 * DH) + 2 * d3;
-      vrow = lds + page_off<Lay>(page0 + kp + off / kPageBytes) + (off % kPageBytes);
-    } else {
-      vrow = reinterpret_cast<const char*>(newv + d3);
-    }
-    if constexpr (PER == 8) {
-      const u4 t = *reinterpret_cast<const u4*>(vrow);
-      vw[0] = t.x; vw[1] = t.y; vw[2] = t.z; vw[3] = t.w;
-    } else if constexpr (PER == 4) {
-      const uint2 t = *reinterpret_cast<const uint2*>(vrow);
-      vw[0] = t.x; vw[1] = t.y;
-    } else if constexpr (PER == 2) {
-      vw[0] = *reinterpret_cast<const uint32_t*>(vrow);
-    } else {
-      vw[0] = *reinterpret_cast<const uint16_t*>(vrow);
-    }
-  };
-  // four positions per step, all LDS reads issued before the FMAs
-  constexpr int U = 4;
-  for (int32_t p = c.w; p < ntot; p += U * kNComp) {
-    float wp[U];
-    uint32_t vw[U][(PER + 1) / 2];
-#pragma unroll
-    for (int k = 0; k < U; k++) {
-      const int32_t pk = p + k * kNComp;
-      const int32_t pc = pk < ntot ? pk : p;  // past the end: re-read p, weight 0
-      wp[k] = pk < ntot ? scores[h3 * Bat + pc] : 0.f;
-      v_of(pc, vw[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < U; k++)
-#pragma unroll
-      for (int e = 0; e < PER; e++)
-        acc[e] = fmaf(wp[k], (e & 1) ? bf_hi(vw[k][e / 2]) : bf_lo(vw[k][e / 2]), acc[e]);
   }
   if (lane == 0) lds_st(C_RELEASED + 4 * c.w, page0 + I->n_pages);
+  if (trl) trace_put(a, c.cu, i, TR_ITEM0, now32());
+  // merge the lane groups of the wave (butterfly: every lane ends with the
+  // same result)
+  auto merge = [&](int h, float mo, float lo_, const float (&ao)[8]) {
+    const float mn = fmaxf(m[h], mo);
+    const float sa = m[h] == -__builtin_inff() ? 0.f : __expf(m[h] - mn);
+    const float sb = mo == -__builtin_inff() ? 0.f : __expf(mo - mn);
+    l[h] = l[h] * sa + lo_ * sb;
 #pragma unroll
-  for (int e = 0; e < PER; e++) xs[c.w * OUT + o0 + e] = acc[e];
+    for (int e = 0; e < 8; e++) acc[h][e] = acc[h][e] * sa + ao[e] * sb;
+    m[h] = mn;
+  };
+#pragma unroll
+  for (int off = LPRA; off < 64; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < HPT; h++) {
+      float ao[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) ao[e] = __shfl_xor(acc[h][e], off, 64);
+      const float mo = __shfl_xor(m[h], off, 64), lo_ = __shfl_xor(l[h], off, 64);
+      merge(h, mo, lo_, ao);
+    }
+  }
+  // the wave's record per head after the staged inputs: o~ [DH] | m | l
+  constexpr int REC = DH + 2;
+  constexpr int PBASE = (HPT * DH + 3 * DH + 3) & ~3;
+  static_assert(PBASE + kNComp * HPT * REC <= Lay::x_floats, "attention partials");
+  float* wrec = xs + PBASE;
+  if (lane < uint32_t(LPRA)) {
+#pragma unroll
+    for (int h = 0; h < HPT; h++) {
+      float* r = wrec + (c.w * HPT + h) * REC;
+      *reinterpret_cast<f4*>(r + 8 * s) = f4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+      *reinterpret_cast<f4*>(r + 8 * s + 4) = f4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+      if (s == 0) {
+        r[DH] = m[h];
+        r[DH + 1] = l[h];
+      }
+    }
+  }
   if (!comp_barrier()) return false;
   if (trl) trace_put(a, c.cu, i, TR_A_PASS3, now32());
 
-  // final: sum the wave partials in order, normalise, store
+  // final: merge the waves' records in order, normalise, store
   for (uint32_t o = c.w * 64 + lane; o < uint32_t(OUT); o += 64 * kNComp) {
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kNComp; w++) sum += xs[w * OUT + o];
     const uint32_t h = o / DH, d = o % DH;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kNComp; w++) M = fmaxf(M, wrec[(w * HPT + h) * REC + DH]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNComp; w++) {
+      const float* r = wrec + (w * HPT + h) * REC;
+      const float sw = r[DH] == -__builtin_inff() ? 0.f : __expf(r[DH] - M);
+      num = fmaf(sw, r[d], num);
+      den = fmaf(sw, r[DH + 1], den);
+    }
     const uint32_t head = head0 + h;
     if (nblk == 1) {
-      st_tag(reinterpret_cast<uint64_t*>(I->out_ptr) + head * DH + d, sum / stat_l[h], a.epoch);
+      st_tag(reinterpret_cast<uint64_t*>(I->out_ptr) + head * DH + d, num / den, a.epoch);
     } else {
       // partial record of (head tile, block, head): o~ [DH] | m | l
       const size_t tg = head0 / HPT;
       float* part = reinterpret_cast<float*>(I->res_ptr) + ((tg * nblk + blk) * HPT + h) * (DH + 2);
-      st_act(part + d, sum);
+      st_act(part + d, num);
       if (d == 0) {
-        st_act(part + DH, stat_m[h]);
-        st_act(part + DH + 1, stat_l[h]);
+        st_act(part + DH, M);
+        st_act(part + DH + 1, den);
       }
     }
   }
