@@ -42,9 +42,6 @@ constexpr int kLdsX = 2048;          // staged input vector / q,k,v (16 KiB)
 constexpr int kLdsXBytes = 4 * kMaxK;
 constexpr int kLdsAttn = kLdsX + kLdsXBytes;   // attention scratch
 constexpr int kLdsAttnBytes = 12800;   // scores 8 KiB, new V row 512 B, partials 4 KiB
-// RMSNorm gain of a staged GEMV input (bf16), in the attention scratch
-constexpr int kLdsGain = kLdsAttn;
-static_assert(2 * kMaxK <= kLdsAttnBytes, "gain area");
 constexpr int kLdsPages = kLdsAttn + kLdsAttnBytes;
 // staged residual rows: two slots (by instruction parity) of 128 floats
 constexpr int kLdsRes = kLdsPages + kPages * kPageBytes;

@@ -71,10 +71,19 @@ DEV const float* res_slot(uint32_t i) {
   return reinterpret_cast<const float*>(lds + kLdsRes + (i & 1) * 4 * kMaxResRows);
 }
 
-DEV void epi_row(Comp& c, InstrCP I, uint32_t i, uint32_t t_row, uint32_t row, float v, ArgBest& best) {
+// instruction fields of the epilogue, read once per instruction
+struct EpiCtx {
+  uint64_t* out;
+  uint32_t epi, acc0, row0;
+};
+DEV EpiCtx epi_of(InstrCP I) {
+  return EpiCtx{reinterpret_cast<uint64_t*>(I->out_ptr), i_epi(I), I->aux[0], I->row0};
+}
+DEV void epi_row(Comp& c, const EpiCtx& E, uint32_t i, uint32_t t_row, float v, ArgBest& best) {
   const KArgs& a = *c.a;
-  uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
-  switch (i_epi(I)) {
+  uint64_t* out = E.out;
+  const uint32_t row = E.row0 + t_row;
+  switch (E.epi) {
     case EPI_STORE:
     case EPI_SWIGLU:
       st_tag(out + row, v, a.epoch);
@@ -84,13 +93,13 @@ DEV void epi_row(Comp& c, InstrCP I, uint32_t i, uint32_t t_row, uint32_t row, f
       st_tag(out + row, res_slot(i)[t_row] + v, a.epoch);
       break;
     case EPI_ACC_FIRST:
-      reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] = res_slot(i)[t_row] + v;
+      reinterpret_cast<float*>(lds + kLdsAcc)[E.acc0 + t_row] = res_slot(i)[t_row] + v;
       break;
     case EPI_ACC_MID:
-      reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] += v;
+      reinterpret_cast<float*>(lds + kLdsAcc)[E.acc0 + t_row] += v;
       break;
     case EPI_ACC_LAST:
-      st_tag(out + row, reinterpret_cast<float*>(lds + kLdsAcc)[I->aux[0] + t_row] + v, a.epoch);
+      st_tag(out + row, reinterpret_cast<float*>(lds + kLdsAcc)[E.acc0 + t_row] + v, a.epoch);
       break;
     case EPI_ARGMAX:
       if (a.logits) gp(a.logits)[row] = v;
@@ -116,47 +125,21 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
     xv[j][4] = hi.x; xv[j][5] = hi.y; xv[j][6] = hi.z; xv[j][7] = hi.w;
   }
   if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
+  // RMSNorm: the staged input is x * gain, and its row sums are scaled by
+  // 1 / rms(x), from the staged shares of the sum of squares
+  float inv = 1.f;
   if (i_flags(I) & F_NORM) {
-    // RMSNorm: every wave normalises its copy of the input with the staged
-    // gain.  A cooperatively staged input comes with the waves' shares of the
-    // sum of squares; the embedding input (leader staging) is summed here
-    // (every wave holds the whole input; RPU 2: each half-wave does).
     float ss = 0.f;
-    if (!(i_flags(I) & F_IN_EMBED)) {
 #pragma unroll
-      for (int w = 0; w < kNComp; w++) ss += *reinterpret_cast<const float*>(lds + kLdsSS + 4 * w);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NIT; j++)
-#pragma unroll
-        for (int e = 0; e < 8; e++) ss = fmaf(xv[j][e], xv[j][e], ss);
-      if (RPU == 1) {
-        ss = sum64(ss);
-      } else {
-        float lo, hi;
-        sum32x2(ss, lo, hi);
-        ss = lo;
-      }
-    }
-    const float inv = rsqrtf(ss / float(I->k) + a.rms_eps);
-    const uint16_t* gs = reinterpret_cast<const uint16_t*>(lds + kLdsGain);
-#pragma unroll
-    for (int j = 0; j < NIT; j++) {
-      const uint32_t col = RPU == 1 ? j * 512 + lane * 8 : (lane % LPR) * 8;
-      const u4 gv = *reinterpret_cast<const u4*>(gs + col);
-      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        xv[j][2 * e] *= inv * bf_lo(gw[e]);
-        xv[j][2 * e + 1] *= inv * bf_hi(gw[e]);
-      }
-    }
+    for (int w = 0; w < kNComp; w++) ss += *reinterpret_cast<const float*>(lds + kLdsSS + 4 * w);
+    inv = rsqrtf(ss / float(I->k) + a.rms_eps);
   }
   const bool trl = c.a->trace && c.w == 0 && lane == 0;
   if (trl) trace_put(a, c.cu, i, TR_XREADY, now32());
 
   const uint32_t n_items = I->n_items, page0 = I->page0;
   const bool pair = i_epi(I) == EPI_SWIGLU;
+  const EpiCtx E = epi_of(I);
   const uint32_t upi = RPU == 1 ? (pair ? 2 * NIT : NIT) : 1;
   ArgBest best{-__builtin_inff(), 0xFFFFFFFFu};
   for (uint32_t t = c.w; t < n_items; t += kNComp) {
@@ -183,19 +166,20 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
         for (int j = 0; j < NIT; j++) acc += dot8(wr[j], xv[j]);
         if (r == 0) acc0 = acc; else acc1 = acc;
       }
-      acc0 = sum64(acc0);
-      if (pair) acc1 = sum64(acc1);
-      if (lane == 0) epi_row(c, I, i, t, I->row0 + t, pair ? silu(acc0) * acc1 : acc0, best);
+      acc0 = sum64(acc0) * inv;
+      if (pair) acc1 = sum64(acc1) * inv;
+      if (lane == 0) epi_row(c, E, i, t, pair ? silu(acc0) * acc1 : acc0, best);
     } else {
       const u4 wa = *reinterpret_cast<const u4*>(lds + page_off<LayA>(page0 + u0 / kUnitsPerPage) +
                                                  (u0 % kUnitsPerPage) * kUnit + lane * 16);
       float lo, hi;
       sum32x2(dot8(wa, xv[0]), lo, hi);
+      lo *= inv;
+      hi *= inv;
       if (pair) {
-        if (lane == 0) epi_row(c, I, i, t, I->row0 + t, silu(lo) * hi, best);
+        if (lane == 0) epi_row(c, E, i, t, silu(lo) * hi, best);
       } else if ((lane & 31) == 0) {
-        const uint32_t tr = 2 * t + (lane >> 5);
-        epi_row(c, I, i, tr, I->row0 + tr, lane ? hi : lo, best);
+        epi_row(c, E, i, 2 * t + (lane >> 5), lane ? hi : lo, best);
       }
     }
     if (trl && t == 0) trace_put(a, c.cu, i, TR_ITEM0, now32());
@@ -224,8 +208,8 @@ DEV uint32_t out_rows(InstrCP I) {
 }
 
 // Leader staging (attention and the embedding input of the first layer):
-// the input into the x slot and, for a GEMV, its RMSNorm gain into the gain
-// area (the compute waves normalise; see gemv).  For attention: the group's
+// for a GEMV, the input times its RMSNorm gain into the x slot and the sum of
+// squares of the input (the GEMV scales its row sums by 1 / rms).  For attention: the group's
 // q, k, v and the position's cos, sin.  Every load is issued before the first
 // is waited for: one memory round trip.  false = abort or watchdog.
 DEV bool stage_leader(Comp& c, InstrCP I, uint32_t i) {
@@ -248,13 +232,30 @@ DEV bool stage_leader(Comp& c, InstrCP I, uint32_t i) {
       raw[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (lane * 8 + 512 * j) * 2, 0, 0));
       gw[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rg, (lane * 8 + 512 * j) * 2, 0, 0));
     }
-    uint16_t* gs = reinterpret_cast<uint16_t*>(lds + kLdsGain);
+    // x * gain into the x slot (the GEMV applies 1 / rms to its row sums)
+    // and the sum of squares of x
+    float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < NE; j++) {
       const uint32_t o = lane * 8 + 512 * j;
-      *reinterpret_cast<f4*>(xs + o) = f4{bf_lo(raw[j].x), bf_hi(raw[j].x), bf_lo(raw[j].y), bf_hi(raw[j].y)};
-      *reinterpret_cast<f4*>(xs + o + 4) = f4{bf_lo(raw[j].z), bf_hi(raw[j].z), bf_lo(raw[j].w), bf_hi(raw[j].w)};
-      if (norm) *reinterpret_cast<u4*>(gs + o) = gw[j];
+      const uint32_t xw[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+      const uint32_t gg[4] = {gw[j].x, gw[j].y, gw[j].z, gw[j].w};
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float x0 = bf_lo(xw[e]), x1 = bf_hi(xw[e]);
+        ss = fmaf(x0, x0, fmaf(x1, x1, ss));
+        v[2 * e] = norm ? x0 * bf_lo(gg[e]) : x0;
+        v[2 * e + 1] = norm ? x1 * bf_hi(gg[e]) : x1;
+      }
+      if (o < K) {
+        *reinterpret_cast<f4*>(xs + o) = f4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f4*>(xs + o + 4) = f4{v[4], v[5], v[6], v[7]};
+      }
+    }
+    if (norm) {
+      ss = sum64(ss);
+      if (lane < uint32_t(kNComp)) *reinterpret_cast<float*>(lds + kLdsSS + 4 * lane) = lane == 0 ? ss : 0.f;
     }
   } else {
     return stage_attn<LayA>(c, I);
@@ -265,9 +266,10 @@ DEV bool stage_leader(Comp& c, InstrCP I, uint32_t i) {
 // Cooperative staging of a GEMV's tagged input: wave w loads the chunks of
 // 128 values j = w, w + kNComp, ... (every load before the first wait: one
 // round trip per wave, all waves in parallel), re-reads stale ones, and
-// writes them raw to the x slot with their RMSNorm gains to the gain area
-// once every wave has read the previous input.  The leader also stages the
-// epilogue's residual rows.  A barrier of the compute waves follows.
+// writes them times their RMSNorm gains to the x slot, with the wave's share
+// of the sum of squares, once every wave has read the previous input.  The
+// leader also stages the epilogue's residual rows.  A barrier of the compute
+// waves follows.
 // false = abort or watchdog.
 DEV bool coop_stage(Comp& c, InstrCP I, uint32_t i, bool stage_x) {
   const KArgs& a = *c.a;
@@ -316,17 +318,17 @@ DEV bool coop_stage(Comp& c, InstrCP I, uint32_t i, bool stage_x) {
     // every wave has read the previous input out of the x slot
     if (!wait_all_ge(C_XCONS, i)) return false;
     float* xs = reinterpret_cast<float*>(lds + kLdsX);
-    uint16_t* gs = reinterpret_cast<uint16_t*>(lds + kLdsGain);
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < NC; q++) {
       if (q >= int(live)) continue;
       const uint32_t o = chunk(q) * 128 + 2 * lane;
       const float v0 = __uint_as_float(t[q].x), v1 = __uint_as_float(t[q].z);
-      *reinterpret_cast<float2*>(xs + o) = float2{v0, v1};
       if (norm) {
-        *reinterpret_cast<uint32_t*>(gs + o) = gw[q];
+        *reinterpret_cast<float2*>(xs + o) = float2{v0 * bf_lo(gw[q]), v1 * bf_hi(gw[q])};
         ss = fmaf(v0, v0, fmaf(v1, v1, ss));
+      } else {
+        *reinterpret_cast<float2*>(xs + o) = float2{v0, v1};
       }
     }
     // this wave's share of the sum of squares (gemv adds the kNComp shares)
