@@ -15,11 +15,13 @@
 //    «三点关键差异» item 3 and «快在哪里» item 3).  Loaders never wait on
 //    global counters; they track their own DMA with vmcnt and publish each
 //    page through an LDS word.
-//  * Compute wave 0 (the leader) waits on the instruction's counters in global
-//    memory and stages the input vector (or q/k/v) into LDS; then all compute
-//    waves run the op from the LDS pages.  The last wave to finish an
-//    instruction increments its counter (the counter system of the write-up,
-//    "Custom Synchronization Mechanism").
+//  * The compute waves stage the instruction's input vector into LDS (the
+//    leader alone for attention's q/k/v and the embedding row), polling the
+//    step tag every activation element carries until the producers' values
+//    are there; then all compute waves run the op from the LDS pages.  The
+//    last wave to finish an instruction increments its counter or takes its
+//    ticket (the counter system of the write-up, "Custom Synchronization
+//    Mechanism", kept for the data that carries no tag).
 #include "mk_dev.h"
 
 namespace mk {
