@@ -204,6 +204,20 @@ DEV float sum64(float v) {
   v = row_sum16(v);
   return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
 }
+// wave-uniform sums of two values at once: the first exchange leaves a's
+// pair sums in even lanes and b's in odd lanes, which the remaining
+// (parity-preserving) steps reduce side by side; each sum is added in the
+// same order as sum64 adds it
+DEV void sum64x2(float a, float b, float& sa, float& sb) {
+  const bool odd = threadIdx.x & 1;
+  const float pa = dpp<0xB1>(a), pb = dpp<0xB1>(b);  // quad_perm [1,0,3,2]
+  float v = odd ? b + pb : a + pa;
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
+  sa = (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
+  sb = (rl(v, 1) + rl(v, 17)) + (rl(v, 33) + rl(v, 49));
+}
 // sums of lanes [0,32) and [32,64)
 DEV void sum32x2(float v, float& lo, float& hi) {
   v = row_sum16(v);

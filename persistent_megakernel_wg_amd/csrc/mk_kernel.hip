@@ -142,36 +142,72 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
   const uint32_t n_items = I->n_items, page0 = I->page0;
   const bool pair = i_epi(I) == EPI_SWIGLU;
   const EpiCtx E = epi_of(I);
-  const uint32_t upi = RPU == 1 ? (pair ? 2 * NIT : NIT) : 1;
   ArgBest best{-__builtin_inff(), 0xFFFFFFFFu};
-  for (uint32_t t = c.w; t < n_items; t += kNComp) {
-    const uint32_t u0 = t * upi;
-    if (lane == 0) lds_st(C_RELEASED + 4 * c.w, page0 + u0 / kUnitsPerPage);
-    {
-      const uint32_t tw = trl ? now32() : 0;
-      if (!wait_page(page0 + (u0 + upi - 1) / kUnitsPerPage, c.fcache)) return false;
-      if (trl) c.pagewait += now32() - tw;
-    }
-    float acc0 = 0.f, acc1 = 0.f;
-    if (RPU == 1) {
-      // gate (or only) row, then the up row of a pair: one row of loads live at a time
-      for (int r = 0; r < (pair ? 2 : 1); r++) {
-        u4 wr[NIT];
-#pragma unroll
-        for (int j = 0; j < NIT; j++) {
-          const uint32_t u = u0 + r * NIT + j;
-          wr[j] = *reinterpret_cast<const u4*>(lds + page_off<LayA>(page0 + u / kUnitsPerPage) +
-                                               (u % kUnitsPerPage) * kUnit + lane * 16);
+  if constexpr (RPU == 1) {
+    // Whole rows.  The wave's items are t = w, w + kNComp, ...; it takes two
+    // at a time, with the loads of both issued before the first product
+    // (one row, or one row of each pair, at a time for the widest inputs),
+    // and reduces them together.
+    auto rows = [&](auto pair_c) -> bool {
+      constexpr int RU = decltype(pair_c)::value ? 2 : 1;  // rows per item
+      constexpr uint32_t UPI = RU * NIT;                    // units per item
+      constexpr int RL = 2 * RU * NIT <= 16 ? RU : 1;       // rows loaded together
+      for (uint32_t t = c.w; t < n_items; t += 2 * kNComp) {
+        const uint32_t tb = t + kNComp;
+        const bool two = tb < n_items;
+        const uint32_t ua = t * UPI, ub = (two ? tb : t) * UPI;
+        if (lane == 0) lds_st(C_RELEASED + 4 * c.w, page0 + ua / kUnitsPerPage);
+        {
+          const uint32_t tw = trl ? now32() : 0;
+          if (!wait_page(page0 + (ub + UPI - 1) / kUnitsPerPage, c.fcache)) return false;
+          if (trl) c.pagewait += now32() - tw;
         }
-        float acc = 0.f;
+        float sum[2][RU];
 #pragma unroll
-        for (int j = 0; j < NIT; j++) acc += dot8(wr[j], xv[j]);
-        if (r == 0) acc0 = acc; else acc1 = acc;
+        for (int r0 = 0; r0 < RU; r0 += RL) {
+          u4 wr[2][RL][NIT];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; s2++)
+#pragma unroll
+            for (int r = 0; r < RL; r++)
+#pragma unroll
+              for (int j = 0; j < NIT; j++) {
+                const uint32_t u = (s2 ? ub : ua) + (r0 + r) * NIT + j;
+                wr[s2][r][j] = *reinterpret_cast<const u4*>(lds + page_off<LayA>(page0 + u / kUnitsPerPage) +
+                                                            (u % kUnitsPerPage) * kUnit + lane * 16);
+              }
+#pragma unroll
+          for (int r = 0; r < RL; r++) {
+            float acc[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; s2++) {
+              acc[s2] = 0.f;
+#pragma unroll
+              for (int j = 0; j < NIT; j++) acc[s2] += dot8(wr[s2][r][j], xv[j]);
+            }
+            sum64x2(acc[0], acc[1], sum[0][r0 + r], sum[1][r0 + r]);
+          }
+        }
+        if (lane == 0) {
+          const float a0 = sum[0][0] * inv, b0 = sum[1][0] * inv;
+          epi_row(c, E, i, t, RU == 2 ? silu(a0) * (sum[0][RU - 1] * inv) : a0, best);
+          if (two) epi_row(c, E, i, tb, RU == 2 ? silu(b0) * (sum[1][RU - 1] * inv) : b0, best);
+        }
+        if (trl && t == 0) trace_put(a, c.cu, i, TR_ITEM0, now32());
       }
-      acc0 = sum64(acc0) * inv;
-      if (pair) acc1 = sum64(acc1) * inv;
-      if (lane == 0) epi_row(c, E, i, t, pair ? silu(acc0) * acc1 : acc0, best);
-    } else {
+      return true;
+    };
+    if (!(pair ? rows(std::true_type{}) : rows(std::false_type{}))) return false;
+  } else {
+    // half-wave rows of 512 B (K = 256): one unit holds two rows (or a pair)
+    for (uint32_t t = c.w; t < n_items; t += kNComp) {
+      const uint32_t u0 = t;
+      if (lane == 0) lds_st(C_RELEASED + 4 * c.w, page0 + u0 / kUnitsPerPage);
+      {
+        const uint32_t tw = trl ? now32() : 0;
+        if (!wait_page(page0 + u0 / kUnitsPerPage, c.fcache)) return false;
+        if (trl) c.pagewait += now32() - tw;
+      }
       const u4 wa = *reinterpret_cast<const u4*>(lds + page_off<LayA>(page0 + u0 / kUnitsPerPage) +
                                                  (u0 % kUnitsPerPage) * kUnit + lane * 16);
       float lo, hi;
@@ -183,8 +219,8 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
       } else if ((lane & 31) == 0) {
         epi_row(c, E, i, 2 * t + (lane >> 5), lane ? hi : lo, best);
       }
+      if (trl && t == 0) trace_put(a, c.cu, i, TR_ITEM0, now32());
     }
-    if (trl && t == 0) trace_put(a, c.cu, i, TR_ITEM0, now32());
   }
   if (i_epi(I) == EPI_ARGMAX) {
     // combine lanes 0 and 32 (512 B rows) and publish the wave's best
