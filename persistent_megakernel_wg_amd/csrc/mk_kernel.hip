@@ -307,82 +307,104 @@ DEV bool stage_leader(Comp& c, InstrCP I, uint32_t i) {
 // writes them times their RMSNorm gains to the x slot, with the wave's share
 // of the sum of squares, once every wave has read the previous input.  The
 // leader also stages the epilogue's residual rows.  A barrier of the compute
-// waves follows.
-// false = abort or watchdog.
-DEV bool coop_stage(Comp& c, InstrCP I, uint32_t i, bool stage_x) {
-  const KArgs& a = *c.a;
-  const uint32_t lane = c.lane;
-  const uint32_t tag = in_tag(a, I);
-  constexpr int NC = (kMaxK / 128 + kNComp - 1) / kNComp;
+// waves follows.  The loads can be issued early (stage_issue, while the
+// previous instruction's items run) and completed later (stage_finish).
+constexpr int kStageNC = (kMaxK / 128 + kNComp - 1) / kNComp;
+struct StageIn {
+  u4 t[kStageNC];        // value | tag pairs of the wave's chunks
+  uint32_t gw[kStageNC]; // their RMSNorm gains (bf16 pairs)
+  uint2 res_t[2];        // leader: tagged residual rows
+  uint16_t res_e[2];     // leader: residual rows from the embedding
+};
+struct StageGeo {
+  __amdgpu_buffer_rsrc_t r, rg, rr;
+  uint32_t nch;
+  bool norm, has_res, res_embed;
+};
+DEV StageGeo stage_geo(Comp& c, InstrCP I, bool stage_x) {
+  StageGeo g;
+  const uint32_t K = I->k;
+  g.nch = K / 128;
+  g.norm = i_flags(I) & F_NORM;
+  g.r = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), stage_x ? K * kActBytes : 0);
+  g.rg = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(I->gain_ptr), 0, (stage_x && g.norm) ? K * 2 : 0,
+                                           0x00020000);
+  g.has_res = c.w == 0 && needs_res(I);
+  g.res_embed = g.has_res && (i_flags(I) & F_RES_EMBED);
+  const uint32_t n_res = g.has_res ? out_rows(I) : 0;
+  g.rr = act_rsrc(reinterpret_cast<const char*>(I->res_ptr) + size_t(I->row0) * kActBytes,
+                  (g.has_res && !g.res_embed) ? n_res * kActBytes : 0);
+  return g;
+}
+DEV uint32_t stage_off(const Comp& c, int q) { return ((uint32_t(c.w) + kNComp * q) * 128 + 2 * c.lane) * kActBytes; }
+
+DEV void stage_issue(Comp& c, InstrCP I, bool stage_x, StageIn& S) {
   static_assert(kMaxResRows == 128, "residual staging takes two rows per lane");
-  const uint32_t K = I->k, nch = K / 128;
-  const bool norm = i_flags(I) & F_NORM;
-  const __amdgpu_buffer_rsrc_t r = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), stage_x ? K * kActBytes : 0);
-  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<void*>(I->gain_ptr), 0, (stage_x && norm) ? K * 2 : 0, 0x00020000);
-  auto chunk = [&](int q) -> uint32_t { return uint32_t(c.w) + kNComp * q; };
-  auto off = [&](int, int q) -> uint32_t { return (chunk(q) * 128 + 2 * lane) * kActBytes; };
-  u4 t[NC];
-  uint32_t gw[NC];
+  const uint32_t lane = c.lane;
+  const StageGeo g = stage_geo(c, I, stage_x);
 #pragma unroll
-  for (int q = 0; q < NC; q++) {
-    t[q] = ld_tag2(r, off(0, q));
-    gw[q] = __builtin_amdgcn_raw_buffer_load_b32(rg, (chunk(q) * 128 + 2 * lane) * 2, 0, 0);
+  for (int q = 0; q < kStageNC; q++) {
+    S.t[q] = ld_tag2(g.r, stage_off(c, q));
+    S.gw[q] = __builtin_amdgcn_raw_buffer_load_b32(g.rg, ((uint32_t(c.w) + kNComp * q) * 128 + 2 * lane) * 2, 0, 0);
   }
   // residual rows r0 + 2*lane + {0,1} (leader): tagged elements, or the bf16
   // row of the token's embedding (per-element loads: a resource of n_res
   // elements reads zero past the tile)
-  const bool has_res = c.w == 0 && needs_res(I);
-  const bool res_embed = has_res && (i_flags(I) & F_RES_EMBED);
-  const uint32_t n_res = has_res ? out_rows(I) : 0;
-  const uint32_t r0 = I->row0;
-  const __amdgpu_buffer_rsrc_t rr = act_rsrc(reinterpret_cast<const char*>(I->res_ptr) + size_t(r0) * kActBytes,
-                                             (has_res && !res_embed) ? n_res * kActBytes : 0);
-  uint2 res_t[2];
-  const uint32_t res_off[2] = {2 * lane * kActBytes, (2 * lane + 1) * kActBytes};
-  reload(res_t[0], rr, res_off[0]);
-  reload(res_t[1], rr, res_off[1]);
-  uint16_t res_e[2] = {0, 0};
-  if (res_embed) {
-    const uint16_t* e = reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(token0(a)) * a.hidden + r0;
+  reload(S.res_t[0], g.rr, 2 * lane * kActBytes);
+  reload(S.res_t[1], g.rr, (2 * lane + 1) * kActBytes);
+  S.res_e[0] = S.res_e[1] = 0;
+  if (g.res_embed) {
+    const KArgs& a = *c.a;
+    const uint32_t n_res = out_rows(I);
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(token0(a)) * a.hidden + I->row0;
     const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(e), 0, n_res * 2, 0x00020000);
-    res_e[0] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane, 0, 0);
-    res_e[1] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane + 2, 0, 0);
+    S.res_e[0] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane, 0, 0);
+    S.res_e[1] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane + 2, 0, 0);
   }
+}
+
+// false = abort or watchdog
+DEV bool stage_finish(Comp& c, InstrCP I, uint32_t i, bool stage_x, StageIn& S) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane;
+  const uint32_t tag = in_tag(a, I);
+  const StageGeo g = stage_geo(c, I, stage_x);
+  const uint32_t n_res = g.has_res ? out_rows(I) : 0;
   const uint32_t res_live = 2 * lane >= n_res ? 0 : (2 * lane + 1 < n_res ? 2 : 1);
   if (stage_x) {
-    const uint32_t live = uint32_t(c.w) < nch ? (nch - c.w + kNComp - 1) / kNComp : 0;
-    if (!wait_fresh(t, live, r, off, 0, tag, c.retries)) return false;
+    const uint32_t live = uint32_t(c.w) < g.nch ? (g.nch - c.w + kNComp - 1) / kNComp : 0;
+    if (!wait_fresh(S.t, live, g.r, [&](int, int q) { return stage_off(c, q); }, 0, tag, c.retries)) return false;
     // every wave has read the previous input out of the x slot
     if (!wait_all_ge(C_XCONS, i)) return false;
     float* xs = reinterpret_cast<float*>(lds + kLdsX);
     float ss = 0.f;
 #pragma unroll
-    for (int q = 0; q < NC; q++) {
+    for (int q = 0; q < kStageNC; q++) {
       if (q >= int(live)) continue;
-      const uint32_t o = chunk(q) * 128 + 2 * lane;
-      const float v0 = __uint_as_float(t[q].x), v1 = __uint_as_float(t[q].z);
-      if (norm) {
-        *reinterpret_cast<float2*>(xs + o) = float2{v0 * bf_lo(gw[q]), v1 * bf_hi(gw[q])};
+      const uint32_t o = (uint32_t(c.w) + kNComp * q) * 128 + 2 * lane;
+      const float v0 = __uint_as_float(S.t[q].x), v1 = __uint_as_float(S.t[q].z);
+      if (g.norm) {
+        *reinterpret_cast<float2*>(xs + o) = float2{v0 * bf_lo(S.gw[q]), v1 * bf_hi(S.gw[q])};
         ss = fmaf(v0, v0, fmaf(v1, v1, ss));
       } else {
         *reinterpret_cast<float2*>(xs + o) = float2{v0, v1};
       }
     }
     // this wave's share of the sum of squares (gemv adds the kNComp shares)
-    if (norm) {
+    if (g.norm) {
       ss = sum64(ss);
       if (lane == 0) *reinterpret_cast<float*>(lds + kLdsSS + 4 * c.w) = ss;
     }
   }
-  if (has_res) {
+  if (g.has_res) {
     float* rs = const_cast<float*>(res_slot(i));
-    if (!res_embed && !wait_fresh(res_t, res_live, rr, [&](int, int j) { return res_off[j]; }, 0, tag, c.retries))
+    const uint32_t res_off[2] = {2 * lane * kActBytes, (2 * lane + 1) * kActBytes};
+    if (!g.res_embed && !wait_fresh(S.res_t, res_live, g.rr, [&](int, int j) { return res_off[j]; }, 0, tag, c.retries))
       return false;
 #pragma unroll
     for (int j = 0; j < 2; j++)
       if (j < int(res_live))
-        rs[2 * lane + j] = res_embed ? __uint_as_float(uint32_t(res_e[j]) << 16) : __uint_as_float(res_t[j].x);
+        rs[2 * lane + j] = g.res_embed ? __uint_as_float(uint32_t(S.res_e[j]) << 16) : __uint_as_float(S.res_t[j].x);
   }
   return true;
 }
@@ -507,16 +529,23 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
   uint64_t staged_in = 0;
   uint32_t staged_flags = 0, staged_k = 0;
   uint64_t staged_gain = 0;
+  // the staged input of the previous GEMV can be reused as is
+  auto reuses = [&](InstrCP I) {
+    return i_op(I) == OP_GEMV && I->in_ptr == staged_in &&
+           (i_flags(I) & (F_IN_EMBED | F_NORM)) == staged_flags && I->k == staged_k &&
+           (!(i_flags(I) & F_NORM) || I->gain_ptr == staged_gain);
+  };
+  // tagged GEMV inputs are staged by all compute waves together; the
+  // embedding input and attention inputs by the leader
+  auto is_coop = [](InstrCP I) { return i_op(I) == OP_GEMV && !(i_flags(I) & F_IN_EMBED); };
+  // loads of the next instruction's input, issued while this one's items run
+  StageIn pre;
+  uint32_t pre_i = 0xFFFFFFFFu;
   for (uint32_t i = 0; i < n; i++) {
     InstrCP I = q + i;
     const bool is_gemv = i_op(I) == OP_GEMV;
-    // the staged input of the previous GEMV can be reused as is
-    const bool reuse = is_gemv && I->in_ptr == staged_in &&
-                       (i_flags(I) & (F_IN_EMBED | F_NORM)) == staged_flags && I->k == staged_k &&
-                       (!(i_flags(I) & F_NORM) || I->gain_ptr == staged_gain);
-    // tagged GEMV inputs are staged by all compute waves together; the
-    // embedding input and attention inputs by the leader
-    const bool coop = is_gemv && !(i_flags(I) & F_IN_EMBED);
+    const bool reuse = reuses(I);
+    const bool coop = is_coop(I);
     if (w == 0) {
       if (tr && c.lane == 0) {
         trace_put(a, cu, i, TR_START, now32());
@@ -537,7 +566,8 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
     if (coop) {
       // every wave stages its share; a barrier publishes the x slot
       if (!reuse || needs_res(I)) {
-        if (!coop_stage(c, I, i, !reuse)) {
+        if (pre_i != i) stage_issue(c, I, !reuse, pre);
+        if (!stage_finish(c, I, i, !reuse, pre)) {
           if (c.lane == 0) lds_st(C_ABORT, 1);
           return;
         }
@@ -572,6 +602,21 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       staged_flags = i_flags(I) & (F_IN_EMBED | F_NORM);
       staged_k = I->k;
       staged_gain = I->gain_ptr;
+      // A down-projection chunk reads the gate/up output of a chunk that
+      // every CU finished before its previous instruction began, so its
+      // input is usually complete by now: issue its loads while this
+      // instruction's items run, and staging it later costs only the
+      // re-reads of what was still stale.  (The other inputs are written by
+      // the stage that runs at the same time, and early loads of them would
+      // only be read twice.)
+      const uint32_t ne = i + 1 < n ? i_epi(I + 1) : 0u;
+      if (i + 1 < n && is_coop(I + 1) && (ne == EPI_ACC_FIRST || ne == EPI_ACC_MID || ne == EPI_ACC_LAST)) {
+        const bool nreuse = reuses(I + 1);
+        if (!nreuse || needs_res(I + 1)) {
+          stage_issue(c, I + 1, !nreuse, pre);
+          pre_i = i + 1;
+        }
+      }
     } else {
       staged_in = 0;
     }
