@@ -379,9 +379,8 @@ DEV bool coop_stage_b(Comp& c, InstrCP I, uint32_t i, bool stage_x) {
   const uint32_t K = I->k, nB = uint32_t(a.batch), nch = nB * K / 128;
   const bool norm = i_flags(I) & F_NORM, embed = i_flags(I) & F_IN_EMBED;
   const __amdgpu_buffer_rsrc_t r =
-      act_rsrc(reinterpret_cast<const void*>(I->in_ptr), (stage_x && !embed) ? nB * K * kActBytes : 0);
-  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<void*>(I->gain_ptr), 0, (stage_x && norm) ? K * 2 : 0, 0x00020000);
+      act_rsrc_u(reinterpret_cast<const void*>(I->in_ptr), (stage_x && !embed) ? nB * K * kActBytes : 0);
+  const __amdgpu_buffer_rsrc_t rg = act_rsrc_u(reinterpret_cast<const void*>(I->gain_ptr), (stage_x && norm) ? K * 2 : 0);
   auto chunk = [&](int qq) -> uint32_t { return uint32_t(c.w) + kNComp * qq; };
   auto off = [&](int, int qq) -> uint32_t { return (chunk(qq) * 128 + 2 * lane) * kActBytes; };
   const uint32_t live = (stage_x && uint32_t(c.w) < nch) ? (nch - c.w + kNComp - 1) / kNComp : 0;

@@ -147,6 +147,12 @@ DEV void st_tag(uint64_t* p, float v, uint32_t tag) {
 DEV __amdgpu_buffer_rsrc_t act_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
+// The same for a base and size the compiler cannot prove wave-uniform (they
+// are): readfirstlane keeps the descriptor in scalar registers, where the
+// compiler would otherwise loop over the lanes for every load.
+DEV __amdgpu_buffer_rsrc_t act_rsrc_u(const void* base, uint32_t bytes) {
+  return act_rsrc(reinterpret_cast<const void*>(uni64(reinterpret_cast<uint64_t>(base))), uni(bytes));
+}
 DEV f4 ld_act4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16 /* sc1 */));
 }
@@ -845,8 +851,7 @@ DEV void attn_merge(Comp& c, InstrCP I) {
   const uint32_t g = I->aux[0], nblk = I->aux[3];
   const uint32_t head0 = g * uint32_t(c.a->hpg) + I->row0;
   const float* part = reinterpret_cast<const float*>(I->res_ptr) + size_t(head0 / HPT) * nblk * (HPT * REC);
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(part), 0,
-                                                                     nblk * HPT * REC * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t r = act_rsrc_u(part, nblk * HPT * REC * 4);
   const uint32_t o0 = c.lane * PER, h = o0 / DH, d0 = o0 % DH;
   float M = -__builtin_inff(), den = 0.f, num[PER];
 #pragma unroll
@@ -948,10 +953,8 @@ DEV bool stage_attn(Comp& c, InstrCP I) {
       const __amdgpu_buffer_rsrc_t rk = act_rsrc(qkv + size_t(a.q_dim + g * dh) * kActBytes, dh * kActBytes);
       const __amdgpu_buffer_rsrc_t rv =
           act_rsrc(qkv + size_t(a.q_dim + a.kv_dim + g * dh) * kActBytes, dh * kActBytes);
-      const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(a.rope_cos + size_t(a.pos) * half), 0, half * 4, 0x00020000);
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(a.rope_sin + size_t(a.pos) * half), 0, half * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rc = act_rsrc(a.rope_cos + size_t(a.pos) * half, half * 4);
+      const __amdgpu_buffer_rsrc_t rs = act_rsrc(a.rope_sin + size_t(a.pos) * half, half * 4);
       static_assert(kMaxK >= 512, "q staging");
       constexpr int NQ = 4;  // up to 512 q values
       u4 tq[NQ], tk[1], tv[1];

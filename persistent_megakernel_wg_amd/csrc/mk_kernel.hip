@@ -261,9 +261,8 @@ DEV bool stage_leader(Comp& c, InstrCP I, uint32_t i) {
     const uint32_t K = I->k;
     const bool norm = i_flags(I) & F_NORM;
     const uint16_t* e = reinterpret_cast<const uint16_t*>(I->in_ptr) + size_t(token0(a)) * K;
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(e), 0, K * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void*>(I->gain_ptr), 0, norm ? K * 2 : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t r = act_rsrc(e, K * 2);
+    const __amdgpu_buffer_rsrc_t rg = act_rsrc(reinterpret_cast<const void*>(I->gain_ptr), norm ? K * 2 : 0);
     u4 raw[NE], gw[NE];
 #pragma unroll
     for (int j = 0; j < NE; j++) {
@@ -326,13 +325,12 @@ DEV StageGeo stage_geo(Comp& c, InstrCP I, bool stage_x) {
   const uint32_t K = I->k;
   g.nch = K / 128;
   g.norm = i_flags(I) & F_NORM;
-  g.r = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), stage_x ? K * kActBytes : 0);
-  g.rg = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(I->gain_ptr), 0, (stage_x && g.norm) ? K * 2 : 0,
-                                           0x00020000);
+  g.r = act_rsrc_u(reinterpret_cast<const void*>(I->in_ptr), stage_x ? K * kActBytes : 0);
+  g.rg = act_rsrc_u(reinterpret_cast<const void*>(I->gain_ptr), (stage_x && g.norm) ? K * 2 : 0);
   g.has_res = c.w == 0 && needs_res(I);
   g.res_embed = g.has_res && (i_flags(I) & F_RES_EMBED);
   const uint32_t n_res = g.has_res ? out_rows(I) : 0;
-  g.rr = act_rsrc(reinterpret_cast<const char*>(I->res_ptr) + size_t(I->row0) * kActBytes,
+  g.rr = act_rsrc_u(reinterpret_cast<const char*>(I->res_ptr) + size_t(I->row0) * kActBytes,
                   (g.has_res && !g.res_embed) ? n_res * kActBytes : 0);
   return g;
 }
@@ -357,7 +355,7 @@ DEV void stage_issue(Comp& c, InstrCP I, bool stage_x, StageIn& S) {
     const KArgs& a = *c.a;
     const uint32_t n_res = out_rows(I);
     const uint16_t* e = reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(token0(a)) * a.hidden + I->row0;
-    const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(e), 0, n_res * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t re = act_rsrc_u(e, n_res * 2);
     S.res_e[0] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane, 0, 0);
     S.res_e[1] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane + 2, 0, 0);
   }
