@@ -152,6 +152,9 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
       constexpr int RU = decltype(pair_c)::value ? 2 : 1;  // rows per item
       constexpr uint32_t UPI = RU * NIT;                    // units per item
       constexpr int RL = 2 * RU * NIT <= 16 ? RU : 1;       // rows loaded together
+      // the units an iteration spans must fit in the page ring, or the wave
+      // would wait for a page that only its own release can free
+      static_assert((kNComp + 1) * UPI <= uint32_t(kPages * kUnitsPerPage), "an iteration's rows exceed the page ring");
       for (uint32_t t = c.w; t < n_items; t += 2 * kNComp) {
         const uint32_t tb = t + kNComp;
         const bool two = tb < n_items;
