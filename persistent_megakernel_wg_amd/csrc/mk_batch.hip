@@ -337,6 +337,33 @@ DEV float reduce16(float (&v)[16]) {
   return r;
 }
 
+// Sums over the wave of 32 values at once: after five exchange stages
+// (mirrors inside 16-lane rows first, so that no stage's partner flips a lane
+// bit an earlier stage has assigned, then xor 16) and a final xor-32 add,
+// lane l holds the sum of v[idx(l)], idx(l) = l3 l2 l1 l0 l4 (bits, high to
+// low).
+template <int N, class X>
+DEV void bfly_stage32(float (&v)[32], bool keep_lo, X xch) {
+#pragma unroll
+  for (int j = 0; j < N; j++) {
+    const float send = keep_lo ? v[j + N] : v[j];
+    const float keep = keep_lo ? v[j] : v[j + N];
+    v[j] = keep + xch(send);
+  }
+}
+DEV float reduce32(float (&v)[32]) {
+  const uint32_t l = threadIdx.x & 63;
+  bfly_stage32<16>(v, (l & 15) < 8, [](float x) { return dpp<0x140>(x); });  // row_mirror
+  bfly_stage32<8>(v, (l & 7) < 4, [](float x) { return dpp<0x141>(x); });    // row_half_mirror
+  bfly_stage32<4>(v, (l & 3) < 2, [](float x) { return dpp<0x4E>(x); });     // quad_perm [2,3,0,1]
+  bfly_stage32<2>(v, (l & 1) == 0, [](float x) { return dpp<0xB1>(x); });    // quad_perm [1,0,3,2]
+  bfly_stage32<1>(v, (l & 16) == 0, [](float x) { return __shfl_xor(x, 16, 64); });
+  return v[0] + __shfl_xor(v[0], 32, 64);
+}
+DEV uint32_t reduce32_index(uint32_t l) {
+  return (((l >> 3) & 1) << 4) | (((l >> 2) & 1) << 3) | (((l >> 1) & 1) << 2) | ((l & 1) << 1) | ((l >> 4) & 1);
+}
+
 DEV const float* res_slot_b(uint32_t i) {
   return reinterpret_cast<const float*>(lds + lb::kRes + (i & 1) * 4 * kMaxResRows);
 }
@@ -490,6 +517,31 @@ DEV void dot_pair(uint32_t pg, uint32_t ua, uint32_t ub, uint32_t nit, uint32_t 
       x8_ld(xs + xoff(b) + j * 512 + lane * 8, x);
       acc[b] += dot8(wa, x);
       acc[8 + b] += dot8(wb, x);
+    }
+  }
+}
+
+// acc[8 r + b] = row r . x_b for four consecutive rows (rows at or past
+// nrows count as zero) and the sequences in `tm`; row r is NIT units from
+// unit u0 + r * NIT.  Each sequence's input is read once for the four rows.
+template <class XOff>
+DEV void dot_rows4(uint32_t pg, uint32_t u0, uint32_t nit, uint32_t nrows, uint32_t tm, XOff xoff,
+                   float (&acc)[32]) {
+  const uint32_t lane = threadIdx.x & 63;
+  const float* xs = reinterpret_cast<const float*>(lds + lb::kX);
+#pragma unroll
+  for (int e = 0; e < 32; e++) acc[e] = 0.f;
+  for (uint32_t j = 0; j < nit; j++) {
+    u4 w[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) w[r] = uint32_t(r) < nrows ? unit_ld(pg, u0 + r * nit + j, lane) : u4{0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < lb::kMaxB; b++) {
+      if (!((tm >> b) & 1)) continue;
+      float x[8];
+      x8_ld(xs + xoff(b) + j * 512 + lane * 8, x);
+#pragma unroll
+      for (int r = 0; r < 4; r++) acc[8 * r + b] += dot8(w[r], x);
     }
   }
 }
@@ -673,7 +725,7 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
   const uint32_t lane = c.lane, K = I->k, nit = i_nit(I), nB = uint32_t(a.batch);
   const int rt = rt_base(I->layer);
   const uint32_t nsel = *lw(rt + RT_NSEL), npair = *lw(rt + RT_NPAIR);
-  const uint32_t ppe = I->aux[2], nr = I->aux[3], ipe = (nr + 1) / 2;
+  const uint32_t ppe = I->aux[2], nr = I->aux[3];
   const uint32_t k = uint32_t(a.top_k), Fe = uint32_t(a.expert_ffn);
   const uint32_t cap = uint32_t(lb::kXFloats) / K;  // pairs per group
   const uint32_t ngroups = (npair + cap - 1) / cap;
@@ -718,11 +770,12 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
     if (!comp_barrier()) return false;
     if (g + 1 < ngroups) load_group(g + 1);
     if (trl && g == 0) trace_put(a, c.cu, i, TR_ITEM0, now32());
-    // items: (expert rank er in [er_a, er_b], row pair p)
+    // items: (expert rank er in [er_a, er_b], block of 4 rows)
     const uint32_t er_a = uni(rank_of(p0)), er_b = uni(rank_of(p0 + np - 1));
-    const uint32_t n_items = (er_b - er_a + 1) * ipe;
+    const uint32_t nrb = (nr + 3) / 4;
+    const uint32_t n_items = (er_b - er_a + 1) * nrb;
     for (uint32_t it = c.w; it < n_items; it += kNComp) {
-      const uint32_t er = er_a + it / ipe, p = it % ipe;
+      const uint32_t er = er_a + it / nrb, r0 = 4 * (it % nrb);
       const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
       const uint32_t tok = uni(rt_u8(rt, RT_TOK + int(e)));
       const uint32_t base = uni(rt_u8(rt, RT_PBASE + int(er)));
@@ -732,15 +785,16 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
         const uint32_t pi = base + rank;
         if (pi >= p0 && pi < p0 + np) tm |= 1u << __builtin_ctz(bits);
       }
-      const uint32_t u0 = er * ppe * kUnitsPerPage + 2 * p * nit;
+      const uint32_t nrows = min(4u, nr - r0);
+      const uint32_t u0 = er * ppe * kUnitsPerPage + r0 * nit;
       if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + u0 / kUnitsPerPage);
-      if (!wait_page(pg + (u0 + 2 * nit - 1) / kUnitsPerPage, c.fcache)) return false;
-      float acc[16];
-      dot_pair(pg, u0, u0 + nit, nit, tm,
-               [&](int b) { return (base + __builtin_popcount(tok & ((1u << b) - 1)) - p0) * K; }, acc);
-      const float sdot = reduce16(acc);
-      const uint32_t li = lane & 15, ri = li >> 3, bb = li & 7, row = 2 * p + ri;
-      if (lane < 16 && ((tm >> bb) & 1) && row < nr) {
+      if (!wait_page(pg + (u0 + nrows * nit - 1) / kUnitsPerPage, c.fcache)) return false;
+      float acc[32];
+      dot_rows4(pg, u0, nit, nrows, tm,
+                [&](int b) { return (base + __builtin_popcount(tok & ((1u << b) - 1)) - p0) * K; }, acc);
+      const float sdot = reduce32(acc);
+      const uint32_t idx = reduce32_index(lane), row = r0 + (idx >> 3), bb = idx & 7;
+      if (lane < 32 && ((tm >> bb) & 1) && row < nr) {
         const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + bb));
         dots[(bb * lb::kMaxTopK + slot) * lb::kMaxDnRows + row] = sdot;
       }
