@@ -490,6 +490,22 @@ DEV u4 unit_ld(uint32_t pg, uint32_t u, uint32_t lane) {
   return *reinterpret_cast<const u4*>(lds + page_off<LayB>(pg + u / kUnitsPerPage) + (u % kUnitsPerPage) * kUnit +
                                       lane * 16);
 }
+DEV void widen8(u4 w, float (&o)[8]) {
+  o[0] = bf_lo(w.x); o[1] = bf_hi(w.x); o[2] = bf_lo(w.y); o[3] = bf_hi(w.y);
+  o[4] = bf_lo(w.z); o[5] = bf_hi(w.z); o[6] = bf_lo(w.w); o[7] = bf_hi(w.w);
+}
+// the same sum as dot8, on widened weights
+DEV float dot8f(const float (&w)[8], const float (&x)[8]) {
+  float a = w[0] * x[0];
+  a = fmaf(w[1], x[1], a);
+  float b = w[2] * x[2];
+  b = fmaf(w[3], x[3], b);
+  a = fmaf(w[4], x[4], a);
+  a = fmaf(w[5], x[5], a);
+  b = fmaf(w[6], x[6], b);
+  b = fmaf(w[7], x[7], b);
+  return a + b;
+}
 DEV void x8_ld(const float* p, float (&o)[8]) {
   const f4 lo = *reinterpret_cast<const f4*>(p);
   const f4 hi = *reinterpret_cast<const f4*>(p + 4);
@@ -508,15 +524,17 @@ DEV void dot_pair(uint32_t pg, uint32_t ua, uint32_t ub, uint32_t nit, uint32_t 
 #pragma unroll
   for (int e = 0; e < 16; e++) acc[e] = 0.f;
   for (uint32_t j = 0; j < nit; j++) {
-    const u4 wa = unit_ld(pg, ua + j, lane);
-    const u4 wb = unit_ld(pg, ub + j, lane);
+    // the weights widened once, then applied to every sequence
+    float fa[8], fb[8];
+    widen8(unit_ld(pg, ua + j, lane), fa);
+    widen8(unit_ld(pg, ub + j, lane), fb);
 #pragma unroll
     for (int b = 0; b < lb::kMaxB; b++) {
       if (!((tm >> b) & 1)) continue;
       float x[8];
       x8_ld(xs + xoff(b) + j * 512 + lane * 8, x);
-      acc[b] += dot8(wa, x);
-      acc[8 + b] += dot8(wb, x);
+      acc[b] += dot8f(fa, x);
+      acc[8 + b] += dot8f(fb, x);
     }
   }
 }
@@ -532,16 +550,17 @@ DEV void dot_rows4(uint32_t pg, uint32_t u0, uint32_t nit, uint32_t nrows, uint3
 #pragma unroll
   for (int e = 0; e < 32; e++) acc[e] = 0.f;
   for (uint32_t j = 0; j < nit; j++) {
-    u4 w[4];
+    // the weights widened once, then applied to every sequence
+    float w[4][8];
 #pragma unroll
-    for (int r = 0; r < 4; r++) w[r] = uint32_t(r) < nrows ? unit_ld(pg, u0 + r * nit + j, lane) : u4{0, 0, 0, 0};
+    for (int r = 0; r < 4; r++) widen8(uint32_t(r) < nrows ? unit_ld(pg, u0 + r * nit + j, lane) : u4{0, 0, 0, 0}, w[r]);
 #pragma unroll
     for (int b = 0; b < lb::kMaxB; b++) {
       if (!((tm >> b) & 1)) continue;
       float x[8];
       x8_ld(xs + xoff(b) + j * 512 + lane * 8, x);
 #pragma unroll
-      for (int r = 0; r < 4; r++) acc[8 * r + b] += dot8(w[r], x);
+      for (int r = 0; r < 4; r++) acc[8 * r + b] += dot8f(w[r], x);
     }
   }
 }
