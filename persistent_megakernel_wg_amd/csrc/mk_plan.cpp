@@ -802,6 +802,18 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     return int(cu % C);
   };
 
+  // CUs that take O rows: all, or, with few attention tiles (at most one
+  // CU in four), the CUs without one
+  std::vector<int> o_rank(C, 0);
+  const bool o_skip_att = int64_t(n_att) * 4 <= C;
+  int o_cus = C;
+  if (o_skip_att) {
+    for (int a = 0; a < n_att; a++) o_rank[att_cu(a)] = -1;
+    o_cus = 0;
+    for (int cu = 0; cu < C; cu++)
+      if (o_rank[cu] == 0) o_rank[cu] = o_cus++;
+  }
+
   for (int l = 0; l < L; l++) {
     const int stg = l * ST_PER_LAYER;
     // ------------------------------------------------------------ QKV
@@ -898,7 +910,16 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
       const int64_t N = d / gq.rpu;
       for (int cu = 0; cu < C; cu++) {
         int64_t c0, c1;
-        split(N, cu, &c0, &c1);
+        // With few attention tiles, their CUs take no O rows: they finish
+        // attention when the O stage can start, and would otherwise be its
+        // last to finish.  The other CUs share the rows evenly.
+        if (o_skip_att) {
+          if (o_rank[cu] < 0) continue;
+          c0 = N * o_rank[cu] / o_cus;
+          c1 = N * (o_rank[cu] + 1) / o_cus;
+        } else {
+          split(N, cu, &c0, &c1);
+        }
         const int64_t step = kMaxResRows / gq.rpu;  // residual rows staged per tile
         for (int64_t i0 = c0; i0 < c1; i0 += step) {
         const int64_t i1 = std::min(c1, i0 + step);
