@@ -67,7 +67,7 @@ static_assert(C_FILLED + 4 * kNLoad <= C_RELEASED, "ctrl layout");
 static_assert(C_RELEASED + 4 * kNComp <= C_XOK, "ctrl layout");
 static_assert(C_XCONS + 4 * kNComp <= C_DONE, "ctrl layout");
 static_assert(C_DONE + 4 * kDoneRing <= C_ABORT, "ctrl layout");
-static_assert(C_CTRL_END <= kLdsSS && kLdsSS + 4 * kNComp <= kLdsAcc, "ctrl layout");
+static_assert(C_CTRL_END <= kLdsSS && kLdsSS + 4 * kNComp <= kLdsPf && kLdsPf + 256 <= kLdsAcc, "ctrl layout");
 
 DEV uint32_t* lw(int off) { return reinterpret_cast<uint32_t*>(lds + off); }
 DEV uint32_t lds_ld(int off) {
@@ -429,6 +429,19 @@ DEV void dma_lane(uint32_t lds_addr, uint64_t src) {
 }
 
 constexpr uint32_t kDmaPerPage = kUnitsPerPage / kNLoad;  // 8
+
+// One wave-wide 4 B/lane load with its lanes 128 B (one L2 line) apart: it
+// brings the 8 KiB that a loader wave later copies into a page half into the
+// XCD's L2, so that copy does not wait on HBM.  The words land in a 256 B LDS
+// sink nobody reads; no register holds them.
+DEV void l2_touch(uint32_t sink, uint64_t src, uint32_t voff128) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t" MK_DMA_NOP "\n\t"
+      "global_load_lds_dword %1, %2"
+      :
+      : "s"(sink), "v"(voff128), "s"(src)
+      : "memory", "m0");
+}
 
 // wait until at most `pages_after` pages of this loader's DMA are in flight
 DEV void wait_vm_pages(uint32_t pages_after) {

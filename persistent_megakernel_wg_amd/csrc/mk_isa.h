@@ -37,6 +37,7 @@ constexpr int kActBytes = 8;
 // LDS layout (bytes)
 constexpr int kLdsCtrl = 0;          // control words
 constexpr int kLdsSS = 512;          // per-wave shares of an input's sum of squares
+constexpr int kLdsPf = 768;          // 256 B sink of the loaders' L2 prefetch loads (never read)
 constexpr int kLdsAcc = 1024;        // down-projection accumulators (256 floats)
 constexpr int kLdsX = 2048;          // staged input vector / q,k,v (16 KiB)
 constexpr int kLdsXBytes = 4 * kMaxK;

@@ -26,12 +26,50 @@
 
 namespace mk {
 
+// Pages of weights a loader wave brings into L2 ahead of its DMA while the
+// page ring is full (the compute waves are staging or waiting on a producer,
+// so HBM would otherwise idle for this CU).  With 32 CUs per XCD, 4 pages
+// ahead hold 2 MiB of the XCD's 4 MiB L2.
+#ifndef MK_PF_PAGES
+#define MK_PF_PAGES 4
+#endif
+constexpr uint32_t kPfPages = MK_PF_PAGES;
+
+// Prefetch cursor of a loader wave: the next page (instruction, page of it)
+// whose lines it has not yet touched.
+struct PfCursor {
+  uint32_t i, p;
+};
+
+// Touch this wave's half of the next page after the DMA cursor (instruction
+// i, page p, ring index g) not yet touched, if it lies less than kPfPages
+// past g.  Only GEMV weight streams are touched; attention pages (the KV
+// cache) are skipped.  Returns false when no page is due.
+DEV bool prefetch_next(InstrCP q, uint32_t n, uint32_t i, uint32_t p, uint32_t g, int v, PfCursor& c,
+                       uint32_t sink, uint32_t voff128) {
+  if (c.i < i || (c.i == i && c.p < p)) c = {i, p};
+  while (c.i < n && c.p >= q[c.i].n_pages) c = {c.i + 1, 0};
+  if (c.i >= n) return false;
+  InstrCP I = q + c.i;
+  if (I->page0 + c.p >= g + kPfPages) return false;
+  if (i_op(I) == OP_GEMV) {
+    const uint32_t u0 = c.p * kUnitsPerPage + uint32_t(v) * kDmaPerPage;
+    const uint32_t units = (I->n_rows * I->row_bytes + kUnit - 1) / kUnit;
+    // the DMA reads the same half page (the stream is padded to it)
+    if (u0 < units) l2_touch(sink, uni64(I->src_ptr + uint64_t(u0) * kUnit), voff128);
+  }
+  c.p++;
+  return true;
+}
+
 DEV void loader(const KArgs& a, InstrCP q, uint32_t n, int v) {
   const uint32_t voff = (threadIdx.x & 63) * 16, voff4k = voff + 4096;
+  const uint32_t voff128 = (threadIdx.x & 63) * 128, sink = uint32_t(size_t(lds)) + kLdsPf;
   uint32_t nd = 0;       // DMAs issued by this wave (kDmaPerPage per page)
   uint32_t g_issue = 0;  // pages issued
   uint32_t g_pub = 0;    // pages published
   uint32_t min_rel = 0;  // oldest page a compute wave may still read
+  PfCursor pf{0, 0};
   for (uint32_t i = 0; i < n; i++) {
     InstrCP I = q + i;
     LoadView L;
@@ -49,6 +87,9 @@ DEV void loader(const KArgs& a, InstrCP q, uint32_t n, int v) {
             publish(g_pub, g_pub + 1, v);
             continue;
           }
+          // (every DMA is published here, so the loads below are the
+          // newest and no page's completion waits on them)
+          if (kPfPages && prefetch_next(q, n, i, p, g, v, pf, sink, voff128)) continue;
           if (aborted() || local_timeout(t0, local_limit())) {
             if (!aborted()) local_abort(STC_LOCAL_TIMEOUT);
             wait_vm0();
