@@ -430,6 +430,15 @@ DEV void dma_lane(uint32_t lds_addr, uint64_t src) {
 
 constexpr uint32_t kDmaPerPage = kUnitsPerPage / kNLoad;  // 8
 
+// Pages of weights a loader wave brings into L2 ahead of its DMA while the
+// page ring is full (the compute waves are staging or waiting on a producer,
+// so HBM would otherwise idle for this CU).  With 32 CUs per XCD, 4 pages
+// ahead hold 2 MiB of the XCD's 4 MiB L2.
+#ifndef MK_PF_PAGES
+#define MK_PF_PAGES 4
+#endif
+constexpr uint32_t kPfPages = MK_PF_PAGES;
+
 // One wave-wide 4 B/lane load with its lanes 128 B (one L2 line) apart: it
 // brings the 8 KiB that a loader wave later copies into a page half into the
 // XCD's L2, so that copy does not wait on HBM.  The words land in a 256 B LDS

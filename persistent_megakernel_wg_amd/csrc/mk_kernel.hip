@@ -26,15 +26,6 @@
 
 namespace mk {
 
-// Pages of weights a loader wave brings into L2 ahead of its DMA while the
-// page ring is full (the compute waves are staging or waiting on a producer,
-// so HBM would otherwise idle for this CU).  With 32 CUs per XCD, 4 pages
-// ahead hold 2 MiB of the XCD's 4 MiB L2.
-#ifndef MK_PF_PAGES
-#define MK_PF_PAGES 4
-#endif
-constexpr uint32_t kPfPages = MK_PF_PAGES;
-
 // Prefetch cursor of a loader wave: the next page (instruction, page of it)
 // whose lines it has not yet touched.
 struct PfCursor {
