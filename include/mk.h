@@ -178,6 +178,12 @@ mk_status mk_build_plan(mk_ctx *ctx, const mk_plan_opts *opts);
  * Appends the new key/value rows at `pos` to the caller's caches.  Asynchronous:
  * a watchdog timeout or device error surfaces from mk_sync (or the next call).
  * d_tokens may alias d_next of the previous step (device-side chaining).
+ * The kernel is one workgroup per CU.  It is launched plainly: a workgroup
+ * fills a CU's LDS and the grid is at most the device's CU count, so every
+ * workgroup becomes resident once its CU is free of other work, and every
+ * wait inside is bounded by the watchdog.  With MK_COOP=1 in the environment
+ * at mk_create, the launch is cooperative instead (the runtime then checks
+ * residency before the launch, at about 16 us more per step).
  * Errors: MK_ERR_NO_PLAN, MK_ERR_INVALID_ARG, MK_ERR_HIP. */
 mk_status mk_decode_step(mk_ctx *ctx, const int32_t *d_tokens, int32_t pos,
                          int32_t *d_next, float *d_logits, void *stream);

@@ -40,7 +40,7 @@ struct mk_ctx {
   uint32_t epoch = 0;
   hipStream_t last_stream = nullptr;
   bool has_step = false;
-  int cooperative = 1;
+  int cooperative = 0;
   int variant = 0;        // kernel launched for the current plan
   uint32_t* d_trace = nullptr;
   uint32_t trace_stride = 0;
@@ -150,8 +150,9 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, int device, mk_ct
   if (!c->w.lm_head) c->w.lm_head = c->w.embed;
   c->device = device;
   c->dev_cus = prop.multiProcessorCount;
-  const char* nc = std::getenv("MK_NONCOOP");
-  c->cooperative = (nc && nc[0] == '1') ? 0 : 1;
+  // plain launch unless MK_COOP=1 (see mk_decode_step in mk.h)
+  const char* co = std::getenv("MK_COOP");
+  c->cooperative = (co && co[0] == '1') ? 1 : 0;
 
   rope_tables(c->cfg, &c->rope_cos, &c->rope_sin);
   *out = c;
