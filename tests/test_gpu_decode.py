@@ -170,6 +170,26 @@ def test_tiny_repeat_is_bitwise_deterministic(need_gpu):
         assert np.array_equal(o, outs[0])
 
 
+def test_cooperative_launch_matches_plain(need_gpu, monkeypatch):
+    # MK_COOP=1 at context creation selects the cooperative launch; the
+    # kernel and plan are the same, so the step is bitwise the same
+    from persistent_megakernel_wg_amd.engine import Engine
+    s = synth.SHAPES["tiny"]
+    _say("case tiny cooperative vs plain launch")
+    w = synth.make_weights(s)
+    outs = []
+    for coop in ("0", "1"):
+        monkeypatch.setenv("MK_COOP", coop)
+        kc, vc = synth.make_kv_cache(s)
+        eng = Engine(s, w, kc, vc)
+        try:
+            outs.append(eng.step(synth.make_tokens(s), s.prefill))
+        finally:
+            eng.close()
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
 def test_abi_errors(need_gpu):
     from persistent_megakernel_wg_amd import binding as B
     from persistent_megakernel_wg_amd.engine import Engine
