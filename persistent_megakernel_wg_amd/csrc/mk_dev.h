@@ -673,20 +673,6 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
   const uint32_t s = lane % LPRA;        // dims [8s, 8s+8)
   const uint32_t jrow = lane / LPRA;     // row within a unit
   const bool trl = a.trace && c.w == 0 && lane == 0;
-  // A one-head tile of a short block is a chain of latencies, and merging
-  // six waves' records costs more than the units they share: wave 0 then
-  // takes every unit, and the others leave at once (their x-slot and page
-  // releases let the next instruction's staging wait for wave 0 only).
-  constexpr uint32_t kSoloUnits = 24;
-  const bool solo = HPT == 1 && (Bat + UPOS - 1) / UPOS <= kSoloUnits;
-  const uint32_t n_w = solo ? 1u : uint32_t(kNComp);
-  if (solo && c.w != 0) {
-    if (lane == 0) {
-      lds_st(C_RELEASED + 4 * c.w, page0 + I->n_pages);
-      lds_st(C_XCONS + 4 * c.w, i + 1);
-    }
-    return true;
-  }
 
   // rotated (RoPE, rotate-half pairing), scaled query slices of every head.
   // A lane's 8 dims [8s, 8s+8) lie in one half, so every operand is two
@@ -755,7 +741,7 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
     for (int e = 0; e < 8; e++) acc[h][e] = fmaf(acc[h][e], sa, w * v[e]);
     m[h] = up ? sc : m[h];
   };
-  for (uint32_t u = c.w; u < n_units; u += n_w) {
+  for (uint32_t u = c.w; u < n_units; u += kNComp) {
     // the v unit streams after every k unit of the tile
     if (!wait_page(page0 + kp + u / kUnitsPerPage, c.fcache)) return false;
     const uint32_t lo = (u % kUnitsPerPage) * kUnit + lane * 16;
@@ -770,7 +756,7 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
       if (valid) update(h, sc, v);
     }
   }
-  if (own && uint32_t(c.w) == n_units % n_w) {
+  if (own && uint32_t(c.w) == n_units % kNComp) {
     // (every tile of the group scores the new row; the one holding the
     // group's first head appends it to the cache)
     float v[8];
@@ -820,29 +806,6 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
       const float mo = __shfl_xor(m[h], off, 64), lo_ = __shfl_xor(l[h], off, 64);
       merge(h, mo, lo_, ao);
     }
-  }
-  if (solo) {
-    // lanes of group 0 hold the merged o~, m and l of their 8 dims
-    if (lane < uint32_t(LPRA)) {
-      const uint32_t head = head0;
-      if (nblk == 1) {
-        uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr) + head * DH + 8 * s;
-#pragma unroll
-        for (int e = 0; e < 8; e++) st_tag(out + e, acc[0][e] / l[0], a.epoch);
-      } else {
-        const size_t tg = head0 / HPT;
-        float* part = reinterpret_cast<float*>(I->res_ptr) + ((tg * nblk + blk) * HPT) * (DH + 2);
-#pragma unroll
-        for (int e = 0; e < 8; e++) st_act(part + 8 * s + e, acc[0][e]);
-        if (s == 0) {
-          st_act(part + DH, m[0]);
-          st_act(part + DH + 1, l[0]);
-        }
-      }
-    }
-    if (trl) trace_put(a, c.cu, i, TR_A_PASS3, now32());
-    if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
-    return true;
   }
   // the wave's record per head after the staged inputs: o~ [DH] | m | l
   constexpr int REC = DH + 2;
