@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mk_isa.h"
 
 #define DEV __device__ __forceinline__
@@ -197,6 +199,26 @@ DEV float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 DEV float rl(float v, int lane) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane)); }
+// The value of lane l ^ OFF, exchanged in registers rather than through the
+// LDS crossbar (what a generic shuffle compiles to): a DPP rotation by 8
+// inside each 16-lane row for OFF = 8, and for 16 and 32 gfx950's lane-swap
+// instructions, whose two results hold the lower and the upper row (half) of
+// each pair; a lane takes the one it is not in.
+template <int OFF>
+DEV float lane_xor(float v) {
+  const uint32_t l = threadIdx.x & 63;
+  if constexpr (OFF == 8) {
+    return dpp<0x128>(v);  // row_ror:8
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((l & 16) ? r[0] : r[1]);
+  } else if constexpr (OFF == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((l & 32) ? r[0] : r[1]);
+  } else {
+    return __shfl_xor(v, OFF, 64);
+  }
+}
 // every lane receives the sum of its 16-lane row
 DEV float row_sum16(float v) {
   v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
@@ -658,7 +680,7 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
   constexpr int UPOS = kUnit / (2 * DH);  // rows per 1 KiB unit
   constexpr int HALF = DH / 2;
   constexpr int OUT = HPT * DH;           // outputs of the group
-  static_assert(64 % LPRA == 0 && HPT >= 1 && HPT <= 8, "attention shape");
+  static_assert(64 % LPRA == 0 && LPRA >= 4 && LPRA <= 32 && HPT >= 1 && HPT <= 8, "attention shape");
   const uint32_t g = I->aux[0], blk = I->aux[1], Bat = I->aux[2], nblk = I->aux[3], kp = I->aux[4];
   const uint32_t h0 = I->row0;                  // first query head of the tile in its group
   const uint32_t head0 = g * uint32_t(a.hpg) + h0;  // ... in the layer
@@ -796,17 +818,27 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
     for (int e = 0; e < 8; e++) acc[h][e] = acc[h][e] * sa + ao[e] * sb;
     m[h] = mn;
   };
-#pragma unroll
-  for (int off = LPRA; off < 64; off <<= 1) {
+  // register exchanges in the one-sequence kernel; the batched kernel keeps
+  // the generic shuffle, which measured faster there
+  auto xch = [](auto off_c, float v) {
+    constexpr int OFF = decltype(off_c)::value;
+    if constexpr (std::is_same<Lay, LayA>::value) return lane_xor<OFF>(v);
+    else return __shfl_xor(v, OFF, 64);
+  };
+  auto merge_step = [&](auto off_c) {
 #pragma unroll
     for (int h = 0; h < HPT; h++) {
       float ao[8];
 #pragma unroll
-      for (int e = 0; e < 8; e++) ao[e] = __shfl_xor(acc[h][e], off, 64);
-      const float mo = __shfl_xor(m[h], off, 64), lo_ = __shfl_xor(l[h], off, 64);
+      for (int e = 0; e < 8; e++) ao[e] = xch(off_c, acc[h][e]);
+      const float mo = xch(off_c, m[h]), lo_ = xch(off_c, l[h]);
       merge(h, mo, lo_, ao);
     }
-  }
+  };
+  if constexpr (LPRA <= 4) merge_step(std::integral_constant<int, 4>{});
+  if constexpr (LPRA <= 8) merge_step(std::integral_constant<int, 8>{});
+  if constexpr (LPRA <= 16) merge_step(std::integral_constant<int, 16>{});
+  merge_step(std::integral_constant<int, 32>{});
   // the wave's record per head after the staged inputs: o~ [DH] | m | l
   constexpr int REC = DH + 2;
   constexpr int PBASE = (HPT * DH + 3 * DH + 3) & ~3;
