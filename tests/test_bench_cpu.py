@@ -35,3 +35,21 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=60, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_moe_fixed_bytes_from_the_architecture():
+    # bench.py's algorithmic bytes for the MoE shape: the plan's routing-
+    # independent weight bytes plus 6 * d * Fe per selected expert and layer
+    from persistent_megakernel_wg_amd import binding as B
+    s = synth.SHAPES["moe_b8_ctx2048"]
+    d, q, kv, E, Fe, V, L, nb = 2048, 16 * 128, 4 * 128, 64, 1024, 65536, 24, 8
+    assert (s.hidden, s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim, s.n_experts, s.expert_ffn,
+            s.vocab, s.n_layers, s.batch) == (d, q, kv, E, Fe, V, L, nb)
+    bf16 = 2
+    attn = bf16 * (d * q + 2 * d * kv + q * d)   # Wq, Wk, Wv, Wo
+    router = bf16 * E * d
+    fixed = L * (attn + router) + bf16 * V * d + bf16 * d * (L + 1) + bf16 * nb * d
+    #        layers                untied LM head   one norm per layer + final   embedding rows
+    assert fixed == 778_178_560
+    summ, _ = B.mk_plan_check(B.config_from_shape(s), 256)
+    assert summ["weight_bytes"] == fixed
