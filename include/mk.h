@@ -157,6 +157,11 @@ typedef struct {
 } mk_plan_summary;
 
 /* Create a context on `device` for this model and these caller-owned buffers.
+ * Source: the pages define no programming interface.  This call sets up the
+ * resident decode of Cohere's write-up (airebao.com, «Megakernel 是什么»: one
+ * persistent kernel per step over state the host prepared) for one model; the
+ * model is the Llama-style decoder of the Llama-1B megakernel write-up
+ * (rocketrecap.com summary, "Megakernel: The Core Solution").
  * Validates the shape, allocates the arena and builds the RoPE tables.
  * Errors: MK_ERR_INVALID_ARG (NULL/inconsistent arguments), MK_ERR_UNSUPPORTED
  * (shape outside the kernel's code paths), MK_ERR_HIP, MK_ERR_OOM. */
@@ -170,6 +175,9 @@ mk_status mk_create(const mk_config *cfg, const mk_weights *w, int device, mk_ct
 mk_status mk_build_plan(mk_ctx *ctx, const mk_plan_opts *opts);
 
 /* Enqueue one decode step on `stream` (a hipStream_t; NULL = default stream).
+ * Source: the whole forward pass of one token as one kernel launch (the
+ * javascript.cn article, "Megakernel：从零设计的融合思路"; airebao.com,
+ * «Megakernel 是什么»); the pages define no signature.
  *   d_tokens: device int32 [B], the input token of each sequence;
  *   pos:      position of the new token (= cached positions), 0 <= pos < max_seq;
  *   d_next:   device int32 [B], receives the greedy next token;
@@ -189,18 +197,28 @@ mk_status mk_decode_step(mk_ctx *ctx, const int32_t *d_tokens, int32_t pos,
                          int32_t *d_next, float *d_logits, void *stream);
 
 /* Wait for the context's last step and read the device status word.
+ * Source: none on the pages (they define no interface); the status word
+ * reports the bounded waits of the counter system (rocketrecap.com summary,
+ * "Custom Synchronization Mechanism") that ran out.
  * Returns MK_ERR_TIMEOUT / MK_ERR_DEVICE with a message if the kernel reported
  * one; the counters are then reset so the context can be used again. */
 mk_status mk_sync(mk_ctx *ctx);
 
-/* Destroy the context and free the arena.  NULL is accepted (MK_OK). */
+/* Destroy the context and free the arena.  NULL is accepted (MK_OK).
+ * Source: none on the pages (they define no interface); the counterpart of
+ * mk_create. */
 mk_status mk_destroy(mk_ctx *ctx);
 
 /* Message for the last error on ctx (or of the calling thread if ctx is NULL).
- * The string is owned by the library and valid until the next call. */
+ * The string is owned by the library and valid until the next call.
+ * Source: none on the pages (they define no interface); error reporting of
+ * this C boundary. */
 const char *mk_last_error(const mk_ctx *ctx);
 
-/* Routing statistics of the mixture-of-experts decoder: per_layer[l] receives
+/* Routing statistics of the mixture-of-experts decoder (Cohere's write-up,
+ * airebao.com, «为什么值得做»: each step streams only the selected experts'
+ * weights; this counts them so that a caller can price the step in bytes).
+ * per_layer[l] receives
  * the number of distinct experts the router selected in layer l (union over
  * the batch), summed over the steps since the last reset; each selected
  * expert streams 6 * hidden * expert_ffn weight bytes.  n >= n_layers.
@@ -209,16 +227,23 @@ const char *mk_last_error(const mk_ctx *ctx);
  * MK_ERR_HIP. */
 mk_status mk_route_stats(mk_ctx *ctx, int64_t *per_layer, int32_t n, int reset);
 
-/* Summary of the context's current plan.  Errors: MK_ERR_NO_PLAN. */
+/* Summary of the context's current plan (the host-side static schedule of
+ * the javascript.cn article, "Megakernel：从零设计的融合思路").
+ * Errors: MK_ERR_NO_PLAN. */
 mk_status mk_plan_info(const mk_ctx *ctx, mk_plan_summary *out);
 
-/* Host-only planning for tests and tools: build and verify a plan for
+/* Host-only planning for tests and tools (the same static schedule as
+ * mk_build_plan, javascript.cn article, "Megakernel：从零设计的融合思路"):
+ * build and verify a plan for
  * `n_cus` workgroups without a device or buffers.  Writes a text report
  * (truncated to report_len, may be NULL) and the summary (may be NULL). */
 mk_status mk_plan_check(const mk_config *cfg, const mk_plan_opts *opts, int32_t n_cus,
                         mk_plan_summary *summary, char *report, size_t report_len);
 
 /* ---- diagnostics -------------------------------------------------------
+ * Source: the per-stage runtime breakdown of the Llama-1B write-up
+ * (rocketrecap.com summary, "Detailed Runtime Breakdown") is what these
+ * stamps reproduce for this kernel.
  * Per-instruction timestamps of the next steps (s_memrealtime, 100 MHz, low
  * 32 bits): for every CU and queue slot 16 words
  *   {start, deps satisfied, inputs staged, leader's items done, signal,

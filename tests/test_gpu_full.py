@@ -1,25 +1,71 @@
 """Full-size GPU parity: the workloads at their real shapes, in the launch
-configuration bench.py times (default plan), against the CPU oracle."""
+configuration bench.py times (default plan), against the CPU oracle.
+
+Bars, per step and per sequence:
+  * relative L2 error of the logits <= TOL (the contract) and <= TIGHT;
+  * element-wise: max |logit - oracle| <= ELEM * RMS(oracle logits);
+  * the same greedy token as the oracle, the device free-running on its own
+    chained tokens (so every step's input agrees only if every earlier token
+    did);
+  * appended K/V rows within one bf16 step (plus the KV floor of
+    test_gpu_decode.kv_rows_close), every pre-filled row untouched.
+"""
+import concurrent.futures as cf
+
 import numpy as np
 import pytest
 
 from oracle import DecoderOracle
 from persistent_megakernel_wg_amd import synth
-from test_gpu_decode import kv_rows_close
+from test_gpu_decode import TIGHT, TOL, kv_rows_close
 
 pytestmark = pytest.mark.gpu
 
-TOL = 1e-2
+# A logit is a d-term dot product of an LM-head row with the final normed
+# vector; the float32 path perturbs that vector by about its rel-L2 error in a
+# random direction, so each logit's error is of the order of rel_l2 * RMS(ref)
+# and the largest of 10^5 such errors stays within a few times that.  With
+# rel_l2 <= TIGHT the bar below leaves a factor of 10 for the tail, while one
+# wrong row (an error of the order of RMS(ref)) fails it.
+ELEM = 10 * TIGHT
 
 
 def rel_l2(a, b):
     return float(np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b))
 
 
-def _greedy_case(name, steps, keep_f64=True):
+def elem_err(a, b):
+    """max |a - b| in units of RMS(b)."""
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(np.asarray(a, np.float64) - b)) / np.sqrt(np.mean(b * b)))
+
+
+def keep_f64(shape) -> bool:
+    """Keep the oracle's widened float64 weights between steps when the host
+    has room for them (a speed choice only: the arithmetic is the same)."""
+    try:
+        import psutil
+        avail = psutil.virtual_memory().available
+    except Exception:
+        return False
+    f64 = 4 * sum(int(np.prod(v)) * 2 for v in synth.weight_shapes(shape).values())
+    return avail > 2 * f64 + (16 << 30)
+
+
+def _check_logits(tag, got, ref):
+    err, el = rel_l2(got, ref), elem_err(got, ref)
+    print("  %s: rel_l2 %.3e  max elem %.3e RMS" % (tag, err, el), flush=True)
+    assert err <= TOL and err <= TIGHT, (tag, err)
+    assert el <= ELEM, (tag, el)
+    return err, el
+
+
+def _greedy_case(name, steps, chained_too=False):
     from persistent_megakernel_wg_amd.engine import Engine
     s = synth.SHAPES[name]
-    print("case %s: %d greedy steps from position %d" % (name, steps, s.prefill), flush=True)
+    keep = keep_f64(s)
+    print("case %s: %d greedy steps from position %d (oracle keeps f64: %s)"
+          % (name, steps, s.prefill, keep), flush=True)
     w = synth.make_weights(s)
     kc, vc = synth.make_kv_cache(s)
     tok = synth.make_tokens(s)
@@ -27,56 +73,74 @@ def _greedy_case(name, steps, keep_f64=True):
     try:
         lgs, toks = eng.generate(tok, s.prefill, steps, logits=True)
         kg, vg = eng.read_kv()
+        toks2 = kg2 = None
+        if chained_too:
+            # the launch sequence bench.py times: back to back on one
+            # stream, no logits, no host synchronisation between steps
+            i16 = eng.torch.int16
+            eng.k_cache.view(i16).copy_(eng.torch.from_numpy(kc.view(np.int16)))
+            eng.v_cache.view(i16).copy_(eng.torch.from_numpy(vc.view(np.int16)))
+            _, toks2 = eng.generate(tok, s.prefill, steps, logits=False)
+            kg2, vg2 = eng.read_kv()
     finally:
         eng.close()
-    orc = DecoderOracle(s, w, keep_f64=keep_f64)
+    print("  device steps done", flush=True)
+    orc = DecoderOracle(s, w, keep_f64=keep)
     k_ref, v_ref = kc.copy(), vc.copy()
     t = tok
-    worst = 0.0
+    worst = [0.0, 0.0]
+    ref_toks = []
     for i in range(steps):
         ref_lg, ref_nx = orc.step(t, s.prefill + i, k_ref, v_ref)
-        err = rel_l2(lgs[i][0], ref_lg[0])
-        worst = max(worst, err)
-        print("  step %d: rel_l2 %.3e token %d / oracle %d" % (i, err, toks[i][0], ref_nx[0]), flush=True)
+        ref_toks.append(int(ref_nx[0]))
+        err, el = _check_logits("step %d token %d / oracle %d" % (i, toks[i][0], ref_nx[0]),
+                                lgs[i][0], ref_lg[0])
+        worst = [max(worst[0], err), max(worst[1], el)]
         if toks[i][0] != ref_nx[0]:
             top = np.sort(ref_lg[0])[-2:]
             pytest.fail("step %d: token %d vs oracle %d (oracle top-2 margin %.3e)"
                         % (i, toks[i][0], ref_nx[0], top[1] - top[0]))
-        assert err <= TOL, (i, err)
         t = ref_nx
-    print("  worst rel_l2 %.3e" % worst, flush=True)
+    print("  worst rel_l2 %.3e, worst element %.3e RMS" % tuple(worst), flush=True)
     # appended rows within one bf16 step; the rest of the cache untouched
     span = slice(s.prefill, s.prefill + steps)
     for got, ref in ((kg, k_ref), (vg, v_ref)):
         assert kv_rows_close(got[:, :, :, span], ref[:, :, :, span])
         assert np.array_equal(got[:, :, :, :s.prefill], ref[:, :, :, :s.prefill])
+    if chained_too:
+        assert [int(x[0]) for x in toks2] == ref_toks
+        # the synchronised and the back-to-back runs are the same computation
+        assert np.array_equal(kg2, kg) and np.array_equal(vg2, vg)
+        print("  back-to-back launches without logits: same tokens and caches", flush=True)
 
 
 @pytest.mark.timeout(900)
 def test_llama1b_ctx128_32_greedy_steps(need_gpu):
-    _greedy_case("llama1b_ctx128", 32)
+    _greedy_case("llama1b_ctx128", 32, chained_too=True)
 
 
 @pytest.mark.timeout(900)
-def test_llama1b_ctx8192_4_steps(need_gpu):
-    _greedy_case("llama1b_ctx8192", 4)
+def test_llama1b_ctx8192_32_greedy_steps(need_gpu):
+    _greedy_case("llama1b_ctx8192", 32)
 
 
-@pytest.mark.timeout(900)
-def test_llama8b_ctx2048_1_step(need_gpu):
-    _greedy_case("llama8b_ctx2048", 1, keep_f64=False)
+@pytest.mark.timeout(1200)
+def test_llama8b_ctx2048_8_greedy_steps(need_gpu):
+    _greedy_case("llama8b_ctx2048", 8)
 
 
-@pytest.mark.timeout(1100)
-def test_moe_b8_ctx2048_2_steps_sampled(need_gpu):
-    """The batch-8 MoE shape at full size: two device-chained greedy steps,
-    checked against the oracle on two of the eight sequences (the sequences
-    of a step are independent, so each is a full check of its own outputs)."""
+@pytest.mark.timeout(1500)
+def test_moe_b8_ctx2048_4_steps_all_sequences(need_gpu):
+    """The batch-8 MoE shape at full size: four device-chained greedy steps,
+    every sequence checked against the oracle.  The sequences of a step are
+    independent, so the oracle runs them in parallel threads, each on its
+    own tokens; a step's inputs agree with the device's because every
+    earlier token is checked equal."""
     from persistent_megakernel_wg_amd.engine import Engine
     s = synth.SHAPES["moe_b8_ctx2048"]
-    steps, sample = 2, [0, 5]
-    print("case %s: %d greedy steps from position %d, sequences %s checked"
-          % (s.name, steps, s.prefill, sample), flush=True)
+    steps = 4
+    print("case %s: %d greedy steps from position %d, all %d sequences"
+          % (s.name, steps, s.prefill, s.batch), flush=True)
     w = synth.make_weights(s)
     kc, vc = synth.make_kv_cache(s)
     tok = synth.make_tokens(s)
@@ -90,18 +154,28 @@ def test_moe_b8_ctx2048_2_steps_sampled(need_gpu):
     print("  device steps done", flush=True)
     orc = DecoderOracle(s, w, keep_f64=False)
     k_ref, v_ref = kc.copy(), vc.copy()
-    t = tok.copy()
+
+    def run_seq(b):
+        # one sequence's greedy steps (writes only its own cache rows)
+        t = tok.copy()
+        out = []
+        for i in range(steps):
+            lg, nx = orc.step(t, s.prefill + i, k_ref, v_ref, seqs=[b])
+            out.append((lg[b].copy(), int(nx[b])))
+            print("  oracle sequence %d step %d done" % (b, i), flush=True)
+            t = t.copy()
+            t[b] = nx[b]
+        return out
+
+    with cf.ThreadPoolExecutor(max_workers=s.batch) as ex:
+        ref = list(ex.map(run_seq, range(s.batch)))
     for i in range(steps):
-        ref_lg, ref_nx = orc.step(t, s.prefill + i, k_ref, v_ref, seqs=sample)
-        for b in sample:
-            err = rel_l2(lgs[i][b], ref_lg[b])
-            print("  step %d seq %d: rel_l2 %.3e token %d / oracle %d"
-                  % (i, b, err, toks[i][b], ref_nx[b]), flush=True)
-            assert err <= TOL, (i, b, err)
-            assert toks[i][b] == ref_nx[b], (i, b)
-        t = toks[i].copy()
+        for b in range(s.batch):
+            ref_lg, ref_nx = ref[b][i]
+            _check_logits("step %d seq %d token %d / oracle %d" % (i, b, toks[i][b], ref_nx),
+                          lgs[i][b], ref_lg)
+            assert toks[i][b] == ref_nx, (i, b)
     span = slice(s.prefill, s.prefill + steps)
-    for got, ref in ((kg, k_ref), (vg, v_ref)):
-        for b in sample:
-            assert kv_rows_close(got[:, b, :, span], ref[:, b, :, span])
-        assert np.array_equal(got[:, :, :, :s.prefill], ref[:, :, :, :s.prefill])
+    for got, r in ((kg, k_ref), (vg, v_ref)):
+        assert kv_rows_close(got[:, :, :, span], r[:, :, :, span])
+        assert np.array_equal(got[:, :, :, :s.prefill], r[:, :, :, :s.prefill])
