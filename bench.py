@@ -54,37 +54,60 @@ def traffic_from_profiles(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline_moe(shape, weights, kc, vc, tokens):
-    """Time the CPU oracle on one sequence of one step of the batched workload
-    (the sequences of a step are independent) and scale it to the batch."""
-    import numpy as np
-    from oracle import DecoderOracle
+def host_info():
+    """Host CPU model, logical cores and the BLAS thread count numpy uses."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        blas = None
+    return {"cpu_model": model, "host_cores": os.cpu_count(), "blas_threads": blas}
+
+
+def _one_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1)
+    except Exception:
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def cpu_baseline_moe(shape, weights, kc, vc, tokens):
+    """Time the float64 CPU oracle on one sequence of one step of the batched
+    workload (the sequences of a step are independent) and scale it to the
+    batch."""
+    import numpy as np
+    from oracle import DecoderOracle
+    hi = host_info()
     orc = DecoderOracle(shape, weights, keep_f64=False)
     k, v = kc.copy(), vc.copy()
     t0 = time.perf_counter()
     orc.step(np.asarray(tokens), shape.prefill, k, v, seqs=[0])
     one = time.perf_counter() - t0
-    return {"value": round(1e6 * one * shape.batch, 1), "unit": "us/step", "cores": threads,
-            "kind": "oracle",
+    return {"value": round(1e6 * one * shape.batch, 1), "unit": "us/step",
+            "cores": hi["blas_threads"] or hi["host_cores"], "kind": "oracle",
+            "oracle": "float64 (bf16 weights widened exactly per use)", **hi,
             "sample": "%s: sequence 0 of one float64 decode step at position %d (%.1f s, weights "
                       "widened per use), times %d sequences" % (shape.name, shape.prefill, one,
                                                                 shape.batch)}
 
 
 def cpu_baseline(shape, weights, kc, vc, tokens, budget_s: float = 20.0):
-    """Time the CPU oracle on a bounded sample of the same workload."""
+    """Time the float64 CPU oracle on a bounded sample of the same workload:
+    with numpy's BLAS on all its threads, then on one thread."""
     import numpy as np
     from oracle import DecoderOracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    hi = host_info()
     orc = DecoderOracle(shape, weights)
     k, v = kc.copy(), vc.copy()
     tok = np.asarray(tokens)
@@ -99,10 +122,21 @@ def cpu_baseline(shape, weights, kc, vc, tokens, budget_s: float = 20.0):
         times.append(time.perf_counter() - t0)
         pos += 1
     us = 1e6 * sum(times) / len(times)
-    return {"value": round(us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+    # the same oracle on one thread, for a few steps of the budget
+    t1 = []
+    with _one_thread():
+        while sum(t1) < budget_s / 4 and pos < shape.max_seq and len(t1) < 8:
+            t0 = time.perf_counter()
+            _, tok = orc.step(tok, pos, k, v)
+            t1.append(time.perf_counter() - t0)
+            pos += 1
+    return {"value": round(us, 1), "unit": "us/step", "cores": hi["blas_threads"] or hi["host_cores"],
+            "kind": "oracle", "oracle": "float64 (bf16 weights widened exactly once)", **hi,
+            "value_1thread": round(1e6 * sum(t1) / max(1, len(t1)), 1) if t1 else None,
             "sample": "%s: %d float64 decode steps at positions %d..%d after one warm-up step "
-                      "(%.1f s, weight widening) on the host" % (
-                          shape.name, len(times), shape.prefill + 1, pos - 1, warm)}
+                      "(%.1f s, weight widening) with BLAS on %s threads, then %d steps on one "
+                      "thread" % (shape.name, len(times), shape.prefill + 1,
+                                  shape.prefill + len(times), warm, hi["blas_threads"], len(t1))}
 
 
 def main() -> int:
@@ -200,6 +234,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "precision": "bf16 weights and KV cache, fp32 arithmetic",
         "data": "synthetic",
         "config": {"workload": shape.name, "layers": shape.n_layers, "hidden": shape.hidden,
                    "q_heads": shape.n_q_heads, "kv_heads": shape.n_kv_heads,

@@ -86,6 +86,9 @@ def analyse(tr: np.ndarray, batched: bool = False) -> dict:
             r["staged"].append(rel(np.array(w[TR["STAGED"]])))
             r["end"].append(rel(np.array(end)))
             r["pagewait"].append(int(w[TR["PAGEWAIT"]]) * TICK_US)
+            # phases inside the instruction, per CU (leader's stamps)
+            for name in ("XREADY", "ITEM0", "ITEMS", "VISIBLE"):
+                r[name.lower()].append(rel(np.array(w[TR[name]])) if w[TR[name]] else np.nan)
     order = sorted(rec.keys(), key=lambda k: (k[0], float(np.median(rec[k]["start"])), k[2]))
     rows = []
     prev_end = 0.0
@@ -97,7 +100,17 @@ def analyse(tr: np.ndarray, batched: bool = False) -> dict:
         st_med = float(np.median(staged))
         handover = max(0.0, min(st_med, end_max) - prev_end)
         work = max(0.0, end_max - max(prev_end, min(st_med, end_max)))
-        rows.append({"layer": key[0], "stage": key[1], "part": key[2], "cus": len(end),
+        def med(a, b):
+            d = np.array(r[a], dtype=np.float64) - np.array(r[b], dtype=np.float64)
+            d = d[np.isfinite(d)]
+            return float(np.median(d)) if d.size else float("nan")
+        phases = {"staged_to_xready_us": med("xready", "staged"),
+                  "xready_to_item0_us": med("item0", "xready"),
+                  "item0_to_items_us": med("items", "item0"),
+                  "items_to_end_us": med("end", "items"),
+                  "staged_to_end_us": med("end", "staged"),
+                  "start_to_staged_us": med("staged", "start")}
+        rows.append({"layer": key[0], "stage": key[1], "part": key[2], "cus": len(end), **phases,
                      "staged_median_us": st_med, "end_median_us": float(np.median(end)),
                      "end_max_us": end_max, "handover_us": handover, "work_us": work,
                      "pagewait_median_us": float(np.median(r["pagewait"]))})
@@ -131,6 +144,15 @@ def report(res: dict, title: str) -> str:
             out.append("| %d | %s | %d | %d | %.2f | %.2f | %.2f | %.2f |" % (
                 r["layer"], r["stage"], r["part"], r["cus"], r["staged_median_us"],
                 r["end_median_us"], r["end_max_us"], r["pagewait_median_us"]))
+    out += ["", "Inside one instruction of the same layer (medians over CUs of per-CU differences, us):", "",
+            "| stage | part | start->staged | staged->x ready | x ready->first item | first item->items done "
+            "| items done->end | staged->end |", "|---|---|---|---|---|---|---|---|"]
+    for r in res["rows"]:
+        if r["layer"] == mid or r["stage"] == "lm_head":
+            out.append("| %s | %d | %.2f | %.2f | %.2f | %.2f | %.2f | %.2f |" % (
+                r["stage"], r["part"], r["start_to_staged_us"], r["staged_to_xready_us"],
+                r["xready_to_item0_us"], r["item0_to_items_us"], r["items_to_end_us"],
+                r["staged_to_end_us"]))
     return "\n".join(out)
 
 
