@@ -153,7 +153,9 @@ typedef struct {
                               for this shape (the Llama-3.2-1B, Llama-3-8B
                               and small test decoder geometries; MoE: 1 for
                               4 query heads per group of head_dim 128)   */
-  int32_t reserved;
+  int32_t scratch_bytes;   /* device scratch one step of this plan uses in
+                              mk_decode_step_noalloc (must not exceed
+                              MK_NOALLOC_SCRATCH_BYTES)                   */
 } mk_plan_summary;
 
 /* Create a context on `device` for this model and these caller-owned buffers.
@@ -195,6 +197,29 @@ mk_status mk_build_plan(mk_ctx *ctx, const mk_plan_opts *opts);
  * Errors: MK_ERR_NO_PLAN, MK_ERR_INVALID_ARG, MK_ERR_HIP. */
 mk_status mk_decode_step(mk_ctx *ctx, const int32_t *d_tokens, int32_t pos,
                          int32_t *d_next, float *d_logits, void *stream);
+
+/* Bytes of the fixed per-device scratch array of mk_decode_step_noalloc. */
+#define MK_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+/* mk_decode_step without any device allocation, for callers that cannot
+ * allocate while they decode: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, kernels and results
+ * as mk_decode_step.  The step's scratch (tagged activations, counters, argmax
+ * slots, status word; mk_plan_summary.scratch_bytes of it) lives in a fixed
+ * file-scope device array of MK_NOALLOC_SCRATCH_BYTES bytes, one per GPU,
+ * held until the process ends, instead of the context's arena.  Each call
+ * first clears the part it uses (a fill kernel on `stream`), then runs the
+ * step, so a call does not depend on what an earlier call (of any context)
+ * left there.  All contexts on one GPU share the array: calls that overlap
+ * on one GPU (other streams, other threads) race and must not be issued.
+ * Allocates nothing and calls no allocating routine; the plan (built by
+ * mk_build_plan, which does allocate) is reused.  Errors and the device
+ * status word surface from mk_sync as for mk_decode_step.
+ * Errors: MK_ERR_NO_PLAN, MK_ERR_INVALID_ARG (as mk_decode_step),
+ * MK_ERR_UNSUPPORTED (the plan needs more scratch than
+ * MK_NOALLOC_SCRATCH_BYTES), MK_ERR_HIP. */
+mk_status mk_decode_step_noalloc(mk_ctx *ctx, const int32_t *d_tokens, int32_t pos,
+                                 int32_t *d_next, float *d_logits, void *stream);
 
 /* Wait for the context's last step and read the device status word.
  * Source: none on the pages (they define no interface); the status word

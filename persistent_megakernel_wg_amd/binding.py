@@ -53,15 +53,16 @@ class MkPlanSummary(ctypes.Structure):
         "n_cus", "n_instr", "max_queue", "n_counters", "lds_bytes", "n_pages", "page_bytes",
         "attn_block", "attn_tiles", "mlp_chunks")] + [
         (n, ctypes.c_int64) for n in ("weight_bytes", "max_cu_bytes", "min_cu_bytes")] + [
-        ("kernel_variant", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+        ("kernel_variant", ctypes.c_int32), ("scratch_bytes", ctypes.c_int32)]
 
     def as_dict(self):
-        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+        return {n: getattr(self, n) for n, _ in self._fields_}
 
 
 EXPORTS = ("mk_create", "mk_build_plan", "mk_decode_step", "mk_sync", "mk_destroy",
            "mk_last_error", "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read",
-           "mk_route_stats")
+           "mk_route_stats", "mk_decode_step_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # MK_NOALLOC_SCRATCH_BYTES
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -79,6 +80,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               ctypes.POINTER(vp)]
     lib.mk_build_plan.argtypes = [vp, ctypes.POINTER(MkPlanOpts)]
     lib.mk_decode_step.argtypes = [vp, vp, i32, vp, vp, vp]
+    lib.mk_decode_step_noalloc.argtypes = [vp, vp, i32, vp, vp, vp]
     lib.mk_sync.argtypes = [vp]
     lib.mk_destroy.argtypes = [vp]
     lib.mk_last_error.argtypes = [vp]
@@ -90,7 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_trace_read.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), ctypes.c_size_t,
                                   ctypes.POINTER(i32)]
     lib.mk_route_stats.argtypes = [vp, ctypes.POINTER(ctypes.c_int64), i32, ctypes.c_int]
-    for name in ("mk_create", "mk_build_plan", "mk_decode_step", "mk_sync", "mk_destroy",
+    for name in ("mk_create", "mk_build_plan", "mk_decode_step", "mk_decode_step_noalloc", "mk_sync",
+                 "mk_destroy",
                  "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read",
                  "mk_route_stats"):
         getattr(lib, name).restype = st
@@ -139,6 +142,12 @@ def mk_decode_step(ctx: int, d_tokens: int, pos: int, d_next: int, d_logits: int
                    stream: int = 0) -> None:
     lib = load_library()
     _check(lib.mk_decode_step(ctx, d_tokens, pos, d_next, d_logits or None, stream or None), ctx)
+
+
+def mk_decode_step_noalloc(ctx: int, d_tokens: int, pos: int, d_next: int, d_logits: int = 0,
+                           stream: int = 0) -> None:
+    lib = load_library()
+    _check(lib.mk_decode_step_noalloc(ctx, d_tokens, pos, d_next, d_logits or None, stream or None), ctx)
 
 
 def mk_sync(ctx: int) -> None:

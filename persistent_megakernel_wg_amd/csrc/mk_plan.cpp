@@ -1600,7 +1600,44 @@ void summarize(const PlanInput& in, const Plan& p, mk_plan_summary* s) {
   s->weight_bytes = p.weight_bytes;
   s->max_cu_bytes = p.max_cu_bytes;
   s->min_cu_bytes = p.min_cu_bytes;
+  const uint64_t sc = scratch_layout(p).total;
+  s->scratch_bytes = int32_t(std::min<uint64_t>(sc, uint64_t(INT32_MAX)));
   (void)in;
+}
+
+ScratchLayout scratch_layout(const Plan& p) {
+  ScratchLayout s;
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t r = off;
+    off = align256(off + bytes);
+    return r;
+  };
+  s.act = take(p.arena.rope_cos);
+  s.slots = take(p.arena.status - p.arena.lm_slots);
+  s.status = take(64);
+  s.route = take(4 * 128);
+  s.ctr_bytes = uint64_t(std::max(1, p.n_counters)) * kCtrSpread * kCtrStride * 4;
+  s.ctr = take(s.ctr_bytes);
+  s.total = off;
+  return s;
+}
+
+std::vector<Instr> rebase_to_scratch(const Plan& p, uint64_t arena_base, uint64_t scratch_base) {
+  const uint64_t lo = arena_base, hi = arena_base + p.arena.rope_cos;
+  auto mv = [&](uint64_t& v) {
+    if (v >= lo && v < hi) v = scratch_base + (v - lo);
+  };
+  std::vector<Instr> out = p.instrs;
+  for (Instr& I : out) {
+    mv(I.in_ptr);
+    mv(I.res_ptr);
+    mv(I.out_ptr);
+    mv(I.gain_ptr);
+    mv(I.src_ptr);
+    for (int k = 0; k < 3; k++) mv(I.seg_ptr[k]);
+  }
+  return out;
 }
 
 std::string plan_report(const PlanInput& in, const Plan& p) {

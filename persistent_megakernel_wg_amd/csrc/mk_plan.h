@@ -99,6 +99,19 @@ std::string plan_report(const PlanInput& in, const Plan& p);
 
 void summarize(const PlanInput& in, const Plan& p, mk_plan_summary* s);
 
+// Scratch of one step in the fixed device array of mk_decode_step_noalloc
+// (byte offsets): the tagged activations (the arena's [0, rope_cos)), the
+// argmax slots, the status word, the routing statistics and the counters.
+// The whole span is cleared before every such step.
+struct ScratchLayout {
+  uint64_t act, slots, status, route, ctr, ctr_bytes, total;
+};
+ScratchLayout scratch_layout(const Plan& p);
+
+// The plan's instructions with every arena activation address moved into the
+// scratch at `scratch_base` (weights, packed stream and caches unchanged).
+std::vector<Instr> rebase_to_scratch(const Plan& p, uint64_t arena_base, uint64_t scratch_base);
+
 // GEMV row geometry for input length K: 1 KiB units per row (nit) and rows
 // per unit (rpu).  false if the kernel has no code path for K.
 bool gemv_geometry(int K, int* nit, int* rpu);

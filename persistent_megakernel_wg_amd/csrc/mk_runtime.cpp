@@ -20,6 +20,8 @@ extern "C" hipError_t mk_launch_batched(const mk::KArgs* args, int n_cus, hipStr
 extern "C" int mk_pick_batched(int hpt, int dh);
 extern "C" hipError_t mk_launch_pack(const mk::PackCopy* copies, uint32_t n, void* base,
                                      hipStream_t stream);
+extern "C" hipError_t mk_scratch_init(int device, void** out);
+extern "C" hipError_t mk_launch_fill_zero(void* p, uint64_t bytes, hipStream_t stream);
 
 struct mk_ctx {
   mk_config cfg;
@@ -44,6 +46,13 @@ struct mk_ctx {
   int variant = 0;        // kernel launched for the current plan
   uint32_t* d_trace = nullptr;
   uint32_t trace_stride = 0;
+  // mk_decode_step_noalloc: this device's fixed scratch array, its layout for
+  // the current plan and the plan's instructions rebased into it (null when
+  // the plan needs more than MK_NOALLOC_SCRATCH_BYTES)
+  void* scratch = nullptr;
+  mk::ScratchLayout sc{};
+  mk::Instr* d_instrs_static = nullptr;
+  bool last_static = false;   // the last step ran on the scratch array
 };
 
 namespace {
@@ -73,6 +82,8 @@ void free_plan(mk_ctx* c) {
   if (c->d_instrs) (void)hipFree(c->d_instrs);
   if (c->d_qoff) (void)hipFree(c->d_qoff);
   if (c->d_counters) (void)hipFree(c->d_counters);
+  if (c->d_instrs_static) (void)hipFree(c->d_instrs_static);
+  c->d_instrs_static = nullptr;
   c->arena = nullptr;
   c->d_instrs = nullptr;
   c->d_qoff = nullptr;
@@ -144,7 +155,12 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, int device, mk_ct
   for (const void* ptr : aligned)
     if (uintptr_t(ptr) % 16)
       return fail(nullptr, MK_ERR_INVALID_ARG, "mk_create: weight and cache pointers must be 16-byte aligned");
+  // the no-allocation entry point's scratch array on this device (looked up
+  // once per device, with the device current)
+  void* scratch = nullptr;
+  if ((e = mk_scratch_init(device, &scratch)) != hipSuccess) return hip_fail(nullptr, e, "mk_create: scratch array");
   mk_ctx* c = new mk_ctx();
+  c->scratch = scratch;
   c->cfg = *cfg;
   c->w = *w;
   if (!c->w.lm_head) c->w.lm_head = c->w.embed;
@@ -222,6 +238,14 @@ mk_status mk_build_plan(mk_ctx* c, const mk_plan_opts* opts) {
   const size_t ctr_bytes = size_t(std::max(1, p.n_counters)) * mk::kCtrSpread * mk::kCtrStride * 4;
   if (e == hipSuccess) e = hipMalloc(&c->d_counters, ctr_bytes);
   if (e == hipSuccess) e = hipMemset(c->d_counters, 0, ctr_bytes);
+  // the same instructions with the activations in the scratch array
+  c->sc = mk::scratch_layout(p);
+  if (e == hipSuccess && c->sc.total <= MK_NOALLOC_SCRATCH_BYTES) {
+    const std::vector<mk::Instr> st = mk::rebase_to_scratch(p, uint64_t(c->arena), uint64_t(c->scratch));
+    e = hipMalloc(&c->d_instrs_static, std::max<size_t>(1, st.size()) * sizeof(mk::Instr));
+    if (e == hipSuccess)
+      e = hipMemcpy(c->d_instrs_static, st.data(), st.size() * sizeof(mk::Instr), hipMemcpyHostToDevice);
+  }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     free_plan(c);
@@ -233,27 +257,41 @@ mk_status mk_build_plan(mk_ctx* c, const mk_plan_opts* opts) {
   return MK_OK;
 }
 
-mk_status mk_decode_step(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_t* d_next,
-                         float* d_logits, void* stream) {
-  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "mk_decode_step: ctx is NULL");
-  if (!c->planned) return fail(c, MK_ERR_NO_PLAN, "mk_decode_step: call mk_build_plan first");
-  if (!d_tokens || !d_next) return fail(c, MK_ERR_INVALID_ARG, "mk_decode_step: tokens and next are required");
-  if (pos < 0 || pos >= c->cfg.max_seq) return fail(c, MK_ERR_INVALID_ARG, "mk_decode_step: pos outside [0, max_seq)");
+}  // extern "C"
+
+namespace {
+// Shared by both decode entry points: validate, fill the launch arguments and
+// launch.  `noalloc` puts every scratch buffer in the fixed array (cleared
+// first) and runs the step as step 1 of that scratch.
+mk_status decode_launch(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_t* d_next, float* d_logits,
+                        void* stream, bool noalloc, const char* who) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, std::string(who) + ": ctx is NULL");
+  if (!c->planned) return fail(c, MK_ERR_NO_PLAN, std::string(who) + ": call mk_build_plan first");
+  if (!d_tokens || !d_next) return fail(c, MK_ERR_INVALID_ARG, std::string(who) + ": tokens and next are required");
+  if (pos < 0 || pos >= c->cfg.max_seq)
+    return fail(c, MK_ERR_INVALID_ARG, std::string(who) + ": pos outside [0, max_seq)");
+  if (noalloc && !c->d_instrs_static) {
+    char msg[200];
+    std::snprintf(msg, sizeof(msg), "%s: the plan needs %llu bytes of scratch, above the %u-byte limit", who,
+                  (unsigned long long)c->sc.total, MK_NOALLOC_SCRATCH_BYTES);
+    return fail(c, MK_ERR_UNSUPPORTED, msg);
+  }
   const mk::Plan& p = c->plan;
+  char* sc = static_cast<char*>(c->scratch);
   mk::KArgs a;
   std::memset(&a, 0, sizeof(a));
-  a.instrs = c->d_instrs;
+  a.instrs = noalloc ? c->d_instrs_static : c->d_instrs;
   a.q_off = c->d_qoff;
-  a.counters = c->d_counters;
-  a.status = reinterpret_cast<uint32_t*>(c->arena + p.arena.status);
+  a.counters = noalloc ? reinterpret_cast<uint32_t*>(sc + c->sc.ctr) : c->d_counters;
+  a.status = reinterpret_cast<uint32_t*>(noalloc ? sc + c->sc.status : c->arena + p.arena.status);
   a.tokens = d_tokens;
   a.next = d_next;
   a.logits = d_logits;
   a.rope_cos = reinterpret_cast<const float*>(c->arena + p.arena.rope_cos);
   a.rope_sin = reinterpret_cast<const float*>(c->arena + p.arena.rope_sin);
-  a.lm_slots = reinterpret_cast<float*>(c->arena + p.arena.lm_slots);
+  a.lm_slots = reinterpret_cast<float*>(noalloc ? sc + c->sc.slots : c->arena + p.arena.lm_slots);
   a.zero_page = c->arena + p.arena.zero_page;
-  a.epoch = c->epoch + 1;
+  a.epoch = noalloc ? 1 : c->epoch + 1;
   a.pos = pos;
   a.vocab = c->cfg.vocab;
   a.hidden = c->cfg.hidden;
@@ -265,22 +303,41 @@ mk_status mk_decode_step(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_
   a.rms_eps = c->cfg.rms_eps;
   a.attn_scale = float(1.0 / std::sqrt(double(c->cfg.head_dim)));
   a.watchdog_ticks = uint64_t(c->pin.opts.watchdog_ms) * 100000ull;
-  a.trace = c->d_trace;
-  a.trace_stride = c->trace_stride;
+  a.trace = noalloc ? nullptr : c->d_trace;
+  a.trace_stride = noalloc ? 0 : c->trace_stride;
   a.batch = c->cfg.batch;
   a.n_experts = c->cfg.n_experts;
   a.top_k = c->cfg.top_k;
   a.expert_ffn = c->cfg.expert_ffn;
-  a.route_stats = reinterpret_cast<uint32_t*>(c->arena + p.arena.route_stats);
+  a.route_stats = reinterpret_cast<uint32_t*>(noalloc ? sc + c->sc.route : c->arena + p.arena.route_stats);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = p.batched ? mk_launch_batched(&a, p.n_cus, s, c->cooperative, c->variant)
-                           : mk_launch_megakernel(&a, p.n_cus, s, c->cooperative, c->variant);
+  hipError_t e = hipSuccess;
+  // the scratch array keeps the last call's contents: clear the span this
+  // plan uses (tags, counters, status) so the step starts from step 1
+  if (noalloc) e = mk_launch_fill_zero(sc, c->sc.total, s);
+  if (e == hipSuccess)
+    e = p.batched ? mk_launch_batched(&a, p.n_cus, s, c->cooperative, c->variant)
+                  : mk_launch_megakernel(&a, p.n_cus, s, c->cooperative, c->variant);
   if (e != hipSuccess) return hip_fail(c, e, "launch");
-  c->epoch++;
+  if (!noalloc) c->epoch++;
+  c->last_static = noalloc;
   c->last_stream = s;
   c->has_step = true;
   return MK_OK;
+}
+}  // namespace
+
+extern "C" {
+
+mk_status mk_decode_step(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_t* d_next,
+                         float* d_logits, void* stream) {
+  return decode_launch(c, d_tokens, pos, d_next, d_logits, stream, false, "mk_decode_step");
+}
+
+mk_status mk_decode_step_noalloc(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_t* d_next,
+                                 float* d_logits, void* stream) {
+  return decode_launch(c, d_tokens, pos, d_next, d_logits, stream, true, "mk_decode_step_noalloc");
 }
 
 mk_status mk_sync(mk_ctx* c) {
@@ -289,7 +346,9 @@ mk_status mk_sync(mk_ctx* c) {
   hipError_t e = hipStreamSynchronize(c->last_stream);
   if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
   uint32_t stw[8];
-  e = hipMemcpy(stw, c->arena + c->plan.arena.status, sizeof(stw), hipMemcpyDeviceToHost);
+  const char* st_src = c->last_static ? static_cast<const char*>(c->scratch) + c->sc.status
+                                      : c->arena + c->plan.arena.status;
+  e = hipMemcpy(stw, st_src, sizeof(stw), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(c, e, "status readback");
   if (stw[mk::ST_CODE] == 0 && stw[mk::ST_NAN] == 0 && stw[mk::ST_BADTOK] == 0) return MK_OK;
   char msg[256];

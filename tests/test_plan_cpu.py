@@ -165,3 +165,14 @@ def test_moe_bad_plan_options_are_rejected():
     for opts in ({"attn_block": 256}, {"attn_heads": 3}, {"attn_block": 96}):
         with pytest.raises(B.MkError):
             B.mk_plan_check(_cfg("moe_tiny"), 64, B.plan_opts(**opts))
+
+
+@pytest.mark.parametrize("name", DENSE + ["moe_tiny", "moe_b8_ctx2048"])
+def test_noalloc_scratch_fits_the_fixed_array(name):
+    # the no-allocation entry point runs every workload's plan in the fixed
+    # per-GPU array; its size in the header matches the binding's constant
+    with open(os.path.join(ROOT, "include", "mk.h")) as fh:
+        m = re.search(r"#define MK_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", fh.read())
+    assert m and int(m.group(1)) << 20 == B.NOALLOC_SCRATCH_BYTES
+    summ, _ = B.mk_plan_check(B.config_from_shape(synth.SHAPES[name]), 256)
+    assert 0 < summ["scratch_bytes"] <= B.NOALLOC_SCRATCH_BYTES
