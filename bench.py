@@ -139,6 +139,36 @@ def cpu_baseline(shape, weights, kc, vc, tokens, budget_s: float = 20.0):
                                   shape.prefill + len(times), warm, hi["blas_threads"], len(t1))}
 
 
+def stream_read_calibration(nbytes: int, dev, stream, reps: int = 5):
+    """Achievable streaming read rate: a plain read of nbytes of device memory
+    (the step's algorithmic bytes) with the library's calibration kernel,
+    timed with HIP events on the launch stream (best block count of a few)."""
+    import numpy as np
+    import torch
+    from persistent_megakernel_wg_amd import binding as B
+    nbytes -= nbytes % 16
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            B.mk_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream.cuda_stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            B.mk_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream.cuda_stream)
+            b.record(stream)
+        torch.cuda.synchronize(dev)
+        us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        gbps = nbytes / (us * 1e-6) / 1e9
+        if best is None or gbps > best["stream_read_GBps"]:
+            best = {"stream_read_GBps": round(gbps, 1), "bytes": nbytes, "blocks": blocks,
+                    "us": round(us, 2), "kernel": "mk_stream_read (16 B non-temporal loads)"}
+    del buf
+    return best
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +250,8 @@ def main() -> int:
     achieved = alg_bytes / avg_kernel_s
     traffic = traffic_from_profiles(shape.name)
 
+    calib = stream_read_calibration(int(alg_bytes), dev, stream)
+
     metric = METRIC if not shape.is_moe else \
         "µs per decode step @batch%d (parallel-block MoE shape); achieved HBM GB/s vs peak" % shape.batch
     out = {
@@ -251,7 +283,10 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
                      "traffic": traffic, "alg_bytes_per_launch": int(alg_bytes)},
         "cpu_baseline": None,
+        "calibration": calib,
     }
+    if calib:
+        out["roofline"]["frac_of_stream_read"] = round(achieved / (calib["stream_read_GBps"] * 1e9), 4)
     if shape.is_moe:
         out["config"].update({"experts": shape.n_experts, "top_k": shape.top_k,
                               "expert_ffn": shape.expert_ffn, "parallel_block": True})

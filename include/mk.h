@@ -284,6 +284,16 @@ mk_status mk_plan_check(const mk_config *cfg, const mk_plan_opts *opts, int32_t 
  * (n_words >= n_cus * stride * 16) after mk_sync; *stride receives the slots
  * per CU.  Errors: MK_ERR_NO_PLAN, MK_ERR_INVALID_ARG, MK_ERR_HIP. */
 mk_status mk_trace_enable(mk_ctx *ctx, int on);
+
+/* Calibration (the measurement plan of the Llama-1B write-up reports its step
+ * against the memory system's rate; rocketrecap.com summary, "Performance
+ * Metrics"): read `bytes` (a multiple of 16) of device memory at d_src
+ * (16-byte aligned) once with 16-byte non-temporal loads over `blocks`
+ * workgroups of 256 threads on `stream`, and store one fold word per block to
+ * d_sink[blocks] (device memory, caller-owned).  Time it with events on the
+ * stream to get the achievable streaming read rate.  Errors:
+ * MK_ERR_INVALID_ARG, MK_ERR_HIP. */
+mk_status mk_stream_read(const void *d_src, size_t bytes, uint32_t *d_sink, int32_t blocks, void *stream);
 mk_status mk_trace_read(mk_ctx *ctx, uint32_t *host, size_t n_words, int32_t *stride);
 
 #ifdef __cplusplus

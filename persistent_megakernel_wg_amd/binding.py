@@ -61,7 +61,7 @@ class MkPlanSummary(ctypes.Structure):
 
 EXPORTS = ("mk_create", "mk_build_plan", "mk_decode_step", "mk_sync", "mk_destroy",
            "mk_last_error", "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read",
-           "mk_route_stats", "mk_decode_step_noalloc")
+           "mk_route_stats", "mk_decode_step_noalloc", "mk_stream_read")
 NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # MK_NOALLOC_SCRATCH_BYTES
 
 _lib: Optional[ctypes.CDLL] = None
@@ -92,10 +92,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_trace_read.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), ctypes.c_size_t,
                                   ctypes.POINTER(i32)]
     lib.mk_route_stats.argtypes = [vp, ctypes.POINTER(ctypes.c_int64), i32, ctypes.c_int]
+    lib.mk_stream_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
     for name in ("mk_create", "mk_build_plan", "mk_decode_step", "mk_decode_step_noalloc", "mk_sync",
                  "mk_destroy",
                  "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read",
-                 "mk_route_stats"):
+                 "mk_route_stats", "mk_stream_read"):
         getattr(lib, name).restype = st
     _lib = lib
     return lib
@@ -199,3 +200,8 @@ def mk_trace_read(ctx: int, n_cus: int, max_queue: int):
         ctx, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), buf.size,
         ctypes.byref(stride)), ctx)
     return buf[: n_cus * stride.value * TRACE_WORDS].reshape(n_cus, stride.value, TRACE_WORDS)
+
+
+def mk_stream_read(d_src: int, nbytes: int, d_sink: int, blocks: int, stream: int = 0) -> None:
+    """Enqueue one streaming read of nbytes at d_src (calibration kernel)."""
+    _check(load_library().mk_stream_read(d_src, nbytes, d_sink, blocks, stream or None))

@@ -52,14 +52,16 @@ def build(verbose: bool = False, extra_defines=()) -> str:
     r_obj = os.path.join(BUILD, "mk_runtime.o")
     b_obj = os.path.join(BUILD, "mk_batch.o")
     s_obj = os.path.join(BUILD, "mk_static.o")
+    d_obj = os.path.join(BUILD, "mk_diag.o")
     _run([hipcc, *DEVICE_FLAGS, *defs, "-c", os.path.join(CSRC, "mk_kernel.hip"), "-o", k_obj], verbose)
     _run([hipcc, *DEVICE_FLAGS, *defs, "-c", os.path.join(CSRC, "mk_batch.hip"), "-o", b_obj], verbose)
     _run([hipcc, *DEVICE_FLAGS, *defs, "-c", os.path.join(CSRC, "mk_static.hip"), "-o", s_obj], verbose)
+    _run([hipcc, *DEVICE_FLAGS, *defs, "-c", os.path.join(CSRC, "mk_diag.hip"), "-o", d_obj], verbose)
     _run([gxx, *HOST_FLAGS, "-c", os.path.join(CSRC, "mk_plan.cpp"), "-o", p_obj], verbose)
     _run([gxx, *HOST_FLAGS, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
           "-c", os.path.join(CSRC, "mk_runtime.cpp"), "-o", r_obj], verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, b_obj, s_obj, p_obj, r_obj,
+    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", k_obj, b_obj, s_obj, d_obj, p_obj, r_obj,
           "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
