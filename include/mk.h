@@ -198,6 +198,28 @@ mk_status mk_build_plan(mk_ctx *ctx, const mk_plan_opts *opts);
 mk_status mk_decode_step(mk_ctx *ctx, const int32_t *d_tokens, int32_t pos,
                          int32_t *d_next, float *d_logits, void *stream);
 
+/* Enqueue n_steps greedy decode steps in ONE launch (the resident decode of
+ * the Llama-1B write-up's future work and of Cohere's kernel: the step
+ * boundary is one more dependency inside the running kernel instead of a
+ * kernel launch, whose gap the javascript.cn article, «传统推理方式效率低下的原因»,
+ * and the rocketrecap.com summary, "Memory Pipeline Bubbles Explained", price
+ * at 1.3-2.1 us even with CUDA Graphs).
+ *   d_tokens: device int32 [B], the input tokens of the first step;
+ *   pos:      position of the first step; steps run at pos .. pos+n_steps-1,
+ *             which must lie in [0, max_seq);
+ *   d_next:   device int32 [n_steps][B], receives every step's greedy token
+ *             (step s > 0 takes step s-1's token as its input, on the device);
+ *   d_logits: device float [n_steps][B][V] or NULL.
+ * Results are those of n_steps mk_decode_step calls chained on the device.
+ * The dense decoder runs the steps inside one kernel: its loader waves stream
+ * the next step's weights while the current step finishes, the argmax's last
+ * arriver publishes the token with its step's tag, and the next step's first
+ * stage polls for it.  The mixture-of-experts decoder runs one launch per step
+ * on `stream`.  Errors: as mk_decode_step, and MK_ERR_INVALID_ARG for
+ * n_steps < 1 or pos + n_steps > max_seq. */
+mk_status mk_decode_steps(mk_ctx *ctx, const int32_t *d_tokens, int32_t pos, int32_t n_steps,
+                          int32_t *d_next, float *d_logits, void *stream);
+
 /* Bytes of the fixed per-device scratch array of mk_decode_step_noalloc. */
 #define MK_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
 

@@ -61,7 +61,7 @@ class MkPlanSummary(ctypes.Structure):
 
 EXPORTS = ("mk_create", "mk_build_plan", "mk_decode_step", "mk_sync", "mk_destroy",
            "mk_last_error", "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read",
-           "mk_route_stats", "mk_decode_step_noalloc", "mk_stream_read")
+           "mk_route_stats", "mk_decode_step_noalloc", "mk_stream_read", "mk_decode_steps")
 NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # MK_NOALLOC_SCRATCH_BYTES
 
 _lib: Optional[ctypes.CDLL] = None
@@ -81,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_build_plan.argtypes = [vp, ctypes.POINTER(MkPlanOpts)]
     lib.mk_decode_step.argtypes = [vp, vp, i32, vp, vp, vp]
     lib.mk_decode_step_noalloc.argtypes = [vp, vp, i32, vp, vp, vp]
+    lib.mk_decode_steps.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     lib.mk_sync.argtypes = [vp]
     lib.mk_destroy.argtypes = [vp]
     lib.mk_last_error.argtypes = [vp]
@@ -96,7 +97,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("mk_create", "mk_build_plan", "mk_decode_step", "mk_decode_step_noalloc", "mk_sync",
                  "mk_destroy",
                  "mk_plan_info", "mk_plan_check", "mk_trace_enable", "mk_trace_read",
-                 "mk_route_stats", "mk_stream_read"):
+                 "mk_route_stats", "mk_stream_read", "mk_decode_steps"):
         getattr(lib, name).restype = st
     _lib = lib
     return lib
@@ -149,6 +150,12 @@ def mk_decode_step_noalloc(ctx: int, d_tokens: int, pos: int, d_next: int, d_log
                            stream: int = 0) -> None:
     lib = load_library()
     _check(lib.mk_decode_step_noalloc(ctx, d_tokens, pos, d_next, d_logits or None, stream or None), ctx)
+
+
+def mk_decode_steps(ctx: int, d_tokens: int, pos: int, n_steps: int, d_next: int, d_logits: int = 0,
+                    stream: int = 0) -> None:
+    lib = load_library()
+    _check(lib.mk_decode_steps(ctx, d_tokens, pos, n_steps, d_next, d_logits or None, stream or None), ctx)
 
 
 def mk_sync(ctx: int) -> None:

@@ -82,7 +82,7 @@ DEV bool route_topk(const KArgs& a, InstrCP I, uint64_t& mask, int table, uint32
   auto off = [&](int, int j) -> uint32_t { return (b * E + 8 * s + uint32_t(j)) * kActBytes; };
 #pragma unroll
   for (int j = 0; j < 8; j++) reload(t[j], r, off(0, j));
-  if (!wait_fresh(t, live, r, off, 0, in_tag(a, I), retries)) return false;
+  if (!wait_fresh(t, live, r, off, 0, in_tag(a.epoch, I), retries)) return false;
   float v[8];
 #pragma unroll
   for (int j = 0; j < 8; j++) {
@@ -297,7 +297,7 @@ DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
       continue;
     }
     LoadView L;
-    load_view(a, I, L);
+    load_view(a, I, L, a.pos);
     const uint32_t np = I->n_pages;
     for (uint32_t p = 0; p < np; p++) {
       const uint32_t g = pg++;
@@ -430,7 +430,7 @@ DEV bool coop_stage_b(Comp& c, InstrCP I, uint32_t i, bool stage_x) {
     }
   }
   if (stage_x) {
-    if (!embed && !wait_fresh(t, live, r, off, 0, in_tag(a, I), c.retries)) return false;
+    if (!embed && !wait_fresh(t, live, r, off, 0, in_tag(a.epoch, I), c.retries)) return false;
     if (!wait_all_ge(C_XCONS, i)) return false;
     float* xs = reinterpret_cast<float*>(lds + lb::kX);
     float* ss = reinterpret_cast<float*>(lds + lb::kSS);
@@ -475,7 +475,7 @@ DEV bool stage_res_b(Comp& c, InstrCP I, uint32_t i, uint32_t n_rows, uint32_t r
     }
   }
   const uint32_t live = 2 * lane >= total ? 0 : (2 * lane + 1 < total ? 2 : 1);
-  if (!embed && !wait_fresh(t, live, rr, [&](int, int j) { return offs[j]; }, 0, in_tag(a, I), c.retries))
+  if (!embed && !wait_fresh(t, live, rr, [&](int, int j) { return offs[j]; }, 0, in_tag(a.epoch, I), c.retries))
     return false;
   float* rs = const_cast<float*>(res_slot_b(i));
   for (int j = 0; j < 2; j++)
@@ -931,7 +931,7 @@ DEV void run_merge_b(Comp& c, InstrCP I) {
 
 template <class G>
 DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
-  Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0, 0, 0};
+  Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0, 0, 0, a.epoch, a.pos, 0, 0};
   const bool tr = a.trace != nullptr;
   uint64_t staged_in = 0, staged_gain = 0;
   uint32_t staged_flags = 0, staged_k = 0;

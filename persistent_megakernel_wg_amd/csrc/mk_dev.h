@@ -170,10 +170,32 @@ DEV uint16_t f2bf(float f) {  // round to nearest even (no NaN inputs expected)
   u += 0x7FFFu + ((u >> 16) & 1u);
   return uint16_t(u >> 16);
 }
-// input token, checked against the vocabulary (an out-of-range id is reported
-// and replaced by 0 so that no access leaves the embedding table)
-DEV uint32_t token0(const KArgs& a) {
-  const int32_t t = *gp(a.tokens);
+// input token of a step, checked against the vocabulary (an out-of-range id
+// is reported and replaced by 0 so that no access leaves the embedding
+// table).  The first step of a launch reads the caller's token; a later step
+// reads the tagged copy the previous step's argmax wrote, polling until it
+// carries that step's epoch (bounded by the watchdog: a stale tag past the
+// limit aborts the workgroup and reads token 0).
+DEV bool local_timeout_tok(uint64_t& t0, uint32_t& n, uint64_t limit);
+DEV uint32_t token_of(const KArgs& a, uint32_t step, uint32_t ep) {
+  int32_t t;
+  if (step == 0) {
+    t = *gp(a.tokens);
+  } else {
+    uint64_t t0 = 0;
+    uint32_t n = 0;
+    for (;;) {
+      const uint64_t w = __hip_atomic_load(gp(a.tok_tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (uint32_t(w >> 32) == ep - 1) {
+        t = int32_t(uint32_t(w));
+        break;
+      }
+      if (local_timeout_tok(t0, n, a.watchdog_ticks)) {
+        t = 0;
+        break;
+      }
+    }
+  }
   if (t >= 0 && t < a.vocab) return uint32_t(t);
   __hip_atomic_store(gp(a.status) + ST_BADTOK, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return 0;
@@ -346,6 +368,19 @@ DEV bool local_timeout(Watch& w, uint64_t limit) {
   if (w.t0 == 0) w.t0 = now;
   return now - w.t0 > limit;
 }
+// the token poll's limit: on expiry the step is recorded as a tag timeout
+DEV bool local_timeout_tok(uint64_t& t0, uint32_t& n, uint64_t limit) {
+  if ((++n & 255) != 0) return false;
+  const uint64_t now = __builtin_amdgcn_s_memrealtime();
+  if (t0 == 0) t0 = now;
+  if (now - t0 <= limit) return false;
+  uint32_t expected = 0;
+  __hip_atomic_compare_exchange_strong(gp(status_ptr()) + ST_CODE, &expected, uint32_t(STC_TAG_TIMEOUT),
+                                       __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lds_st(C_ABORT, 1);
+  return true;
+}
+
 DEV void local_abort(uint32_t code) {
   uint32_t expected = 0;
   if (__hip_atomic_compare_exchange_strong(gp(status_ptr()) + ST_CODE, &expected, code, __ATOMIC_RELAXED,
@@ -507,7 +542,7 @@ struct LoadView {
   bool deep;               // deep DMA queue (the LM head)
 };
 
-DEV void load_view(const KArgs& a, InstrCP I, LoadView& L) {
+DEV void load_view(const KArgs& a, InstrCP I, LoadView& L, int32_t pos) {
   L.op = i_op(I);
   L.deep = (L.op == OP_GEMV || L.op == OP_BGEMV) && i_epi(I) == EPI_ARGMAX;
   L.stream_units = (I->n_rows * I->row_bytes + kUnit - 1) / kUnit;
@@ -517,7 +552,7 @@ DEV void load_view(const KArgs& a, InstrCP I, LoadView& L) {
   L.kv_base[0] = L.kv_base[1] = 0;
   if (L.op == OP_ATTN) {
     const int32_t p0 = int32_t(I->aux[1] * I->aux[2]);
-    int32_t nc = a.pos - p0;
+    int32_t nc = pos - p0;
     nc = nc < 0 ? 0 : (nc > int32_t(I->aux[2]) ? int32_t(I->aux[2]) : nc);
     L.valid_bytes = uint32_t(nc) * I->row_bytes;
     L.kv_base[0] = I->seg_ptr[0] + uint64_t(p0) * I->row_bytes;
@@ -652,6 +687,10 @@ struct Comp {
   uint32_t fcache;  // cached min published page
   uint32_t pagewait;  // ticks spent waiting for pages (leader, traced runs)
   uint32_t retries;   // re-reads of stale tagged inputs (leader, traced runs)
+  uint32_t ep;        // epoch (1-based step count) of the step being run
+  int32_t pos;        // its position
+  uint32_t step;      // its index within the launch
+  uint32_t pbase;     // the step's first page in the CU's page stream
 };
 
 
@@ -684,7 +723,7 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
   const uint32_t g = I->aux[0], blk = I->aux[1], Bat = I->aux[2], nblk = I->aux[3], kp = I->aux[4];
   const uint32_t h0 = I->row0;                  // first query head of the tile in its group
   const uint32_t head0 = g * uint32_t(a.hpg) + h0;  // ... in the layer
-  const int32_t P = a.pos;
+  const int32_t P = c.pos;
   const int32_t p0 = int32_t(blk * Bat);
   int32_t nc = P - p0;
   nc = nc < 0 ? 0 : (nc > int32_t(Bat) ? int32_t(Bat) : nc);
@@ -793,16 +832,19 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
       if (jrow == 0) update(h, d, v);
     }
     if (lane < uint32_t(LPRA) && h0 == 0) {
+      // device-scope stores: a later step of the same launch streams this
+      // row from another CU (ordered behind every CU's LM-head release)
       const size_t row = size_t(P) * DH + 8 * s;
-      uint16_t* kc = reinterpret_cast<uint16_t*>(I->seg_ptr[0]) + row;
-      uint16_t* vc = reinterpret_cast<uint16_t*>(I->seg_ptr[1]) + row;
-      u4 kk, vv;
-      kk.x = kb[0] | uint32_t(kb[1]) << 16; kk.y = kb[2] | uint32_t(kb[3]) << 16;
-      kk.z = kb[4] | uint32_t(kb[5]) << 16; kk.w = kb[6] | uint32_t(kb[7]) << 16;
-      vv.x = vb[0] | uint32_t(vb[1]) << 16; vv.y = vb[2] | uint32_t(vb[3]) << 16;
-      vv.z = vb[4] | uint32_t(vb[5]) << 16; vv.w = vb[6] | uint32_t(vb[7]) << 16;
-      *gp(reinterpret_cast<u4*>(kc)) = kk;
-      *gp(reinterpret_cast<u4*>(vc)) = vv;
+      uint64_t* kc = reinterpret_cast<uint64_t*>(reinterpret_cast<uint16_t*>(I->seg_ptr[0]) + row);
+      uint64_t* vc = reinterpret_cast<uint64_t*>(reinterpret_cast<uint16_t*>(I->seg_ptr[1]) + row);
+      const uint64_t k0 = uint64_t(kb[0] | uint32_t(kb[1]) << 16) | uint64_t(kb[2] | uint32_t(kb[3]) << 16) << 32;
+      const uint64_t k1 = uint64_t(kb[4] | uint32_t(kb[5]) << 16) | uint64_t(kb[6] | uint32_t(kb[7]) << 16) << 32;
+      const uint64_t v0 = uint64_t(vb[0] | uint32_t(vb[1]) << 16) | uint64_t(vb[2] | uint32_t(vb[3]) << 16) << 32;
+      const uint64_t v1 = uint64_t(vb[4] | uint32_t(vb[5]) << 16) | uint64_t(vb[6] | uint32_t(vb[7]) << 16) << 32;
+      __hip_atomic_store(gp(kc), k0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gp(kc + 1), k1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gp(vc), v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gp(vc + 1), v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (lane == 0) lds_st(C_RELEASED + 4 * c.w, page0 + I->n_pages);
@@ -875,7 +917,7 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
     }
     const uint32_t head = head0 + h;
     if (nblk == 1) {
-      st_tag(reinterpret_cast<uint64_t*>(I->out_ptr) + head * DH + d, num / den, a.epoch);
+      st_tag(reinterpret_cast<uint64_t*>(I->out_ptr) + head * DH + d, num / den, c.ep);
     } else {
       // partial record of (head tile, block, head): o~ [DH] | m | l
       const size_t tg = head0 / HPT;
@@ -949,7 +991,7 @@ DEV void attn_merge(Comp& c, InstrCP I) {
   }
   uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr) + (head0 + h) * DH + d0;
 #pragma unroll
-  for (int e = 0; e < PER; e++) st_tag(out + e, num[e] / den, c.a->epoch);
+  for (int e = 0; e < PER; e++) st_tag(out + e, num[e] / den, c.ep);
 }
 
 // ---- staging of the instruction's inputs into the LDS x slot (leader wave)
@@ -986,7 +1028,7 @@ DEV bool wait_fresh(T (&t)[N], uint32_t live, __amdgpu_buffer_rsrc_t r, Off off,
 }
 
 // The tag that an instruction's inputs carry once this step has written them.
-DEV uint32_t in_tag(const KArgs& a, InstrCP I) { return a.epoch + ((i_flags(I) & F_DEBUG_STALL) ? 1u : 0u); }
+DEV uint32_t in_tag(uint32_t ep, InstrCP I) { return ep + ((i_flags(I) & F_DEBUG_STALL) ? 1u : 0u); }
 
 // Leader staging of an attention tile: the tile's q, the group's k and v
 // (tagged) and cos | sin of the position into the x slot.  Every load is
@@ -995,7 +1037,7 @@ template <class Lay>
 DEV bool stage_attn(Comp& c, InstrCP I) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane;
-  const uint32_t tag = in_tag(a, I);
+  const uint32_t tag = in_tag(c.ep, I);
   float* xs = reinterpret_cast<float*>(lds + Lay::x);
   {
       // attention: q, k, v of the group (tagged) and cos | sin (tables)
@@ -1007,8 +1049,8 @@ DEV bool stage_attn(Comp& c, InstrCP I) {
       const __amdgpu_buffer_rsrc_t rk = act_rsrc(qkv + size_t(a.q_dim + g * dh) * kActBytes, dh * kActBytes);
       const __amdgpu_buffer_rsrc_t rv =
           act_rsrc(qkv + size_t(a.q_dim + a.kv_dim + g * dh) * kActBytes, dh * kActBytes);
-      const __amdgpu_buffer_rsrc_t rc = act_rsrc(a.rope_cos + size_t(a.pos) * half, half * 4);
-      const __amdgpu_buffer_rsrc_t rs = act_rsrc(a.rope_sin + size_t(a.pos) * half, half * 4);
+      const __amdgpu_buffer_rsrc_t rc = act_rsrc(a.rope_cos + size_t(c.pos) * half, half * 4);
+      const __amdgpu_buffer_rsrc_t rs = act_rsrc(a.rope_sin + size_t(c.pos) * half, half * 4);
       static_assert(kMaxK >= 512, "q staging");
       constexpr int NQ = 4;  // up to 512 q values
       u4 tq[NQ], tk[1], tv[1];

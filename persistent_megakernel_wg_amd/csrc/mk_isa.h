@@ -194,9 +194,9 @@ struct KArgs {
   const uint32_t* q_off;    // [n_cus + 1] queue offsets
   uint32_t* counters;       // [n_ctr][kCtrSpread][kCtrStride]
   uint32_t* status;         // [16] error record
-  const int32_t* tokens;    // [B]
-  int32_t* next;            // [B]
-  float* logits;            // [B, V] or null
+  const int32_t* tokens;    // [B], the input tokens of the launch's first step
+  int32_t* next;            // [n_steps][B], the greedy token of every step
+  float* logits;            // [n_steps][B, V] or null
   const float* rope_cos;    // [max_seq][Dh/2]
   const float* rope_sin;
   float* lm_slots;          // [n_lm_tiles][2] (value, index)
@@ -220,6 +220,11 @@ struct KArgs {
   int32_t top_k;            // experts per token
   int32_t expert_ffn;       // intermediate size of one expert
   uint32_t* route_stats;    // [L] distinct experts selected per layer, summed over steps
+  uint32_t n_steps;         // decode steps run back to back by this launch (>= 1;
+                            // only the one-sequence kernel runs more than one)
+  uint64_t* tok_tag;        // [B] tagged copy of the last greedy token: value |
+                            // epoch of the step that chose it (steps after the
+                            // first read their input token here)
 };
 
 // trace record words (s_memrealtime, 100 MHz, low 32 bits)

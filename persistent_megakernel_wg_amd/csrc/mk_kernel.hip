@@ -26,23 +26,27 @@
 
 namespace mk {
 
-// Prefetch cursor of a loader wave: the next page (instruction, page of it)
-// whose lines it has not yet touched.
+// Pages of a CU's queue are numbered over the launch: step s's instruction i
+// takes pages s * P + page0(i) ..., where P is the pages of one step.
+DEV uint32_t step_pages(InstrCP q, uint32_t n) { return n ? q[n - 1].page0 + q[n - 1].n_pages : 0; }
+
+// Prefetch cursor of a loader wave: the next page (instruction of the launch,
+// step * n + i, and page of it) whose lines it has not yet touched.
 struct PfCursor {
-  uint32_t i, p;
+  uint32_t ig, p;
 };
 
 // Touch this wave's half of the next page after the DMA cursor (instruction
-// i, page p, ring index g) not yet touched, if it lies less than kPfPages
-// past g.  Only GEMV weight streams are touched; attention pages (the KV
-// cache) are skipped.  Returns false when no page is due.
-DEV bool prefetch_next(InstrCP q, uint32_t n, uint32_t i, uint32_t p, uint32_t g, int v, PfCursor& c,
-                       uint32_t sink, uint32_t voff128) {
-  if (c.i < i || (c.i == i && c.p < p)) c = {i, p};
-  while (c.i < n && c.p >= q[c.i].n_pages) c = {c.i + 1, 0};
-  if (c.i >= n) return false;
-  InstrCP I = q + c.i;
-  if (I->page0 + c.p >= g + kPfPages) return false;
+// ig of the launch, page p, ring index g) not yet touched, if it lies less
+// than kPfPages past g.  Only GEMV weight streams are touched; attention pages
+// (the KV cache) are skipped.  Returns false when no page is due.
+DEV bool prefetch_next(InstrCP q, uint32_t n, uint32_t n_total, uint32_t P, uint32_t ig, uint32_t p, uint32_t g,
+                       int v, PfCursor& c, uint32_t sink, uint32_t voff128) {
+  if (c.ig < ig || (c.ig == ig && c.p < p)) c = {ig, p};
+  while (c.ig < n_total && c.p >= q[c.ig % n].n_pages) c = {c.ig + 1, 0};
+  if (c.ig >= n_total) return false;
+  InstrCP I = q + c.ig % n;
+  if ((c.ig / n) * P + I->page0 + c.p >= g + kPfPages) return false;
   if (i_op(I) == OP_GEMV) {
     const uint32_t u0 = c.p * kUnitsPerPage + uint32_t(v) * kDmaPerPage;
     const uint32_t units = (I->n_rows * I->row_bytes + kUnit - 1) / kUnit;
@@ -53,19 +57,24 @@ DEV bool prefetch_next(InstrCP q, uint32_t n, uint32_t i, uint32_t p, uint32_t g
   return true;
 }
 
+// The loader waves walk the launch's steps back to back: the weights of the
+// next step are streamed (and touched ahead) while the current step's last
+// instructions still run, since they do not depend on its results.
 DEV void loader(const KArgs& a, InstrCP q, uint32_t n, int v) {
   const uint32_t voff = (threadIdx.x & 63) * 16, voff4k = voff + 4096;
   const uint32_t voff128 = (threadIdx.x & 63) * 128, sink = uint32_t(size_t(lds)) + kLdsPf;
+  const uint32_t P = step_pages(q, n), n_total = n * a.n_steps;
   uint32_t nd = 0;       // DMAs issued by this wave (kDmaPerPage per page)
   uint32_t g_issue = 0;  // pages issued
   uint32_t g_pub = 0;    // pages published
   uint32_t min_rel = 0;  // oldest page a compute wave may still read
   PfCursor pf{0, 0};
-  for (uint32_t i = 0; i < n; i++) {
-    InstrCP I = q + i;
+  for (uint32_t ig = 0; ig < n_total; ig++) {
+    const uint32_t step = ig / n;
+    InstrCP I = q + (ig - step * n);
     LoadView L;
-    load_view(a, I, L);
-    const uint32_t np = I->n_pages, page0 = I->page0;
+    load_view(a, I, L, a.pos + int32_t(step));
+    const uint32_t np = I->n_pages, page0 = step * P + I->page0;
     for (uint32_t p = 0; p < np; p++) {
       const uint32_t g = page0 + p;
       if (g >= min_rel + kPages) {
@@ -80,7 +89,7 @@ DEV void loader(const KArgs& a, InstrCP q, uint32_t n, int v) {
           }
           // (every DMA is published here, so the loads below are the
           // newest and no page's completion waits on them)
-          if (kPfPages && prefetch_next(q, n, i, p, g, v, pf, sink, voff128)) continue;
+          if (kPfPages && prefetch_next(q, n, n_total, P, ig, p, g, v, pf, sink, voff128)) continue;
           if (aborted() || local_timeout(t0, local_limit())) {
             if (!aborted()) local_abort(STC_LOCAL_TIMEOUT);
             wait_vm0();
@@ -120,11 +129,11 @@ DEV void epi_row(Comp& c, const EpiCtx& E, uint32_t i, uint32_t t_row, float v, 
   switch (E.epi) {
     case EPI_STORE:
     case EPI_SWIGLU:
-      st_tag(out + row, v, a.epoch);
+      st_tag(out + row, v, c.ep);
       break;
     case EPI_RESID:
     case EPI_ACC_ONLY:
-      st_tag(out + row, res_slot(i)[t_row] + v, a.epoch);
+      st_tag(out + row, res_slot(i)[t_row] + v, c.ep);
       break;
     case EPI_ACC_FIRST:
       reinterpret_cast<float*>(lds + kLdsAcc)[E.acc0 + t_row] = res_slot(i)[t_row] + v;
@@ -133,10 +142,10 @@ DEV void epi_row(Comp& c, const EpiCtx& E, uint32_t i, uint32_t t_row, float v, 
       reinterpret_cast<float*>(lds + kLdsAcc)[E.acc0 + t_row] += v;
       break;
     case EPI_ACC_LAST:
-      st_tag(out + row, reinterpret_cast<float*>(lds + kLdsAcc)[E.acc0 + t_row] + v, a.epoch);
+      st_tag(out + row, reinterpret_cast<float*>(lds + kLdsAcc)[E.acc0 + t_row] + v, c.ep);
       break;
     case EPI_ARGMAX:
-      if (a.logits) gp(a.logits)[row] = v;
+      if (a.logits) gp(a.logits)[size_t(c.step) * uint32_t(a.vocab) + row] = v;
       if (v != v) __hip_atomic_store(gp(a.status) + ST_NAN, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       arg_update(best, v, row);
       break;
@@ -171,7 +180,7 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
   const bool trl = c.a->trace && c.w == 0 && lane == 0;
   if (trl) trace_put(a, c.cu, i, TR_XREADY, now32());
 
-  const uint32_t n_items = I->n_items, page0 = I->page0;
+  const uint32_t n_items = I->n_items, page0 = c.pbase + I->page0;
   const bool pair = i_epi(I) == EPI_SWIGLU;
   const EpiCtx E = epi_of(I);
   ArgBest best{-__builtin_inff(), 0xFFFFFFFFu};
@@ -288,14 +297,13 @@ DEV uint32_t out_rows(InstrCP I) {
 DEV bool stage_leader(Comp& c, InstrCP I, uint32_t i) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane;
-  const uint32_t tag = a.epoch;
   float* xs = reinterpret_cast<float*>(lds + kLdsX);
   if (i_op(I) == OP_GEMV) {
     // bf16 embedding row of the token (8 values per lane per 512) and the gain
     constexpr int NE = kMaxK / 512;
     const uint32_t K = I->k;
     const bool norm = i_flags(I) & F_NORM;
-    const uint16_t* e = reinterpret_cast<const uint16_t*>(I->in_ptr) + size_t(token0(a)) * K;
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(I->in_ptr) + size_t(token_of(a, c.step, c.ep)) * K;
     const __amdgpu_buffer_rsrc_t r = act_rsrc(e, K * 2);
     const __amdgpu_buffer_rsrc_t rg = act_rsrc(reinterpret_cast<const void*>(I->gain_ptr), norm ? K * 2 : 0);
     u4 raw[NE], gw[NE];
@@ -389,7 +397,8 @@ DEV void stage_issue(Comp& c, InstrCP I, bool stage_x, StageIn& S) {
   if (g.res_embed) {
     const KArgs& a = *c.a;
     const uint32_t n_res = out_rows(I);
-    const uint16_t* e = reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(token0(a)) * a.hidden + I->row0;
+    const uint16_t* e =
+        reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(token_of(a, c.step, c.ep)) * a.hidden + I->row0;
     const __amdgpu_buffer_rsrc_t re = act_rsrc_u(e, n_res * 2);
     S.res_e[0] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane, 0, 0);
     S.res_e[1] = __builtin_amdgcn_raw_buffer_load_b16(re, 4 * lane + 2, 0, 0);
@@ -398,9 +407,8 @@ DEV void stage_issue(Comp& c, InstrCP I, bool stage_x, StageIn& S) {
 
 // false = abort or watchdog
 DEV bool stage_finish(Comp& c, InstrCP I, uint32_t i, bool stage_x, StageIn& S) {
-  const KArgs& a = *c.a;
   const uint32_t lane = c.lane;
-  const uint32_t tag = in_tag(a, I);
+  const uint32_t tag = in_tag(c.ep, I);
   const StageGeo g = stage_geo(c, I, stage_x);
   const uint32_t n_res = g.has_res ? out_rows(I) : 0;
   const uint32_t res_live = 2 * lane >= n_res ? 0 : (2 * lane + 1 < n_res ? 2 : 1);
@@ -484,21 +492,21 @@ DEV bool run_gemv(Comp& c, InstrCP I, uint32_t i) {
 template <class G>
 DEV bool run_attn(Comp& c, InstrCP I, uint32_t i) {
   if constexpr (!G::any) {
-    return attn<G::hpt, G::dh, LayA>(c, I, i, I->page0);
+    return attn<G::hpt, G::dh, LayA>(c, I, i, c.pbase + I->page0);
   } else {
     const uint32_t hpt = I->n_items;
     if (c.a->head_dim == 64) {
       switch (hpt) {
-        case 1: return attn<1, 64, LayA>(c, I, i, I->page0);
-        case 2: return attn<2, 64, LayA>(c, I, i, I->page0);
-        case 4: return attn<4, 64, LayA>(c, I, i, I->page0);
-        default: return attn<8, 64, LayA>(c, I, i, I->page0);
+        case 1: return attn<1, 64, LayA>(c, I, i, c.pbase + I->page0);
+        case 2: return attn<2, 64, LayA>(c, I, i, c.pbase + I->page0);
+        case 4: return attn<4, 64, LayA>(c, I, i, c.pbase + I->page0);
+        default: return attn<8, 64, LayA>(c, I, i, c.pbase + I->page0);
       }
     }
     switch (hpt) {
-      case 1: return attn<1, 128, LayA>(c, I, i, I->page0);
-      case 2: return attn<2, 128, LayA>(c, I, i, I->page0);
-      default: return attn<4, 128, LayA>(c, I, i, I->page0);
+      case 1: return attn<1, 128, LayA>(c, I, i, c.pbase + I->page0);
+      case 2: return attn<2, 128, LayA>(c, I, i, c.pbase + I->page0);
+      default: return attn<4, 128, LayA>(c, I, i, c.pbase + I->page0);
     }
   }
 }
@@ -540,7 +548,7 @@ DEV void lm_finish(Comp& c, InstrCP I) {
   uint32_t old = 0;
   if (lane == 0) old = ctr_release(ctr_line(a, I->sig_ctr, 0));
   old = uni(old);
-  if (old + 1 != a.epoch * n_tiles) return;
+  if (old + 1 != c.ep * n_tiles) return;
   ArgBest all{-__builtin_inff(), 0xFFFFFFFFu};
   for (uint32_t t = lane; t < n_tiles; t += 64)
     arg_update(all, ld_act(a.lm_slots + 2 * t), __float_as_uint(ld_act(a.lm_slots + 2 * t + 1)));
@@ -550,13 +558,18 @@ DEV void lm_finish(Comp& c, InstrCP I) {
     const uint32_t oi = __shfl_xor(all.i, m, 64);
     arg_update(all, ov, oi);
   }
-  if (lane == 0) *gp(a.next) = int32_t(all.i);
+  if (lane == 0) {
+    gp(a.next)[c.step] = int32_t(all.i);
+    // the next step of the launch takes its input token from here
+    if (c.step + 1 < a.n_steps) st_tag(a.tok_tag, __uint_as_float(all.i), c.ep);
+  }
 }
 
 template <class G>
 DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
-  Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0, 0, 0};
+  Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0, 0, 0, a.epoch, a.pos, 0, 0};
   const bool tr = a.trace != nullptr;
+  const uint32_t P = step_pages(q, n), n_total = n * a.n_steps;
   // input currently in the x slot (every wave tracks it, so all take the
   // same staging decision)
   uint64_t staged_in = 0;
@@ -574,16 +587,30 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
   // loads of the next instruction's input, issued while this one's items run
   StageIn pre;
   uint32_t pre_i = 0xFFFFFFFFu;
-  for (uint32_t i = 0; i < n; i++) {
+  // The launch runs a.n_steps steps back to back.  Instruction i of step s is
+  // instruction ig = s * n + i of the launch: the LDS words that order the
+  // waves count instructions and pages of the launch, and each step carries
+  // its own epoch (the activation tag and counter target), position and
+  // page base.  The trace keeps the first step of a launch.
+  for (uint32_t ig = 0; ig < n_total; ig++) {
+    const uint32_t step = ig / n, i = ig - step * n;
+    const uint32_t ti = step == 0 ? i : 0xFFFFFFFFu;  // trace slot
+    if (i == 0) {
+      c.ep = a.epoch + step;
+      c.pos = a.pos + int32_t(step);
+      c.step = step;
+      c.pbase = step * P;
+      staged_in = 0;
+    }
     InstrCP I = q + i;
     const bool is_gemv = i_op(I) == OP_GEMV;
     const bool reuse = reuses(I);
     const bool coop = is_coop(I);
     if (w == 0) {
       if (tr && c.lane == 0) {
-        trace_put(a, cu, i, TR_START, now32());
-        trace_put(a, cu, i, TR_HW0, hw0(I));
-        trace_put(a, cu, i, TR_HW1, hw1(I));
+        trace_put(a, cu, ti, TR_START, now32());
+        trace_put(a, cu, ti, TR_HW0, hw0(I));
+        trace_put(a, cu, ti, TR_HW1, hw1(I));
       }
       c.pagewait = 0;
       c.retries = 0;
@@ -594,40 +621,40 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       // elements it reads and re-reads only the stale ones, so it starts
       // while the producers' last rows are still in flight instead of a
       // counter round trip after the last of them.
-      if (tr && c.lane == 0) trace_put(a, cu, i, TR_DEPS, now32());
+      if (tr && c.lane == 0) trace_put(a, cu, ti, TR_DEPS, now32());
     }
     if (coop) {
       // every wave stages its share; a barrier publishes the x slot
       if (!reuse || needs_res(I)) {
-        if (pre_i != i) stage_issue(c, I, !reuse, pre);
-        if (!stage_finish(c, I, i, !reuse, pre)) {
+        if (pre_i != ig) stage_issue(c, I, !reuse, pre);
+        if (!stage_finish(c, I, ig, !reuse, pre)) {
           if (c.lane == 0) lds_st(C_ABORT, 1);
           return;
         }
         if (!comp_barrier()) return;
       }
       if (tr && w == 0 && c.lane == 0) {
-        trace_put(a, cu, i, TR_XFREE, now32());
-        trace_put(a, cu, i, TR_STAGED, now32());
-        trace_put(a, cu, i, TR_RETRY, c.retries);
+        trace_put(a, cu, ti, TR_XFREE, now32());
+        trace_put(a, cu, ti, TR_STAGED, now32());
+        trace_put(a, cu, ti, TR_RETRY, c.retries);
       }
     } else if (w == 0) {
       // every compute wave has read the previous instruction's staged inputs
-      if (!wait_all_ge(C_XCONS, i)) {
+      if (!wait_all_ge(C_XCONS, ig)) {
         if (c.lane == 0) lds_st(C_ABORT, 1);
         return;
       }
-      if (tr && c.lane == 0) trace_put(a, cu, i, TR_XFREE, now32());
-      if (!stage_leader(c, I, i)) {
+      if (tr && c.lane == 0) trace_put(a, cu, ti, TR_XFREE, now32());
+      if (!stage_leader(c, I, ig)) {
         if (c.lane == 0) lds_st(C_ABORT, 1);
         return;
       }
-      if (c.lane == 0) lds_st(C_XOK, i + 1);
+      if (c.lane == 0) lds_st(C_XOK, ig + 1);
       if (tr && c.lane == 0) {
-        trace_put(a, cu, i, TR_STAGED, now32());
-        trace_put(a, cu, i, TR_RETRY, c.retries);
+        trace_put(a, cu, ti, TR_STAGED, now32());
+        trace_put(a, cu, ti, TR_RETRY, c.retries);
       }
-    } else if (!wait_lds_ge(C_XOK, i + 1)) {
+    } else if (!wait_lds_ge(C_XOK, ig + 1)) {
       return;
     }
     if (is_gemv) {
@@ -647,17 +674,17 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
         const bool nreuse = reuses(I + 1);
         if (!nreuse || needs_res(I + 1)) {
           stage_issue(c, I + 1, !nreuse, pre);
-          pre_i = i + 1;
+          pre_i = ig + 1;
         }
       }
     } else {
       staged_in = 0;
     }
-    bool ok = i_op(I) == OP_GEMV ? run_gemv<G>(c, I, i) : run_attn<G>(c, I, i);
+    bool ok = i_op(I) == OP_GEMV ? run_gemv<G>(c, I, ig) : run_attn<G>(c, I, ig);
     if (!ok) return;
     if (tr && w == 0 && c.lane == 0) {
-      trace_put(a, cu, i, TR_ITEMS, now32());
-      trace_put(a, cu, i, TR_PAGEWAIT, c.pagewait);
+      trace_put(a, cu, ti, TR_ITEMS, now32());
+      trace_put(a, cu, ti, TR_PAGEWAIT, c.pagewait);
     }
     // completion: the last wave signals.  Tagged outputs need no wait; the
     // untagged data behind a ticket (argmax slots, attention partials) must
@@ -665,12 +692,12 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
     const bool release = (i_op(I) == OP_GEMV && i_epi(I) == EPI_ARGMAX) ||
                          (i_op(I) == OP_ATTN && I->aux[3] > 1);
     if (release) wait_vm0();
-    if (tr && w == 0 && c.lane == 0) trace_put(a, cu, i, TR_VISIBLE, now32());
+    if (tr && w == 0 && c.lane == 0) trace_put(a, cu, ti, TR_VISIBLE, now32());
     uint32_t prev = 0;
-    if (c.lane == 0) prev = lds_add(C_DONE + 4 * (i % kDoneRing), 1);
+    if (c.lane == 0) prev = lds_add(C_DONE + 4 * (ig % kDoneRing), 1);
     prev = uni(prev);
     if (prev != kNComp - 1) continue;
-    if (c.lane == 0) lds_st(C_DONE + 4 * (i % kDoneRing), 0);
+    if (c.lane == 0) lds_st(C_DONE + 4 * (ig % kDoneRing), 0);
     if (i_op(I) == OP_GEMV && i_epi(I) == EPI_ARGMAX) {
       lm_finish(c, I);
       continue;
@@ -679,11 +706,11 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       uint32_t old = 0;
       if (c.lane == 0) old = ctr_release(ctr_line(a, I->seg_rows[0], 0));
       old = uni(old);
-      if (old + 1 != a.epoch * I->aux[3]) continue;
+      if (old + 1 != c.ep * I->aux[3]) continue;
       run_merge<G>(c, I);
     }
     if ((i_flags(I) & F_SIGNAL) && c.lane == 0) ctr_signal(ctr_line(a, I->sig_ctr, uint32_t(cu) % kCtrSpread));
-    if (tr && c.lane == 0) trace_put(a, cu, i, TR_SIGNAL, now32());
+    if (tr && c.lane == 0) trace_put(a, cu, ti, TR_SIGNAL, now32());
   }
 }
 

@@ -271,6 +271,7 @@ ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
     a.rl[l] = is_batched(c) ? take(E * B * c.n_experts) : 0;
     a.part[l] = take(4 * uint64_t(max_parts) * hpg * (c.head_dim + 2));
   }
+  a.tok = take(E * B);
   a.rope_cos = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
   a.rope_sin = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
   a.zero_page = take(kPageBytes);

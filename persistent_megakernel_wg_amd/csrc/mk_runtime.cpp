@@ -264,12 +264,14 @@ namespace {
 // launch.  `noalloc` puts every scratch buffer in the fixed array (cleared
 // first) and runs the step as step 1 of that scratch.
 mk_status decode_launch(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_t* d_next, float* d_logits,
-                        void* stream, bool noalloc, const char* who) {
+                        void* stream, bool noalloc, const char* who, int32_t n_steps = 1) {
   if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, std::string(who) + ": ctx is NULL");
   if (!c->planned) return fail(c, MK_ERR_NO_PLAN, std::string(who) + ": call mk_build_plan first");
   if (!d_tokens || !d_next) return fail(c, MK_ERR_INVALID_ARG, std::string(who) + ": tokens and next are required");
   if (pos < 0 || pos >= c->cfg.max_seq)
     return fail(c, MK_ERR_INVALID_ARG, std::string(who) + ": pos outside [0, max_seq)");
+  if (n_steps < 1 || int64_t(pos) + n_steps > c->cfg.max_seq)
+    return fail(c, MK_ERR_INVALID_ARG, std::string(who) + ": n_steps < 1 or pos + n_steps > max_seq");
   if (noalloc && !c->d_instrs_static) {
     char msg[200];
     std::snprintf(msg, sizeof(msg), "%s: the plan needs %llu bytes of scratch, above the %u-byte limit", who,
@@ -310,6 +312,8 @@ mk_status decode_launch(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_t
   a.top_k = c->cfg.top_k;
   a.expert_ffn = c->cfg.expert_ffn;
   a.route_stats = reinterpret_cast<uint32_t*>(noalloc ? sc + c->sc.route : c->arena + p.arena.route_stats);
+  a.tok_tag = reinterpret_cast<uint64_t*>((noalloc ? sc + c->sc.act : c->arena) + p.arena.tok);
+  a.n_steps = uint32_t(n_steps);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
@@ -320,7 +324,7 @@ mk_status decode_launch(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_t
     e = p.batched ? mk_launch_batched(&a, p.n_cus, s, c->cooperative, c->variant)
                   : mk_launch_megakernel(&a, p.n_cus, s, c->cooperative, c->variant);
   if (e != hipSuccess) return hip_fail(c, e, "launch");
-  if (!noalloc) c->epoch++;
+  if (!noalloc) c->epoch += uint32_t(n_steps);
   c->last_static = noalloc;
   c->last_stream = s;
   c->has_step = true;
@@ -338,6 +342,24 @@ mk_status mk_decode_step(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_
 mk_status mk_decode_step_noalloc(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_t* d_next,
                                  float* d_logits, void* stream) {
   return decode_launch(c, d_tokens, pos, d_next, d_logits, stream, true, "mk_decode_step_noalloc");
+}
+
+mk_status mk_decode_steps(mk_ctx* c, const int32_t* d_tokens, int32_t pos, int32_t n_steps, int32_t* d_next,
+                          float* d_logits, void* stream) {
+  if (c && c->planned && c->plan.batched) {
+    // the batched kernel runs one step per launch: chain the launches on
+    // the stream, each step's input being the previous step's output
+    if (n_steps < 1) return fail(c, MK_ERR_INVALID_ARG, "mk_decode_steps: n_steps < 1");
+    const int32_t B = c->cfg.batch;
+    for (int32_t s = 0; s < n_steps; s++) {
+      const mk_status st = decode_launch(c, s ? d_next + size_t(s - 1) * B : d_tokens, pos + s, d_next + size_t(s) * B,
+                                         d_logits ? d_logits + size_t(s) * B * c->cfg.vocab : nullptr, stream,
+                                         false, "mk_decode_steps");
+      if (st != MK_OK) return st;
+    }
+    return MK_OK;
+  }
+  return decode_launch(c, d_tokens, pos, d_next, d_logits, stream, false, "mk_decode_steps", n_steps);
 }
 
 mk_status mk_sync(mk_ctx* c) {

@@ -91,6 +91,21 @@ class Engine:
         toks = [b.cpu().numpy().copy() for b in bufs[1:]]
         return out_logits, toks
 
+    def generate_resident(self, tokens: np.ndarray, pos0: int, steps: int, logits: bool = False,
+                          stream=None):
+        """Greedy decode of `steps` steps in one launch (mk_decode_steps);
+        returns (logits [steps, B, V] or None, tokens [steps, B])."""
+        torch = self.torch
+        self.tokens.copy_(torch.from_numpy(np.asarray(tokens, dtype=np.int32)))
+        out = torch.zeros(steps, self.shape.batch, dtype=torch.int32, device=self.dev)
+        lg = (torch.zeros(steps, self.shape.batch, self.shape.vocab, dtype=torch.float32, device=self.dev)
+              if logits else None)
+        s = (stream or torch.cuda.current_stream(self.dev)).cuda_stream
+        B.mk_decode_steps(self.ctx, self.tokens.data_ptr(), pos0, steps, out.data_ptr(),
+                          lg.data_ptr() if logits else 0, s)
+        B.mk_sync(self.ctx)
+        return (lg.cpu().numpy() if logits else None), out.cpu().numpy()
+
     def read_kv(self):
         k = self.k_cache.view(self.torch.int16).cpu().numpy().view(np.uint16)
         v = self.v_cache.view(self.torch.int16).cpu().numpy().view(np.uint16)
