@@ -42,8 +42,8 @@ def kernel_source_hash() -> str:
 
 
 def traffic_from_profiles(workload: str):
-    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
-    on the current kernel source; else None."""
+    """HBM bytes per decode step measured with rocprofv3 counters, if they were
+    taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
@@ -51,7 +51,7 @@ def traffic_from_profiles(workload: str):
         rec = json.load(fh)
     if rec.get("kernel_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_launch") / rec.get("steps_per_launch", 1)
 
 
 def host_info():
@@ -180,6 +180,9 @@ def main() -> int:
     ap.add_argument("--n-cus", type=int, default=0)
     ap.add_argument("--attn-block", type=int, default=0)
     ap.add_argument("--mlp-chunks", type=int, default=0)
+    ap.add_argument("--launch", choices=("resident", "single"), default="resident",
+                    help="resident: the K timed steps run in one launch (mk_decode_steps); "
+                         "single: one launch per step, chained on the device")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode megakernel runs on a single device "
@@ -214,25 +217,46 @@ def main() -> int:
     def pos_of(i):
         return shape.prefill + (i % span)
 
+    resident = args.launch == "resident"
+    if resident and (K > span or W > span):
+        print("bench.py: --steps and --warmup must fit the cache (%d positions after the "
+              "pre-filled ones) with --launch resident" % span, file=sys.stderr)
+        return 2
     # warm-up from the initial state, then restart at the pre-filled position
-    for i in range(W):
-        eng.launch(pos_of(i), tokens=bufs[i], next_out=bufs[i + 1], stream=stream)
+    if resident:
+        warm_out = torch.zeros(max(W, 1), shape.batch, dtype=torch.int32, device=dev)
+        if W:
+            B.mk_decode_steps(eng.ctx, bufs[0].data_ptr(), shape.prefill, W, warm_out.data_ptr(), 0,
+                              stream.cuda_stream)
+    else:
+        for i in range(W):
+            eng.launch(pos_of(i), tokens=bufs[i], next_out=bufs[i + 1], stream=stream)
     eng.sync()
     bufs[W].copy_(bufs[0])
+    n_launch = 1 if resident else K
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+          for _ in range(n_launch)]
     if shape.is_moe:
         B.mk_route_stats(eng.ctx, shape.n_layers, reset=True)
+    out_k = torch.zeros(K, shape.batch, dtype=torch.int32, device=dev)
     torch.cuda.synchronize(dev)
     t_start = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        eng.launch(pos_of(i), tokens=bufs[W + i], next_out=bufs[W + i + 1], stream=stream)
-        ev[i][1].record(stream)
+    if resident:
+        # K greedy steps in one launch; the events bracket the launch
+        ev[0][0].record(stream)
+        B.mk_decode_steps(eng.ctx, bufs[W].data_ptr(), shape.prefill, K, out_k.data_ptr(), 0,
+                          stream.cuda_stream)
+        ev[0][1].record(stream)
+    else:
+        for i in range(K):
+            ev[i][0].record(stream)
+            eng.launch(pos_of(i), tokens=bufs[W + i], next_out=bufs[W + i + 1], stream=stream)
+            ev[i][1].record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t_start
     eng.sync()
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    # per-step kernel time: launch durations divided by the steps they ran
+    kern_ms = [a.elapsed_time(b) / (K if resident else 1) for a, b in ev]
     avg_kernel_s = float(np.mean(kern_ms)) / 1e3
     ms_per_step = 1e3 * wall / K
 
@@ -249,6 +273,8 @@ def main() -> int:
     alg_bytes = wbytes + float(np.mean(kvb))
     achieved = alg_bytes / avg_kernel_s
     traffic = traffic_from_profiles(shape.name)
+    if traffic is not None:
+        traffic = int(traffic * (K if resident else 1))  # per launch, like achieved
 
     calib = stream_read_calibration(int(alg_bytes), dev, stream)
 
@@ -275,13 +301,15 @@ def main() -> int:
                    "kv_cache": "bf16", "n_cus": info["n_cus"], "attn_block": info["attn_block"],
                    "mlp_chunks": info["mlp_chunks"]},
         "tokens_per_step": shape.batch,
+        "launch": ("one launch of %d steps (mk_decode_steps)" % K) if resident else "one launch per step",
         "kernel_us_per_step": round(avg_kernel_s * 1e6, 2),
         "kernel_us_median": round(float(np.median(kern_ms)) * 1e3, 2),
         "kernel_us_p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 2),
         "tok_per_s": round(shape.batch / (ms_per_step / 1e3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
-                     "traffic": traffic, "alg_bytes_per_launch": int(alg_bytes)},
+                     "traffic": traffic, "alg_bytes_per_step": int(alg_bytes),
+                     "alg_bytes_per_launch": int(alg_bytes * (K if resident else 1))},
         "cpu_baseline": None,
         "calibration": calib,
     }
