@@ -33,7 +33,7 @@ import numpy as np
 
 TR = dict(START=0, DEPS=1, STAGED=2, ITEMS=3, SIGNAL=4, PAGEWAIT=5, HW0=6, HW1=7,
           XREADY=8, ITEM0=9, VISIBLE=10, XFREE=11, RETRY=15)
-OP_GEMV, OP_ATTN, OP_BGEMV, OP_EGU, OP_EDN = 1, 2, 3, 4, 5
+OP_GEMV, OP_ATTN, OP_BGEMV, OP_EGU, OP_EDN, OP_ERD = 1, 2, 3, 4, 5, 6
 EPI_NAMES = {0: "qkv", 1: "o", 2: "gate_up", 3: "down", 4: "down", 5: "down", 6: "down",
              7: "lm_head"}
 TICK_US = 0.01  # s_memrealtime runs at 100 MHz
@@ -47,6 +47,8 @@ def stage_of(hw0: int, batched: bool) -> str:
         return "expert_gate_up"
     if op == OP_EDN:
         return "expert_down"
+    if op == OP_ERD:
+        return "expert_sum"
     if op == OP_BGEMV and epi == 0:
         return "qkv_router"
     return EPI_NAMES.get(epi, "op%d" % op)
@@ -83,7 +85,10 @@ def analyse(tr: np.ndarray, batched: bool = False) -> dict:
             end = w[TR["SIGNAL"]] if w[TR["SIGNAL"]] else w[TR["ITEMS"]]
             r = rec[(layer, st, k)]
             r["start"].append(rel(np.array(w[TR["START"]])))
-            r["staged"].append(rel(np.array(w[TR["STAGED"]])))
+            # instructions without a staging stamp (attention tiles, CUs
+            # with no expert units) count as staged once their waits passed
+            staged = w[TR["STAGED"]] or w[TR["DEPS"]] or w[TR["START"]]
+            r["staged"].append(rel(np.array(staged)))
             r["end"].append(rel(np.array(end)))
             r["pagewait"].append(int(w[TR["PAGEWAIT"]]) * TICK_US)
             # phases inside the instruction, per CU (leader's stamps)

@@ -51,6 +51,19 @@ DEV int rt_base(uint32_t layer) { return lb::kRoute + int(layer & 1) * lb::kRout
 DEV uint32_t rt_u8(int base, int off) { return *reinterpret_cast<const uint8_t*>(lds + base + off); }
 DEV void rt_st8(int base, int off, uint32_t v) { *reinterpret_cast<uint8_t*>(lds + base + off) = uint8_t(v); }
 
+// The layer's down projections are cut into units of Rb consecutive rows of
+// one selected expert; the U = (selected experts) x (units per expert) units,
+// in expert order, go to the CUs in even contiguous ranges.  Loader and
+// compute waves take the same range from the same routing decision.
+DEV void edn_range(uint32_t nsel, uint32_t nb, uint32_t n_cus, uint32_t cu, uint32_t& lo, uint32_t& hi) {
+  const uint64_t U = uint64_t(nsel) * nb;
+  lo = uint32_t(U * cu / n_cus);
+  hi = uint32_t(U * (cu + 1) / n_cus);
+}
+// Tag of the expert outputs y: the step and the layer (one buffer serves
+// every layer; a reader must not take the previous layer's values).
+DEV uint32_t y_tag(uint32_t ep, uint32_t layer) { return (ep << 7) | (layer & 127u); }
+
 // Reductions over aligned groups of 8 lanes (every lane of the group gets
 // the result): xor 1, xor 2, then the half-row mirror pairs the two quads.
 template <class T, class Op>
@@ -75,7 +88,7 @@ DEV T group8(T v, Op op) {
 // pair index.  false = abort or watchdog while waiting for fresh logits.
 DEV bool route_topk(const KArgs& a, InstrCP I, uint64_t& mask, int table, uint32_t& retries) {
   const uint32_t lane = threadIdx.x & 63, b = lane >> 3, s = lane & 7;
-  const uint32_t E = I->aux[4], k = uint32_t(a.top_k), nB = uint32_t(a.batch);
+  const uint32_t E = uint32_t(a.n_experts), k = uint32_t(a.top_k), nB = uint32_t(a.batch);
   const __amdgpu_buffer_rsrc_t r = act_rsrc(reinterpret_cast<const void*>(I->seg_ptr[0]), nB * E * kActBytes);
   const uint32_t live = (b < nB && 8 * s < E) ? min(8u, E - 8 * s) : 0u;
   uint2 t[8];
@@ -263,7 +276,7 @@ DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
   for (uint32_t i = 0; i < n; i++) {
     InstrCP I = q + i;
     const uint32_t op = i_op(I);
-    if (i_flags(I) & F_DIRECT) continue;
+    if ((i_flags(I) & F_DIRECT) || op == OP_ERD) continue;
     if (op == OP_EGU || op == OP_EDN) {
       const uint32_t layer = I->layer;
       if (layer != route_layer) {
@@ -280,6 +293,29 @@ DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
       }
       const uint32_t ppe = I->aux[2], npu = I->aux[3], run = I->seg_rows[0], nit = i_nit(I), rb = I->row_bytes;
       const uint64_t stride = I->seg_stride[0];
+      if (op == OP_EDN) {
+        // this CU's units of the selected experts' down projections
+        const uint32_t Rb = npu, nb = I->aux[4], d = uint32_t(a.hidden);
+        uint32_t lo, hi;
+        edn_range(uint32_t(__builtin_popcountll(mask)), nb, I->n_items, uint32_t(cu), lo, hi);
+        uint64_t m = mask;
+        uint32_t er = 0;
+        for (uint32_t u = lo; u < hi; u++) {
+          const uint32_t ue = u / nb, ub = u % nb;
+          for (; er < ue; er++) m &= m - 1;
+          const uint32_t e = uint32_t(__builtin_ctzll(m));
+          const uint64_t src = I->seg_ptr[1] + e * stride + uint64_t(ub) * run;
+          const uint32_t valid = min(Rb, d - ub * Rb) * rb;
+          for (uint32_t p = 0; p < ppe; p++) {
+            const uint32_t g = pg++;
+            if (!acquire(g)) return;
+            const uint32_t dst = uint32_t(size_t(lds)) + page_off<LayB>(g) + half * kUnit;
+            issue_run(a, dst, src, (p * kUnitsPerPage + half) * kUnit, valid, voff, voff4k, nd, true);
+            after_issue(g, true);
+          }
+        }
+        continue;
+      }
       for (uint64_t m = mask; m; m &= m - 1) {
         const uint32_t e = uint32_t(__builtin_ctzll(m));
         const uint64_t b0 = I->seg_ptr[1] + e * stride, b1 = I->seg_ptr[2] + e * stride;
@@ -287,10 +323,7 @@ DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
           const uint32_t g = pg++;
           if (!acquire(g)) return;
           const uint32_t dst = uint32_t(size_t(lds)) + page_off<LayB>(g) + half * kUnit;
-          if (op == OP_EGU)
-            issue_gate_up(a, dst, b0, b1, p * kUnitsPerPage + half, npu, nit, rb, voff, voff4k, nd);
-          else
-            issue_run(a, dst, b0, (p * kUnitsPerPage + half) * kUnit, run, voff, voff4k, nd, true);
+          issue_gate_up(a, dst, b0, b1, p * kUnitsPerPage + half, npu, nit, rb, voff, voff4k, nd);
           after_issue(g, true);
         }
       }
@@ -733,111 +766,152 @@ done:
 }
 
 // ---------------------------------------------------- expert down projection
-// The routed (expert, sequence) pairs, in expert then sequence order, are
-// staged into the x slot in groups of cap = 16384 / K pairs (an expert's
-// pairs may straddle two groups).  While a group is computed, the next one is
-// already being loaded into registers.  Items are (expert with pairs in the
-// group, row pair); each stores its dots per (sequence, slot, row).  At the end
-// x_{l+1}[b][row] = h[b][row] + sum over slots s of w[b][s] * dot[b][s][row].
+// A CU's units touch one expert, or a few; only the routed sequences of
+// those experts are staged: their intermediates m[b][slot] go into the x slot
+// in groups of whole experts (at most cap = 16384 / Fe vectors; most CUs
+// need one group).  Items are (unit,
+// block of four rows); an item applies its rows to every sequence routed to
+// the unit's expert and stores y[b][slot of the expert in b's top-k][row].
 DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane, K = I->k, nit = i_nit(I), nB = uint32_t(a.batch);
   const int rt = rt_base(I->layer);
-  const uint32_t nsel = *lw(rt + RT_NSEL), npair = *lw(rt + RT_NPAIR);
-  const uint32_t ppe = I->aux[2], nr = I->aux[3];
+  const uint32_t nsel = *lw(rt + RT_NSEL);
+  const uint32_t ppu = I->aux[2], Rb = I->aux[3], nb = I->aux[4], d = uint32_t(a.hidden);
   const uint32_t k = uint32_t(a.top_k), Fe = uint32_t(a.expert_ffn);
-  const uint32_t cap = uint32_t(lb::kXFloats) / K;  // pairs per group
-  const uint32_t ngroups = (npair + cap - 1) / cap;
+  const uint32_t cap = uint32_t(lb::kXFloats) / K;  // staged vectors per group
+  uint32_t u_lo, u_hi;
+  edn_range(nsel, nb, I->n_items, uint32_t(c.cu), u_lo, u_hi);
+  const uint32_t ytag = y_tag(c.ep, I->layer);
   float* xs = reinterpret_cast<float*>(lds + lb::kX);
-  float* dots = reinterpret_cast<float*>(lds + lb::kDots);
-  constexpr int NC = (lb::kXFloats / 256 + kNComp - 1) / kNComp;  // 256-value chunks per wave
+  uint64_t* yout = reinterpret_cast<uint64_t*>(I->out_ptr);
   const bool trl = a.trace && c.w == 0 && lane == 0;
   const __amdgpu_buffer_rsrc_t rm = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), nB * k * Fe * 4);
-  // rank of the selected expert holding pair index pi
-  auto rank_of = [&](uint32_t pi) -> uint32_t { return rt_u8(rt, RT_PRANK + int(pi)); };
-  // this wave's chunks of group g (256 values each), loaded into registers
-  f4 t[NC];
-  auto load_group = [&](uint32_t g) {
-    const uint32_t p0 = g * cap, np = min(cap, npair - p0), nch = np * K / 256;
+  auto n_pairs = [&](uint32_t er) -> uint32_t {
+    return uint32_t(__builtin_popcount(rt_u8(rt, RT_TOK + int(rt_u8(rt, RT_LIST + int(er))))));
+  };
+  // last expert rank of the group that starts at rank g0 (whole experts,
+  // at most cap pairs; one expert has at most B <= cap)
+  const uint32_t er_last = u_lo < u_hi ? (u_hi - 1) / nb : 0;
+  auto group_end = [&](uint32_t g0) -> uint32_t {
+    uint32_t g1 = g0, cnt = n_pairs(g0);
+    while (g1 < er_last && cnt + n_pairs(g1 + 1) <= cap) cnt += n_pairs(++g1);
+    return g1;
+  };
+  // the intermediates of the pairs [p0, p0 + np) into the x slot, 256
+  // values per wave and chunk, four chunks of a wave in flight at a time
+  auto stage_group = [&](uint32_t p0, uint32_t np) {
+    const uint32_t nch = np * K / 256;
+    for (uint32_t c0 = uint32_t(c.w); c0 < nch; c0 += 4 * kNComp) {
+      f4 t[4];
 #pragma unroll
-    for (int qq = 0; qq < NC; qq++) {
-      const uint32_t ch = uint32_t(c.w) + kNComp * qq;
-      uint32_t off = 0;
-      if (ch < nch) {
-        const uint32_t pi = p0 + ch * 256 / K, kk = ch * 256 % K;
-        const uint32_t pr = *reinterpret_cast<const uint16_t*>(lds + rt + RT_PAIR + int(pi) * 2);
-        const uint32_t b = (pr >> 6) & 7, sl = pr >> 9;
-        off = ((b * k + sl) * Fe + kk + 4 * lane) * 4;
+      for (int j = 0; j < 4; j++) {
+        const uint32_t ch = c0 + kNComp * j;
+        uint32_t off = 0;
+        if (ch < nch) {
+          const uint32_t pi = p0 + ch * 256 / K, kk = ch * 256 % K;
+          const uint32_t pr = *reinterpret_cast<const uint16_t*>(lds + rt + RT_PAIR + int(pi) * 2);
+          const uint32_t b = (pr >> 6) & 7, sl = pr >> 9;
+          off = ((b * k + sl) * Fe + kk + 4 * lane) * 4;
+        }
+        t[j] = ld_act4(rm, off);
       }
-      t[qq] = ld_act4(rm, off);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const uint32_t ch = c0 + kNComp * j;
+        if (ch < nch) *reinterpret_cast<f4*>(xs + ch * 256 + 4 * lane) = t[j];
+      }
     }
   };
-  // residual rows (leader), then every wave has left the previous input
-  if (c.w == 0 && !stage_res_b(c, I, i, nr, uint32_t(a.hidden))) return false;
+  // every wave has left the previous input before the slot is rewritten
   if (!wait_all_ge(C_XCONS, i)) return false;
   if (trl) trace_put(a, c.cu, i, TR_XFREE, now32());
-  load_group(0);
-  for (uint32_t g = 0; g < ngroups; g++) {
-    const uint32_t p0 = g * cap, np = min(cap, npair - p0), nch = np * K / 256;
-    // every wave has finished the previous group before its slot is rewritten
-    if (g > 0 && !comp_barrier()) return false;
-#pragma unroll
-    for (int qq = 0; qq < NC; qq++) {
-      const uint32_t ch = uint32_t(c.w) + kNComp * qq;
-      if (ch < nch) *reinterpret_cast<f4*>(xs + ch * 256 + 4 * lane) = t[qq];
-    }
+  const uint32_t nrb = (Rb + 3) / 4;
+  for (uint32_t g0 = u_lo / nb; u_lo < u_hi;) {
+    // group: experts g0 .. g1 and their pairs [p0, p0 + np)
+    const uint32_t g1 = group_end(g0);
+    const uint32_t p0 = rt_u8(rt, RT_PBASE + int(g0));
+    const uint32_t np = rt_u8(rt, RT_PBASE + int(g1)) + n_pairs(g1) - p0;
+    stage_group(p0, np);
     if (!comp_barrier()) return false;
-    if (g + 1 < ngroups) load_group(g + 1);
-    if (trl && g == 0) trace_put(a, c.cu, i, TR_ITEM0, now32());
-    // items: (expert rank er in [er_a, er_b], block of 4 rows)
-    const uint32_t er_a = uni(rank_of(p0)), er_b = uni(rank_of(p0 + np - 1));
-    const uint32_t nrb = (nr + 3) / 4;
-    const uint32_t n_items = (er_b - er_a + 1) * nrb;
+    if (trl && g0 == u_lo / nb) {
+      trace_put(a, c.cu, i, TR_STAGED, now32());
+      trace_put(a, c.cu, i, TR_ITEM0, now32());
+    }
+    // the group's units and their blocks of four rows
+    const uint32_t ua = max(u_lo, g0 * nb), ub = min(u_hi, (g1 + 1) * nb);
+    const uint32_t n_items = (ub - ua) * nrb;
     for (uint32_t it = c.w; it < n_items; it += kNComp) {
-      const uint32_t er = er_a + it / nrb, r0 = 4 * (it % nrb);
+      const uint32_t u = ua + it / nrb, r0 = 4 * (it % nrb);
+      const uint32_t er = u / nb, rb = u % nb;
+      const uint32_t rows_u = min(Rb, d - rb * Rb);
+      if (r0 >= rows_u) continue;
       const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
       const uint32_t tok = uni(rt_u8(rt, RT_TOK + int(e)));
-      const uint32_t base = uni(rt_u8(rt, RT_PBASE + int(er)));
-      // the expert's sequences whose pair lies in this group
-      uint32_t tm = 0, rank = 0;
-      for (uint32_t bits = tok; bits; bits &= bits - 1, rank++) {
-        const uint32_t pi = base + rank;
-        if (pi >= p0 && pi < p0 + np) tm |= 1u << __builtin_ctz(bits);
-      }
-      const uint32_t nrows = min(4u, nr - r0);
-      const uint32_t u0 = er * ppe * kUnitsPerPage + r0 * nit;
+      const uint32_t base = uni(rt_u8(rt, RT_PBASE + int(er))) - p0;
+      const uint32_t nrows = min(4u, rows_u - r0);
+      const uint32_t u0 = (u - u_lo) * ppu * kUnitsPerPage + r0 * nit;
       if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + u0 / kUnitsPerPage);
       if (!wait_page(pg + (u0 + nrows * nit - 1) / kUnitsPerPage, c.fcache)) return false;
       float acc[32];
-      dot_rows4(pg, u0, nit, nrows, tm,
-                [&](int b) { return (base + __builtin_popcount(tok & ((1u << b) - 1)) - p0) * K; }, acc);
+      dot_rows4(pg, u0, nit, nrows, tok,
+                [&](int b) { return (base + __builtin_popcount(tok & ((1u << b) - 1))) * K; }, acc);
       const float sdot = reduce32(acc);
-      const uint32_t idx = reduce32_index(lane), row = r0 + (idx >> 3), bb = idx & 7;
-      if (lane < 32 && ((tm >> bb) & 1) && row < nr) {
+      const uint32_t idx = reduce32_index(lane), rr = idx >> 3, bb = idx & 7;
+      if (lane < 32 && ((tok >> bb) & 1) && rr < nrows) {
         const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + bb));
-        dots[(bb * lb::kMaxTopK + slot) * lb::kMaxDnRows + row] = sdot;
+        st_tag(yout + size_t(bb * k + slot) * d + rb * Rb + r0 + rr, sdot, ytag);
       }
     }
-    // no page before the next group's first expert is read again: release
-    // them, or a group longer than the ring would wait on itself
-    if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + (g + 1 < ngroups ? uni(rank_of(p0 + np)) : nsel) * ppe);
+    // the next group starts at the unit after this group's last one
+    if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + (ub - u_lo) * ppu);
+    if (g1 >= er_last) break;
+    g0 = g1 + 1;
+    // every wave has finished this group before the slot is rewritten
+    if (!comp_barrier()) return false;
   }
-  if (!comp_barrier()) return false;
   if (trl) trace_put(a, c.cu, i, TR_A_STATS, now32());
-  // x_{l+1} = h + sum over the top-k slots in order
-  const float* res = res_slot_b(i);
-  const float* wt = reinterpret_cast<const float*>(lds + rt + RT_WT);
-  uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
-  for (uint32_t idx = c.w * 64 + lane; idx < nB * nr; idx += 64 * kNComp) {
-    const uint32_t b = idx / nr, r = idx % nr;
-    float y = 0.f;
-    for (uint32_t s = 0; s < k; s++) y = fmaf(wt[b * 8 + s], dots[(b * lb::kMaxTopK + s) * lb::kMaxDnRows + r], y);
-    st_tag(out + size_t(b) * a.hidden + I->row0 + r, res[b * nr + r] + y, a.epoch);
-  }
   if (lane == 0) {
-    lds_st(C_RELEASED + 4 * c.w, pg + nsel * ppe);
+    lds_st(C_RELEASED + 4 * c.w, pg + (u_hi - u_lo) * ppu);
     lds_st(C_XCONS + 4 * c.w, i + 1);
   }
+  return true;
+}
+
+// Expert sum: x_{l+1}[b][r] = h[b][r] + sum over the top-k slots s, in slot
+// order, of w[b][s] * y[b][s][r] for the instruction's rows.  The outputs of
+// the experts are polled by their tags (their writers are decided by the
+// routing), the residual h by the step's tag.
+DEV bool erd(Comp& c, InstrCP I, uint32_t i) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane, nB = uint32_t(a.batch), k = uint32_t(a.top_k), d = uint32_t(a.hidden);
+  const uint32_t nr = I->n_rows, r0 = I->row0, total = nB * nr;
+  const int rt = rt_base(I->layer);
+  const float* wt = reinterpret_cast<const float*>(lds + rt + RT_WT);
+  const uint32_t htag = in_tag(c.ep, I), ytag = y_tag(htag, I->layer);
+  const __amdgpu_buffer_rsrc_t ry = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), nB * k * d * kActBytes);
+  const __amdgpu_buffer_rsrc_t rh = act_rsrc(reinterpret_cast<const void*>(I->res_ptr), nB * d * kActBytes);
+  uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
+  for (uint32_t base = uint32_t(c.w) * 64; base < total; base += 64 * kNComp) {
+    const uint32_t idx = base + lane, on = idx < total;
+    const uint32_t b = on ? idx / nr : 0, r = on ? idx % nr : 0, row = r0 + r;
+    auto yoff = [&](int, int s) -> uint32_t { return ((b * k + uint32_t(s)) * d + row) * kActBytes; };
+    uint2 ty[lb::kMaxTopK], th[1];
+#pragma unroll
+    for (int s = 0; s < lb::kMaxTopK; s++)
+      if (uint32_t(s) < k) reload(ty[s], ry, yoff(0, s));
+    reload(th[0], rh, (b * d + row) * kActBytes);
+    if (!wait_fresh(ty, on ? k : 0, ry, yoff, 0, ytag, c.retries)) return false;
+    if (!wait_fresh(th, on, rh, [&](int, int) { return (b * d + row) * kActBytes; }, 0, htag, c.retries))
+      return false;
+    if (a.trace && c.w == 0 && lane == 0 && base == 0) trace_put(a, c.cu, i, TR_STAGED, now32());
+    float y = 0.f;
+#pragma unroll
+    for (int s = 0; s < lb::kMaxTopK; s++)
+      if (uint32_t(s) < k) y = fmaf(wt[b * 8 + uint32_t(s)], __uint_as_float(ty[s].x), y);
+    if (on) st_tag(out + size_t(b) * d + row, __uint_as_float(th[0].x) + y, c.ep);
+  }
+  if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
   return true;
 }
 
@@ -933,8 +1007,11 @@ template <class G>
 DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
   Comp c{&a, cu, w, uint32_t(threadIdx.x & 63), 0, 0, 0, a.epoch, a.pos, 0, 0};
   const bool tr = a.trace != nullptr;
-  uint64_t staged_in = 0, staged_gain = 0;
-  uint32_t staged_flags = 0, staged_k = 0;
+  // the instruction whose input the x slot holds (kNoCounter: none); its
+  // record is re-read to decide whether a later instruction can reuse it
+  uint32_t staged = kNoCounter;
+  // the last instruction at which the compute waves synchronised
+  uint32_t last_sync = 0;
   uint32_t seen_ctr = kNoCounter, seen_val = 0;
   uint32_t pg = 0;
   for (uint32_t i = 0; i < n; i++) {
@@ -996,13 +1073,20 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       return;
     }
     uint32_t np = I->n_pages;
-    if (op == OP_EGU || op == OP_EDN) np = *lw(rt_base(I->layer) + RT_NSEL) * I->aux[2];
+    if (op == OP_EGU) np = *lw(rt_base(I->layer) + RT_NSEL) * I->aux[2];
+    if (op == OP_EDN) {
+      uint32_t lo, hi;
+      edn_range(*lw(rt_base(I->layer) + RT_NSEL), I->aux[4], I->n_items, uint32_t(cu), lo, hi);
+      np = (hi - lo) * I->aux[2];
+    }
     if (i_flags(I) & F_DIRECT) np = 0;
     bool ok = true;
     if (op == OP_BGEMV || op == OP_EGU) {
       const uint32_t fl = i_flags(I) & (F_IN_EMBED | F_NORM);
-      const bool reuse = I->in_ptr == staged_in && fl == staged_flags && I->k == staged_k &&
-                         (!(fl & F_NORM) || I->gain_ptr == staged_gain);
+      InstrCP S = q + (staged == kNoCounter ? i : staged);
+      const bool reuse = staged != kNoCounter && I->in_ptr == S->in_ptr &&
+                         fl == (i_flags(S) & (F_IN_EMBED | F_NORM)) && I->k == S->k &&
+                         (!(fl & F_NORM) || I->gain_ptr == S->gain_ptr);
       const bool res = op == OP_BGEMV && i_epi(I) == EPI_RESID;
       if (!reuse || res) {
         if (!coop_stage_b(c, I, i, !reuse)) {
@@ -1010,15 +1094,16 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
           return;
         }
         if (!comp_barrier()) return;
+        last_sync = i;
+      } else if (!done_slot_free(i, last_sync)) {
+        if (c.lane == 0) lds_st(C_ABORT, 1);
+        return;
       }
       if (tr && w == 0 && c.lane == 0) {
         trace_put(a, cu, i, TR_STAGED, now32());
         trace_put(a, cu, i, TR_RETRY, c.retries);
       }
-      staged_in = I->in_ptr;
-      staged_flags = fl;
-      staged_k = I->k;
-      staged_gain = I->gain_ptr;
+      if (!reuse) staged = i;
       if (op == OP_BGEMV) {
         ok = bgemv(c, I, i, pg);
       } else if (i_flags(I) & F_DIRECT) {
@@ -1027,8 +1112,13 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       } else {
         ok = egu(c, I, i, pg);
       }
+    } else if (op == OP_ERD) {
+      ok = done_slot_free(i, last_sync) && erd(c, I, i);
     } else {
-      staged_in = 0;
+      // attention and the expert down projection wait for every wave to
+      // have read the previous instruction's inputs
+      staged = kNoCounter;
+      last_sync = i;
       ok = op == OP_EDN ? edn(c, I, i, pg) : run_attn_b<G>(c, I, i, pg);
     }
     if (!ok) {

@@ -422,6 +422,20 @@ DEV bool wait_all_ge(int off, uint32_t want) {
     __builtin_amdgcn_s_sleep(0);
   }
 }
+// The per-instruction completion counters (C_DONE) are a ring of kDoneRing
+// slots, each cleared by the last wave to add to it; a wave adds to
+// instruction i's slot after its work on i.  An instruction that stages its
+// inputs synchronises the waves: each has read the inputs of the previous
+// instruction (its C_XCONS word has reached i), so each has added to the
+// slots up to i - 2.  Between two such instructions a fast wave can run ahead
+// through instructions without a wait (one that reuses the staged input, an
+// expert sum); at kDoneRing - 1 or more instructions past the last
+// synchronisation it first waits until every wave's word has reached
+// i - kDoneRing + 2, i.e. every wave has added to (and the last one has
+// cleared) the slot of instruction i - kDoneRing.
+DEV bool done_slot_free(uint32_t i, uint32_t last_sync) {
+  return i - last_sync < uint32_t(kDoneRing - 1) || wait_all_ge(C_XCONS, i - kDoneRing + 2);
+}
 DEV uint32_t min_filled() {
   uint32_t m = lds_ld_rlx(C_FILLED);
 #pragma unroll

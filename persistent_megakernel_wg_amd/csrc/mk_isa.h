@@ -82,7 +82,8 @@ enum Op : uint8_t {
   OP_ATTN = 2,        // decode attention tile (one sequence)
   OP_BGEMV = 3,       // batched GEMV tile: every row applied to all B sequences
   OP_EGU = 4,         // expert gate/up slice of every selected expert (SwiGLU)
-  OP_EDN = 5,         // expert down-projection rows, weighted sum over the top-k
+  OP_EDN = 5,         // expert down-projection units of the selected experts
+  OP_ERD = 6,         // weighted sum of the top-k expert outputs + residual
 };
 
 // GEMV epilogues
@@ -175,18 +176,26 @@ struct PackCopy {
 // Batched GEMV (OP_BGEMV): rows are taken in pairs (n_items pairs); the input
 // is [B][k], the output [B][aux[0]] and the residual [B][aux[2]] (elements);
 //   aux[1] = argmax slot index, aux[3] = LM-head tiles (EPI_ARGMAX)
-// Expert instructions (OP_EGU, OP_EDN): the weight runs are read in place.
+// Expert gate/up (OP_EGU): the weight runs are read in place.
 //   aux[0] = router counter, aux[1] = its producers per step
-//   aux[2] = pages per expert region, aux[3] = gate/up pairs (EGU) or rows (EDN)
-//   aux[4] = experts
+//   aux[2] = pages per expert region, aux[3] = gate/up pairs, aux[4] = experts
 //   seg_ptr[0] = router logits [B][E] (tagged)
-//   seg_ptr[1] = first gate row (EGU) / first down row (EDN) of expert 0
-//   seg_ptr[2] = first up row of expert 0 (EGU)
+//   seg_ptr[1] = first gate row, seg_ptr[2] = first up row of expert 0
 //   seg_stride[0] = bytes between experts' runs; seg_rows[0] = bytes of a run
-//   seg_stride[1] = pages of the gate run within an expert region (EGU)
-//   row0 = first FFN row of the slice (EGU) / first output row (EDN)
-//   in_ptr = x (EGU) or m [B][top_k][Fe] (EDN); res_ptr = h (EDN)
-//   out_ptr = m (EGU) or x_{l+1} (EDN)
+//   seg_stride[1] = pages of the gate run within an expert region
+//   row0 = first FFN row of the slice; in_ptr = x; out_ptr = m [B][top_k][Fe]
+// Expert down projection (OP_EDN): units of n_rows (= aux[3]) consecutive
+// down rows of one selected expert; the U = (selected experts) x aux[4] units
+// of a layer, in expert order, go to the n_items CUs in even contiguous
+// ranges, decided at run time from the routing.
+//   aux[0], aux[1] as for OP_EGU; aux[2] = pages per unit; aux[4] = units per expert
+//   seg_ptr[0] = router logits; seg_ptr[1] = expert 0's first down row
+//   seg_stride[0] = bytes between experts; seg_rows[0] = bytes of a full unit
+//   in_ptr = m [B][top_k][Fe]; out_ptr = y [B][top_k][d], tagged with
+//   (step << 7) | layer
+//   n_pages = the most pages a CU can take (the loader streams the CU's units)
+// Expert sum (OP_ERD): rows row0 .. row0 + n_rows of x_{l+1} for every sequence:
+//   in_ptr = y, res_ptr = h, out_ptr = x_{l+1}
 
 // Kernel launch arguments.
 struct KArgs {

@@ -587,6 +587,8 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
   // loads of the next instruction's input, issued while this one's items run
   StageIn pre;
   uint32_t pre_i = 0xFFFFFFFFu;
+  // the last instruction at which the compute waves synchronised
+  uint32_t last_sync = 0;
   // The launch runs a.n_steps steps back to back.  Instruction i of step s is
   // instruction ig = s * n + i of the launch: the LDS words that order the
   // waves count instructions and pages of the launch, and each step carries
@@ -624,14 +626,22 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       if (tr && c.lane == 0) trace_put(a, cu, ti, TR_DEPS, now32());
     }
     if (coop) {
-      // every wave stages its share; a barrier publishes the x slot
-      if (!reuse || needs_res(I)) {
-        if (pre_i != ig) stage_issue(c, I, !reuse, pre);
-        if (!stage_finish(c, I, ig, !reuse, pre)) {
-          if (c.lane == 0) lds_st(C_ABORT, 1);
-          return;
+      // every wave stages its share; a barrier publishes the x slot.  An
+      // instruction that reuses the slot takes the barrier only after a run
+      // of such instructions long enough to wrap the completion-counter
+      // ring (a fast wave must not add to a slot whose previous instruction
+      // a slow wave has not finished)
+      const bool stage = !reuse || needs_res(I);
+      if (stage || ig - last_sync >= uint32_t(kDoneRing - 1)) {
+        if (stage) {
+          if (pre_i != ig) stage_issue(c, I, !reuse, pre);
+          if (!stage_finish(c, I, ig, !reuse, pre)) {
+            if (c.lane == 0) lds_st(C_ABORT, 1);
+            return;
+          }
         }
         if (!comp_barrier()) return;
+        last_sync = ig;
       }
       if (tr && w == 0 && c.lane == 0) {
         trace_put(a, cu, ti, TR_XFREE, now32());
@@ -657,6 +667,7 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
     } else if (!wait_lds_ge(C_XOK, ig + 1)) {
       return;
     }
+    if (!coop) last_sync = ig;
     if (is_gemv) {
       staged_in = I->in_ptr;
       staged_flags = i_flags(I) & (F_IN_EMBED | F_NORM);

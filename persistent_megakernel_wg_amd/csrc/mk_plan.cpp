@@ -26,9 +26,9 @@
 namespace mk {
 namespace {
 
-enum Buf { BUF_EMBED = 0, BUF_X, BUF_QKV, BUF_O, BUF_H, BUF_M, BUF_LOGITS, BUF_RL, BUF_COUNT };
-const char* kBufName[] = {"embed", "x", "qkv", "o", "h", "m", "logits", "router"};
-enum LStage { ST_QKV = 0, ST_ATTN = 1, ST_O = 2, ST_GU = 3, ST_DOWN = 4, ST_PER_LAYER = 8 };
+enum Buf { BUF_EMBED = 0, BUF_X, BUF_QKV, BUF_O, BUF_H, BUF_M, BUF_LOGITS, BUF_RL, BUF_Y, BUF_COUNT };
+const char* kBufName[] = {"embed", "x", "qkv", "o", "h", "m", "logits", "router", "y"};
+enum LStage { ST_QKV = 0, ST_ATTN = 1, ST_O = 2, ST_GU = 3, ST_DOWN = 4, ST_DRED = 5, ST_PER_LAYER = 8 };
 
 uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 
@@ -271,6 +271,9 @@ ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
     a.rl[l] = is_batched(c) ? take(E * B * c.n_experts) : 0;
     a.part[l] = take(4 * uint64_t(max_parts) * hpg * (c.head_dim + 2));
   }
+  // expert outputs [B][top_k][d] of the layer being computed (one buffer for
+  // every layer: its tags carry the layer as well as the step)
+  a.y = is_batched(c) ? take(E * B * uint64_t(c.top_k) * c.hidden) : 0;
   a.tok = take(E * B);
   a.rope_cos = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
   a.rope_sin = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
@@ -345,7 +348,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
     *lo = N * cu / C;
     *hi = N * (cu + 1) / C;
   };
-  std::vector<uint32_t> c_qkv(L), c_rt(L), c_attn(L), c_gu(L), c_o(L), c_dn(L);
+  std::vector<uint32_t> c_qkv(L), c_rt(L), c_attn(L), c_gu(L), c_o(L), c_dny(L), c_dn(L);
   std::vector<std::vector<uint32_t>> c_ticket(L);
   for (int l = 0; l < L; l++) {
     c_qkv[l] = b.new_counter(l * ST_PER_LAYER + ST_QKV);
@@ -355,7 +358,8 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
       for (int t = 0; t < B * G * tpg; t++) c_ticket[l].push_back(b.new_counter(l * ST_PER_LAYER + ST_ATTN));
     c_gu[l] = b.new_counter(l * ST_PER_LAYER + ST_ATTN);
     c_o[l] = b.new_counter(l * ST_PER_LAYER + ST_O);
-    c_dn[l] = b.new_counter(l * ST_PER_LAYER + ST_DOWN);
+    c_dny[l] = b.new_counter(l * ST_PER_LAYER + ST_DOWN);
+    c_dn[l] = b.new_counter(l * ST_PER_LAYER + ST_DRED);
   }
   const uint32_t c_lm = b.new_counter(L * ST_PER_LAYER);
   // a batched GEMV tile: rows [r0, r1) of one matrix (or the Wq|Wk|Wv
@@ -572,12 +576,15 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
       }
     }
     // ---------------------------------------------------------------- EDN
-    for (int cu = 0; cu < C; cu++) {
-      int64_t c0, c1;
-      split(d, cu, &c0, &c1);
-      for (int64_t r0 = c0; r0 < c1; r0 += max_res_rows) {
-        const int64_t r1 = std::min<int64_t>(c1, r0 + max_res_rows), nr = r1 - r0;
-        const int ppe = ceil_div(nr * 2 * Fe, kPageBytes);
+    // The down projections of the selected experts, cut into units of Rb
+    // rows (32 KiB of weights); the units of all selected experts, in expert
+    // order, are split evenly over the CUs at run time.  A unit's outputs go
+    // to y[b][slot][row] for the sequences routed to its expert.
+    {
+      const int Rb = std::max(4, 32768 / (2 * Fe));
+      const int nb = ceil_div(d, Rb), ppu = ceil_div(int64_t(Rb) * 2 * Fe, kPageBytes);
+      const int max_units = int(ceil_div(int64_t(E) * nb, C));
+      for (int cu = 0; cu < C; cu++) {
         Instr I = blank();
         I.op = OP_EDN;
         I.nit = uint8_t(Fe / 512);
@@ -585,35 +592,61 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.layer = uint16_t(l);
         I.flags = F_SIGNAL | (routed[cu] ? 0 : F_ROUTE);
         routed[cu] = 1;
-        I.n_items = uint32_t((nr + 1) / 2);
-        I.row0 = uint32_t(r0);
+        I.n_items = uint32_t(C);
         I.row_bytes = uint32_t(2 * Fe);
-        I.n_rows = uint32_t(nr);
+        I.n_rows = uint32_t(Rb);
         I.k = uint32_t(Fe);
         I.aux[0] = c_rt[l];
-        I.aux[2] = uint32_t(ppe);
-        I.aux[3] = uint32_t(nr);
-        I.aux[4] = uint32_t(E);
+        I.aux[2] = uint32_t(ppu);
+        I.aux[3] = uint32_t(Rb);
+        I.aux[4] = uint32_t(nb);
         I.seg_ptr[0] = A + ar.rl[l];
-        I.seg_ptr[1] = lptr(in.w.e_down, l, uint64_t(E) * d * Fe) + 2ull * Fe * r0;
+        I.seg_ptr[1] = lptr(in.w.e_down, l, uint64_t(E) * d * Fe);
         I.seg_stride[0] = uint32_t(2ull * d * Fe);
-        I.seg_rows[0] = uint32_t(nr * 2 * Fe);
-        I.seg_stride[1] = 0;
+        I.seg_rows[0] = uint32_t(Rb * 2 * Fe);
         I.in_ptr = A + ar.m[l];
-        I.res_ptr = A + ar.h[l];
-        I.out_ptr = A + ar.x[l + 1];
+        I.out_ptr = A + ar.y;
         I.wait_ctr[0] = c_gu[l];
-        I.wait_ctr[1] = c_o[l];
-        I.sig_ctr = c_dn[l];
-        I.n_pages = uint32_t(E * ppe);
+        I.sig_ctr = c_dny[l];
+        I.n_pages = uint32_t(max_units * ppu);
         InstrMeta m;
         m.stage = stg + ST_DOWN;
-        m.merge_write = false;
+        // every unit's writes are decided by the routing: the tiles share
+        // the layer's whole buffer
+        m.merge_write = true;
         m.reads.push_back({BUF_M, l, 0, uint64_t(B) * c.top_k * Fe});
         m.reads.push_back({BUF_RL, l, 0, uint64_t(B) * E});
+        m.writes.push_back({BUF_Y, l, 0, uint64_t(B) * c.top_k * d});
+        b.push(cu, I, std::move(m), int64_t(E) * d * 2 * Fe / C);
+      }
+    }
+    // ---------------------------------------------------------------- ERD
+    // x_{l+1}[b][r] = h[b][r] + sum over the top-k slots s, in slot order, of
+    // w[b][s] * y[b][s][r], for the CU's rows of every sequence
+    for (int cu = 0; cu < C; cu++) {
+      int64_t r0, r1;
+      split(d, cu, &r0, &r1);
+      if (r1 > r0) {
+        const int64_t nr = r1 - r0;
+        Instr I = blank();
+        I.op = OP_ERD;
+        I.layer = uint16_t(l);
+        I.flags = F_SIGNAL;
+        I.row0 = uint32_t(r0);
+        I.n_rows = uint32_t(nr);
+        I.in_ptr = A + ar.y;
+        I.res_ptr = A + ar.h[l];
+        I.out_ptr = A + ar.x[l + 1];
+        I.wait_ctr[0] = c_dny[l];
+        I.wait_ctr[1] = c_o[l];
+        I.sig_ctr = c_dn[l];
+        InstrMeta m;
+        m.stage = stg + ST_DRED;
+        m.merge_write = false;
+        m.reads.push_back({BUF_Y, l, 0, uint64_t(B) * c.top_k * d});
         per_seq(m.reads, BUF_H, l, d, r0, r1);
         per_seq(m.writes, BUF_X, l + 1, d, r0, r1);
-        b.push(cu, I, std::move(m), int64_t(E) * nr * 2 * Fe);
+        b.push(cu, I, std::move(m), 0);
       }
     }
   }
@@ -1240,20 +1273,39 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
           return fail("residual rows exceed the LDS staging slot");
         continue;
       }
-      if (I.op == OP_EGU || I.op == OP_EDN) {
+      if (I.op == OP_EGU) {
         if (!p.batched) return fail("expert instruction in a one-sequence plan");
-        const uint32_t ppe = I.aux[2], runs = I.op == OP_EGU ? 2 : 1;
+        const uint32_t ppe = I.aux[2];
         if (I.k % 512 || I.nit != I.k / 512 || I.row_bytes != 2 * I.k) return fail("expert row geometry");
-        if (uint64_t(ppe) * kPageBytes < uint64_t(runs) * I.seg_rows[0] || ppe > uint32_t(lb::kPages) - 1)
+        if (uint64_t(ppe) * kPageBytes < 2ull * I.seg_rows[0] || ppe > uint32_t(lb::kPages) - 1)
           return fail("expert page regions");
         if (I.n_pages != ((I.flags & F_DIRECT) ? 0 : ppe * I.aux[4]) || I.aux[4] != uint32_t(c.n_experts))
           return fail("expert page budget");
-        if ((I.flags & F_DIRECT) && (I.op != OP_EGU || (I.nit != 1 && I.nit != 2 && I.nit != 4)))
-          return fail("direct expert loads");
-        if (I.op == OP_EGU && I.seg_rows[0] != I.aux[3] * I.row_bytes) return fail("expert gate/up runs");
-        if (I.op == OP_EDN && (I.seg_rows[0] != I.aux[3] * I.row_bytes || I.aux[3] > uint32_t(lb::kMaxDnRows) ||
-                               uint64_t(I.aux[3]) * c.batch > uint64_t(kMaxResRows) || I.aux[3] != I.n_rows))
-          return fail("expert down-projection rows");
+        if ((I.flags & F_DIRECT) && (I.nit != 1 && I.nit != 2 && I.nit != 4)) return fail("direct expert loads");
+        if (I.seg_rows[0] != I.aux[3] * I.row_bytes) return fail("expert gate/up runs");
+        continue;
+      }
+      if (I.op == OP_EDN) {
+        if (!p.batched) return fail("expert instruction in a one-sequence plan");
+        const uint32_t ppu = I.aux[2], Rb = I.aux[3], nb = I.aux[4];
+        if (I.k % 512 || I.nit != I.k / 512 || I.row_bytes != 2 * I.k || I.k != uint32_t(c.expert_ffn))
+          return fail("expert row geometry");
+        if (!Rb || Rb != I.n_rows || nb != uint32_t(ceil_div(c.hidden, Rb)) || I.seg_rows[0] != Rb * I.row_bytes ||
+            ppu != uint32_t(ceil_div(I.seg_rows[0], kPageBytes)))
+          return fail("expert down-projection units");
+        // a 4-row item lies in at most kPages - 1 pages; every sequence routed
+        // to one expert fits the x slot at once
+        if (uint32_t(ceil_div(4 * I.row_bytes, kPageBytes)) + 1 > uint32_t(lb::kPages) ||
+            uint64_t(c.batch) * I.k > uint64_t(lb::kXFloats))
+          return fail("expert down-projection items");
+        if (I.n_items != uint32_t(C) || I.n_pages != uint32_t(ceil_div(uint64_t(c.n_experts) * nb, C)) * ppu ||
+            (I.flags & F_DIRECT))
+          return fail("expert down-projection page budget");
+        continue;
+      }
+      if (I.op == OP_ERD) {
+        if (!p.batched) return fail("expert sum in a one-sequence plan");
+        if (I.n_pages || !I.n_rows || I.row0 + I.n_rows > uint32_t(c.hidden)) return fail("expert sum rows");
         continue;
       }
       if (I.op == OP_GEMV) {
@@ -1462,24 +1514,32 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
       }
       if (I.op == OP_EGU || I.op == OP_EDN) {
         const uint64_t stride = I.seg_stride[0], run = I.seg_rows[0];
-        const int nrun = I.op == OP_EGU ? 2 : 1;
-        for (int r = 0; r < nrun; r++) {
-          const uint64_t lo = I.seg_ptr[1 + r];
-          if (!inside(lo, lo + (NE - 1) * stride + run)) return fail("expert runs outside the expert tensors");
-        }
-        if (!in_arena(I.seg_ptr[0], I.seg_ptr[0] + EB * NB * NE)) return fail("router logits outside the arena");
         const uint64_t mb = EB * NB * c.top_k * Fe;
+        if (!in_arena(I.seg_ptr[0], I.seg_ptr[0] + EB * NB * NE)) return fail("router logits outside the arena");
         if (I.op == OP_EGU) {
+          for (int r = 0; r < 2; r++) {
+            const uint64_t lo = I.seg_ptr[1 + r];
+            if (!inside(lo, lo + (NE - 1) * stride + run)) return fail("expert runs outside the expert tensors");
+          }
           if (I.row0 + I.aux[3] > Fe) return fail("expert gate/up slice");
           if (!(I.flags & F_IN_EMBED) && !in_arena(I.in_ptr, I.in_ptr + EB * NB * d))
             return fail("expert input outside the arena");
           if (!in_arena(I.out_ptr, I.out_ptr + mb)) return fail("expert intermediate outside the arena");
         } else {
+          // the loader clips a unit to the expert's d rows
+          const uint64_t lo = I.seg_ptr[1];
+          if (stride != 2ull * d * Fe || !inside(lo, lo + (NE - 1) * stride + d * I.row_bytes))
+            return fail("expert units outside the expert tensors");
           if (!in_arena(I.in_ptr, I.in_ptr + mb)) return fail("expert intermediate outside the arena");
-          const uint64_t rl = (NB - 1) * d + I.row0 + I.n_rows;
-          if (!in_arena(I.res_ptr, I.res_ptr + EB * rl) || !in_arena(I.out_ptr, I.out_ptr + EB * rl))
-            return fail("expert down-projection rows outside the arena");
+          if (!in_arena(I.out_ptr, I.out_ptr + EB * NB * c.top_k * d)) return fail("expert outputs outside the arena");
         }
+        continue;
+      }
+      if (I.op == OP_ERD) {
+        const uint64_t rl = (NB - 1) * d + I.row0 + I.n_rows;
+        if (!in_arena(I.in_ptr, I.in_ptr + EB * NB * c.top_k * d) || !in_arena(I.res_ptr, I.res_ptr + EB * rl) ||
+            !in_arena(I.out_ptr, I.out_ptr + EB * rl))
+          return fail("expert sum rows outside the arena");
         continue;
       }
       if (I.op == OP_GEMV) {

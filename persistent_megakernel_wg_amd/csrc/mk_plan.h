@@ -22,6 +22,7 @@ struct ArenaLayout {
   uint64_t x[129];        // residual stream entering layer l (x[0] unused: embedding)
   uint64_t qkv[128], o[128], h[128], m[128], part[128];
   uint64_t rl[128];       // router logits (mixture-of-experts decoder)
+  uint64_t y;             // [B][top_k][d] tagged expert outputs (mixture-of-experts decoder)
   uint64_t tok;           // [B] tagged greedy token of the last step
   uint64_t rope_cos, rope_sin, zero_page, lm_slots, status;
   uint64_t route_stats;   // [128] u32: selected experts per layer, summed over steps
