@@ -128,7 +128,16 @@ typedef struct {
                          KV group (default: 1 while n_q_heads * position
                          blocks <= n_cus, else the whole group; the MoE
                          decoder: the whole group) */
-  int32_t reserved;
+  int32_t o_split;    /* the O projection: 1 = split-K per KV group, each
+                         tile waiting only for its own group's attention and
+                         the last tile of a row block adding the residual
+                         and the group partials in group order (the Cohere
+                         kernel's removal of the attention -> O false
+                         dependency, airebao.com «快在哪里» item 2); -1 = whole
+                         rows after the whole attention stage (default;
+                         the MoE decoder always).  The split needs more than
+                         one KV group and heads-per-group * head_dim of 256
+                         or a multiple of 512 */
 } mk_plan_opts;
 
 /* Plan summary (filled by mk_plan_info / mk_plan_check). */

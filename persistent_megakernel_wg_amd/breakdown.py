@@ -1,7 +1,7 @@
 """Per-stage time breakdown of one decode step from the kernel's own trace.
 
     python -m persistent_megakernel_wg_amd.breakdown [--workload llama1b_ctx128]
-        [--steps 4] [--json out.json]
+        [--steps 4] [--json out.json] [--o-split 1]
 
 Runs a few steps of the workload on the GPU with the per-instruction trace
 switched on (mk_trace_enable: s_memrealtime stamps, 100 MHz, written by each
@@ -35,7 +35,7 @@ TR = dict(START=0, DEPS=1, STAGED=2, ITEMS=3, SIGNAL=4, PAGEWAIT=5, HW0=6, HW1=7
           XREADY=8, ITEM0=9, VISIBLE=10, XFREE=11, RETRY=15)
 OP_GEMV, OP_ATTN, OP_BGEMV, OP_EGU, OP_EDN, OP_ERD = 1, 2, 3, 4, 5, 6
 EPI_NAMES = {0: "qkv", 1: "o", 2: "gate_up", 3: "down", 4: "down", 5: "down", 6: "down",
-             7: "lm_head"}
+             7: "lm_head", 8: "o"}
 TICK_US = 0.01  # s_memrealtime runs at 100 MHz
 
 
@@ -166,6 +166,8 @@ def main() -> int:
     ap.add_argument("--workload", default="llama1b_ctx128")
     ap.add_argument("--steps", type=int, default=4)
     ap.add_argument("--json", default="")
+    ap.add_argument("--o-split", type=int, default=0,
+                    help="1: O projection split per KV group; -1: whole rows; 0: the plan's default")
     args = ap.parse_args()
     from . import binding as B
     from . import synth
@@ -174,7 +176,7 @@ def main() -> int:
     w = synth.make_weights(s)
     kc, vc = synth.make_kv_cache(s)
     tok = synth.make_tokens(s)
-    eng = Engine(s, w, kc, vc)
+    eng = Engine(s, w, kc, vc, plan=B.plan_opts(o_split=args.o_split) if args.o_split else None)
     try:
         info = eng.plan_info()
         B.mk_trace_enable(eng.ctx, True)

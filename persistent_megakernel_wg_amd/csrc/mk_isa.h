@@ -96,6 +96,7 @@ enum Epi : uint8_t {
   EPI_ACC_LAST = 5,   // out[r] = acc[r] + dot               (last chunk)
   EPI_ACC_ONLY = 6,   // out[r] = res[r] + dot  (single-chunk down projection)
   EPI_ARGMAX = 7,     // logits + greedy argmax              (LM head)
+  EPI_OPART = 8,      // part[g][r] = dot, split-K O projection of KV group g
 };
 
 // instruction flags
@@ -173,6 +174,13 @@ struct PackCopy {
 //   aux[0] = LDS accumulator offset (down projection)
 //   aux[1] = argmax slot index (LM head)
 //   aux[2] = LM-head ticket counter, aux[3] = LM-head tiles
+// Split-K O projection (OP_GEMV, EPI_OPART): rows row0 .. row0 + n_rows of
+// Wo[:, g*Kg .. (g+1)*Kg) . o_g, with Kg = (query heads per KV group) * Dh:
+//   aux[1] = g, aux[2] = ticket counter of the row block, aux[3] = G (tiles
+//   per row block); in_ptr = o + g*Kg (tagged); out_ptr = part + g*d (fp32,
+//   untagged, behind the ticket); res_ptr = x_l (tagged) or the embedding
+//   (F_RES_EMBED); seg_ptr[2] = h_l.  The tile taking the block's last ticket
+//   writes h_l[r] = x_l[r] + part[0][r] + ... + part[G-1][r] (in g order).
 // Batched GEMV (OP_BGEMV): rows are taken in pairs (n_items pairs); the input
 // is [B][k], the output [B][aux[0]] and the residual [B][aux[2]] (elements);
 //   aux[1] = argmax slot index, aux[3] = LM-head tiles (EPI_ARGMAX)

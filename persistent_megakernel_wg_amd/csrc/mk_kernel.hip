@@ -144,6 +144,10 @@ DEV void epi_row(Comp& c, const EpiCtx& E, uint32_t i, uint32_t t_row, float v, 
     case EPI_ACC_LAST:
       st_tag(out + row, reinterpret_cast<float*>(lds + kLdsAcc)[E.acc0 + t_row] + v, c.ep);
       break;
+    case EPI_OPART:
+      // the group's partial row (untagged fp32, published by the ticket)
+      st_act(reinterpret_cast<float*>(out) + row, v);
+      break;
     case EPI_ARGMAX:
       if (a.logits) gp(a.logits)[size_t(c.step) * uint32_t(a.vocab) + row] = v;
       if (v != v) __hip_atomic_store(gp(a.status) + ST_NAN, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -533,6 +537,35 @@ DEV void run_merge(Comp& c, InstrCP I) {
   }
 }
 
+// Split-K O projection, by the tile that took its row block's last ticket:
+// h_l[r] = x_l[r] + part[0][r] + ... + part[G-1][r], in group order, for the
+// block's rows (x_l tagged, or the token's embedding row in the first layer).
+DEV bool o_merge(Comp& c, InstrCP I) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane, d = uint32_t(a.hidden), G = I->aux[3], n = out_rows(I), r0 = I->row0;
+  const float* part = reinterpret_cast<const float*>(I->out_ptr) - size_t(I->aux[1]) * d;
+  uint64_t* h = reinterpret_cast<uint64_t*>(I->seg_ptr[2]);
+  const bool embed = i_flags(I) & F_RES_EMBED;
+  const uint16_t* e = embed ? reinterpret_cast<const uint16_t*>(I->res_ptr) + size_t(token_of(a, c.step, c.ep)) * d
+                            : nullptr;
+  const __amdgpu_buffer_rsrc_t rx =
+      act_rsrc_u(reinterpret_cast<const void*>(I->res_ptr), embed ? 0 : (r0 + n) * kActBytes);
+  for (uint32_t b0 = 0; b0 < n; b0 += 64) {
+    const uint32_t r = r0 + b0 + lane, on = b0 + lane < n;
+    uint2 t[1];
+    reload(t[0], rx, r * kActBytes);
+    if (!embed && !wait_fresh(t, on, rx, [&](int, int) { return r * kActBytes; }, 0, in_tag(c.ep, I), c.retries))
+      return false;
+    float v = 0.f;
+    if (on) {
+      v = embed ? __uint_as_float(uint32_t(e[r]) << 16) : __uint_as_float(t[0].x);
+      for (uint32_t g = 0; g < G; g++) v += ld_act(part + size_t(g) * d + r);
+      st_tag(h + r, v, c.ep);
+    }
+  }
+  return true;
+}
+
 // LM head: combine the per-wave bests, publish the CU's slot, take a ticket;
 // the last CU reduces all slots (lowest index wins ties) and writes the token.
 DEV void lm_finish(Comp& c, InstrCP I) {
@@ -700,8 +733,9 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
     // completion: the last wave signals.  Tagged outputs need no wait; the
     // untagged data behind a ticket (argmax slots, attention partials) must
     // have landed before the ticket moves.
+    const bool opart = i_op(I) == OP_GEMV && i_epi(I) == EPI_OPART;
     const bool release = (i_op(I) == OP_GEMV && i_epi(I) == EPI_ARGMAX) ||
-                         (i_op(I) == OP_ATTN && I->aux[3] > 1);
+                         (i_op(I) == OP_ATTN && I->aux[3] > 1) || opart;
     if (release) wait_vm0();
     if (tr && w == 0 && c.lane == 0) trace_put(a, cu, ti, TR_VISIBLE, now32());
     uint32_t prev = 0;
@@ -719,6 +753,16 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       old = uni(old);
       if (old + 1 != c.ep * I->aux[3]) continue;
       run_merge<G>(c, I);
+    }
+    if (opart) {
+      uint32_t old = 0;
+      if (c.lane == 0) old = ctr_release(ctr_line(a, I->aux[2], 0));
+      old = uni(old);
+      if (old + 1 != c.ep * I->aux[3]) continue;
+      if (!o_merge(c, I)) {
+        if (c.lane == 0) lds_st(C_ABORT, 1);
+        return;
+      }
     }
     if ((i_flags(I) & F_SIGNAL) && c.lane == 0) ctr_signal(ctr_line(a, I->sig_ctr, uint32_t(cu) % kCtrSpread));
     if (tr && c.lane == 0) trace_put(a, cu, ti, TR_SIGNAL, now32());
@@ -791,6 +835,10 @@ const Variant kVariants[] = {
     MK_VARIANT(4, 1, 4, 1, 8, 1, 4, 64),
     MK_VARIANT(8, 1, 8, 1, 7, 1, 4, 128),
     MK_VARIANT(1, 2, 1, 2, 2, 1, 1, 64),
+    // the same shapes with the O projection split per KV group
+    MK_VARIANT(4, 1, 1, 2, 8, 1, 1, 64),
+    MK_VARIANT(4, 1, 1, 2, 8, 1, 4, 64),
+    MK_VARIANT(8, 1, 1, 1, 7, 1, 4, 128),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 bool g_attr_set[kNumVariants] = {};

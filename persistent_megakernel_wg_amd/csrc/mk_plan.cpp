@@ -90,6 +90,24 @@ Instr blank() {
   return i;
 }
 
+// Instructions that finish through a ticket: a split attention tile (its KV
+// block's partials) and a split-K O tile (its KV group's partial rows).  Each
+// tile of a set takes one of n tickets on counter ctr; the tile that takes
+// the last one merges the set and signals the stage counter.
+bool ticketed(const Instr& I, uint32_t* ctr, uint32_t* n) {
+  if (I.op == OP_ATTN && I.aux[3] > 1) {
+    *ctr = I.seg_rows[0];
+    *n = I.aux[3];
+    return true;
+  }
+  if (I.op == OP_GEMV && I.epi == EPI_OPART) {
+    *ctr = I.aux[2];
+    *n = I.aux[3];
+    return true;
+  }
+  return false;
+}
+
 }  // namespace
 
 bool gemv_geometry(int K, int* nit, int* rpu) {
@@ -192,6 +210,7 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
   if (is_batched(c)) {
     // experts are split over the CUs by rows; the MLP chunk option is unused
     if (r.mlp_chunks <= 0) r.mlp_chunks = 1;
+    r.o_split = -1;
     if (r.attn_block <= 0) {
       // K and V blocks of a tile in four of the five ring pages, scores in
       // the scratch, whole KV groups per tile
@@ -242,6 +261,9 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
     const int nblk = (c.max_seq + r.attn_block - 1) / r.attn_block;
     r.attn_heads = (int64_t(c.n_q_heads) * nblk <= n_cus) ? 1 : hpg;
   }
+  // whole O rows by default: on MI355X the split's ticket and cross-CU merge
+  // cost more than the spread of the attention tiles it lets O overlap
+  if (r.o_split == 0) r.o_split = -1;
   if (r.watchdog_ms <= 0) r.watchdog_ms = 2000;
   return r;
 }
@@ -270,6 +292,7 @@ ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
     a.m[l] = take(E * F);
     a.rl[l] = is_batched(c) ? take(E * B * c.n_experts) : 0;
     a.part[l] = take(4 * uint64_t(max_parts) * hpg * (c.head_dim + 2));
+    a.opart[l] = is_batched(c) ? 0 : take(4 * uint64_t(c.n_kv_heads) * c.hidden);
   }
   // expert outputs [B][top_k][d] of the layer being computed (one buffer for
   // every layer: its tags carry the layer as well as the step)
@@ -838,7 +861,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
 
   // CUs that take O rows: all, or, with few attention tiles (at most one
   // CU in four), the CUs without one
-  std::vector<int> o_rank(C, 0);
+  std::vector<int> o_rank(C, 0), o_cu_of_rank;
   const bool o_skip_att = int64_t(n_att) * 4 <= C;
   int o_cus = C;
   if (o_skip_att) {
@@ -847,6 +870,24 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     for (int cu = 0; cu < C; cu++)
       if (o_rank[cu] == 0) o_rank[cu] = o_cus++;
   }
+  for (int cu = 0; cu < C; cu++)
+    if (!o_skip_att || o_rank[cu] >= 0) o_cu_of_rank.push_back(cu);
+
+  // Split-K O projection: tile (row block, KV group g) takes the rows of the
+  // block over group g's Kg input columns, so it waits only for that group's
+  // attention; G tiles per row block, one per O CU while they last.
+  const int Kg = hpg * Dh;
+  Geo gk;
+  const bool osplit = o.o_split > 0;
+  if (osplit && (G < 2 || !geo_for_k(Kg, &gk))) {
+    *err = "plan: o_split needs more than one KV group and a GEMV width for heads-per-group * head_dim";
+    return MK_ERR_UNSUPPORTED;
+  }
+  const int o_blocks = osplit ? int(std::max<int64_t>(1, std::min<int64_t>(o_cus / G, d / gk.rpu))) : 0;
+  std::vector<std::vector<uint32_t>> c_oticket(L);
+  if (osplit)
+    for (int l = 0; l < L; l++)
+      for (int rb = 0; rb < o_blocks; rb++) c_oticket[l].push_back(b.new_counter(l * ST_PER_LAYER + ST_O));
 
   for (int l = 0; l < L; l++) {
     const int stg = l * ST_PER_LAYER;
@@ -940,7 +981,51 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
       b.push(att_cu(a), I, std::move(m), 2 * rows * kv_rb);
     }
     // -------------------------------------------------------------- O
-    {
+    if (osplit) {
+      const int64_t N = d / gk.rpu;
+      for (int rb = 0; rb < o_blocks; rb++) {
+        const int64_t i0 = N * rb / o_blocks, i1 = N * (rb + 1) / o_blocks;
+        const int r0 = int(i0 * gk.rpu), r1 = int(i1 * gk.rpu);
+        for (int g = 0; g < G; g++) {
+          const int cu = o_cu_of_rank[(rb * G + g) % o_cus];
+          Instr I = blank();
+          I.op = OP_GEMV;
+          I.epi = EPI_OPART;
+          I.nit = uint8_t(gk.nit);
+          I.rpu = uint8_t(gk.rpu);
+          I.layer = uint16_t(l);
+          I.flags = F_SIGNAL | (l == 0 ? F_RES_EMBED : 0);
+          I.n_items = uint32_t(i1 - i0);
+          I.row0 = uint32_t(r0);
+          I.row_bytes = uint32_t(2 * Kg);
+          I.n_rows = uint32_t(r1 - r0);
+          I.k = uint32_t(Kg);
+          I.seg_ptr[0] = lptr(in.w.wo, l, uint64_t(d) * qd) + 2ull * qd * r0 + 2ull * Kg * g;
+          I.seg_rows[0] = uint32_t(r1 - r0);
+          I.seg_stride[0] = uint32_t(2 * qd);
+          I.aux[1] = uint32_t(g);
+          I.aux[2] = c_oticket[l][rb];
+          I.aux[3] = uint32_t(G);
+          I.aux[4] = 1;
+          I.in_ptr = A + ar.o[l] + uint64_t(kActBytes) * g * Kg;
+          I.out_ptr = A + ar.opart[l] + 4ull * g * d;
+          I.res_ptr = l == 0 ? embed : A + ar.x[l];
+          I.seg_ptr[2] = A + ar.h[l];
+          set_wait(I, 0, c_attn[l]);
+          I.sig_ctr = c_o[l];
+          I.n_pages = uint32_t(ceil_div(int64_t(I.n_rows) * I.row_bytes, kPageBytes));
+          InstrMeta m;
+          m.stage = stg + ST_O;
+          // the block's G tiles share the merged rows of h (written by the
+          // tile that takes the last ticket)
+          m.merge_write = true;
+          m.reads.push_back({BUF_O, l, uint64_t(g) * Kg, uint64_t(g + 1) * Kg});
+          m.reads.push_back({l == 0 ? BUF_EMBED : BUF_X, l, uint64_t(r0), uint64_t(r1)});
+          m.writes.push_back({BUF_H, l, uint64_t(r0), uint64_t(r1)});
+          b.push(cu, I, std::move(m), int64_t(I.n_rows) * I.row_bytes);
+        }
+      }
+    } else {
       const int64_t N = d / gq.rpu;
       for (int cu = 0; cu < C; cu++) {
         int64_t c0, c1;
@@ -1134,15 +1219,18 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
   // producers per counter (per step)
   for (int cu = 0; cu < C; cu++)
     for (const Instr& I : b.q[cu]) {
-      if (I.op == OP_ATTN && I.aux[3] > 1) {
-        // every tile of the group takes a ticket; the last one signals ATTN
-        P->ctr_producers[I.seg_rows[0]]++;
+      uint32_t tc, tn;
+      if (ticketed(I, &tc, &tn)) {
+        // every tile of the set takes a ticket; the last one signals
+        P->ctr_producers[tc]++;
         continue;
       }
       if ((I.flags & F_SIGNAL) && I.sig_ctr != kNoCounter) P->ctr_producers[I.sig_ctr]++;
     }
-  for (int l = 0; l < L; l++)
+  for (int l = 0; l < L; l++) {
     if (nblk > 1) P->ctr_producers[c_attn[l]] = uint32_t(G * tpg);
+    if (osplit) P->ctr_producers[c_o[l]] = uint32_t(o_blocks);
+  }
   // fill wait counts
   for (int cu = 0; cu < C; cu++)
     for (Instr& I : b.q[cu])
@@ -1200,9 +1288,10 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
   // 1. counter producers match signalling instructions; waits use them
   std::vector<uint32_t> sig(NC, 0);
   for (const Instr& I : p.instrs) {
-    if (I.op == OP_ATTN && I.aux[3] > 1) {
-      if (I.seg_rows[0] >= uint32_t(NC)) return fail("attention ticket counter out of range");
-      sig[I.seg_rows[0]]++;
+    uint32_t tc, tn;
+    if (ticketed(I, &tc, &tn)) {
+      if (tc >= uint32_t(NC)) return fail("ticket counter out of range");
+      sig[tc]++;
     } else if ((I.flags & F_SIGNAL) && I.sig_ctr != kNoCounter) {
       if (I.sig_ctr >= uint32_t(NC)) return fail("signal counter out of range");
       sig[I.sig_ctr]++;
@@ -1233,8 +1322,10 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
   // a split attention signals once per head tile: by the tile that takes
   // the last ticket of that head tile's blocks
   std::vector<std::vector<uint32_t>> merged_by(NC);
-  for (const Instr& I : p.instrs)
-    if (I.op == OP_ATTN && I.aux[3] > 1 && I.sig_ctr < uint32_t(NC)) merged_by[I.sig_ctr].push_back(I.seg_rows[0]);
+  for (const Instr& I : p.instrs) {
+    uint32_t tc, tn;
+    if (ticketed(I, &tc, &tn) && I.sig_ctr < uint32_t(NC)) merged_by[I.sig_ctr].push_back(tc);
+  }
   for (int ct = 0; ct < NC; ct++) {
     std::vector<uint32_t>& t = merged_by[ct];
     std::sort(t.begin(), t.end());
@@ -1341,9 +1432,11 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
   std::vector<std::vector<uint32_t>> waits_of(NC);
   for (const Instr& I : p.instrs) {
     uint32_t sc = kNoCounter;
-    if (I.op == OP_ATTN && I.aux[3] > 1) sc = I.sig_ctr;  // the merger waits like every tile
+    uint32_t tc, tn;
+    const bool tk = ticketed(I, &tc, &tn);
+    if (tk) sc = I.sig_ctr;  // the merger waits like every tile
     else if ((I.flags & F_SIGNAL) && I.sig_ctr != kNoCounter) sc = I.sig_ctr;
-    if (I.op == OP_ATTN && I.aux[3] > 1) waits_of[I.seg_rows[0]].push_back(I.wait_ctr[0]);
+    if (tk) waits_of[tc].push_back(I.wait_ctr[0]);
     if (sc == kNoCounter) continue;
     for (int k = 0; k < 2; k++)
       if (I.wait_ctr[k] != kNoCounter) waits_of[sc].push_back(I.wait_ctr[k]);
@@ -1560,7 +1653,20 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
           return fail("GEMV input outside the arena");
         }
         uint64_t out_rows = I.rpu == 2 && I.epi != EPI_SWIGLU ? uint64_t(I.n_items) * 2 : I.n_items;
-        if (I.epi != EPI_ARGMAX && I.epi != EPI_ACC_FIRST && I.epi != EPI_ACC_MID &&
+        if (I.epi == EPI_OPART) {
+          // the layer's partials [G][d] (fp32), the merged rows of h and the
+          // residual rows the merging tile reads
+          const uint64_t pb = I.out_ptr - 4ull * I.aux[1] * d;
+          if (I.aux[3] != uint32_t(c.n_kv_heads) || I.aux[1] >= I.aux[3] || I.row0 + out_rows > d ||
+              !in_arena(pb, pb + 4ull * I.aux[3] * d))
+            return fail("split-K O partials outside the arena");
+          if (!in_arena(I.seg_ptr[2] + 8 * I.row0, I.seg_ptr[2] + 8 * (I.row0 + out_rows)))
+            return fail("split-K O output outside the arena");
+          if ((I.flags & F_RES_EMBED) ? I.res_ptr != uint64_t(in.w.embed)
+                                      : !in_arena(I.res_ptr + 8 * I.row0, I.res_ptr + 8 * (I.row0 + out_rows)))
+            return fail("split-K O residual outside the arena");
+        }
+        if (I.epi != EPI_ARGMAX && I.epi != EPI_ACC_FIRST && I.epi != EPI_ACC_MID && I.epi != EPI_OPART &&
             !in_arena(I.out_ptr + uint64_t(kActBytes) * I.row0, I.out_ptr + uint64_t(kActBytes) * (I.row0 + out_rows)))
           return fail("GEMV output outside the arena");
         if ((I.epi == EPI_RESID || I.epi == EPI_ACC_ONLY || I.epi == EPI_ACC_FIRST) &&
@@ -1608,8 +1714,9 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         for (int k = 0; k < 2; k++)
           if (I.wait_ctr[k] != kNoCounter && val[I.wait_ctr[k]] < I.wait_cnt[k]) ready = false;
         if (!ready) continue;
-        if (I.op == OP_ATTN && I.aux[3] > 1) {
-          if (++ticket[I.seg_rows[0]] == I.aux[3]) val[I.sig_ctr]++;
+        uint32_t tc, tn;
+        if (ticketed(I, &tc, &tn)) {
+          if (++ticket[tc] == tn) val[I.sig_ctr]++;
         } else if ((I.flags & F_SIGNAL) && I.sig_ctr != kNoCounter) {
           val[I.sig_ctr]++;
         }

@@ -21,6 +21,7 @@ namespace mk {
 struct ArenaLayout {
   uint64_t x[129];        // residual stream entering layer l (x[0] unused: embedding)
   uint64_t qkv[128], o[128], h[128], m[128], part[128];
+  uint64_t opart[128];    // [G][d] fp32 split-K O partials (one-sequence decoder)
   uint64_t rl[128];       // router logits (mixture-of-experts decoder)
   uint64_t y;             // [B][top_k][d] tagged expert outputs (mixture-of-experts decoder)
   uint64_t tok;           // [B] tagged greedy token of the last step

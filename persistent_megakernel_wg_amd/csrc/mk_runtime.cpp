@@ -111,8 +111,10 @@ int variant_for(const mk_config& cfg, const mk_plan_opts& o) {
   if (mk::is_batched(cfg)) return o.generic_kernel ? 0 : mk_pick_batched(o.attn_heads, cfg.head_dim);
   if (o.generic_kernel) return 0;
   int nd, rd, nq, rq, nf, rf;
+  // the O projection's input: the whole attention output, or one KV group's
+  const int oq = o.o_split > 0 ? cfg.n_q_heads / cfg.n_kv_heads * cfg.head_dim : cfg.n_q_heads * cfg.head_dim;
   if (!mk::gemv_geometry(cfg.hidden, &nd, &rd) ||
-      !mk::gemv_geometry(cfg.n_q_heads * cfg.head_dim, &nq, &rq) ||
+      !mk::gemv_geometry(oq, &nq, &rq) ||
       !mk::gemv_geometry(cfg.ffn / o.mlp_chunks, &nf, &rf))
     return 0;
   return mk_pick_variant(nd, rd, nq, rq, nf, rf, o.attn_heads, cfg.head_dim);

@@ -125,6 +125,18 @@ def test_tiny_step_head_layouts(need_gpu, heads):
     _one_step_case(s, attn_heads=h // g, attn_block=64)
 
 
+@pytest.mark.parametrize("n_cus", [1, 3, 256])
+def test_tiny_split_k_o_projection(need_gpu, n_cus):
+    # O tiles per (row block, KV group), each waiting only for its group's
+    # attention; the block's last ticket adds x and the partials in group
+    # order (the first layer's residual is the embedding row); and the
+    # whole-row O tiles of the same shape
+    s = synth.SHAPES["tiny"].replace(n_q_heads=8)
+    _one_step_case(s, n_cus=n_cus, o_split=1)
+    _one_step_case(s, n_cus=n_cus, o_split=-1)
+    _one_step_case(s.replace(head_dim=128, n_q_heads=4), n_cus=n_cus, o_split=1, attn_block=64)
+
+
 def test_tiny_step_one_cu(need_gpu):
     # the whole decoder on one workgroup: split residual tiles, long queue
     _one_step_case(synth.SHAPES["tiny"], n_cus=1)

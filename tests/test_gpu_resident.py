@@ -74,6 +74,13 @@ def test_resident_tiny_to_the_last_position(need_gpu):
     _resident_case(s.replace(prefill=s.max_seq - 5), 5, attn_block=64)
 
 
+def test_resident_split_k_o_projection(need_gpu):
+    # the O row blocks' tickets and partials are reused by every step
+    s = synth.SHAPES["tiny"].replace(n_q_heads=8)
+    _resident_case(s, 6, o_split=1)
+    _resident_case(s, 4, o_split=1, n_cus=3)
+
+
 def test_resident_moe_tiny(need_gpu):
     _resident_case(synth.SHAPES["moe_tiny"], 3)
 

@@ -64,6 +64,28 @@ def test_plan_variants_verify(name, n_cus, opts):
     B.mk_plan_check(_cfg(name), n_cus, B.plan_opts(**opts))
 
 
+@pytest.mark.parametrize("name,kw,n_cus", [
+    ("tiny", {"n_q_heads": 8}, 1), ("tiny", {"n_q_heads": 8}, 3), ("tiny", {"n_q_heads": 8}, 256),
+    ("tiny", {"head_dim": 128}, 5), ("llama1b_ctx128", {}, 256), ("llama1b_ctx128", {}, 17),
+    ("llama1b_ctx8192", {}, 256), ("llama8b_ctx2048", {}, 256),
+])
+def test_split_k_o_projection_plans_verify(name, kw, n_cus):
+    # O tiles per (row block, KV group), the block's last ticket merging x and
+    # the group partials; against whole-row O tiles of the same shape
+    split, rep = B.mk_plan_check(_cfg(name, **kw), n_cus, B.plan_opts(o_split=1))
+    whole, _ = B.mk_plan_check(_cfg(name, **kw), n_cus, B.plan_opts(o_split=-1))
+    assert split["weight_bytes"] == whole["weight_bytes"]
+
+
+@pytest.mark.parametrize("kw", [{}, {"n_kv_heads": 1, "n_q_heads": 8}])
+def test_split_k_o_projection_needs_groups_and_a_gemv_width(kw):
+    # tiny: two groups of 2 x 64 = 128 inputs (no GEMV path for K = 128); one
+    # KV group: nothing to split
+    with pytest.raises(B.MkError) as e:
+        B.mk_plan_check(_cfg("tiny", **kw), 64, B.plan_opts(o_split=1))
+    assert e.value.status == -4
+
+
 def test_verifier_rejects_a_wrong_counter_target():
     with pytest.raises(B.MkError) as e:
         B.mk_plan_check(_cfg("tiny"), 64, B.plan_opts(debug_corrupt_target=1))
