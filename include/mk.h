@@ -138,6 +138,11 @@ typedef struct {
                          the MoE decoder always).  The split needs more than
                          one KV group and heads-per-group * head_dim of 256
                          or a multiple of 512 */
+  int32_t mfma;       /* batched decoder: 1 = the LM head on matrix cores
+                         (v_mfma_f32_16x16x32_bf16 tiles of 16 rows; the fp32
+                         input split into bf16 high and low parts, fp32
+                         accumulation), run by a kernel variant of its own;
+                         -1 = on the vector ALUs (default).  Batch 1: always -1 */
 } mk_plan_opts;
 
 /* Plan summary (filled by mk_plan_info / mk_plan_check). */

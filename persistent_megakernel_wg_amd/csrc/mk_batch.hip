@@ -652,6 +652,143 @@ DEV bool bgemv(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
   return true;
 }
 
+// ---------------------------------------------- matrix-core batched GEMV
+// F_MFMA tiles: items are blocks of 16 rows, streamed in fragment order (one
+// 1 KiB unit per 32 columns); the B operand is the staged input, the B
+// sequences' bf16 high parts in columns 0 .. 7 and their low parts in 8 .. 15,
+// so that one v_mfma_f32_16x16x32_bf16 applies 32 columns of 16 rows to both.
+// Every compute wave takes the column steps w, w + 6, ... of each block (all
+// waves walk the same pages), adds its high and low columns, and leaves its
+// [16 rows][8 sequences] partial in LDS; the wave that arrives last at a
+// block adds the six partials in wave order and runs the epilogue.  mblk
+// counts the blocks of all such instructions so far (every wave alike).
+// The staged input (g * x, fp32 [B][K]) rewritten in the B operand order of
+// the matrix-core GEMV: column step k / 32, lane 16 ((k % 32) / 8) + b for the
+// bf16 high part of x_b[k] and lane 16 ((k % 32) / 8) + 8 + b for the low part
+// (the rounding residue, so that high + low carries 16 significant bits),
+// value k % 8 of the lane's 8.  Each wave reads its values, all waves meet,
+// then write; one more meeting publishes the slot.
+DEV bool mfma_order(Comp& c, InstrCP I) {
+  constexpr int NC = (lb::kXFloats / 128 + kNComp - 1) / kNComp;
+  const uint32_t lane = c.lane, K = I->k, nch = uint32_t(c.a->batch) * K / 128;
+  const float* xs = reinterpret_cast<const float*>(lds + lb::kX);
+  float2 v[NC];
+#pragma unroll
+  for (int qq = 0; qq < NC; qq++) {
+    const uint32_t ch = uint32_t(c.w) + kNComp * qq;
+    if (ch < nch) v[qq] = *reinterpret_cast<const float2*>(xs + ch * 128 + 2 * lane);
+  }
+  if (!comp_barrier()) return false;
+#pragma unroll
+  for (int qq = 0; qq < NC; qq++) {
+    const uint32_t ch = uint32_t(c.w) + kNComp * qq;
+    if (ch >= nch) continue;
+    const uint32_t flat = ch * 128 + 2 * lane, b = flat / K, k = flat % K;
+    const uint32_t h0 = f2bf(v[qq].x), h1 = f2bf(v[qq].y);
+    const uint32_t l0 = f2bf(v[qq].x - __uint_as_float(h0 << 16)), l1 = f2bf(v[qq].y - __uint_as_float(h1 << 16));
+    char* xb = lds + lb::kX + (k / 32) * 1024 + ((k % 32) / 8) * 256 + (k % 8) * 2;
+    *reinterpret_cast<uint32_t*>(xb + b * 16) = h0 | h1 << 16;
+    *reinterpret_cast<uint32_t*>(xb + (8 + b) * 16) = l0 | l1 << 16;
+  }
+  return comp_barrier();
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+DEV bool bgemv_mfma(Comp& c, InstrCP I, uint32_t i, uint32_t pg, uint32_t& mblk) {
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane, nB = uint32_t(a.batch), ks = I->k / 32;
+  const uint32_t epi = i_epi(I), n_rows = I->n_rows, n_blocks = I->n_items, row0 = I->row0;
+  const uint32_t ostride = I->aux[0];
+  const uint32_t n = lane & 15, q = lane >> 4;  // output column, row quad
+  const bool live_col = (n & 7) < nB;
+  const float inv = inv_rms(a, I);
+  const float my_inv = __shfl(inv, int(n & 7), 64);
+  const char* xb = lds + lb::kX;
+  f4* part = reinterpret_cast<f4*>(lds + lb::kMfma);
+  uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
+  const float* res = res_slot_b(i);
+  ArgBest best{-__builtin_inff(), 0xFFFFFFFFu};
+  for (uint32_t blk = 0; blk < n_blocks; blk++, mblk++) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (uint32_t st = uint32_t(c.w); st < ks; st += kNComp) {
+      const uint32_t u = blk * ks + st;
+      if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + u / kUnitsPerPage);
+      if (!wait_page(pg + u / kUnitsPerPage, c.fcache)) return false;
+      const bf16x8 A = *reinterpret_cast<const bf16x8*>(lds + page_off<LayB>(pg + u / kUnitsPerPage) +
+                                                       (u % kUnitsPerPage) * kUnit + lane * 16);
+      bf16x8 B = *reinterpret_cast<const bf16x8*>(xb + st * 1024 + lane * 16);
+      if (!live_col) B = bf16x8{};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
+    }
+    // lane (q, n < 8): rows 4 q .. 4 q + 3 of sequence n, high + low parts
+    f4 v;
+    v.x = acc[0] + __shfl_down(acc[0], 8, 64);
+    v.y = acc[1] + __shfl_down(acc[1], 8, 64);
+    v.z = acc[2] + __shfl_down(acc[2], 8, 64);
+    v.w = acc[3] + __shfl_down(acc[3], 8, 64);
+    // the partial slots are free once the previous block has been reduced
+    if (!wait_lds_ge(C_MRED, mblk)) return false;
+    if (n < 8) part[c.w * 32 + q * 8 + n] = v;
+    uint32_t prev = 0;
+    if (lane == 0) prev = lds_add(C_MARR, 1);
+    prev = uni(prev);
+    if (prev + 1 != uint32_t(kNComp) * (mblk + 1)) continue;
+    // last to arrive: the block's sums, the six partials in wave order
+    if (n < 8) {
+      f4 t = part[q * 8 + n];
+#pragma unroll
+      for (int w2 = 1; w2 < kNComp; w2++) {
+        const f4 p2 = part[w2 * 32 + q * 8 + n];
+        t.x += p2.x;
+        t.y += p2.y;
+        t.z += p2.z;
+        t.w += p2.w;
+      }
+      const float tv[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const uint32_t rl = blk * 16 + q * 4 + uint32_t(r);
+        if (rl >= n_rows || n >= nB) continue;
+        const float sv = tv[r] * my_inv;
+        const uint32_t row = row0 + rl;
+        switch (epi) {
+          case EPI_STORE:
+            st_tag(out + size_t(n) * ostride + row, sv, c.ep);
+            break;
+          case EPI_RESID:
+            st_tag(out + size_t(n) * ostride + row, res[n * n_rows + rl] + sv, c.ep);
+            break;
+          default:  // EPI_ARGMAX
+            if (a.logits) gp(a.logits)[size_t(n) * a.vocab + row] = sv;
+            if (sv != sv) __hip_atomic_store(gp(a.status) + ST_NAN, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            arg_update(best, sv, row);
+            break;
+        }
+      }
+    }
+    if (lane == 0) lds_st(C_MRED, mblk + 1);
+  }
+  if (epi == EPI_ARGMAX) {
+    // lanes n, n + 16, n + 32, n + 48 hold sequence n's best of their rows
+#pragma unroll
+    for (int m = 16; m < 64; m <<= 1) {
+      const float ov = __shfl_xor(best.v, m, 64);
+      const uint32_t oi = __shfl_xor(best.i, m, 64);
+      arg_update(best, ov, oi);
+    }
+    if (lane < 8) {
+      *lw(lb::kArg + (c.w * 8 + int(lane)) * 8) = __float_as_uint(best.v);
+      *lw(lb::kArg + (c.w * 8 + int(lane)) * 8 + 4) = best.i;
+    }
+  }
+  if (lane == 0) {
+    lds_st(C_RELEASED + 4 * c.w, pg + I->n_pages);
+    lds_st(C_XCONS + 4 * c.w, i + 1);
+  }
+  return true;
+}
+
 // ------------------------------------------------------ expert gate / up
 // Items are (selected expert, pair of the CU's slice) in expert order; the
 // loader lays each pair out as its gate row then its up row.  An item applies
@@ -951,13 +1088,16 @@ DEV void lm_finish_b(Comp& c, InstrCP I) {
 // ---------------------------------------------------------------- variants
 // GeoB: attention tile shape (query heads per tile, head dimension) compiled
 // for one shape; GeoBAny dispatches it per instruction.
-template <int H, int D>
+// MF: the kernel also runs matrix-core GEMV tiles (F_MFMA); compiled into a
+// variant of its own, so that the other variants keep their register
+// allocation.
+template <int H, int D, bool MF>
 struct GeoB {
-  static constexpr bool any = false;
+  static constexpr bool any = false, mf = MF;
   static constexpr int hpt = H, dh = D;
 };
 struct GeoBAny {
-  static constexpr bool any = true;
+  static constexpr bool any = true, mf = true;
 };
 
 template <class G>
@@ -1012,6 +1152,8 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
   uint32_t staged = kNoCounter;
   // the last instruction at which the compute waves synchronised
   uint32_t last_sync = 0;
+  // matrix-core GEMV blocks of the launch so far
+  uint32_t mblk = 0;
   uint32_t seen_ctr = kNoCounter, seen_val = 0;
   uint32_t pg = 0;
   for (uint32_t i = 0; i < n; i++) {
@@ -1082,10 +1224,10 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
     if (i_flags(I) & F_DIRECT) np = 0;
     bool ok = true;
     if (op == OP_BGEMV || op == OP_EGU) {
-      const uint32_t fl = i_flags(I) & (F_IN_EMBED | F_NORM);
+      const uint32_t fl = i_flags(I) & (F_IN_EMBED | F_NORM | F_MFMA);
       InstrCP S = q + (staged == kNoCounter ? i : staged);
       const bool reuse = staged != kNoCounter && I->in_ptr == S->in_ptr &&
-                         fl == (i_flags(S) & (F_IN_EMBED | F_NORM)) && I->k == S->k &&
+                         fl == (i_flags(S) & (F_IN_EMBED | F_NORM | F_MFMA)) && I->k == S->k &&
                          (!(fl & F_NORM) || I->gain_ptr == S->gain_ptr);
       const bool res = op == OP_BGEMV && i_epi(I) == EPI_RESID;
       if (!reuse || res) {
@@ -1094,6 +1236,9 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
           return;
         }
         if (!comp_barrier()) return;
+        if constexpr (G::mf) {
+          if ((i_flags(I) & F_MFMA) && !reuse && !mfma_order(c, I)) return;
+        }
         last_sync = i;
       } else if (!done_slot_free(i, last_sync)) {
         if (c.lane == 0) lds_st(C_ABORT, 1);
@@ -1105,7 +1250,11 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       }
       if (!reuse) staged = i;
       if (op == OP_BGEMV) {
-        ok = bgemv(c, I, i, pg);
+        if constexpr (G::mf) {
+          ok = (i_flags(I) & F_MFMA) ? bgemv_mfma(c, I, i, pg, mblk) : bgemv(c, I, i, pg);
+        } else {
+          ok = bgemv(c, I, i, pg);
+        }
       } else if (i_flags(I) & F_DIRECT) {
         const uint32_t nit = i_nit(I);
         ok = nit == 4 ? egu_direct<4>(c, I, i) : nit == 2 ? egu_direct<2>(c, I, i) : egu_direct<1>(c, I, i);
@@ -1179,20 +1328,23 @@ __global__ __launch_bounds__(kThreads, 1) void mk_megakernel_b(KArgs a) {
 namespace {
 struct BVariant {
   int hpt, dh;  // 0 = generic
+  bool mf;      // runs matrix-core GEMV tiles
   const void* fn;
 };
 const BVariant kBVariants[] = {
-    {0, 0, reinterpret_cast<const void*>(&mk::mk_megakernel_b<mk::GeoBAny>)},
-    {4, 128, reinterpret_cast<const void*>(&mk::mk_megakernel_b<mk::GeoB<4, 128>>)},
+    {0, 0, true, reinterpret_cast<const void*>(&mk::mk_megakernel_b<mk::GeoBAny>)},
+    {4, 128, false, reinterpret_cast<const void*>(&mk::mk_megakernel_b<mk::GeoB<4, 128, false>>)},
+    {4, 128, true, reinterpret_cast<const void*>(&mk::mk_megakernel_b<mk::GeoB<4, 128, true>>)},
 };
 constexpr int kNumBVariants = sizeof(kBVariants) / sizeof(kBVariants[0]);
 bool g_battr_set[kNumBVariants] = {};
 }  // namespace
 
-// Index of the batched kernel built for this attention tile shape, or 0.
-extern "C" int mk_pick_batched(int hpt, int dh) {
+// Index of the batched kernel built for this attention tile shape (with or
+// without matrix-core GEMV tiles), or 0.
+extern "C" int mk_pick_batched(int hpt, int dh, int mfma) {
   for (int v = 1; v < kNumBVariants; v++)
-    if (kBVariants[v].hpt == hpt && kBVariants[v].dh == dh) return v;
+    if (kBVariants[v].hpt == hpt && kBVariants[v].dh == dh && kBVariants[v].mf == (mfma != 0)) return v;
   return 0;
 }
 

@@ -53,6 +53,8 @@ enum : int {
   C_RELEASED = 16,     // [kNComp] pages below this index are done, per wave
   C_XOK = 64,          // instructions whose inputs are staged (leader staging)
   C_DEPOK = 68,        // instructions whose counter waits are satisfied
+  C_MARR = 72,         // matrix-core GEMV: wave arrivals at block ends (all blocks)
+  C_MRED = 76,         // matrix-core GEMV: blocks reduced so far
   C_XCONS = 96,        // [kNComp] instructions whose staged inputs each wave read
   C_DONE = 128,        // [kDoneRing] waves finished, per instruction slot
   C_ABORT = 160,
@@ -559,7 +561,9 @@ struct LoadView {
 DEV void load_view(const KArgs& a, InstrCP I, LoadView& L, int32_t pos) {
   L.op = i_op(I);
   L.deep = (L.op == OP_GEMV || L.op == OP_BGEMV) && i_epi(I) == EPI_ARGMAX;
-  L.stream_units = (I->n_rows * I->row_bytes + kUnit - 1) / kUnit;
+  // packed rows (matrix-core tiles: whole blocks of 16 rows, zero-padded)
+  const uint32_t rows = (i_flags(I) & F_MFMA) ? 16 * I->n_items : I->n_rows;
+  L.stream_units = (rows * I->row_bytes + kUnit - 1) / kUnit;
   L.src = I->src_ptr;
   L.kp = I->aux[4];
   L.valid_bytes = 0;

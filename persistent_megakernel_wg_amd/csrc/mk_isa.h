@@ -58,10 +58,11 @@ constexpr int kMaxB = 8;             // sequences per step
 constexpr int kPages = 5;
 constexpr int kSS = 512;             // sum of squares per 128-value chunk [128]
 constexpr int kArg = 1024;           // argmax per compute wave and sequence [kNComp][kMaxB][2]
-constexpr int kDots = 1536;          // expert down-projection dots [kMaxB][8 slots][16 rows]
+constexpr int kMfma = 1536;          // matrix-core GEMV: each compute wave's partial block sums
+constexpr int kMfmaWaveBytes = 512;  // [16 rows][8 sequences] fp32 per wave
 constexpr int kMaxDnRows = 16;
 constexpr int kMaxTopK = 8;
-constexpr int kRoute = kDots + 4 * kMaxB * kMaxTopK * kMaxDnRows;   // 5632: routing tables
+constexpr int kRoute = kMfma + 4 * kMaxB * kMaxTopK * kMaxDnRows;   // 5632: routing tables
 constexpr int kRouteBytes = 1280;    // one table per layer parity
 constexpr int kRes = kRoute + 2 * kRouteBytes;                      // 8192: residual rows
 constexpr int kX = kRes + 2 * 4 * kMaxResRows;                      // 9216
@@ -113,6 +114,9 @@ enum Flag : uint16_t {
                       // themselves; the instruction takes no LDS pages
   F_DEBUG_STALL = 256,  // tests only: staging expects the next step's tag, so the
                         // inputs never turn fresh and the watchdog ends the step
+  F_MFMA = 512,         // (batched GEMV) matrix-core tiles of 16 rows: the input
+                        // is staged as bf16 hi + lo parts in MFMA operand order
+                        // and the packed rows are in MFMA fragment order
 };
 
 constexpr uint32_t kNoCounter = 0xFFFFFFFFu;
@@ -158,8 +162,15 @@ struct PackCopy {
   uint32_t rows;
   uint32_t row_bytes;  // multiple of 16
   uint32_t src_stride; // bytes between source rows
-  uint32_t dst_stride; // bytes between packed rows
+  uint32_t dst_stride; // bytes between packed rows (0 with frag)
+  uint32_t frag;       // 1: MFMA fragment order for blocks of 16 rows (below)
+  uint32_t pad;
 };
+// MFMA fragment order (F_MFMA tiles, v_mfma_f32_16x16x32_bf16): rows go in
+// blocks of 16, each block's K columns in steps of 32; step s of block b is
+// one 1 KiB unit at (b * K / 32 + s) KiB, in which lane l's 16 bytes are the
+// 8 values of row 16 b + (l % 16) at columns 32 s + 8 (l / 16) .. + 7, the A
+// operand of that lane.  A block's rows past the copy are zero.
 
 // Attention instruction aux fields
 //   aux[0] = kv group g         aux[1] = block index b

@@ -802,7 +802,10 @@ __global__ void __launch_bounds__(256) mk_pack_kernel(const PackCopy* copies, ui
          t += uint64_t(blockDim.x) * gridDim.y) {
       const uint64_t r = t / per_row, k = t - r * per_row;
       const u4 v = *reinterpret_cast<const u4*>(cp.src + r * cp.src_stride + k * 16);
-      *reinterpret_cast<u4*>(base + cp.dst + r * cp.dst_stride + k * 16) = v;
+      // fragment order: block r / 16, column step k / 4, lane (k % 4) * 16 + r % 16
+      const uint64_t o = cp.frag ? (r / 16) * 16 * cp.row_bytes + (k / 4) * 1024 + ((k % 4) * 16 + r % 16) * 16
+                                 : r * cp.dst_stride + k * 16;
+      *reinterpret_cast<u4*>(base + cp.dst + o) = v;
     }
   }
 }

@@ -211,6 +211,9 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
     // experts are split over the CUs by rows; the MLP chunk option is unused
     if (r.mlp_chunks <= 0) r.mlp_chunks = 1;
     r.o_split = -1;
+    // vector-ALU GEMVs by default: the matrix-core LM head measured a few us
+    // faster, but the kernel variant that carries it loses more elsewhere
+    if (r.mfma == 0) r.mfma = -1;
     if (r.attn_block <= 0) {
       // K and V blocks of a tile in four of the five ring pages, scores in
       // the scratch, whole KV groups per tile
@@ -264,6 +267,8 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
   // whole O rows by default: on MI355X the split's ticket and cross-CU merge
   // cost more than the spread of the attention tiles it lets O overlap
   if (r.o_split == 0) r.o_split = -1;
+  // batch 1: no matrix-core tiles (the GEMVs are a single column)
+  r.mfma = -1;
   if (r.watchdog_ms <= 0) r.watchdog_ms = 2000;
   return r;
 }
@@ -404,6 +409,15 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
   };
   auto per_seq = [&](std::vector<Range>& v, int buf, int layer, uint64_t stride, uint64_t lo, uint64_t hi) {
     for (int s = 0; s < B; s++) v.push_back({buf, layer, s * stride + lo, s * stride + hi});
+  };
+  // matrix-core tiles for the LM head: items are blocks of 16 rows, streamed
+  // in fragment order (its input is not shared with other instructions; the
+  // O projection's 8 rows per CU would stream a half-empty block)
+  const bool mfma = o.mfma > 0;
+  auto to_mfma = [&](Instr& I) {
+    I.flags |= F_MFMA;
+    I.n_items = uint32_t(ceil_div(int64_t(I.n_rows), 16));
+    I.n_pages = uint32_t(ceil_div(int64_t(I.n_items) * 16 * I.row_bytes, kPageBytes));
   };
   // attention tile -> CU: spread evenly
   const int n_att = B * G * tpg * nblk;
@@ -699,6 +713,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
       I.gain_ptr = uint64_t(in.w.final_norm);
       I.wait_ctr[0] = c_dn[L - 1];
       I.sig_ctr = c_lm;
+      if (mfma) to_mfma(I);
       InstrMeta m;
       m.stage = L * ST_PER_LAYER;
       m.merge_write = false;
@@ -741,13 +756,19 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
     uint64_t row = 0;
     for (uint32_t sg = 0; sg < I.aux[4]; sg++) {
       if (!I.seg_rows[sg]) continue;
-      PackCopy cp;
+      PackCopy cp{};
       cp.src = I.seg_ptr[sg];
       cp.rows = I.seg_rows[sg];
       cp.row_bytes = I.row_bytes;
       cp.src_stride = I.seg_stride[sg];
-      cp.dst = pack + row * I.row_bytes;
-      cp.dst_stride = I.row_bytes;
+      if (I.flags & F_MFMA) {
+        // one segment, in fragment order from the start of the run
+        cp.dst = pack;
+        cp.frag = 1;
+      } else {
+        cp.dst = pack + row * I.row_bytes;
+        cp.dst_stride = I.row_bytes;
+      }
       row += cp.rows;
       P->pack.push_back(cp);
     }
@@ -1253,7 +1274,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     uint64_t row = 0;
     for (uint32_t sg = 0; sg < I.aux[4]; sg++) {
       if (!I.seg_rows[sg]) continue;
-      PackCopy cp;
+      PackCopy cp{};
       cp.src = I.seg_ptr[sg];
       cp.rows = I.seg_rows[sg];
       cp.row_bytes = I.row_bytes;
@@ -1352,11 +1373,19 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         if (!p.batched) return fail("batched GEMV in a one-sequence plan");
         if (I.k % 512 || I.nit != I.k / 512 || I.row_bytes != 2 * I.k) return fail("batched row geometry");
         if (uint64_t(I.k) * c.batch > uint64_t(lb::kXFloats)) return fail("batched input exceeds the x slot");
-        if (uint64_t(I.n_pages) * kPageBytes < uint64_t(2) * I.n_items * I.row_bytes)
-          return fail("page budget smaller than the tile");
-        if (I.n_items != (I.n_rows + 1) / 2) return fail("row pairs");
-        if (uint32_t(ceil_div(2 * I.row_bytes, kPageBytes)) + 1 > uint32_t(lb::kPages))
-          return fail("an item spans more pages than the ring holds");
+        if (I.flags & F_MFMA) {
+          // blocks of 16 rows in fragment order, consumed one 1 KiB column
+          // step at a time by all compute waves
+          if (I.aux[4] != 1 || I.n_items != uint32_t(ceil_div(I.n_rows, 16)) ||
+              uint64_t(I.n_pages) * kPageBytes < uint64_t(16) * I.n_items * I.row_bytes)
+            return fail("matrix-core tile geometry");
+        } else {
+          if (uint64_t(I.n_pages) * kPageBytes < uint64_t(2) * I.n_items * I.row_bytes)
+            return fail("page budget smaller than the tile");
+          if (I.n_items != (I.n_rows + 1) / 2) return fail("row pairs");
+          if (uint32_t(ceil_div(2 * I.row_bytes, kPageBytes)) + 1 > uint32_t(lb::kPages))
+            return fail("an item spans more pages than the ring holds");
+        }
         uint32_t srows = 0;
         for (uint32_t sg = 0; sg < I.aux[4]; sg++) srows += I.seg_rows[sg];
         if (srows != I.n_rows) return fail("segments do not cover the stream rows");
@@ -1571,8 +1600,9 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         return fail("packed copy not in 16-byte units");
       if (!inside(cp.src, cp.src + uint64_t(cp.rows - 1) * cp.src_stride + cp.row_bytes))
         return fail("packed copy reads outside every weight tensor");
-      if (cp.dst + uint64_t(cp.rows - 1) * cp.dst_stride + cp.row_bytes > p.pack_bytes)
-        return fail("packed copy writes outside the packed stream");
+      const uint64_t span = cp.frag ? uint64_t(ceil_div(cp.rows, 16)) * 16 * cp.row_bytes
+                                    : uint64_t(cp.rows - 1) * cp.dst_stride + cp.row_bytes;
+      if (cp.dst + span > p.pack_bytes) return fail("packed copy writes outside the packed stream");
       copied += uint64_t(cp.rows) * cp.row_bytes;
     }
     if (copied != stream_bytes) return fail("packed copies do not cover the weight streams");

@@ -17,7 +17,7 @@ extern "C" hipError_t mk_launch_megakernel(const mk::KArgs* args, int n_cus, hip
 extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpt, int dh);
 extern "C" hipError_t mk_launch_batched(const mk::KArgs* args, int n_cus, hipStream_t stream, int cooperative,
                                         int variant);
-extern "C" int mk_pick_batched(int hpt, int dh);
+extern "C" int mk_pick_batched(int hpt, int dh, int mfma);
 extern "C" hipError_t mk_launch_pack(const mk::PackCopy* copies, uint32_t n, void* base,
                                      hipStream_t stream);
 extern "C" hipError_t mk_scratch_init(int device, void** out);
@@ -108,7 +108,7 @@ void rope_tables(const mk_config& cfg, std::vector<float>* cs, std::vector<float
 
 // The shape-specific kernel for this plan, or 0 (the generic kernel).
 int variant_for(const mk_config& cfg, const mk_plan_opts& o) {
-  if (mk::is_batched(cfg)) return o.generic_kernel ? 0 : mk_pick_batched(o.attn_heads, cfg.head_dim);
+  if (mk::is_batched(cfg)) return o.generic_kernel ? 0 : mk_pick_batched(o.attn_heads, cfg.head_dim, o.mfma > 0);
   if (o.generic_kernel) return 0;
   int nd, rd, nq, rq, nf, rf;
   // the O projection's input: the whole attention output, or one KV group's

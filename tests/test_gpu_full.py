@@ -179,3 +179,39 @@ def test_moe_b8_ctx2048_4_steps_all_sequences(need_gpu):
     for got, r in ((kg, k_ref), (vg, v_ref)):
         assert kv_rows_close(got[:, :, :, span], r[:, :, :, span])
         assert np.array_equal(got[:, :, :, :s.prefill], r[:, :, :, :s.prefill])
+
+
+@pytest.mark.timeout(900)
+def test_moe_b8_ctx2048_matrix_core_lm_head(need_gpu):
+    """The batch-8 MoE shape with the LM head on matrix cores (plan option
+    mfma=1): one step, sequences 0 and 7 against the oracle, and every
+    sequence's token equal to the vector-ALU plan's on the same inputs."""
+    from persistent_megakernel_wg_amd import binding as B
+    from persistent_megakernel_wg_amd.engine import Engine
+    s = synth.SHAPES["moe_b8_ctx2048"]
+    print("case %s: one step, LM head on matrix cores" % s.name, flush=True)
+    w = synth.make_weights(s)
+    kc, vc = synth.make_kv_cache(s)
+    tok = synth.make_tokens(s)
+    out = {}
+    for m in (1, -1):
+        eng = Engine(s, w, kc, vc, plan=B.plan_opts(mfma=m))
+        try:
+            out[m] = eng.step(tok, s.prefill)
+        finally:
+            eng.close()
+    print("  device steps done", flush=True)
+    orc = DecoderOracle(s, w, keep_f64=False)
+
+    def run_seq(b):
+        k_ref, v_ref = kc.copy(), vc.copy()
+        lg, nx = orc.step(tok, s.prefill, k_ref, v_ref, seqs=[b])
+        return lg[b].copy(), int(nx[b])
+
+    with cf.ThreadPoolExecutor(max_workers=2) as ex:
+        ref = dict(zip((0, 7), ex.map(run_seq, (0, 7))))
+    lg, nx = out[1]
+    for b, (ref_lg, ref_nx) in ref.items():
+        _check_logits("seq %d token %d / oracle %d" % (b, nx[b], ref_nx), lg[b], ref_lg)
+        assert nx[b] == ref_nx, b
+    assert np.array_equal(out[1][1], out[-1][1])

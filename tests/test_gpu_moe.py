@@ -100,6 +100,15 @@ def test_moe_tiny_position_zero_and_last(need_gpu):
     _moe_case(TINY, pos=TINY.max_seq - 1, attn_block=64)
 
 
+@pytest.mark.parametrize("kw,opts", [({}, {}), ({"batch": 3}, {}), ({"batch": 1}, {}),
+                                     ({}, {"n_cus": 1, "attn_block": 64}), ({}, {"n_cus": 37})])
+def test_moe_tiny_matrix_core_lm_head(need_gpu, kw, opts):
+    # the LM head as v_mfma_f32_16x16x32_bf16 tiles of 16 rows (the input as
+    # bf16 high + low parts, fp32 accumulation): padded row blocks, ragged
+    # batches, one CU (16 blocks through one workgroup) and odd CU counts
+    _moe_case(TINY.replace(**kw), mfma=1, **opts)
+
+
 def test_moe_tiny_greedy_chain_on_device(need_gpu):
     from persistent_megakernel_wg_amd.engine import Engine
     s = TINY

@@ -172,6 +172,18 @@ def test_moe_plan_for_the_large_shape_on_fewer_cus():
     B.mk_plan_check(_cfg("moe_b8_ctx2048"), 80)
 
 
+@pytest.mark.parametrize("name,kw,n_cus", [
+    ("moe_tiny", {}, 256), ("moe_tiny", {}, 1), ("moe_tiny", {"batch": 3}, 37), ("moe_b8_ctx2048", {}, 256),
+])
+def test_moe_matrix_core_lm_head_plans_verify(name, kw, n_cus):
+    # LM-head tiles of 16 rows in MFMA fragment order (same bytes streamed,
+    # rows padded to whole blocks), run by the kernel variant that has them
+    mf, _ = B.mk_plan_check(_cfg(name, **kw), n_cus, B.plan_opts(mfma=1))
+    vec, _ = B.mk_plan_check(_cfg(name, **kw), n_cus, B.plan_opts(mfma=-1))
+    assert mf["weight_bytes"] == vec["weight_bytes"]
+    assert mf["kernel_variant"] == 2 and vec["kernel_variant"] == 1
+
+
 @pytest.mark.parametrize("kw", [
     {"top_k": 9, "n_experts": 16}, {"top_k": 4, "n_experts": 3}, {"batch": 9},
     {"expert_ffn": 768}, {"hidden": 4096, "n_q_heads": 32}, {"n_experts": 65},
