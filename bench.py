@@ -182,6 +182,8 @@ def main() -> int:
     ap.add_argument("--mlp-chunks", type=int, default=0)
     ap.add_argument("--mfma", type=int, default=0,
                     help="batched decoder: 1: LM head on matrix cores; -1: vector ALUs; 0: default")
+    ap.add_argument("--edn-queue", type=int, default=0,
+                    help="MoE decoder: q > 1: a 1/q share of the expert down-projection units in a ready queue")
     ap.add_argument("--o-split", type=int, default=0,
                     help="1: O projection split per KV group; -1: whole rows; 0: the plan's default")
     ap.add_argument("--launch", choices=("resident", "single"), default="resident",
@@ -209,7 +211,8 @@ def main() -> int:
 
     eng = Engine(shape, weights, kc, vc,
                  plan=B.plan_opts(n_cus=args.n_cus, attn_block=args.attn_block,
-                                  mlp_chunks=args.mlp_chunks, o_split=args.o_split, mfma=args.mfma))
+                                  mlp_chunks=args.mlp_chunks, o_split=args.o_split, mfma=args.mfma,
+                                  edn_queue=args.edn_queue))
     info = eng.plan_info()
     dev = eng.dev
     stream = torch.cuda.current_stream(dev)

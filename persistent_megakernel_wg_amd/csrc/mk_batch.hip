@@ -55,10 +55,46 @@ DEV void rt_st8(int base, int off, uint32_t v) { *reinterpret_cast<uint8_t*>(lds
 // one selected expert; the U = (selected experts) x (units per expert) units,
 // in expert order, go to the CUs in even contiguous ranges.  Loader and
 // compute waves take the same range from the same routing decision.
-DEV void edn_range(uint32_t nsel, uint32_t nb, uint32_t n_cus, uint32_t cu, uint32_t& lo, uint32_t& hi) {
-  const uint64_t U = uint64_t(nsel) * nb;
-  lo = uint32_t(U * cu / n_cus);
-  hi = uint32_t(U * (cu + 1) / n_cus);
+// All units, or with a ready queue (row0 = q > 0) all but a 1/q share, go to
+// the CUs in even contiguous ranges; the rest wait in the queue: chunks of uc
+// units handed out at run time by a per-layer counter, each to whichever CU
+// asks first, so that CUs that finish early take the tail.
+constexpr uint32_t kDynMax = 512;  // queue entries per layer parity in LDS
+struct EdnSplit {
+  uint32_t T, Ts, uc, n_dyn;  // units, static units, units per chunk, chunks
+};
+DEV EdnSplit edn_split(uint32_t nsel, uint32_t nb, uint32_t queue) {
+  EdnSplit e;
+  e.T = nsel * nb;
+  e.Ts = queue ? e.T - e.T / queue : e.T;
+  const uint32_t rest = e.T - e.Ts;
+  e.uc = max(2u, (rest + kDynMax - 2) / (kDynMax - 1));
+  e.n_dyn = (rest + e.uc - 1) / e.uc;
+  return e;
+}
+DEV void edn_range(uint32_t U, uint32_t n_cus, uint32_t cu, uint32_t& lo, uint32_t& hi) {
+  lo = uint32_t(uint64_t(U) * cu / n_cus);
+  hi = uint32_t(uint64_t(U) * (cu + 1) / n_cus);
+}
+// Queue entry k of the layer's parity: (layer + 1) << 16 | chunk, written by
+// the first loader wave after it took the chunk from the counter.
+DEV int dyn_slot(uint32_t layer, uint32_t k) { return lb::kMfma + 4 * int((layer & 1) * kDynMax + k); }
+// wait for entry k of this layer; false = abort or watchdog
+DEV bool dyn_entry(uint32_t layer, uint32_t k, uint32_t& chunk) {
+  Watch t0;
+  for (;;) {
+    const uint32_t e = lds_ld(dyn_slot(layer, k));
+    if ((e >> 16) == layer + 1) {
+      chunk = e & 0xFFFFu;
+      return true;
+    }
+    if (aborted()) return false;
+    if (local_timeout(t0, local_limit())) {
+      local_abort(STC_LOCAL_TIMEOUT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(0);
+  }
 }
 // Tag of the expert outputs y: the step and the layer (one buffer serves
 // every layer; a reader must not take the previous layer's values).
@@ -248,6 +284,9 @@ DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
   uint32_t route_layer = 0xFFFFFFFFu;
   uint64_t mask = 0;
   uint32_t retries = 0;
+  // the last expert down projection of each layer parity (its ready-queue
+  // entries are reused two layers later)
+  uint32_t dyn_prev[2] = {kNoCounter, kNoCounter};
   // wait for ring space for page g; false = abort
   auto acquire = [&](uint32_t g) -> bool {
     if (g < min_rel + lb::kPages) return true;
@@ -294,25 +333,53 @@ DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
       const uint32_t ppe = I->aux[2], npu = I->aux[3], run = I->seg_rows[0], nit = i_nit(I), rb = I->row_bytes;
       const uint64_t stride = I->seg_stride[0];
       if (op == OP_EDN) {
-        // this CU's units of the selected experts' down projections
-        const uint32_t Rb = npu, nb = I->aux[4], d = uint32_t(a.hidden);
-        uint32_t lo, hi;
-        edn_range(uint32_t(__builtin_popcountll(mask)), nb, I->n_items, uint32_t(cu), lo, hi);
-        uint64_t m = mask;
-        uint32_t er = 0;
-        for (uint32_t u = lo; u < hi; u++) {
-          const uint32_t ue = u / nb, ub = u % nb;
-          for (; er < ue; er++) m &= m - 1;
-          const uint32_t e = uint32_t(__builtin_ctzll(m));
-          const uint64_t src = I->seg_ptr[1] + e * stride + uint64_t(ub) * run;
-          const uint32_t valid = min(Rb, d - ub * Rb) * rb;
-          for (uint32_t p = 0; p < ppe; p++) {
-            const uint32_t g = pg++;
-            if (!acquire(g)) return;
-            const uint32_t dst = uint32_t(size_t(lds)) + page_off<LayB>(g) + half * kUnit;
-            issue_run(a, dst, src, (p * kUnitsPerPage + half) * kUnit, valid, voff, voff4k, nd, true);
-            after_issue(g, true);
+        // this CU's units of the selected experts' down projections: its
+        // static range, then the chunks it takes from the ready queue
+        const uint32_t Rb = npu, nb = I->aux[4], d = uint32_t(a.hidden), layer = I->layer;
+        const EdnSplit sp = edn_split(uint32_t(__builtin_popcountll(mask)), nb, I->row0);
+        auto stream = [&](uint32_t lo, uint32_t hi) -> bool {
+          for (uint32_t u = lo; u < hi; u++) {
+            const uint32_t ue = u / nb, ub = u % nb;
+            uint64_t m = mask;
+            for (uint32_t er = 0; er < ue; er++) m &= m - 1;
+            const uint32_t e = uint32_t(__builtin_ctzll(m));
+            const uint64_t src = I->seg_ptr[1] + e * stride + uint64_t(ub) * run;
+            const uint32_t valid = min(Rb, d - ub * Rb) * rb;
+            for (uint32_t p = 0; p < ppe; p++) {
+              const uint32_t g = pg++;
+              if (!acquire(g)) return false;
+              const uint32_t dst = uint32_t(size_t(lds)) + page_off<LayB>(g) + half * kUnit;
+              issue_run(a, dst, src, (p * kUnitsPerPage + half) * kUnit, valid, voff, voff4k, nd, true);
+              after_issue(g, true);
+            }
           }
+          return true;
+        };
+        uint32_t lo, hi;
+        edn_range(sp.Ts, I->n_items, uint32_t(cu), lo, hi);
+        if (!stream(lo, hi)) return;
+        if (!I->row0) continue;
+        // the queue entries of this parity were last read by the compute
+        // waves in the expert down projection two layers back
+        if (dyn_prev[layer & 1] != kNoCounter && !wait_all_ge(C_XCONS, dyn_prev[layer & 1] + 1)) {
+          if ((threadIdx.x & 63) == 0) lds_st(C_ABORT, 1);
+          return;
+        }
+        dyn_prev[layer & 1] = i;
+        uint32_t* ctr = reinterpret_cast<uint32_t*>(I->res_ptr) + (a.epoch & 1);
+        for (uint32_t k = 0;; k++) {
+          uint32_t ch = 0;
+          if (v == 0) {
+            if ((threadIdx.x & 63) == 0)
+              ch = __hip_atomic_fetch_add(gp(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ch = min(uni(ch), 0xFFFFu);
+            if ((threadIdx.x & 63) == 0) lds_st(dyn_slot(layer, k), (layer + 1) << 16 | ch);
+          } else if (!dyn_entry(layer, k, ch)) {
+            return;
+          }
+          if (ch >= sp.n_dyn) break;
+          const uint32_t u0 = sp.Ts + ch * sp.uc;
+          if (!stream(u0, min(sp.T, u0 + sp.uc))) return;
         }
         continue;
       }
@@ -909,7 +976,7 @@ done:
 // need one group).  Items are (unit,
 // block of four rows); an item applies its rows to every sequence routed to
 // the unit's expert and stores y[b][slot of the expert in b's top-k][row].
-DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
+DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg, uint32_t& np) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane, K = I->k, nit = i_nit(I), nB = uint32_t(a.batch);
   const int rt = rt_base(I->layer);
@@ -917,8 +984,7 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
   const uint32_t ppu = I->aux[2], Rb = I->aux[3], nb = I->aux[4], d = uint32_t(a.hidden);
   const uint32_t k = uint32_t(a.top_k), Fe = uint32_t(a.expert_ffn);
   const uint32_t cap = uint32_t(lb::kXFloats) / K;  // staged vectors per group
-  uint32_t u_lo, u_hi;
-  edn_range(nsel, nb, I->n_items, uint32_t(c.cu), u_lo, u_hi);
+  const EdnSplit sp = edn_split(nsel, nb, I->row0);
   const uint32_t ytag = y_tag(c.ep, I->layer);
   float* xs = reinterpret_cast<float*>(lds + lb::kX);
   uint64_t* yout = reinterpret_cast<uint64_t*>(I->out_ptr);
@@ -927,18 +993,10 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
   auto n_pairs = [&](uint32_t er) -> uint32_t {
     return uint32_t(__builtin_popcount(rt_u8(rt, RT_TOK + int(rt_u8(rt, RT_LIST + int(er))))));
   };
-  // last expert rank of the group that starts at rank g0 (whole experts,
-  // at most cap pairs; one expert has at most B <= cap)
-  const uint32_t er_last = u_lo < u_hi ? (u_hi - 1) / nb : 0;
-  auto group_end = [&](uint32_t g0) -> uint32_t {
-    uint32_t g1 = g0, cnt = n_pairs(g0);
-    while (g1 < er_last && cnt + n_pairs(g1 + 1) <= cap) cnt += n_pairs(++g1);
-    return g1;
-  };
   // the intermediates of the pairs [p0, p0 + np) into the x slot, 256
   // values per wave and chunk, four chunks of a wave in flight at a time
-  auto stage_group = [&](uint32_t p0, uint32_t np) {
-    const uint32_t nch = np * K / 256;
+  auto stage_group = [&](uint32_t p0, uint32_t npr) {
+    const uint32_t nch = npr * K / 256;
     for (uint32_t c0 = uint32_t(c.w); c0 < nch; c0 += 4 * kNComp) {
       f4 t[4];
 #pragma unroll
@@ -960,58 +1018,81 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg) {
       }
     }
   };
+  const uint32_t nrb = (Rb + 3) / 4;
+  bool staged_any = false;
+  // Units [u_lo, u_hi), whose pages start pofs pages into the instruction's
+  // stream: their experts' routed sequences are staged in groups of whole
+  // experts (at most cap pairs); items are (unit, block of four rows).
+  auto run_units = [&](uint32_t u_lo, uint32_t u_hi, uint32_t pofs) -> bool {
+    const uint32_t er_last = (u_hi - 1) / nb;
+    for (uint32_t g0 = u_lo / nb;;) {
+      uint32_t g1 = g0, cnt = n_pairs(g0);
+      while (g1 < er_last && cnt + n_pairs(g1 + 1) <= cap) cnt += n_pairs(++g1);
+      const uint32_t p0 = rt_u8(rt, RT_PBASE + int(g0));
+      const uint32_t npr = rt_u8(rt, RT_PBASE + int(g1)) + n_pairs(g1) - p0;
+      // every wave has finished the previous group before its slot is rewritten
+      if (staged_any && !comp_barrier()) return false;
+      staged_any = true;
+      stage_group(p0, npr);
+      if (!comp_barrier()) return false;
+      if (trl && pofs == 0 && g0 == u_lo / nb) {
+        trace_put(a, c.cu, i, TR_STAGED, now32());
+        trace_put(a, c.cu, i, TR_ITEM0, now32());
+      }
+      const uint32_t ua = max(u_lo, g0 * nb), ub = min(u_hi, (g1 + 1) * nb);
+      const uint32_t n_items = (ub - ua) * nrb;
+      for (uint32_t it = c.w; it < n_items; it += kNComp) {
+        const uint32_t u = ua + it / nrb, r0 = 4 * (it % nrb);
+        const uint32_t er = u / nb, rb = u % nb;
+        const uint32_t rows_u = min(Rb, d - rb * Rb);
+        if (r0 >= rows_u) continue;
+        const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
+        const uint32_t tok = uni(rt_u8(rt, RT_TOK + int(e)));
+        const uint32_t base = uni(rt_u8(rt, RT_PBASE + int(er))) - p0;
+        const uint32_t nrows = min(4u, rows_u - r0);
+        const uint32_t u0 = (pofs + (u - u_lo) * ppu) * kUnitsPerPage + r0 * nit;
+        if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + u0 / kUnitsPerPage);
+        if (!wait_page(pg + (u0 + nrows * nit - 1) / kUnitsPerPage, c.fcache)) return false;
+        float acc[32];
+        dot_rows4(pg, u0, nit, nrows, tok,
+                  [&](int b) { return (base + __builtin_popcount(tok & ((1u << b) - 1))) * K; }, acc);
+        const float sdot = reduce32(acc);
+        const uint32_t idx = reduce32_index(lane), rr = idx >> 3, bb = idx & 7;
+        if (lane < 32 && ((tok >> bb) & 1) && rr < nrows) {
+          const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + bb));
+          st_tag(yout + size_t(bb * k + slot) * d + rb * Rb + r0 + rr, sdot, ytag);
+        }
+      }
+      // the next group starts at the unit after this group's last one
+      if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + pofs + (ub - u_lo) * ppu);
+      if (g1 >= er_last) return true;
+      g0 = g1 + 1;
+    }
+  };
   // every wave has left the previous input before the slot is rewritten
   if (!wait_all_ge(C_XCONS, i)) return false;
   if (trl) trace_put(a, c.cu, i, TR_XFREE, now32());
-  const uint32_t nrb = (Rb + 3) / 4;
-  for (uint32_t g0 = u_lo / nb; u_lo < u_hi;) {
-    // group: experts g0 .. g1 and their pairs [p0, p0 + np)
-    const uint32_t g1 = group_end(g0);
-    const uint32_t p0 = rt_u8(rt, RT_PBASE + int(g0));
-    const uint32_t np = rt_u8(rt, RT_PBASE + int(g1)) + n_pairs(g1) - p0;
-    stage_group(p0, np);
-    if (!comp_barrier()) return false;
-    if (trl && g0 == u_lo / nb) {
-      trace_put(a, c.cu, i, TR_STAGED, now32());
-      trace_put(a, c.cu, i, TR_ITEM0, now32());
-    }
-    // the group's units and their blocks of four rows
-    const uint32_t ua = max(u_lo, g0 * nb), ub = min(u_hi, (g1 + 1) * nb);
-    const uint32_t n_items = (ub - ua) * nrb;
-    for (uint32_t it = c.w; it < n_items; it += kNComp) {
-      const uint32_t u = ua + it / nrb, r0 = 4 * (it % nrb);
-      const uint32_t er = u / nb, rb = u % nb;
-      const uint32_t rows_u = min(Rb, d - rb * Rb);
-      if (r0 >= rows_u) continue;
-      const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
-      const uint32_t tok = uni(rt_u8(rt, RT_TOK + int(e)));
-      const uint32_t base = uni(rt_u8(rt, RT_PBASE + int(er))) - p0;
-      const uint32_t nrows = min(4u, rows_u - r0);
-      const uint32_t u0 = (u - u_lo) * ppu * kUnitsPerPage + r0 * nit;
-      if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + u0 / kUnitsPerPage);
-      if (!wait_page(pg + (u0 + nrows * nit - 1) / kUnitsPerPage, c.fcache)) return false;
-      float acc[32];
-      dot_rows4(pg, u0, nit, nrows, tok,
-                [&](int b) { return (base + __builtin_popcount(tok & ((1u << b) - 1))) * K; }, acc);
-      const float sdot = reduce32(acc);
-      const uint32_t idx = reduce32_index(lane), rr = idx >> 3, bb = idx & 7;
-      if (lane < 32 && ((tok >> bb) & 1) && rr < nrows) {
-        const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + bb));
-        st_tag(yout + size_t(bb * k + slot) * d + rb * Rb + r0 + rr, sdot, ytag);
-      }
-    }
-    // the next group starts at the unit after this group's last one
-    if (lane == 0) lds_st(C_RELEASED + 4 * c.w, pg + (ub - u_lo) * ppu);
-    if (g1 >= er_last) break;
-    g0 = g1 + 1;
-    // every wave has finished this group before the slot is rewritten
-    if (!comp_barrier()) return false;
+  uint32_t u_lo, u_hi, pofs = 0;
+  edn_range(sp.Ts, I->n_items, uint32_t(c.cu), u_lo, u_hi);
+  if (u_lo < u_hi) {
+    if (!run_units(u_lo, u_hi, 0)) return false;
+    pofs = (u_hi - u_lo) * ppu;
+  }
+  // then the chunks the loader took from the ready queue, in its order
+  for (uint32_t q = 0; I->row0; q++) {
+    uint32_t ch;
+    if (!dyn_entry(I->layer, q, ch)) return false;
+    if (ch >= sp.n_dyn) break;
+    const uint32_t u0 = sp.Ts + ch * sp.uc, u1 = min(sp.T, u0 + sp.uc);
+    if (!run_units(u0, u1, pofs)) return false;
+    pofs += (u1 - u0) * ppu;
   }
   if (trl) trace_put(a, c.cu, i, TR_A_STATS, now32());
   if (lane == 0) {
-    lds_st(C_RELEASED + 4 * c.w, pg + (u_hi - u_lo) * ppu);
+    lds_st(C_RELEASED + 4 * c.w, pg + pofs);
     lds_st(C_XCONS + 4 * c.w, i + 1);
   }
+  np = pofs;
   return true;
 }
 
@@ -1029,6 +1110,11 @@ DEV bool erd(Comp& c, InstrCP I, uint32_t i) {
   const __amdgpu_buffer_rsrc_t ry = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), nB * k * d * kActBytes);
   const __amdgpu_buffer_rsrc_t rh = act_rsrc(reinterpret_cast<const void*>(I->res_ptr), nB * d * kActBytes);
   uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
+  // one CU clears the layer's ready-queue counter of the next step (this
+  // step's expert down projections use the other one)
+  if (I->seg_ptr[0] && c.w == 0 && lane == 0)
+    __hip_atomic_store(gp(reinterpret_cast<uint32_t*>(I->seg_ptr[0])) + ((c.ep + 1) & 1), 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   for (uint32_t base = uint32_t(c.w) * 64; base < total; base += 64 * kNComp) {
     const uint32_t idx = base + lane, on = idx < total;
     const uint32_t b = on ? idx / nr : 0, r = on ? idx % nr : 0, row = r0 + r;
@@ -1216,11 +1302,7 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
     }
     uint32_t np = I->n_pages;
     if (op == OP_EGU) np = *lw(rt_base(I->layer) + RT_NSEL) * I->aux[2];
-    if (op == OP_EDN) {
-      uint32_t lo, hi;
-      edn_range(*lw(rt_base(I->layer) + RT_NSEL), I->aux[4], I->n_items, uint32_t(cu), lo, hi);
-      np = (hi - lo) * I->aux[2];
-    }
+
     if (i_flags(I) & F_DIRECT) np = 0;
     bool ok = true;
     if (op == OP_BGEMV || op == OP_EGU) {
@@ -1268,7 +1350,7 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       // have read the previous instruction's inputs
       staged = kNoCounter;
       last_sync = i;
-      ok = op == OP_EDN ? edn(c, I, i, pg) : run_attn_b<G>(c, I, i, pg);
+      ok = op == OP_EDN ? edn(c, I, i, pg, np) : run_attn_b<G>(c, I, i, pg);
     }
     if (!ok) {
       if (c.lane == 0) lds_st(C_ABORT, 1);
@@ -1305,6 +1387,8 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
 template <class G>
 __global__ __launch_bounds__(kThreads, 1) void mk_megakernel_b(KArgs a) {
   for (int o = threadIdx.x * 4; o < C_CTRL_END; o += kThreads * 4) *lw(o) = 0;
+  // the expert down projection's ready-queue entries (tagged by layer)
+  for (int o = threadIdx.x * 4; o < 4 * int(2 * kDynMax); o += kThreads * 4) *lw(lb::kMfma + o) = 0;
   __syncthreads();
   if (threadIdx.x == 0) {
     *lw(C_STATUS_LO) = uint32_t(uint64_t(a.status));

@@ -58,7 +58,9 @@ constexpr int kMaxB = 8;             // sequences per step
 constexpr int kPages = 5;
 constexpr int kSS = 512;             // sum of squares per 128-value chunk [128]
 constexpr int kArg = 1024;           // argmax per compute wave and sequence [kNComp][kMaxB][2]
-constexpr int kMfma = 1536;          // matrix-core GEMV: each compute wave's partial block sums
+constexpr int kMfma = 1536;          // 4 KiB: the matrix-core GEMV's per-wave partial block sums
+                                     // (LM head), and the expert down projection's ready queue
+                                     // (two layer parities of 512 entries)
 constexpr int kMfmaWaveBytes = 512;  // [16 rows][8 sequences] fp32 per wave
 constexpr int kMaxDnRows = 16;
 constexpr int kMaxTopK = 8;

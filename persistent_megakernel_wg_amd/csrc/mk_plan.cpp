@@ -214,6 +214,11 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
     // vector-ALU GEMVs by default: the matrix-core LM head measured a few us
     // faster, but the kernel variant that carries it loses more elsewhere
     if (r.mfma == 0) r.mfma = -1;
+    // an eighth of the expert down-projection units in the ready queue
+    // (measured on the MoE shape: 1/4 4605, 1/8 4583, 1/16 4590 and no
+    // queue 4618 us per step)
+    if (r.edn_queue == 0) r.edn_queue = 8;
+    if (r.edn_queue < 0 || r.edn_queue == 1) r.edn_queue = 0;
     if (r.attn_block <= 0) {
       // K and V blocks of a tile in four of the five ring pages, scores in
       // the scratch, whole KV groups per tile
@@ -269,6 +274,7 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
   if (r.o_split == 0) r.o_split = -1;
   // batch 1: no matrix-core tiles (the GEMVs are a single column)
   r.mfma = -1;
+  r.edn_queue = 0;
   if (r.watchdog_ms <= 0) r.watchdog_ms = 2000;
   return r;
 }
@@ -302,6 +308,7 @@ ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
   // expert outputs [B][top_k][d] of the layer being computed (one buffer for
   // every layer: its tags carry the layer as well as the step)
   a.y = is_batched(c) ? take(E * B * uint64_t(c.top_k) * c.hidden) : 0;
+  a.edn_ctr = is_batched(c) ? take(8ull * c.n_layers) : 0;
   a.tok = take(E * B);
   a.rope_cos = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
   a.rope_sin = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
@@ -620,7 +627,6 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
     {
       const int Rb = std::max(4, 32768 / (2 * Fe));
       const int nb = ceil_div(d, Rb), ppu = ceil_div(int64_t(Rb) * 2 * Fe, kPageBytes);
-      const int max_units = int(ceil_div(int64_t(E) * nb, C));
       for (int cu = 0; cu < C; cu++) {
         Instr I = blank();
         I.op = OP_EDN;
@@ -643,9 +649,12 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.seg_rows[0] = uint32_t(Rb * 2 * Fe);
         I.in_ptr = A + ar.m[l];
         I.out_ptr = A + ar.y;
+        I.res_ptr = A + ar.edn_ctr + 8ull * l;  // the layer's ready-queue counters
+        I.row0 = uint32_t(std::max(0, o.edn_queue));
         I.wait_ctr[0] = c_gu[l];
         I.sig_ctr = c_dny[l];
-        I.n_pages = uint32_t(max_units * ppu);
+        // at most every unit (the static share and the queue's chunks)
+        I.n_pages = uint32_t(E * nb * ppu);
         InstrMeta m;
         m.stage = stg + ST_DOWN;
         // every unit's writes are decided by the routing: the tiles share
@@ -674,6 +683,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.in_ptr = A + ar.y;
         I.res_ptr = A + ar.h[l];
         I.out_ptr = A + ar.x[l + 1];
+        if (r0 == 0) I.seg_ptr[0] = A + ar.edn_ctr + 8ull * l;  // clears the next step's counter
         I.wait_ctr[0] = c_dny[l];
         I.wait_ctr[1] = c_o[l];
         I.sig_ctr = c_dn[l];
@@ -1418,8 +1428,7 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         if (uint32_t(ceil_div(4 * I.row_bytes, kPageBytes)) + 1 > uint32_t(lb::kPages) ||
             uint64_t(c.batch) * I.k > uint64_t(lb::kXFloats))
           return fail("expert down-projection items");
-        if (I.n_items != uint32_t(C) || I.n_pages != uint32_t(ceil_div(uint64_t(c.n_experts) * nb, C)) * ppu ||
-            (I.flags & F_DIRECT))
+        if (I.n_items != uint32_t(C) || I.n_pages != uint32_t(c.n_experts) * nb * ppu || (I.flags & F_DIRECT))
           return fail("expert down-projection page budget");
         continue;
       }
@@ -1655,13 +1664,14 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
             return fail("expert units outside the expert tensors");
           if (!in_arena(I.in_ptr, I.in_ptr + mb)) return fail("expert intermediate outside the arena");
           if (!in_arena(I.out_ptr, I.out_ptr + EB * NB * c.top_k * d)) return fail("expert outputs outside the arena");
+          if (!in_arena(I.res_ptr, I.res_ptr + 8)) return fail("ready-queue counters outside the arena");
         }
         continue;
       }
       if (I.op == OP_ERD) {
         const uint64_t rl = (NB - 1) * d + I.row0 + I.n_rows;
         if (!in_arena(I.in_ptr, I.in_ptr + EB * NB * c.top_k * d) || !in_arena(I.res_ptr, I.res_ptr + EB * rl) ||
-            !in_arena(I.out_ptr, I.out_ptr + EB * rl))
+            !in_arena(I.out_ptr, I.out_ptr + EB * rl) || (I.seg_ptr[0] && !in_arena(I.seg_ptr[0], I.seg_ptr[0] + 8)))
           return fail("expert sum rows outside the arena");
         continue;
       }

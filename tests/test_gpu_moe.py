@@ -109,6 +109,15 @@ def test_moe_tiny_matrix_core_lm_head(need_gpu, kw, opts):
     _moe_case(TINY.replace(**kw), mfma=1, **opts)
 
 
+@pytest.mark.parametrize("queue,opts", [(2, {}), (2, {"n_cus": 1, "attn_block": 64}), (4, {"n_cus": 3}),
+                                        (-1, {}), (-1, {"n_cus": 37})])
+def test_moe_tiny_ready_queue(need_gpu, queue, opts):
+    # the expert down projection with a 1/queue share of its units handed out
+    # at run time (chunks to whichever CU asks first), and with none
+    _moe_case(TINY, edn_queue=queue, **opts)
+    _moe_case(TINY.replace(expert_ffn=2048, top_k=4, n_experts=16), edn_queue=queue, **opts)
+
+
 def test_moe_tiny_greedy_chain_on_device(need_gpu):
     from persistent_megakernel_wg_amd.engine import Engine
     s = TINY

@@ -172,6 +172,13 @@ def test_moe_plan_for_the_large_shape_on_fewer_cus():
     B.mk_plan_check(_cfg("moe_b8_ctx2048"), 80)
 
 
+@pytest.mark.parametrize("queue", [-1, 2, 4, 8, 16])
+def test_moe_ready_queue_plans_verify(queue):
+    for n_cus in (1, 3, 256):
+        B.mk_plan_check(_cfg("moe_tiny"), n_cus, B.plan_opts(edn_queue=queue))
+    B.mk_plan_check(_cfg("moe_b8_ctx2048"), 256, B.plan_opts(edn_queue=queue))
+
+
 @pytest.mark.parametrize("name,kw,n_cus", [
     ("moe_tiny", {}, 256), ("moe_tiny", {}, 1), ("moe_tiny", {"batch": 3}, 37), ("moe_b8_ctx2048", {}, 256),
 ])
