@@ -122,10 +122,19 @@ struct EpiCtx {
 DEV EpiCtx epi_of(InstrCP I) {
   return EpiCtx{reinterpret_cast<uint64_t*>(I->out_ptr), i_epi(I), I->aux[0], I->row0};
 }
+// OP: the kernel variant also runs split-K O tiles (EPI_OPART)
+template <bool OP>
 DEV void epi_row(Comp& c, const EpiCtx& E, uint32_t i, uint32_t t_row, float v, ArgBest& best) {
   const KArgs& a = *c.a;
   uint64_t* out = E.out;
   const uint32_t row = E.row0 + t_row;
+  if constexpr (OP) {
+    if (E.epi == EPI_OPART) {
+      // the group's partial row (untagged fp32, published by the ticket)
+      st_act(reinterpret_cast<float*>(out) + row, v);
+      return;
+    }
+  }
   switch (E.epi) {
     case EPI_STORE:
     case EPI_SWIGLU:
@@ -144,10 +153,6 @@ DEV void epi_row(Comp& c, const EpiCtx& E, uint32_t i, uint32_t t_row, float v, 
     case EPI_ACC_LAST:
       st_tag(out + row, reinterpret_cast<float*>(lds + kLdsAcc)[E.acc0 + t_row] + v, c.ep);
       break;
-    case EPI_OPART:
-      // the group's partial row (untagged fp32, published by the ticket)
-      st_act(reinterpret_cast<float*>(out) + row, v);
-      break;
     case EPI_ARGMAX:
       if (a.logits) gp(a.logits)[size_t(c.step) * uint32_t(a.vocab) + row] = v;
       if (v != v) __hip_atomic_store(gp(a.status) + ST_NAN, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -156,7 +161,7 @@ DEV void epi_row(Comp& c, const EpiCtx& E, uint32_t i, uint32_t t_row, float v, 
   }
 }
 
-template <int NIT, int RPU>
+template <int NIT, int RPU, bool OP = false>
 DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
   constexpr int LPR = 64 / RPU;
   const KArgs& a = *c.a;
@@ -238,8 +243,8 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
         }
         if (lane == 0) {
           const float a0 = sum[0][0] * inv, b0 = sum[1][0] * inv;
-          epi_row(c, E, i, t, RU == 2 ? silu(a0) * (sum[0][RU - 1] * inv) : a0, best);
-          if (two) epi_row(c, E, i, tb, RU == 2 ? silu(b0) * (sum[1][RU - 1] * inv) : b0, best);
+          epi_row<OP>(c, E, i, t, RU == 2 ? silu(a0) * (sum[0][RU - 1] * inv) : a0, best);
+          if (two) epi_row<OP>(c, E, i, tb, RU == 2 ? silu(b0) * (sum[1][RU - 1] * inv) : b0, best);
         }
         if (trl && t == 0) trace_put(a, c.cu, i, TR_ITEM0, now32());
       }
@@ -263,9 +268,9 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
       lo *= inv;
       hi *= inv;
       if (pair) {
-        if (lane == 0) epi_row(c, E, i, t, silu(lo) * hi, best);
+        if (lane == 0) epi_row<OP>(c, E, i, t, silu(lo) * hi, best);
       } else if ((lane & 31) == 0) {
-        epi_row(c, E, i, 2 * t + (lane >> 5), lane ? hi : lo, best);
+        epi_row<OP>(c, E, i, 2 * t + (lane >> 5), lane ? hi : lo, best);
       }
       if (trl && t == 0) trace_put(a, c.cu, i, TR_ITEM0, now32());
     }
@@ -462,12 +467,14 @@ DEV bool stage_finish(Comp& c, InstrCP I, uint32_t i, bool stage_x, StageIn& S) 
 // kernel spills) and its code small.  The runtime picks a GeoFix kernel when
 // every instruction of the plan matches it.
 struct GeoAny {
-  static constexpr bool any = true;
+  static constexpr bool any = true, os = true;
 };
 // H = query heads per attention tile, D = head dimension
-template <int ND, int RD, int NQ, int RQ, int NF, int RF, int H, int D>
+// OS: the O projection is split per KV group (its tiles and merges are
+// compiled only into these variants)
+template <int ND, int RD, int NQ, int RQ, int NF, int RF, int H, int D, bool OS>
 struct GeoFix {
-  static constexpr bool any = false;
+  static constexpr bool any = false, os = OS;
   static constexpr int nd = ND, rd = RD, nq = NQ, rq = RQ, nf = NF, rf = RF, hpt = H, dh = D;
 };
 
@@ -476,15 +483,15 @@ DEV bool run_gemv(Comp& c, InstrCP I, uint32_t i) {
   if constexpr (!G::any) {
     const uint32_t nit = i_nit(I), rpu = i_rpu(I);
     if (nit == uint32_t(G::nd) && rpu == uint32_t(G::rd)) return gemv<G::nd, G::rd>(c, I, i);
-    if (nit == uint32_t(G::nq) && rpu == uint32_t(G::rq)) return gemv<G::nq, G::rq>(c, I, i);
+    if (nit == uint32_t(G::nq) && rpu == uint32_t(G::rq)) return gemv<G::nq, G::rq, G::os>(c, I, i);
     return gemv<G::nf, G::rf>(c, I, i);
   } else {
-    if (i_rpu(I) == 2) return gemv<1, 2>(c, I, i);
+    if (i_rpu(I) == 2) return gemv<1, 2, true>(c, I, i);
     switch (i_nit(I)) {
-      case 1: return gemv<1, 1>(c, I, i);
-      case 2: return gemv<2, 1>(c, I, i);
+      case 1: return gemv<1, 1, true>(c, I, i);
+      case 2: return gemv<2, 1, true>(c, I, i);
       case 3: return gemv<3, 1>(c, I, i);
-      case 4: return gemv<4, 1>(c, I, i);
+      case 4: return gemv<4, 1, true>(c, I, i);
       case 5: return gemv<5, 1>(c, I, i);
       case 6: return gemv<6, 1>(c, I, i);
       case 7: return gemv<7, 1>(c, I, i);
@@ -733,7 +740,7 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
     // completion: the last wave signals.  Tagged outputs need no wait; the
     // untagged data behind a ticket (argmax slots, attention partials) must
     // have landed before the ticket moves.
-    const bool opart = i_op(I) == OP_GEMV && i_epi(I) == EPI_OPART;
+    const bool opart = G::os && i_op(I) == OP_GEMV && i_epi(I) == EPI_OPART;
     const bool release = (i_op(I) == OP_GEMV && i_epi(I) == EPI_ARGMAX) ||
                          (i_op(I) == OP_ATTN && I->aux[3] > 1) || opart;
     if (release) wait_vm0();
@@ -754,14 +761,16 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       if (old + 1 != c.ep * I->aux[3]) continue;
       run_merge<G>(c, I);
     }
-    if (opart) {
-      uint32_t old = 0;
-      if (c.lane == 0) old = ctr_release(ctr_line(a, I->aux[2], 0));
-      old = uni(old);
-      if (old + 1 != c.ep * I->aux[3]) continue;
-      if (!o_merge(c, I)) {
-        if (c.lane == 0) lds_st(C_ABORT, 1);
-        return;
+    if constexpr (G::os) {
+      if (opart) {
+        uint32_t old = 0;
+        if (c.lane == 0) old = ctr_release(ctr_line(a, I->aux[2], 0));
+        old = uni(old);
+        if (old + 1 != c.ep * I->aux[3]) continue;
+        if (!o_merge(c, I)) {
+          if (c.lane == 0) lds_st(C_ABORT, 1);
+          return;
+        }
       }
     }
     if ((i_flags(I) & F_SIGNAL) && c.lane == 0) ctr_signal(ctr_line(a, I->sig_ctr, uint32_t(cu) % kCtrSpread));
@@ -824,35 +833,36 @@ extern "C" hipError_t mk_launch_pack(const mk::PackCopy* copies, uint32_t n, voi
 namespace {
 struct Variant {
   int nd, rd, nq, rq, nf, rf, hpt, dh;  // 0 = generic
+  bool os;                              // split-K O projection
   const void* fn;
 };
-#define MK_VARIANT(ND, RD, NQ, RQ, NF, RF, H, D) \
-  {ND, RD, NQ, RQ, NF, RF, H, D,                 \
-   reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoFix<ND, RD, NQ, RQ, NF, RF, H, D>>)}
+#define MK_VARIANT(ND, RD, NQ, RQ, NF, RF, H, D, OS) \
+  {ND, RD, NQ, RQ, NF, RF, H, D, OS,                 \
+   reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoFix<ND, RD, NQ, RQ, NF, RF, H, D, OS>>)}
 // Shapes with their own kernel: the Llama-3.2-1B shape (MLP in two chunks;
 // one query head per attention tile at short contexts, the whole KV group at
 // long ones), the Llama-3-8B shape (four chunks) and the small test decoder.
 const Variant kVariants[] = {
-    {0, 0, 0, 0, 0, 0, 0, 0, reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoAny>)},
-    MK_VARIANT(4, 1, 4, 1, 8, 1, 1, 64),
-    MK_VARIANT(4, 1, 4, 1, 8, 1, 4, 64),
-    MK_VARIANT(8, 1, 8, 1, 7, 1, 4, 128),
-    MK_VARIANT(1, 2, 1, 2, 2, 1, 1, 64),
+    {0, 0, 0, 0, 0, 0, 0, 0, true, reinterpret_cast<const void*>(&mk::mk_megakernel<mk::GeoAny>)},
+    MK_VARIANT(4, 1, 4, 1, 8, 1, 1, 64, false),
+    MK_VARIANT(4, 1, 4, 1, 8, 1, 4, 64, false),
+    MK_VARIANT(8, 1, 8, 1, 7, 1, 4, 128, false),
+    MK_VARIANT(1, 2, 1, 2, 2, 1, 1, 64, false),
     // the same shapes with the O projection split per KV group
-    MK_VARIANT(4, 1, 1, 2, 8, 1, 1, 64),
-    MK_VARIANT(4, 1, 1, 2, 8, 1, 4, 64),
-    MK_VARIANT(8, 1, 1, 1, 7, 1, 4, 128),
+    MK_VARIANT(4, 1, 1, 2, 8, 1, 1, 64, true),
+    MK_VARIANT(4, 1, 1, 2, 8, 1, 4, 64, true),
+    MK_VARIANT(8, 1, 1, 1, 7, 1, 4, 128, true),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 bool g_attr_set[kNumVariants] = {};
 }  // namespace
 
 // Index of the kernel built for this geometry, or 0 (the generic kernel).
-extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpt, int dh) {
+extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpt, int dh, int os) {
   for (int v = 1; v < kNumVariants; v++) {
     const Variant& k = kVariants[v];
     if (k.nd == nd && k.rd == rd && k.nq == nq && k.rq == rq && k.nf == nf && k.rf == rf && k.hpt == hpt &&
-        k.dh == dh)
+        k.dh == dh && k.os == (os != 0))
       return v;
   }
   return 0;

@@ -14,7 +14,7 @@
 
 extern "C" hipError_t mk_launch_megakernel(const mk::KArgs* args, int n_cus, hipStream_t stream,
                                            int cooperative, int variant);
-extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpt, int dh);
+extern "C" int mk_pick_variant(int nd, int rd, int nq, int rq, int nf, int rf, int hpt, int dh, int os);
 extern "C" hipError_t mk_launch_batched(const mk::KArgs* args, int n_cus, hipStream_t stream, int cooperative,
                                         int variant);
 extern "C" int mk_pick_batched(int hpt, int dh, int mfma);
@@ -117,7 +117,7 @@ int variant_for(const mk_config& cfg, const mk_plan_opts& o) {
       !mk::gemv_geometry(oq, &nq, &rq) ||
       !mk::gemv_geometry(cfg.ffn / o.mlp_chunks, &nf, &rf))
     return 0;
-  return mk_pick_variant(nd, rd, nq, rq, nf, rf, o.attn_heads, cfg.head_dim);
+  return mk_pick_variant(nd, rd, nq, rq, nf, rf, o.attn_heads, cfg.head_dim, o.o_split > 0);
 }
 
 bool dense_pointers_ok(const mk_weights& w) {
