@@ -426,9 +426,45 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
     I.n_items = uint32_t(ceil_div(int64_t(I.n_rows), 16));
     I.n_pages = uint32_t(ceil_div(int64_t(I.n_items) * 16 * I.row_bytes, kPageBytes));
   };
-  // attention tile -> CU: spread evenly
+  // attention tile -> CU.  The tiles of the last position block (the
+  // positions past the pre-filled context: a few rows at most) cost a
+  // fraction of a full block's; the full blocks are spread evenly and each
+  // last-block tile goes to a CU with the fewest tiles, near an even spread,
+  // so that the CUs that take one tile more take a light one.
   const int n_att = B * G * tpg * nblk;
-  auto att_cu = [&](int a) { return int((int64_t(a) * C / n_att) % C); };
+  std::vector<int> att_cu_of(n_att);
+  {
+    const bool split_last = nblk > 1;
+    const int n_full = split_last ? B * G * tpg * (nblk - 1) : n_att, n_last = n_att - n_full;
+    std::vector<int> count(C, 0);
+    int j = 0, k = 0;
+    for (int a = 0; a < n_att; a++) {
+      if (split_last && a % nblk == nblk - 1) continue;
+      const int cu = int((int64_t(j++) * C / n_full) % C);
+      att_cu_of[a] = cu;
+      count[cu]++;
+    }
+    for (int a = 0; split_last && a < n_att; a++) {
+      if (a % nblk != nblk - 1) continue;
+      const int want = int((int64_t(k++) * C / std::max(1, n_last)) % C);
+      int best = want;
+      for (int dc = 0; dc < C; dc++) {
+        const int cu = (want + dc) % C;
+        if (count[cu] < count[best]) best = cu;
+        if (count[best] == 0) break;
+      }
+      // the first CU at or after the even position among those with the fewest tiles
+      int mn = count[best];
+      for (int dc = 0; dc < C; dc++)
+        if (count[(want + dc) % C] == mn) {
+          best = (want + dc) % C;
+          break;
+        }
+      att_cu_of[a] = best;
+      count[best]++;
+    }
+  }
+  auto att_cu = [&](int a) { return att_cu_of[a]; };
   const int n_rt = (E + 1) / 2;  // router tiles of two rows
   auto rt_cu = [&](int t) { return int(int64_t(t) * C / n_rt); };
   const int max_res_rows = std::min(kMaxResRows / B, lb::kMaxDnRows);
