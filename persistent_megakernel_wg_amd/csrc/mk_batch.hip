@@ -287,6 +287,9 @@ DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
   // the last expert down projection of each layer parity (its ready-queue
   // entries are reused two layers later)
   uint32_t dyn_prev[2] = {kNoCounter, kNoCounter};
+  // the last expert sum of each layer parity (the last reader of that
+  // parity's routing table)
+  uint32_t rt_last[2] = {kNoCounter, kNoCounter};
   // wait for ring space for page g; false = abort
   auto acquire = [&](uint32_t g) -> bool {
     if (g < min_rel + lb::kPages) return true;
@@ -315,21 +318,42 @@ DEV void loader_b(const KArgs& a, InstrCP q, uint32_t n, int v, int cu) {
   for (uint32_t i = 0; i < n; i++) {
     InstrCP I = q + i;
     const uint32_t op = i_op(I);
-    if ((i_flags(I) & F_DIRECT) || op == OP_ERD) continue;
+    if (op == OP_ERD) {
+      // the last reader of its layer's routing table slot
+      rt_last[I->layer & 1] = i;
+      continue;
+    }
     if (op == OP_EGU || op == OP_EDN) {
       const uint32_t layer = I->layer;
       if (layer != route_layer) {
-        // every issued page is published before the wait
+        // The routing decision, at the layer's first expert instruction: the
+        // selected-expert union for the streaming, and (first loader wave)
+        // the whole table for the compute waves, which then find it ready
+        // instead of deciding it between their attention and gate/up work.
+        // Every issued page is published before the waits.
         wait_vm0();
         publish(g_pub, g_issue, v);
-        if (!wait_counter(a, I->aux[0], a.epoch * I->aux[1], cu, i) ||
-            !route_topk(a, I, mask, -1, retries)) {
+        // the table slot of this parity was last read by the expert sum two
+        // layers back
+        const bool table = v == 0;
+        bool ok = wait_counter(a, I->aux[0], a.epoch * I->aux[1], cu, i);
+        if (ok && table && rt_last[layer & 1] != kNoCounter) ok = wait_all_ge(C_XCONS, rt_last[layer & 1] + 1);
+        ok = ok && route_topk(a, I, mask, table ? rt_base(layer) : -1, retries);
+        if (!ok) {
           if ((threadIdx.x & 63) == 0) lds_st(C_ABORT, 1);
           return;
         }
         mask = uni64(mask);
         route_layer = layer;
+        if (table && (threadIdx.x & 63) == 0) {
+          lds_st(C_RTOK, layer + 1);
+          // CU 0 counts the layer's selected experts (bytes streamed per step)
+          if (cu == 0)
+            __hip_atomic_fetch_add(gp(a.route_stats) + layer, uint32_t(__builtin_popcountll(mask)),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
+      if (i_flags(I) & F_DIRECT) continue;
       const uint32_t ppe = I->aux[2], npu = I->aux[3], run = I->seg_rows[0], nit = i_nit(I), rb = I->row_bytes;
       const uint64_t stride = I->seg_stride[0];
       if (op == OP_EDN) {
@@ -1267,18 +1291,10 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
         seen_val = target;
       }
       if (ok && (i_flags(I) & F_ROUTE)) {
-        // every wave has finished the earlier instructions (and with them
-        // every read of this table slot) before it is rewritten
-        uint64_t mask = 0;
+        // the first loader wave has written the layer's routing table
         if (tr && c.lane == 0) trace_put(a, cu, i, TR_A_PASS1, now32());
-        ok = wait_all_ge(C_XCONS, i);
-        if (tr && c.lane == 0) trace_put(a, cu, i, TR_A_STATS, now32());
-        ok = ok && route_topk(a, I, mask, rt_base(I->layer), c.retries);
+        ok = wait_lds_ge(C_RTOK, I->layer + 1);
         if (tr && c.lane == 0) trace_put(a, cu, i, TR_A_PASS3, now32());
-        // CU 0 counts the layer's selected experts (bytes streamed per step)
-        if (ok && cu == 0 && c.lane == 0)
-          __hip_atomic_fetch_add(gp(a.route_stats) + I->layer, uint32_t(__builtin_popcountll(mask)),
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (!ok) {
         if (c.lane == 0) lds_st(C_ABORT, 1);

@@ -55,6 +55,7 @@ enum : int {
   C_DEPOK = 68,        // instructions whose counter waits are satisfied
   C_MARR = 72,         // matrix-core GEMV: wave arrivals at block ends (all blocks)
   C_MRED = 76,         // matrix-core GEMV: blocks reduced so far
+  C_RTOK = 80,         // batched kernel: layer + 1 of the last routing table written
   C_XCONS = 96,        // [kNComp] instructions whose staged inputs each wave read
   C_DONE = 128,        // [kDoneRing] waves finished, per instruction slot
   C_ABORT = 160,
