@@ -934,61 +934,94 @@ DEV bool egu_direct(Comp& c, InstrCP I, uint32_t i) {
   const int rt = rt_base(I->layer);
   const uint32_t nsel = *lw(rt + RT_NSEL), npu = I->aux[3];
   const uint32_t Fe = uint32_t(a.expert_ffn), k = uint32_t(a.top_k), rb = I->row_bytes;
-  const uint64_t stride = I->seg_stride[0], gate0 = I->seg_ptr[1], up0 = I->seg_ptr[2];
+  const uint64_t stride = I->seg_stride[0];
+  // row 0 of expert 0's gate and up matrices
+  const uint64_t gate0 = I->seg_ptr[1] - uint64_t(I->row0) * rb, up0 = I->seg_ptr[2] - uint64_t(I->row0) * rb;
   const float inv = inv_rms(a, I);
   const float my_inv = __shfl(inv, int(lane & 7), 64);
   const float* xs = reinterpret_cast<const float*>(lds + lb::kX);
   float* out = reinterpret_cast<float*>(I->out_ptr);
-  const uint32_t n_items = nsel * npu;
-  u4 wg[D][NIT], wu[D][NIT];
-  auto issue = [&](int slot_unused, uint32_t t, u4 (&g)[NIT], u4 (&u)[NIT]) {
-    (void)slot_unused;
-    if (t >= n_items) return;
-    const uint32_t er = t / npu, p = t % npu;
-    const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
-    const u4* gs = reinterpret_cast<const u4*>(gate0 + e * stride + uint64_t(p) * rb) + lane;
-    const u4* us = reinterpret_cast<const u4*>(up0 + e * stride + uint64_t(p) * rb) + lane;
-#pragma unroll
-    for (int j = 0; j < NIT; j++) {
-      g[j] = __builtin_nontemporal_load(gp(gs + 64 * j));
-      u[j] = __builtin_nontemporal_load(gp(us + 64 * j));
-    }
-  };
-#pragma unroll
-  for (int s = 0; s < D - 1; s++) issue(s, c.w + kNComp * s, wg[s], wu[s]);
-  for (uint32_t i0 = 0;; i0 += D) {
-#pragma unroll
-    for (int s = 0; s < D; s++) {
-      const uint32_t t = c.w + kNComp * (i0 + s);
-      if (t >= n_items) goto done;
-      issue((s + D - 1) % D, t + kNComp * (D - 1), wg[(s + D - 1) % D], wu[(s + D - 1) % D]);
-      const uint32_t er = t / npu, p = t % npu;
+  // With a ready queue (seg_rows[2] = q): the CU's slice covers all but the
+  // last nsel / q selected experts, whose rows are handed out at run time in
+  // chunks of seg_stride[2] rows, each to whichever wave of an F_QUEUE
+  // instruction asks first.
+  const uint32_t q = I->seg_rows[2];
+  const uint32_t nq = q ? nsel / q : 0u, n_static = (nsel - nq) * npu;
+  // n items of this wave, item j = (selected-expert rank, FFN row), with
+  // the rows of the next D - 1 items in flight while one is computed
+  auto run = [&](uint32_t n, auto item) {
+    u4 wg[D][NIT], wu[D][NIT];
+    auto issue = [&](uint32_t j, u4 (&g)[NIT], u4 (&u)[NIT]) {
+      if (j >= n) return;
+      uint32_t er, row;
+      item(j, er, row);
       const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
-      const uint32_t tm = uni(rt_u8(rt, RT_TOK + int(e)));
-      float acc[16];
+      const u4* gs = reinterpret_cast<const u4*>(gate0 + e * stride + uint64_t(row) * rb) + lane;
+      const u4* us = reinterpret_cast<const u4*>(up0 + e * stride + uint64_t(row) * rb) + lane;
 #pragma unroll
-      for (int q = 0; q < 16; q++) acc[q] = 0.f;
+      for (int jj = 0; jj < NIT; jj++) {
+        g[jj] = __builtin_nontemporal_load(gp(gs + 64 * jj));
+        u[jj] = __builtin_nontemporal_load(gp(us + 64 * jj));
+      }
+    };
 #pragma unroll
-      for (int j = 0; j < NIT; j++) {
+    for (int s = 0; s < D - 1; s++) issue(uint32_t(s), wg[s], wu[s]);
+    for (uint32_t i0 = 0;; i0 += D) {
 #pragma unroll
-        for (int b = 0; b < lb::kMaxB; b++) {
-          if (!((tm >> b) & 1)) continue;
-          float x[8];
-          x8_ld(xs + uint32_t(b) * K + j * 512 + lane * 8, x);
-          acc[b] += dot8(wg[s][j], x);
-          acc[8 + b] += dot8(wu[s][j], x);
+      for (int s = 0; s < D; s++) {
+        const uint32_t j = i0 + uint32_t(s);
+        if (j >= n) return;
+        issue(j + D - 1, wg[(s + D - 1) % D], wu[(s + D - 1) % D]);
+        uint32_t er, row;
+        item(j, er, row);
+        const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
+        const uint32_t tm = uni(rt_u8(rt, RT_TOK + int(e)));
+        float acc[16];
+#pragma unroll
+        for (int qq = 0; qq < 16; qq++) acc[qq] = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < NIT; jj++) {
+#pragma unroll
+          for (int b = 0; b < lb::kMaxB; b++) {
+            if (!((tm >> b) & 1)) continue;
+            float x[8];
+            x8_ld(xs + uint32_t(b) * K + jj * 512 + lane * 8, x);
+            acc[b] += dot8(wg[s][jj], x);
+            acc[8 + b] += dot8(wu[s][jj], x);
+          }
+        }
+        const float sv = reduce16(acc);
+        const float upv = __shfl(sv, int((lane & 7) + 8), 64);
+        if (lane < 8 && ((tm >> lane) & 1)) {
+          const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + lane));
+          const float m = silu(sv * my_inv) * (upv * my_inv);
+          st_act(out + (size_t(lane) * k + slot) * Fe + row, m);
         }
       }
-      const float sv = reduce16(acc);
-      const float upv = __shfl(sv, int((lane & 7) + 8), 64);
-      if (lane < 8 && ((tm >> lane) & 1)) {
-        const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + lane));
-        const float m = silu(sv * my_inv) * (upv * my_inv);
-        st_act(out + (size_t(lane) * k + slot) * Fe + I->row0 + p, m);
-      }
+    }
+  };
+  // the CU's slice: items t = w, w + kNComp, ... of (rank, pair) in rank order
+  const uint32_t n_mine = uint32_t(c.w) < n_static ? (n_static - c.w + kNComp - 1) / kNComp : 0u;
+  run(n_mine, [&](uint32_t j, uint32_t& er, uint32_t& row) {
+    const uint32_t t = uint32_t(c.w) + kNComp * j;
+    er = t / npu;
+    row = I->row0 + t % npu;
+  });
+  if (nq && (i_flags(I) & F_QUEUE)) {
+    const uint32_t ck = I->seg_stride[2], per_e = Fe / ck, n_chunks = nq * per_e;
+    uint32_t* ctr = reinterpret_cast<uint32_t*>(I->res_ptr) + 2 + (c.ep & 1);
+    for (;;) {
+      uint32_t ch = 0;
+      if (lane == 0) ch = __hip_atomic_fetch_add(gp(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ch = uni(ch);
+      if (ch >= n_chunks) break;
+      const uint32_t er0 = nsel - nq + ch / per_e, p0 = (ch % per_e) * ck;
+      run(ck, [&](uint32_t j, uint32_t& er, uint32_t& row) {
+        er = er0;
+        row = p0 + j;
+      });
     }
   }
-done:
   if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
   return true;
 }
@@ -1134,11 +1167,11 @@ DEV bool erd(Comp& c, InstrCP I, uint32_t i) {
   const __amdgpu_buffer_rsrc_t ry = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), nB * k * d * kActBytes);
   const __amdgpu_buffer_rsrc_t rh = act_rsrc(reinterpret_cast<const void*>(I->res_ptr), nB * d * kActBytes);
   uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
-  // one CU clears the layer's ready-queue counter of the next step (this
-  // step's expert down projections use the other one)
-  if (I->seg_ptr[0] && c.w == 0 && lane == 0)
-    __hip_atomic_store(gp(reinterpret_cast<uint32_t*>(I->seg_ptr[0])) + ((c.ep + 1) & 1), 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  // one CU clears the layer's ready-queue counters of the next step (the
+  // down projection's and the gate/up's; this step uses the other pair)
+  if (I->seg_ptr[0] && c.w == 0 && lane < 2)
+    __hip_atomic_store(gp(reinterpret_cast<uint32_t*>(I->seg_ptr[0])) + 2 * lane + ((c.ep + 1) & 1), 0u,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (uint32_t base = uint32_t(c.w) * 64; base < total; base += 64 * kNComp) {
     const uint32_t idx = base + lane, on = idx < total;
     const uint32_t b = on ? idx / nr : 0, r = on ? idx % nr : 0, row = r0 + r;

@@ -219,6 +219,10 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
     // queue 4618 us per step)
     if (r.edn_queue == 0) r.edn_queue = 8;
     if (r.edn_queue < 0 || r.edn_queue == 1) r.edn_queue = 0;
+    // no gate/up ready queue by default: measured on the MoE shape, none
+    // 4242, 1/16 4357, 1/8 4509 and 1/4 4748 us per step (a chunk costs
+    // its wave a pipeline restart and an atomic round trip)
+    if (r.egu_queue <= 1) r.egu_queue = 0;
     if (r.attn_block <= 0) {
       // K and V blocks of a tile in four of the five ring pages, scores in
       // the scratch, whole KV groups per tile
@@ -275,6 +279,7 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
   // batch 1: no matrix-core tiles (the GEMVs are a single column)
   r.mfma = -1;
   r.edn_queue = 0;
+  r.egu_queue = 0;
   if (r.watchdog_ms <= 0) r.watchdog_ms = 2000;
   return r;
 }
@@ -308,7 +313,7 @@ ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
   // expert outputs [B][top_k][d] of the layer being computed (one buffer for
   // every layer: its tags carry the layer as well as the step)
   a.y = is_batched(c) ? take(E * B * uint64_t(c.top_k) * c.hidden) : 0;
-  a.edn_ctr = is_batched(c) ? take(8ull * c.n_layers) : 0;
+  a.edn_ctr = is_batched(c) ? take(16ull * c.n_layers) : 0;
   a.tok = take(E * B);
   a.rope_cos = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
   a.rope_sin = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
@@ -471,6 +476,9 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
   // pairs of an expert gate/up instruction (each pair is a gate row and an up
   // row side by side in the page stream): a slice of at most four pages
   const int max_pairs = std::max(1, 4 * kPageBytes / (4 * d));
+  // gate/up ready-queue chunks: about 32 KiB of gate and up rows
+  int egu_chunk = std::max(1, 32768 / (4 * d));
+  while (Fe % egu_chunk) egu_chunk /= 2;
 
   for (int l = 0; l < L; l++) {
     const int stg = l * ST_PER_LAYER;
@@ -614,6 +622,14 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.wait_ctr[0] = c_rt[l];
         I.sig_ctr = c_gu[l];
         I.n_pages = direct ? 0 : uint32_t(E * ppe);
+        if (direct && o.egu_queue > 1) {
+          // the last 1/q of the selected experts in the ready queue, in
+          // chunks of egu_chunk rows; the CU's last instruction drains it
+          I.seg_rows[2] = uint32_t(o.egu_queue);
+          I.seg_stride[2] = uint32_t(egu_chunk);
+          I.res_ptr = A + ar.edn_ctr + 16ull * l;
+          if (p1 == f1) I.flags |= F_QUEUE;
+        }
         InstrMeta m;
         m.stage = stg + ST_ATTN;
         m.merge_write = false;
@@ -685,7 +701,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.seg_rows[0] = uint32_t(Rb * 2 * Fe);
         I.in_ptr = A + ar.m[l];
         I.out_ptr = A + ar.y;
-        I.res_ptr = A + ar.edn_ctr + 8ull * l;  // the layer's ready-queue counters
+        I.res_ptr = A + ar.edn_ctr + 16ull * l;  // the layer's ready-queue counters
         I.row0 = uint32_t(std::max(0, o.edn_queue));
         I.wait_ctr[0] = c_gu[l];
         I.sig_ctr = c_dny[l];
@@ -719,7 +735,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.in_ptr = A + ar.y;
         I.res_ptr = A + ar.h[l];
         I.out_ptr = A + ar.x[l + 1];
-        if (r0 == 0) I.seg_ptr[0] = A + ar.edn_ctr + 8ull * l;  // clears the next step's counter
+        if (r0 == 0) I.seg_ptr[0] = A + ar.edn_ctr + 16ull * l;  // clears the next step's counters
         I.wait_ctr[0] = c_dny[l];
         I.wait_ctr[1] = c_o[l];
         I.sig_ctr = c_dn[l];
@@ -1449,6 +1465,10 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
           return fail("expert page budget");
         if ((I.flags & F_DIRECT) && (I.nit != 1 && I.nit != 2 && I.nit != 4)) return fail("direct expert loads");
         if (I.seg_rows[0] != I.aux[3] * I.row_bytes) return fail("expert gate/up runs");
+        if (I.seg_rows[2] && (!(I.flags & F_DIRECT) || I.seg_rows[2] < 2 || !I.seg_stride[2] ||
+                              uint32_t(c.expert_ffn) % I.seg_stride[2]))
+          return fail("expert gate/up ready queue");
+        if ((I.flags & F_QUEUE) && !I.seg_rows[2]) return fail("expert gate/up ready queue");
         continue;
       }
       if (I.op == OP_EDN) {
@@ -1690,6 +1710,14 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
             if (!inside(lo, lo + (NE - 1) * stride + run)) return fail("expert runs outside the expert tensors");
           }
           if (I.row0 + I.aux[3] > Fe) return fail("expert gate/up slice");
+          if (I.seg_rows[2]) {
+            // queued chunks: any row of the expert tensors
+            for (int r = 0; r < 2; r++) {
+              const uint64_t lo = I.seg_ptr[1 + r] - uint64_t(I.row0) * I.row_bytes;
+              if (!inside(lo, lo + (NE - 1) * stride + Fe * I.row_bytes)) return fail("queued expert rows");
+            }
+            if (!in_arena(I.res_ptr, I.res_ptr + 16)) return fail("ready-queue counters outside the arena");
+          }
           if (!(I.flags & F_IN_EMBED) && !in_arena(I.in_ptr, I.in_ptr + EB * NB * d))
             return fail("expert input outside the arena");
           if (!in_arena(I.out_ptr, I.out_ptr + mb)) return fail("expert intermediate outside the arena");
@@ -1700,14 +1728,14 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
             return fail("expert units outside the expert tensors");
           if (!in_arena(I.in_ptr, I.in_ptr + mb)) return fail("expert intermediate outside the arena");
           if (!in_arena(I.out_ptr, I.out_ptr + EB * NB * c.top_k * d)) return fail("expert outputs outside the arena");
-          if (!in_arena(I.res_ptr, I.res_ptr + 8)) return fail("ready-queue counters outside the arena");
+          if (!in_arena(I.res_ptr, I.res_ptr + 16)) return fail("ready-queue counters outside the arena");
         }
         continue;
       }
       if (I.op == OP_ERD) {
         const uint64_t rl = (NB - 1) * d + I.row0 + I.n_rows;
         if (!in_arena(I.in_ptr, I.in_ptr + EB * NB * c.top_k * d) || !in_arena(I.res_ptr, I.res_ptr + EB * rl) ||
-            !in_arena(I.out_ptr, I.out_ptr + EB * rl) || (I.seg_ptr[0] && !in_arena(I.seg_ptr[0], I.seg_ptr[0] + 8)))
+            !in_arena(I.out_ptr, I.out_ptr + EB * rl) || (I.seg_ptr[0] && !in_arena(I.seg_ptr[0], I.seg_ptr[0] + 16)))
           return fail("expert sum rows outside the arena");
         continue;
       }
