@@ -937,6 +937,7 @@ DEV bool egu_direct(Comp& c, InstrCP I, uint32_t i) {
   const uint64_t stride = I->seg_stride[0];
   // row 0 of expert 0's gate and up matrices
   const uint64_t gate0 = I->seg_ptr[1] - uint64_t(I->row0) * rb, up0 = I->seg_ptr[2] - uint64_t(I->row0) * rb;
+  const uint64_t zero = uint64_t(a.zero_page);
   const float inv = inv_rms(a, I);
   const float my_inv = __shfl(inv, int(lane & 7), 64);
   const float* xs = reinterpret_cast<const float*>(lds + lb::kX);
@@ -951,13 +952,20 @@ DEV bool egu_direct(Comp& c, InstrCP I, uint32_t i) {
   // the rows of the next D - 1 items in flight while one is computed
   auto run = [&](uint32_t n, auto item) {
     u4 wg[D][NIT], wu[D][NIT];
+    // Every call issues the same loads (items past the end read the zero
+    // page), so that the wait before an item's use counts exactly the loads
+    // issued after it and the next items stay in flight.
     auto issue = [&](uint32_t j, u4 (&g)[NIT], u4 (&u)[NIT]) {
-      if (j >= n) return;
-      uint32_t er, row;
-      item(j, er, row);
-      const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
-      const u4* gs = reinterpret_cast<const u4*>(gate0 + e * stride + uint64_t(row) * rb) + lane;
-      const u4* us = reinterpret_cast<const u4*>(up0 + e * stride + uint64_t(row) * rb) + lane;
+      uint64_t ga = zero, ua = zero;
+      if (j < n) {
+        uint32_t er, row;
+        item(j, er, row);
+        const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
+        ga = gate0 + e * stride + uint64_t(row) * rb;
+        ua = up0 + e * stride + uint64_t(row) * rb;
+      }
+      const u4* gs = reinterpret_cast<const u4*>(ga) + lane;
+      const u4* us = reinterpret_cast<const u4*>(ua) + lane;
 #pragma unroll
       for (int jj = 0; jj < NIT; jj++) {
         g[jj] = __builtin_nontemporal_load(gp(gs + 64 * jj));
@@ -1033,6 +1041,95 @@ DEV bool egu_direct(Comp& c, InstrCP I, uint32_t i) {
 // need one group).  Items are (unit,
 // block of four rows); an item applies its rows to every sequence routed to
 // the unit's expert and stores y[b][slot of the expert in b's top-k][row].
+// The items of units [ua, ub) of an expert down projection, loaded by the
+// compute waves themselves: item t = (unit, block of four rows) goes to wave
+// t mod kNComp; its rows (DN 1 KiB units each) are loaded two items ahead.
+// The routed sequences of the item's expert are taken four at a time (one
+// pass covers the usual case); the experts' routed inputs are in the x slot
+// from pair p0 on.
+template <int DN>
+DEV void edn_items_direct(Comp& c, InstrCP I, uint32_t ua, uint32_t ub, uint32_t p0, const float* xs,
+                          uint64_t* yout, uint32_t ytag) {
+  constexpr int D = 3;
+  const KArgs& a = *c.a;
+  const uint32_t lane = c.lane, K = I->k, Rb = I->aux[3], nb = I->aux[4], d = uint32_t(a.hidden);
+  const uint32_t k = uint32_t(a.top_k), rbytes = I->row_bytes;
+  const uint64_t stride = I->seg_stride[0], w0 = I->seg_ptr[1];
+  const int rt = rt_base(I->layer);
+  const uint32_t nrb = (Rb + 3) / 4, n_items = (ub - ua) * nrb;
+  const uint32_t n = uint32_t(c.w) < n_items ? (n_items - uint32_t(c.w) + kNComp - 1) / kNComp : 0u;
+  // Every call issues the same loads (items past the end read the zero
+  // page, a row past the unit's last re-reads that row, its sums unused), so
+  // that the wait before an item's use counts exactly the loads issued after
+  // it and the next items stay in flight.
+  const uint64_t zero = uint64_t(a.zero_page);
+  u4 wr[D][4][DN];
+  // (selects, not branches: the loads must not sit in conditional blocks)
+  auto issue = [&](uint32_t j, u4 (&w)[4][DN]) {
+    const bool ok = j < n;
+    const uint32_t it = uint32_t(c.w) + kNComp * (ok ? j : 0u);
+    const uint32_t u = ua + it / nrb, r0 = 4 * (it % nrb), rb = u % nb;
+    const uint32_t er = ok ? u / nb : 0u, rows = min(Rb, d - rb * Rb);
+    const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
+    const uint64_t src = ok ? w0 + e * stride + uint64_t(rb * Rb) * rbytes : zero;
+    const uint32_t step = ok ? rbytes : 0u;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const uint64_t rs = src + uint64_t(min(r0 + uint32_t(r), rows - 1) * step);
+#pragma unroll
+      for (int jj = 0; jj < DN; jj++) w[r][jj] = __builtin_nontemporal_load(gp(reinterpret_cast<const u4*>(rs) + lane + 64 * jj));
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < D - 1; s++) issue(uint32_t(s), wr[s]);
+  for (uint32_t i0 = 0;; i0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; s++) {
+      const uint32_t j = i0 + uint32_t(s);
+      if (j >= n) return;
+      issue(j + D - 1, wr[(s + D - 1) % D]);
+      const uint32_t it = uint32_t(c.w) + kNComp * j;
+      const uint32_t u = ua + it / nrb, r0 = 4 * (it % nrb), er = u / nb, rb = u % nb;
+      const uint32_t rows = min(Rb, d - rb * Rb);
+      const uint32_t e = uni(rt_u8(rt, RT_LIST + int(er)));
+      const uint32_t tok = uni(rt_u8(rt, RT_TOK + int(e)));
+      const uint32_t base = uni(rt_u8(rt, RT_PBASE + int(er))) - p0;
+      const uint32_t nt = uint32_t(__builtin_popcount(tok));
+      for (uint32_t p = 0; p < nt; p += 4) {
+        // acc[4 r + q] = row r . x of the routed sequence of rank p + q
+        float acc[16];
+#pragma unroll
+        for (int q = 0; q < 16; q++) acc[q] = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < DN; jj++) {
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            if (p + q >= nt) continue;
+            float x[8];
+            x8_ld(xs + (base + p + uint32_t(q)) * K + jj * 512 + lane * 8, x);
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[4 * r + q] += dot8(wr[s][r][jj], x);
+          }
+        }
+        // lane l < 16 holds the sum of acc[l]: row l / 4, rank p + l % 4
+        const float sdot = reduce16(acc);
+        const uint32_t rr = lane >> 2, rank = p + (lane & 3);
+        if (lane < 16 && rank < nt && r0 + rr < rows) {
+          uint32_t m = tok;
+          for (uint32_t t = 0; t < rank; t++) m &= m - 1;
+          const uint32_t bb = uint32_t(__builtin_ctz(m));
+          const uint32_t slot = rt_u8(rt, RT_SLOT + int(e * 8 + bb));
+          st_tag(yout + size_t(bb * k + slot) * d + rb * Rb + r0 + rr, sdot, ytag);
+        }
+      }
+    }
+  }
+}
+
+// DN = 0: the loader streams the units through the page ring; DN = 1, 2
+// (F_DIRECT, DN = 1 KiB units per row): each compute wave loads its own
+// rows, three items in flight, and wave 0 takes the ready-queue chunks.
+template <int DN>
 DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg, uint32_t& np) {
   const KArgs& a = *c.a;
   const uint32_t lane = c.lane, K = I->k, nit = i_nit(I), nB = uint32_t(a.batch);
@@ -1098,6 +1195,12 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg, uint32_t& np) {
       }
       const uint32_t ua = max(u_lo, g0 * nb), ub = min(u_hi, (g1 + 1) * nb);
       const uint32_t n_items = (ub - ua) * nrb;
+      if constexpr (DN > 0) {
+        edn_items_direct<DN>(c, I, ua, ub, p0, xs, yout, ytag);
+        if (g1 >= er_last) return true;
+        g0 = g1 + 1;
+        continue;
+      }
       for (uint32_t it = c.w; it < n_items; it += kNComp) {
         const uint32_t u = ua + it / nrb, r0 = 4 * (it % nrb);
         const uint32_t er = u / nb, rb = u % nb;
@@ -1135,16 +1238,26 @@ DEV bool edn(Comp& c, InstrCP I, uint32_t i, uint32_t pg, uint32_t& np) {
     if (!run_units(u_lo, u_hi, 0)) return false;
     pofs = (u_hi - u_lo) * ppu;
   }
-  // then the chunks the loader took from the ready queue, in its order
+  // then the chunks the loader (direct: compute wave 0) took from the ready
+  // queue, in its order
   for (uint32_t q = 0; I->row0; q++) {
-    uint32_t ch;
-    if (!dyn_entry(I->layer, q, ch)) return false;
+    uint32_t ch = 0;
+    if (DN > 0 && c.w == 0) {
+      if (lane == 0)
+        ch = __hip_atomic_fetch_add(gp(reinterpret_cast<uint32_t*>(I->res_ptr)) + (c.ep & 1), 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+      ch = min(uni(ch), 0xFFFFu);
+      if (lane == 0) lds_st(dyn_slot(I->layer, q), (I->layer + 1) << 16 | ch);
+    } else if (!dyn_entry(I->layer, q, ch)) {
+      return false;
+    }
     if (ch >= sp.n_dyn) break;
     const uint32_t u0 = sp.Ts + ch * sp.uc, u1 = min(sp.T, u0 + sp.uc);
     if (!run_units(u0, u1, pofs)) return false;
     pofs += (u1 - u0) * ppu;
   }
   if (trl) trace_put(a, c.cu, i, TR_A_STATS, now32());
+  if constexpr (DN > 0) pofs = 0;
   if (lane == 0) {
     lds_st(C_RELEASED + 4 * c.w, pg + pofs);
     lds_st(C_XCONS + 4 * c.w, i + 1);
@@ -1399,7 +1512,11 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       // have read the previous instruction's inputs
       staged = kNoCounter;
       last_sync = i;
-      ok = op == OP_EDN ? edn(c, I, i, pg, np) : run_attn_b<G>(c, I, i, pg);
+      if (op == OP_EDN)
+        ok = !(i_flags(I) & F_DIRECT) ? edn<0>(c, I, i, pg, np)
+                                       : i_nit(I) == 2 ? edn<2>(c, I, i, pg, np) : edn<1>(c, I, i, pg, np);
+      else
+        ok = run_attn_b<G>(c, I, i, pg);
     }
     if (!ok) {
       if (c.lane == 0) lds_st(C_ABORT, 1);

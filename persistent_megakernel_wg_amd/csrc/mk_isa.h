@@ -112,8 +112,8 @@ enum Flag : uint16_t {
   F_OWN_POS = 32,     // (attention) placeholder, decided at run time
   F_ROUTE = 64,       // (experts) first expert instruction of its layer on the CU:
                       // take the top-k routing decision from the router logits
-  F_DIRECT = 128,     // (expert gate/up) the compute waves load the weight rows
-                      // themselves; the instruction takes no LDS pages
+  F_DIRECT = 128,     // (expert gate/up and down) the compute waves load the
+                      // weight rows themselves; the instruction takes no LDS pages
   F_DEBUG_STALL = 256,  // tests only: staging expects the next step's tag, so the
                         // inputs never turn fresh and the watchdog ends the step
   F_MFMA = 512,         // (batched GEMV) matrix-core tiles of 16 rows: the input
@@ -220,7 +220,10 @@ struct PackCopy {
 //   seg_stride[0] = bytes between experts; seg_rows[0] = bytes of a full unit
 //   in_ptr = m [B][top_k][Fe]; out_ptr = y [B][top_k][d], tagged with
 //   (step << 7) | layer
-//   n_pages = the most pages a CU can take (the loader streams the CU's units)
+//   n_pages = the most pages a CU can take (the loader streams the CU's units),
+//   or 0 with F_DIRECT (rows of at most 2 KiB: the compute waves load them)
+//   row0 = q > 0: a 1/q share of the units waits in the ready queue, handed
+//   out in chunks by the counter at res_ptr + 4 (step parity)
 // Expert sum (OP_ERD): rows row0 .. row0 + n_rows of x_{l+1} for every sequence:
 //   in_ptr = y, res_ptr = h, out_ptr = x_{l+1}
 

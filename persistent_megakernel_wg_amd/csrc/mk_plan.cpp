@@ -685,7 +685,9 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.nit = uint8_t(Fe / 512);
         I.rpu = 1;
         I.layer = uint16_t(l);
-        I.flags = F_SIGNAL | (routed[cu] ? 0 : F_ROUTE);
+        // rows of at most 2 KiB are loaded by the compute waves directly
+        const bool direct = Fe / 512 <= 2;
+        I.flags = F_SIGNAL | (routed[cu] ? 0 : F_ROUTE) | (direct ? F_DIRECT : 0);
         routed[cu] = 1;
         I.n_items = uint32_t(C);
         I.row_bytes = uint32_t(2 * Fe);
@@ -706,7 +708,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.wait_ctr[0] = c_gu[l];
         I.sig_ctr = c_dny[l];
         // at most every unit (the static share and the queue's chunks)
-        I.n_pages = uint32_t(E * nb * ppu);
+        I.n_pages = direct ? 0 : uint32_t(E * nb * ppu);
         InstrMeta m;
         m.stage = stg + ST_DOWN;
         // every unit's writes are decided by the routing: the tiles share
@@ -1484,7 +1486,9 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         if (uint32_t(ceil_div(4 * I.row_bytes, kPageBytes)) + 1 > uint32_t(lb::kPages) ||
             uint64_t(c.batch) * I.k > uint64_t(lb::kXFloats))
           return fail("expert down-projection items");
-        if (I.n_items != uint32_t(C) || I.n_pages != uint32_t(c.n_experts) * nb * ppu || (I.flags & F_DIRECT))
+        if (I.n_items != uint32_t(C) ||
+            I.n_pages != ((I.flags & F_DIRECT) ? 0u : uint32_t(c.n_experts) * nb * ppu) ||
+            ((I.flags & F_DIRECT) && I.nit > 2))
           return fail("expert down-projection page budget");
         continue;
       }
