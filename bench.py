@@ -184,8 +184,8 @@ def main() -> int:
                     help="batched decoder: 1: LM head on matrix cores; -1: vector ALUs; 0: default")
     ap.add_argument("--edn-queue", type=int, default=0,
                     help="MoE decoder: q > 1: a 1/q share of the expert down-projection units in a ready queue")
-    ap.add_argument("--egu-queue", type=int, default=0,
-                    help="MoE decoder: q > 1: the gate/up rows of the last 1/q of the selected experts in a ready queue")
+    ap.add_argument("--egu-balance", type=int, default=0,
+                    help="MoE decoder: 1: gate/up shares weighted by each CU's earlier work; -1: even row slices")
     ap.add_argument("--o-split", type=int, default=0,
                     help="1: O projection split per KV group; -1: whole rows; 0: the plan's default")
     ap.add_argument("--launch", choices=("resident", "single"), default="resident",
@@ -215,7 +215,7 @@ def main() -> int:
                  plan=B.plan_opts(n_cus=args.n_cus, attn_block=args.attn_block,
                                   mlp_chunks=args.mlp_chunks, o_split=args.o_split, mfma=args.mfma,
                                   edn_queue=args.edn_queue,
-                                  egu_queue=args.egu_queue))
+                                  egu_balance=args.egu_balance))
     info = eng.plan_info()
     dev = eng.dev
     stream = torch.cuda.current_stream(dev)

@@ -149,11 +149,12 @@ typedef struct {
                          asks first: Cohere's «快在哪里» item 1), the rest split
                          evenly over the CUs; -1 = every unit split evenly.
                          Default: 8 */
-  int32_t egu_queue;  /* MoE decoder: q > 1 = the gate/up rows of the last
-                         1/q of each layer's selected experts wait in a
-                         ready queue, in chunks that the CUs' compute waves
-                         take once their own slices are done; -1 = every
-                         expert's rows split evenly over the CUs (default) */
+  int32_t egu_balance; /* MoE decoder with gate/up rows of at most 4 KiB:
+                          1 = each CU takes a share of the layer's (expert,
+                          row) gate/up items sized so that its attention
+                          and router tiles plus its share take about the
+                          same time on every CU; -1 = an even slice of
+                          every selected expert's rows per CU (default) */
 } mk_plan_opts;
 
 /* Plan summary (filled by mk_plan_info / mk_plan_check). */

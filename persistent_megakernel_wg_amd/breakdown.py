@@ -1,7 +1,7 @@
 """Per-stage time breakdown of one decode step from the kernel's own trace.
 
     python -m persistent_megakernel_wg_amd.breakdown [--workload llama1b_ctx128]
-        [--steps 4] [--json out.json] [--o-split 1] [--mfma 1]
+        [--steps 4] [--json out.json] [--o-split 1] [--mfma 1] [--egu-balance 1]
 
 Runs a few steps of the workload on the GPU with the per-instruction trace
 switched on (mk_trace_enable: s_memrealtime stamps, 100 MHz, written by each
@@ -168,6 +168,8 @@ def main() -> int:
     ap.add_argument("--json", default="")
     ap.add_argument("--o-split", type=int, default=0,
                     help="1: O projection split per KV group; -1: whole rows; 0: the plan's default")
+    ap.add_argument("--egu-balance", type=int, default=0,
+                    help="MoE decoder: 1: weighted gate/up shares; -1: even row slices")
     ap.add_argument("--mfma", type=int, default=0,
                     help="batched decoder: 1: LM head on matrix cores; -1: vector ALUs; 0: default")
     args = ap.parse_args()
@@ -178,7 +180,8 @@ def main() -> int:
     w = synth.make_weights(s)
     kc, vc = synth.make_kv_cache(s)
     tok = synth.make_tokens(s)
-    opts = B.plan_opts(o_split=args.o_split, mfma=args.mfma) if (args.o_split or args.mfma) else None
+    opts = (B.plan_opts(o_split=args.o_split, mfma=args.mfma, egu_balance=args.egu_balance)
+            if (args.o_split or args.mfma or args.egu_balance) else None)
     eng = Engine(s, w, kc, vc, plan=opts)
     try:
         info = eng.plan_info()

@@ -942,12 +942,6 @@ DEV bool egu_direct(Comp& c, InstrCP I, uint32_t i) {
   const float my_inv = __shfl(inv, int(lane & 7), 64);
   const float* xs = reinterpret_cast<const float*>(lds + lb::kX);
   float* out = reinterpret_cast<float*>(I->out_ptr);
-  // With a ready queue (seg_rows[2] = q): the CU's slice covers all but the
-  // last nsel / q selected experts, whose rows are handed out at run time in
-  // chunks of seg_stride[2] rows, each to whichever wave of an F_QUEUE
-  // instruction asks first.
-  const uint32_t q = I->seg_rows[2];
-  const uint32_t nq = q ? nsel / q : 0u, n_static = (nsel - nq) * npu;
   // n items of this wave, item j = (selected-expert rank, FFN row), with
   // the rows of the next D - 1 items in flight while one is computed
   auto run = [&](uint32_t n, auto item) {
@@ -1008,27 +1002,27 @@ DEV bool egu_direct(Comp& c, InstrCP I, uint32_t i) {
       }
     }
   };
-  // the CU's slice: items t = w, w + kNComp, ... of (rank, pair) in rank order
-  const uint32_t n_mine = uint32_t(c.w) < n_static ? (n_static - c.w + kNComp - 1) / kNComp : 0u;
-  run(n_mine, [&](uint32_t j, uint32_t& er, uint32_t& row) {
-    const uint32_t t = uint32_t(c.w) + kNComp * j;
-    er = t / npu;
-    row = I->row0 + t % npu;
-  });
-  if (nq && (i_flags(I) & F_QUEUE)) {
-    const uint32_t ck = I->seg_stride[2], per_e = Fe / ck, n_chunks = nq * per_e;
-    uint32_t* ctr = reinterpret_cast<uint32_t*>(I->res_ptr) + 2 + (c.ep & 1);
-    for (;;) {
-      uint32_t ch = 0;
-      if (lane == 0) ch = __hip_atomic_fetch_add(gp(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ch = uni(ch);
-      if (ch >= n_chunks) break;
-      const uint32_t er0 = nsel - nq + ch / per_e, p0 = (ch % per_e) * ck;
-      run(ck, [&](uint32_t j, uint32_t& er, uint32_t& row) {
-        er = er0;
-        row = p0 + j;
-      });
-    }
+  if (i_flags(I) & F_SHARE) {
+    // the CU's share [g0, g1) of the (rank, row) items in rank order; item
+    // g0 + t goes to wave t mod kNComp
+    const uint64_t T = uint64_t(nsel) * Fe;
+    const uint32_t g0 = uint32_t((T * I->seg_rows[1]) >> 16), g1 = uint32_t((T * I->seg_rows[2]) >> 16);
+    const uint32_t n_mine = g0 + uint32_t(c.w) < g1 ? (g1 - g0 - c.w + kNComp - 1) / kNComp : 0u;
+    run(n_mine, [&](uint32_t j, uint32_t& er, uint32_t& row) {
+      const uint32_t g = g0 + uint32_t(c.w) + kNComp * j;
+      er = g / Fe;
+      row = g % Fe;
+    });
+  } else {
+    // the CU's slice of every expert: items t = w, w + kNComp, ... of
+    // (rank, pair) in rank order
+    const uint32_t n_static = nsel * npu;
+    const uint32_t n_mine = uint32_t(c.w) < n_static ? (n_static - c.w + kNComp - 1) / kNComp : 0u;
+    run(n_mine, [&](uint32_t j, uint32_t& er, uint32_t& row) {
+      const uint32_t t = uint32_t(c.w) + kNComp * j;
+      er = t / npu;
+      row = I->row0 + t % npu;
+    });
   }
   if (lane == 0) lds_st(C_XCONS + 4 * c.w, i + 1);
   return true;
@@ -1280,11 +1274,11 @@ DEV bool erd(Comp& c, InstrCP I, uint32_t i) {
   const __amdgpu_buffer_rsrc_t ry = act_rsrc(reinterpret_cast<const void*>(I->in_ptr), nB * k * d * kActBytes);
   const __amdgpu_buffer_rsrc_t rh = act_rsrc(reinterpret_cast<const void*>(I->res_ptr), nB * d * kActBytes);
   uint64_t* out = reinterpret_cast<uint64_t*>(I->out_ptr);
-  // one CU clears the layer's ready-queue counters of the next step (the
-  // down projection's and the gate/up's; this step uses the other pair)
-  if (I->seg_ptr[0] && c.w == 0 && lane < 2)
-    __hip_atomic_store(gp(reinterpret_cast<uint32_t*>(I->seg_ptr[0])) + 2 * lane + ((c.ep + 1) & 1), 0u,
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // one CU clears the layer's ready-queue counter of the next step (this
+  // step's expert down projections use the other one)
+  if (I->seg_ptr[0] && c.w == 0 && lane == 0)
+    __hip_atomic_store(gp(reinterpret_cast<uint32_t*>(I->seg_ptr[0])) + ((c.ep + 1) & 1), 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   for (uint32_t base = uint32_t(c.w) * 64; base < total; base += 64 * kNComp) {
     const uint32_t idx = base + lane, on = idx < total;
     const uint32_t b = on ? idx / nr : 0, r = on ? idx % nr : 0, row = r0 + r;

@@ -119,8 +119,8 @@ enum Flag : uint16_t {
   F_MFMA = 512,         // (batched GEMV) matrix-core tiles of 16 rows: the input
                         // is staged as bf16 hi + lo parts in MFMA operand order
                         // and the packed rows are in MFMA fragment order
-  F_QUEUE = 1024,       // (expert gate/up) the CU's last instruction of its layer:
-                        // after its slice it takes chunks from the ready queue
+  F_SHARE = 1024,       // (expert gate/up) a weighted share of the layer's (expert,
+                        // row) items instead of a slice of rows of every expert
 };
 
 constexpr uint32_t kNoCounter = 0xFFFFFFFFu;
@@ -207,10 +207,10 @@ struct PackCopy {
 //   seg_stride[0] = bytes between experts' runs; seg_rows[0] = bytes of a run
 //   seg_stride[1] = pages of the gate run within an expert region
 //   row0 = first FFN row of the slice; in_ptr = x; out_ptr = m [B][top_k][Fe]
-//   seg_rows[2] = q > 1: the last nsel / q selected experts are not in the
-//   slices but wait in a ready queue, in chunks of seg_stride[2] rows, that
-//   the F_QUEUE instructions drain; res_ptr = the layer's ready-queue
-//   counters [down p0, down p1, gate/up p0, gate/up p1] (p = step parity)
+//   F_SHARE (direct only): row0 = 0, seg_ptr[1], seg_ptr[2] = expert 0's
+//   first rows; the CU takes items [T s0, T s1) / 65536 of the T =
+//   (selected experts) x Fe (expert rank, row) items in that order, with
+//   s0 = seg_rows[1] and s1 = seg_rows[2]
 // Expert down projection (OP_EDN): units of n_rows (= aux[3]) consecutive
 // down rows of one selected expert; the U = (selected experts) x aux[4] units
 // of a layer, in expert order, go to the n_items CUs in even contiguous

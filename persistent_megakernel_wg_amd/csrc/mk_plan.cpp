@@ -219,10 +219,9 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
     // queue 4618 us per step)
     if (r.edn_queue == 0) r.edn_queue = 8;
     if (r.edn_queue < 0 || r.edn_queue == 1) r.edn_queue = 0;
-    // no gate/up ready queue by default: measured on the MoE shape, none
-    // 4242, 1/16 4357, 1/8 4509 and 1/4 4748 us per step (a chunk costs
-    // its wave a pipeline restart and an atomic round trip)
-    if (r.egu_queue <= 1) r.egu_queue = 0;
+    // even gate/up slices by default: the weighted shares measured slower
+    // on the MoE shape (4137 against 4001 us per step)
+    if (r.egu_balance == 0) r.egu_balance = -1;
     if (r.attn_block <= 0) {
       // K and V blocks of a tile in four of the five ring pages, scores in
       // the scratch, whole KV groups per tile
@@ -279,7 +278,7 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
   // batch 1: no matrix-core tiles (the GEMVs are a single column)
   r.mfma = -1;
   r.edn_queue = 0;
-  r.egu_queue = 0;
+  r.egu_balance = 0;
   if (r.watchdog_ms <= 0) r.watchdog_ms = 2000;
   return r;
 }
@@ -313,7 +312,7 @@ ArenaLayout arena_layout(const mk_config& c, int max_lm_tiles, int max_parts) {
   // expert outputs [B][top_k][d] of the layer being computed (one buffer for
   // every layer: its tags carry the layer as well as the step)
   a.y = is_batched(c) ? take(E * B * uint64_t(c.top_k) * c.hidden) : 0;
-  a.edn_ctr = is_batched(c) ? take(16ull * c.n_layers) : 0;
+  a.edn_ctr = is_batched(c) ? take(8ull * c.n_layers) : 0;
   a.tok = take(E * B);
   a.rope_cos = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
   a.rope_sin = take(4 * uint64_t(c.max_seq) * (c.head_dim / 2));
@@ -438,10 +437,15 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
   // so that the CUs that take one tile more take a light one.
   const int n_att = B * G * tpg * nblk;
   std::vector<int> att_cu_of(n_att);
+  const int n_rt = (E + 1) / 2;  // router tiles of two rows
+  auto rt_cu = [&](int t) { return int(int64_t(t) * C / n_rt); };
   {
     const bool split_last = nblk > 1;
     const int n_full = split_last ? B * G * tpg * (nblk - 1) : n_att, n_last = n_att - n_full;
+    // a router tile counts as a tile here, so that the light tiles avoid
+    // the CUs that compute the router
     std::vector<int> count(C, 0);
+    for (int t = 0; t < n_rt; t++) count[rt_cu(t)]++;
     int j = 0, k = 0;
     for (int a = 0; a < n_att; a++) {
       if (split_last && a % nblk == nblk - 1) continue;
@@ -470,15 +474,50 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
     }
   }
   auto att_cu = [&](int a) { return att_cu_of[a]; };
-  const int n_rt = (E + 1) / 2;  // router tiles of two rows
-  auto rt_cu = [&](int t) { return int(int64_t(t) * C / n_rt); };
+  // Gate/up shares: cumulative 1/65536 fractions of a layer's (expert, row)
+  // items per CU, so that the work each CU does before its gate/up items
+  // (attention tiles, router tiles) plus its items ends at about the same
+  // time everywhere.  The costs are MI355X measurements of this kernel: an
+  // attention tile ~12 us, a router tile ~6 us, gate/up rows streamed at
+  // ~27.5 GB/s per CU; the number of selected experts is its expectation
+  // for uniform routing.
+  std::vector<uint32_t> egu_cum;
+  {
+    constexpr double kAttnTileUs = 12.0, kRouterTileUs = 6.0, kCuBytesPerUs = 27500.0;
+    std::vector<double> pre(C, 0.0);
+    for (int a = 0; a < n_att; a++) pre[att_cu_of[a]] += kAttnTileUs;
+    for (int t = 0; t < n_rt; t++) pre[rt_cu(t)] += kRouterTileUs;
+    const double nsel = E * (1.0 - std::pow(1.0 - double(c.top_k) / E, B));
+    const double total = C * (nsel * Fe * 4.0 * d / C / kCuBytesPerUs);
+    // the level L with sum over CUs of max(0, L - pre) = total
+    std::vector<double> srt(pre);
+    std::sort(srt.begin(), srt.end());
+    double level = srt[0], acc = 0.0;
+    for (int i = 0; i < C; i++) {
+      const double next = i + 1 < C ? srt[i + 1] : 1e300;
+      // CUs 0..i are below the level: raising it to next adds (i + 1) (next - level)
+      if (acc + (i + 1) * (next - level) >= total) {
+        level += (total - acc) / (i + 1);
+        break;
+      }
+      acc += (i + 1) * (next - level);
+      level = next;
+    }
+    std::vector<double> w(C);
+    double sw = 0.0;
+    for (int cu = 0; cu < C; cu++) sw += (w[cu] = std::max(0.0, level - pre[cu]));
+    egu_cum.assign(C + 1, 0u);
+    double run = 0.0;
+    for (int cu = 0; cu < C; cu++) {
+      run += w[cu];
+      egu_cum[cu + 1] = cu + 1 == C ? 65536u : uint32_t(std::llround(65536.0 * run / sw));
+    }
+  }
+  auto egu_shares = [&](int) { return egu_cum; };
   const int max_res_rows = std::min(kMaxResRows / B, lb::kMaxDnRows);
   // pairs of an expert gate/up instruction (each pair is a gate row and an up
   // row side by side in the page stream): a slice of at most four pages
   const int max_pairs = std::max(1, 4 * kPageBytes / (4 * d));
-  // gate/up ready-queue chunks: about 32 KiB of gate and up rows
-  int egu_chunk = std::max(1, 32768 / (4 * d));
-  while (Fe % egu_chunk) egu_chunk /= 2;
 
   for (int l = 0; l < L; l++) {
     const int stg = l * ST_PER_LAYER;
@@ -584,7 +623,54 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
     }
     // ---------------------------------------------------------------- EGU
     std::vector<char> routed(C, 0);  // CU already has an expert instruction of this layer
-    for (int cu = 0; cu < C; cu++) {
+    // rows of at most 4 KiB are loaded by the compute waves directly
+    const bool egu_direct = d / 512 == 1 || d / 512 == 2 || d / 512 == 4;
+    if (egu_direct && o.egu_balance > 0) {
+      // Weighted shares: CU c takes items [T f_c, T f_{c+1}) of the T =
+      // (selected experts) x Fe (expert, row) items in expert order, its
+      // share cut so that its earlier work of the layer plus its gate/up
+      // items take about the same time on every CU.
+      const std::vector<uint32_t> cum = egu_shares(l);
+      for (int cu = 0; cu < C; cu++) {
+        Instr I = blank();
+        I.op = OP_EGU;
+        I.epi = EPI_SWIGLU;
+        I.nit = uint8_t(d / 512);
+        I.rpu = 1;
+        I.layer = uint16_t(l);
+        I.flags = F_NORM | F_SIGNAL | F_DIRECT | F_SHARE | (l == 0 ? F_IN_EMBED : 0) | (routed[cu] ? 0 : F_ROUTE);
+        routed[cu] = 1;
+        I.n_items = uint32_t(Fe);
+        I.row_bytes = uint32_t(2 * d);
+        I.n_rows = uint32_t(2 * Fe);
+        I.k = uint32_t(d);
+        I.aux[0] = c_rt[l];
+        I.aux[3] = uint32_t(Fe);
+        I.aux[4] = uint32_t(E);
+        I.seg_ptr[0] = A + ar.rl[l];
+        I.seg_ptr[1] = lptr(in.w.e_gate, l, uint64_t(E) * Fe * d);
+        I.seg_ptr[2] = lptr(in.w.e_up, l, uint64_t(E) * Fe * d);
+        I.seg_stride[0] = uint32_t(2ull * Fe * d);
+        I.seg_rows[0] = uint32_t(Fe * 2 * d);
+        I.seg_rows[1] = cum[cu];
+        I.seg_rows[2] = cum[cu + 1];
+        I.in_ptr = x_in;
+        I.out_ptr = A + ar.m[l];
+        I.gain_ptr = lptr(in.w.attn_norm, l, d);
+        I.wait_ctr[0] = c_rt[l];
+        I.sig_ctr = c_gu[l];
+        I.n_pages = 0;
+        InstrMeta m;
+        m.stage = stg + ST_ATTN;
+        // the rows a CU writes are decided by the routing
+        m.merge_write = true;
+        m.reads.push_back({x_buf, l, 0, uint64_t(B) * d});
+        m.reads.push_back({BUF_RL, l, 0, uint64_t(B) * E});
+        m.writes.push_back({BUF_M, l, 0, uint64_t(B) * c.top_k * Fe});
+        b.push(cu, I, std::move(m), int64_t((uint64_t(E) * Fe * 4 * d * (cum[cu + 1] - cum[cu])) >> 16));
+      }
+    }
+    for (int cu = 0; cu < C && !(egu_direct && o.egu_balance > 0); cu++) {
       int64_t f0, f1;
       split(Fe, cu, &f0, &f1);
       for (int64_t p0 = f0; p0 < f1; p0 += max_pairs) {
@@ -596,8 +682,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.nit = uint8_t(d / 512);
         I.rpu = 1;
         I.layer = uint16_t(l);
-        // rows of at most 4 KiB are loaded by the compute waves directly
-        const bool direct = d / 512 == 1 || d / 512 == 2 || d / 512 == 4;
+        const bool direct = egu_direct;
         I.flags = F_NORM | F_SIGNAL | (l == 0 ? F_IN_EMBED : 0) | (routed[cu] ? 0 : F_ROUTE) |
                   (direct ? F_DIRECT : 0);
         routed[cu] = 1;
@@ -622,14 +707,6 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.wait_ctr[0] = c_rt[l];
         I.sig_ctr = c_gu[l];
         I.n_pages = direct ? 0 : uint32_t(E * ppe);
-        if (direct && o.egu_queue > 1) {
-          // the last 1/q of the selected experts in the ready queue, in
-          // chunks of egu_chunk rows; the CU's last instruction drains it
-          I.seg_rows[2] = uint32_t(o.egu_queue);
-          I.seg_stride[2] = uint32_t(egu_chunk);
-          I.res_ptr = A + ar.edn_ctr + 16ull * l;
-          if (p1 == f1) I.flags |= F_QUEUE;
-        }
         InstrMeta m;
         m.stage = stg + ST_ATTN;
         m.merge_write = false;
@@ -703,7 +780,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.seg_rows[0] = uint32_t(Rb * 2 * Fe);
         I.in_ptr = A + ar.m[l];
         I.out_ptr = A + ar.y;
-        I.res_ptr = A + ar.edn_ctr + 16ull * l;  // the layer's ready-queue counters
+        I.res_ptr = A + ar.edn_ctr + 8ull * l;  // the layer's ready-queue counters
         I.row0 = uint32_t(std::max(0, o.edn_queue));
         I.wait_ctr[0] = c_gu[l];
         I.sig_ctr = c_dny[l];
@@ -737,7 +814,7 @@ static mk_status build_plan_moe(const PlanInput& in, Plan* P, std::string* err) 
         I.in_ptr = A + ar.y;
         I.res_ptr = A + ar.h[l];
         I.out_ptr = A + ar.x[l + 1];
-        if (r0 == 0) I.seg_ptr[0] = A + ar.edn_ctr + 16ull * l;  // clears the next step's counters
+        if (r0 == 0) I.seg_ptr[0] = A + ar.edn_ctr + 8ull * l;  // clears the next step's counter
         I.wait_ctr[0] = c_dny[l];
         I.wait_ctr[1] = c_o[l];
         I.sig_ctr = c_dn[l];
@@ -1423,6 +1500,7 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
     }
   }
   // 3. queue order per CU is by stage; pages are contiguous and within budget
+  std::vector<std::vector<std::pair<uint32_t, uint32_t>>> shares(c.n_layers);
   for (int cu = 0; cu < C; cu++) {
     uint32_t page = 0;
     int last_stage = -1;
@@ -1461,16 +1539,19 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
         if (!p.batched) return fail("expert instruction in a one-sequence plan");
         const uint32_t ppe = I.aux[2];
         if (I.k % 512 || I.nit != I.k / 512 || I.row_bytes != 2 * I.k) return fail("expert row geometry");
-        if (uint64_t(ppe) * kPageBytes < 2ull * I.seg_rows[0] || ppe > uint32_t(lb::kPages) - 1)
+        if (I.flags & F_SHARE) {
+          // a weighted share of every selected expert's rows
+          if (!(I.flags & F_DIRECT) || I.row0 || I.aux[3] != uint32_t(c.expert_ffn) ||
+              I.seg_rows[1] > I.seg_rows[2] || I.seg_rows[2] > 65536u)
+            return fail("expert gate/up share");
+          shares[I.layer].push_back({I.seg_rows[1], I.seg_rows[2]});
+        } else if (uint64_t(ppe) * kPageBytes < 2ull * I.seg_rows[0] || ppe > uint32_t(lb::kPages) - 1) {
           return fail("expert page regions");
+        }
         if (I.n_pages != ((I.flags & F_DIRECT) ? 0 : ppe * I.aux[4]) || I.aux[4] != uint32_t(c.n_experts))
           return fail("expert page budget");
         if ((I.flags & F_DIRECT) && (I.nit != 1 && I.nit != 2 && I.nit != 4)) return fail("direct expert loads");
         if (I.seg_rows[0] != I.aux[3] * I.row_bytes) return fail("expert gate/up runs");
-        if (I.seg_rows[2] && (!(I.flags & F_DIRECT) || I.seg_rows[2] < 2 || !I.seg_stride[2] ||
-                              uint32_t(c.expert_ffn) % I.seg_stride[2]))
-          return fail("expert gate/up ready queue");
-        if ((I.flags & F_QUEUE) && !I.seg_rows[2]) return fail("expert gate/up ready queue");
         continue;
       }
       if (I.op == OP_EDN) {
@@ -1521,6 +1602,17 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
           return fail("attention scores exceed the LDS scratch");
       }
     }
+  }
+  // weighted gate/up shares of a layer tile [0, 65536) exactly
+  for (auto& sh : shares) {
+    if (sh.empty()) continue;
+    std::sort(sh.begin(), sh.end());
+    uint32_t at = 0;
+    for (const auto& s : sh) {
+      if (s.first != at) return fail("gate/up shares do not tile the layer's items");
+      at = s.second;
+    }
+    if (at != 65536u) return fail("gate/up shares do not tile the layer's items");
   }
   // 4. read coverage: every element read must be written by an instruction
   //    whose signal the reader transitively waits for; each element written once
@@ -1714,14 +1806,6 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
             if (!inside(lo, lo + (NE - 1) * stride + run)) return fail("expert runs outside the expert tensors");
           }
           if (I.row0 + I.aux[3] > Fe) return fail("expert gate/up slice");
-          if (I.seg_rows[2]) {
-            // queued chunks: any row of the expert tensors
-            for (int r = 0; r < 2; r++) {
-              const uint64_t lo = I.seg_ptr[1 + r] - uint64_t(I.row0) * I.row_bytes;
-              if (!inside(lo, lo + (NE - 1) * stride + Fe * I.row_bytes)) return fail("queued expert rows");
-            }
-            if (!in_arena(I.res_ptr, I.res_ptr + 16)) return fail("ready-queue counters outside the arena");
-          }
           if (!(I.flags & F_IN_EMBED) && !in_arena(I.in_ptr, I.in_ptr + EB * NB * d))
             return fail("expert input outside the arena");
           if (!in_arena(I.out_ptr, I.out_ptr + mb)) return fail("expert intermediate outside the arena");
@@ -1732,14 +1816,14 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
             return fail("expert units outside the expert tensors");
           if (!in_arena(I.in_ptr, I.in_ptr + mb)) return fail("expert intermediate outside the arena");
           if (!in_arena(I.out_ptr, I.out_ptr + EB * NB * c.top_k * d)) return fail("expert outputs outside the arena");
-          if (!in_arena(I.res_ptr, I.res_ptr + 16)) return fail("ready-queue counters outside the arena");
+          if (!in_arena(I.res_ptr, I.res_ptr + 8)) return fail("ready-queue counters outside the arena");
         }
         continue;
       }
       if (I.op == OP_ERD) {
         const uint64_t rl = (NB - 1) * d + I.row0 + I.n_rows;
         if (!in_arena(I.in_ptr, I.in_ptr + EB * NB * c.top_k * d) || !in_arena(I.res_ptr, I.res_ptr + EB * rl) ||
-            !in_arena(I.out_ptr, I.out_ptr + EB * rl) || (I.seg_ptr[0] && !in_arena(I.seg_ptr[0], I.seg_ptr[0] + 16)))
+            !in_arena(I.out_ptr, I.out_ptr + EB * rl) || (I.seg_ptr[0] && !in_arena(I.seg_ptr[0], I.seg_ptr[0] + 8)))
           return fail("expert sum rows outside the arena");
         continue;
       }

@@ -24,7 +24,7 @@ struct ArenaLayout {
   uint64_t opart[128];    // [G][d] fp32 split-K O partials (one-sequence decoder)
   uint64_t rl[128];       // router logits (mixture-of-experts decoder)
   uint64_t y;             // [B][top_k][d] tagged expert outputs (mixture-of-experts decoder)
-  uint64_t edn_ctr;       // [L][4] u32 ready-queue counters (down projection, gate/up; by step parity)
+  uint64_t edn_ctr;       // [L][2] u32 ready-queue counters of the expert down projection
   uint64_t tok;           // [B] tagged greedy token of the last step
   uint64_t rope_cos, rope_sin, zero_page, lm_slots, status;
   uint64_t route_stats;   // [128] u32: selected experts per layer, summed over steps

@@ -118,16 +118,15 @@ def test_moe_tiny_ready_queue(need_gpu, queue, opts):
     _moe_case(TINY.replace(expert_ffn=2048, top_k=4, n_experts=16), edn_queue=queue, **opts)
 
 
-@pytest.mark.parametrize("queue,opts", [(2, {}), (8, {}), (2, {"n_cus": 1, "attn_block": 64}),
-                                        (4, {"n_cus": 3}), (2, {"n_cus": 37, "edn_queue": -1})])
-def test_moe_tiny_gate_up_ready_queue(need_gpu, queue, opts):
-    # the gate/up rows of the last 1/queue of the selected experts handed out
-    # at run time, in chunks, to the compute waves that finish their own
-    # slices first; a queue larger than the number of selected experts
-    # leaves it empty
-    _moe_case(TINY, egu_queue=queue, **opts)
-    _moe_case(TINY.replace(expert_ffn=2048, top_k=4, n_experts=16), egu_queue=queue, **opts)
-    _moe_case(TINY.replace(batch=1, top_k=1), egu_queue=queue, **opts)
+@pytest.mark.parametrize("balance,opts", [(1, {}), (-1, {}), (1, {"n_cus": 1, "attn_block": 64}),
+                                          (1, {"n_cus": 3}), (-1, {"n_cus": 3}), (1, {"n_cus": 37, "edn_queue": -1})])
+def test_moe_tiny_gate_up_shares(need_gpu, balance, opts):
+    # gate/up items as weighted shares of the layer's (expert, row) items
+    # (share boundaries inside an expert, CUs with no items) and as even row
+    # slices of every expert
+    _moe_case(TINY, egu_balance=balance, **opts)
+    _moe_case(TINY.replace(expert_ffn=2048, top_k=4, n_experts=16), egu_balance=balance, **opts)
+    _moe_case(TINY.replace(batch=1, top_k=1), egu_balance=balance, **opts)
 
 
 def test_moe_tiny_greedy_chain_on_device(need_gpu):

@@ -91,11 +91,11 @@ def test_resident_llama1b_ctx128_32_steps(need_gpu):
     _resident_case(synth.SHAPES["llama1b_ctx128"], 32, oracle_check=True)
 
 
-def test_resident_moe_tiny_ready_queues(need_gpu):
-    # both ready-queue counters of a layer alternate between the steps of
-    # the launch: each step's expert sums clear the next step's pair
-    _resident_case(synth.SHAPES["moe_tiny"], 4, egu_queue=2, edn_queue=2)
-    _resident_case(synth.SHAPES["moe_tiny"], 3, egu_queue=4, n_cus=3)
+def test_resident_moe_tiny_ready_queue(need_gpu):
+    # the down projection's ready-queue counters alternate between steps:
+    # each step's expert sums clear the next step's
+    _resident_case(synth.SHAPES["moe_tiny"], 4, edn_queue=2)
+    _resident_case(synth.SHAPES["moe_tiny"], 3, edn_queue=4, n_cus=3, egu_balance=-1)
 
 
 def test_resident_argument_checks(need_gpu):

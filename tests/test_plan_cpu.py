@@ -179,13 +179,14 @@ def test_moe_ready_queue_plans_verify(queue):
     B.mk_plan_check(_cfg("moe_b8_ctx2048"), 256, B.plan_opts(edn_queue=queue))
 
 
-@pytest.mark.parametrize("queue", [-1, 2, 4, 8])
-def test_moe_gate_up_ready_queue_plans_verify(queue):
+@pytest.mark.parametrize("balance", [-1, 1])
+def test_moe_gate_up_share_plans_verify(balance):
+    # weighted shares (the verifier checks that a layer's shares tile its
+    # items exactly) and even row slices
     for n_cus in (1, 3, 37, 256):
-        B.mk_plan_check(_cfg("moe_tiny"), n_cus, B.plan_opts(egu_queue=queue))
-    B.mk_plan_check(_cfg("moe_tiny", expert_ffn=2048, top_k=4, n_experts=16), 64, B.plan_opts(egu_queue=queue))
-    summ, _ = B.mk_plan_check(_cfg("moe_b8_ctx2048"), 256, B.plan_opts(egu_queue=queue))
-    # the queue changes who streams which rows, not the fixed bytes
+        B.mk_plan_check(_cfg("moe_tiny"), n_cus, B.plan_opts(egu_balance=balance))
+    B.mk_plan_check(_cfg("moe_tiny", expert_ffn=2048, top_k=4, n_experts=16), 64, B.plan_opts(egu_balance=balance))
+    summ, _ = B.mk_plan_check(_cfg("moe_b8_ctx2048"), 256, B.plan_opts(egu_balance=balance))
     assert summ["weight_bytes"] == moe_fixed_bytes(synth.SHAPES["moe_b8_ctx2048"])
 
 
