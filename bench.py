@@ -188,6 +188,9 @@ def main() -> int:
                     help="MoE decoder: 1: gate/up shares weighted by each CU's earlier work; -1: even row slices")
     ap.add_argument("--o-split", type=int, default=0,
                     help="1: O projection split per KV group; -1: whole rows; 0: the plan's default")
+    ap.add_argument("--gu-all", type=int, default=0,
+                    help="1: gate/up of every MLP chunk in one instruction per CU; -1: one per chunk; "
+                         "0: the plan's default")
     ap.add_argument("--launch", choices=("resident", "single"), default="resident",
                     help="resident: the K timed steps run in one launch (mk_decode_steps); "
                          "single: one launch per step, chained on the device")
@@ -215,7 +218,7 @@ def main() -> int:
                  plan=B.plan_opts(n_cus=args.n_cus, attn_block=args.attn_block,
                                   mlp_chunks=args.mlp_chunks, o_split=args.o_split, mfma=args.mfma,
                                   edn_queue=args.edn_queue,
-                                  egu_balance=args.egu_balance))
+                                  egu_balance=args.egu_balance, gu_all=args.gu_all))
     info = eng.plan_info()
     dev = eng.dev
     stream = torch.cuda.current_stream(dev)

@@ -155,6 +155,16 @@ typedef struct {
                           and router tiles plus its share take about the
                           same time on every CU; -1 = an even slice of
                           every selected expert's rows per CU (default) */
+  int32_t gu_all;     /* one-sequence decoder with mlp_chunks > 1: 1 = each
+                         CU's gate/up pairs of every MLP chunk in one
+                         instruction, chunk by chunk (all chunks read the
+                         same input, and the per-element step tags still let
+                         a down-projection chunk start once its own chunk is
+                         written: the early start of the write-up's chunk
+                         counters, "Custom Synchronization Mechanism",
+                         without one staging per chunk); -1 = one gate/up
+                         instruction per chunk.  Default: 1 from four
+                         chunks on, else -1.  The MoE decoder: unused */
 } mk_plan_opts;
 
 /* Plan summary (filled by mk_plan_info / mk_plan_check). */

@@ -45,7 +45,7 @@ class MkWeights(ctypes.Structure):
 class MkPlanOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_cus", "mlp_chunks", "attn_block", "watchdog_ms", "debug_corrupt_target",
-        "generic_kernel", "attn_heads", "o_split", "mfma", "edn_queue", "egu_balance")]
+        "generic_kernel", "attn_heads", "o_split", "mfma", "edn_queue", "egu_balance", "gu_all")]
 
 
 class MkPlanSummary(ctypes.Structure):
@@ -122,11 +122,12 @@ def config_from_shape(shape) -> MkConfig:
 
 def plan_opts(n_cus=0, mlp_chunks=0, attn_block=0, watchdog_ms=0, debug_corrupt_target=0,
               generic_kernel=0, attn_heads=0, o_split=0, mfma=0, edn_queue=0,
-              egu_balance=0):
+              egu_balance=0, gu_all=0):
     return MkPlanOpts(n_cus=n_cus, mlp_chunks=mlp_chunks, attn_block=attn_block,
                       watchdog_ms=watchdog_ms, debug_corrupt_target=debug_corrupt_target,
                       generic_kernel=generic_kernel, attn_heads=attn_heads, o_split=o_split,
-                      mfma=mfma, edn_queue=edn_queue, egu_balance=egu_balance)
+                      mfma=mfma, edn_queue=edn_queue, egu_balance=egu_balance,
+                      gu_all=gu_all)
 
 
 # ------------------------------------------------------------ the C entry points

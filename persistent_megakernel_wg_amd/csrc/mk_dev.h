@@ -958,10 +958,10 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
 // (log-sum-exp of the block maxima, taken as a running maximum over batches
 // of blocks).  Lane l merges the PER consecutive outputs from l*PER (one
 // head); every load of a batch of blocks is issued before the first is used,
-// so a merge of n blocks costs about n/8 memory round trips.
-template <int HPT, int DH>
+// so a merge of n blocks costs about n/NB memory round trips.
+template <int HPT, int DH, int NB = 8>
 DEV void attn_merge(Comp& c, InstrCP I) {
-  constexpr int OUT = HPT * DH, PER = OUT / 64, REC = DH + 2, NB = 8;
+  constexpr int OUT = HPT * DH, PER = OUT / 64, REC = DH + 2;
   static_assert(PER == 1 || PER == 2 || PER == 4 || PER == 8, "merge lane shape");
   const uint32_t g = I->aux[0], nblk = I->aux[3];
   const uint32_t head0 = g * uint32_t(c.a->hpg) + I->row0;

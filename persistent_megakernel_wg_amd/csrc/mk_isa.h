@@ -121,6 +121,8 @@ enum Flag : uint16_t {
                         // and the packed rows are in MFMA fragment order
   F_SHARE = 1024,       // (expert gate/up) a weighted share of the layer's (expert,
                         // row) items instead of a slice of rows of every expert
+  F_GU_ALL = 2048,      // (gate/up) the CU's pairs of every MLP chunk in one
+                        // instruction, chunk by chunk (GEMV aux fields below)
 };
 
 constexpr uint32_t kNoCounter = 0xFFFFFFFFu;
@@ -189,6 +191,10 @@ struct PackCopy {
 //   aux[0] = LDS accumulator offset (down projection)
 //   aux[1] = argmax slot index (LM head)
 //   aux[2] = LM-head ticket counter, aux[3] = LM-head tiles
+// Gate/up over every MLP chunk (EPI_SWIGLU with F_GU_ALL): aux[1] = pairs of
+//   one chunk on this CU (n), aux[2] = pairs per chunk (Fc), aux[3] = chunks;
+//   item t is pair row0 + (t / n) * Fc + t % n, and segment s (gate, up)
+//   holds the n rows from seg_ptr[s] + ch * Fc * row_bytes for each chunk ch
 // Split-K O projection (OP_GEMV, EPI_OPART): rows row0 .. row0 + n_rows of
 // Wo[:, g*Kg .. (g+1)*Kg) . o_g, with Kg = (query heads per KV group) * Dh:
 //   aux[1] = g, aux[2] = ticket counter of the row block, aux[3] = G (tiles

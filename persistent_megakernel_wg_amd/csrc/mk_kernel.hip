@@ -118,9 +118,12 @@ DEV const float* res_slot(uint32_t i) {
 struct EpiCtx {
   uint64_t* out;
   uint32_t epi, acc0, row0;
+  uint32_t gn, gstride;  // gate/up over every chunk: pairs per chunk here, pairs per chunk
 };
 DEV EpiCtx epi_of(InstrCP I) {
-  return EpiCtx{reinterpret_cast<uint64_t*>(I->out_ptr), i_epi(I), I->aux[0], I->row0};
+  const bool all = i_flags(I) & F_GU_ALL;
+  return EpiCtx{reinterpret_cast<uint64_t*>(I->out_ptr), i_epi(I), I->aux[0], I->row0,
+                all ? I->aux[1] : 0u, all ? I->aux[2] : 0u};
 }
 // OP: the kernel variant also runs split-K O tiles (EPI_OPART)
 template <bool OP>
@@ -136,8 +139,17 @@ DEV void epi_row(Comp& c, const EpiCtx& E, uint32_t i, uint32_t t_row, float v, 
     }
   }
   switch (E.epi) {
-    case EPI_STORE:
     case EPI_SWIGLU:
+      if (E.gn) {
+        // item t of a gate/up instruction over every chunk: pair t % n of
+        // chunk t / n
+        const uint32_t ch = t_row / E.gn;
+        st_tag(out + E.row0 + ch * E.gstride + (t_row - ch * E.gn), v, c.ep);
+        break;
+      }
+      st_tag(out + row, v, c.ep);
+      break;
+    case EPI_STORE:
       st_tag(out + row, v, c.ep);
       break;
     case EPI_RESID:
@@ -525,7 +537,11 @@ DEV bool run_attn(Comp& c, InstrCP I, uint32_t i) {
 template <class G>
 DEV void run_merge(Comp& c, InstrCP I) {
   if constexpr (!G::any) {
-    attn_merge<G::hpt, G::dh>(c, I);
+    // the kernels built for one shape issue the loads of up to 32 blocks
+    // (16 for 8 outputs per lane) before using any: one memory round trip
+    // for the long-context tiles instead of one per 8 blocks
+    constexpr int PER = G::hpt * G::dh / 64;
+    attn_merge<G::hpt, G::dh, (PER <= 2 ? 32 : PER == 4 ? 16 : 8)>(c, I);
   } else {
     const uint32_t hpt = I->n_items;
     if (c.a->head_dim == 64) {
@@ -720,8 +736,11 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       // re-reads of what was still stale.  (The other inputs are written by
       // the stage that runs at the same time, and early loads of them would
       // only be read twice.)
+      // Not during a gate/up instruction over every chunk: the first
+      // chunk's pairs are written by its own items on every CU.
       const uint32_t ne = i + 1 < n ? i_epi(I + 1) : 0u;
-      if (i + 1 < n && is_coop(I + 1) && (ne == EPI_ACC_FIRST || ne == EPI_ACC_MID || ne == EPI_ACC_LAST)) {
+      if (i + 1 < n && is_coop(I + 1) && !(i_flags(I) & F_GU_ALL) &&
+          (ne == EPI_ACC_FIRST || ne == EPI_ACC_MID || ne == EPI_ACC_LAST)) {
         const bool nreuse = reuses(I + 1);
         if (!nreuse || needs_res(I + 1)) {
           stage_issue(c, I + 1, !nreuse, pre);

@@ -222,6 +222,7 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
     // even gate/up slices by default: the weighted shares measured slower
     // on the MoE shape (4137 against 4001 us per step)
     if (r.egu_balance == 0) r.egu_balance = -1;
+    r.gu_all = -1;
     if (r.attn_block <= 0) {
       // K and V blocks of a tile in four of the five ring pages, scores in
       // the scratch, whole KV groups per tile
@@ -251,6 +252,13 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
       }
     }
   }
+  // gate/up of every MLP chunk in one instruction per CU (see build_plan)
+  // from four chunks on: measured on the 8B shape (4 chunks) 4034-4043
+  // against 4061-4066 us per step; with two chunks the per-chunk
+  // instructions keep the early loads of the first down-projection chunk's
+  // input during the second gate/up chunk (1B shape, context 8192: 897-902
+  // against 910 us; context 128: equal)
+  if (r.gu_all == 0) r.gu_all = r.mlp_chunks >= 4 ? 1 : -1;
   if (r.attn_block <= 0) {
     const int rows_per_page = kPageBytes / (2 * c.head_dim);
     if (c.max_seq <= 512 && c.max_seq * 2 * c.head_dim <= (kPages / 2) * kPageBytes) {
@@ -948,6 +956,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     return MK_ERR_INVALID_ARG;
   }
   const int Fc = F / chunks;
+  const bool gu_all = chunks > 1 && o.gu_all > 0;
   Geo gd, gq, gf;
   if (!geo_for_k(d, &gd) || !geo_for_k(qd, &gq) || !geo_for_k(Fc, &gf) || Fc > kMaxK) {
     *err = "plan: ffn/mlp_chunks must be 256 or a multiple of 512 up to 4096";
@@ -1000,7 +1009,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     if (nblk > 1)
       for (int t = 0; t < G * tpg; t++) c_ticket[l].push_back(b.new_counter(l * ST_PER_LAYER + ST_ATTN));
     c_o[l] = b.new_counter(l * ST_PER_LAYER + ST_O);
-    for (int ch = 0; ch < chunks; ch++) c_gu[l].push_back(b.new_counter(l * ST_PER_LAYER + ST_GU));
+    for (int ch = 0; ch < (gu_all ? 1 : chunks); ch++) c_gu[l].push_back(b.new_counter(l * ST_PER_LAYER + ST_GU));
     c_down[l] = b.new_counter(l * ST_PER_LAYER + ST_DOWN);
   }
   const uint32_t c_lm = b.new_counter(L * ST_PER_LAYER);
@@ -1238,29 +1247,39 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
       }
     }
     // ------------------------------------------------------- GATE/UP
-    for (int ch = 0; ch < chunks; ch++) {
+    // One instruction per chunk and CU, or (gu_all) one per CU holding its
+    // pairs of every chunk, chunk by chunk: all chunks read the same input,
+    // and the per-element tags let a down-projection chunk start on its
+    // input while later chunks are still being computed.
+    for (int ch = 0; ch < (gu_all ? 1 : chunks); ch++) {
       const int64_t N = Fc;  // pairs
       for (int cu = 0; cu < C; cu++) {
         int64_t i0, i1;
         split(N, cu, &i0, &i1);
         if (i1 <= i0) continue;
         const int p0 = ch * Fc + int(i0), p1 = ch * Fc + int(i1);
+        const int nch = gu_all ? chunks : 1;  // chunks in the instruction
         Instr I = blank();
         I.op = OP_GEMV;
         I.epi = EPI_SWIGLU;
         I.nit = uint8_t(gd.nit);
         I.rpu = uint8_t(gd.rpu);
         I.layer = uint16_t(l);
-        I.flags = F_NORM | F_SIGNAL | F_INTERLEAVE;
-        I.n_items = uint32_t(p1 - p0);
+        I.flags = F_NORM | F_SIGNAL | F_INTERLEAVE | (gu_all ? F_GU_ALL : 0);
+        I.n_items = uint32_t(nch * (p1 - p0));
         I.row0 = uint32_t(p0);
         I.row_bytes = uint32_t(2 * d);
-        I.n_rows = uint32_t(2 * (p1 - p0));
+        I.n_rows = 2 * I.n_items;
         I.k = uint32_t(d);
         I.seg_ptr[0] = lptr(in.w.w_gate, l, uint64_t(F) * d) + 2ull * d * p0;
         I.seg_ptr[1] = lptr(in.w.w_up, l, uint64_t(F) * d) + 2ull * d * p0;
-        I.seg_rows[0] = I.seg_rows[1] = uint32_t(p1 - p0);
+        I.seg_rows[0] = I.seg_rows[1] = I.n_items;
         I.seg_stride[0] = I.seg_stride[1] = uint32_t(2 * d);
+        if (gu_all) {
+          I.aux[1] = uint32_t(p1 - p0);
+          I.aux[2] = uint32_t(Fc);
+          I.aux[3] = uint32_t(chunks);
+        }
         I.aux[4] = 2;
         I.in_ptr = A + ar.h[l];
         I.out_ptr = A + ar.m[l];
@@ -1272,7 +1291,8 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
         m.stage = stg + ST_GU;
         m.merge_write = false;
         m.reads.push_back({BUF_H, l, 0, uint64_t(d)});
-        m.writes.push_back({BUF_M, l, uint64_t(p0), uint64_t(p1)});
+        for (int k = 0; k < nch; k++)
+          m.writes.push_back({BUF_M, l, uint64_t(k * Fc + p0), uint64_t(k * Fc + p1)});
         b.push(cu, I, std::move(m), int64_t(I.n_rows) * I.row_bytes);
       }
     }
@@ -1314,7 +1334,7 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
           I.in_ptr = A + ar.m[l] + uint64_t(kActBytes) * ch * Fc;
           I.res_ptr = A + ar.h[l];
           I.out_ptr = A + ar.x[l + 1];
-          set_wait(I, 0, c_gu[l][ch]);
+          set_wait(I, 0, c_gu[l][gu_all ? 0 : ch]);
           I.sig_ctr = last ? c_down[l] : kNoCounter;
           I.n_pages = uint32_t(ceil_div(int64_t(I.n_rows) * I.row_bytes, kPageBytes));
           InstrMeta m;
@@ -1412,6 +1432,24 @@ mk_status build_plan(const PlanInput& in, Plan* P, std::string* err) {
     if (I.op != OP_GEMV) continue;
     I.src_ptr = in.pack_base + pack;
     const bool inter = I.flags & F_INTERLEAVE;
+    if (I.flags & F_GU_ALL) {
+      // gate/up pairs of every chunk, chunk by chunk, each chunk's rows
+      // interleaved
+      const uint32_t n = I.aux[1];
+      for (uint32_t ch = 0; ch < I.aux[3]; ch++)
+        for (uint32_t sg = 0; sg < 2; sg++) {
+          PackCopy cp{};
+          cp.src = I.seg_ptr[sg] + uint64_t(ch) * I.aux[2] * I.seg_stride[sg];
+          cp.rows = n;
+          cp.row_bytes = I.row_bytes;
+          cp.src_stride = I.seg_stride[sg];
+          cp.dst = pack + (uint64_t(ch) * 2 * n + sg) * I.row_bytes;
+          cp.dst_stride = 2 * I.row_bytes;
+          P->pack.push_back(cp);
+        }
+      pack += uint64_t(I.n_pages) * kPageBytes;
+      continue;
+    }
     uint64_t row = 0;
     for (uint32_t sg = 0; sg < I.aux[4]; sg++) {
       if (!I.seg_rows[sg]) continue;
@@ -1858,8 +1896,15 @@ mk_status verify_plan(const PlanInput& in, const Plan& p, std::string* err, uint
                                       : !in_arena(I.res_ptr + 8 * I.row0, I.res_ptr + 8 * (I.row0 + out_rows)))
             return fail("split-K O residual outside the arena");
         }
+        uint64_t out_hi = I.row0 + out_rows;  // one past the last output row
+        if (I.flags & F_GU_ALL) {
+          if (I.epi != EPI_SWIGLU || !I.aux[1] || I.aux[3] < 2 || I.n_items != I.aux[1] * I.aux[3] ||
+              uint64_t(I.aux[2]) * I.aux[3] != uint64_t(c.ffn) || I.row0 + I.aux[1] > I.aux[2])
+            return fail("gate/up over every chunk: chunk geometry");
+          out_hi = I.row0 + uint64_t(I.aux[3] - 1) * I.aux[2] + I.aux[1];
+        }
         if (I.epi != EPI_ARGMAX && I.epi != EPI_ACC_FIRST && I.epi != EPI_ACC_MID && I.epi != EPI_OPART &&
-            !in_arena(I.out_ptr + uint64_t(kActBytes) * I.row0, I.out_ptr + uint64_t(kActBytes) * (I.row0 + out_rows)))
+            !in_arena(I.out_ptr + uint64_t(kActBytes) * I.row0, I.out_ptr + uint64_t(kActBytes) * out_hi))
           return fail("GEMV output outside the arena");
         if ((I.epi == EPI_RESID || I.epi == EPI_ACC_ONLY || I.epi == EPI_ACC_FIRST) &&
             !(I.flags & F_RES_EMBED) &&

@@ -49,16 +49,18 @@ def counter_per_dispatch(path: str, counter: str, kernel_sub: str):
     """Mean of `counter` over dispatches whose kernel name contains kernel_sub
     (summed over the rows a dispatch reports), and the dispatch count."""
     per = {}
+    matched = None  # name of the counted kernel (the last matching row's)
     for r in _rows(path):
         name = _key(r, "Kernel_Name", "KernelName")
         if kernel_sub not in name or _key(r, "Counter_Name", "CounterName") != counter:
             continue
+        matched = name
         d = _key(r, "Dispatch_Id", "DispatchId")
         per[d] = per.get(d, 0.0) + float(_key(r, "Counter_Value", "CounterValue"))
     if not per:
         raise SystemExit("no %s rows for a kernel containing %r in %s" % (counter, kernel_sub, path))
     vals = [per[k] for k in sorted(per, key=lambda x: int(x))]
-    return vals, name
+    return vals, matched
 
 
 def traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, alg_bytes, steps_per_launch=1):

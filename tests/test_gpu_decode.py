@@ -114,6 +114,15 @@ def test_tiny_step_four_chunks(need_gpu):
     _one_step_case(synth.SHAPES["tiny"], mlp_chunks=4)
 
 
+@pytest.mark.parametrize("n_cus", [1, 7, 256])
+def test_tiny_gate_up_per_chunk_and_over_every_chunk(need_gpu, n_cus):
+    # gate/up of every chunk in one instruction per CU (items chunk by chunk,
+    # each written to its chunk's rows) against one instruction per chunk
+    for chunks in (2, 4):
+        _one_step_case(synth.SHAPES["tiny"], n_cus=n_cus, mlp_chunks=chunks, gu_all=1)
+        _one_step_case(synth.SHAPES["tiny"], n_cus=n_cus, mlp_chunks=chunks, gu_all=-1)
+
+
 @pytest.mark.parametrize("heads", [(4, 4, 64), (8, 2, 64), (8, 1, 64), (4, 2, 128), (4, 1, 128)])
 def test_tiny_step_head_layouts(need_gpu, heads):
     # every attention code path: 1, 2, 4, 8 query heads per KV group, Dh 64/128

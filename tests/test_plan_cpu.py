@@ -172,6 +172,22 @@ def test_moe_plan_for_the_large_shape_on_fewer_cus():
     B.mk_plan_check(_cfg("moe_b8_ctx2048"), 80)
 
 
+@pytest.mark.parametrize("gu_all", [-1, 1])
+def test_gate_up_over_every_chunk_plans_verify(gu_all):
+    # one gate/up instruction per CU over every chunk removes chunks - 1
+    # instructions per CU and layer; the verifier checks the chunk geometry,
+    # the output rows and the packed copies
+    for name, chunks, cus in (("tiny", 2, (1, 7, 256)), ("tiny", 4, (1, 7, 256)),
+                              ("llama1b_ctx128", 0, (37, 256)), ("llama8b_ctx2048", 0, (64, 256))):
+        for n_cus in cus:
+            on, _ = B.mk_plan_check(_cfg(name), n_cus, B.plan_opts(mlp_chunks=chunks, gu_all=gu_all))
+            off, _ = B.mk_plan_check(_cfg(name), n_cus, B.plan_opts(mlp_chunks=chunks, gu_all=-1))
+            assert on["weight_bytes"] == off["weight_bytes"]
+            if gu_all > 0:
+                L = synth.SHAPES[name].n_layers
+                assert off["n_instr"] - on["n_instr"] == L * (on["mlp_chunks"] - 1) * min(n_cus, 256)
+
+
 @pytest.mark.parametrize("queue", [-1, 2, 4, 8, 16])
 def test_moe_ready_queue_plans_verify(queue):
     for n_cus in (1, 3, 256):
