@@ -32,7 +32,7 @@ from collections import defaultdict
 import numpy as np
 
 TR = dict(START=0, DEPS=1, STAGED=2, ITEMS=3, SIGNAL=4, PAGEWAIT=5, HW0=6, HW1=7,
-          XREADY=8, ITEM0=9, VISIBLE=10, XFREE=11, RETRY=15)
+          XREADY=8, ITEM0=9, VISIBLE=10, XFREE=11, A_PASS1=12, A_STATS=13, A_PASS3=14, RETRY=15)
 OP_GEMV, OP_ATTN, OP_BGEMV, OP_EGU, OP_EDN, OP_ERD = 1, 2, 3, 4, 5, 6
 EPI_NAMES = {0: "qkv", 1: "o", 2: "gate_up", 3: "down", 4: "down", 5: "down", 6: "down",
              7: "lm_head", 8: "o"}
@@ -92,7 +92,7 @@ def analyse(tr: np.ndarray, batched: bool = False) -> dict:
             r["end"].append(rel(np.array(end)))
             r["pagewait"].append(int(w[TR["PAGEWAIT"]]) * TICK_US)
             # phases inside the instruction, per CU (leader's stamps)
-            for name in ("XREADY", "ITEM0", "ITEMS", "VISIBLE"):
+            for name in ("XREADY", "ITEM0", "ITEMS", "VISIBLE", "A_PASS1", "A_STATS", "A_PASS3"):
                 r[name.lower()].append(rel(np.array(w[TR[name]])) if w[TR[name]] else np.nan)
     order = sorted(rec.keys(), key=lambda k: (k[0], float(np.median(rec[k]["start"])), k[2]))
     rows = []
@@ -114,7 +114,15 @@ def analyse(tr: np.ndarray, batched: bool = False) -> dict:
                   "item0_to_items_us": med("items", "item0"),
                   "items_to_end_us": med("end", "items"),
                   "staged_to_end_us": med("end", "staged"),
-                  "start_to_staged_us": med("staged", "start")}
+                  "start_to_staged_us": med("staged", "start"),
+                  # one-sequence GEMV rows: the first iteration of wave 0
+                  "xready_to_page_us": med("a_pass1", "xready"),
+                  "page_to_sums_us": med("a_stats", "a_pass1"),
+                  "sums_to_item0_us": med("item0", "a_stats"),
+                  # attention tiles: wave 0's pass to the barrier after the
+                  # lane-group merge, then the wave merge and the stores
+                  "item0_to_wavemerge_us": med("a_pass3", "item0"),
+                  "wavemerge_to_items_us": med("items", "a_pass3")}
         rows.append({"layer": key[0], "stage": key[1], "part": key[2], "cus": len(end), **phases,
                      "staged_median_us": st_med, "end_median_us": float(np.median(end)),
                      "end_max_us": end_max, "handover_us": handover, "work_us": work,
@@ -125,7 +133,7 @@ def analyse(tr: np.ndarray, batched: bool = False) -> dict:
     for r in rows:
         kinds[r["stage"]][0] += r["handover_us"]
         kinds[r["stage"]][1] += r["work_us"]
-    return {"step_us": total, "rows": rows,
+    return {"step_us": total, "rows": rows, "batched": bool(batched),
             "by_stage": {k: {"handover_us": v[0], "work_us": v[1], "total_us": v[0] + v[1]}
                          for k, v in kinds.items()}}
 
@@ -158,6 +166,23 @@ def report(res: dict, title: str) -> str:
                 r["stage"], r["part"], r["start_to_staged_us"], r["staged_to_xready_us"],
                 r["xready_to_item0_us"], r["item0_to_items_us"], r["items_to_end_us"],
                 r["staged_to_end_us"]))
+    gem = [r for r in res["rows"] if not res.get("batched") and (r["layer"] == mid or r["stage"] == "lm_head")
+           and np.isfinite(r.get("page_to_sums_us", np.nan))]
+    if gem:
+        out += ["", "The first item of wave 0 in the same GEMV instructions (medians, us):", "",
+                "| stage | part | x ready->pages ready | pages ready->sums reduced | sums reduced->first item done |",
+                "|---|---|---|---|---|"]
+        for r in gem:
+            out.append("| %s | %d | %.2f | %.2f | %.2f |" % (
+                r["stage"], r["part"], r["xready_to_page_us"], r["page_to_sums_us"], r["sums_to_item0_us"]))
+    att = [r for r in res["rows"] if r["layer"] == mid and r["stage"] == "attention"
+           and np.isfinite(r.get("item0_to_wavemerge_us", np.nan))]
+    if att:
+        out += ["", "After the position loop of wave 0 in the attention tiles of the same layer (medians, us):", "",
+                "| part | loop end->lane groups merged, records written, barrier | ->waves merged, outputs stored, barrier |",
+                "|---|---|---|"]
+        for r in att:
+            out.append("| %d | %.2f | %.2f |" % (r["part"], r["item0_to_wavemerge_us"], r["wavemerge_to_items_us"]))
     return "\n".join(out)
 
 

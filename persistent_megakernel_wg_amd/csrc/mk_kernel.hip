@@ -226,6 +226,7 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
           const uint32_t tw = trl ? now32() : 0;
           if (!wait_page(page0 + (ub + UPI - 1) / kUnitsPerPage, c.fcache)) return false;
           if (trl) c.pagewait += now32() - tw;
+          if (trl && t == 0) trace_put(a, c.cu, i, TR_A_PASS1, now32());  // first pages ready
         }
         float sum[2][RU];
 #pragma unroll
@@ -253,6 +254,7 @@ DEV bool gemv(Comp& c, InstrCP I, uint32_t i) {
             sum64x2(acc[0], acc[1], sum[0][r0 + r], sum[1][r0 + r]);
           }
         }
+        if (trl && t == 0) trace_put(a, c.cu, i, TR_A_STATS, now32());  // first sums reduced
         if (lane == 0) {
           const float a0 = sum[0][0] * inv, b0 = sum[1][0] * inv;
           epi_row<OP>(c, E, i, t, RU == 2 ? silu(a0) * (sum[0][RU - 1] * inv) : a0, best);
