@@ -122,7 +122,11 @@ def analyse(tr: np.ndarray, batched: bool = False) -> dict:
                   # attention tiles: wave 0's pass to the barrier after the
                   # lane-group merge, then the wave merge and the stores
                   "item0_to_wavemerge_us": med("a_pass3", "item0"),
-                  "wavemerge_to_items_us": med("items", "a_pass3")}
+                  "wavemerge_to_items_us": med("items", "a_pass3"),
+                  # one-sequence attention tiles: the waves' loop ends
+                  # (earliest, latest) against wave 0's and the barrier
+                  "loop_spread_us": med("a_stats", "a_pass1"),
+                  "lastloop_to_wavemerge_us": med("a_pass3", "a_stats")}
         rows.append({"layer": key[0], "stage": key[1], "part": key[2], "cus": len(end), **phases,
                      "staged_median_us": st_med, "end_median_us": float(np.median(end)),
                      "end_max_us": end_max, "handover_us": handover, "work_us": work,
@@ -167,7 +171,7 @@ def report(res: dict, title: str) -> str:
                 r["xready_to_item0_us"], r["item0_to_items_us"], r["items_to_end_us"],
                 r["staged_to_end_us"]))
     gem = [r for r in res["rows"] if not res.get("batched") and (r["layer"] == mid or r["stage"] == "lm_head")
-           and np.isfinite(r.get("page_to_sums_us", np.nan))]
+           and r["stage"] != "attention" and np.isfinite(r.get("page_to_sums_us", np.nan))]
     if gem:
         out += ["", "The first item of wave 0 in the same GEMV instructions (medians, us):", "",
                 "| stage | part | x ready->pages ready | pages ready->sums reduced | sums reduced->first item done |",
@@ -183,6 +187,11 @@ def report(res: dict, title: str) -> str:
                 "|---|---|---|"]
         for r in att:
             out.append("| %d | %.2f | %.2f |" % (r["part"], r["item0_to_wavemerge_us"], r["wavemerge_to_items_us"]))
+        if not res.get("batched"):
+            out += ["", "| part | first to last wave's loop end | last loop end->lane groups merged, barrier |",
+                    "|---|---|---|"]
+            for r in att:
+                out.append("| %d | %.2f | %.2f |" % (r["part"], r["loop_spread_us"], r["lastloop_to_wavemerge_us"]))
     return "\n".join(out)
 
 

@@ -66,7 +66,8 @@ enum : int {
   C_STATUS_HI = 260,
   C_LIMIT_LO = 264,    // time limit of local waits, s_memrealtime ticks
   C_LIMIT_HI = 268,
-  C_CTRL_END = 272,
+  C_TR_LOOP = 272,     // traced runs: earliest, latest end of the attention waves' loops
+  C_CTRL_END = 280,
 };
 static_assert(C_FILLED + 4 * kNLoad <= C_RELEASED, "ctrl layout");
 static_assert(C_RELEASED + 4 * kNComp <= C_XOK, "ctrl layout");
@@ -868,17 +869,22 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
   }
   if (lane == 0) lds_st(C_RELEASED + 4 * c.w, page0 + I->n_pages);
   if (trl) trace_put(a, c.cu, i, TR_ITEM0, now32());
-  // merge the lane groups of the wave (butterfly: every lane ends with the
-  // same result)
-  auto merge = [&](int h, float mo, float lo_, const float (&ao)[8]) {
-    const float mn = fmaxf(m[h], mo);
-    const float sa = m[h] == -__builtin_inff() ? 0.f : __expf(m[h] - mn);
-    const float sb = mo == -__builtin_inff() ? 0.f : __expf(mo - mn);
-    l[h] = l[h] * sa + lo_ * sb;
-#pragma unroll
-    for (int e = 0; e < 8; e++) acc[h][e] = acc[h][e] * sa + ao[e] * sb;
-    m[h] = mn;
-  };
+  if constexpr (std::is_same<Lay, LayA>::value) {
+    // traced runs: earliest and latest end of the waves' position loops
+    if (a.trace && lane == 0) {
+      const uint32_t t = now32();
+      __hip_atomic_fetch_min(lw(C_TR_LOOP), t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_max(lw(C_TR_LOOP + 4), t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  // Merge the lane groups of the wave.  A butterfly gives every lane the
+  // wave's maximum of each head; each group rescales its sums to it once;
+  // a butterfly sums the weights, and a reduce-scatter the value sums: each
+  // exchange keeps half of a lane's values and adds the partner's copy of
+  // that half, so the NG groups' 8 values per lane end as 8 / NG sums per
+  // lane, each added in one fixed tree.
+  constexpr int NG = 64 / LPRA, NV = 8 / NG;  // lane groups, sums per lane
+  static_assert(NG * NV == 8 && (LPRA == 8 || LPRA == 16), "lane groups");
   // register exchanges in the one-sequence kernel; the batched kernel keeps
   // the generic shuffle, which measured faster there
   auto xch = [](auto off_c, float v) {
@@ -886,39 +892,70 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
     if constexpr (std::is_same<Lay, LayA>::value) return lane_xor<OFF>(v);
     else return __shfl_xor(v, OFF, 64);
   };
-  auto merge_step = [&](auto off_c) {
-#pragma unroll
-    for (int h = 0; h < HPT; h++) {
-      float ao[8];
-#pragma unroll
-      for (int e = 0; e < 8; e++) ao[e] = xch(off_c, acc[h][e]);
-      const float mo = xch(off_c, m[h]), lo_ = xch(off_c, l[h]);
-      merge(h, mo, lo_, ao);
-    }
+  // the exchange offsets between lane groups: LPRA, 2 LPRA, ..., 32
+  auto over_groups = [&](auto f) {
+    if constexpr (LPRA <= 8) f(std::integral_constant<int, 8>{});
+    f(std::integral_constant<int, 16>{});
+    f(std::integral_constant<int, 32>{});
   };
-  if constexpr (LPRA <= 4) merge_step(std::integral_constant<int, 4>{});
-  if constexpr (LPRA <= 8) merge_step(std::integral_constant<int, 8>{});
-  if constexpr (LPRA <= 16) merge_step(std::integral_constant<int, 16>{});
-  merge_step(std::integral_constant<int, 32>{});
+  float M[HPT];
+#pragma unroll
+  for (int h = 0; h < HPT; h++) M[h] = m[h];
+  over_groups([&](auto oc) {
+#pragma unroll
+    for (int h = 0; h < HPT; h++) M[h] = fmaxf(M[h], xch(oc, M[h]));
+  });
+#pragma unroll
+  for (int h = 0; h < HPT; h++) {
+    // a group without rows (m = -inf) adds nothing
+    const float sc = m[h] == -__builtin_inff() ? 0.f : __expf(m[h] - M[h]);
+    l[h] *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[h][e] *= sc;
+  }
+  over_groups([&](auto oc) {
+#pragma unroll
+    for (int h = 0; h < HPT; h++) l[h] += xch(oc, l[h]);
+  });
+  over_groups([&](auto oc) {
+    constexpr int OFF = decltype(oc)::value, HN = 4 * LPRA / OFF;  // values kept: 4, 2, 1
+    const bool up = lane & OFF;
+#pragma unroll
+    for (int h = 0; h < HPT; h++)
+#pragma unroll
+      for (int e = 0; e < HN; e++) {
+        const float send = up ? acc[h][e] : acc[h][HN + e];
+        const float keep = up ? acc[h][HN + e] : acc[h][e];
+        acc[h][e] = keep + xch(oc, send);
+      }
+  });
+  // lane (group j, slice s) holds the sums of dims 8 s + dof .. + NV - 1,
+  // dof from the bits of j that chose the kept halves
+  const uint32_t dof = ((lane & uint32_t(LPRA)) ? 4u : 0u) + ((lane & uint32_t(2 * LPRA)) ? 2u : 0u) +
+                       ((NG == 8 && (lane & uint32_t(4 * LPRA))) ? 1u : 0u);
   // the wave's record per head after the staged inputs: o~ [DH] | m | l
   constexpr int REC = DH + 2;
   constexpr int PBASE = (HPT * DH + 3 * DH + 3) & ~3;
   static_assert(PBASE + kNComp * HPT * REC <= Lay::x_floats, "attention partials");
   float* wrec = xs + PBASE;
-  if (lane < uint32_t(LPRA)) {
 #pragma unroll
-    for (int h = 0; h < HPT; h++) {
-      float* r = wrec + (c.w * HPT + h) * REC;
-      *reinterpret_cast<f4*>(r + 8 * s) = f4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-      *reinterpret_cast<f4*>(r + 8 * s + 4) = f4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
-      if (s == 0) {
-        r[DH] = m[h];
-        r[DH + 1] = l[h];
-      }
+  for (int h = 0; h < HPT; h++) {
+    float* r = wrec + (c.w * HPT + h) * REC;
+#pragma unroll
+    for (int e = 0; e < NV; e++) r[8 * s + dof + e] = acc[h][e];
+    if (lane == 0) {
+      r[DH] = M[h];
+      r[DH + 1] = l[h];
     }
   }
   if (!comp_barrier()) return false;
-  if (trl) trace_put(a, c.cu, i, TR_A_PASS3, now32());
+  if (trl) {
+    trace_put(a, c.cu, i, TR_A_PASS3, now32());
+    if constexpr (std::is_same<Lay, LayA>::value) {
+      trace_put(a, c.cu, i, TR_A_PASS1, *lw(C_TR_LOOP));
+      trace_put(a, c.cu, i, TR_A_STATS, *lw(C_TR_LOOP + 4));
+    }
+  }
 
   // final: merge the waves' records in order, normalise, store
   for (uint32_t o = c.w * 64 + lane; o < uint32_t(OUT); o += 64 * kNComp) {

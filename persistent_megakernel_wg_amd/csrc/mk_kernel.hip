@@ -712,7 +712,11 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
         if (c.lane == 0) lds_st(C_ABORT, 1);
         return;
       }
-      if (tr && c.lane == 0) trace_put(a, cu, ti, TR_XFREE, now32());
+      if (tr && c.lane == 0) {
+        trace_put(a, cu, ti, TR_XFREE, now32());
+        *lw(C_TR_LOOP) = 0xFFFFFFFFu;  // the attention loops' end stamps
+        *lw(C_TR_LOOP + 4) = 0u;
+      }
       if (!stage_leader(c, I, ig)) {
         if (c.lane == 0) lds_st(C_ABORT, 1);
         return;
