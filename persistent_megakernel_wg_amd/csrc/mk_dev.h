@@ -798,10 +798,11 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
 
   // One pass per wave, softmax online: wave w takes the position units
   // u = w (mod waves); in a unit, lane group jrow holds row u*UPOS + jrow,
-  // its lanes 8 dims each of k and v.  Every lane group keeps, per head, the
-  // running maximum m, the sum l of exp(score - m) and o~ = sum exp(score - m)
-  // v over its rows; the groups of a wave, then the waves, are merged by the
-  // log-sum-exp rule.  The wave after the last unit's takes the new row.
+  // its lanes 8 dims each of k and v.  Every lane group keeps, per head, a
+  // reference m (at most kLazy below the maximum of its scores), the sum l
+  // of exp(score - m) and o~ = sum exp(score - m) v over its rows; the
+  // groups of a wave, then the waves, are merged by the log-sum-exp rule.
+  // The wave after the last unit's takes the new row.
   const uint32_t n_units = (uint32_t(nc) + UPOS - 1) / UPOS;
   float m[HPT], l[HPT], acc[HPT][8];
 #pragma unroll
@@ -811,16 +812,25 @@ DEV bool attn(Comp& c, InstrCP I, uint32_t i, uint32_t page0) {
 #pragma unroll
     for (int e = 0; e < 8; e++) acc[h][e] = 0.f;
   }
-  // one exponential per row: exp(-|score - m|) is the new row's weight when
-  // the maximum stays, and the rescale of the old sums when it moves
+  // m is the reference of a group's sums (l and o~ are taken relative to
+  // exp(m)): it moves to a row's score only when the score exceeds it by
+  // more than kLazy, which rescales the old sums, so every weight
+  // exp(score - m) stays below e^kLazy and most rows cost one exponential
+  // and one fused multiply-add per dimension.  The first row moves it from
+  // -inf (the old sums, all zero, scale by 0).
+  constexpr float kLazy = 8.f;
   auto update = [&](int h, float sc, const float (&v)[8]) {
-    const bool up = sc > m[h];
-    const float d = __expf(-fabsf(sc - m[h]));  // m = -inf: exp(-inf) = 0
-    const float sa = up ? d : 1.f, w = up ? 1.f : d;
-    l[h] = fmaf(l[h], sa, w);
+    if (sc > m[h] + kLazy) {
+      const float sa = __expf(m[h] - sc);  // m = -inf: exp(-inf) = 0
+      l[h] *= sa;
 #pragma unroll
-    for (int e = 0; e < 8; e++) acc[h][e] = fmaf(acc[h][e], sa, w * v[e]);
-    m[h] = up ? sc : m[h];
+      for (int e = 0; e < 8; e++) acc[h][e] *= sa;
+      m[h] = sc;
+    }
+    const float w = __expf(sc - m[h]);
+    l[h] += w;
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[h][e] = fmaf(w, v[e], acc[h][e]);
   };
   for (uint32_t u = c.w; u < n_units; u += kNComp) {
     // the v unit streams after every k unit of the tile
