@@ -92,7 +92,7 @@ def analyse(tr: np.ndarray, batched: bool = False) -> dict:
             r["end"].append(rel(np.array(end)))
             r["pagewait"].append(int(w[TR["PAGEWAIT"]]) * TICK_US)
             # phases inside the instruction, per CU (leader's stamps)
-            for name in ("XREADY", "ITEM0", "ITEMS", "VISIBLE", "A_PASS1", "A_STATS", "A_PASS3"):
+            for name in ("XREADY", "ITEM0", "ITEMS", "VISIBLE", "A_PASS1", "A_STATS", "A_PASS3", "XFREE"):
                 r[name.lower()].append(rel(np.array(w[TR[name]])) if w[TR[name]] else np.nan)
     order = sorted(rec.keys(), key=lambda k: (k[0], float(np.median(rec[k]["start"])), k[2]))
     rows = []
@@ -116,6 +116,10 @@ def analyse(tr: np.ndarray, batched: bool = False) -> dict:
                   "staged_to_end_us": med("end", "staged"),
                   "start_to_staged_us": med("staged", "start"),
                   # one-sequence GEMV rows: the first iteration of wave 0
+                  # one-sequence GEMV rows: the leader's own staging, then
+                  # the barrier of the staging waves
+                  "start_to_ownstage_us": med("xfree", "start"),
+                  "ownstage_to_staged_us": med("staged", "xfree"),
                   "xready_to_page_us": med("a_pass1", "xready"),
                   "page_to_sums_us": med("a_stats", "a_pass1"),
                   "sums_to_item0_us": med("item0", "a_stats"),
@@ -174,11 +178,13 @@ def report(res: dict, title: str) -> str:
            and r["stage"] != "attention" and np.isfinite(r.get("page_to_sums_us", np.nan))]
     if gem:
         out += ["", "The first item of wave 0 in the same GEMV instructions (medians, us):", "",
-                "| stage | part | x ready->pages ready | pages ready->sums reduced | sums reduced->first item done |",
-                "|---|---|---|---|---|"]
+                "| stage | part | start->leader's share staged | ->barrier passed | x ready->pages ready "
+                "| pages ready->sums reduced | sums reduced->first item done |",
+                "|---|---|---|---|---|---|---|"]
         for r in gem:
-            out.append("| %s | %d | %.2f | %.2f | %.2f |" % (
-                r["stage"], r["part"], r["xready_to_page_us"], r["page_to_sums_us"], r["sums_to_item0_us"]))
+            out.append("| %s | %d | %.2f | %.2f | %.2f | %.2f | %.2f |" % (
+                r["stage"], r["part"], r["start_to_ownstage_us"], r["ownstage_to_staged_us"],
+                r["xready_to_page_us"], r["page_to_sums_us"], r["sums_to_item0_us"]))
     att = [r for r in res["rows"] if r["layer"] == mid and r["stage"] == "attention"
            and np.isfinite(r.get("item0_to_wavemerge_us", np.nan))]
     if att:

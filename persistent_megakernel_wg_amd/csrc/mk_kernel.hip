@@ -698,11 +698,12 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
             return;
           }
         }
+        // the leader's own share staged (the barrier then waits for the others)
+        if (tr && w == 0 && c.lane == 0) trace_put(a, cu, ti, TR_XFREE, now32());
         if (!comp_barrier()) return;
         last_sync = ig;
       }
       if (tr && w == 0 && c.lane == 0) {
-        trace_put(a, cu, ti, TR_XFREE, now32());
         trace_put(a, cu, ti, TR_STAGED, now32());
         trace_put(a, cu, ti, TR_RETRY, c.retries);
       }
