@@ -1320,6 +1320,7 @@ DEV void lm_finish_b(Comp& c, InstrCP I) {
   if (lane == 0) old = ctr_release(ctr_line(a, I->sig_ctr, 0));
   old = uni(old);
   if (old + 1 != a.epoch * n_tiles) return;
+  ctr_acquire();
   for (uint32_t b = 0; b < nB; b++) {
     ArgBest all{-__builtin_inff(), 0xFFFFFFFFu};
     for (uint32_t t = lane; t < n_tiles; t += 64)
@@ -1537,6 +1538,7 @@ DEV void compute_b(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       if (c.lane == 0) old = ctr_release(ctr_line(a, I->seg_rows[0], 0));
       old = uni(old);
       if (old + 1 != a.epoch * I->aux[3]) continue;
+      ctr_acquire();
       run_merge_b<G>(c, I);
     }
     if ((i_flags(I) & F_SIGNAL) && c.lane == 0) ctr_signal(ctr_line(a, I->sig_ctr, uint32_t(cu) % kCtrSpread));

@@ -607,6 +607,7 @@ DEV void lm_finish(Comp& c, InstrCP I) {
   if (lane == 0) old = ctr_release(ctr_line(a, I->sig_ctr, 0));
   old = uni(old);
   if (old + 1 != c.ep * n_tiles) return;
+  ctr_acquire();
   ArgBest all{-__builtin_inff(), 0xFFFFFFFFu};
   for (uint32_t t = lane; t < n_tiles; t += 64)
     arg_update(all, ld_act(a.lm_slots + 2 * t), __float_as_uint(ld_act(a.lm_slots + 2 * t + 1)));
@@ -785,6 +786,7 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
       if (c.lane == 0) old = ctr_release(ctr_line(a, I->seg_rows[0], 0));
       old = uni(old);
       if (old + 1 != c.ep * I->aux[3]) continue;
+      ctr_acquire();
       run_merge<G>(c, I);
     }
     if constexpr (G::os) {
@@ -793,6 +795,7 @@ DEV void compute(const KArgs& a, InstrCP q, uint32_t n, int w, int cu) {
         if (c.lane == 0) old = ctr_release(ctr_line(a, I->aux[2], 0));
         old = uni(old);
         if (old + 1 != c.ep * I->aux[3]) continue;
+        ctr_acquire();
         if (!o_merge(c, I)) {
           if (c.lane == 0) lds_st(C_ABORT, 1);
           return;
