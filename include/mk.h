@@ -112,7 +112,8 @@ typedef struct {
                          Synchronization Mechanism", uses 4).  Default: the
                          fewest chunks of at most 4096 values each, since
                          every chunk adds two instructions per CU */
-  int32_t attn_block; /* KV positions per attention tile (multiple of 64;
+  int32_t attn_block; /* KV positions per attention tile (a multiple of 8 for
+                         the one-sequence decoder, of 64 for the MoE decoder;
                          default: chosen from max_seq and the CU count) */
   int32_t watchdog_ms;/* limit of any one wait on the device (a counter, a
                          step-tagged input, an LDS page or barrier) before

@@ -190,8 +190,9 @@ mk_status mk_build_plan(mk_ctx* c, const mk_plan_opts* opts) {
   in.opts = mk::resolve_opts(c->cfg, opts, n_cus);
   in.n_cus = n_cus;
   in.w = c->w;
-  if (in.opts.attn_block <= 0 || in.opts.attn_block % 64)
-    return fail(c, MK_ERR_INVALID_ARG, "mk_build_plan: attn_block must be a positive multiple of 64");
+  // (the one-sequence plan takes multiples of 8, the batched plan of 64)
+  if (in.opts.attn_block <= 0 || in.opts.attn_block % 8)
+    return fail(c, MK_ERR_INVALID_ARG, "mk_build_plan: attn_block must be a positive multiple of 8");
   if (mk::is_batched(c->cfg) && in.opts.generic_kernel)
     return fail(c, MK_ERR_UNSUPPORTED, "mk_build_plan: the batched decoder has no generic-kernel option");
   const int nblk = (c->cfg.max_seq + in.opts.attn_block - 1) / in.opts.attn_block;

@@ -134,6 +134,17 @@ def test_tiny_step_head_layouts(need_gpu, heads):
     _one_step_case(s, attn_heads=h // g, attn_block=64)
 
 
+@pytest.mark.parametrize("block", [24, 40])
+def test_tiny_position_blocks_of_eight_row_multiples(need_gpu, block):
+    # blocks that are not multiples of 64 positions: block boundaries inside
+    # a KV page, a last block holding the new position, 4 and 8 rows per unit
+    for h, g, dh in ((4, 2, 64), (8, 2, 64), (4, 1, 128)):
+        s = synth.SHAPES["tiny"].replace(n_q_heads=h, n_kv_heads=g, head_dim=dh)
+        _one_step_case(s, attn_block=block)
+        _one_step_case(s, attn_block=block, attn_heads=h // g)
+        _one_step_case(s, attn_block=block, pos=block)  # the new row opens a block
+
+
 @pytest.mark.parametrize("n_cus", [1, 3, 256])
 def test_tiny_split_k_o_projection(need_gpu, n_cus):
     # O tiles per (row block, KV group), each waiting only for its group's
