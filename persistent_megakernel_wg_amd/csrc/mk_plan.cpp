@@ -214,10 +214,12 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
     // vector-ALU GEMVs by default: the matrix-core LM head measured a few us
     // faster, but the kernel variant that carries it loses more elsewhere
     if (r.mfma == 0) r.mfma = -1;
-    // an eighth of the expert down-projection units in the ready queue
-    // (measured on the MoE shape: 1/4 4605, 1/8 4583, 1/16 4590 and no
-    // queue 4618 us per step)
-    if (r.edn_queue == 0) r.edn_queue = 8;
+    // half of the expert down-projection units in the ready queue (measured
+    // on the MoE shape with the current kernel, two interleaved rounds: 1/2
+    // 3878-3879, 1/3 3886, 1/4 3884-3890, 1/6 3942-3944, 1/8 3921-3930,
+    // 1/16 3888-3891 and no queue 3939-3940 us per step; an earlier build
+    // had measured 1/8 best by a few us)
+    if (r.edn_queue == 0) r.edn_queue = 2;
     if (r.edn_queue < 0 || r.edn_queue == 1) r.edn_queue = 0;
     // even gate/up slices by default: the weighted shares measured slower
     // on the MoE shape (4137 against 4001 us per step)
