@@ -142,8 +142,9 @@ typedef struct {
   int32_t mfma;       /* batched decoder: 1 = the LM head on matrix cores
                          (v_mfma_f32_16x16x32_bf16 tiles of 16 rows; the fp32
                          input split into bf16 high and low parts, fp32
-                         accumulation), run by a kernel variant of its own;
-                         -1 = on the vector ALUs (default).  Batch 1: always -1 */
+                         accumulation), run by a kernel variant of its own
+                         (default); -1 = on the vector ALUs.  Batch 1:
+                         always -1 */
   int32_t edn_queue;  /* MoE decoder: q > 1 = a 1/q share of each layer's
                          expert down-projection units waits in a ready queue
                          (chunks handed out at run time, each to whichever CU

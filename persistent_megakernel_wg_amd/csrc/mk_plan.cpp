@@ -211,9 +211,11 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
     // experts are split over the CUs by rows; the MLP chunk option is unused
     if (r.mlp_chunks <= 0) r.mlp_chunks = 1;
     r.o_split = -1;
-    // vector-ALU GEMVs by default: the matrix-core LM head measured a few us
-    // faster, but the kernel variant that carries it loses more elsewhere
-    if (r.mfma == 0) r.mfma = -1;
+    // the LM head on matrix cores by default: with the current kernel its
+    // variant measured 3845-3850 against 3872-3875 us per step on the MoE
+    // shape (two interleaved rounds; on earlier builds the variant lost
+    // elsewhere what its LM head gained)
+    if (r.mfma == 0) r.mfma = 1;
     // half of the expert down-projection units in the ready queue (measured
     // on the MoE shape with the current kernel, two interleaved rounds: 1/2
     // 3878-3879, 1/3 3886, 1/4 3884-3890, 1/6 3942-3944, 1/8 3921-3930,

@@ -138,7 +138,10 @@ def test_moe_default_plan_verifies(name):
     s = synth.SHAPES[name]
     summ, rep = B.mk_plan_check(B.config_from_shape(s), 256)
     assert summ["weight_bytes"] == moe_fixed_bytes(s)
-    assert summ["kernel_variant"] == 1          # the kernel built for 4 heads/group, Dh 128
+    # the kernel built for 4 heads/group, Dh 128, with the matrix-core LM head
+    # (the default); without it, the same shape's vector-ALU kernel
+    assert summ["kernel_variant"] == 2
+    assert B.mk_plan_check(B.config_from_shape(s), 256, B.plan_opts(mfma=-1))[0]["kernel_variant"] == 1
     assert summ["lds_bytes"] == 159744 and summ["n_pages"] == 5
     hpg = s.n_q_heads // s.n_kv_heads
     assert summ["attn_block"] * hpg <= 512      # scores of one tile fit the scratch
