@@ -222,7 +222,7 @@ mk_plan_opts resolve_opts(const mk_config& c, const mk_plan_opts* o, int n_cus) 
     // 1/16 3888-3891 and no queue 3939-3940 us per step; an earlier build
     // had measured 1/8 best by a few us)
     if (r.edn_queue == 0) r.edn_queue = 2;
-    if (r.edn_queue < 0 || r.edn_queue == 1) r.edn_queue = 0;
+    if (r.edn_queue < 0) r.edn_queue = 0;  // 1: every unit in the queue
     // even gate/up slices by default: the weighted shares measured slower
     // on the MoE shape (4137 against 4001 us per step)
     if (r.egu_balance == 0) r.egu_balance = -1;

@@ -110,7 +110,7 @@ def test_moe_tiny_matrix_core_lm_head(need_gpu, kw, opts):
 
 
 @pytest.mark.parametrize("queue,opts", [(2, {}), (2, {"n_cus": 1, "attn_block": 64}), (4, {"n_cus": 3}),
-                                        (-1, {}), (-1, {"n_cus": 37})])
+                                        (1, {"n_cus": 3}), (1, {"n_cus": 37}), (-1, {}), (-1, {"n_cus": 37})])
 def test_moe_tiny_ready_queue(need_gpu, queue, opts):
     # the expert down projection with a 1/queue share of its units handed out
     # at run time (chunks to whichever CU asks first), and with none

@@ -191,7 +191,7 @@ def test_gate_up_over_every_chunk_plans_verify(gu_all):
                 assert off["n_instr"] - on["n_instr"] == L * (on["mlp_chunks"] - 1) * min(n_cus, 256)
 
 
-@pytest.mark.parametrize("queue", [-1, 2, 4, 8, 16])
+@pytest.mark.parametrize("queue", [-1, 1, 2, 4, 8, 16])
 def test_moe_ready_queue_plans_verify(queue):
     for n_cus in (1, 3, 256):
         B.mk_plan_check(_cfg("moe_tiny"), n_cus, B.plan_opts(edn_queue=queue))
