@@ -188,6 +188,8 @@ def main() -> int:
                     help="MoE decoder: 1: gate/up shares weighted by each CU's earlier work; -1: even row slices")
     ap.add_argument("--o-split", type=int, default=0,
                     help="1: O projection split per KV group; -1: whole rows; 0: the plan's default")
+    ap.add_argument("--attn-heads", type=int, default=0,
+                    help="query heads per attention tile (0: the plan's default)")
     ap.add_argument("--gu-all", type=int, default=0,
                     help="1: gate/up of every MLP chunk in one instruction per CU; -1: one per chunk; "
                          "0: the plan's default")
@@ -217,6 +219,7 @@ def main() -> int:
     eng = Engine(shape, weights, kc, vc,
                  plan=B.plan_opts(n_cus=args.n_cus, attn_block=args.attn_block,
                                   mlp_chunks=args.mlp_chunks, o_split=args.o_split, mfma=args.mfma,
+                                  attn_heads=args.attn_heads,
                                   edn_queue=args.edn_queue,
                                   egu_balance=args.egu_balance, gu_all=args.gu_all))
     info = eng.plan_info()
